@@ -1,0 +1,363 @@
+"""Plain FP64 CPU oracle of one MiniMax-H3 DiT block forward.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module. The product path never calls it, and it
+shares no code with the HIP library or its Python binding.
+
+Every function is the plain definition written out in float64 with numpy. There is
+no blocking, fusion or reordering beyond what the definition states; library
+primitives (matrix products, exp) serve as steps.
+
+Sources (cited by page title and section):
+
+* [Sol-H3] "Sol-H3: Recursive Self-Improvement for MiniMax-H3 Inference
+  Acceleration on Sol-Engine across Cloud and Edge".
+  - §3.5 "Kernel Fusion": the block's three operator groups: (1) residual
+    addition with indexed gating, RMSNorm and indexed scale/shift modulation;
+    (2) QK normalization with partial RoPE; (3) SwiGLU splitting, SiLU and
+    multiplication. Hidden width 5376.
+  - §3.5 "Precision-preserving LoRA fusion": BF16 rounding points (the SwiGLU
+    gate product is kept in BF16 before the down projection).
+  - §3.2 "Optimized attention collectives": packed QKV storage; flat
+    (total, heads, head_dim) layout.
+  - §3.2 "Quantized communication": a token/head record holds 3x128 QKV values,
+    so the head width is 128.
+  - §3.4 "Safety rails": sequence packing [text | conditioning video | audio |
+    target video].
+* [vLLM-Omni H3] "MiniMax H3 on vLLM-Omni: integrating FastVideo FastH3" (blog).
+  - §3.1: 58,758 valid tokens in a 58,816-token aligned buffer; the attention
+    backend receives the valid length and drops the structural padding suffix.
+  - §3.2: fused Q/K RMSNorm + RoPE; merged FP32 modulation, normalization and
+    residual; fused SwiGLU.
+* [SolarWM] "SolarWM H3 Realtime Interaction".
+  - stage 2 "attention backend": queries are grouped (condition, audio,
+    current video); video queries also read a longer history context.
+  - stage 3 "history K/V reuse": the history K/V is concatenated once per
+    refresh and reused by the chunk's four denoise forwards.
+
+Readings where the pages are silent (each also listed in the design notes):
+  R1 norm inside AdaLN is RMSNorm without an affine weight; LayerNorm optional.
+  R3 eps = 1e-6 for every norm unless given.
+  R4 modulation h = n * (1 + scale) + shift; gated residual x + gate * branch.
+  R5 table rows (shift_a, scale_a, gate_a, shift_f, scale_f, gate_f).
+  R7 QK-norm is per head over its 128 channels with one gain vector for q and
+     one for k, shared by all heads.
+  R8 partial RoPE rotates the first rot_dim channels of a head; default
+     rotate-half pairing (i, i + rot_dim/2); omega_i = theta^(-2i/rot_dim);
+     the angle is position * omega_i; position defaults to the packed row.
+  R9 RMSNorm first, then RoPE.
+  R10 attention is non-causal with scale 1/sqrt(head_dim); keys limited to
+      the valid prefix [0, valid_len); padding query rows give 0.
+  R11 w_qkv rows are q | k | v, each head-major; w_up rows are gate | up.
+  R13 the exact result keeps no intermediate rounding (float64 throughout);
+      an optional diagnosis mode rounds at the BF16 store points.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+# Row order of one modulation-table entry (reading R5).
+SHIFT_A, SCALE_A, GATE_A, SHIFT_F, SCALE_F, GATE_F = range(6)
+
+
+# ----------------------------------------------------------------------------
+# Decoding of the bytes the GPU receives (storage formats, not the method).
+# ----------------------------------------------------------------------------
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of BF16 bit patterns (uint16) as float64.
+
+    A BF16 number is the upper half of an IEEE binary32 number, so shifting the
+    pattern into the high 16 bits of a 32-bit word gives the same value."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(F64)
+
+
+def round_to_bf16(a: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest BF16 value, ties to even (used only
+    by the optional BF16-store-point diagnosis mode, reading R13).
+
+    Rounding is done in two exact steps: float64 -> nearest binary32 would
+    double-round, so the BF16 grid is computed directly from the float64 value:
+    the spacing of BF16 at |a| is 2^(e - 7) for a in [2^e, 2^(e+1))."""
+    a = np.asarray(a, dtype=F64)
+    out = np.zeros_like(a)
+    nz = (a != 0) & np.isfinite(a)
+    m, e = np.frexp(a[nz])            # a = m * 2^e, 0.5 <= |m| < 1
+    # BF16 has 8 significant bits: scale the mantissa to [128, 256).
+    scaled = m * 256.0
+    r = np.round(scaled)              # numpy rounds half to even
+    out[nz] = np.ldexp(r, e - 8)
+    out[~nz] = a[~nz]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Normalisation and modulation (Sol-H3 §3.5 group (1); vLLM-Omni H3 §3.2).
+# ----------------------------------------------------------------------------
+def rms_norm(z: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis without affine weight: z / sqrt(mean(z^2) + eps)."""
+    z = np.asarray(z, dtype=F64)
+    ms = np.mean(z * z, axis=-1, keepdims=True)
+    return z / np.sqrt(ms + eps)
+
+
+def layer_norm(z: np.ndarray, eps: float) -> np.ndarray:
+    """LayerNorm over the last axis without affine weight: (z - mean) / sqrt(var + eps),
+    with the population variance (optional norm type, reading R1)."""
+    z = np.asarray(z, dtype=F64)
+    mu = np.mean(z, axis=-1, keepdims=True)
+    d = z - mu
+    var = np.mean(d * d, axis=-1, keepdims=True)
+    return d / np.sqrt(var + eps)
+
+
+def modulate(n: np.ndarray, shift: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """AdaLN scale/shift modulation n * (1 + scale) + shift (reading R4)."""
+    return n * (1.0 + scale) + shift
+
+
+def modulate_norm(x, shift, scale, eps, norm_type=0):
+    """Group (1) second half: normalise each row, then indexed scale/shift.
+
+    `shift` and `scale` are per-row already (the caller gathers the table entry
+    each row's index selects)."""
+    n = rms_norm(x, eps) if norm_type == 0 else layer_norm(x, eps)
+    return modulate(n, shift, scale)
+
+
+def gated_residual(x, gate, branch):
+    """Group (1) first half: residual addition with (indexed) gating x + gate * branch."""
+    return x + gate * branch
+
+
+def gather_mod(mod: np.ndarray, mod_idx, n_rows: int) -> np.ndarray:
+    """Per-row modulation rows: entry mod_idx[r] of the [G, 6, H] table, or
+    entry 0 for every row when no index is given (broadcast, reading R6).
+    Returns [n_rows, 6, H] float64."""
+    mod = np.asarray(mod, dtype=F64)
+    if mod_idx is None:
+        return np.broadcast_to(mod[0], (n_rows,) + mod.shape[1:])
+    return mod[np.asarray(mod_idx[:n_rows], dtype=np.int64)]
+
+
+# ----------------------------------------------------------------------------
+# Linear layers (packed QKV: Sol-H3 §3.2; output and FFN projections).
+# ----------------------------------------------------------------------------
+def linear(x: np.ndarray, w: np.ndarray, b=None) -> np.ndarray:
+    """y = x W^T (+ b) with W stored [out, in]."""
+    y = np.asarray(x, dtype=F64) @ np.asarray(w, dtype=F64).T
+    if b is not None:
+        y = y + np.asarray(b, dtype=F64)
+    return y
+
+
+# ----------------------------------------------------------------------------
+# Group (2): QK RMSNorm with partial RoPE (Sol-H3 §3.5; vLLM-Omni H3 §3.2).
+# ----------------------------------------------------------------------------
+def head_rms_norm(t: np.ndarray, heads: int, head_dim: int, gain, eps: float) -> np.ndarray:
+    """Per-head RMSNorm over the head's channels, times a per-channel gain shared
+    by all heads (reading R7). t is [L, heads*head_dim]."""
+    L = t.shape[0]
+    th = np.asarray(t, dtype=F64).reshape(L, heads, head_dim)
+    out = rms_norm(th, eps) * np.asarray(gain, dtype=F64)[None, None, :]
+    return out.reshape(L, heads * head_dim)
+
+
+def rope_frequencies(rot_dim: int, theta: float) -> np.ndarray:
+    """omega_i = theta^(-2i/rot_dim) for i in [0, rot_dim/2) (reading R8)."""
+    i = np.arange(rot_dim // 2, dtype=F64)
+    return np.power(F64(theta), -2.0 * i / rot_dim)
+
+
+def apply_rope(t: np.ndarray, pos, heads: int, head_dim: int, rot_dim: int,
+               theta: float, pairing: int = 0) -> np.ndarray:
+    """Partial rotary embedding of each head's first rot_dim channels.
+
+    pairing 0 (rotate-half): channel pair (i, i + rot_dim/2);
+    pairing 1 (interleaved): channel pair (2i, 2i + 1).
+    A pair (a, b) at angle phi = pos * omega_i becomes
+    (a cos phi - b sin phi, a sin phi + b cos phi). Channels [rot_dim, head_dim)
+    pass through. Rows with pos < 0 are left unrotated."""
+    L = t.shape[0]
+    out = np.array(t, dtype=F64).reshape(L, heads, head_dim)
+    if rot_dim == 0:
+        return out.reshape(L, heads * head_dim)
+    pos = np.asarray(pos, dtype=F64)
+    half = rot_dim // 2
+    phi = pos[:, None] * rope_frequencies(rot_dim, theta)[None, :]   # [L, half]
+    c = np.cos(phi)[:, None, :]
+    s = np.sin(phi)[:, None, :]
+    if pairing == 0:
+        ia = np.arange(half)
+        ib = ia + half
+    else:
+        ia = 2 * np.arange(half)
+        ib = ia + 1
+    a = out[:, :, ia].copy()
+    b = out[:, :, ib].copy()
+    ra = a * c - b * s
+    rb = a * s + b * c
+    keep = (pos < 0)
+    ra[keep] = a[keep]
+    rb[keep] = b[keep]
+    out[:, :, ia] = ra
+    out[:, :, ib] = rb
+    return out.reshape(L, heads * head_dim)
+
+
+def qk_norm_rope(t, pos, heads, head_dim, gain, eps, rot_dim, theta, pairing=0):
+    """Group (2): RMSNorm per head (with gain), then partial RoPE (reading R9)."""
+    return apply_rope(head_rms_norm(t, heads, head_dim, gain, eps), pos, heads,
+                      head_dim, rot_dim, theta, pairing)
+
+
+# ----------------------------------------------------------------------------
+# Attention (Sol-H3 §3.2 profile; vLLM-Omni H3 §3.1 valid length;
+# SolarWM stages 2-3 grouped queries and history K/V).
+# ----------------------------------------------------------------------------
+def _softmax_rows(s: np.ndarray) -> np.ndarray:
+    m = np.max(s, axis=-1, keepdims=True)
+    p = np.exp(s - m)
+    return p / np.sum(p, axis=-1, keepdims=True)
+
+
+def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                   q_chunk: int = 1024) -> np.ndarray:
+    """softmax(q k^T * scale) v for one head over every key given.
+
+    q [Lq, d], k and v [Lk, d]. The subtraction of the row maximum before exp is
+    the usual exact rewriting of softmax. Queries are processed in chunks only to
+    bound memory; each chunk is the full definition."""
+    q = np.asarray(q, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    v = np.asarray(v, dtype=F64)
+    out = np.empty((q.shape[0], v.shape[1]), dtype=F64)
+    for a in range(0, q.shape[0], q_chunk):
+        s = (q[a:a + q_chunk] @ k.T) * scale
+        out[a:a + q_chunk] = _softmax_rows(s) @ v
+    return out
+
+
+def attention(q, k, v, heads: int, head_dim: int, scale=None, q_chunk: int = 1024):
+    """Multi-head attention in the flat (rows, heads*head_dim) layout: each head
+    attends over all rows of k/v given. Returns [Lq, heads*head_dim]."""
+    if scale is None or scale == 0:
+        scale = 1.0 / np.sqrt(head_dim)
+    Lq = q.shape[0]
+    out = np.empty((Lq, heads * head_dim), dtype=F64)
+    for h in range(heads):
+        sl = slice(h * head_dim, (h + 1) * head_dim)
+        out[:, sl] = attention_head(q[:, sl], k[:, sl], v[:, sl], scale, q_chunk)
+    return out
+
+
+def attention_grouped(q, groups, heads: int, head_dim: int, n_rows: int, scale=None):
+    """Grouped attention: each query group [q_begin, q_end) attends over the
+    concatenation of its K/V segments (SolarWM stages 2-3). `groups` is a list of
+    (q_begin, q_end, [(k_seg, v_seg), ...]). Rows outside every group give 0."""
+    out = np.zeros((n_rows, heads * head_dim), dtype=F64)
+    for (qb, qe, segs) in groups:
+        if qe <= qb:
+            continue
+        kk = np.concatenate([np.asarray(s[0], dtype=F64) for s in segs], axis=0)
+        vv = np.concatenate([np.asarray(s[1], dtype=F64) for s in segs], axis=0)
+        out[qb:qe] = attention(q[qb:qe], kk, vv, heads, head_dim, scale)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Group (3): SwiGLU (Sol-H3 §3.5; vLLM-Omni H3 §3.2).
+# ----------------------------------------------------------------------------
+def silu(z: np.ndarray) -> np.ndarray:
+    """silu(z) = z / (1 + exp(-z)), written to avoid overflow for large |z|."""
+    z = np.asarray(z, dtype=F64)
+    out = np.empty_like(z)
+    pos = z >= 0
+    out[pos] = z[pos] / (1.0 + np.exp(-z[pos]))
+    ez = np.exp(z[~pos])
+    out[~pos] = z[~pos] * ez / (1.0 + ez)
+    return out
+
+
+def swiglu(u: np.ndarray, ffn: int) -> np.ndarray:
+    """Split u = [gate | up] along columns, then silu(gate) * up (reading R11)."""
+    u = np.asarray(u, dtype=F64)
+    return silu(u[:, :ffn]) * u[:, ffn:2 * ffn]
+
+
+# ----------------------------------------------------------------------------
+# The whole block.
+# ----------------------------------------------------------------------------
+def block_forward(x, w, mod, *, heads: int, head_dim: int, ffn: int, valid_len: int,
+                  rot_dim: int = 64, theta: float = 10000.0, eps: float = 1e-6,
+                  norm_type: int = 0, pairing: int = 0, mod_idx=None, pos=None,
+                  groups=None, scale=None, bf16_points: bool = False):
+    """One DiT block forward over a packed sequence of L_buf rows, valid_len valid.
+
+    x      [L_buf, H] float64 (decoded BF16 values)
+    w      dict with w_qkv [3H, H], w_o [H, H], w_up [2F, H], w_down [H, F],
+           q_gain [head_dim], k_gain [head_dim], optional b_qkv, b_o, b_up, b_down
+    mod    [G, 6, H] modulation table (reading R5 row order)
+    groups None for dense attention over [0, valid_len); else a list of
+           (q_begin, q_end, segs) where segs lists ('self', begin, len) for rows of
+           this call's own K/V, or (k_array, v_array) for external (history) K/V.
+
+    Steps (Sol-H3 §3.5 groups (1)-(3) around the projections):
+      h   = modnorm(x; shift_a, scale_a)
+      qkv = h W_qkv^T                     (q | k | v column blocks)
+      q~, k~ = RoPE(RMSNorm_head(q) * g_q), RoPE(RMSNorm_head(k) * g_k)
+      o   = attention(q~, k~, v)          (keys [0, valid_len) or per group)
+      a   = o W_o^T ;   x1 = x + gate_a * a
+      h2  = modnorm(x1; shift_f, scale_f)
+      u   = h2 W_up^T ; g = silu(u_gate) * u_up
+      f   = g W_down^T ; y = x1 + gate_f * f ;   y = 0 on padding rows
+    Returns a dict with y and every intermediate, each [L_buf, .] with padding
+    rows zero."""
+    x = np.asarray(x, dtype=F64)
+    L_buf, H = x.shape
+    V = int(valid_len)
+    rnd = round_to_bf16 if bf16_points else (lambda a: a)
+    m = gather_mod(mod, mod_idx, V)
+    xv = x[:V]
+    if pos is None:
+        posv = np.arange(V, dtype=F64)
+    else:
+        posv = np.asarray(pos[:V], dtype=F64)
+
+    h = rnd(modulate_norm(xv, m[:, SHIFT_A], m[:, SCALE_A], eps, norm_type))
+    qkv = rnd(linear(h, w['w_qkv'], w.get('b_qkv')))
+    q, k, v = qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:3 * H]
+    qn = rnd(qk_norm_rope(q, posv, heads, head_dim, w['q_gain'], eps, rot_dim, theta, pairing))
+    kn = rnd(qk_norm_rope(k, posv, heads, head_dim, w['k_gain'], eps, rot_dim, theta, pairing))
+    if groups is None:
+        o = attention(qn, kn, v, heads, head_dim, scale)
+    else:
+        gl = []
+        for (qb, qe, segs) in groups:
+            ss = []
+            for s in segs:
+                if isinstance(s[0], str):
+                    _, b0, ln = s
+                    ss.append((kn[b0:b0 + ln], v[b0:b0 + ln]))
+                else:
+                    ss.append((s[0], s[1]))
+            gl.append((qb, qe, ss))
+        o = attention_grouped(qn, gl, heads, head_dim, V, scale)
+    o = rnd(o)
+    a = linear(o, w['w_o'], w.get('b_o'))
+    x1 = rnd(gated_residual(xv, m[:, GATE_A], a))
+    h2 = rnd(modulate_norm(x1, m[:, SHIFT_F], m[:, SCALE_F], eps, norm_type))
+    u = linear(h2, w['w_up'], w.get('b_up'))
+    g = rnd(swiglu(u, ffn))
+    f = linear(g, w['w_down'], w.get('b_down'))
+    y = rnd(gated_residual(x1, m[:, GATE_F], f))
+
+    def pad(t):
+        full = np.zeros((L_buf, t.shape[1]), dtype=F64)
+        full[:V] = t
+        return full
+
+    return {k_: pad(t_) for k_, t_ in dict(h=h, qkv=qkv, q=qn, k=kn, v=v, o=o, a=a,
+                                            x1=x1, h2=h2, u=u, g=g, f=f, y=y).items()}

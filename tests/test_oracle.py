@@ -1,0 +1,453 @@
+"""Pins of the FP64 oracle against what the definitions and the pages fix.
+
+Each test checks the oracle against something other than itself: a library
+routine computing the same quantity by another route, a closed form, an
+invariant of the definition, a worked case, or brute force on tiny inputs.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from oracle import h3_oracle as O
+from video_diffusion_transformer_dit_amd import inputs as I
+
+RNG = np.random.default_rng(12345)
+
+
+def _load(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# storage decoding and rounding
+# --------------------------------------------------------------------------
+def test_bf16_decode_matches_torch():
+    bits = RNG.integers(0, 0x7F80, size=4096, dtype=np.uint16)   # finite positives
+    bits[::2] |= np.uint16(0x8000)
+    t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.bf16_to_f64(bits), t)
+
+
+def test_round_to_bf16_matches_torch_rne():
+    # float32-representable values so torch's float32 -> bfloat16 rounding is single-step
+    a = RNG.standard_normal(20000).astype(np.float32)
+    a[:8] = np.array([1.00390625, 1.01171875, -1.00390625, 3.0, 0.0, 255.5, 257.0, 1e-20],
+                     dtype=np.float32)
+    ref = torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_to_bf16(a.astype(np.float64)), ref)
+
+
+# --------------------------------------------------------------------------
+# group (1): norms, modulation, gated residual
+# --------------------------------------------------------------------------
+def test_rms_norm_closed_form(golden_dir):
+    c = _load(golden_dir, "closed_forms.json")["rmsnorm_3_4"]
+    np.testing.assert_allclose(O.rms_norm(np.array(c["x"]), c["eps"]), c["expect"], rtol=1e-15)
+
+
+def test_rms_norm_matches_torch_library():
+    x = RNG.standard_normal((7, 384)) * 3.0
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (384,), eps=1e-6).numpy()
+    np.testing.assert_allclose(O.rms_norm(x, 1e-6), ref, rtol=1e-13, atol=1e-14)
+
+
+def test_rms_norm_scale_invariance_and_unit_rms():
+    x = RNG.standard_normal((5, 256))
+    for c in (1e-3, 0.5, 7.0, 1e4):
+        np.testing.assert_allclose(O.rms_norm(c * x, 0.0), O.rms_norm(x, 0.0), rtol=1e-13)
+    n = O.rms_norm(x, 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(n * n, axis=-1)), 1.0, rtol=1e-14)
+    # with eps the error against the eps-free norm is bounded by eps / mean(x^2)
+    eps = 1e-6
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    assert np.all(np.abs(O.rms_norm(x, eps) / n - 1.0) <= eps / ms)
+
+
+def test_layer_norm_matches_torch_and_moments():
+    x = RNG.standard_normal((6, 512)) * 2.0 + 0.7
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (512,), eps=1e-6).numpy()
+    np.testing.assert_allclose(O.layer_norm(x, 1e-6), ref, rtol=1e-12, atol=1e-13)
+    n = O.layer_norm(x, 0.0)
+    np.testing.assert_allclose(n.mean(-1), 0.0, atol=1e-14)
+    np.testing.assert_allclose(n.var(-1), 1.0, rtol=1e-13)
+
+
+def test_modulation_special_cases():
+    x = RNG.standard_normal((4, 64))
+    z = np.zeros((4, 64))
+    np.testing.assert_allclose(O.modulate_norm(x, z, z, 1e-6), O.rms_norm(x, 1e-6), rtol=0, atol=0)
+    # scale = -1 removes the normalised signal entirely, leaving the shift
+    sh = RNG.standard_normal((4, 64))
+    np.testing.assert_allclose(O.modulate_norm(x, sh, -np.ones((4, 64)), 1e-6), sh, atol=1e-15)
+    # scale and shift act per channel: n*(1+s)+t
+    s = RNG.standard_normal(64)
+    t = RNG.standard_normal(64)
+    n = O.rms_norm(x, 1e-6)
+    np.testing.assert_allclose(O.modulate_norm(x, t, s, 1e-6)[:, 5], n[:, 5] * (1 + s[5]) + t[5], rtol=1e-15)
+    # gate = 0 leaves the residual stream unchanged, exactly
+    br = RNG.standard_normal((4, 64)) * 1e3
+    np.testing.assert_array_equal(O.gated_residual(x, np.zeros(64), br), x)
+
+
+def test_gather_mod_indexing():
+    mod = RNG.standard_normal((3, 6, 8))
+    idx = np.array([2, 0, 1, 1, 2], dtype=np.int32)
+    g = O.gather_mod(mod, idx, 5)
+    for r in range(5):
+        np.testing.assert_array_equal(g[r], mod[idx[r]])
+    g0 = O.gather_mod(mod, None, 5)
+    for r in range(5):
+        np.testing.assert_array_equal(g0[r], mod[0])
+
+
+# --------------------------------------------------------------------------
+# projections
+# --------------------------------------------------------------------------
+def test_linear_matches_triple_loop():
+    x = RNG.standard_normal((3, 5))
+    w = RNG.standard_normal((4, 5))
+    b = RNG.standard_normal(4)
+    ref = np.zeros((3, 4))
+    for i in range(3):
+        for j in range(4):
+            acc = 0.0
+            for kk in range(5):
+                acc += x[i, kk] * w[j, kk]
+            ref[i, j] = acc + b[j]
+    np.testing.assert_allclose(O.linear(x, w, b), ref, rtol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# group (2): QK RMSNorm + partial RoPE
+# --------------------------------------------------------------------------
+def test_head_rms_norm_matches_torch_with_gain():
+    heads, d = 3, 128
+    t = RNG.standard_normal((9, heads * d)) * 4.0
+    gain = 1.0 + 0.02 * RNG.standard_normal(d)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(t.reshape(9, heads, d)), (d,),
+                                       weight=torch.from_numpy(gain), eps=1e-6).numpy()
+    np.testing.assert_allclose(O.head_rms_norm(t, heads, d, gain, 1e-6), ref.reshape(9, -1),
+                               rtol=1e-13, atol=1e-14)
+    # heads are normalised independently: scaling one head leaves the others unchanged
+    t2 = t.copy()
+    t2[:, d:2 * d] *= 50.0
+    a, b = O.head_rms_norm(t, heads, d, gain, 0.0), O.head_rms_norm(t2, heads, d, gain, 0.0)
+    np.testing.assert_allclose(a, b, rtol=1e-13)
+
+
+def test_rope_frequencies_closed_form():
+    w = O.rope_frequencies(64, 10000.0)
+    assert w.shape == (32,)
+    assert w[0] == 1.0
+    np.testing.assert_allclose(w[16], 0.01, rtol=1e-15)    # theta^(-1/2)
+    np.testing.assert_allclose(w[8], 0.1, rtol=1e-15)      # theta^(-1/4)
+
+
+@pytest.mark.parametrize("pairing", [0, 1])
+def test_rope_matches_complex_multiplication(pairing):
+    heads, d, R, theta = 2, 128, 64, 10000.0
+    L = 11
+    t = RNG.standard_normal((L, heads * d))
+    pos = RNG.integers(0, 60000, size=L)
+    out = O.apply_rope(t, pos, heads, d, R, theta, pairing).reshape(L, heads, d)
+    th = t.reshape(L, heads, d)
+    half = R // 2
+    ia = np.arange(half) if pairing == 0 else 2 * np.arange(half)
+    ib = ia + half if pairing == 0 else ia + 1
+    for r in range(L):
+        for h in range(heads):
+            for i in range(half):
+                z = complex(th[r, h, ia[i]], th[r, h, ib[i]])
+                zr = z * complex(math.cos(pos[r] * theta ** (-2 * i / R)),
+                                 math.sin(pos[r] * theta ** (-2 * i / R)))
+                assert abs(out[r, h, ia[i]] - zr.real) < 1e-10   # angles reach 6e4 rad: ulp ~7e-12
+                assert abs(out[r, h, ib[i]] - zr.imag) < 1e-10
+    # channels beyond rot_dim pass through untouched
+    np.testing.assert_array_equal(out[:, :, R:], th[:, :, R:])
+
+
+def test_rope_invariants():
+    heads, d, R = 2, 128, 64
+    L = 16
+    t = RNG.standard_normal((L, heads * d))
+    pos = np.arange(L) * 3977
+    r = O.apply_rope(t, pos, heads, d, R, 1e4)
+    # per-head norm preserved
+    np.testing.assert_allclose(np.linalg.norm(r.reshape(L, heads, d), axis=-1),
+                               np.linalg.norm(t.reshape(L, heads, d), axis=-1), rtol=1e-13)
+    # pos 0, rot_dim 0, negative pos: identity
+    np.testing.assert_allclose(O.apply_rope(t, np.zeros(L), heads, d, R, 1e4), t, rtol=0, atol=0)
+    np.testing.assert_array_equal(O.apply_rope(t, pos, heads, d, 0, 1e4), t)
+    np.testing.assert_array_equal(O.apply_rope(t, -np.ones(L), heads, d, R, 1e4), t)
+    # scores depend only on relative position: shifting every position changes nothing
+    q = RNG.standard_normal((L, heads * d))
+    k = RNG.standard_normal((L, heads * d))
+    s1 = O.apply_rope(q, pos, heads, d, R, 1e4)[:, :d] @ O.apply_rope(k, pos, heads, d, R, 1e4)[:, :d].T
+    s2 = (O.apply_rope(q, pos + 12345, heads, d, R, 1e4)[:, :d]
+          @ O.apply_rope(k, pos + 12345, heads, d, R, 1e4)[:, :d].T)
+    np.testing.assert_allclose(s1, s2, rtol=1e-9, atol=1e-9)
+
+
+# --------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------
+def _naive_attention(q, k, v, scale):
+    Lq, d = q.shape
+    out = np.zeros((Lq, v.shape[1]))
+    for i in range(Lq):
+        s = [sum(q[i, c] * k[j, c] for c in range(d)) * scale for j in range(k.shape[0])]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        z = sum(e)
+        for j in range(k.shape[0]):
+            out[i] += (e[j] / z) * v[j]
+    return out
+
+
+def test_attention_matches_naive_loops():
+    q = RNG.standard_normal((6, 8)) * 2
+    k = RNG.standard_normal((9, 8)) * 2
+    v = RNG.standard_normal((9, 8))
+    np.testing.assert_allclose(O.attention_head(q, k, v, 1 / math.sqrt(8)),
+                               _naive_attention(q, k, v, 1 / math.sqrt(8)), rtol=1e-12, atol=1e-13)
+
+
+def test_attention_matches_torch_sdpa_library():
+    heads, d = 3, 128
+    q = RNG.standard_normal((40, heads * d))
+    k = RNG.standard_normal((57, heads * d))
+    v = RNG.standard_normal((57, heads * d))
+    tq = torch.from_numpy(q.reshape(40, heads, d)).transpose(0, 1)
+    tk = torch.from_numpy(k.reshape(57, heads, d)).transpose(0, 1)
+    tv = torch.from_numpy(v.reshape(57, heads, d)).transpose(0, 1)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv).transpose(0, 1).reshape(40, -1)
+    np.testing.assert_allclose(O.attention(q, k, v, heads, d), ref.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_attention_worked_case(golden_dir):
+    c = _load(golden_dir, "closed_forms.json")["attention_two_keys"]
+    d = c["head_dim"]
+    o = O.attention_head(np.array([c["q"]]), np.array(c["k"]), np.array(c["v"]), 1 / math.sqrt(d))
+    np.testing.assert_allclose(o[0], c["expect"], atol=c["tol"])
+
+
+def test_attention_invariants():
+    d = 128
+    q = RNG.standard_normal((10, d)) * 3
+    k = RNG.standard_normal((33, d))
+    v = RNG.standard_normal((33, d))
+    sc = 1 / math.sqrt(d)
+    # softmax weights sum to one: a constant value column comes back unchanged
+    vc = np.ones((33, d)) * 2.5
+    np.testing.assert_allclose(O.attention_head(q, k, vc, sc), 2.5, rtol=1e-14)
+    # equal keys: the output is the mean of the values
+    ke = np.tile(k[:1], (33, 1))
+    np.testing.assert_allclose(O.attention_head(q, ke, v, sc), np.tile(v.mean(0), (10, 1)), rtol=1e-12, atol=1e-13)
+    # a single key: the output is that key's value, for every query
+    np.testing.assert_allclose(O.attention_head(q, k[:1], v[:1], sc), np.tile(v[:1], (10, 1)), rtol=1e-15)
+    # jointly permuting keys and values changes nothing
+    p = RNG.permutation(33)
+    np.testing.assert_allclose(O.attention_head(q, k[p], v[p], sc), O.attention_head(q, k, v, sc), rtol=1e-12)
+
+
+def test_attention_segment_merge_equals_unsplit():
+    """Splitting the keys into segments, attending to each, and merging the partial
+    results by their log-sum-exp equals attending over the concatenation; this pins
+    the grouped path (history segment followed by current rows)."""
+    d = 128
+    q = RNG.standard_normal((12, d)) * 2
+    k = RNG.standard_normal((50, d))
+    v = RNG.standard_normal((50, d))
+    sc = 1 / math.sqrt(d)
+    cuts = [0, 17, 18, 50]
+    parts = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        s = q @ k[a:b].T * sc
+        m = s.max(1, keepdims=True)
+        e = np.exp(s - m)
+        parts.append((m, e.sum(1, keepdims=True), e @ v[a:b]))
+    M = np.max(np.concatenate([p[0] for p in parts], 1), 1, keepdims=True)
+    num = sum(np.exp(p[0] - M) * p[2] for p in parts)
+    den = sum(np.exp(p[0] - M) * p[1] for p in parts)
+    heads = 1
+    g = O.attention_grouped(q, [(0, 12, [(k[:17], v[:17]), (k[17:], v[17:])])], heads, d, 12)
+    np.testing.assert_allclose(g, num / den, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_grouped_rows_outside_groups_are_zero():
+    d = 128
+    q = RNG.standard_normal((20, d))
+    k = RNG.standard_normal((20, d))
+    v = RNG.standard_normal((20, d))
+    g = O.attention_grouped(q, [(2, 5, [(k, v)]), (9, 14, [(k[:3], v[:3])])], 1, d, 20)
+    assert np.all(g[:2] == 0) and np.all(g[5:9] == 0) and np.all(g[14:] == 0)
+    np.testing.assert_allclose(g[9:14], O.attention_head(q[9:14], k[:3], v[:3], 1 / math.sqrt(d)))
+
+
+# --------------------------------------------------------------------------
+# group (3): SwiGLU
+# --------------------------------------------------------------------------
+def test_silu_matches_scipy_expit_and_limits():
+    z = np.concatenate([RNG.standard_normal(1000) * 10, [0.0, 40.0, -40.0, 750.0, -750.0]])
+    np.testing.assert_allclose(O.silu(z), z * scipy.special.expit(z), rtol=1e-14, atol=1e-300)
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    assert O.silu(np.array([750.0]))[0] == 750.0
+
+
+def test_swiglu_worked_case(golden_dir):
+    c = _load(golden_dir, "closed_forms.json")["swiglu_split"]
+    np.testing.assert_allclose(O.swiglu(np.array(c["u"]), c["ffn"]), c["expect"], atol=c["tol"])
+
+
+# --------------------------------------------------------------------------
+# the whole block
+# --------------------------------------------------------------------------
+def _tiny_block(L=7, V=6, H=16, heads=2, d=8, F=12, R=4, seed=0, bias=True):
+    r = np.random.default_rng(seed)
+    w = dict(w_qkv=r.standard_normal((3 * H, H)) * 0.3, w_o=r.standard_normal((H, H)) * 0.3,
+             w_up=r.standard_normal((2 * F, H)) * 0.3, w_down=r.standard_normal((H, F)) * 0.3,
+             q_gain=1 + 0.1 * r.standard_normal(d), k_gain=1 + 0.1 * r.standard_normal(d))
+    if bias:
+        w.update(b_qkv=r.standard_normal(3 * H) * 0.1, b_o=r.standard_normal(H) * 0.1,
+                 b_up=r.standard_normal(2 * F) * 0.1, b_down=r.standard_normal(H) * 0.1)
+    x = r.standard_normal((L, H))
+    mod = r.standard_normal((2, 6, H)) * 0.3
+    idx = r.integers(0, 2, size=L).astype(np.int32)
+    return x, w, mod, idx, dict(heads=heads, head_dim=d, ffn=F, valid_len=V, rot_dim=R, theta=100.0)
+
+
+def _naive_block(x, w, mod, idx, heads, head_dim, ffn, valid_len, rot_dim, theta, eps=1e-6):
+    """The block written as scalar loops, independently of the oracle's array code."""
+    H = x.shape[1]
+    d = head_dim
+    y = np.zeros_like(x)
+
+    def rms(vec):
+        ms = sum(t * t for t in vec) / len(vec)
+        return [t / math.sqrt(ms + eps) for t in vec]
+
+    def mat(wm, b, vec):
+        return [sum(wm[j][c] * vec[c] for c in range(len(vec))) + (b[j] if b is not None else 0.0)
+                for j in range(len(wm))]
+
+    rows = []
+    for r in range(valid_len):
+        m = mod[idx[r]]
+        n = rms(list(x[r]))
+        h = [n[c] * (1 + m[1][c]) + m[0][c] for c in range(H)]
+        qkv = mat(w['w_qkv'], w.get('b_qkv'), h)
+        rows.append(qkv)
+    qs, ks, vs = [], [], []
+    for r in range(valid_len):
+        qkv = rows[r]
+        qrow, krow = [], []
+        for (src, gain, dst) in ((qkv[0:H], w['q_gain'], qrow), (qkv[H:2 * H], w['k_gain'], krow)):
+            for hh in range(heads):
+                seg = rms(src[hh * d:(hh + 1) * d])
+                seg = [seg[c] * gain[c] for c in range(d)]
+                out = list(seg)
+                for i in range(rot_dim // 2):
+                    ang = r * theta ** (-2.0 * i / rot_dim)
+                    a, b = seg[i], seg[i + rot_dim // 2]
+                    out[i] = a * math.cos(ang) - b * math.sin(ang)
+                    out[i + rot_dim // 2] = a * math.sin(ang) + b * math.cos(ang)
+                dst.extend(out)
+        qs.append(qrow)
+        ks.append(krow)
+        vs.append(qkv[2 * H:3 * H])
+    for r in range(valid_len):
+        m = mod[idx[r]]
+        o = []
+        for hh in range(heads):
+            sl = slice(hh * d, (hh + 1) * d)
+            s = [sum(a * b for a, b in zip(qs[r][sl], ks[t][sl])) / math.sqrt(d) for t in range(valid_len)]
+            mx = max(s)
+            e = [math.exp(t - mx) for t in s]
+            z = sum(e)
+            for c in range(d):
+                o.append(sum(e[t] * vs[t][sl][c] for t in range(valid_len)) / z)
+        a = mat(w['w_o'], w.get('b_o'), o)
+        x1 = [x[r][c] + m[2][c] * a[c] for c in range(H)]
+        n2 = rms(x1)
+        h2 = [n2[c] * (1 + m[4][c]) + m[3][c] for c in range(H)]
+        u = mat(w['w_up'], w.get('b_up'), h2)
+        g = [u[j] / (1 + math.exp(-u[j])) * u[ffn + j] for j in range(ffn)]
+        f = mat(w['w_down'], w.get('b_down'), g)
+        y[r] = [x1[c] + m[5][c] * f[c] for c in range(H)]
+    return y
+
+
+def test_block_matches_scalar_loop_block():
+    x, w, mod, idx, kw = _tiny_block()
+    got = O.block_forward(x, w, mod, mod_idx=idx, **kw)["y"]
+    ref = _naive_block(x, w, mod, idx, **kw)
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+    assert np.all(got[kw["valid_len"]:] == 0)
+
+
+def _tiny_inputs():
+    s = I.TINY
+    w = {k: O.bf16_to_f64(v) for k, v in I.block_weights(s).items()}
+    x = O.bf16_to_f64(I.activations(s))
+    mod = I.mod_table(s).astype(np.float64)
+    kw = dict(heads=s.heads, head_dim=s.head_dim, ffn=s.ffn, rot_dim=s.rot_dim, theta=s.theta)
+    return s, w, x, mod, kw
+
+
+def test_block_padding_suffix_does_not_leak():
+    """Valid rows of the block on (L_buf=512, V=500) equal the block run on the 500
+    valid rows alone, and do not change when the padding rows hold huge values."""
+    s, w, x, mod, kw = _tiny_inputs()
+    V = s.valid_len
+    full = O.block_forward(x, w, mod, valid_len=V, **kw)
+    alone = O.block_forward(x[:V], w, mod, valid_len=V, **kw)
+    for name in ("y", "o", "x1", "g"):
+        np.testing.assert_allclose(full[name][:V], alone[name], rtol=1e-12, atol=1e-12)
+        assert np.all(full[name][V:] == 0)
+    x2 = x.copy()
+    x2[V:] = 1e30
+    pad = O.block_forward(x2, w, mod, valid_len=V, **kw)
+    np.testing.assert_array_equal(pad["y"], full["y"])
+
+
+def test_block_gate_zero_and_grouped_dense_equivalence():
+    s, w, x, mod, kw = _tiny_inputs()
+    V = s.valid_len
+    m0 = mod.copy()
+    m0[:, 2] = 0.0
+    m0[:, 5] = 0.0
+    r = O.block_forward(x, w, m0, valid_len=V, **kw)
+    np.testing.assert_array_equal(r["y"][:V], x[:V])
+    # one group covering every valid row with the block's own keys == dense attention
+    dense = O.block_forward(x, w, mod, valid_len=V, **kw)
+    grouped = O.block_forward(x, w, mod, valid_len=V, groups=[(0, V, [("self", 0, V)])], **kw)
+    np.testing.assert_allclose(grouped["y"], dense["y"], rtol=1e-13, atol=1e-13)
+
+
+def test_bf16_points_mode_stays_close():
+    s, w, x, mod, kw = _tiny_inputs()
+    V = s.valid_len
+    ex = O.block_forward(x, w, mod, valid_len=V, **kw)
+    rb = O.block_forward(x, w, mod, valid_len=V, bf16_points=True, **kw)
+    for name in ("y", "o", "g"):
+        a, b = ex[name][:V], rb[name][:V]
+        assert np.linalg.norm(a - b) / np.linalg.norm(a) < 1e-2
+
+
+def test_pages_constants(golden_dir):
+    c = _load(golden_dir, "pages_constants.json")
+    s = I.FULL_58816
+    assert s.hidden == c["hidden"]["value"] and s.head_dim == c["head_dim"]["value"]
+    assert s.heads * s.head_dim == s.hidden
+    assert s.valid_len == c["valid_tokens"]["value"] and s.L_buf == c["aligned_buffer"]["value"]
+    # the aligned buffer is the valid length rounded up to a multiple of 64
+    assert -(-s.valid_len // 64) * 64 == s.L_buf
+    assert sum(n for _, n in s.segments) == s.L_buf
+    for ms, fps in c["chunk_ms_to_fps"]["pairs"]:
+        assert abs(c["chunk_frames"]["value"] / (ms / 1000.0) - fps) < 0.006
