@@ -1,0 +1,315 @@
+/*
+ * h3block.h - C ABI of the MI355X (gfx950) forward pass of one MiniMax-H3 DiT
+ * block over one long packed token sequence.
+ *
+ * Sources (cited by page title and section):
+ *  [Sol-H3]   "Sol-H3: Recursive Self-Improvement for MiniMax-H3 Inference
+ *             Acceleration on Sol-Engine across Cloud and Edge"
+ *  [vLLM-H3]  "MiniMax H3 on vLLM-Omni: integrating FastVideo FastH3" (blog)
+ *  [vflash]   vflash architecture notes, "choosing a memory strategy"
+ *  [SolarWM]  "SolarWM H3 Realtime Interaction"
+ *
+ * Conventions shared by every entry point
+ *  - BF16 tensors are passed as uint16_t bit patterns; FP32 as float.
+ *  - Every matrix is row-major with an explicit row stride (ld, in elements).
+ *  - Device pointers are HIP device (or managed) memory owned by the caller. The
+ *    library allocates nothing, keeps no pointer after it returns and has no
+ *    mutable state apart from a per-device cache of the architecture check.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue
+ *    work; buffers must stay alive until the stream has reached it.
+ *  - A token buffer has L_buf rows of which the first valid_len are valid; rows
+ *    [valid_len, L_buf) are the structural padding suffix ([vLLM-H3] §3.1: the
+ *    attention backend receives the valid length and drops the suffix). Every
+ *    output writes its padding rows as +0.0 and never reads padding inputs.
+ *  - Every argument is validated on the host before anything is launched, so a
+ *    call that returns an error has written nothing. H3_ERR_HIP means a HIP call
+ *    failed after launches may have begun: the caller must treat the stream and
+ *    its buffers as unusable (as [vflash] treats a failed worker's context).
+ *  - Pointers to BF16 rows must be 16-byte aligned and row strides multiples of
+ *    8 elements (128-bit loads), else H3_ERR_ALIGN.
+ *  - Element offsets are computed in 64 bits wherever a buffer can exceed 2^31
+ *    elements ([vflash]: widen large offsets before multiplying; the FFN-up
+ *    output at 58,816 x 43,008 holds 2.53e9 elements).
+ */
+#ifndef H3BLOCK_H
+#define H3BLOCK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define H3_ABI_VERSION 1
+#define H3_MAX_SEGMENTS 4   /* K/V segments per query group */
+#define H3_MAX_GROUPS 8     /* query groups per attention call */
+
+enum h3_status {
+    H3_OK = 0,
+    H3_ERR_NULL = 1,        /* a required pointer is NULL                         */
+    H3_ERR_SHAPE = 2,       /* sizes inconsistent or out of range                 */
+    H3_ERR_UNSUPPORTED = 3, /* valid request this library does not implement      */
+    H3_ERR_ALIGN = 4,       /* pointer not 16-B aligned or ld not a multiple of 8 */
+    H3_ERR_ALIAS = 5,       /* buffers overlap in a way the call does not allow   */
+    H3_ERR_WORKSPACE = 6,   /* workspace missing or too small                     */
+    H3_ERR_DEVICE = 7,      /* current device is not an MI355X-class gfx950       */
+    H3_ERR_HIP = 8          /* a HIP runtime call failed                          */
+};
+
+/* Width of one block. [Sol-H3] §3.5 gives hidden 5376; §3.2 (quantized
+ * communication: a token/head record carries 3 x 128 QKV values) gives 128
+ * channels per head, so 42 heads. */
+typedef struct {
+    int32_t hidden;       /* H = heads * head_dim                                 */
+    int32_t heads;        /* attention heads                                      */
+    int32_t head_dim;     /* channels per head; only 128 is accepted              */
+    int32_t ffn;          /* F: SwiGLU width (w_up has 2F rows: gate | up);
+                             multiple of 64                                       */
+    int32_t rot_dim;      /* channels rotated by partial RoPE, multiple of 16,
+                             0..head_dim                                          */
+    int32_t norm_type;    /* 0 = RMSNorm (the pages' choice), 1 = LayerNorm       */
+    int32_t rope_pairing; /* 0 = rotate-half pairs (i, i+rot/2); 1 = (2i, 2i+1)   */
+    int32_t reserved;     /* must be 0                                            */
+    float rope_theta;     /* RoPE base; omega_i = theta^(-2i/rot_dim)             */
+    float eps;            /* epsilon of every norm                                */
+} h3_dims;
+
+/* Weights of one block, BF16, row-major [out, in]. Biases may be NULL.
+ * w_qkv rows are q | k | v, each head-major (packed QKV, [Sol-H3] §3.2);
+ * w_up rows are gate | up ([Sol-H3] §3.5 group (3): SwiGLU splitting). */
+typedef struct {
+    const uint16_t *w_qkv;  /* [3H, H] */
+    const uint16_t *b_qkv;  /* [3H] or NULL */
+    const uint16_t *q_gain; /* [head_dim], QK-norm gain shared by all heads */
+    const uint16_t *k_gain; /* [head_dim] */
+    const uint16_t *w_o;    /* [H, H] */
+    const uint16_t *b_o;    /* [H] or NULL */
+    const uint16_t *w_up;   /* [2F, H] */
+    const uint16_t *b_up;   /* [2F] or NULL */
+    const uint16_t *w_down; /* [H, F] */
+    const uint16_t *b_down; /* [H] or NULL */
+} h3_block_weights;
+
+/* One K/V segment a query group attends over ([SolarWM] stages 2-3: video
+ * queries read a pre-concatenated history K/V followed by the current chunk).
+ * k == NULL selects rows [begin, begin+len) of the call's own K/V; otherwise
+ * rows [begin, begin+len) of k and v, each [rows, heads*head_dim] with row
+ * stride ld. Attention is non-causal; a group's keys are the concatenation of
+ * its segments in order. */
+typedef struct {
+    const uint16_t *k;
+    const uint16_t *v;
+    int64_t ld;
+    int64_t begin;
+    int64_t len;
+} h3_kv_seg;
+
+/* A query group: rows [q_begin, q_end) attend over n_seg segments. Groups must
+ * be disjoint and lie inside [0, valid_len); valid rows outside every group are
+ * written as zero. */
+typedef struct {
+    int64_t q_begin;
+    int64_t q_end;
+    int32_t n_seg;
+    int32_t reserved;  /* must be 0 */
+    h3_kv_seg seg[H3_MAX_SEGMENTS];
+} h3_qgroup;
+
+/* K/V refresh: copy the block's normalised, rotated K and its V for rows
+ * [src_begin, src_begin+len) into k and v (row stride ld), so the next chunk's
+ * forwards can read them as a history segment ([SolarWM] stage 3/4: the KV
+ * refresh forward prepares the history for the following chunk). */
+typedef struct {
+    uint16_t *k;
+    uint16_t *v;
+    int64_t ld;
+    int64_t src_begin;
+    int64_t len;
+} h3_kv_export;
+
+/* ---------------------------------------------------------------------------
+ * h3_block_forward - one DiT block ([Sol-H3] §3.5, its three operator groups
+ * around the projections; [vLLM-H3] §3.1-3.2):
+ *   h   = RMSNorm(x) * (1 + scale_a) + shift_a            group (1)
+ *   qkv = h W_qkv^T (+ b_qkv)                              packed QKV
+ *   q~, k~ = RoPE(RMSNorm_head(q) * q_gain), same for k    group (2)
+ *   o   = softmax(q~ k~^T / sqrt(128)) v  per head, keys [0, valid_len) or per
+ *         query group
+ *   x1  = x + gate_a * (o W_o^T (+ b_o))                   group (1) residual
+ *   h2  = RMSNorm(x1) * (1 + scale_f) + shift_f            group (1)
+ *   g   = silu(u_gate) * u_up,  u = h2 W_up^T (+ b_up)     group (3)
+ *   y   = x1 + gate_f * (g W_down^T (+ b_down));  y = 0 on padding rows
+ * BF16 storage with FP32 arithmetic, FP32 modulation.
+ *
+ * x, y     [L_buf, hidden], ld = hidden. y == x is allowed (in place); any
+ *          other overlap of y with x, the weights or the workspace is rejected.
+ * mod      FP32 table [n_mod_groups, 6, hidden], rows per entry in the order
+ *          shift_a, scale_a, gate_a, shift_f, scale_f, gate_f.
+ * mod_idx  [L_buf] int32 table entry per row ("indexed" modulation), or NULL
+ *          (entry 0 for every row). Indices are clamped into [0, n_mod_groups).
+ * pos      [L_buf] int32 RoPE position per row, or NULL (position = row index);
+ *          rows with a negative position are not rotated.
+ * groups   NULL: dense attention of every valid row over keys [0, valid_len).
+ *          Otherwise n_groups (1..H3_MAX_GROUPS) query groups.
+ * kv_export NULL or one refresh copy (see h3_kv_export).
+ * workspace device memory of at least h3_block_workspace_bytes(dims, L_buf)
+ *          bytes, 256-byte aligned. After the call it holds the block's
+ *          intermediates at the offsets h3_block_workspace_layout reports.
+ * ------------------------------------------------------------------------- */
+int h3_block_forward(const h3_dims *dims, const h3_block_weights *w,
+                     const uint16_t *x, uint16_t *y,
+                     const float *mod, int32_t n_mod_groups, const int32_t *mod_idx,
+                     const int32_t *pos, int64_t L_buf, int64_t valid_len,
+                     const h3_qgroup *groups, int32_t n_groups,
+                     const h3_kv_export *kv_export,
+                     void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace size of h3_block_forward for L_buf rows (bytes). Returns 0 on
+ * invalid dims. */
+size_t h3_block_workspace_bytes(const h3_dims *dims, int64_t L_buf);
+
+/* Intermediates h3_block_forward leaves in its workspace, as byte offsets and
+ * row strides (elements). All are BF16 [L_buf, cols] with padding rows zero:
+ *   H3_WS_H   h   (cols H)      H3_WS_QKV qkv (cols 3H; q~ | k~ | v after
+ *   H3_WS_O   o   (cols H)                  QK-norm and RoPE)
+ *   H3_WS_X1  x1  (cols H)      H3_WS_H2  h2  (cols H)
+ *   H3_WS_G   g   (cols F)                                                  */
+enum { H3_WS_H = 0, H3_WS_QKV = 1, H3_WS_O = 2, H3_WS_X1 = 3, H3_WS_H2 = 4, H3_WS_G = 5,
+       H3_WS_COUNT = 6 };
+int h3_block_workspace_layout(const h3_dims *dims, int64_t L_buf,
+                              int64_t offsets[H3_WS_COUNT], int64_t lds[H3_WS_COUNT]);
+
+/* ---------------------------------------------------------------------------
+ * h3_attention - exact multi-head attention over a packed sequence
+ * ([Sol-H3] §3.2 dense SDPA attention over the packed QKV, flat
+ * (total, heads, head_dim) layout; [vLLM-H3] §3.1 valid length; [SolarWM]
+ * stage 2 grouped queries):
+ *   o[r, h] = sum_t softmax_t(q[r,h] . k[t,h] * scale) v[t,h]
+ * q, k, v  [L_buf, heads*head_dim] BF16 at row strides ld_q, ld_k, ld_v (they
+ *          may be column blocks of one packed qkv buffer).
+ * o        [L_buf, heads*head_dim] BF16 at ld_o; must not overlap q, k or v.
+ * softmax_scale 0 selects 1/sqrt(head_dim).
+ * groups   NULL: every row in [0, valid_len) attends over keys [0, valid_len).
+ * FP32 scores, softmax and accumulation; P is rounded to BF16 for the P.V
+ * product. Padding rows and valid rows outside every group are written 0.
+ * ------------------------------------------------------------------------- */
+int h3_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k,
+                 const uint16_t *v, int64_t ld_v, uint16_t *o, int64_t ld_o,
+                 int64_t L_buf, int64_t valid_len, int32_t heads, int32_t head_dim,
+                 float softmax_scale, const h3_qgroup *groups, int32_t n_groups,
+                 void *stream);
+
+/* ---------------------------------------------------------------------------
+ * h3_fused_modulate_norm - operator group (1) of [Sol-H3] §3.5 (residual
+ * addition with indexed gating, RMSNorm, indexed scale/shift modulation), the
+ * merged FP32 modulation + norm + residual of [vLLM-H3] §3.2:
+ *   if branch: x1 = bf16(x + gate[i] * branch), written to x1_out; z = x1
+ *   else:      z = x
+ *   h = bf16(norm(z) * (1 + scale[i]) + shift[i]),  i = mod_idx[r] or 0
+ * x, branch, x1_out, h_out: [L_buf, hidden] BF16 at their ld. x1_out may equal
+ * x (in place); h_out must not overlap the inputs.
+ * shift, scale, gate: FP32 [G][hidden] with ld_mod_group floats between table
+ * entries (6*hidden for the block's [G, 6, hidden] table). gate may be NULL
+ * when branch is NULL. Indices are clamped into [0, n_mod_groups).
+ * norm_type 0 = RMSNorm z / sqrt(mean z^2 + eps); 1 = LayerNorm with the
+ * population variance. hidden <= 16384, multiple of 8.
+ * ------------------------------------------------------------------------- */
+int h3_fused_modulate_norm(const uint16_t *x, int64_t ld_x,
+                           const uint16_t *branch, int64_t ld_b,
+                           const float *shift, const float *scale, const float *gate,
+                           int64_t ld_mod_group, int32_t n_mod_groups, const int32_t *mod_idx,
+                           uint16_t *x1_out, int64_t ld_x1, uint16_t *h_out, int64_t ld_h,
+                           int64_t L_buf, int64_t valid_len, int32_t hidden, float eps,
+                           int32_t norm_type, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * h3_qk_norm_rope - operator group (2) of [Sol-H3] §3.5 (QK normalization with
+ * partial RoPE), the fused Q/K RMSNorm + RoPE of [vLLM-H3] §3.2, in place:
+ *   per row r and head j: t = RMSNorm(t[r, j*128 : j*128+128]) * gain
+ *   then rotate the first rot_dim channels by phi_i = pos[r] * theta^(-2i/rot)
+ *   (pairing 0: channels (i, i + rot/2); pairing 1: (2i, 2i+1)):
+ *   (a, b) -> (a cos phi - b sin phi, a sin phi + b cos phi)
+ * q, k     [L_buf, heads*128] BF16 at row stride ld (3*hidden when they are
+ *          the column blocks of a packed qkv buffer). Padding rows are zeroed.
+ * pos      [L_buf] int32 or NULL (= row index); negative: no rotation.
+ * The angle and its sine/cosine are computed in FP64 and rounded to FP32, so
+ * rows at positions near 6e4 keep full accuracy.
+ * ------------------------------------------------------------------------- */
+int h3_qk_norm_rope(uint16_t *q, uint16_t *k, int64_t ld,
+                    const uint16_t *q_gain, const uint16_t *k_gain, const int32_t *pos,
+                    int64_t L_buf, int64_t valid_len, int32_t heads, int32_t head_dim,
+                    int32_t rot_dim, int32_t pairing, float theta, float eps, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * h3_swiglu - operator group (3) of [Sol-H3] §3.5 (SwiGLU splitting, SiLU,
+ * multiplication), the fused SwiGLU of [vLLM-H3] §3.2:
+ *   g[r, j] = bf16(silu(u[r, j]) * u[r, ffn + j]),  silu(z) = z / (1 + e^-z)
+ * u [L_buf, 2*ffn] BF16 at ld_u; g [L_buf, ffn] BF16 at ld_g, not overlapping u.
+ * ------------------------------------------------------------------------- */
+int h3_swiglu(const uint16_t *u, int64_t ld_u, uint16_t *g, int64_t ld_g,
+              int64_t L_buf, int64_t valid_len, int32_t ffn, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * h3_linear - the block's projections as one BF16 MFMA GEMM with FP32
+ * accumulation, c = a W^T (+ bias), W stored [N, K] ([Sol-H3] §3.2 packed QKV
+ * projection; §3.5 group (1) gated residual and group (3) SwiGLU as epilogues):
+ *   H3_EPI_STORE    c[r, n] = bf16(acc + bias[n])                (N columns)
+ *   H3_EPI_RESIDUAL c[r, n] = bf16(resid[r, n] + gate[i][n] * (acc + bias[n]))
+ *   H3_EPI_SWIGLU   W has N = 2F rows (gate | up); c has F columns:
+ *                   c[r, j] = bf16(silu(acc_j + b_j) * (acc_{F+j} + b_{F+j}))
+ * a [M_buf, K] at lda; rows [M_valid, M_buf) of c are written 0.
+ * resid: [M_buf, N] at ld_r (H3_EPI_RESIDUAL; may equal c for in place).
+ * gate: FP32 [G][N] with ld_gate_group floats between entries; i = mod_idx[r]
+ * or 0, clamped into [0, n_mod_groups).
+ * K must be a multiple of 64 (else H3_ERR_UNSUPPORTED); N a multiple of 8
+ * (SwiGLU: N a multiple of 16). gate's ld_gate_group must be a multiple of 4.
+ * ------------------------------------------------------------------------- */
+enum { H3_EPI_STORE = 0, H3_EPI_RESIDUAL = 1, H3_EPI_SWIGLU = 2 };
+int h3_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ldw,
+              const uint16_t *bias, uint16_t *c, int64_t ldc,
+              int64_t M_buf, int64_t M_valid, int64_t N, int64_t K, int32_t epilogue,
+              const uint16_t *resid, int64_t ld_r, const float *gate, int64_t ld_gate_group,
+              int32_t n_mod_groups, const int32_t *mod_idx, void *stream);
+
+/* Host-only validators: the same checks each entry point runs before it
+ * launches anything, callable without a GPU. They return an h3_status. */
+int h3_check_block_forward(const h3_dims *dims, const h3_block_weights *w,
+                           const uint16_t *x, uint16_t *y,
+                           const float *mod, int32_t n_mod_groups, const int32_t *mod_idx,
+                           const int32_t *pos, int64_t L_buf, int64_t valid_len,
+                           const h3_qgroup *groups, int32_t n_groups,
+                           const h3_kv_export *kv_export,
+                           const void *workspace, size_t ws_bytes);
+int h3_check_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k,
+                       const uint16_t *v, int64_t ld_v, const uint16_t *o, int64_t ld_o,
+                       int64_t L_buf, int64_t valid_len, int32_t heads, int32_t head_dim,
+                       float softmax_scale, const h3_qgroup *groups, int32_t n_groups);
+int h3_check_fused_modulate_norm(const uint16_t *x, int64_t ld_x,
+                                 const uint16_t *branch, int64_t ld_b,
+                                 const float *shift, const float *scale, const float *gate,
+                                 int64_t ld_mod_group, int32_t n_mod_groups,
+                                 const uint16_t *x1_out, int64_t ld_x1,
+                                 const uint16_t *h_out, int64_t ld_h,
+                                 int64_t L_buf, int64_t valid_len, int32_t hidden, float eps,
+                                 int32_t norm_type);
+int h3_check_qk_norm_rope(const uint16_t *q, const uint16_t *k, int64_t ld,
+                          const uint16_t *q_gain, const uint16_t *k_gain,
+                          int64_t L_buf, int64_t valid_len, int32_t heads, int32_t head_dim,
+                          int32_t rot_dim, int32_t pairing, float theta, float eps);
+int h3_check_swiglu(const uint16_t *u, int64_t ld_u, const uint16_t *g, int64_t ld_g,
+                    int64_t L_buf, int64_t valid_len, int32_t ffn);
+int h3_check_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ldw,
+                    const uint16_t *c, int64_t ldc, int64_t M_buf, int64_t M_valid,
+                    int64_t N, int64_t K, int32_t epilogue, const uint16_t *resid,
+                    int64_t ld_r, const float *gate, int32_t n_mod_groups);
+
+/* Human-readable name of a status code (static string). */
+const char *h3_status_string(int status);
+/* H3_ABI_VERSION of the built library. */
+int h3_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* H3BLOCK_H */

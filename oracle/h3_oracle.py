@@ -361,3 +361,43 @@ def block_forward(x, w, mod, *, heads: int, head_dim: int, ffn: int, valid_len: 
 
     return {k_: pad(t_) for k_, t_ in dict(h=h, qkv=qkv, q=qn, k=kn, v=v, o=o, a=a,
                                             x1=x1, h2=h2, u=u, g=g, f=f, y=y).items()}
+
+
+def block_forward_rows(x, w, mod, rows, *, heads: int, head_dim: int, ffn: int, valid_len: int,
+                       rot_dim: int = 64, theta: float = 10000.0, eps: float = 1e-6, norm_type: int = 0,
+                       pairing: int = 0, mod_idx=None, pos=None, scale=None, q_chunk: int = 64):
+    """block_forward restricted to the selected valid rows (dense attention).
+
+    Attention reads the keys and values of every valid row, so h, k~ and v are
+    formed for all valid rows; every other step (q~, attention, the output
+    projection, the FFN and the residuals) runs on the selected rows only. The
+    definitions are those of block_forward, step for step. Returns a dict of
+    [len(rows), .] arrays."""
+    x = np.asarray(x, dtype=F64)
+    H = x.shape[1]
+    V = int(valid_len)
+    rows = np.asarray(rows, dtype=np.int64)
+    m_all = gather_mod(mod, mod_idx, V)
+    posv = np.arange(V, dtype=F64) if pos is None else np.asarray(pos[:V], dtype=F64)
+
+    h_all = modulate_norm(x[:V], m_all[:, SHIFT_A], m_all[:, SCALE_A], eps, norm_type)
+    w_qkv = np.asarray(w['w_qkv'], dtype=F64)
+    b_qkv = w.get('b_qkv')
+    b = (lambda i: None) if b_qkv is None else (lambda i: np.asarray(b_qkv, dtype=F64)[i * H:(i + 1) * H])
+    k_all = linear(h_all, w_qkv[H:2 * H], b(1))
+    v_all = linear(h_all, w_qkv[2 * H:3 * H], b(2))
+    kn = qk_norm_rope(k_all, posv, heads, head_dim, w['k_gain'], eps, rot_dim, theta, pairing)
+
+    m = m_all[rows]
+    h = h_all[rows]
+    q = linear(h, w_qkv[:H], b(0))
+    qn = qk_norm_rope(q, posv[rows], heads, head_dim, w['q_gain'], eps, rot_dim, theta, pairing)
+    o = attention(qn, kn, v_all, heads, head_dim, scale, q_chunk)
+    a = linear(o, w['w_o'], w.get('b_o'))
+    x1 = gated_residual(x[rows], m[:, GATE_A], a)
+    h2 = modulate_norm(x1, m[:, SHIFT_F], m[:, SCALE_F], eps, norm_type)
+    u = linear(h2, w['w_up'], w.get('b_up'))
+    g = swiglu(u, ffn)
+    f = linear(g, w['w_down'], w.get('b_down'))
+    y = gated_residual(x1, m[:, GATE_F], f)
+    return dict(h=h, q=qn, k=kn[rows], v=v_all[rows], o=o, a=a, x1=x1, h2=h2, g=g, f=f, y=y)

@@ -1,0 +1,213 @@
+"""Host-side checks of the C-ABI library, runnable without a GPU.
+
+* The shared library loads and exports every function include/h3block.h declares.
+* The host validators reject malformed calls before anything could launch
+  (fail-closed: a rejected call writes nothing).
+* Workspace size and layout arithmetic.
+No compute entry point is called here.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from video_diffusion_transformer_dit_amd import h3
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "h3block.h")
+
+A = 1 << 20          # fake, 256-byte aligned "device" addresses: never dereferenced
+MB = 1 << 20
+
+
+def addr(i):
+    return A + i * 64 * MB
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(h3_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "h3_block_forward" in names and "h3_attention" in names and len(names) >= 16
+    for n in names:
+        assert hasattr(h3.LIB, n), f"{n} declared in h3block.h but not exported"
+    assert set(names) == set(h3.EXPORTS)
+
+
+def test_abi_version_and_status_strings():
+    assert h3.LIB.h3_abi_version() == 1
+    assert h3.status_string(h3.H3_ERR_ALIGN).startswith("H3_ERR_ALIGN")
+    assert "unknown" in h3.status_string(99)
+
+
+FULL = h3.make_dims(5376, 42, 21504)
+TINY = h3.make_dims(256, 2, 1024)
+
+
+def test_workspace_layout_is_disjoint_and_aligned():
+    for d, L in ((TINY, 512), (FULL, 58816), (FULL, 5424)):
+        off, lds = h3.workspace_layout(d, L)
+        total = h3.workspace_bytes(d, L)
+        cols = [d.hidden, 3 * d.hidden, d.hidden, d.hidden, d.hidden, d.ffn]
+        assert lds == cols
+        ends = [o + L * c * 2 for o, c in zip(off, cols)]
+        for i in range(6):
+            assert off[i] % 256 == 0
+            if i:
+                assert off[i] >= ends[i - 1]
+        assert total >= ends[-1]
+    # the full-size workspace (qkv alone is 1.9 GB) is far below 288 GB of HBM
+    assert h3.workspace_bytes(FULL, 58816) < 8 * (1 << 30)
+
+
+def test_dims_validation():
+    bad = [h3.make_dims(5376, 42, 21504, head_dim=64),       # head_dim != 128
+           h3.make_dims(5376, 41, 21504),                    # hidden != heads * 128
+           h3.make_dims(5376, 42, 21500),                    # ffn not a multiple of 64
+           h3.make_dims(5376, 42, 21504, rot_dim=24),        # rot_dim not a multiple of 16
+           h3.make_dims(5376, 42, 21504, norm_type=2),
+           h3.make_dims(5376, 42, 21504, rope_pairing=3),
+           h3.make_dims(5376, 42, 21504, eps=-1.0)]
+    for d in bad:
+        assert h3.workspace_bytes(d, 100) == 0
+
+
+def _block_args(d=TINY, L=512, V=500, ws=None, x=None, y=None, groups=None, n_groups=0, exp=None, mod=None):
+    H, F = d.hidden, d.ffn
+    w = h3.BlockWeights(addr(1), None, addr(2), addr(2) + 4096, addr(3), None, addr(4), None, addr(5), None)
+    x = addr(6) if x is None else x
+    y = addr(7) if y is None else y
+    mod = addr(8) if mod is None else mod
+    ws_ptr = addr(10) if ws is None else ws
+    return (C.byref(d), C.byref(w), x, y, mod, 1, None, None, L, V, groups, n_groups, exp, ws_ptr,
+            h3.workspace_bytes(d, L))
+
+
+def check_block(*args):
+    return h3.LIB.h3_check_block_forward(*args)
+
+
+def test_block_validator_accepts_good_call_and_rejects_bad():
+    assert check_block(*_block_args()) == h3.H3_OK
+    assert check_block(*_block_args(L=0, V=0)) == h3.H3_OK            # empty input: nothing to do
+    a = list(_block_args())
+    a[9] = 513                                                          # valid_len > L_buf
+    assert check_block(*a) == h3.H3_ERR_SHAPE
+    a = list(_block_args())
+    a[2] = None                                                         # x missing
+    assert check_block(*a) == h3.H3_ERR_NULL
+    a = list(_block_args())
+    a[2] = addr(6) + 2                                                  # x misaligned
+    assert check_block(*a) == h3.H3_ERR_ALIGN
+    a = list(_block_args())
+    a[14] -= 1                                                          # workspace too small
+    assert check_block(*a) == h3.H3_ERR_WORKSPACE
+    a = list(_block_args())
+    a[13] = None
+    assert check_block(*a) == h3.H3_ERR_WORKSPACE
+    # y overlapping x partially is rejected; y == x (in place) is allowed
+    assert check_block(*_block_args(y=addr(6) + 512)) == h3.H3_ERR_ALIAS
+    assert check_block(*_block_args(y=addr(6))) == h3.H3_OK
+    # y inside the workspace
+    assert check_block(*_block_args(y=addr(10) + 4096)) == h3.H3_ERR_ALIAS
+    # unsupported dims
+    d = h3.make_dims(128, 2, 1024, head_dim=64)        # consistent, but head_dim != 128
+    assert check_block(*_block_args(d=d)) == h3.H3_ERR_UNSUPPORTED
+
+
+def test_block_validator_groups():
+    V = 500
+    g, n = h3.make_groups([(0, 100, [("self", 0, V)]), (100, V, [("self", 0, 300)])])
+    assert check_block(*_block_args(groups=g, n_groups=n)) == h3.H3_OK
+    g, n = h3.make_groups([(0, 100, [("self", 0, V)]), (50, V, [("self", 0, V)])])     # overlapping groups
+    assert check_block(*_block_args(groups=g, n_groups=n)) == h3.H3_ERR_SHAPE
+    g, n = h3.make_groups([(0, 600, [("self", 0, V)])])                                 # beyond valid_len
+    assert check_block(*_block_args(groups=g, n_groups=n)) == h3.H3_ERR_SHAPE
+    g, n = h3.make_groups([(0, 100, [("self", 0, 501)])])                               # own keys beyond V
+    assert check_block(*_block_args(groups=g, n_groups=n)) == h3.H3_ERR_SHAPE
+    g, n = h3.make_groups([(0, 100, [])])                                               # no segment
+    assert check_block(*_block_args(groups=g, n_groups=n)) == h3.H3_ERR_UNSUPPORTED
+    arr = (h3.QGroup * 1)()
+    arr[0].q_begin, arr[0].q_end, arr[0].n_seg = 0, 10, 5                              # too many segments
+    assert check_block(*_block_args(groups=arr, n_groups=1)) == h3.H3_ERR_UNSUPPORTED
+    # external history segment inside the workspace is rejected
+    arr = (h3.QGroup * 1)()
+    arr[0].q_begin, arr[0].q_end, arr[0].n_seg = 0, 10, 1
+    arr[0].seg[0] = h3.KvSeg(addr(10), addr(10) + 1 * MB, 256, 0, 100)
+    assert check_block(*_block_args(groups=arr, n_groups=1)) == h3.H3_ERR_ALIAS
+    arr[0].seg[0] = h3.KvSeg(addr(20), addr(21), 256, 0, 100)
+    assert check_block(*_block_args(groups=arr, n_groups=1)) == h3.H3_OK
+    # KV export range and aliasing
+    e = h3.KvExport(addr(22), addr(23), 256, 400, 100)
+    assert check_block(*_block_args(exp=C.byref(e))) == h3.H3_OK
+    e = h3.KvExport(addr(22), addr(23), 256, 450, 100)
+    assert check_block(*_block_args(exp=C.byref(e))) == h3.H3_ERR_SHAPE
+    e = h3.KvExport(addr(22), addr(22) + 1024, 256, 0, 100)
+    assert check_block(*_block_args(exp=C.byref(e))) == h3.H3_ERR_ALIAS
+
+
+def test_attention_validator():
+    L, H = 512, 256
+    base = addr(1)
+    q, k, v = base, base + 2 * H, base + 4 * H        # column blocks of one packed qkv (ld 3H)
+    o = addr(2)
+    ok = h3.LIB.h3_check_attention(q, 3 * H, k, 3 * H, v, 3 * H, o, H, L, 500, 2, 128, 0.0, None, 0)
+    assert ok == h3.H3_OK
+    # o overlapping the packed qkv
+    assert h3.LIB.h3_check_attention(q, 3 * H, k, 3 * H, v, 3 * H, base + 6 * H, H, L, 500, 2, 128, 0.0, None,
+                                     0) == h3.H3_ERR_ALIAS
+    assert h3.LIB.h3_check_attention(q, 3 * H, k, 3 * H, v, 3 * H, o, H, L, 500, 2, 64, 0.0, None,
+                                     0) == h3.H3_ERR_UNSUPPORTED
+    assert h3.LIB.h3_check_attention(q, 3 * H, k, 3 * H, v, 3 * H, o, H, L, 500, 2, 128, -1.0, None,
+                                     0) == h3.H3_ERR_SHAPE
+    assert h3.LIB.h3_check_attention(q, 3 * H + 4, k, 3 * H, v, 3 * H, o, H, L, 500, 2, 128, 0.0, None,
+                                     0) == h3.H3_ERR_ALIGN
+    assert h3.LIB.h3_check_attention(q, 3 * H, k, 3 * H, v, 3 * H, o, H, 0, 0, 2, 128, 0.0, None, 0) == h3.H3_OK
+
+
+def test_elementwise_and_linear_validators():
+    L, H = 64, 256
+    x, hh, sh, sc = addr(1), addr(2), addr(3), addr(3) + 4 * H
+    lib = h3.LIB
+    assert lib.h3_check_fused_modulate_norm(x, H, None, 0, sh, sc, None, 6 * H, 1, None, 0, hh, H, L, L, H, 1e-6,
+                                            0) == h3.H3_OK
+    # output aliasing the input
+    assert lib.h3_check_fused_modulate_norm(x, H, None, 0, sh, sc, None, 6 * H, 1, None, 0, x, H, L, L, H, 1e-6,
+                                            0) == h3.H3_ERR_ALIAS
+    # branch given without gate
+    assert lib.h3_check_fused_modulate_norm(x, H, addr(4), H, sh, sc, None, 6 * H, 1, addr(5), H, hh, H, L, L, H,
+                                            1e-6, 0) == h3.H3_ERR_NULL
+    # in-place x1 (== x) is allowed
+    assert lib.h3_check_fused_modulate_norm(x, H, addr(4), H, sh, sc, sc + 4 * H, 6 * H, 1, x, H, hh, H, L, L, H,
+                                            1e-6, 0) == h3.H3_OK
+    assert lib.h3_check_fused_modulate_norm(x, H, None, 0, sh, sc, None, 6 * H, 1, None, 0, hh, H, L, L, 20000,
+                                            1e-6, 0) == h3.H3_ERR_UNSUPPORTED
+    # qk-norm: q and k column blocks of one packed buffer are disjoint
+    assert lib.h3_check_qk_norm_rope(x, x + 2 * H, 3 * H, addr(6), addr(6) + 256, L, L, 2, 128, 64, 0, 1e4,
+                                     1e-6) == h3.H3_OK
+    assert lib.h3_check_qk_norm_rope(x, x + 2, 3 * H, addr(6), addr(6) + 256, L, L, 2, 128, 64, 0, 1e4,
+                                     1e-6) == h3.H3_ERR_ALIGN
+    assert lib.h3_check_qk_norm_rope(x, x + 2 * 128, 3 * H, addr(6), addr(6) + 256, L, L, 2, 128, 64, 0, 1e4,
+                                     1e-6) == h3.H3_ERR_ALIAS
+    assert lib.h3_check_qk_norm_rope(x, x + 2 * H, 3 * H, addr(6), addr(6) + 256, L, L, 2, 128, 72, 0, 1e4,
+                                     1e-6) == h3.H3_ERR_UNSUPPORTED
+    # swiglu
+    assert lib.h3_check_swiglu(x, 2048, hh, 1024, L, L, 1024) == h3.H3_OK
+    assert lib.h3_check_swiglu(x, 2048, x + 2048, 1024, L, L, 1024) == h3.H3_ERR_ALIAS
+    # linear
+    assert lib.h3_check_linear(x, 256, addr(7), 256, hh, 512, L, L, 512, 256, 0, None, 0, None, 1) == h3.H3_OK
+    assert lib.h3_check_linear(x, 256, addr(7), 256, hh, 512, L, L, 512, 204, 0, None, 0, None,
+                               1) == h3.H3_ERR_ALIGN
+    assert lib.h3_check_linear(x, 256, addr(7), 256, hh, 512, L, L, 512, 264, 0, None, 0, None,
+                               1) == h3.H3_ERR_UNSUPPORTED
+    assert lib.h3_check_linear(x, 256, addr(7), 256, hh, 512, L, L, 512, 256, 1, None, 0, None,
+                               1) == h3.H3_ERR_NULL
+    assert lib.h3_check_linear(x, 256, addr(7), 256, x, 512, L, L, 512, 256, 0, None, 0, None,
+                               1) == h3.H3_ERR_ALIAS
+    assert lib.h3_check_linear(x, 256, addr(7), 256, hh, 512, L, L, 512, 256, 3, None, 0, None,
+                               1) == h3.H3_ERR_UNSUPPORTED

@@ -1,0 +1,247 @@
+"""Parity of each C-ABI entry point against the FP64 oracle on the same seeded
+inputs, at sizes spanning several tiles with ragged tails, plus edge cases.
+All calls go through the C ABI (ctypes binding)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import h3_oracle as O
+from video_diffusion_transformer_dit_amd import h3
+from video_diffusion_transformer_dit_amd import inputs as I
+
+from util import (BF16_SLACK, assert_parity, assert_zero_rows, bits, dev_bf16, dev_f32, dev_i32, f64, poison)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# group (1): modulate-norm
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("H,L,V", [(256, 512, 500), (5376, 130, 117), (1024, 1, 1), (512, 64, 0)])
+@pytest.mark.parametrize("norm_type", [0, 1])
+@pytest.mark.parametrize("with_branch", [False, True])
+def test_modnorm(H, L, V, norm_type, with_branch):
+    _say(f"modnorm H={H} L={L} V={V} norm={norm_type} branch={with_branch}")
+    G = 3
+    xb = I.normal_bf16("mn.x", (L, H))
+    bb = I.normal_bf16("mn.b", (L, H))
+    mod = I.normal_f32("mn.mod", (G, 6, H), 0.1)
+    idx = I.rng_for("mn.idx").integers(0, G, size=L).astype(np.int32)
+    x, br, md, ix = dev_bf16(xb), dev_bf16(bb), dev_f32(mod), dev_i32(idx)
+    h_out = poison((L, H))
+    x1_out = poison((L, H)) if with_branch else None
+    h3.fused_modulate_norm(x, md[:, 0], md[:, 1], h_out, V, eps=1e-6, norm_type=norm_type,
+                           branch=br if with_branch else None, gate=md[:, 2] if with_branch else None,
+                           x1_out=x1_out, ld_mod_group=6 * H, n_mod_groups=G, mod_idx=ix)
+    torch.cuda.synchronize()
+    m = O.gather_mod(mod.astype(np.float64), idx, V)
+    z = O.bf16_to_f64(xb[:V])
+    if with_branch:
+        z = O.gated_residual(z, m[:, O.GATE_A], O.bf16_to_f64(bb[:V]))
+        if V:
+            assert_parity(f64(x1_out)[:V], z, "x1")
+        assert_zero_rows(x1_out, V, "x1")
+    ref = O.modulate_norm(z, m[:, O.SHIFT_A], m[:, O.SCALE_A], 1e-6, norm_type)
+    if V:
+        assert_parity(f64(h_out)[:V], ref, "h")
+    assert_zero_rows(h_out, V, "h")
+
+
+def test_modnorm_gate_zero_is_bit_exact_and_inplace():
+    H, L = 5376, 64
+    _say("modnorm gate=0 in place")
+    xb = I.normal_bf16("mz.x", (L, H))
+    bb = I.normal_bf16("mz.b", (L, H), 100.0)
+    mod = I.normal_f32("mz.mod", (1, 6, H), 0.1)
+    mod[:, 2] = 0.0
+    x, md = dev_bf16(xb), dev_f32(mod)
+    h_out = poison((L, H))
+    h3.fused_modulate_norm(x, md[:, 0], md[:, 1], h_out, L, branch=dev_bf16(bb), gate=md[:, 2], x1_out=x,
+                           ld_mod_group=6 * H)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(x), xb)
+
+
+# ---------------------------------------------------------------------------
+# group (2): QK RMSNorm + partial RoPE, in place on a packed qkv buffer
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("heads,L,V", [(2, 512, 500), (42, 70, 67)])
+@pytest.mark.parametrize("rot_dim,pairing", [(64, 0), (64, 1), (128, 0), (0, 0), (32, 0)])
+@pytest.mark.parametrize("pos_kind", ["row", "explicit"])
+def test_qk_norm_rope(heads, L, V, rot_dim, pairing, pos_kind):
+    _say(f"qk_norm_rope heads={heads} L={L} V={V} rot={rot_dim} pairing={pairing} pos={pos_kind}")
+    H = heads * 128
+    qkv_b = I.normal_bf16("qk.qkv", (L, 3 * H), 3.0)
+    gq = I.normal_bf16("qk.gq", (128,), 0.02, 1.0)
+    gk = I.normal_bf16("qk.gk", (128,), 0.02, 1.0)
+    if pos_kind == "row":
+        pos = None
+        posv = np.arange(L)
+    else:
+        posv = I.rng_for("qk.pos").integers(0, 60000, size=L).astype(np.int32)
+        posv[::7] = -1     # rows with a negative position are not rotated
+        pos = dev_i32(posv)
+    qkv = dev_bf16(qkv_b)
+    h3.qk_norm_rope(qkv[:, :H], qkv[:, H:2 * H], dev_bf16(gq), dev_bf16(gk), V, heads, rot_dim, pairing, 1e4,
+                    1e-6, pos=pos)
+    torch.cuda.synchronize()
+    got = f64(qkv)
+    src = O.bf16_to_f64(qkv_b)
+    for name, sl, g in (("q", slice(0, H), gq), ("k", slice(H, 2 * H), gk)):
+        ref = O.qk_norm_rope(src[:V, sl], posv[:V], heads, 128, O.bf16_to_f64(g), 1e-6, rot_dim, 1e4, pairing)
+        assert_parity(got[:V, sl], ref, name)
+        assert_zero_rows(qkv[:, sl], V, name)
+    # v columns untouched, bit for bit
+    np.testing.assert_array_equal(bits(qkv[:, 2 * H:]), qkv_b[:, 2 * H:])
+
+
+# ---------------------------------------------------------------------------
+# group (3): SwiGLU
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("F,L,V", [(1024, 512, 500), (21504, 20, 19), (8, 3, 3)])
+def test_swiglu(F, L, V):
+    _say(f"swiglu F={F} L={L} V={V}")
+    ub = I.normal_bf16("sw.u", (L, 2 * F), 2.0)
+    g = poison((L, F))
+    h3.swiglu(dev_bf16(ub), g, V, F)
+    torch.cuda.synchronize()
+    ref = O.swiglu(O.bf16_to_f64(ub[:V]), F)
+    assert_parity(f64(g)[:V], ref, "g", slack=BF16_SLACK)
+    assert_zero_rows(g, V, "g")
+
+
+# ---------------------------------------------------------------------------
+# projections (MFMA GEMM) with their epilogues
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,Mv,N,K", [(300, 291, 512, 256), (600, 599, 768, 5376), (64, 1, 256, 64),
+                                      (257, 257, 264, 128)])
+@pytest.mark.parametrize("bias", [False, True])
+def test_linear_store(M, Mv, N, K, bias):
+    _say(f"linear store M={M} Mv={Mv} N={N} K={K} bias={bias}")
+    ab = I.normal_bf16("ln.a", (M, K))
+    wb = I.normal_bf16("ln.w", (N, K), 0.02)
+    bb = I.normal_bf16("ln.b", (N,), 0.5)
+    c = poison((M, N))
+    h3.linear(dev_bf16(ab), dev_bf16(wb), c, Mv, h3.H3_EPI_STORE, bias=dev_bf16(bb) if bias else None)
+    torch.cuda.synchronize()
+    ref = O.linear(O.bf16_to_f64(ab[:Mv]), O.bf16_to_f64(wb), O.bf16_to_f64(bb) if bias else None)
+    assert_parity(f64(c)[:Mv], ref, "c")
+    assert_zero_rows(c, Mv, "c")
+
+
+@pytest.mark.parametrize("M,Mv,N,K,G", [(300, 291, 512, 256, 1), (520, 515, 5376, 512, 3)])
+def test_linear_gated_residual(M, Mv, N, K, G):
+    _say(f"linear residual M={M} N={N} K={K} G={G}")
+    ab = I.normal_bf16("lr.a", (M, K))
+    wb = I.normal_bf16("lr.w", (N, K), 0.05)
+    rb = I.normal_bf16("lr.r", (M, N))
+    mod = I.normal_f32("lr.mod", (G, 6, N), 0.5)
+    idx = I.rng_for("lr.idx").integers(0, G, size=M).astype(np.int32)
+    md = dev_f32(mod)
+    c = poison((M, N))
+    h3.linear(dev_bf16(ab), dev_bf16(wb), c, Mv, h3.H3_EPI_RESIDUAL, resid=dev_bf16(rb), gate=md[:, 2],
+              ld_gate_group=6 * N, n_mod_groups=G, mod_idx=dev_i32(idx) if G > 1 else None)
+    torch.cuda.synchronize()
+    m = O.gather_mod(mod.astype(np.float64), idx if G > 1 else None, Mv)
+    branch = O.linear(O.bf16_to_f64(ab[:Mv]), O.bf16_to_f64(wb))
+    ref = O.gated_residual(O.bf16_to_f64(rb[:Mv]), m[:, O.GATE_A], branch)
+    assert_parity(f64(c)[:Mv], ref, "x1")
+    # the gated branch alone (the residual dominates the sum)
+    assert_parity(f64(c)[:Mv] - O.bf16_to_f64(rb[:Mv]), ref - O.bf16_to_f64(rb[:Mv]), "gate*branch",
+                  rel_tol=3e-2, max_tol=2e-1)
+    assert_zero_rows(c, Mv, "x1")
+
+
+@pytest.mark.parametrize("M,Mv,F,K", [(300, 291, 512, 256), (260, 257, 1040, 512)])
+@pytest.mark.parametrize("bias", [False, True])
+def test_linear_swiglu(M, Mv, F, K, bias):
+    _say(f"linear swiglu M={M} F={F} K={K} bias={bias}")
+    ab = I.normal_bf16("lg.a", (M, K))
+    wb = I.normal_bf16("lg.w", (2 * F, K), 0.05)
+    bb = I.normal_bf16("lg.b", (2 * F,), 0.5)
+    g = poison((M, F))
+    h3.linear(dev_bf16(ab), dev_bf16(wb), g, Mv, h3.H3_EPI_SWIGLU, bias=dev_bf16(bb) if bias else None)
+    torch.cuda.synchronize()
+    u = O.linear(O.bf16_to_f64(ab[:Mv]), O.bf16_to_f64(wb), O.bf16_to_f64(bb) if bias else None)
+    assert_parity(f64(g)[:Mv], O.swiglu(u, F), "g", slack=BF16_SLACK)
+    assert_zero_rows(g, Mv, "g")
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+def _qkv(L, heads, tag, q_scale=1.0):
+    H = heads * 128
+    q = I.normal_bf16(f"{tag}.q", (L, H), q_scale)
+    k = I.normal_bf16(f"{tag}.k", (L, H))
+    v = I.normal_bf16(f"{tag}.v", (L, H))
+    return q, k, v
+
+
+@pytest.mark.parametrize("heads,L,V,q_scale", [(2, 512, 500, 1.0), (2, 512, 500, 8.0), (3, 700, 643, 1.0),
+                                               (1, 70, 33, 3.0)])
+@pytest.mark.parametrize("packed", [False, True])
+def test_attention_dense(heads, L, V, q_scale, packed):
+    _say(f"attention dense heads={heads} L={L} V={V} q_scale={q_scale} packed={packed}")
+    H = heads * 128
+    qb, kb, vb = _qkv(L, heads, "at", q_scale)
+    if packed:
+        qkv = dev_bf16(np.concatenate([qb, kb, vb], axis=1))
+        q, k, v = qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:]
+    else:
+        q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    o = poison((L, H))
+    h3.attention(q, k, v, o, V, heads)
+    torch.cuda.synchronize()
+    ref = O.attention(O.bf16_to_f64(qb[:V]), O.bf16_to_f64(kb[:V]), O.bf16_to_f64(vb[:V]), heads, 128)
+    assert_parity(f64(o)[:V], ref, "o")
+    assert_zero_rows(o, V, "o")
+
+
+def test_attention_single_key_is_exact():
+    """One valid key: softmax weight exactly 1, so o equals that key's value bit for bit."""
+    heads, L = 2, 64
+    H = heads * 128
+    qb, kb, vb = _qkv(L, heads, "a1", 5.0)
+    o = poison((L, H))
+    h3.attention(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), o, 1, heads)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(o[:1]), vb[:1])
+    assert_zero_rows(o, 1, "o")
+
+
+def test_attention_grouped_with_history():
+    """Query groups over [external history ; own keys] segments; rows outside
+    every group are zero (the streaming chunk's structure, scaled down)."""
+    heads, L, V, Lh = 2, 600, 590, 300
+    H = heads * 128
+    qb, kb, vb = _qkv(L, heads, "ag")
+    hk = I.normal_bf16("ag.hk", (Lh, H))
+    hv = I.normal_bf16("ag.hv", (Lh, H))
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    tk, tv = dev_bf16(hk), dev_bf16(hv)
+    groups = [(0, 64, [("self", 0, 200)]),
+              (64, 100, [("self", 0, V)]),
+              (150, 560, [(tk, tv, 20, 280), ("self", 0, V)]),
+              (570, 590, [(tk, tv, 0, 1), ("self", 10, 50), ("self", 300, 3), (tk, tv, 299, 1)])]
+    o = poison((L, H))
+    h3.attention(q, k, v, o, V, heads, groups=groups)
+    torch.cuda.synchronize()
+    Q, K, Vv = O.bf16_to_f64(qb), O.bf16_to_f64(kb), O.bf16_to_f64(vb)
+    HK, HV = O.bf16_to_f64(hk), O.bf16_to_f64(hv)
+    og = [(0, 64, [(K[:200], Vv[:200])]),
+          (64, 100, [(K[:V], Vv[:V])]),
+          (150, 560, [(HK[20:300], HV[20:300]), (K[:V], Vv[:V])]),
+          (570, 590, [(HK[0:1], HV[0:1]), (K[10:60], Vv[10:60]), (K[300:303], Vv[300:303]),
+                      (HK[299:300], HV[299:300])])]
+    ref = O.attention_grouped(Q[:V], og, heads, 128, V)
+    got = f64(o)
+    for (a, b, _) in og:
+        assert_parity(got[a:b], ref[a:b], f"o[{a}:{b}]")
+    for (a, b) in ((100, 150), (560, 570)):
+        assert np.all(bits(o[a:b]) == 0), f"rows {a}:{b} outside every group must be zero"
+    assert_zero_rows(o, V, "o")

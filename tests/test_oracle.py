@@ -451,3 +451,15 @@ def test_pages_constants(golden_dir):
     assert sum(n for _, n in s.segments) == s.L_buf
     for ms, fps in c["chunk_ms_to_fps"]["pairs"]:
         assert abs(c["chunk_frames"]["value"] / (ms / 1000.0) - fps) < 0.006
+
+
+def test_block_rows_equals_full_block_at_those_rows():
+    s, w, x, mod, kw = _tiny_inputs()
+    V = s.valid_len
+    idx = (np.arange(s.L_buf) % 3).astype(np.int32)
+    mod3 = np.concatenate([mod, mod * 0.5, -mod], axis=0)
+    full = O.block_forward(x, w, mod3, valid_len=V, mod_idx=idx, **kw)
+    rows = np.array([0, 1, 63, 64, 255, 498, 499])
+    part = O.block_forward_rows(x, w, mod3, rows, valid_len=V, mod_idx=idx, **kw)
+    for name in ("h", "q", "k", "v", "o", "x1", "h2", "g", "y"):
+        np.testing.assert_allclose(part[name], full[name][rows], rtol=1e-11, atol=1e-12)

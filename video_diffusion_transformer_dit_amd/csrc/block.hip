@@ -1,0 +1,82 @@
+// h3_block_forward: one MiniMax-H3 DiT block over a packed token sequence,
+// composed from the library's kernels on the caller's stream (Sol-H3 report,
+// §3.5 "Kernel Fusion": the three operator groups around the projections;
+// vLLM-Omni H3 blog, §3.1-3.2).
+//
+//   1 modnorm        h   = RMSNorm(x) (1 + scale_a) + shift_a           group (1)
+//   2 GEMM           qkv = h W_qkv^T (+ b)                               packed QKV
+//   3 qk-norm+RoPE   q~, k~ in place in qkv                              group (2)
+//   4 attention      o   = softmax(q~ k~^T / sqrt(128)) v
+//   5 GEMM+residual  x1  = x + gate_a (o W_o^T (+ b))                    group (1)
+//   6 modnorm        h2  = RMSNorm(x1) (1 + scale_f) + shift_f           group (1)
+//   7 GEMM+SwiGLU    g   = silu(h2 W_gate^T) * (h2 W_up^T)               group (3)
+//   8 GEMM+residual  y   = x1 + gate_f (g W_down^T (+ b))                group (1)
+//   9 KV export      (refresh forwards only) copy k~ and v rows out
+// Every kernel works on the valid rows only; padding rows of every output and
+// intermediate are written as zero.
+#include "h3_runtime.h"
+
+using namespace h3;
+
+extern "C" int h3_block_forward(const h3_dims *dims, const h3_block_weights *w, const uint16_t *x, uint16_t *y,
+                                const float *mod, int32_t n_mod_groups, const int32_t *mod_idx,
+                                const int32_t *pos, int64_t L_buf, int64_t valid_len, const h3_qgroup *groups,
+                                int32_t n_groups, const h3_kv_export *kv_export, void *workspace,
+                                size_t ws_bytes, void *stream) {
+    int s = h3_check_block_forward(dims, w, x, y, mod, n_mod_groups, mod_idx, pos, L_buf, valid_len, groups,
+                                   n_groups, kv_export, workspace, ws_bytes);
+    if (s != H3_OK || L_buf == 0) return s;
+    if ((s = device_check()) != H3_OK) return s;
+    const hipStream_t st = (hipStream_t)stream;
+
+    WsLayout l;
+    ws_layout(dims, L_buf, &l);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    uint16_t *h = reinterpret_cast<uint16_t *>(ws + l.off[H3_WS_H]);
+    uint16_t *qkv = reinterpret_cast<uint16_t *>(ws + l.off[H3_WS_QKV]);
+    uint16_t *o = reinterpret_cast<uint16_t *>(ws + l.off[H3_WS_O]);
+    uint16_t *x1 = reinterpret_cast<uint16_t *>(ws + l.off[H3_WS_X1]);
+    uint16_t *h2 = reinterpret_cast<uint16_t *>(ws + l.off[H3_WS_H2]);
+    uint16_t *g = reinterpret_cast<uint16_t *>(ws + l.off[H3_WS_G]);
+
+    const int64_t H = dims->hidden, F = dims->ffn, V = valid_len;
+    const int64_t ldm = 6 * H;  // floats between modulation-table entries
+    const float *shift_a = mod, *scale_a = mod + H, *gate_a = mod + 2 * H;
+    const float *shift_f = mod + 3 * H, *scale_f = mod + 4 * H, *gate_f = mod + 5 * H;
+
+    // 1 h
+    launch_modnorm(x, H, nullptr, 0, shift_a, scale_a, nullptr, ldm, n_mod_groups, mod_idx, nullptr, 0, h, H, L_buf,
+                   V, (int32_t)H, dims->eps, dims->norm_type, st);
+    // 2 qkv
+    launch_linear(h, H, w->w_qkv, H, w->b_qkv, qkv, 3 * H, V, 3 * H, H, H3_EPI_STORE, nullptr, 0, nullptr, 0, 1,
+                  nullptr, st);
+    launch_zero_rows(qkv, 3 * H, 3 * H, V, L_buf, st);
+    // 3 q~, k~ (also zeroes their padding rows)
+    launch_qk_norm_rope(qkv, qkv + H, 3 * H, w->q_gain, w->k_gain, pos, L_buf, V, dims->heads, dims->rot_dim,
+                        dims->rope_pairing, dims->rope_theta, dims->eps, st);
+    // 4 o
+    launch_attention(qkv, 3 * H, qkv + H, 3 * H, qkv + 2 * H, 3 * H, o, H, L_buf, V, dims->heads, 0.0f, groups,
+                     n_groups, st);
+    // 5 x1 = x + gate_a * (o W_o^T)
+    launch_linear(o, H, w->w_o, H, w->b_o, x1, H, V, H, H, H3_EPI_RESIDUAL, x, H, gate_a, ldm, n_mod_groups, mod_idx,
+                  st);
+    launch_zero_rows(x1, H, H, V, L_buf, st);
+    // 6 h2
+    launch_modnorm(x1, H, nullptr, 0, shift_f, scale_f, nullptr, ldm, n_mod_groups, mod_idx, nullptr, 0, h2, H,
+                   L_buf, V, (int32_t)H, dims->eps, dims->norm_type, st);
+    // 7 g = silu(gate) * up
+    launch_linear(h2, H, w->w_up, H, w->b_up, g, F, V, 2 * F, H, H3_EPI_SWIGLU, nullptr, 0, nullptr, 0, 1, nullptr,
+                  st);
+    launch_zero_rows(g, F, F, V, L_buf, st);
+    // 8 y = x1 + gate_f * (g W_down^T)
+    launch_linear(g, F, w->w_down, F, w->b_down, y, H, V, H, F, H3_EPI_RESIDUAL, x1, H, gate_f, ldm, n_mod_groups,
+                  mod_idx, st);
+    launch_zero_rows(y, H, H, V, L_buf, st);
+    // 9 KV refresh export
+    if (kv_export && kv_export->len > 0) {
+        const h3_kv_export &e = *kv_export;
+        launch_copy_rows(qkv + e.src_begin * 3 * H + H, 3 * H, e.k, e.ld, e.len, H, st);
+        launch_copy_rows(qkv + e.src_begin * 3 * H + 2 * H, 3 * H, e.v, e.ld, e.len, H, st);
+    }
+    return launch_status();
+}

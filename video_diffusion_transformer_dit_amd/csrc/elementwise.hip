@@ -1,0 +1,434 @@
+// HBM-bound fused elementwise kernels of the H3 DiT block for gfx950:
+//   * modulate-norm  - operator group (1) of the Sol-H3 report, §3.5 "Kernel
+//     Fusion": residual addition with indexed gating, RMSNorm and indexed
+//     scale/shift modulation (merged FP32 modulation + norm + residual in the
+//     vLLM-Omni H3 blog, §3.2);
+//   * QK-norm + RoPE - operator group (2): per-head RMSNorm and partial rotary
+//     embedding, in place on the packed QKV buffer;
+//   * SwiGLU         - operator group (3): split, SiLU, multiply.
+// All use 128-bit coalesced loads and stores of BF16 rows, FP32 arithmetic and
+// round-to-nearest-even BF16 stores. Row offsets are formed in 64 bits (the
+// vflash notes, "choosing a memory strategy": widen large offsets before the
+// multiply); in-row offsets stay 32-bit.
+#include <algorithm>
+
+#include "h3_device.h"
+#include "h3_runtime.h"
+
+namespace h3 {
+namespace {
+
+// ---------------------------------------------------------------------------
+// modulate-norm: one wavefront owns ROWS rows; lane i holds 16-byte chunks
+// i, i+64, ... of each row in registers (NCH chunks max), so x (and the
+// branch) are read once and h (and x1) written once.
+// ---------------------------------------------------------------------------
+struct ModnormArgs {
+    const uint16_t *x;
+    const uint16_t *branch;
+    const float *shift;
+    const float *scale;
+    const float *gate;
+    const int32_t *mod_idx;
+    uint16_t *x1;
+    uint16_t *h;
+    int64_t ld_x, ld_b, ld_x1, ld_h, ld_mod;
+    int64_t L_buf, valid;
+    int32_t hidden, n_groups;
+    float eps;
+};
+
+__device__ __forceinline__ void load_f8(const float *p, float f[8]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+template <int NCH, int ROWS, bool BRANCH, int NORM>
+__global__ __launch_bounds__(256) void modnorm_kernel(ModnormArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * ROWS;
+    if (r0 >= a.L_buf) return;
+    const int nch = a.hidden >> 3;
+
+    uint4 xv[ROWS][NCH];
+    int grp[ROWS];
+    bool valid[ROWS], inbuf[ROWS];
+#pragma unroll
+    for (int p = 0; p < ROWS; ++p) {
+        const int64_t r = r0 + p;
+        inbuf[p] = r < a.L_buf;
+        valid[p] = r < a.valid;
+        int g = 0;
+        if (valid[p] && a.mod_idx) g = min(max(a.mod_idx[r], 0), a.n_groups - 1);
+        grp[p] = g;
+    }
+
+    // Pass 1: load rows (forming x1 = x + gate * branch), accumulate the sum of
+    // squares (RMSNorm) or the sum (LayerNorm).
+    float acc[ROWS];
+#pragma unroll
+    for (int p = 0; p < ROWS; ++p) acc[p] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nch) {
+            float gv[8];
+            int gcur = -1;
+#pragma unroll
+            for (int p = 0; p < ROWS; ++p) {
+                if (!valid[p]) continue;
+                const int64_t r = r0 + p;
+                uint4 xw = *reinterpret_cast<const uint4 *>(a.x + r * a.ld_x + 8 * c);
+                if (BRANCH) {
+                    if (grp[p] != gcur) {
+                        load_f8(a.gate + (int64_t)grp[p] * a.ld_mod + 8 * c, gv);
+                        gcur = grp[p];
+                    }
+                    const uint4 bw = *reinterpret_cast<const uint4 *>(a.branch + r * a.ld_b + 8 * c);
+                    float xf[8], bf[8];
+                    unpack8(xw, xf);
+                    unpack8(bw, bf);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) xf[e] = xf[e] + gv[e] * bf[e];
+                    xw = pack8(xf);
+                    *reinterpret_cast<uint4 *>(a.x1 + r * a.ld_x1 + 8 * c) = xw;
+                }
+                xv[p][i] = xw;
+                float xf[8];
+                unpack8(xw, xf);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[p] += NORM == 0 ? xf[e] * xf[e] : xf[e];
+            }
+        }
+    }
+    float mean[ROWS], inv[ROWS];
+#pragma unroll
+    for (int p = 0; p < ROWS; ++p) {
+        const float s = wave_sum(acc[p]);
+        mean[p] = NORM == 0 ? 0.f : s / (float)a.hidden;
+        if (NORM == 0) inv[p] = rsqrtf(s / (float)a.hidden + a.eps);
+    }
+    if (NORM == 1) {
+        // two-pass population variance from the register copy
+#pragma unroll
+        for (int p = 0; p < ROWS; ++p) acc[p] = 0.f;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int c = lane + 64 * i;
+            if (c < nch) {
+#pragma unroll
+                for (int p = 0; p < ROWS; ++p) {
+                    if (!valid[p]) continue;
+                    float xf[8];
+                    unpack8(xv[p][i], xf);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float dlt = xf[e] - mean[p];
+                        acc[p] += dlt * dlt;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < ROWS; ++p) inv[p] = rsqrtf(wave_sum(acc[p]) / (float)a.hidden + a.eps);
+    }
+
+    // Pass 2: h = n * (1 + scale) + shift; padding rows are written as zero.
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nch) {
+            float sh[8], sc[8];
+            int gcur = -1;
+#pragma unroll
+            for (int p = 0; p < ROWS; ++p) {
+                const int64_t r = r0 + p;
+                if (!inbuf[p]) continue;
+                if (!valid[p]) {
+                    const uint4 z = make_uint4(0, 0, 0, 0);
+                    *reinterpret_cast<uint4 *>(a.h + r * a.ld_h + 8 * c) = z;
+                    if (BRANCH) *reinterpret_cast<uint4 *>(a.x1 + r * a.ld_x1 + 8 * c) = z;
+                    continue;
+                }
+                if (grp[p] != gcur) {
+                    load_f8(a.shift + (int64_t)grp[p] * a.ld_mod + 8 * c, sh);
+                    load_f8(a.scale + (int64_t)grp[p] * a.ld_mod + 8 * c, sc);
+                    gcur = grp[p];
+                }
+                float xf[8];
+                unpack8(xv[p][i], xf);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) xf[e] = (xf[e] - mean[p]) * inv[p] * (1.f + sc[e]) + sh[e];
+                *reinterpret_cast<uint4 *>(a.h + r * a.ld_h + 8 * c) = pack8(xf);
+            }
+        }
+    }
+}
+
+template <int NCH>
+void modnorm_dispatch_nch(const ModnormArgs &a, bool branch, int norm, hipStream_t s) {
+    constexpr int ROWS = 2;
+    const int64_t waves = (a.L_buf + ROWS - 1) / ROWS;
+    const dim3 grid((unsigned)((waves + 3) / 4));
+    if (branch) {
+        if (norm == 0) modnorm_kernel<NCH, ROWS, true, 0><<<grid, 256, 0, s>>>(a);
+        else modnorm_kernel<NCH, ROWS, true, 1><<<grid, 256, 0, s>>>(a);
+    } else {
+        if (norm == 0) modnorm_kernel<NCH, ROWS, false, 0><<<grid, 256, 0, s>>>(a);
+        else modnorm_kernel<NCH, ROWS, false, 1><<<grid, 256, 0, s>>>(a);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// QK RMSNorm + partial RoPE: one workgroup per row; 16 lanes per 128-channel
+// head vector (8 channels per lane); q heads then k heads.
+// ---------------------------------------------------------------------------
+struct QkArgs {
+    uint16_t *q;
+    uint16_t *k;
+    const uint16_t *q_gain;
+    const uint16_t *k_gain;
+    const int32_t *pos;
+    int64_t ld, L_buf, valid;
+    int32_t heads, rot_dim, pairing;
+    float theta, eps;
+};
+
+__global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkArgs a) {
+    __shared__ float cs_cos[64];
+    __shared__ float cs_sin[64];
+    const int64_t r = blockIdx.x;
+    const int t = threadIdx.x;
+    const int slot = t >> 4;  // head-vector slot 0..15
+    const int c = t & 15;     // 8-channel chunk within the head
+    const int nhv = 2 * a.heads;
+    if (r >= a.valid) {
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        for (int hv = slot; hv < nhv; hv += 16) {
+            uint16_t *base = hv < a.heads ? a.q + (int64_t)hv * 128 : a.k + (int64_t)(hv - a.heads) * 128;
+            *reinterpret_cast<uint4 *>(base + r * a.ld + 8 * c) = z;
+        }
+        return;
+    }
+    const int p = a.pos ? a.pos[r] : (int)r;
+    const bool rot = p >= 0 && a.rot_dim > 0;
+    const int half = a.rot_dim >> 1;
+    if (rot && t < half) {
+        // FP64 angle and its sine/cosine, rounded to FP32 (positions reach 6e4,
+        // where an FP32 angle would carry errors of ~4e-3 rad).
+        const double w = pow((double)a.theta, -2.0 * (double)t / (double)a.rot_dim);
+        double sn, cn;
+        sincos((double)p * w, &sn, &cn);
+        cs_cos[t] = (float)cn;
+        cs_sin[t] = (float)sn;
+    }
+    __syncthreads();
+    float gq[8], gk[8];
+    unpack8(*reinterpret_cast<const uint4 *>(a.q_gain + 8 * c), gq);
+    unpack8(*reinterpret_cast<const uint4 *>(a.k_gain + 8 * c), gk);
+    const int lane = t & 63;
+    // rotate-half partner chunk (half is a multiple of 8)
+    const int hc = half >> 3;
+    int pc = c;
+    if (c < hc) pc = c + hc;
+    else if (c < 2 * hc) pc = c - hc;
+    const int src_lane = (lane & ~15) | pc;
+    const bool first_half = 8 * c < half;
+    const bool rotated_chunk = 8 * c < a.rot_dim;
+
+    for (int hv0 = 0; hv0 < nhv; hv0 += 16) {
+        const int hv = hv0 + slot;
+        const bool act = hv < nhv;
+        const bool is_k = hv >= a.heads;
+        uint16_t *ptr = nullptr;
+        float f[8];
+        if (act) {
+            ptr = (is_k ? a.k + (int64_t)(hv - a.heads) * 128 : a.q + (int64_t)hv * 128) + r * a.ld + 8 * c;
+            unpack8(*reinterpret_cast<const uint4 *>(ptr), f);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = 0.f;
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+        ss = sum16(ss);
+        const float inv = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = f[e] * inv * (is_k ? gk[e] : gq[e]);
+        if (rot) {
+            if (a.pairing == 0) {
+                float pv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pv[e] = __shfl(f[e], src_lane);
+                if (rotated_chunk) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = (8 * c + e) % half;
+                        const float cs = cs_cos[j], sn = cs_sin[j];
+                        // first half: a' = a cos - b sin; second half: b' = a sin + b cos
+                        f[e] = first_half ? f[e] * cs - pv[e] * sn : pv[e] * sn + f[e] * cs;
+                    }
+                }
+            } else if (rotated_chunk) {
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const int j = (8 * c + e) >> 1;
+                    const float cs = cs_cos[j], sn = cs_sin[j];
+                    const float x0 = f[e], x1 = f[e + 1];
+                    f[e] = x0 * cs - x1 * sn;
+                    f[e + 1] = x0 * sn + x1 * cs;
+                }
+            }
+        }
+        if (act) *reinterpret_cast<uint4 *>(ptr) = pack8(f);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// SwiGLU: one thread per 8 output columns; a workgroup covers 2048 columns of
+// one row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t *u, int64_t ld_u, uint16_t *g,
+                                                     int64_t ld_g, int64_t valid, int32_t ffn,
+                                                     uint32_t blocks_per_row) {
+    const uint32_t row = blockIdx.x / blocks_per_row;
+    const uint32_t cb = blockIdx.x - row * blocks_per_row;
+    const int c = (int)(cb * 256 + threadIdx.x) * 8;
+    if (c >= ffn) return;
+    uint16_t *dst = g + (int64_t)row * ld_g + c;
+    if ((int64_t)row >= valid) {
+        *reinterpret_cast<uint4 *>(dst) = make_uint4(0, 0, 0, 0);
+        return;
+    }
+    const uint16_t *src = u + (int64_t)row * ld_u + c;
+    float a[8], b[8];
+    unpack8(*reinterpret_cast<const uint4 *>(src), a);
+    unpack8(*reinterpret_cast<const uint4 *>(src + ffn), b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = a[e] / (1.0f + __expf(-a[e])) * b[e];
+    *reinterpret_cast<uint4 *>(dst) = pack8(a);
+}
+
+__global__ __launch_bounds__(256) void zero_rows_kernel(uint16_t *p, int64_t ld, int32_t chunks, int64_t r0,
+                                                        int64_t rows) {
+    const int64_t n = rows * chunks;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int64_t r = i / chunks;
+        const int c = (int)(i - r * chunks);
+        *reinterpret_cast<uint4 *>(p + (r0 + r) * ld + 8 * c) = make_uint4(0, 0, 0, 0);
+    }
+}
+
+__global__ __launch_bounds__(256) void copy_rows_kernel(const uint16_t *src, int64_t ld_s, uint16_t *dst,
+                                                        int64_t ld_d, int32_t chunks, int64_t rows) {
+    const int64_t n = rows * chunks;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int64_t r = i / chunks;
+        const int c = (int)(i - r * chunks);
+        *reinterpret_cast<uint4 *>(dst + r * ld_d + 8 * c) =
+            *reinterpret_cast<const uint4 *>(src + r * ld_s + 8 * c);
+    }
+}
+
+}  // namespace
+
+void launch_modnorm(const uint16_t *x, int64_t ld_x, const uint16_t *branch, int64_t ld_b, const float *shift,
+                    const float *scale, const float *gate, int64_t ld_mod_group, int32_t n_mod_groups,
+                    const int32_t *mod_idx, uint16_t *x1_out, int64_t ld_x1, uint16_t *h_out, int64_t ld_h,
+                    int64_t L_buf, int64_t valid_len, int32_t hidden, float eps, int32_t norm_type,
+                    hipStream_t stream) {
+    ModnormArgs a;
+    a.x = x; a.branch = branch; a.shift = shift; a.scale = scale; a.gate = gate; a.mod_idx = mod_idx;
+    a.x1 = x1_out; a.h = h_out;
+    a.ld_x = ld_x; a.ld_b = ld_b; a.ld_x1 = ld_x1; a.ld_h = ld_h;
+    a.ld_mod = n_mod_groups > 1 ? ld_mod_group : 0;
+    a.L_buf = L_buf; a.valid = valid_len; a.hidden = hidden; a.n_groups = n_mod_groups; a.eps = eps;
+    const int need = (hidden / 8 + 63) / 64;
+    const bool b = branch != nullptr;
+    if (need <= 1) modnorm_dispatch_nch<1>(a, b, norm_type, stream);
+    else if (need <= 2) modnorm_dispatch_nch<2>(a, b, norm_type, stream);
+    else if (need <= 4) modnorm_dispatch_nch<4>(a, b, norm_type, stream);
+    else if (need <= 8) modnorm_dispatch_nch<8>(a, b, norm_type, stream);
+    else if (need <= 11) modnorm_dispatch_nch<11>(a, b, norm_type, stream);
+    else if (need <= 16) modnorm_dispatch_nch<16>(a, b, norm_type, stream);
+    else if (need <= 24) modnorm_dispatch_nch<24>(a, b, norm_type, stream);
+    else modnorm_dispatch_nch<32>(a, b, norm_type, stream);
+}
+
+void launch_qk_norm_rope(uint16_t *q, uint16_t *k, int64_t ld, const uint16_t *q_gain, const uint16_t *k_gain,
+                         const int32_t *pos, int64_t L_buf, int64_t valid_len, int32_t heads, int32_t rot_dim,
+                         int32_t pairing, float theta, float eps, hipStream_t stream) {
+    QkArgs a;
+    a.q = q; a.k = k; a.q_gain = q_gain; a.k_gain = k_gain; a.pos = pos;
+    a.ld = ld; a.L_buf = L_buf; a.valid = valid_len;
+    a.heads = heads; a.rot_dim = rot_dim; a.pairing = pairing; a.theta = theta; a.eps = eps;
+    qk_norm_rope_kernel<<<dim3((unsigned)L_buf), 256, 0, stream>>>(a);
+}
+
+void launch_swiglu(const uint16_t *u, int64_t ld_u, uint16_t *g, int64_t ld_g, int64_t L_buf, int64_t valid_len,
+                   int32_t ffn, hipStream_t stream) {
+    const uint32_t bpr = (uint32_t)((ffn / 8 + 255) / 256);
+    swiglu_kernel<<<dim3((unsigned)(L_buf * bpr)), 256, 0, stream>>>(u, ld_u, g, ld_g, valid_len, ffn, bpr);
+}
+
+void launch_zero_rows(uint16_t *p, int64_t ld, int64_t cols, int64_t r0, int64_t r1, hipStream_t stream) {
+    if (r1 <= r0) return;
+    const int64_t n = (r1 - r0) * (cols / 8);
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 65536);
+    zero_rows_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(p, ld, (int32_t)(cols / 8), r0, r1 - r0);
+}
+
+void launch_copy_rows(const uint16_t *src, int64_t ld_src, uint16_t *dst, int64_t ld_dst, int64_t rows,
+                      int64_t cols, hipStream_t stream) {
+    if (rows <= 0) return;
+    const int64_t n = rows * (cols / 8);
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 65536);
+    copy_rows_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(src, ld_src, dst, ld_dst, (int32_t)(cols / 8),
+                                                                rows);
+}
+
+}  // namespace h3
+
+using namespace h3;
+
+extern "C" {
+
+int h3_fused_modulate_norm(const uint16_t *x, int64_t ld_x, const uint16_t *branch, int64_t ld_b,
+                           const float *shift, const float *scale, const float *gate, int64_t ld_mod_group,
+                           int32_t n_mod_groups, const int32_t *mod_idx, uint16_t *x1_out, int64_t ld_x1,
+                           uint16_t *h_out, int64_t ld_h, int64_t L_buf, int64_t valid_len, int32_t hidden,
+                           float eps, int32_t norm_type, void *stream) {
+    int s = h3_check_fused_modulate_norm(x, ld_x, branch, ld_b, shift, scale, gate, ld_mod_group, n_mod_groups,
+                                         x1_out, ld_x1, h_out, ld_h, L_buf, valid_len, hidden, eps, norm_type);
+    if (s != H3_OK || L_buf == 0) return s;
+    if ((s = device_check()) != H3_OK) return s;
+    launch_modnorm(x, ld_x, branch, ld_b, shift, scale, gate, ld_mod_group, n_mod_groups, mod_idx, x1_out, ld_x1,
+                   h_out, ld_h, L_buf, valid_len, hidden, eps, norm_type, (hipStream_t)stream);
+    return launch_status();
+}
+
+int h3_qk_norm_rope(uint16_t *q, uint16_t *k, int64_t ld, const uint16_t *q_gain, const uint16_t *k_gain,
+                    const int32_t *pos, int64_t L_buf, int64_t valid_len, int32_t heads, int32_t head_dim,
+                    int32_t rot_dim, int32_t pairing, float theta, float eps, void *stream) {
+    int s = h3_check_qk_norm_rope(q, k, ld, q_gain, k_gain, L_buf, valid_len, heads, head_dim, rot_dim, pairing,
+                                  theta, eps);
+    if (s != H3_OK || L_buf == 0) return s;
+    if ((s = device_check()) != H3_OK) return s;
+    launch_qk_norm_rope(q, k, ld, q_gain, k_gain, pos, L_buf, valid_len, heads, rot_dim, pairing, theta, eps,
+                        (hipStream_t)stream);
+    return launch_status();
+}
+
+int h3_swiglu(const uint16_t *u, int64_t ld_u, uint16_t *g, int64_t ld_g, int64_t L_buf, int64_t valid_len,
+              int32_t ffn, void *stream) {
+    int s = h3_check_swiglu(u, ld_u, g, ld_g, L_buf, valid_len, ffn);
+    if (s != H3_OK || L_buf == 0) return s;
+    if ((s = device_check()) != H3_OK) return s;
+    launch_swiglu(u, ld_u, g, ld_g, L_buf, valid_len, ffn, (hipStream_t)stream);
+    return launch_status();
+}
+
+}  // extern "C"

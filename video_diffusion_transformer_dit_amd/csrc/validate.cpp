@@ -1,0 +1,397 @@
+// Host-only argument validation for every entry point of libh3block.
+//
+// No HIP header is included: these checks run before anything is launched
+// (a call that fails here writes nothing) and are callable on a machine
+// without a GPU. Fail-closed rejection of unsupported configurations follows
+// the Sol-H3 report (Appendix B, "Implementation scope": unsupported
+// configurations are rejected before installation).
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "h3_internal.h"
+
+namespace h3 {
+namespace {
+
+constexpr int64_t kBf16 = 2;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A strided matrix in memory: `rows` rows of `cols` elements, row stride `ld`.
+struct Mat {
+    uintptr_t base;
+    int64_t rows, cols, ld, elem;
+    bool empty() const { return base == 0 || rows <= 0 || cols <= 0; }
+    uintptr_t end() const { return base + (uintptr_t)(((rows - 1) * ld + cols) * elem); }
+};
+
+Mat mat(const void *p, int64_t rows, int64_t cols, int64_t ld, int64_t elem = kBf16) {
+    return Mat{reinterpret_cast<uintptr_t>(p), rows, cols, ld, elem};
+}
+
+// True when two strided matrices can share a byte. Matrices with the same
+// row stride are compared column-block-wise (column blocks of one packed
+// buffer are disjoint); otherwise their spans are compared.
+bool overlap(const Mat &a, const Mat &b) {
+    if (a.empty() || b.empty()) return false;
+    if (a.end() <= b.base || b.end() <= a.base) return false;
+    if (a.ld == b.ld && a.elem == b.elem) {
+        const int64_t rowb = a.ld * a.elem;
+        const int64_t diff = (int64_t)b.base - (int64_t)a.base;
+        int64_t c = diff % rowb;
+        if (c < 0) c += rowb;
+        const int64_t wa = a.cols * a.elem, wb = b.cols * b.elem;
+        // b's columns start c bytes into a row of a (or c - rowb, wrapping)
+        const bool hit1 = c < wa && c + wb > 0;
+        const bool hit2 = (c - rowb) < wa && (c - rowb) + wb > 0;
+        return hit1 || hit2;
+    }
+    return true;
+}
+
+bool same(const Mat &a, const Mat &b) { return a.base == b.base && a.ld == b.ld; }
+
+int check_rows(int64_t L_buf, int64_t valid_len) {
+    if (L_buf < 0 || valid_len < 0 || valid_len > L_buf) return H3_ERR_SHAPE;
+    return H3_OK;
+}
+
+int check_bf16_mat(const void *p, int64_t ld, int64_t cols, bool required = true) {
+    if (p == nullptr) return required ? H3_ERR_NULL : H3_OK;
+    if (ld < cols) return H3_ERR_SHAPE;
+    if (!aligned16(p) || (ld % 8) != 0) return H3_ERR_ALIGN;
+    return H3_OK;
+}
+
+#define H3_TRY(expr)                 \
+    do {                             \
+        int _s = (expr);             \
+        if (_s != H3_OK) return _s;  \
+    } while (0)
+
+}  // namespace
+
+int check_dims(const h3_dims *d) {
+    if (d == nullptr) return H3_ERR_NULL;
+    if (d->heads <= 0 || d->head_dim <= 0 || d->hidden <= 0 || d->ffn <= 0) return H3_ERR_SHAPE;
+    if ((int64_t)d->heads * d->head_dim != d->hidden) return H3_ERR_SHAPE;
+    if (d->head_dim != kHeadDim) return H3_ERR_UNSUPPORTED;
+    if (d->hidden > kMaxHidden) return H3_ERR_UNSUPPORTED;
+    if (d->ffn % 64 != 0) return H3_ERR_UNSUPPORTED;  // FFN-down reduction runs in K steps of 64
+    if (d->rot_dim < 0 || d->rot_dim > d->head_dim || d->rot_dim % 16 != 0) return H3_ERR_UNSUPPORTED;
+    if (d->norm_type != 0 && d->norm_type != 1) return H3_ERR_UNSUPPORTED;
+    if (d->rope_pairing != 0 && d->rope_pairing != 1) return H3_ERR_UNSUPPORTED;
+    if (d->reserved != 0) return H3_ERR_SHAPE;
+    if (!(d->eps >= 0.0f) || !std::isfinite(d->eps)) return H3_ERR_SHAPE;
+    if (!(d->rope_theta > 0.0f) || !std::isfinite(d->rope_theta)) return H3_ERR_SHAPE;
+    return H3_OK;
+}
+
+bool ws_layout(const h3_dims *d, int64_t L_buf, WsLayout *out) {
+    if (check_dims(d) != H3_OK || L_buf < 0) return false;
+    const int64_t H = d->hidden, F = d->ffn;
+    const int64_t cols[H3_WS_COUNT] = {H, 3 * H, H, H, H, F};
+    int64_t off = 0;
+    for (int i = 0; i < H3_WS_COUNT; ++i) {
+        out->off[i] = off;
+        out->ld[i] = cols[i];
+        out->cols[i] = cols[i];
+        int64_t bytes = L_buf * cols[i] * kBf16;
+        bytes = (bytes + (int64_t)kWsAlign - 1) / (int64_t)kWsAlign * (int64_t)kWsAlign;
+        off += bytes;
+    }
+    out->total = (size_t)off;
+    return true;
+}
+
+}  // namespace h3
+
+using namespace h3;
+
+extern "C" {
+
+const char *h3_status_string(int s) {
+    switch (s) {
+        case H3_OK: return "H3_OK";
+        case H3_ERR_NULL: return "H3_ERR_NULL: a required pointer is NULL";
+        case H3_ERR_SHAPE: return "H3_ERR_SHAPE: sizes inconsistent or out of range";
+        case H3_ERR_UNSUPPORTED: return "H3_ERR_UNSUPPORTED: configuration not implemented";
+        case H3_ERR_ALIGN: return "H3_ERR_ALIGN: pointer not 16-byte aligned or stride not a multiple of 8";
+        case H3_ERR_ALIAS: return "H3_ERR_ALIAS: buffers overlap";
+        case H3_ERR_WORKSPACE: return "H3_ERR_WORKSPACE: workspace missing or too small";
+        case H3_ERR_DEVICE: return "H3_ERR_DEVICE: current device is not gfx950";
+        case H3_ERR_HIP: return "H3_ERR_HIP: a HIP runtime call failed";
+        default: return "unknown h3 status";
+    }
+}
+
+int h3_abi_version(void) { return H3_ABI_VERSION; }
+
+size_t h3_block_workspace_bytes(const h3_dims *dims, int64_t L_buf) {
+    WsLayout l;
+    if (!ws_layout(dims, L_buf, &l)) return 0;
+    return l.total;
+}
+
+int h3_block_workspace_layout(const h3_dims *dims, int64_t L_buf, int64_t offsets[H3_WS_COUNT],
+                              int64_t lds[H3_WS_COUNT]) {
+    if (offsets == nullptr || lds == nullptr) return H3_ERR_NULL;
+    H3_TRY(check_dims(dims));
+    if (L_buf < 0) return H3_ERR_SHAPE;
+    WsLayout l;
+    ws_layout(dims, L_buf, &l);
+    for (int i = 0; i < H3_WS_COUNT; ++i) {
+        offsets[i] = l.off[i];
+        lds[i] = l.ld[i];
+    }
+    return H3_OK;
+}
+
+int h3_check_fused_modulate_norm(const uint16_t *x, int64_t ld_x, const uint16_t *branch, int64_t ld_b,
+                                 const float *shift, const float *scale, const float *gate,
+                                 int64_t ld_mod_group, int32_t n_mod_groups, const uint16_t *x1_out,
+                                 int64_t ld_x1, const uint16_t *h_out, int64_t ld_h, int64_t L_buf,
+                                 int64_t valid_len, int32_t hidden, float eps, int32_t norm_type) {
+    H3_TRY(check_rows(L_buf, valid_len));
+    if (hidden <= 0) return H3_ERR_SHAPE;
+    if (hidden > kMaxHidden) return H3_ERR_UNSUPPORTED;
+    if (hidden % 8 != 0) return H3_ERR_ALIGN;
+    if (norm_type != 0 && norm_type != 1) return H3_ERR_UNSUPPORTED;
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return H3_ERR_SHAPE;
+    if (L_buf == 0) return H3_OK;
+    if (!x || !h_out || !shift || !scale) return H3_ERR_NULL;
+    if (branch && (!gate || !x1_out)) return H3_ERR_NULL;
+    if (n_mod_groups < 1) return H3_ERR_SHAPE;
+    if (ld_mod_group < hidden && n_mod_groups > 1) return H3_ERR_SHAPE;
+    if (ld_mod_group % 4 != 0) return H3_ERR_ALIGN;
+    if (!aligned16(shift) || !aligned16(scale) || (gate && !aligned16(gate))) return H3_ERR_ALIGN;
+    H3_TRY(check_bf16_mat(x, ld_x, hidden));
+    H3_TRY(check_bf16_mat(h_out, ld_h, hidden));
+    if (branch) {
+        H3_TRY(check_bf16_mat(branch, ld_b, hidden));
+        H3_TRY(check_bf16_mat(x1_out, ld_x1, hidden));
+    }
+    const Mat mx = mat(x, L_buf, hidden, ld_x), mh = mat(h_out, L_buf, hidden, ld_h);
+    const Mat mb = mat(branch, branch ? L_buf : 0, hidden, ld_b);
+    const Mat m1 = mat(x1_out, branch ? L_buf : 0, hidden, ld_x1);
+    const int64_t modrows = n_mod_groups;
+    const Mat msh = mat(shift, modrows, hidden, std::max<int64_t>(ld_mod_group, hidden), 4);
+    const Mat msc = mat(scale, modrows, hidden, std::max<int64_t>(ld_mod_group, hidden), 4);
+    const Mat mg = mat(gate, gate ? modrows : 0, hidden, std::max<int64_t>(ld_mod_group, hidden), 4);
+    for (const Mat *in : {&mx, &mb, &msh, &msc, &mg})
+        if (overlap(mh, *in)) return H3_ERR_ALIAS;
+    if (branch) {
+        if (overlap(m1, mh)) return H3_ERR_ALIAS;
+        if (!same(m1, mx) && overlap(m1, mx)) return H3_ERR_ALIAS;
+        for (const Mat *in : {&mb, &msh, &msc, &mg})
+            if (overlap(m1, *in)) return H3_ERR_ALIAS;
+    }
+    return H3_OK;
+}
+
+int h3_check_qk_norm_rope(const uint16_t *q, const uint16_t *k, int64_t ld, const uint16_t *q_gain,
+                          const uint16_t *k_gain, int64_t L_buf, int64_t valid_len, int32_t heads,
+                          int32_t head_dim, int32_t rot_dim, int32_t pairing, float theta, float eps) {
+    H3_TRY(check_rows(L_buf, valid_len));
+    if (heads <= 0 || head_dim <= 0) return H3_ERR_SHAPE;
+    if (head_dim != kHeadDim) return H3_ERR_UNSUPPORTED;
+    if ((int64_t)heads * head_dim > kMaxHidden) return H3_ERR_UNSUPPORTED;
+    if (rot_dim < 0 || rot_dim > head_dim || rot_dim % 16 != 0) return H3_ERR_UNSUPPORTED;
+    if (pairing != 0 && pairing != 1) return H3_ERR_UNSUPPORTED;
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return H3_ERR_SHAPE;
+    if (!(theta > 0.0f) || !std::isfinite(theta)) return H3_ERR_SHAPE;
+    if (L_buf == 0) return H3_OK;
+    if (!q || !k || !q_gain || !k_gain) return H3_ERR_NULL;
+    const int64_t H = (int64_t)heads * head_dim;
+    H3_TRY(check_bf16_mat(q, ld, H));
+    H3_TRY(check_bf16_mat(k, ld, H));
+    if (!aligned16(q_gain) || !aligned16(k_gain)) return H3_ERR_ALIGN;
+    const Mat mq = mat(q, L_buf, H, ld), mk = mat(k, L_buf, H, ld);
+    if (overlap(mq, mk)) return H3_ERR_ALIAS;
+    const Mat gq = mat(q_gain, 1, head_dim, head_dim), gk = mat(k_gain, 1, head_dim, head_dim);
+    if (overlap(mq, gq) || overlap(mq, gk) || overlap(mk, gq) || overlap(mk, gk)) return H3_ERR_ALIAS;
+    return H3_OK;
+}
+
+int h3_check_swiglu(const uint16_t *u, int64_t ld_u, const uint16_t *g, int64_t ld_g, int64_t L_buf,
+                    int64_t valid_len, int32_t ffn) {
+    H3_TRY(check_rows(L_buf, valid_len));
+    if (ffn <= 0) return H3_ERR_SHAPE;
+    if (ffn % 8 != 0) return H3_ERR_ALIGN;
+    if (L_buf == 0) return H3_OK;
+    if (!u || !g) return H3_ERR_NULL;
+    H3_TRY(check_bf16_mat(u, ld_u, 2 * (int64_t)ffn));
+    H3_TRY(check_bf16_mat(g, ld_g, ffn));
+    if (overlap(mat(u, L_buf, 2 * (int64_t)ffn, ld_u), mat(g, L_buf, ffn, ld_g))) return H3_ERR_ALIAS;
+    return H3_OK;
+}
+
+int h3_check_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ldw, const uint16_t *c,
+                    int64_t ldc, int64_t M_buf, int64_t M_valid, int64_t N, int64_t K, int32_t epilogue,
+                    const uint16_t *resid, int64_t ld_r, const float *gate, int32_t n_mod_groups) {
+    H3_TRY(check_rows(M_buf, M_valid));
+    if (N <= 0 || K <= 0) return H3_ERR_SHAPE;
+    if (epilogue < H3_EPI_STORE || epilogue > H3_EPI_SWIGLU) return H3_ERR_UNSUPPORTED;
+    if (N % 8 != 0 || K % 8 != 0) return H3_ERR_ALIGN;
+    if (K % 64 != 0) return H3_ERR_UNSUPPORTED;  // the MFMA kernel steps K by 64
+    if (epilogue == H3_EPI_SWIGLU && (N % 16) != 0) return H3_ERR_ALIGN;
+    if (M_buf == 0) return H3_OK;
+    if (!a || !w || !c) return H3_ERR_NULL;
+    const int64_t Nc = epilogue == H3_EPI_SWIGLU ? N / 2 : N;
+    H3_TRY(check_bf16_mat(a, lda, K));
+    H3_TRY(check_bf16_mat(w, ldw, K));
+    H3_TRY(check_bf16_mat(c, ldc, Nc));
+    const Mat ma = mat(a, M_buf, K, lda), mw = mat(w, N, K, ldw), mc = mat(c, M_buf, Nc, ldc);
+    if (overlap(mc, ma) || overlap(mc, mw)) return H3_ERR_ALIAS;
+    if (epilogue == H3_EPI_RESIDUAL) {
+        if (!resid || !gate) return H3_ERR_NULL;
+        if (n_mod_groups < 1) return H3_ERR_SHAPE;
+        if (!aligned16(gate)) return H3_ERR_ALIGN;
+        H3_TRY(check_bf16_mat(resid, ld_r, N));
+        const Mat mr = mat(resid, M_buf, N, ld_r);
+        if (!same(mr, mc) && overlap(mr, mc)) return H3_ERR_ALIAS;
+    }
+    return H3_OK;
+}
+
+int h3_check_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k,
+                       const uint16_t *v, int64_t ld_v, const uint16_t *o, int64_t ld_o, int64_t L_buf,
+                       int64_t valid_len, int32_t heads, int32_t head_dim, float softmax_scale,
+                       const h3_qgroup *groups, int32_t n_groups) {
+    H3_TRY(check_rows(L_buf, valid_len));
+    if (heads <= 0 || head_dim <= 0) return H3_ERR_SHAPE;
+    if (head_dim != kHeadDim) return H3_ERR_UNSUPPORTED;
+    if (!std::isfinite(softmax_scale) || softmax_scale < 0.0f) return H3_ERR_SHAPE;
+    const int64_t H = (int64_t)heads * head_dim;
+    if (groups != nullptr && (n_groups < 1 || n_groups > H3_MAX_GROUPS)) return H3_ERR_SHAPE;
+    if (groups == nullptr && n_groups != 0) return H3_ERR_SHAPE;
+    if (L_buf == 0) return H3_OK;
+    if (!q || !k || !v || !o) return H3_ERR_NULL;
+    H3_TRY(check_bf16_mat(q, ld_q, H));
+    H3_TRY(check_bf16_mat(k, ld_k, H));
+    H3_TRY(check_bf16_mat(v, ld_v, H));
+    H3_TRY(check_bf16_mat(o, ld_o, H));
+    const Mat mo = mat(o, L_buf, H, ld_o);
+    if (overlap(mo, mat(q, L_buf, H, ld_q)) || overlap(mo, mat(k, L_buf, H, ld_k)) ||
+        overlap(mo, mat(v, L_buf, H, ld_v)))
+        return H3_ERR_ALIAS;
+    if (groups) {
+        std::vector<std::pair<int64_t, int64_t>> spans;
+        for (int gi = 0; gi < n_groups; ++gi) {
+            const h3_qgroup &g = groups[gi];
+            if (g.reserved != 0) return H3_ERR_SHAPE;
+            if (g.q_begin < 0 || g.q_end < g.q_begin || g.q_end > valid_len) return H3_ERR_SHAPE;
+            if (g.n_seg < 1 || g.n_seg > H3_MAX_SEGMENTS) return H3_ERR_UNSUPPORTED;
+            if (g.q_end > g.q_begin) spans.push_back({g.q_begin, g.q_end});
+            for (int si = 0; si < g.n_seg; ++si) {
+                const h3_kv_seg &s = g.seg[si];
+                if (s.begin < 0 || s.len < 1) return H3_ERR_SHAPE;
+                if (s.k == nullptr) {
+                    if (s.v != nullptr) return H3_ERR_NULL;
+                    if (s.begin + s.len > valid_len) return H3_ERR_SHAPE;
+                } else {
+                    if (s.v == nullptr) return H3_ERR_NULL;
+                    H3_TRY(check_bf16_mat(s.k, s.ld, H));
+                    H3_TRY(check_bf16_mat(s.v, s.ld, H));
+                    const Mat sk = mat(s.k + s.begin * s.ld, s.len, H, s.ld);
+                    const Mat sv = mat(s.v + s.begin * s.ld, s.len, H, s.ld);
+                    if (overlap(mo, sk) || overlap(mo, sv)) return H3_ERR_ALIAS;
+                }
+            }
+        }
+        std::sort(spans.begin(), spans.end());
+        for (size_t i = 1; i < spans.size(); ++i)
+            if (spans[i].first < spans[i - 1].second) return H3_ERR_SHAPE;
+    }
+    return H3_OK;
+}
+
+int h3_check_block_forward(const h3_dims *dims, const h3_block_weights *w, const uint16_t *x, uint16_t *y,
+                           const float *mod, int32_t n_mod_groups, const int32_t *mod_idx,
+                           const int32_t *pos, int64_t L_buf, int64_t valid_len, const h3_qgroup *groups,
+                           int32_t n_groups, const h3_kv_export *kv_export, const void *workspace,
+                           size_t ws_bytes) {
+    (void)mod_idx;
+    (void)pos;
+    H3_TRY(check_dims(dims));
+    H3_TRY(check_rows(L_buf, valid_len));
+    if (w == nullptr) return H3_ERR_NULL;
+    if (groups != nullptr && (n_groups < 1 || n_groups > H3_MAX_GROUPS)) return H3_ERR_SHAPE;
+    if (groups == nullptr && n_groups != 0) return H3_ERR_SHAPE;
+    if (L_buf == 0) return H3_OK;
+    const int64_t H = dims->hidden, F = dims->ffn, d = dims->head_dim;
+    if (!x || !y || !mod) return H3_ERR_NULL;
+    if (!w->w_qkv || !w->q_gain || !w->k_gain || !w->w_o || !w->w_up || !w->w_down) return H3_ERR_NULL;
+    if (n_mod_groups < 1) return H3_ERR_SHAPE;
+    if (!aligned16(mod)) return H3_ERR_ALIGN;
+    H3_TRY(check_bf16_mat(x, H, H));
+    H3_TRY(check_bf16_mat(y, H, H));
+    for (const uint16_t *p : {w->w_qkv, w->b_qkv, w->q_gain, w->k_gain, w->w_o, w->b_o, w->w_up, w->b_up,
+                              w->w_down, w->b_down})
+        if (p && !aligned16(p)) return H3_ERR_ALIGN;
+    // workspace
+    WsLayout l;
+    ws_layout(dims, L_buf, &l);
+    if (workspace == nullptr || ws_bytes < l.total) return H3_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0) return H3_ERR_ALIGN;
+    const Mat mx = mat(x, L_buf, H, H), my = mat(y, L_buf, H, H);
+    const Mat mws = mat(workspace, 1, (int64_t)l.total, (int64_t)l.total, 1);
+    const Mat weights[] = {mat(w->w_qkv, 3 * H, H, H), mat(w->b_qkv, w->b_qkv ? 1 : 0, 3 * H, 3 * H),
+                           mat(w->q_gain, 1, d, d),     mat(w->k_gain, 1, d, d),
+                           mat(w->w_o, H, H, H),        mat(w->b_o, w->b_o ? 1 : 0, H, H),
+                           mat(w->w_up, 2 * F, H, H),   mat(w->b_up, w->b_up ? 1 : 0, 2 * F, 2 * F),
+                           mat(w->w_down, H, F, F),     mat(w->b_down, w->b_down ? 1 : 0, H, H)};
+    const Mat mmod = mat(mod, 1, (int64_t)n_mod_groups * 6 * H, (int64_t)n_mod_groups * 6 * H, 4);
+    if (!same(mx, my) && overlap(mx, my)) return H3_ERR_ALIAS;
+    if (overlap(my, mws) || overlap(mx, mws) || overlap(my, mmod) || overlap(mws, mmod)) return H3_ERR_ALIAS;
+    for (const Mat &m : weights)
+        if (overlap(my, m) || overlap(mws, m)) return H3_ERR_ALIAS;
+    if (groups) {
+        // Same rules as h3_attention on the block's own q~/k~/v inside the workspace.
+        std::vector<std::pair<int64_t, int64_t>> spans;
+        for (int gi = 0; gi < n_groups; ++gi) {
+            const h3_qgroup &g = groups[gi];
+            if (g.reserved != 0) return H3_ERR_SHAPE;
+            if (g.q_begin < 0 || g.q_end < g.q_begin || g.q_end > valid_len) return H3_ERR_SHAPE;
+            if (g.n_seg < 1 || g.n_seg > H3_MAX_SEGMENTS) return H3_ERR_UNSUPPORTED;
+            if (g.q_end > g.q_begin) spans.push_back({g.q_begin, g.q_end});
+            for (int si = 0; si < g.n_seg; ++si) {
+                const h3_kv_seg &s = g.seg[si];
+                if (s.begin < 0 || s.len < 1) return H3_ERR_SHAPE;
+                if (s.k == nullptr) {
+                    if (s.v != nullptr) return H3_ERR_NULL;
+                    if (s.begin + s.len > valid_len) return H3_ERR_SHAPE;
+                } else {
+                    if (s.v == nullptr) return H3_ERR_NULL;
+                    H3_TRY(check_bf16_mat(s.k, s.ld, H));
+                    H3_TRY(check_bf16_mat(s.v, s.ld, H));
+                    const Mat sk = mat(s.k + s.begin * s.ld, s.len, H, s.ld);
+                    const Mat sv = mat(s.v + s.begin * s.ld, s.len, H, s.ld);
+                    if (overlap(my, sk) || overlap(my, sv) || overlap(mws, sk) || overlap(mws, sv))
+                        return H3_ERR_ALIAS;
+                }
+            }
+        }
+        std::sort(spans.begin(), spans.end());
+        for (size_t i = 1; i < spans.size(); ++i)
+            if (spans[i].first < spans[i - 1].second) return H3_ERR_SHAPE;
+    }
+    if (kv_export) {
+        const h3_kv_export &e = *kv_export;
+        if (!e.k || !e.v) return H3_ERR_NULL;
+        if (e.src_begin < 0 || e.len < 0 || e.src_begin + e.len > valid_len) return H3_ERR_SHAPE;
+        H3_TRY(check_bf16_mat(e.k, e.ld, H));
+        H3_TRY(check_bf16_mat(e.v, e.ld, H));
+        const Mat ek = mat(e.k, e.len, H, e.ld), ev = mat(e.v, e.len, H, e.ld);
+        if (overlap(ek, ev)) return H3_ERR_ALIAS;
+        for (const Mat *m : {&mx, &my, &mws, &mmod})
+            if (overlap(ek, *m) || overlap(ev, *m)) return H3_ERR_ALIAS;
+        for (const Mat &m : weights)
+            if (overlap(ek, m) || overlap(ev, m)) return H3_ERR_ALIAS;
+    }
+    return H3_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,224 @@
+"""Thin ctypes binding of libh3block.so (include/h3block.h).
+
+Argument marshalling only: every step of the block runs in the library's HIP
+kernels. Tensors are torch tensors on the GPU (PyTorch supplies device memory
+and streams); BF16 tensors are passed by their bit patterns. Each wrapper
+raises H3Error on a non-zero status. If the library has not been built the
+import of this module fails loudly; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libh3block.so")
+
+H3_OK, H3_ERR_NULL, H3_ERR_SHAPE, H3_ERR_UNSUPPORTED, H3_ERR_ALIGN, H3_ERR_ALIAS, \
+    H3_ERR_WORKSPACE, H3_ERR_DEVICE, H3_ERR_HIP = range(9)
+H3_EPI_STORE, H3_EPI_RESIDUAL, H3_EPI_SWIGLU = range(3)
+H3_WS_H, H3_WS_QKV, H3_WS_O, H3_WS_X1, H3_WS_H2, H3_WS_G = range(6)
+H3_WS_COUNT = 6
+H3_MAX_SEGMENTS = 4
+H3_MAX_GROUPS = 8
+
+
+class H3Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+class Dims(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("heads", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32),
+                ("rot_dim", C.c_int32), ("norm_type", C.c_int32), ("rope_pairing", C.c_int32),
+                ("reserved", C.c_int32), ("rope_theta", C.c_float), ("eps", C.c_float)]
+
+
+class BlockWeights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("w_qkv", "b_qkv", "q_gain", "k_gain", "w_o", "b_o", "w_up", "b_up",
+                                          "w_down", "b_down")]
+
+
+class KvSeg(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("ld", C.c_int64), ("begin", C.c_int64),
+                ("len", C.c_int64)]
+
+
+class QGroup(C.Structure):
+    _fields_ = [("q_begin", C.c_int64), ("q_end", C.c_int64), ("n_seg", C.c_int32), ("reserved", C.c_int32),
+                ("seg", KvSeg * H3_MAX_SEGMENTS)]
+
+
+class KvExport(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("ld", C.c_int64), ("src_begin", C.c_int64),
+                ("len", C.c_int64)]
+
+
+def _load():
+    # torch supplies device memory and streams, and ships its own HIP runtime
+    # (libamdhip64, soname libamdhip64.so.7). Importing torch first makes the
+    # library bind to that same runtime; loading the library first would bring
+    # in a second HIP runtime that does not see torch's device state.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m video_diffusion_transformer_dit_amd.build`")
+    lib = C.CDLL(LIB_PATH)
+    P, I32, I64, F32, SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
+    sig = {
+        "h3_block_forward": [C.POINTER(Dims), C.POINTER(BlockWeights), P, P, P, I32, P, P, I64, I64,
+                             C.POINTER(QGroup), I32, C.POINTER(KvExport), P, SZ, P],
+        "h3_check_block_forward": [C.POINTER(Dims), C.POINTER(BlockWeights), P, P, P, I32, P, P, I64, I64,
+                                   C.POINTER(QGroup), I32, C.POINTER(KvExport), P, SZ],
+        "h3_attention": [P, I64, P, I64, P, I64, P, I64, I64, I64, I32, I32, F32, C.POINTER(QGroup), I32, P],
+        "h3_check_attention": [P, I64, P, I64, P, I64, P, I64, I64, I64, I32, I32, F32, C.POINTER(QGroup), I32],
+        "h3_fused_modulate_norm": [P, I64, P, I64, P, P, P, I64, I32, P, P, I64, P, I64, I64, I64, I32, F32, I32, P],
+        "h3_check_fused_modulate_norm": [P, I64, P, I64, P, P, P, I64, I32, P, I64, P, I64, I64, I64, I32, F32,
+                                         I32],
+        "h3_qk_norm_rope": [P, P, I64, P, P, P, I64, I64, I32, I32, I32, I32, F32, F32, P],
+        "h3_check_qk_norm_rope": [P, P, I64, P, P, I64, I64, I32, I32, I32, I32, F32, F32],
+        "h3_swiglu": [P, I64, P, I64, I64, I64, I32, P],
+        "h3_check_swiglu": [P, I64, P, I64, I64, I64, I32],
+        "h3_linear": [P, I64, P, I64, P, P, I64, I64, I64, I64, I64, I32, P, I64, P, I64, I32, P, P],
+        "h3_check_linear": [P, I64, P, I64, P, I64, I64, I64, I64, I64, I32, P, I64, P, I32],
+        "h3_block_workspace_bytes": [C.POINTER(Dims), I64],
+        "h3_block_workspace_layout": [C.POINTER(Dims), I64, C.POINTER(I64), C.POINTER(I64)],
+        "h3_status_string": [C.c_int],
+        "h3_abi_version": [],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = C.c_int
+    lib.h3_block_workspace_bytes.restype = C.c_size_t
+    lib.h3_status_string.restype = C.c_char_p
+    return lib
+
+
+LIB = _load()
+EXPORTS = ["h3_block_forward", "h3_attention", "h3_fused_modulate_norm", "h3_qk_norm_rope", "h3_swiglu",
+           "h3_linear", "h3_block_workspace_bytes", "h3_block_workspace_layout", "h3_status_string",
+           "h3_abi_version", "h3_check_block_forward", "h3_check_attention", "h3_check_fused_modulate_norm",
+           "h3_check_qk_norm_rope", "h3_check_swiglu", "h3_check_linear"]
+
+
+def status_string(s: int) -> str:
+    return LIB.h3_status_string(int(s)).decode()
+
+
+def _ok(s: int, where: str) -> None:
+    if s != H3_OK:
+        raise H3Error(s, where)
+
+
+def _ptr(t):
+    """Device (or host) address of a tensor, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _ld(t, default=None):
+    if t is None:
+        return 0 if default is None else default
+    return t.stride(0) if t.dim() > 1 else t.shape[0]
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def make_dims(hidden, heads, ffn, head_dim=128, rot_dim=64, norm_type=0, rope_pairing=0, rope_theta=10000.0,
+              eps=1e-6) -> Dims:
+    return Dims(hidden, heads, head_dim, ffn, rot_dim, norm_type, rope_pairing, 0, rope_theta, eps)
+
+
+def make_weights(w: dict) -> BlockWeights:
+    return BlockWeights(*[_ptr(w.get(n)) for n in ("w_qkv", "b_qkv", "q_gain", "k_gain", "w_o", "b_o", "w_up",
+                                                   "b_up", "w_down", "b_down")])
+
+
+def make_groups(groups):
+    """groups: list of (q_begin, q_end, segs) with segs a list of
+    ('self', begin, len) or (k_tensor, v_tensor, begin, len)."""
+    if groups is None:
+        return None, 0
+    arr = (QGroup * len(groups))()
+    for i, (qb, qe, segs) in enumerate(groups):
+        arr[i].q_begin, arr[i].q_end, arr[i].n_seg = qb, qe, len(segs)
+        for j, s in enumerate(segs):
+            if isinstance(s[0], str):
+                arr[i].seg[j] = KvSeg(None, None, 0, s[1], s[2])
+            else:
+                k, v, b, ln = s
+                arr[i].seg[j] = KvSeg(_ptr(k), _ptr(v), k.stride(0), b, ln)
+    return arr, len(groups)
+
+
+def workspace_bytes(dims: Dims, L_buf: int) -> int:
+    return int(LIB.h3_block_workspace_bytes(C.byref(dims), L_buf))
+
+
+def workspace_layout(dims: Dims, L_buf: int):
+    off = (C.c_int64 * H3_WS_COUNT)()
+    lds = (C.c_int64 * H3_WS_COUNT)()
+    _ok(LIB.h3_block_workspace_layout(C.byref(dims), L_buf, off, lds), "h3_block_workspace_layout")
+    return list(off), list(lds)
+
+
+def block_forward(dims: Dims, weights: BlockWeights, x, y, mod, n_mod_groups, valid_len, workspace,
+                  mod_idx=None, pos=None, groups=None, kv_export=None, stream=None):
+    garr, ng = make_groups(groups)
+    exp = None
+    if kv_export is not None:
+        k, v, src_begin, ln = kv_export
+        exp = KvExport(_ptr(k), _ptr(v), k.stride(0), src_begin, ln)
+    s = LIB.h3_block_forward(C.byref(dims), C.byref(weights), _ptr(x), _ptr(y), _ptr(mod), n_mod_groups,
+                             _ptr(mod_idx), _ptr(pos), x.shape[0], valid_len, garr, ng,
+                             C.byref(exp) if exp is not None else None, _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream))
+    _ok(s, "h3_block_forward")
+
+
+def attention(q, k, v, o, valid_len, heads, softmax_scale=0.0, groups=None, stream=None):
+    garr, ng = make_groups(groups)
+    s = LIB.h3_attention(_ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0), _ptr(o), o.stride(0),
+                         q.shape[0], valid_len, heads, 128, softmax_scale, garr, ng, _stream(stream))
+    _ok(s, "h3_attention")
+
+
+def fused_modulate_norm(x, shift, scale, h_out, valid_len, eps=1e-6, norm_type=0, branch=None, gate=None,
+                        x1_out=None, ld_mod_group=0, n_mod_groups=1, mod_idx=None, stream=None):
+    hidden = x.shape[1]
+    s = LIB.h3_fused_modulate_norm(_ptr(x), x.stride(0), _ptr(branch), _ld(branch), _ptr(shift), _ptr(scale),
+                                   _ptr(gate), ld_mod_group, n_mod_groups, _ptr(mod_idx), _ptr(x1_out),
+                                   _ld(x1_out), _ptr(h_out), h_out.stride(0), x.shape[0], valid_len, hidden, eps,
+                                   norm_type, _stream(stream))
+    _ok(s, "h3_fused_modulate_norm")
+
+
+def qk_norm_rope(q, k, q_gain, k_gain, valid_len, heads, rot_dim=64, pairing=0, theta=10000.0, eps=1e-6,
+                 pos=None, stream=None):
+    s = LIB.h3_qk_norm_rope(_ptr(q), _ptr(k), q.stride(0), _ptr(q_gain), _ptr(k_gain), _ptr(pos), q.shape[0],
+                            valid_len, heads, 128, rot_dim, pairing, theta, eps, _stream(stream))
+    _ok(s, "h3_qk_norm_rope")
+
+
+def swiglu(u, g, valid_len, ffn, stream=None):
+    s = LIB.h3_swiglu(_ptr(u), u.stride(0), _ptr(g), g.stride(0), u.shape[0], valid_len, ffn, _stream(stream))
+    _ok(s, "h3_swiglu")
+
+
+def linear(a, w, c, M_valid, epilogue=H3_EPI_STORE, bias=None, resid=None, gate=None, ld_gate_group=0,
+           n_mod_groups=1, mod_idx=None, stream=None):
+    N, K = w.shape
+    s = LIB.h3_linear(_ptr(a), a.stride(0), _ptr(w), w.stride(0), _ptr(bias), _ptr(c), c.stride(0), a.shape[0],
+                      M_valid, N, K, epilogue, _ptr(resid), _ld(resid), _ptr(gate), ld_gate_group, n_mod_groups,
+                      _ptr(mod_idx), _stream(stream))
+    _ok(s, "h3_linear")
