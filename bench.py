@@ -1,0 +1,212 @@
+"""Benchmark of the H3 DiT block forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one h3_block_forward over the full-width block at the pages'
+packed length: 58,758 valid tokens in a 58,816-token buffer, hidden 5376,
+42 heads x 128, SwiGLU width 21504, BF16 with FP32 modulation. Inputs are
+synthetic (seeded normal weights ~N(0, 0.02), activations ~N(0, 1), AdaLN
+table ~N(0, 0.1)) generated on the GPU and resident in HBM before timing.
+
+Prints ONE JSON line: ms per block (HIP events on the library's stream,
+bracketed by synchronize), algorithmic TFLOP/s, a per-kernel breakdown timed
+the same way with the block's own launch configurations, the roofline of the
+dominant kernel (attention) and the FP64 CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense BF16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+SEED = 20260903
+
+
+def block_flops(V: int, H: int, F: int, heads_dim_total: int | None = None):
+    """Algorithmic work over valid rows: GEMMs 2 V H (4H + 3F); attention
+    4 V^2 H (QK^T and PV, no causal halving)."""
+    gemm = 2.0 * V * H * (4 * H + 3 * F)
+    attn = 4.0 * V * V * H
+    return gemm, attn
+
+
+def elementwise_bytes(V: int, H: int, F: int):
+    """Algorithmic HBM bytes of the memory-bound steps (BF16 = 2 B):
+    modnorm x->h 4VH; qk-norm+RoPE in place on q,k 8VH; modnorm x1->h2 4VH."""
+    return {"modnorm": 4.0 * V * H, "qk_norm_rope": 8.0 * V * H, "modnorm2": 4.0 * V * H}
+
+
+def time_calls(torch, fn, iters: int, warmup: int) -> float:
+    """Average ms per call with HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def cpu_baseline(seconds_target: float = 20.0):
+    """FP64 oracle on a bounded sample: the full-width block at L tokens, scaled
+    to ms per block at the 58,758-token workload by algorithmic flops."""
+    from oracle import h3_oracle as O
+    from video_diffusion_transformer_dit_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    L = 1024
+    s = I.scaled(I.FULL_4096, L, name=f"full-{L}")
+    wb = I.block_weights(s, "cpu0")
+    w = {k: O.bf16_to_f64(v) for k, v in wb.items()}
+    x = O.bf16_to_f64(I.activations(s, tag="cpu0.x"))
+    mod = I.mod_table(s, 1, tag="cpu0.mod").astype(np.float64)
+    t0 = time.perf_counter()
+    O.block_forward(x, w, mod, heads=s.heads, head_dim=128, ffn=s.ffn, valid_len=L, rot_dim=s.rot_dim)
+    dt = time.perf_counter() - t0
+    g_s, a_s = block_flops(L, s.hidden, s.ffn)
+    g_f, a_f = block_flops(58758, 5376, 21504)
+    ms_full = dt * 1e3 * (g_f + a_f) / (g_s + a_s)
+    return {"value": round(ms_full, 1), "unit": "ms/block", "cores": int(threads), "kind": "oracle",
+            "sample": f"FP64 numpy oracle, one full-width block (H 5376, 42x128, F 21504) at {L} tokens: "
+                      f"{dt:.2f} s for {(g_s + a_s) / 1e12:.3f} TFLOP, scaled by algorithmic flops to the "
+                      f"58,758-token block ({(g_f + a_f) / 1e12:.1f} TFLOP)",
+            "sample_seconds": round(dt, 3), "sample_gflops_per_s": round((g_s + a_s) / dt / 1e9, 1)}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-iters", type=int, default=5)
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from video_diffusion_transformer_dit_amd import h3
+
+    H, heads, F = 5376, 42, 21504
+    L, V = 58816, 58758
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(SEED)
+
+    def normal(shape, std=1.0, mean=0.0, dtype=torch.bfloat16):
+        t = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+        if std != 1.0:
+            t.mul_(std)
+        if mean != 0.0:
+            t.add_(mean)
+        return t.to(dtype)
+
+    w = {"w_qkv": normal((3 * H, H), 0.02), "w_o": normal((H, H), 0.02), "w_up": normal((2 * F, H), 0.02),
+         "w_down": normal((H, F), 0.02), "q_gain": normal((128,), 0.02, 1.0), "k_gain": normal((128,), 0.02, 1.0)}
+    x = normal((L, H))
+    mod = normal((1, 6, H), 0.1, dtype=torch.float32)
+    y = torch.empty_like(x)
+    dims = h3.make_dims(H, heads, F)
+    weights = h3.make_weights(w)
+    ws = torch.empty(h3.workspace_bytes(dims, L), dtype=torch.uint8, device=dev)
+    off, lds = h3.workspace_layout(dims, L)
+
+    def wsv(i, cols):
+        return ws[off[i]:off[i] + L * cols * 2].view(torch.bfloat16).view(L, cols)
+
+    def step():
+        h3.block_forward(dims, weights, x, y, mod, 1, V, ws)
+
+    ms = time_calls(torch, step, a.steps, a.warmup)
+
+    # Per-kernel breakdown: the block's launches, one at a time, same buffers.
+    hbuf, qkv, o, x1, h2, g = (wsv(h3.H3_WS_H, H), wsv(h3.H3_WS_QKV, 3 * H), wsv(h3.H3_WS_O, H),
+                               wsv(h3.H3_WS_X1, H), wsv(h3.H3_WS_H2, H), wsv(h3.H3_WS_G, F))
+    kit = a.kernel_iters
+    k_ms = {}
+    k_ms["modnorm"] = time_calls(torch, lambda: h3.fused_modulate_norm(
+        x, mod[:, 0], mod[:, 1], hbuf, V, ld_mod_group=6 * H), kit, 1)
+    k_ms["gemm_qkv"] = time_calls(torch, lambda: h3.linear(hbuf, w["w_qkv"], qkv, V), kit, 1)
+    k_ms["qk_norm_rope"] = time_calls(torch, lambda: h3.qk_norm_rope(
+        qkv[:, :H], qkv[:, H:2 * H], w["q_gain"], w["k_gain"], V, heads), kit, 1)
+    k_ms["attention"] = time_calls(torch, lambda: h3.attention(
+        qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:], o, V, heads), kit, 1)
+    k_ms["gemm_out_residual"] = time_calls(torch, lambda: h3.linear(
+        o, w["w_o"], x1, V, h3.H3_EPI_RESIDUAL, resid=x, gate=mod[:, 2], ld_gate_group=6 * H), kit, 1)
+    k_ms["modnorm2"] = time_calls(torch, lambda: h3.fused_modulate_norm(
+        x1, mod[:, 3], mod[:, 4], h2, V, ld_mod_group=6 * H), kit, 1)
+    k_ms["gemm_up_swiglu"] = time_calls(torch, lambda: h3.linear(h2, w["w_up"], g, V, h3.H3_EPI_SWIGLU), kit, 1)
+    k_ms["gemm_down_residual"] = time_calls(torch, lambda: h3.linear(
+        g, w["w_down"], y, V, h3.H3_EPI_RESIDUAL, resid=x1, gate=mod[:, 5], ld_gate_group=6 * H), kit, 1)
+
+    gemm_f, attn_f = block_flops(V, H, F)
+    gflops = {"gemm_qkv": 2.0 * V * H * 3 * H, "gemm_out_residual": 2.0 * V * H * H,
+              "gemm_up_swiglu": 2.0 * V * H * 2 * F, "gemm_down_residual": 2.0 * V * F * H, "attention": attn_f}
+    ebytes = elementwise_bytes(V, H, F)
+    kernels = {}
+    for k, t in k_ms.items():
+        d = {"ms": round(t, 4)}
+        if k in gflops:
+            tf = gflops[k] / (t * 1e-3) / 1e12
+            d.update(tflops=round(tf, 1), frac_mfma=round(tf / PEAK_BF16_TFLOPS, 4))
+        if k in ebytes:
+            gbs = ebytes[k] / (t * 1e-3) / 1e9
+            d.update(gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+        kernels[k] = d
+
+    attn_tf = gflops["attention"] / (k_ms["attention"] * 1e-3) / 1e12
+    gemm_ms = sum(k_ms[k] for k in k_ms if k.startswith("gemm"))
+    total_tf = (gemm_f + attn_f) / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "ms per DiT block at 58,816 tokens",
+        "value": round(ms, 3),
+        "unit": "ms/block",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "one full-width H3 DiT block forward, 58,758 valid tokens in a 58,816-token "
+                               "buffer", "hidden": H, "heads": heads, "head_dim": 128, "ffn": F, "L_buf": L,
+                   "valid_len": V, "rot_dim": 64, "weights": "random-init N(0,0.02)"},
+        "block_tflops": round(total_tf, 1),
+        "block_frac_mfma": round(total_tf / PEAK_BF16_TFLOPS, 4),
+        "attention_tflops": round(attn_tf, 1),
+        "gemm_tflops": round(gemm_f / (gemm_ms * 1e-3) / 1e12, 1),
+        "kernels": kernels,
+        "roofline": {"kernel": "attention_fwd_kernel", "bound": "mfma", "achieved": round(attn_tf, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "work_per_launch": "4 * 58758^2 * 5376 = 7.424e13 flop (QK^T and PV over valid rows)"},
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -4,7 +4,7 @@ This module holds none of the block's arithmetic: it draws seeded normal
 samples, stores them in BF16 or FP32 bit patterns, and describes the packed
 token layouts of the workloads. Both sides receive the same bytes.
 
-Recipe: master seed 20260903; each tensor draws from its own PCG64 stream whose
+Recipe: master seed 20260903; each tensor draws from its own SFC64 stream whose
 SeedSequence entropy is (master seed, CRC32 of the tensor's name). Samples are
 drawn as float32 normals and cast to BF16 with round-to-nearest-even.
 """
@@ -19,17 +19,22 @@ MASTER_SEED = 20260903
 
 
 def rng_for(name: str, seed: int = MASTER_SEED) -> np.random.Generator:
-    """Independent PCG64 stream for one named tensor."""
+    """Independent SFC64 stream for one named tensor."""
     ss = np.random.SeedSequence([seed, zlib.crc32(name.encode())])
-    return np.random.Generator(np.random.PCG64(ss))
+    return np.random.Generator(np.random.SFC64(ss))
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
-    """float32 -> BF16 bit patterns (uint16), round to nearest, ties to even.
-    Inputs are finite normals, so NaN handling is not needed."""
+    """float32 -> BF16 bit patterns (uint16), round to nearest, ties to even:
+    add 0x7FFF plus the lowest kept bit, then drop the low 16 bits. Inputs are
+    finite normals, so NaN handling is not needed."""
     u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
-    lsb = (u >> np.uint32(16)) & np.uint32(1)
-    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+    t = np.right_shift(u, np.uint32(16))
+    np.bitwise_and(t, np.uint32(1), out=t)
+    np.add(t, np.uint32(0x7FFF), out=t)
+    np.add(t, u, out=t)
+    np.right_shift(t, np.uint32(16), out=t)
+    return t.astype(np.uint16)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
