@@ -148,8 +148,9 @@ def main(argv=None) -> int:
     k_ms["gemm_qkv"] = time_calls(torch, lambda: h3.linear(hbuf, w["w_qkv"], qkv, V), kit, 1)
     k_ms["qk_norm_rope"] = time_calls(torch, lambda: h3.qk_norm_rope(
         qkv[:, :H], qkv[:, H:2 * H], w["q_gain"], w["k_gain"], V, heads), kit, 1)
+    vt_ws = ws[off[h3.H3_WS_VT]:off[h3.H3_WS_VT] + lds[h3.H3_WS_VT]]
     k_ms["attention"] = time_calls(torch, lambda: h3.attention(
-        qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:], o, V, heads), kit, 1)
+        qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:], o, V, heads, workspace=vt_ws), kit, 1)
     k_ms["gemm_out_residual"] = time_calls(torch, lambda: h3.linear(
         o, w["w_o"], x1, V, h3.H3_EPI_RESIDUAL, resid=x, gate=mod[:, 2], ld_gate_group=6 * H), kit, 1)
     k_ms["modnorm2"] = time_calls(torch, lambda: h3.fused_modulate_norm(

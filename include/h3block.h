@@ -153,9 +153,10 @@ typedef struct {
  * groups   NULL: dense attention of every valid row over keys [0, valid_len).
  *          Otherwise n_groups (1..H3_MAX_GROUPS) query groups.
  * kv_export NULL or one refresh copy (see h3_kv_export).
- * workspace device memory of at least h3_block_workspace_bytes(dims, L_buf)
- *          bytes, 256-byte aligned. After the call it holds the block's
- *          intermediates at the offsets h3_block_workspace_layout reports.
+ * workspace device memory of at least
+ *          h3_block_workspace_bytes(dims, L_buf, groups, n_groups) bytes,
+ *          256-byte aligned. After the call it holds the block's intermediates at
+ *          the offsets h3_block_workspace_layout reports.
  * ------------------------------------------------------------------------- */
 int h3_block_forward(const h3_dims *dims, const h3_block_weights *w,
                      const uint16_t *x, uint16_t *y,
@@ -165,19 +166,23 @@ int h3_block_forward(const h3_dims *dims, const h3_block_weights *w,
                      const h3_kv_export *kv_export,
                      void *workspace, size_t ws_bytes, void *stream);
 
-/* Workspace size of h3_block_forward for L_buf rows (bytes). Returns 0 on
- * invalid dims. */
-size_t h3_block_workspace_bytes(const h3_dims *dims, int64_t L_buf);
+/* Workspace size of h3_block_forward for L_buf rows and the given query groups
+ * (NULL for dense attention), in bytes. Returns 0 on invalid arguments. */
+size_t h3_block_workspace_bytes(const h3_dims *dims, int64_t L_buf,
+                                const h3_qgroup *groups, int32_t n_groups);
 
 /* Intermediates h3_block_forward leaves in its workspace, as byte offsets and
  * row strides (elements). All are BF16 [L_buf, cols] with padding rows zero:
  *   H3_WS_H   h   (cols H)      H3_WS_QKV qkv (cols 3H; q~ | k~ | v after
  *   H3_WS_O   o   (cols H)                  QK-norm and RoPE)
  *   H3_WS_X1  x1  (cols H)      H3_WS_H2  h2  (cols H)
- *   H3_WS_G   g   (cols F)                                                  */
+ *   H3_WS_G   g   (cols F)
+ *   H3_WS_VT  attention's V^T staging (see h3_attention_workspace_bytes);
+ *             its "row stride" entry holds its size in bytes.              */
 enum { H3_WS_H = 0, H3_WS_QKV = 1, H3_WS_O = 2, H3_WS_X1 = 3, H3_WS_H2 = 4, H3_WS_G = 5,
-       H3_WS_COUNT = 6 };
+       H3_WS_VT = 6, H3_WS_COUNT = 7 };
 int h3_block_workspace_layout(const h3_dims *dims, int64_t L_buf,
+                              const h3_qgroup *groups, int32_t n_groups,
                               int64_t offsets[H3_WS_COUNT], int64_t lds[H3_WS_COUNT]);
 
 /* ---------------------------------------------------------------------------
@@ -193,12 +198,20 @@ int h3_block_workspace_layout(const h3_dims *dims, int64_t L_buf,
  * groups   NULL: every row in [0, valid_len) attends over keys [0, valid_len).
  * FP32 scores, softmax and accumulation; P is rounded to BF16 for the P.V
  * product. Padding rows and valid rows outside every group are written 0.
+ * workspace device memory of at least h3_attention_workspace_bytes(...) bytes,
+ *          256-byte aligned: each distinct K/V segment's V is first staged
+ *          there transposed per head ([heads][128][keys rounded up to 64]).
  * ------------------------------------------------------------------------- */
 int h3_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k,
                  const uint16_t *v, int64_t ld_v, uint16_t *o, int64_t ld_o,
                  int64_t L_buf, int64_t valid_len, int32_t heads, int32_t head_dim,
                  float softmax_scale, const h3_qgroup *groups, int32_t n_groups,
-                 void *stream);
+                 void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes h3_attention needs: for every distinct segment (dense: the
+ * valid rows), heads * 128 * round_up(len, 64) BF16 values. 0 on bad input. */
+size_t h3_attention_workspace_bytes(int64_t valid_len, int32_t heads,
+                                    const h3_qgroup *groups, int32_t n_groups);
 
 /* ---------------------------------------------------------------------------
  * h3_fused_modulate_norm - operator group (1) of [Sol-H3] §3.5 (residual
@@ -284,7 +297,8 @@ int h3_check_block_forward(const h3_dims *dims, const h3_block_weights *w,
 int h3_check_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k,
                        const uint16_t *v, int64_t ld_v, const uint16_t *o, int64_t ld_o,
                        int64_t L_buf, int64_t valid_len, int32_t heads, int32_t head_dim,
-                       float softmax_scale, const h3_qgroup *groups, int32_t n_groups);
+                       float softmax_scale, const h3_qgroup *groups, int32_t n_groups,
+                       const void *workspace, size_t ws_bytes);
 int h3_check_fused_modulate_norm(const uint16_t *x, int64_t ld_x,
                                  const uint16_t *branch, int64_t ld_b,
                                  const float *shift, const float *scale, const float *gate,

@@ -54,9 +54,11 @@ def test_workspace_layout_is_disjoint_and_aligned():
         off, lds = h3.workspace_layout(d, L)
         total = h3.workspace_bytes(d, L)
         cols = [d.hidden, 3 * d.hidden, d.hidden, d.hidden, d.hidden, d.ffn]
-        assert lds == cols
-        ends = [o + L * c * 2 for o, c in zip(off, cols)]
-        for i in range(6):
+        assert lds[:6] == cols
+        # V^T staging: heads x 128 x round_up(L, 64) BF16 for the dense case
+        assert lds[6] == d.heads * 128 * (-(-L // 64) * 64) * 2
+        ends = [o + L * c * 2 for o, c in zip(off, cols)] + [off[6] + lds[6]]
+        for i in range(7):
             assert off[i] % 256 == 0
             if i:
                 assert off[i] >= ends[i - 1]
@@ -85,7 +87,7 @@ def _block_args(d=TINY, L=512, V=500, ws=None, x=None, y=None, groups=None, n_gr
     mod = addr(8) if mod is None else mod
     ws_ptr = addr(10) if ws is None else ws
     return (C.byref(d), C.byref(w), x, y, mod, 1, None, None, L, V, groups, n_groups, exp, ws_ptr,
-            h3.workspace_bytes(d, L))
+            h3.LIB.h3_block_workspace_bytes(C.byref(d), L, groups, n_groups))
 
 
 def check_block(*args):
@@ -156,18 +158,28 @@ def test_attention_validator():
     base = addr(1)
     q, k, v = base, base + 2 * H, base + 4 * H        # column blocks of one packed qkv (ld 3H)
     o = addr(2)
-    ok = h3.LIB.h3_check_attention(q, 3 * H, k, 3 * H, v, 3 * H, o, H, L, 500, 2, 128, 0.0, None, 0)
+    ws = addr(3)
+    need = h3.attention_workspace_bytes(500, 2)
+    assert need == 2 * 128 * 512 * 2
+    ok = h3.LIB.h3_check_attention(q, 3 * H, k, 3 * H, v, 3 * H, o, H, L, 500, 2, 128, 0.0, None, 0, ws, need)
     assert ok == h3.H3_OK
+    assert h3.LIB.h3_check_attention(q, 3 * H, k, 3 * H, v, 3 * H, o, H, L, 500, 2, 128, 0.0, None, 0, ws,
+                                     need - 1) == h3.H3_ERR_WORKSPACE
+    assert h3.LIB.h3_check_attention(q, 3 * H, k, 3 * H, v, 3 * H, o, H, L, 500, 2, 128, 0.0, None, 0, o,
+                                     need) == h3.H3_ERR_ALIAS
+    # groups sharing one segment stage its V^T once
+    g, n = h3.make_groups([(0, 100, [("self", 0, 500)]), (100, 500, [("self", 0, 500)])])
+    assert h3.LIB.h3_attention_workspace_bytes(500, 2, g, n) == need
     # o overlapping the packed qkv
     assert h3.LIB.h3_check_attention(q, 3 * H, k, 3 * H, v, 3 * H, base + 6 * H, H, L, 500, 2, 128, 0.0, None,
-                                     0) == h3.H3_ERR_ALIAS
+                                     0, ws, need) == h3.H3_ERR_ALIAS
     assert h3.LIB.h3_check_attention(q, 3 * H, k, 3 * H, v, 3 * H, o, H, L, 500, 2, 64, 0.0, None,
-                                     0) == h3.H3_ERR_UNSUPPORTED
+                                     0, ws, need) == h3.H3_ERR_UNSUPPORTED
     assert h3.LIB.h3_check_attention(q, 3 * H, k, 3 * H, v, 3 * H, o, H, L, 500, 2, 128, -1.0, None,
-                                     0) == h3.H3_ERR_SHAPE
+                                     0, ws, need) == h3.H3_ERR_SHAPE
     assert h3.LIB.h3_check_attention(q, 3 * H + 4, k, 3 * H, v, 3 * H, o, H, L, 500, 2, 128, 0.0, None,
-                                     0) == h3.H3_ERR_ALIGN
-    assert h3.LIB.h3_check_attention(q, 3 * H, k, 3 * H, v, 3 * H, o, H, 0, 0, 2, 128, 0.0, None, 0) == h3.H3_OK
+                                     0, ws, need) == h3.H3_ERR_ALIGN
+    assert h3.LIB.h3_check_attention(q, 3 * H, k, 3 * H, v, 3 * H, o, H, 0, 0, 2, 128, 0.0, None, 0, None, 0) == h3.H3_OK
 
 
 def test_elementwise_and_linear_validators():

@@ -29,10 +29,16 @@ class Block:
         self.weights = h3.make_weights(self.w)
         self.md = dev_f32(self.mod)
         self.G = G
-        self.ws = torch.empty(h3.workspace_bytes(self.dims, shape.L_buf), dtype=torch.uint8, device="cuda")
-        self.off, self.lds = h3.workspace_layout(self.dims, shape.L_buf)
+        self.ws = None
+
+    def _ws(self, groups):
+        need = h3.workspace_bytes(self.dims, self.s.L_buf, groups)
+        if self.ws is None or self.ws.numel() < need:
+            self.ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        self.off, self.lds = h3.workspace_layout(self.dims, self.s.L_buf, groups)
 
     def run(self, xb, y=None, mod_idx=None, groups=None, kv_export=None, pos=None):
+        self._ws(groups)
         x = dev_bf16(xb)
         if y is None:
             y = poison(x.shape)

@@ -10,15 +10,19 @@
 // How (flash-style, one pass, the L^2 score matrix never exists):
 //  * A workgroup of 4 wavefronts owns 256 queries of one head; each wavefront
 //    owns 64 queries, kept in registers as MFMA operands.
-//  * K and V stream through LDS in tiles of 64 keys, double-buffered: the next
-//    tile's global loads are in flight while the current one is consumed.
+//  * V is first staged transposed per head (V^T[head][d][key], keys padded to
+//    a multiple of 64) by a small pre-pass, once per distinct K/V segment.
+//  * K and V^T stream through LDS in tiles of 64 keys, double-buffered, with
+//    gfx950's direct global->LDS buffer loads (16 bytes per lane straight into
+//    LDS): no staging registers, and the next tile is in flight while the
+//    current one is consumed.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    a lane then holds 16 keys of one query per 32x32 block, which is exactly
 //    the B-operand layout the O^T = V^T P^T product needs, so P goes from the
 //    score accumulators to the next MFMA without an LDS round trip.
-//  * V is stored transposed in LDS (V^T[d][key]) with the keys of every
-//    16-key group permuted (bits 2 and 3 of the key index swapped) so each
-//    lane's 8 keys of a P.V k-step are one 16-byte read.
+//  * In V^T the keys of every 16-key group are permuted (bits 2 and 3 of the
+//    key index swapped) so each lane's 8 keys of a P.V k-step are one 16-byte
+//    LDS read.
 //  * Online softmax in FP32 in the exp2 domain (scale * log2 e folded into one
 //    FMA); the O accumulator is rescaled only when some row maximum grew.
 //    P is rounded to BF16 for the P.V MFMA.
@@ -52,15 +56,15 @@ struct AttnArgs {
     int32_t tiles_per_head;  // ceil(rows / BQ)
     int32_t n_seg;
     float scale_log2;        // softmax scale * log2(e)
-    const uint16_t *sk[H3_MAX_SEGMENTS];  // segment row 0, head 0
-    const uint16_t *sv[H3_MAX_SEGMENTS];
-    int64_t sldk[H3_MAX_SEGMENTS], sldv[H3_MAX_SEGMENTS], slen[H3_MAX_SEGMENTS];
+    const uint16_t *sk[H3_MAX_SEGMENTS];   // segment row 0, head 0
+    const uint16_t *svt[H3_MAX_SEGMENTS];  // segment's V^T planes [heads][128][lpad]
+    int64_t sldk[H3_MAX_SEGMENTS], slpad[H3_MAX_SEGMENTS], slen[H3_MAX_SEGMENTS];
 };
 
 // Segment fields held in scalar registers while the segment is streamed.
 struct SegState {
-    const uint16_t *k, *v;
-    int64_t ldk, ldv, len;
+    const uint16_t *k, *vt;
+    int64_t ldk, lpad, len;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
@@ -85,18 +89,19 @@ __device__ __forceinline__ int kperm(int k) { return (k & ~12) | ((k & 4) << 1) 
 // Fields of segment s, read from the kernel arguments at static offsets
 // under a uniform condition (dynamic indexing would go through memory).
 __device__ __forceinline__ SegState seg_of(const AttnArgs &a, int s) {
-    SegState r{a.sk[0], a.sv[0], a.sldk[0], a.sldv[0], a.slen[0]};
+    SegState r{a.sk[0], a.svt[0], a.sldk[0], a.slpad[0], a.slen[0]};
 #pragma unroll
     for (int j = 1; j < H3_MAX_SEGMENTS; ++j)
-        if (j == s) r = SegState{a.sk[j], a.sv[j], a.sldk[j], a.sldv[j], a.slen[j]};
+        if (j == s) r = SegState{a.sk[j], a.svt[j], a.sldk[j], a.slpad[j], a.slen[j]};
     return r;
 }
 
-__device__ __forceinline__ uint32_t perm_lo(uint32_t x, uint32_t y) {  // lo16(x) | lo16(y) << 16
-    return __builtin_amdgcn_perm(y, x, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t perm_hi(uint32_t x, uint32_t y) {  // hi16(x) | hi16(y) << 16
-    return __builtin_amdgcn_perm(y, x, 0x07060302u);
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// Direct global -> LDS load of one 1 KB slab: lane i's 16 bytes (descriptor
+// rsrc, byte offset voff + soff) land at slab + 16 i.
+__device__ __forceinline__ void load_slab(__amdgpu_buffer_rsrc_t rsrc, const uint4 *slab, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)slab, 16, voff, soff, 0, 0);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) {
@@ -135,6 +140,12 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
                     bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
                                   rq, (int)(((32 * j + l32) * a.ld_q + 8 * (2 * ks + h)) * 2), 0, 0));
     }
+    // Register-class hints (empty asm, no instruction): the Q operands live in
+    // AGPRs, which the MFMA reads directly, leaving VGPRs for scores and P.
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+a"(qop[j][ks]));
 
     f32x16_t oacc[4][2];
 #pragma unroll
@@ -143,15 +154,22 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) oacc[i][j][e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(oacc[i][j]));
     float m_run[2] = {-__builtin_huge_valf(), -__builtin_huge_valf()};
     float l_run[2] = {0.f, 0.f};
 
-    // ---- K/V tile loader: thread t loads K rows (t>>4) + 16 i, chunk t & 15,
-    //      and V rows 4 (t>>4) + i, chunk t & 15 (i < 4) ----
-    const int ld_r = t >> 4, ld_c = t & 15;
-    uint4 kst[4], vst[4];
+    // ---- K / V^T tile loader (direct to LDS). A tile is 16 slabs of K (4 keys
+    //      x 16 chunks) and 16 slabs of V^T (8 channels x 8 chunks); wave w
+    //      loads slabs 4w .. 4w+3 of each. Lane i of K slab s holds key
+    //      4s + i/16, physical chunk i%16 = logical chunk c ^ (key & 15); lane i
+    //      of V^T slab s holds channel 8s + i/8, physical chunk i%8. ----
+    int k_voff[4], vt_voff[4];
+    const int kkey0 = lane >> 4, kp = lane & 15;
+    const int vd0 = lane >> 3, vp = lane & 7;
 
-    // Count tiles over all segments.
     int n_tiles = 0;
 #pragma unroll
     for (int s = 0; s < H3_MAX_SEGMENTS; ++s)
@@ -161,39 +179,24 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     int seg = 0;
     int64_t seg_k0 = 0;
     SegState nS = seg_of(a, 0);
-    auto load_tile = [&](const SegState &S, int64_t k0) {
-        const int64_t rows = min<int64_t>(S.len - k0, BKV);
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(S.k + k0 * S.ldk + head * D, ((rows - 1) * S.ldk + D) * 2);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(S.v + k0 * S.ldv + head * D, ((rows - 1) * S.ldv + D) * 2);
+    auto set_offsets = [&](const SegState &S) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            kst[i] = __builtin_bit_cast(
-                uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(((ld_r + 16 * i) * S.ldk + 8 * ld_c) * 2), 0, 0));
-            vst[i] = __builtin_bit_cast(
-                uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(((4 * ld_r + i) * S.ldv + 8 * ld_c) * 2), 0, 0));
+            const int key = 4 * (4 * wave + i) + kkey0;
+            k_voff[i] = (int)((key * S.ldk + 8 * (kp ^ (key & 15))) * 2);
+            const int d = 8 * (4 * wave + i) + vd0;
+            vt_voff[i] = (int)((d * S.lpad + 8 * (vp ^ ((d ^ (d >> 3)) & 7))) * 2);
         }
     };
-    auto store_tile = [&](int buf) {
+    set_offsets(nS);
+    auto load_tile = [&](const SegState &S, int64_t k0, int buf) {
+        const int64_t rows = min<int64_t>(S.len - k0, BKV);
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(S.k + k0 * S.ldk + head * D, ((rows - 1) * S.ldk + D) * 2);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(S.vt + (int64_t)head * D * S.lpad + k0, (D * S.lpad - k0) * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) k_lds[buf][k_pos(ld_r + 16 * i, ld_c)] = kst[i];
-        // V^T: for channel d = 8 ld_c + e, keys 4 ld_r .. +3 (permuted position)
-        const int kp = kperm(4 * ld_r);
-        uint2 *vt = reinterpret_cast<uint2 *>(&v_lds[buf][0]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int d = 8 * ld_c + e;
-            const int w = e >> 1;
-            const uint32_t x0 = (&vst[0].x)[w], x1 = (&vst[1].x)[w], x2 = (&vst[2].x)[w], x3 = (&vst[3].x)[w];
-            uint2 pk;
-            if (e & 1) {
-                pk.x = perm_hi(x0, x1);
-                pk.y = perm_hi(x2, x3);
-            } else {
-                pk.x = perm_lo(x0, x1);
-                pk.y = perm_lo(x2, x3);
-            }
-            // 8-byte slot: chunk kp / 8, half (kp % 8) / 4
-            vt[2 * vt_pos(d, kp >> 3) + ((kp & 7) >> 2)] = pk;
+        for (int i = 0; i < 4; ++i) {
+            load_slab(rk, &k_lds[buf][64 * (4 * wave + i)], k_voff[i], 0);
+            load_slab(rv, &v_lds[buf][64 * (4 * wave + i)], vt_voff[i], 0);
         }
     };
     auto advance = [&]() {
@@ -201,12 +204,15 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
         if (seg_k0 >= nS.len) {
             ++seg;
             seg_k0 = 0;
-            if (seg < a.n_seg) nS = seg_of(a, seg);
+            if (seg < a.n_seg) {
+                nS = seg_of(a, seg);
+                set_offsets(nS);
+            }
         }
     };
 
-    load_tile(nS, 0);
-    store_tile(0);
+    load_tile(nS, 0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
     int64_t cur_len = nS.len;  // length of the segment the current tile is in
@@ -218,107 +224,102 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
         const bool has_next = it + 1 < n_tiles;
         const int64_t nk0 = seg_k0;
         const int64_t nlen = nS.len;
-        if (has_next) load_tile(nS, nk0);
-        __builtin_amdgcn_sched_barrier(0);
+        if (has_next) load_tile(nS, nk0, buf ^ 1);
 
-        // ---- S^T = K Q^T: sacc[i][j] keys 32i.., queries 32j.. ----
-        f32x16_t sacc[2][2];
+        // The 64-key tile is consumed in two halves of 32 keys: scores S^T
+        // (32 keys x 64 queries), online-softmax update, then O^T += V^T P^T.
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int hb = 0; hb < 2; ++hb) {
+            // ---- S^T = K Q^T: sacc[j] = keys 32 hb .. +31, queries 32 j .. +31 ----
+            f32x16_t sacc[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) sacc[i][j][e] = 0.f;
+                for (int e = 0; e < 16; ++e) sacc[j][e] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const bf16x8_t kop = __builtin_bit_cast(bf16x8_t, k_lds[buf][k_pos(32 * i + l32, 2 * ks + h)]);
+            for (int ks = 0; ks < 8; ++ks) {
+                const bf16x8_t kop = __builtin_bit_cast(bf16x8_t, k_lds[buf][k_pos(32 * hb + l32, 2 * ks + h)]);
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    sacc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[j][ks], sacc[i][j], 0, 0, 0);
+                    sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[j][ks], sacc[j], 0, 0, 0);
             }
-        }
-
-        // ---- mask keys past the segment end (last tile of a segment only) ----
-        if (cur_k0 + BKV > cur_len) {
-            const int valid = (int)(cur_len - cur_k0);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(sacc[j]));  // scores in VGPRs
+
+            // ---- mask keys past the segment end (last tile of a segment only) ----
+            if (cur_k0 + 32 * hb + 32 > cur_len) {
+                const int valid = (int)(cur_len - cur_k0) - 32 * hb;
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
-                        const int key = 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-                        if (key >= valid) sacc[i][j][v] = -__builtin_huge_valf();
+                        const int key = 8 * (v >> 2) + 4 * h + (v & 3);
+                        if (key >= valid) sacc[j][v] = -__builtin_huge_valf();
                     }
-        }
+            }
 
-        // ---- online softmax (exp2 domain) ----
-        bf16x8_t pop[2][4];  // P^T operands: [query tile j][key step s]
-        bool need_rescale = false;
-        float alpha[2];
+            // ---- online softmax (exp2 domain); P^T operands pop[j][s2] ----
+            bf16x8_t pop[2][2];
+            bool need_rescale = false;
+            float alpha[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            float mx = sacc[0][j][0];
+            for (int j = 0; j < 2; ++j) {
+                float mx = sacc[j][0];
 #pragma unroll
-            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sacc[0][j][v]);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[1][j][v]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run[j], mx * a.scale_log2);
-            alpha[j] = __builtin_amdgcn_exp2f(m_run[j] - m_new);
-            need_rescale |= m_new > m_run[j];
-            m_run[j] = m_new;
-            float sum = 0.f;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
+                for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sacc[j][v]);
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float m_new = fmaxf(m_run[j], mx * a.scale_log2);
+                alpha[j] = __builtin_amdgcn_exp2f(m_run[j] - m_new);
+                need_rescale |= m_new > m_run[j];
+                m_run[j] = m_new;
                 float p[16];
+                float sum = 0.f;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i][j][v], a.scale_log2, -m_new));
+                    p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][v], a.scale_log2, -m_new));
                     sum += p[v];
                 }
 #pragma unroll
-                for (int sh = 0; sh < 2; ++sh) {
+                for (int s2 = 0; s2 < 2; ++s2) {
                     uint4 u;
-                    u.x = pack_bf16x2(p[8 * sh + 0], p[8 * sh + 1]);
-                    u.y = pack_bf16x2(p[8 * sh + 2], p[8 * sh + 3]);
-                    u.z = pack_bf16x2(p[8 * sh + 4], p[8 * sh + 5]);
-                    u.w = pack_bf16x2(p[8 * sh + 6], p[8 * sh + 7]);
-                    pop[j][2 * i + sh] = __builtin_bit_cast(bf16x8_t, u);
+                    u.x = pack_bf16x2(p[8 * s2 + 0], p[8 * s2 + 1]);
+                    u.y = pack_bf16x2(p[8 * s2 + 2], p[8 * s2 + 3]);
+                    u.z = pack_bf16x2(p[8 * s2 + 4], p[8 * s2 + 5]);
+                    u.w = pack_bf16x2(p[8 * s2 + 6], p[8 * s2 + 7]);
+                    pop[j][s2] = __builtin_bit_cast(bf16x8_t, u);
                 }
+                l_run[j] = l_run[j] * alpha[j] + sum;
             }
-            l_run[j] = l_run[j] * alpha[j] + sum;
-        }
-        if (__any(need_rescale)) {
+            if (__builtin_expect(__any(need_rescale), 0)) {
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
+                for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                    for (int j = 0; j < 2; ++j)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) oacc[dt][j][e] *= alpha[j];
-        }
+                        for (int e = 0; e < 16; ++e) oacc[dt][j][e] *= alpha[j];
+            }
 
-        // ---- O^T += V^T P^T ----
+            // ---- O^T += V^T P^T over keys 32 hb .. +31 (k-steps s = 2 hb + s2) ----
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+            for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, v_lds[buf][vt_pos(32 * dt + l32, 2 * s + h)]);
+                for (int dt = 0; dt < 4; ++dt) {
+                    const bf16x8_t vop =
+                        __builtin_bit_cast(bf16x8_t, v_lds[buf][vt_pos(32 * dt + l32, 2 * (2 * hb + s2) + h)]);
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    oacc[dt][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[j][s], oacc[dt][j], 0, 0, 0);
+                    for (int j = 0; j < 2; ++j)
+                        oacc[dt][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[j][s2], oacc[dt][j], 0, 0, 0);
+                }
             }
         }
 
         if (has_next) {
-            store_tile(buf ^ 1);
             cur_len = nlen;
             cur_k0 = nk0;
             advance();
         }
-        __syncthreads();
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's slabs landed
+        __syncthreads();                                   // all slabs visible, buf free
     }
 
     // ---- normalise and store: lane holds O[q][32 dt + 8 g + 4 h + (0..3)] ----
@@ -342,21 +343,68 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     }
 }
 
+// V -> V^T staging for one segment: tile of 64 keys x 128 channels of one head
+// through LDS; output rows are channels, keys permuted inside 16-key groups
+// (kperm) and zero-filled past the segment end.
+__global__ __launch_bounds__(256) void vt_transpose_kernel(const uint16_t *v, int64_t ld_v, int64_t len,
+                                                           uint16_t *vt, int64_t lpad) {
+    __shared__ uint16_t tile[BKV][D + 8];  // +8: row stride 272 B
+    const int64_t k0 = (int64_t)blockIdx.x * BKV;
+    const int head = blockIdx.y;
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int idx = t + 256 * j;
+        const int key = idx >> 4, c = idx & 15;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (k0 + key < len) val = *reinterpret_cast<const uint4 *>(v + (k0 + key) * ld_v + head * D + 8 * c);
+        *reinterpret_cast<uint4 *>(&tile[key][8 * c]) = val;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int idx = t + 256 * j;
+        const int d = idx >> 3, c = idx & 7;
+        uint16_t e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = tile[kperm(8 * c + i)][d];
+        uint4 out;
+        out.x = e[0] | ((uint32_t)e[1] << 16);
+        out.y = e[2] | ((uint32_t)e[3] << 16);
+        out.z = e[4] | ((uint32_t)e[5] << 16);
+        out.w = e[6] | ((uint32_t)e[7] << 16);
+        *reinterpret_cast<uint4 *>(vt + ((int64_t)head * D + d) * lpad + k0 + 8 * c) = out;
+    }
+}
+
 }  // namespace
 
 void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k, const uint16_t *v,
                       int64_t ld_v, uint16_t *o, int64_t ld_o, int64_t L_buf, int64_t valid_len, int32_t heads,
-                      float softmax_scale, const h3_qgroup *groups, int32_t n_groups, hipStream_t stream) {
+                      float softmax_scale, const h3_qgroup *groups, int32_t n_groups, void *workspace,
+                      hipStream_t stream) {
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
     // The dense case is one group over [0, valid_len) attending to keys [0, valid_len).
     h3_qgroup dense = {};
-    if (groups == nullptr) {
+    const bool is_dense = groups == nullptr;
+    if (is_dense) {
         dense.q_begin = 0;
         dense.q_end = valid_len;
         dense.n_seg = 1;
         dense.seg[0] = h3_kv_seg{nullptr, nullptr, 0, 0, valid_len};
         groups = &dense;
         n_groups = valid_len > 0 ? 1 : 0;
+    }
+    // Stage V^T once per distinct segment.
+    VtPlan plan;
+    vt_plan(is_dense ? nullptr : groups, is_dense ? 0 : n_groups, valid_len, heads, &plan);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    for (int i = 0; i < plan.n; ++i) {
+        const VtSeg &e = plan.seg[i];
+        const uint16_t *src = e.own ? v + e.begin * ld_v : e.v + e.begin * e.ld;
+        const int64_t ld = e.own ? ld_v : e.ld;
+        vt_transpose_kernel<<<dim3((unsigned)(e.lpad / BKV), (unsigned)heads), 256, 0, stream>>>(
+            src, ld, e.len, reinterpret_cast<uint16_t *>(ws + e.off), e.lpad);
     }
     std::pair<int64_t, int64_t> cov[H3_MAX_GROUPS];
     int nc = 0;
@@ -376,17 +424,16 @@ void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_
         a.scale_log2 = scale * 1.4426950408889634f;
         for (int s = 0; s < g.n_seg; ++s) {
             const h3_kv_seg &ss = g.seg[s];
+            const VtSeg &e = plan.seg[plan.map[gi][s]];
             if (ss.k == nullptr) {
                 a.sk[s] = k + ss.begin * ld_k;
-                a.sv[s] = v + ss.begin * ld_v;
                 a.sldk[s] = ld_k;
-                a.sldv[s] = ld_v;
             } else {
                 a.sk[s] = ss.k + ss.begin * ss.ld;
-                a.sv[s] = ss.v + ss.begin * ss.ld;
                 a.sldk[s] = ss.ld;
-                a.sldv[s] = ss.ld;
             }
+            a.svt[s] = reinterpret_cast<const uint16_t *>(ws + e.off);
+            a.slpad[s] = e.lpad;
             a.slen[s] = ss.len;
         }
         attention_fwd_kernel<<<dim3((unsigned)(a.tiles_per_head * heads)), kThreads, 0, stream>>>(a);
@@ -408,12 +455,12 @@ using namespace h3;
 extern "C" int h3_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k, const uint16_t *v,
                             int64_t ld_v, uint16_t *o, int64_t ld_o, int64_t L_buf, int64_t valid_len,
                             int32_t heads, int32_t head_dim, float softmax_scale, const h3_qgroup *groups,
-                            int32_t n_groups, void *stream) {
+                            int32_t n_groups, void *workspace, size_t ws_bytes, void *stream) {
     int s = h3_check_attention(q, ld_q, k, ld_k, v, ld_v, o, ld_o, L_buf, valid_len, heads, head_dim,
-                               softmax_scale, groups, n_groups);
+                               softmax_scale, groups, n_groups, workspace, ws_bytes);
     if (s != H3_OK || L_buf == 0) return s;
     if ((s = device_check()) != H3_OK) return s;
     launch_attention(q, ld_q, k, ld_k, v, ld_v, o, ld_o, L_buf, valid_len, heads, softmax_scale, groups, n_groups,
-                     (hipStream_t)stream);
+                     workspace, (hipStream_t)stream);
     return launch_status();
 }

@@ -30,7 +30,7 @@ extern "C" int h3_block_forward(const h3_dims *dims, const h3_block_weights *w, 
     const hipStream_t st = (hipStream_t)stream;
 
     WsLayout l;
-    ws_layout(dims, L_buf, &l);
+    ws_layout(dims, L_buf, groups, n_groups, &l);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     uint16_t *h = reinterpret_cast<uint16_t *>(ws + l.off[H3_WS_H]);
     uint16_t *qkv = reinterpret_cast<uint16_t *>(ws + l.off[H3_WS_QKV]);
@@ -38,6 +38,7 @@ extern "C" int h3_block_forward(const h3_dims *dims, const h3_block_weights *w, 
     uint16_t *x1 = reinterpret_cast<uint16_t *>(ws + l.off[H3_WS_X1]);
     uint16_t *h2 = reinterpret_cast<uint16_t *>(ws + l.off[H3_WS_H2]);
     uint16_t *g = reinterpret_cast<uint16_t *>(ws + l.off[H3_WS_G]);
+    void *vt = ws + l.off[H3_WS_VT];
 
     const int64_t H = dims->hidden, F = dims->ffn, V = valid_len;
     const int64_t ldm = 6 * H;  // floats between modulation-table entries
@@ -56,7 +57,7 @@ extern "C" int h3_block_forward(const h3_dims *dims, const h3_block_weights *w, 
                         dims->rope_pairing, dims->rope_theta, dims->eps, st);
     // 4 o
     launch_attention(qkv, 3 * H, qkv + H, 3 * H, qkv + 2 * H, 3 * H, o, H, L_buf, V, dims->heads, 0.0f, groups,
-                     n_groups, st);
+                     n_groups, vt, st);
     // 5 x1 = x + gate_a * (o W_o^T)
     launch_linear(o, H, w->w_o, H, w->b_o, x1, H, V, H, H, H3_EPI_RESIDUAL, x, H, gate_a, ldm, n_mod_groups, mod_idx,
                   st);

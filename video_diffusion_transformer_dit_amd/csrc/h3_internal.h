@@ -13,6 +13,24 @@ constexpr int64_t kHeadDim = 128;
 constexpr int64_t kMaxHidden = 16384;
 constexpr size_t kWsAlign = 256;
 
+// Attention stages each distinct K/V segment's V transposed per head in the
+// workspace: [heads][128][lpad] BF16 with lpad = len rounded up to 64.
+// Segments are identified by (own rows or external pointer, stride, begin, len).
+struct VtSeg {
+    int own;              // rows of the call's own K/V
+    const uint16_t *v;    // external V (own == 0)
+    int64_t ld, begin, len, lpad;
+    int64_t off;          // byte offset inside the V^T staging area
+};
+struct VtPlan {
+    int n;
+    VtSeg seg[H3_MAX_GROUPS * H3_MAX_SEGMENTS];
+    int map[H3_MAX_GROUPS][H3_MAX_SEGMENTS];  // (group, segment) -> seg index
+    size_t bytes;
+};
+// groups == NULL plans one own segment [0, dense_len).
+void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads, VtPlan *out);
+
 // Byte offsets and row strides of the block's workspace buffers.
 struct WsLayout {
     int64_t off[H3_WS_COUNT];
@@ -20,7 +38,7 @@ struct WsLayout {
     int64_t cols[H3_WS_COUNT];
     size_t total;
 };
-bool ws_layout(const h3_dims *d, int64_t L_buf, WsLayout *out);
+bool ws_layout(const h3_dims *d, int64_t L_buf, const h3_qgroup *groups, int n_groups, WsLayout *out);
 
 // Validation of dims shared by several checks.
 int check_dims(const h3_dims *d);

@@ -38,6 +38,6 @@ void launch_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ld
 void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k,
                       const uint16_t *v, int64_t ld_v, uint16_t *o, int64_t ld_o, int64_t L_buf,
                       int64_t valid_len, int32_t heads, float softmax_scale, const h3_qgroup *groups,
-                      int32_t n_groups, hipStream_t stream);
+                      int32_t n_groups, void *workspace, hipStream_t stream);
 
 }  // namespace h3

@@ -89,19 +89,51 @@ int check_dims(const h3_dims *d) {
     return H3_OK;
 }
 
-bool ws_layout(const h3_dims *d, int64_t L_buf, WsLayout *out) {
+void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads, VtPlan *out) {
+    out->n = 0;
+    out->bytes = 0;
+    auto add = [&](int own, const uint16_t *v, int64_t ld, int64_t begin, int64_t len) {
+        for (int i = 0; i < out->n; ++i) {
+            const VtSeg &e = out->seg[i];
+            if (e.own == own && e.v == v && e.ld == ld && e.begin == begin && e.len == len) return i;
+        }
+        VtSeg &e = out->seg[out->n];
+        e.own = own; e.v = v; e.ld = ld; e.begin = begin; e.len = len;
+        e.lpad = (len + 63) / 64 * 64;
+        e.off = (int64_t)out->bytes;
+        out->bytes += (size_t)heads * kHeadDim * e.lpad * 2;
+        return out->n++;
+    };
+    if (groups == nullptr) {
+        if (dense_len > 0) out->map[0][0] = add(1, nullptr, 0, 0, dense_len);
+        return;
+    }
+    for (int g = 0; g < n_groups && g < H3_MAX_GROUPS; ++g)
+        for (int s = 0; s < groups[g].n_seg && s < H3_MAX_SEGMENTS; ++s) {
+            const h3_kv_seg &x = groups[g].seg[s];
+            out->map[g][s] = x.k == nullptr ? add(1, nullptr, 0, x.begin, x.len) : add(0, x.v, x.ld, x.begin, x.len);
+        }
+}
+
+bool ws_layout(const h3_dims *d, int64_t L_buf, const h3_qgroup *groups, int n_groups, WsLayout *out) {
     if (check_dims(d) != H3_OK || L_buf < 0) return false;
+    if (groups != nullptr && (n_groups < 1 || n_groups > H3_MAX_GROUPS)) return false;
     const int64_t H = d->hidden, F = d->ffn;
-    const int64_t cols[H3_WS_COUNT] = {H, 3 * H, H, H, H, F};
+    const int64_t cols[H3_WS_COUNT - 1] = {H, 3 * H, H, H, H, F};
     int64_t off = 0;
-    for (int i = 0; i < H3_WS_COUNT; ++i) {
+    auto align = [](int64_t b) { return (b + (int64_t)kWsAlign - 1) / (int64_t)kWsAlign * (int64_t)kWsAlign; };
+    for (int i = 0; i < H3_WS_COUNT - 1; ++i) {
         out->off[i] = off;
         out->ld[i] = cols[i];
         out->cols[i] = cols[i];
-        int64_t bytes = L_buf * cols[i] * kBf16;
-        bytes = (bytes + (int64_t)kWsAlign - 1) / (int64_t)kWsAlign * (int64_t)kWsAlign;
-        off += bytes;
+        off += align(L_buf * cols[i] * kBf16);
     }
+    VtPlan p;
+    vt_plan(groups, n_groups, L_buf, d->heads, &p);
+    out->off[H3_WS_VT] = off;
+    out->ld[H3_WS_VT] = (int64_t)p.bytes;
+    out->cols[H3_WS_VT] = 0;
+    off += align((int64_t)p.bytes);
     out->total = (size_t)off;
     return true;
 }
@@ -129,19 +161,28 @@ const char *h3_status_string(int s) {
 
 int h3_abi_version(void) { return H3_ABI_VERSION; }
 
-size_t h3_block_workspace_bytes(const h3_dims *dims, int64_t L_buf) {
+size_t h3_block_workspace_bytes(const h3_dims *dims, int64_t L_buf, const h3_qgroup *groups, int32_t n_groups) {
     WsLayout l;
-    if (!ws_layout(dims, L_buf, &l)) return 0;
+    if (!ws_layout(dims, L_buf, groups, n_groups, &l)) return 0;
     return l.total;
 }
 
-int h3_block_workspace_layout(const h3_dims *dims, int64_t L_buf, int64_t offsets[H3_WS_COUNT],
-                              int64_t lds[H3_WS_COUNT]) {
+size_t h3_attention_workspace_bytes(int64_t valid_len, int32_t heads, const h3_qgroup *groups,
+                                    int32_t n_groups) {
+    if (valid_len < 0 || heads <= 0) return 0;
+    if (groups != nullptr && (n_groups < 1 || n_groups > H3_MAX_GROUPS)) return 0;
+    VtPlan p;
+    vt_plan(groups, n_groups, valid_len, heads, &p);
+    return p.bytes;
+}
+
+int h3_block_workspace_layout(const h3_dims *dims, int64_t L_buf, const h3_qgroup *groups, int32_t n_groups,
+                              int64_t offsets[H3_WS_COUNT], int64_t lds[H3_WS_COUNT]) {
     if (offsets == nullptr || lds == nullptr) return H3_ERR_NULL;
     H3_TRY(check_dims(dims));
     if (L_buf < 0) return H3_ERR_SHAPE;
     WsLayout l;
-    ws_layout(dims, L_buf, &l);
+    if (!ws_layout(dims, L_buf, groups, n_groups, &l)) return H3_ERR_SHAPE;
     for (int i = 0; i < H3_WS_COUNT; ++i) {
         offsets[i] = l.off[i];
         lds[i] = l.ld[i];
@@ -259,7 +300,7 @@ int h3_check_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t l
 int h3_check_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k,
                        const uint16_t *v, int64_t ld_v, const uint16_t *o, int64_t ld_o, int64_t L_buf,
                        int64_t valid_len, int32_t heads, int32_t head_dim, float softmax_scale,
-                       const h3_qgroup *groups, int32_t n_groups) {
+                       const h3_qgroup *groups, int32_t n_groups, const void *workspace, size_t ws_bytes) {
     H3_TRY(check_rows(L_buf, valid_len));
     if (heads <= 0 || head_dim <= 0) return H3_ERR_SHAPE;
     if (head_dim != kHeadDim) return H3_ERR_UNSUPPORTED;
@@ -305,6 +346,21 @@ int h3_check_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64
         for (size_t i = 1; i < spans.size(); ++i)
             if (spans[i].first < spans[i - 1].second) return H3_ERR_SHAPE;
     }
+    // V^T staging workspace
+    VtPlan plan;
+    vt_plan(groups, n_groups, valid_len, heads, &plan);
+    if (plan.bytes > 0) {
+        if (workspace == nullptr || ws_bytes < plan.bytes) return H3_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0) return H3_ERR_ALIGN;
+        const Mat mw = mat(workspace, 1, (int64_t)plan.bytes, (int64_t)plan.bytes, 1);
+        if (overlap(mw, mo) || overlap(mw, mat(q, L_buf, H, ld_q)) || overlap(mw, mat(k, L_buf, H, ld_k)) ||
+            overlap(mw, mat(v, L_buf, H, ld_v)))
+            return H3_ERR_ALIAS;
+        for (int i = 0; i < plan.n; ++i) {
+            const VtSeg &e = plan.seg[i];
+            if (!e.own && overlap(mw, mat(e.v + e.begin * e.ld, e.len, H, e.ld))) return H3_ERR_ALIAS;
+        }
+    }
     return H3_OK;
 }
 
@@ -333,7 +389,7 @@ int h3_check_block_forward(const h3_dims *dims, const h3_block_weights *w, const
         if (p && !aligned16(p)) return H3_ERR_ALIGN;
     // workspace
     WsLayout l;
-    ws_layout(dims, L_buf, &l);
+    if (!ws_layout(dims, L_buf, groups, n_groups, &l)) return H3_ERR_SHAPE;
     if (workspace == nullptr || ws_bytes < l.total) return H3_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0) return H3_ERR_ALIGN;
     const Mat mx = mat(x, L_buf, H, H), my = mat(y, L_buf, H, H);

@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(_PKG, "libh3block.so")
 H3_OK, H3_ERR_NULL, H3_ERR_SHAPE, H3_ERR_UNSUPPORTED, H3_ERR_ALIGN, H3_ERR_ALIAS, \
     H3_ERR_WORKSPACE, H3_ERR_DEVICE, H3_ERR_HIP = range(9)
 H3_EPI_STORE, H3_EPI_RESIDUAL, H3_EPI_SWIGLU = range(3)
-H3_WS_H, H3_WS_QKV, H3_WS_O, H3_WS_X1, H3_WS_H2, H3_WS_G = range(6)
-H3_WS_COUNT = 6
+H3_WS_H, H3_WS_QKV, H3_WS_O, H3_WS_X1, H3_WS_H2, H3_WS_G, H3_WS_VT = range(7)
+H3_WS_COUNT = 7
 H3_MAX_SEGMENTS = 4
 H3_MAX_GROUPS = 8
 
@@ -71,8 +71,11 @@ def _load():
                              C.POINTER(QGroup), I32, C.POINTER(KvExport), P, SZ, P],
         "h3_check_block_forward": [C.POINTER(Dims), C.POINTER(BlockWeights), P, P, P, I32, P, P, I64, I64,
                                    C.POINTER(QGroup), I32, C.POINTER(KvExport), P, SZ],
-        "h3_attention": [P, I64, P, I64, P, I64, P, I64, I64, I64, I32, I32, F32, C.POINTER(QGroup), I32, P],
-        "h3_check_attention": [P, I64, P, I64, P, I64, P, I64, I64, I64, I32, I32, F32, C.POINTER(QGroup), I32],
+        "h3_attention": [P, I64, P, I64, P, I64, P, I64, I64, I64, I32, I32, F32, C.POINTER(QGroup), I32, P, SZ,
+                         P],
+        "h3_check_attention": [P, I64, P, I64, P, I64, P, I64, I64, I64, I32, I32, F32, C.POINTER(QGroup), I32,
+                               P, SZ],
+        "h3_attention_workspace_bytes": [I64, I32, C.POINTER(QGroup), I32],
         "h3_fused_modulate_norm": [P, I64, P, I64, P, P, P, I64, I32, P, P, I64, P, I64, I64, I64, I32, F32, I32, P],
         "h3_check_fused_modulate_norm": [P, I64, P, I64, P, P, P, I64, I32, P, I64, P, I64, I64, I64, I32, F32,
                                          I32],
@@ -82,8 +85,9 @@ def _load():
         "h3_check_swiglu": [P, I64, P, I64, I64, I64, I32],
         "h3_linear": [P, I64, P, I64, P, P, I64, I64, I64, I64, I64, I32, P, I64, P, I64, I32, P, P],
         "h3_check_linear": [P, I64, P, I64, P, I64, I64, I64, I64, I64, I32, P, I64, P, I32],
-        "h3_block_workspace_bytes": [C.POINTER(Dims), I64],
-        "h3_block_workspace_layout": [C.POINTER(Dims), I64, C.POINTER(I64), C.POINTER(I64)],
+        "h3_block_workspace_bytes": [C.POINTER(Dims), I64, C.POINTER(QGroup), I32],
+        "h3_block_workspace_layout": [C.POINTER(Dims), I64, C.POINTER(QGroup), I32, C.POINTER(I64),
+                                      C.POINTER(I64)],
         "h3_status_string": [C.c_int],
         "h3_abi_version": [],
     }
@@ -92,13 +96,14 @@ def _load():
         f.argtypes = args
         f.restype = C.c_int
     lib.h3_block_workspace_bytes.restype = C.c_size_t
+    lib.h3_attention_workspace_bytes.restype = C.c_size_t
     lib.h3_status_string.restype = C.c_char_p
     return lib
 
 
 LIB = _load()
 EXPORTS = ["h3_block_forward", "h3_attention", "h3_fused_modulate_norm", "h3_qk_norm_rope", "h3_swiglu",
-           "h3_linear", "h3_block_workspace_bytes", "h3_block_workspace_layout", "h3_status_string",
+           "h3_linear", "h3_attention_workspace_bytes", "h3_block_workspace_bytes", "h3_block_workspace_layout", "h3_status_string",
            "h3_abi_version", "h3_check_block_forward", "h3_check_attention", "h3_check_fused_modulate_norm",
            "h3_check_qk_norm_rope", "h3_check_swiglu", "h3_check_linear"]
 
@@ -161,15 +166,22 @@ def make_groups(groups):
     return arr, len(groups)
 
 
-def workspace_bytes(dims: Dims, L_buf: int) -> int:
-    return int(LIB.h3_block_workspace_bytes(C.byref(dims), L_buf))
+def workspace_bytes(dims: Dims, L_buf: int, groups=None) -> int:
+    garr, ng = make_groups(groups)
+    return int(LIB.h3_block_workspace_bytes(C.byref(dims), L_buf, garr, ng))
 
 
-def workspace_layout(dims: Dims, L_buf: int):
+def workspace_layout(dims: Dims, L_buf: int, groups=None):
+    garr, ng = make_groups(groups)
     off = (C.c_int64 * H3_WS_COUNT)()
     lds = (C.c_int64 * H3_WS_COUNT)()
-    _ok(LIB.h3_block_workspace_layout(C.byref(dims), L_buf, off, lds), "h3_block_workspace_layout")
+    _ok(LIB.h3_block_workspace_layout(C.byref(dims), L_buf, garr, ng, off, lds), "h3_block_workspace_layout")
     return list(off), list(lds)
+
+
+def attention_workspace_bytes(valid_len: int, heads: int, groups=None) -> int:
+    garr, ng = make_groups(groups)
+    return int(LIB.h3_attention_workspace_bytes(valid_len, heads, garr, ng))
 
 
 def block_forward(dims: Dims, weights: BlockWeights, x, y, mod, n_mod_groups, valid_len, workspace,
@@ -186,10 +198,17 @@ def block_forward(dims: Dims, weights: BlockWeights, x, y, mod, n_mod_groups, va
     _ok(s, "h3_block_forward")
 
 
-def attention(q, k, v, o, valid_len, heads, softmax_scale=0.0, groups=None, stream=None):
+def attention(q, k, v, o, valid_len, heads, softmax_scale=0.0, groups=None, workspace=None, stream=None):
+    """workspace: uint8 device tensor of at least attention_workspace_bytes(...)
+    bytes, or None to allocate one here (torch's caching allocator)."""
     garr, ng = make_groups(groups)
+    if workspace is None:
+        import torch
+        workspace = torch.empty(max(attention_workspace_bytes(valid_len, heads, groups), 1), dtype=torch.uint8,
+                                device=q.device)
     s = LIB.h3_attention(_ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0), _ptr(o), o.stride(0),
-                         q.shape[0], valid_len, heads, 128, softmax_scale, garr, ng, _stream(stream))
+                         q.shape[0], valid_len, heads, 128, softmax_scale, garr, ng, _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _stream(stream))
     _ok(s, "h3_attention")
 
 
