@@ -157,8 +157,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(oacc[i][j]));
-    float m_run[2] = {-__builtin_huge_valf(), -__builtin_huge_valf()};
+        for (int j = 0; j < 2; ++j) asm volatile("" : "+a"(oacc[i][j]));  // O lives in AGPRs
     float l_run[2] = {0.f, 0.f};
 
     // ---- K / V^T tile loader (direct to LDS). A tile is 16 slabs of K (4 keys
@@ -218,108 +217,173 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     int64_t cur_len = nS.len;  // length of the segment the current tile is in
     int64_t cur_k0 = 0;
     advance();
+
+    // Softmax with a per-row reference maximum m_ref (exp2 domain): p =
+    // exp2(s c - m_ref) stays <= 2^kSlack while no score exceeds m_ref + kSlack,
+    // so the hot loop never rescales O. A tile whose maximum would break that
+    // bound makes the wave leave the inner loop before any P.V of the tile,
+    // rescale O and l to the new maximum and redo the tile (always at the
+    // first tile, rarely afterwards). The redone tile re-issues the same
+    // prefetch (identical bytes) and reaches the same barriers, so every wave
+    // still passes the same number of barriers.
+    constexpr float kSlack = 10.0f;
+    float m_ref[2] = {-__builtin_huge_valf(), -__builtin_huge_valf()};
+    int it = 0;
 #pragma unroll 1
-    for (int it = 0; it < n_tiles; ++it) {
-        const int buf = it & 1;
-        const bool has_next = it + 1 < n_tiles;
-        const int64_t nk0 = seg_k0;
-        const int64_t nlen = nS.len;
-        if (has_next) load_tile(nS, nk0, buf ^ 1);
+    while (true) {
+        bool brk = false;
+        float tmax[2];
+#pragma unroll 1
+        for (; it < n_tiles; ++it) {
+            const int buf = it & 1;
+            const bool has_next = it + 1 < n_tiles;
+            const int64_t nk0 = seg_k0;
+            const int64_t nlen = nS.len;
+            if (has_next) load_tile(nS, nk0, buf ^ 1);
 
-        // The 64-key tile is consumed in two halves of 32 keys: scores S^T
-        // (32 keys x 64 queries), online-softmax update, then O^T += V^T P^T.
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-            // ---- S^T = K Q^T: sacc[j] = keys 32 hb .. +31, queries 32 j .. +31 ----
-            f32x16_t sacc[2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) sacc[j][e] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const bf16x8_t kop = __builtin_bit_cast(bf16x8_t, k_lds[buf][k_pos(32 * hb + l32, 2 * ks + h)]);
+            auto qk = [&](int hb, f32x16_t (&sacc)[2]) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[j][ks], sacc[j], 0, 0, 0);
-            }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(sacc[j]));  // scores in VGPRs
-
-            // ---- mask keys past the segment end (last tile of a segment only) ----
-            if (cur_k0 + 32 * hb + 32 > cur_len) {
-                const int valid = (int)(cur_len - cur_k0) - 32 * hb;
+                    for (int e = 0; e < 16; ++e) sacc[j][e] = 0.f;
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int ks = 0; ks < 8; ++ks) {
+                    const bf16x8_t kop =
+                        __builtin_bit_cast(bf16x8_t, k_lds[buf][k_pos(32 * hb + l32, 2 * ks + h)]);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[j][ks], sacc[j], 0, 0, 0);
+                }
+            };
+            auto mask = [&](int hb, f32x16_t (&sacc)[2]) {
+                if (cur_k0 + 32 * hb + 32 > cur_len) {  // keys past the segment end
+                    const int valid = (int)(cur_len - cur_k0) - 32 * hb;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const int key = 8 * (v >> 2) + 4 * h + (v & 3);
+                            if (key >= valid) sacc[j][v] = -__builtin_huge_valf();
+                        }
+                }
+            };
+            auto rowmax = [&](const f32x16_t (&sacc)[2], float (&mx)[2]) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    float m = sacc[j][0];
+#pragma unroll
+                    for (int v = 1; v < 16; ++v) m = fmaxf(m, sacc[j][v]);
+                    mx[j] = m;
+                }
+            };
+            // P = exp2(s c - m_ref) packed to BF16; row sums returned in `sums`
+            // (committed to l only once the tile is known not to be redone).
+            auto expo = [&](const f32x16_t (&sacc)[2], bf16x8_t (&pop)[2][2], float (&sums)[2]) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    float p[16];
+                    float sum = 0.f;
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
-                        const int key = 8 * (v >> 2) + 4 * h + (v & 3);
-                        if (key >= valid) sacc[j][v] = -__builtin_huge_valf();
+                        p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][v], a.scale_log2, -m_ref[j]));
+                        sum += p[v];
                     }
-            }
-
-            // ---- online softmax (exp2 domain); P^T operands pop[j][s2] ----
-            bf16x8_t pop[2][2];
-            bool need_rescale = false;
-            float alpha[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                float mx = sacc[j][0];
-#pragma unroll
-                for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sacc[j][v]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float m_new = fmaxf(m_run[j], mx * a.scale_log2);
-                alpha[j] = __builtin_amdgcn_exp2f(m_run[j] - m_new);
-                need_rescale |= m_new > m_run[j];
-                m_run[j] = m_new;
-                float p[16];
-                float sum = 0.f;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][v], a.scale_log2, -m_new));
-                    sum += p[v];
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        uint4 u;
+                        u.x = pack_bf16x2(p[8 * s2 + 0], p[8 * s2 + 1]);
+                        u.y = pack_bf16x2(p[8 * s2 + 2], p[8 * s2 + 3]);
+                        u.z = pack_bf16x2(p[8 * s2 + 4], p[8 * s2 + 5]);
+                        u.w = pack_bf16x2(p[8 * s2 + 6], p[8 * s2 + 7]);
+                        pop[j][s2] = __builtin_bit_cast(bf16x8_t, u);
+                    }
+                    sums[j] = sum;
                 }
+            };
+            auto pv = [&](int hb, const bf16x8_t (&pop)[2][2]) {
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
-                    uint4 u;
-                    u.x = pack_bf16x2(p[8 * s2 + 0], p[8 * s2 + 1]);
-                    u.y = pack_bf16x2(p[8 * s2 + 2], p[8 * s2 + 3]);
-                    u.z = pack_bf16x2(p[8 * s2 + 4], p[8 * s2 + 5]);
-                    u.w = pack_bf16x2(p[8 * s2 + 6], p[8 * s2 + 7]);
-                    pop[j][s2] = __builtin_bit_cast(bf16x8_t, u);
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt) {
+                        const bf16x8_t vop =
+                            __builtin_bit_cast(bf16x8_t, v_lds[buf][vt_pos(32 * dt + l32, 2 * (2 * hb + s2) + h)]);
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            oacc[dt][j] =
+                                __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[j][s2], oacc[dt][j], 0, 0, 0);
+                    }
                 }
-                l_run[j] = l_run[j] * alpha[j] + sum;
-            }
-            if (__builtin_expect(__any(need_rescale), 0)) {
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) oacc[dt][j][e] *= alpha[j];
-            }
+            };
+            // Interleave each MFMA with a few VALU instructions of the other
+            // half's softmax and the LDS operand read it needs.
+#define H3_INTERLEAVE(VALU)                                           \
+    do {                                                              \
+        _Pragma("unroll") for (int i_ = 0; i_ < 16; ++i_) {           \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        \
+            __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);     \
+        }                                                             \
+    } while (0)
 
-            // ---- O^T += V^T P^T over keys 32 hb .. +31 (k-steps s = 2 hb + s2) ----
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                    const bf16x8_t vop =
-                        __builtin_bit_cast(bf16x8_t, v_lds[buf][vt_pos(32 * dt + l32, 2 * (2 * hb + s2) + h)]);
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        oacc[dt][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[j][s2], oacc[dt][j], 0, 0, 0);
-                }
+            f32x16_t s0[2], s1[2];
+            bf16x8_t p0[2][2], p1[2][2];
+            float mx0[2], mx1[2], sum0[2], sum1[2];
+            qk(0, s0);                                   // A: S0
+            mask(0, s0);
+            {                                            // B: S1 || max(S0), P0
+                qk(1, s1);
+                rowmax(s0, mx0);
+                expo(s0, p0, sum0);
+                H3_INTERLEAVE(8);
             }
-        }
+            mask(1, s1);
+            rowmax(s1, mx1);
+            bool over = false;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                float m = fmaxf(mx0[j], mx1[j]);
+                m = fmaxf(m, __shfl_xor(m, 32)) * a.scale_log2;
+                tmax[j] = m;
+                over |= m > m_ref[j] + kSlack;
+            }
+            if (__any(over)) {  // leave before any P.V of this tile
+                brk = true;
+                break;
+            }
+            {                                            // C: O += V0 P0 || P1
+                pv(0, p0);
+                expo(s1, p1, sum1);
+                H3_INTERLEAVE(7);
+            }
+            pv(1, p1);                                   // D: O += V1 P1
+#pragma unroll
+            for (int j = 0; j < 2; ++j) l_run[j] += sum0[j] + sum1[j];
 
-        if (has_next) {
-            cur_len = nlen;
-            cur_k0 = nk0;
-            advance();
+            if (has_next) {
+                cur_len = nlen;
+                cur_k0 = nk0;
+                advance();
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's slabs landed
+            __syncthreads();                                   // all slabs visible, buf free
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's slabs landed
-        __syncthreads();                                   // all slabs visible, buf free
+        if (!brk) break;
+        // Rare path: raise the reference maximum and rescale O and l.
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float m_new = fmaxf(m_ref[j], tmax[j]);
+            const float alpha = __builtin_amdgcn_exp2f(m_ref[j] - m_new);
+            m_ref[j] = m_new;
+            l_run[j] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) oacc[dt][j][e] *= alpha;
+        }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) asm volatile("" : "+a"(oacc[dt][j]));
     }
 
     // ---- normalise and store: lane holds O[q][32 dt + 8 g + 4 h + (0..3)] ----
