@@ -45,6 +45,25 @@ def elementwise_bytes(V: int, H: int, F: int):
     return {"modnorm": 4.0 * V * H, "qk_norm_rope": 8.0 * V * H, "modnorm2": 4.0 * V * H}
 
 
+def counter_traffic(kernel: str, source: str):
+    """HBM-side bytes per dispatch of `kernel` from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary (profiles/counters.json, already scaled by
+    the copy calibration), or None when the kernel's source has changed since
+    the counters were taken."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "counters.json")) as f:
+            c = json.load(f)
+        with open(os.path.join(ROOT, "video_diffusion_transformer_dit_amd", "csrc", source), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()[:16]
+        if c["source_sha256_16"].get(source) != sha:
+            return None
+        k = c["kernels"][kernel]
+        return int(k["read_bytes"] + k["write_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def time_calls(torch, fn, iters: int, warmup: int) -> float:
     """Average ms per call with HIP events on the current stream."""
     for _ in range(warmup):
@@ -96,6 +115,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-iters", type=int, default=5)
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run one plain 1 GiB device-to-device copy (the known-size reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); this build has no multi-GPU path.",
@@ -200,9 +222,17 @@ def main(argv=None) -> int:
         "kernels": kernels,
         "roofline": {"kernel": "attention_fwd_kernel", "bound": "mfma", "achieved": round(attn_tf, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": counter_traffic("attention_fwd_kernel", "attention.hip"),
+                     "traffic_unit": "bytes per launch (FETCH_SIZE x2 + WRITE_SIZE x1, copy-calibrated)",
                      "work_per_launch": "4 * 58758^2 * 5376 = 7.424e13 flop (QK^T and PV over valid rows)"},
     }
+    if a.calibration_copy:
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)   # 1 GiB
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calibration_copy_bytes"] = int(src.numel() * 2)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
