@@ -118,7 +118,7 @@ def test_swiglu(F, L, V):
 # projections (MFMA GEMM) with their epilogues
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("M,Mv,N,K", [(300, 291, 512, 256), (600, 599, 768, 5376), (64, 1, 256, 64),
-                                      (257, 257, 264, 128)])
+                                      (257, 257, 264, 128), (130, 129, 256, 192)])
 @pytest.mark.parametrize("bias", [False, True])
 def test_linear_store(M, Mv, N, K, bias):
     _say(f"linear store M={M} Mv={Mv} N={N} K={K} bias={bias}")
@@ -133,7 +133,8 @@ def test_linear_store(M, Mv, N, K, bias):
     assert_zero_rows(c, Mv, "c")
 
 
-@pytest.mark.parametrize("M,Mv,N,K,G", [(300, 291, 512, 256, 1), (520, 515, 5376, 512, 3)])
+@pytest.mark.parametrize("M,Mv,N,K,G", [(300, 291, 512, 256, 1), (520, 515, 5376, 512, 3),
+                                           (70, 66, 256, 320, 2)])
 def test_linear_gated_residual(M, Mv, N, K, G):
     _say(f"linear residual M={M} N={N} K={K} G={G}")
     ab = I.normal_bf16("lr.a", (M, K))

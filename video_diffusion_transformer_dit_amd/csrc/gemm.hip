@@ -11,12 +11,15 @@
 //                    [M, 2F] intermediate never reaches HBM.
 //
 // Tiling (CDNA4): 256 x 256 output tile per 256-thread workgroup, 4 wavefronts
-// of 128 x 128, K step 64, v_mfma_f32_32x32x16_bf16. The weight tile is the
+// of 128 x 128, K step 32, v_mfma_f32_32x32x16_bf16. The weight tile is the
 // MFMA A operand and the activation tile the B operand, so each lane's
 // accumulator holds groups of 4 consecutive output columns of one row
 // (8-byte stores).
-// LDS holds two stages of both tiles (128 KB) with a 16-byte-chunk XOR swizzle
-// (chunk c of row r at c ^ (r & 7)): conflict-free 128-bit reads and writes.
+// Operand tiles go global -> LDS directly (buffer loads with the LDS bit, no
+// register staging) through a 4-stage ring of 2 x 16 KB slots (128 KB): three
+// K steps are in flight while the fourth is consumed, with explicit vmcnt
+// waits, so a step waits only for its own stage. A 16-byte-chunk XOR swizzle
+// keeps the 128-bit LDS reads conflict-free.
 // Tiles are ordered so each XCD (workgroups are dealt round-robin over 8 XCDs)
 // walks a contiguous range of a grouped tile order, keeping the operand
 // K-slices its 32 CUs share in that XCD's L2.
@@ -26,11 +29,12 @@
 namespace h3 {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256, BK = 32;
 constexpr int kThreads = 256;
-constexpr int kChunksPerRow = BK / 8;                    // 8 x 16 B
-constexpr int kTileChunks = BM * kChunksPerRow;           // 2048 per operand tile
-constexpr int kLoadsPerThread = kTileChunks / kThreads;   // 8
+constexpr int kStages = 4;                                // LDS ring depth
+constexpr int kChunksPerRow = BK / 8;                     // 4 x 16 B per tile row
+constexpr int kTileChunks = BM * kChunksPerRow;           // 1024 per operand tile (16 KB)
+constexpr int kSlabsPerWave = kTileChunks / 64 / 4;       // 1 KB slabs per wave per operand: 4
 constexpr int kGroupM = 8;
 
 struct GemmArgs {
@@ -48,20 +52,10 @@ struct GemmArgs {
     int32_t ffn;          // SwiGLU output width
 };
 
-// Raw buffer descriptor over `bytes` bytes from `base` (clamped to 4 GiB);
-// loads past the end return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
-    // Every descriptor is wave-uniform by construction; readfirstlane keeps it
-    // in scalar registers even where the index arithmetic ran on the VALU.
-    const uint64_t addr = reinterpret_cast<uint64_t>(base);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
-    const int32_t n = __builtin_amdgcn_readfirstlane(bytes >= 0xFFFFFFFFll ? (int32_t)0xFFFFFFFF : (int32_t)bytes);
-    void *p = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
-    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, n, 0x00020000);
-}
-
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kChunksPerRow + (chunk ^ (row & 7)); }
+// LDS operand tile: row r holds 4 chunks of 16 B (32 k values); chunk c of row
+// r is stored at c ^ ((r >> 2) & 3), so the 8 lanes an LDS cycle serves (rows
+// r..r+7, one chunk) hit distinct banks.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kChunksPerRow + (chunk ^ ((row >> 2) & 3)); }
 
 // Map a linear workgroup id to (tile_m, tile_n): XCD-contiguous ranges of a
 // grouped (kGroupM tile-rows at a time) order.
@@ -81,7 +75,13 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
-    __shared__ uint4 lds[2][2][kTileChunks];  // [stage][0 = W, 1 = A]
+    // One LDS object per ring stage ([0 = W, 1 = A] x 16 KB each): distinct
+    // objects let the compiler tell an in-flight stage's direct loads apart
+    // from reads of the stage being consumed.
+    __shared__ uint4 lds0[2][kTileChunks];
+    __shared__ uint4 lds1[2][kTileChunks];
+    __shared__ uint4 lds2[2][kTileChunks];
+    __shared__ uint4 lds3[2][kTileChunks];
 
     int tm, tn;
     tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
@@ -90,35 +90,53 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
     const int wm = wave >> 1, wn = wave & 1;
 
-    // Thread t loads 16-byte chunk c = t & 7 of tile rows r0 + 32 j (j < 8),
-    // r0 = t >> 3, through buffer loads: a wave-uniform resource descriptor
-    // spans the tile's valid rows, so rows past M (or N) read as zero without a
-    // branch, and the K offset and row step travel in a scalar offset. The
-    // SwiGLU weight tile interleaves 16-row blocks of the gate and up halves:
-    // tile row r0 + 32 j is gate (waves 0-1, r0 < 16) or up (waves 2-3) column
-    // tn * 128 + 16 j + (r0 & 15).
-    const int r0 = t >> 3, c8 = 8 * (t & 7);
+    // Operand tiles stream straight into LDS (gfx950 buffer loads with the LDS
+    // bit: lane i's 16 bytes land at slab + 16 i). A 16 KB operand tile is 16
+    // slabs of 16 rows x 4 chunks; wave w loads slabs 4w .. 4w+3 of both
+    // operands. Lane i of a slab holds row 16 s + i/4 and physical chunk i%4,
+    // i.e. logical chunk (i%4) ^ ((row >> 2) & 3). A wave-uniform buffer
+    // descriptor spans the tile's valid rows: rows past M (or N) read as zero.
+    // The SwiGLU weight tile interleaves 16-row blocks of the gate and up
+    // halves: tile row r is gate (r & 16 == 0) or up column tn*128 + 16 (r/32) + r%16.
     const int64_t m_first = (int64_t)tm * BM;
     const int64_t a_rows = min<int64_t>(p.M - m_first, BM);
-    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(p.a + m_first * p.lda, ((a_rows - 1) * p.lda + p.K) * 2);
-    const int voff_a = (int)((r0 * p.lda + c8) * 2);
-    const int a_row_step = (int)(32 * p.lda * 2);
-    __amdgpu_buffer_rsrc_t rs_w;
-    int voff_w, w_row_step;
+    const i32x4_t rs_a = raw_rsrc(p.a + m_first * p.lda, ((a_rows - 1) * p.lda + p.K) * 2);
+    i32x4_t rs_w, rs_w2;
     if (EPI == H3_EPI_SWIGLU) {
         const int64_t col_first = (int64_t)tn * (BN / 2);
         const int64_t w_rows = min<int64_t>(p.ffn - col_first, BN / 2);
-        const int64_t half = wave >> 1;
-        rs_w = make_rsrc(p.w + (half * p.ffn + col_first) * p.ldw, ((w_rows - 1) * p.ldw + p.K) * 2);
-        voff_w = (int)(((r0 & 15) * p.ldw + c8) * 2);
-        w_row_step = (int)(16 * p.ldw * 2);
+        rs_w = raw_rsrc(p.w + col_first * p.ldw, ((w_rows - 1) * p.ldw + p.K) * 2);
+        rs_w2 = raw_rsrc(p.w + (p.ffn + col_first) * p.ldw, ((w_rows - 1) * p.ldw + p.K) * 2);
     } else {
         const int64_t n_first = (int64_t)tn * BN;
         const int64_t w_rows = min<int64_t>(p.N - n_first, BN);
-        rs_w = make_rsrc(p.w + n_first * p.ldw, ((w_rows - 1) * p.ldw + p.K) * 2);
-        voff_w = (int)((r0 * p.ldw + c8) * 2);
-        w_row_step = (int)(32 * p.ldw * 2);
+        rs_w = raw_rsrc(p.w + n_first * p.ldw, ((w_rows - 1) * p.ldw + p.K) * 2);
+        rs_w2 = rs_w;
     }
+    int a_voff[kSlabsPerWave], w_voff[kSlabsPerWave];
+#pragma unroll
+    for (int i = 0; i < kSlabsPerWave; ++i) {
+        const int slab = 4 * wave + i;
+        const int row = 16 * slab + (lane >> 2);
+        const int c = (lane & 3) ^ ((row >> 2) & 3);
+        a_voff[i] = (int)((row * p.lda + 8 * c) * 2);
+        if (EPI == H3_EPI_SWIGLU) {
+            // slab rows are all gate (slab even) or all up (slab odd)
+            const int col = 16 * (slab >> 1) + (lane >> 2);
+            w_voff[i] = (int)((col * p.ldw + 8 * c) * 2);
+        } else {
+            w_voff[i] = (int)((row * p.ldw + 8 * c) * 2);
+        }
+    }
+    auto issue_to = [&](uint4 (&buf)[2][kTileChunks], int kt) {
+        const int k0b = kt * BK * 2;
+#pragma unroll
+        for (int i = 0; i < kSlabsPerWave; ++i) {
+            const int slab = 4 * wave + i;
+            dma_slab(rs_a, lds_addr(&buf[1][64 * slab]), a_voff[i], k0b);
+            dma_slab((EPI == H3_EPI_SWIGLU && (slab & 1)) ? rs_w2 : rs_w, lds_addr(&buf[0][64 * slab]), w_voff[i], k0b);
+        }
+    };
 
     f32x16_t acc[4][4];
 #pragma unroll
@@ -129,50 +147,59 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     const int KT = (int)(p.K / BK);
-    uint4 ra[kLoadsPerThread], rw[kLoadsPerThread];
-    auto gload = [&](int kt) {
-        const int k0b = kt * BK * 2;
-#pragma unroll
-        for (int j = 0; j < kLoadsPerThread; ++j) {
-            ra[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_a, voff_a, k0b + j * a_row_step, 0));
-            rw[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_w, voff_w, k0b + j * w_row_step, 0));
-        }
-    };
-    auto lstore = [&](int stage) {
-#pragma unroll
-        for (int j = 0; j < kLoadsPerThread; ++j) {
-            const int pos = swz(r0 + 32 * j, t & 7);
-            lds[stage][0][pos] = rw[j];
-            lds[stage][1][pos] = ra[j];
-        }
-    };
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
     const int r32 = lane & 31, g2 = lane >> 5;
-    for (int kt = 0; kt < KT; ++kt) {
-        const int st = kt & 1;
-        gload(kt + 1);  // the last prefetch reads a harmless in-descriptor tile
-        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the MFMA work
+    auto compute = [&](const uint4 (&buf)[2][kTileChunks]) {
+        // All operands of the stage first (16 x 128-bit LDS reads), then the
+        // 32 MFMAs, so LDS latency overlaps the matrix work.
+        bf16x8_t aop[2][4], wop[2][4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            bf16x8_t aop[4];
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                aop[j] = __builtin_bit_cast(bf16x8_t, lds[st][1][swz(wm * 128 + j * 32 + r32, ks * 2 + g2)]);
+            for (int j = 0; j < 4; ++j) {
+                aop[ks][j] = __builtin_bit_cast(bf16x8_t, buf[1][swz(wm * 128 + j * 32 + r32, ks * 2 + g2)]);
+                wop[ks][j] = __builtin_bit_cast(bf16x8_t, buf[0][swz(wn * 128 + j * 32 + r32, ks * 2 + g2)]);
+            }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bf16x8_t wop = __builtin_bit_cast(bf16x8_t, lds[st][0][swz(wn * 128 + i * 32 + r32, ks * 2 + g2)]);
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop, aop[j], acc[i][j], 0, 0, 0);
-            }
-        }
-        lstore(st ^ 1);
-        __syncthreads();
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop[ks][i], aop[ks][j], acc[i][j], 0, 0, 0);
+    };
+    // One ring step: wait until stage kt landed (later stages may stay in
+    // flight), barrier, refill the slot consumed at kt-1 with stage kt+3,
+    // compute stage kt. Raw barrier: __syncthreads()'s fences would wait for
+    // every outstanding load, including the stages meant to stay in flight.
+    auto step = [&](int kt, const uint4 (&cur)[2][kTileChunks], uint4 (&refill)[2][kTileChunks]) {
+        const int ahead = min(KT - 1 - kt, kStages - 2);
+        if (ahead >= 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else if (ahead == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + kStages - 1 < KT) issue_to(refill, kt + kStages - 1);
+        compute(cur);
+    };
+
+    // Only stages < KT are ever issued, so no load is in flight past the loop
+    // (the final vmcnt(0) drains nothing, and guards against an LDS write
+    // landing after the workgroup has ended).
+    issue_to(lds0, 0);
+    if (KT > 1) issue_to(lds1, 1);
+    if (KT > 2) issue_to(lds2, 2);
+    int kt = 0;
+#pragma unroll 1
+    for (; kt + 4 <= KT; kt += 4) {
+        step(kt + 0, lds0, lds3);
+        step(kt + 1, lds1, lds0);
+        step(kt + 2, lds2, lds1);
+        step(kt + 3, lds3, lds2);
     }
+    if (kt < KT) step(kt, lds0, lds3);          // remainder: KT % 4 steps
+    if (kt + 1 < KT) step(kt + 1, lds1, lds0);
+    if (kt + 2 < KT) step(kt + 2, lds2, lds1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Epilogue: in each 32 x 32 sub-tile the lane holds row m = lane & 31 and,
     // for register group q (0..3), the 4 columns 8 q + 4 (lane >> 5) + (0..3).

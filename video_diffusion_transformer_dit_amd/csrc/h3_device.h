@@ -12,6 +12,42 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (4 SGPRs) over `bytes` bytes from `base` (clamped to
+// 4 GiB), wave-uniform by construction: loads past the end return zero.
+__device__ __forceinline__ i32x4_t raw_rsrc(const void *base, int64_t bytes) {
+    const uint64_t addr = reinterpret_cast<uint64_t>(base);
+    i32x4_t r;
+    r.x = (int)__builtin_amdgcn_readfirstlane((uint32_t)addr);
+    r.y = (int)(__builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32)) & 0xFFFFu);  // stride 0
+    r.z = (int)__builtin_amdgcn_readfirstlane(bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes);
+    r.w = 0x00020000;
+    return r;
+}
+
+// LDS byte address of a __shared__ object, wave-uniform.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
+}
+
+// Direct global -> LDS load of one 1 KB slab: lane i's 16 bytes (descriptor
+// rsrc, byte offset voff + soff) land at LDS address lds + 16 i. Issued as one
+// asm statement (M0 set, the M0 -> LDS-DMA wait state, the load) so the
+// compiler neither reuses M0 in between nor inserts its conservative
+// "may alias any LDS read" waits: callers order these loads themselves with
+// s_waitcnt vmcnt and a barrier before reading the slab.
+__device__ __forceinline__ void dma_slab(i32x4_t rsrc, uint32_t lds, int voff, int soff) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
+        : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+        : "memory", "m0");
+}
+
 // BF16 bit pattern -> float (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
