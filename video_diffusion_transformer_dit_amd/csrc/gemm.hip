@@ -75,13 +75,8 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
-    // One LDS object per ring stage ([0 = W, 1 = A] x 16 KB each): distinct
-    // objects let the compiler tell an in-flight stage's direct loads apart
-    // from reads of the stage being consumed.
-    __shared__ uint4 lds0[2][kTileChunks];
-    __shared__ uint4 lds1[2][kTileChunks];
-    __shared__ uint4 lds2[2][kTileChunks];
-    __shared__ uint4 lds3[2][kTileChunks];
+    // LDS ring: kStages slots of [W tile, A tile], 16 KB each (128 KB).
+    __shared__ uint4 smem[kStages * 2 * kTileChunks];
 
     int tm, tn;
     tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
@@ -128,14 +123,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
             w_voff[i] = (int)((row * p.ldw + 8 * c) * 2);
         }
     }
-    auto issue_to = [&](uint4 (&buf)[2][kTileChunks], int kt) {
-        const int k0b = kt * BK * 2;
-#pragma unroll
-        for (int i = 0; i < kSlabsPerWave; ++i) {
-            const int slab = 4 * wave + i;
-            dma_slab(rs_a, lds_addr(&buf[1][64 * slab]), a_voff[i], k0b);
-            dma_slab((EPI == H3_EPI_SWIGLU && (slab & 1)) ? rs_w2 : rs_w, lds_addr(&buf[0][64 * slab]), w_voff[i], k0b);
-        }
+    // Stages past the end of K load through a zero-length descriptor: the
+    // loads return zero without touching memory, so every step issues the
+    // same 8 loads and the vmcnt arithmetic below is constant.
+    i32x4_t rs_none = rs_a;
+    rs_none.z = 0;
+    // LDS byte address of this wave's first slab of slot 0's W tile.
+    const uint32_t lds_wave = lds_addr(smem) + (uint32_t)(4 * wave * 64 * 16);
+    // Direct load number d (0..7) of stage kt into ring slot `slot`: slab
+    // 4 wave + d/2 of the A tile (d odd) or the W tile (d even).
+    auto dma = [&](int slot, int d, int kt, bool live) {
+        const int i = d >> 1, op = (d & 1) ? 1 : 0;
+        const int slab = 4 * wave + i;
+        i32x4_t r = op ? rs_a : ((EPI == H3_EPI_SWIGLU && (slab & 1)) ? rs_w2 : rs_w);
+        if (!live) r = rs_none;
+        const uint32_t m0 = lds_wave + (uint32_t)(((slot * 2 + op) * kTileChunks + 64 * i) * 16);
+        dma_slab(r, m0, op ? a_voff[i] : w_voff[i], kt * BK * 2);
     };
 
     f32x16_t acc[4][4];
@@ -148,57 +151,72 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
 
     const int KT = (int)(p.K / BK);
     const int r32 = lane & 31, g2 = lane >> 5;
-    auto compute = [&](const uint4 (&buf)[2][kTileChunks]) {
-        // All operands of the stage first (16 x 128-bit LDS reads), then the
-        // 32 MFMAs, so LDS latency overlaps the matrix work.
-        bf16x8_t aop[2][4], wop[2][4];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                aop[ks][j] = __builtin_bit_cast(bf16x8_t, buf[1][swz(wm * 128 + j * 32 + r32, ks * 2 + g2)]);
-                wop[ks][j] = __builtin_bit_cast(bf16x8_t, buf[0][swz(wn * 128 + j * 32 + r32, ks * 2 + g2)]);
-            }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop[ks][i], aop[ks][j], acc[i][j], 0, 0, 0);
+    // This wave's MFMA operands of one stage: [ks][sub-tile] for A and W.
+    struct Ops {
+        bf16x8_t a[2][4], w[2][4];
     };
-    // One ring step: wait until stage kt landed (later stages may stay in
-    // flight), barrier, refill the slot consumed at kt-1 with stage kt+3,
-    // compute stage kt. Raw barrier: __syncthreads()'s fences would wait for
-    // every outstanding load, including the stages meant to stay in flight.
-    auto step = [&](int kt, const uint4 (&cur)[2][kTileChunks], uint4 (&refill)[2][kTileChunks]) {
-        const int ahead = min(KT - 1 - kt, kStages - 2);
-        if (ahead >= 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-        else if (ahead == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // LDS read number r (0..15) of a stage, in the order the MFMAs consume
+    // the operands: per half ks, W[0], A[0..3], W[1..3].
+    auto read = [&](int slot, int r, Ops &o) {
+        const int ks = r >> 3, q = r & 7;
+        const uint4 *base = smem + slot * 2 * kTileChunks;
+        if (q >= 1 && q <= 4)
+            o.a[ks][q - 1] = __builtin_bit_cast(bf16x8_t, base[kTileChunks + swz(wm * 128 + (q - 1) * 32 + r32, ks * 2 + g2)]);
+        else {
+            const int i = q == 0 ? 0 : q - 4;
+            o.w[ks][i] = __builtin_bit_cast(bf16x8_t, base[swz(wn * 128 + i * 32 + r32, ks * 2 + g2)]);
+        }
+    };
+    // One ring step. On entry `cur` holds stage kt's operands (read from LDS
+    // during the previous step) and stages kt+1, kt+2 are in flight. Wait for
+    // stage kt+1 (8 loads per stage per wave: vmcnt 8 leaves kt+2 pending),
+    // barrier (every wave has then also consumed the LDS slot of stage kt-1),
+    // then run stage kt's 32 MFMAs on `cur` with the refill of that slot
+    // (stage kt+3, one direct load every 4th MFMA) and the 16 LDS reads of
+    // stage kt+1 into `nxt` in between, in a fixed order, so the load issue
+    // never leaves the matrix pipe idle. Raw barrier: __syncthreads()'s
+    // fences would wait for every outstanding load. When kt+1 == KT the slot
+    // read is stale and the values unused.
+    auto step = [&](int kt, int slot_next, int slot_refill, const Ops &cur, Ops &nxt) {
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        if (kt + kStages - 1 < KT) issue_to(refill, kt + kStages - 1);
-        compute(cur);
+        const bool live = kt + 3 < KT;
+        int r = 0;
+#pragma unroll
+        for (int t = 0; t < 32; ++t) {
+            const int ks = t >> 4, i = (t >> 2) & 3, j = t & 3;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.w[ks][i], cur.a[ks][j], acc[i][j], 0, 0, 0);
+            if ((t & 3) == 0) dma(slot_refill, t >> 2, kt + 3, live);
+            else if (r < 16) read(slot_next, r++, nxt);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
-    // Only stages < KT are ever issued, so no load is in flight past the loop
-    // (the final vmcnt(0) drains nothing, and guards against an LDS write
-    // landing after the workgroup has ended).
-    issue_to(lds0, 0);
-    if (KT > 1) issue_to(lds1, 1);
-    if (KT > 2) issue_to(lds2, 2);
+    // Prologue: stages 0..2 in flight, stage 0's operands in registers.
+#pragma unroll
+    for (int st = 0; st < 3; ++st)
+#pragma unroll
+        for (int d = 0; d < 8; ++d) dma(st, d, st, st < KT);
+    Ops opa, opb;
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) read(0, r, opa);
     int kt = 0;
 #pragma unroll 1
     for (; kt + 4 <= KT; kt += 4) {
-        step(kt + 0, lds0, lds3);
-        step(kt + 1, lds1, lds0);
-        step(kt + 2, lds2, lds1);
-        step(kt + 3, lds3, lds2);
+        step(kt + 0, 1, 3, opa, opb);
+        step(kt + 1, 2, 0, opb, opa);
+        step(kt + 2, 3, 1, opa, opb);
+        step(kt + 3, 0, 2, opb, opa);
     }
-    if (kt < KT) step(kt, lds0, lds3);          // remainder: KT % 4 steps
-    if (kt + 1 < KT) step(kt + 1, lds1, lds0);
-    if (kt + 2 < KT) step(kt + 2, lds2, lds1);
+    if (kt < KT) step(kt, 1, 3, opa, opb);  // remainder: KT % 4 steps
+    if (kt + 1 < KT) step(kt + 1, 2, 0, opb, opa);
+    if (kt + 2 < KT) step(kt + 2, 3, 1, opa, opb);
+    // Drain the loads still in flight (stages past K) before the workgroup
+    // can end.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Epilogue: in each 32 x 32 sub-tile the lane holds row m = lane & 31 and,
