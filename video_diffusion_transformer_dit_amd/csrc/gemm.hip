@@ -11,15 +11,17 @@
 //                    [M, 2F] intermediate never reaches HBM.
 //
 // Tiling (CDNA4): 256 x 256 output tile per 256-thread workgroup, 4 wavefronts
-// of 128 x 128, K step 32, v_mfma_f32_32x32x16_bf16. The weight tile is the
+// of 128 x 128, K stage 64, v_mfma_f32_32x32x16_bf16. The weight tile is the
 // MFMA A operand and the activation tile the B operand, so each lane's
 // accumulator holds groups of 4 consecutive output columns of one row
 // (8-byte stores).
 // Operand tiles go global -> LDS directly (buffer loads with the LDS bit, no
-// register staging) through a 4-stage ring of 2 x 16 KB slots (128 KB): three
-// K steps are in flight while the fourth is consumed, with explicit vmcnt
-// waits, so a step waits only for its own stage. A 16-byte-chunk XOR swizzle
-// keeps the 128-bit LDS reads conflict-free.
+// register staging), double-buffered in two 64 KB stage slots. A stage is 64
+// k values, i.e. one whole 128-byte line per tile row, so no line is fetched
+// twice into the CU. The next stage's loads and the next k-step's LDS operand
+// reads are interleaved with the current k-step's MFMAs, with one barrier per
+// stage. A 16-byte-chunk XOR swizzle keeps the 128-bit LDS reads
+// conflict-free.
 // Tiles are ordered so each XCD (workgroups are dealt round-robin over 8 XCDs)
 // walks a contiguous range of a grouped tile order, keeping the operand
 // K-slices its 32 CUs share in that XCD's L2.
@@ -29,13 +31,11 @@
 namespace h3 {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 32;
+constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kThreads = 256;
-constexpr int kStages = 4;                                // LDS ring depth
-constexpr int kChunksPerRow = BK / 8;                     // 4 x 16 B per tile row
-constexpr int kTileChunks = BM * kChunksPerRow;           // 1024 per operand tile (16 KB)
-constexpr int kSlabsPerWave = kTileChunks / 64 / 4;       // 1 KB slabs per wave per operand: 4
-constexpr int kGroupM = 8;
+constexpr int kChunksPerRow = BK / 8;                     // 8 x 16 B per tile row: one 128 B line
+constexpr int kTileChunks = BM * kChunksPerRow;           // 2048 per operand tile (32 KB)
+constexpr int kSlabsPerWave = kTileChunks / 64 / 4;       // 1 KB slabs per wave per operand: 8
 
 struct GemmArgs {
     const uint16_t *a;
@@ -49,25 +49,27 @@ struct GemmArgs {
     int64_t M, N, K;      // M valid rows; N weight rows; K reduction
     int32_t n_groups;
     int32_t tiles_m, tiles_n;
+    int32_t group_m;      // tile rows per group of the tile order
     int32_t ffn;          // SwiGLU output width
 };
 
-// LDS operand tile: row r holds 4 chunks of 16 B (32 k values); chunk c of row
-// r is stored at c ^ ((r >> 2) & 3), so the 8 lanes an LDS cycle serves (rows
-// r..r+7, one chunk) hit distinct banks.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kChunksPerRow + (chunk ^ ((row >> 2) & 3)); }
+// LDS operand tile: row r holds 8 chunks of 16 B (64 k values); chunk c of
+// row r is stored at c ^ ((r >> 1) & 7). A 128-bit LDS read serves 16 lanes
+// (rows r..r+15, one chunk) per cycle: the 8 even and the 8 odd rows each
+// see 8 distinct chunk positions, so the 16 reads hit distinct banks.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kChunksPerRow + (chunk ^ ((row >> 1) & 7)); }
 
 // Map a linear workgroup id to (tile_m, tile_n): XCD-contiguous ranges of a
-// grouped (kGroupM tile-rows at a time) order.
-__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int &tm, int &tn) {
+// grouped (group_m tile-rows at a time, column by column) order.
+__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int group_m, int &tm, int &tn) {
     const int T = tiles_m * tiles_n;
     const int q = T / 8, rr = T % 8;
     const int xcd = bid % 8, local = bid / 8;
     const int lin = xcd < rr ? xcd * (q + 1) + local : rr * (q + 1) + (xcd - rr) * q + local;
-    const int per_group = kGroupM * tiles_n;
+    const int per_group = group_m * tiles_n;
     const int group = lin / per_group;
-    const int first_m = group * kGroupM;
-    const int gsz = min(tiles_m - first_m, kGroupM);
+    const int first_m = group * group_m;
+    const int gsz = min(tiles_m - first_m, group_m);
     const int in_group = lin - group * per_group;
     tm = first_m + in_group % gsz;
     tn = in_group / gsz;
@@ -75,24 +77,26 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
-    // LDS ring: kStages slots of [W tile, A tile], 16 KB each (128 KB).
-    __shared__ uint4 smem[kStages * 2 * kTileChunks];
+    // LDS: two stage slots of [W tile, A tile], 32 KB each (128 KB).
+    __shared__ uint4 smem[2 * 2 * kTileChunks];
 
     int tm, tn;
-    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
     const int wm = wave >> 1, wn = wave & 1;
 
     // Operand tiles stream straight into LDS (gfx950 buffer loads with the LDS
-    // bit: lane i's 16 bytes land at slab + 16 i). A 16 KB operand tile is 16
-    // slabs of 16 rows x 4 chunks; wave w loads slabs 4w .. 4w+3 of both
-    // operands. Lane i of a slab holds row 16 s + i/4 and physical chunk i%4,
-    // i.e. logical chunk (i%4) ^ ((row >> 2) & 3). A wave-uniform buffer
-    // descriptor spans the tile's valid rows: rows past M (or N) read as zero.
+    // bit: lane i's 16 bytes land at slab + 16 i). A 32 KB operand tile is 32
+    // slabs of 8 rows x 8 chunks, so each load instruction covers whole 128 B
+    // lines of 8 rows; wave w loads slabs 8w .. 8w+7 of both operands. Lane i
+    // of a slab holds row 8 s + i/8 and physical chunk i%8, i.e. logical chunk
+    // (i%8) ^ ((row >> 1) & 7). A wave-uniform buffer descriptor spans the
+    // tile's valid rows: rows past M (or N) read as zero.
     // The SwiGLU weight tile interleaves 16-row blocks of the gate and up
-    // halves: tile row r is gate (r & 16 == 0) or up column tn*128 + 16 (r/32) + r%16.
+    // halves: tile row r is gate ((r & 16) == 0) or up, of output column
+    // tn*128 + 16 (r/32) + r%16.
     const int64_t m_first = (int64_t)tm * BM;
     const int64_t a_rows = min<int64_t>(p.M - m_first, BM);
     const i32x4_t rs_a = raw_rsrc(p.a + m_first * p.lda, ((a_rows - 1) * p.lda + p.K) * 2);
@@ -111,32 +115,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
     int a_voff[kSlabsPerWave], w_voff[kSlabsPerWave];
 #pragma unroll
     for (int i = 0; i < kSlabsPerWave; ++i) {
-        const int slab = 4 * wave + i;
-        const int row = 16 * slab + (lane >> 2);
-        const int c = (lane & 3) ^ ((row >> 2) & 3);
+        const int slab = 8 * wave + i;
+        const int row = 8 * slab + (lane >> 3);
+        const int c = (lane & 7) ^ ((row >> 1) & 7);
         a_voff[i] = (int)((row * p.lda + 8 * c) * 2);
         if (EPI == H3_EPI_SWIGLU) {
-            // slab rows are all gate (slab even) or all up (slab odd)
-            const int col = 16 * (slab >> 1) + (lane >> 2);
+            // a slab's 8 rows lie in one 16-row gate (slab/2 even) or up block
+            const int col = 16 * (slab >> 2) + 8 * (slab & 1) + (lane >> 3);
             w_voff[i] = (int)((col * p.ldw + 8 * c) * 2);
         } else {
             w_voff[i] = (int)((row * p.ldw + 8 * c) * 2);
         }
     }
     // Stages past the end of K load through a zero-length descriptor: the
-    // loads return zero without touching memory, so every step issues the
-    // same 8 loads and the vmcnt arithmetic below is constant.
+    // loads return zero without touching memory, so every stage issues the
+    // same 16 loads and the vmcnt arithmetic below is constant.
     i32x4_t rs_none = rs_a;
     rs_none.z = 0;
     // LDS byte address of this wave's first slab of slot 0's W tile.
-    const uint32_t lds_wave = lds_addr(smem) + (uint32_t)(4 * wave * 64 * 16);
-    // Direct load number d (0..7) of stage kt into ring slot `slot`: slab
-    // 4 wave + d/2 of the A tile (d odd) or the W tile (d even).
-    auto dma = [&](int slot, int d, int kt, bool live) {
+    const uint32_t lds_wave = lds_addr(smem) + (uint32_t)(8 * wave * 64 * 16);
+    // Direct load number d (0..15) of stage kt into slot `slot`: slab
+    // 8 wave + d/2 of the A tile (d odd) or the W tile (d even).
+    auto dma = [&](int slot, int d, int kt) {
         const int i = d >> 1, op = (d & 1) ? 1 : 0;
-        const int slab = 4 * wave + i;
-        i32x4_t r = op ? rs_a : ((EPI == H3_EPI_SWIGLU && (slab & 1)) ? rs_w2 : rs_w);
-        if (!live) r = rs_none;
+        const int slab = 8 * wave + i;
+        i32x4_t r = op ? rs_a : ((EPI == H3_EPI_SWIGLU && ((slab >> 1) & 1)) ? rs_w2 : rs_w);
+        if (kt >= (int)(p.K / BK)) r = rs_none;
         const uint32_t m0 = lds_wave + (uint32_t)(((slot * 2 + op) * kTileChunks + 64 * i) * 16);
         dma_slab(r, m0, op ? a_voff[i] : w_voff[i], kt * BK * 2);
     };
@@ -151,70 +155,81 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
 
     const int KT = (int)(p.K / BK);
     const int r32 = lane & 31, g2 = lane >> 5;
-    // This wave's MFMA operands of one stage: [ks][sub-tile] for A and W.
+    // This wave's MFMA operands of one 16-wide k-step: 4 W and 4 A sub-tiles.
     struct Ops {
-        bf16x8_t a[2][4], w[2][4];
+        bf16x8_t a[4], w[4];
     };
-    // LDS read number r (0..15) of a stage, in the order the MFMAs consume
-    // the operands: per half ks, W[0], A[0..3], W[1..3].
-    auto read = [&](int slot, int r, Ops &o) {
-        const int ks = r >> 3, q = r & 7;
+    // LDS read number r (0..7) of k-step ks of the stage in `slot`, in the
+    // order the MFMAs consume the operands: W[0], A[0..3], W[1..3].
+    auto read = [&](int slot, int ks, int r, Ops &o) {
         const uint4 *base = smem + slot * 2 * kTileChunks;
-        if (q >= 1 && q <= 4)
-            o.a[ks][q - 1] = __builtin_bit_cast(bf16x8_t, base[kTileChunks + swz(wm * 128 + (q - 1) * 32 + r32, ks * 2 + g2)]);
+        if (r >= 1 && r <= 4)
+            o.a[r - 1] = __builtin_bit_cast(bf16x8_t, base[kTileChunks + swz(wm * 128 + (r - 1) * 32 + r32, ks * 2 + g2)]);
         else {
-            const int i = q == 0 ? 0 : q - 4;
-            o.w[ks][i] = __builtin_bit_cast(bf16x8_t, base[swz(wn * 128 + i * 32 + r32, ks * 2 + g2)]);
+            const int i = r == 0 ? 0 : r - 4;
+            o.w[i] = __builtin_bit_cast(bf16x8_t, base[swz(wn * 128 + i * 32 + r32, ks * 2 + g2)]);
         }
     };
-    // One ring step. On entry `cur` holds stage kt's operands (read from LDS
-    // during the previous step) and stages kt+1, kt+2 are in flight. Wait for
-    // stage kt+1 (8 loads per stage per wave: vmcnt 8 leaves kt+2 pending),
-    // barrier (every wave has then also consumed the LDS slot of stage kt-1),
-    // then run stage kt's 32 MFMAs on `cur` with the refill of that slot
-    // (stage kt+3, one direct load every 4th MFMA) and the 16 LDS reads of
-    // stage kt+1 into `nxt` in between, in a fixed order, so the load issue
-    // never leaves the matrix pipe idle. Raw barrier: __syncthreads()'s
-    // fences would wait for every outstanding load. When kt+1 == KT the slot
-    // read is stale and the values unused.
-    auto step = [&](int kt, int slot_next, int slot_refill, const Ops &cur, Ops &nxt) {
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        const bool live = kt + 3 < KT;
-        int r = 0;
+    // One k-step (16 MFMAs) of stage kt, whose operands `cur` already holds.
+    // Stage kt lives in slot kt & 1. Per k-step:
+    //  ks 0..2: read k-step ks+1 of stage kt into `nxt`;
+    //  ks 3:    wait for stage kt+1 (its 16 loads are the only ones in
+    //           flight), make sure this wave's reads of stage kt are done,
+    //           barrier (all of stage kt+1 visible, slot kt & 1 free), then
+    //           read k-step 0 of stage kt+1 and issue the first 8 loads of
+    //           stage kt+2 into slot kt & 1;
+    //  ks 0:    issue the other 8 loads of stage kt+1 (begun at k-step 3 of
+    //           stage kt-1).
+    // The loads and reads sit between the MFMAs in a fixed order, so issuing
+    // them never leaves the matrix pipe idle. Raw barrier: __syncthreads()'s
+    // fences would wait for every outstanding load. Reads of a stage at or
+    // past KT see stale or zero data and are never used.
+    auto kstep = [&](int kt, int ks, int slot, const Ops &cur, Ops &nxt) {
+        if (ks == 3) {
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
-        for (int t = 0; t < 32; ++t) {
-            const int ks = t >> 4, i = (t >> 2) & 3, j = t & 3;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.w[ks][i], cur.a[ks][j], acc[i][j], 0, 0, 0);
-            if ((t & 3) == 0) dma(slot_refill, t >> 2, kt + 3, live);
-            else if (r < 16) read(slot_next, r++, nxt);
+        for (int t = 0; t < 16; ++t) {
+            const int i = t >> 2, j = t & 3;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.w[i], cur.a[j], acc[i][j], 0, 0, 0);
+            if (t & 1) {
+                if (ks == 3) dma(slot, t >> 1, kt + 2);
+                if (ks == 0) dma(slot ^ 1, 8 + (t >> 1), kt + 1);
+            } else {
+                if (ks < 3) read(slot, ks + 1, t >> 1, nxt);
+                else read(slot ^ 1, 0, t >> 1, nxt);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
+    auto stage = [&](int kt, int slot, Ops &r0, Ops &r1) {
+        kstep(kt, 0, slot, r0, r1);
+        kstep(kt, 1, slot, r1, r0);
+        kstep(kt, 2, slot, r0, r1);
+        kstep(kt, 3, slot, r1, r0);
+    };
 
-    // Prologue: stages 0..2 in flight, stage 0's operands in registers.
+    // Prologue: stage 0 and the first half of stage 1 in flight; stage 0's
+    // first k-step in registers.
 #pragma unroll
-    for (int st = 0; st < 3; ++st)
+    for (int d = 0; d < 16; ++d) dma(0, d, 0);
 #pragma unroll
-        for (int d = 0; d < 8; ++d) dma(st, d, st, st < KT);
+    for (int d = 0; d < 8; ++d) dma(1, d, 1);
     Ops opa, opb;
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) read(0, r, opa);
+    for (int r = 0; r < 8; ++r) read(0, 0, r, opa);
     int kt = 0;
 #pragma unroll 1
-    for (; kt + 4 <= KT; kt += 4) {
-        step(kt + 0, 1, 3, opa, opb);
-        step(kt + 1, 2, 0, opb, opa);
-        step(kt + 2, 3, 1, opa, opb);
-        step(kt + 3, 0, 2, opb, opa);
+    for (; kt + 2 <= KT; kt += 2) {
+        stage(kt, 0, opa, opb);
+        stage(kt + 1, 1, opa, opb);
     }
-    if (kt < KT) step(kt, 1, 3, opa, opb);  // remainder: KT % 4 steps
-    if (kt + 1 < KT) step(kt + 1, 2, 0, opb, opa);
-    if (kt + 2 < KT) step(kt + 2, 3, 1, opa, opb);
+    if (kt < KT) stage(kt, 0, opa, opb);  // odd KT
     // Drain the loads still in flight (stages past K) before the workgroup
     // can end.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -303,6 +318,9 @@ void launch_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ld
     p.ffn = (int32_t)(N / 2);
     p.tiles_m = (int32_t)((M_valid + BM - 1) / BM);
     p.tiles_n = epilogue == H3_EPI_SWIGLU ? (int32_t)((N / 2 + BN / 2 - 1) / (BN / 2)) : (int32_t)((N + BN - 1) / BN);
+    // Measured on the block's projections: narrow grids keep the L2 best
+    // with 2 tile rows per group, wide ones (the SwiGLU FFN) with 8.
+    p.group_m = p.tiles_n >= 128 ? 8 : 2;
     const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
     switch (epilogue) {
         case H3_EPI_RESIDUAL: gemm_bf16_kernel<H3_EPI_RESIDUAL><<<grid, kThreads, 0, stream>>>(p); break;
