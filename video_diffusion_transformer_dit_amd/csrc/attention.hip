@@ -68,8 +68,7 @@ struct SegState {
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
-    // Every descriptor is wave-uniform by construction; readfirstlane keeps it
-    // in scalar registers even where the index arithmetic ran on the VALU.
+    // Wave-uniform by construction; readfirstlane keeps it in scalar registers.
     const uint64_t addr = reinterpret_cast<uint64_t>(base);
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
@@ -96,17 +95,18 @@ __device__ __forceinline__ SegState seg_of(const AttnArgs &a, int s) {
     return r;
 }
 
-typedef __attribute__((address_space(3))) void *lds_ptr_t;
-
-// Direct global -> LDS load of one 1 KB slab: lane i's 16 bytes (descriptor
-// rsrc, byte offset voff + soff) land at slab + 16 i.
-__device__ __forceinline__ void load_slab(__amdgpu_buffer_rsrc_t rsrc, const uint4 *slab, int voff, int soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)slab, 16, voff, soff, 0, 0);
-}
+// K / V^T tile stream: position (segment, first key) of the next tile to load.
+struct Cursor {
+    int seg;
+    int64_t k0;
+    SegState S;
+};
 
 __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) {
-    __shared__ uint4 k_lds[2][BKV * 16];  // 2 x 16 KB
-    __shared__ uint4 v_lds[2][D * 8];     // 2 x 16 KB
+    constexpr int KB = BKV * 16;  // 16-byte chunks per K tile buffer (16 KB)
+    constexpr int VB = D * 8;     // chunks per V^T tile buffer (16 KB)
+    // K buffers 0, 1 then V^T buffers 0, 1.
+    __shared__ uint4 smem[2 * KB + 2 * VB];
 
     // ---- work item: (head, group, query tile) with XCD-contiguous order ----
     const int total = a.tiles_per_head * a.heads;
@@ -126,11 +126,11 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     const int l32 = lane & 31, h = lane >> 5;
     const int64_t qw = q0 + wave * WQ;  // this wave's first query
 
-    // ---- Q operands: Qop[j][ks] = Q[qw + 32j + l32][8(2ks + h) .. +7] ----
+    // ---- Q operands: qop[j][ks] = Q[qw + 32j + l32][8(2ks + h) .. +7] ----
     bf16x8_t qop[2][8];
     {
         const int64_t rows = a.rows - qw;  // may be <= 0 for idle waves
-        const __amdgpu_buffer_rsrc_t rq =
+        const __amdgpu_buffer_rsrc_t rqb =
             make_rsrc(a.q + qw * a.ld_q + head * D, rows > 0 ? ((min<int64_t>(rows, WQ) - 1) * a.ld_q + D) * 2 : 0);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
@@ -138,10 +138,10 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
             for (int ks = 0; ks < 8; ++ks)
                 qop[j][ks] = __builtin_bit_cast(
                     bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                  rq, (int)(((32 * j + l32) * a.ld_q + 8 * (2 * ks + h)) * 2), 0, 0));
+                                  rqb, (int)(((32 * j + l32) * a.ld_q + 8 * (2 * ks + h)) * 2), 0, 0));
     }
-    // Register-class hints (empty asm, no instruction): the Q operands live in
-    // AGPRs, which the MFMA reads directly, leaving VGPRs for scores and P.
+    // Register-class hints (empty asm, no instruction): Q and O live in AGPRs,
+    // which the MFMA reads directly, leaving the VGPRs for scores and P.
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -157,234 +157,329 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) asm volatile("" : "+a"(oacc[i][j]));  // O lives in AGPRs
+        for (int j = 0; j < 2; ++j) asm volatile("" : "+a"(oacc[i][j]));
     float l_run[2] = {0.f, 0.f};
 
-    // ---- K / V^T tile loader (direct to LDS). A tile is 16 slabs of K (4 keys
-    //      x 16 chunks) and 16 slabs of V^T (8 channels x 8 chunks); wave w
-    //      loads slabs 4w .. 4w+3 of each. Lane i of K slab s holds key
-    //      4s + i/16, physical chunk i%16 = logical chunk c ^ (key & 15); lane i
-    //      of V^T slab s holds channel 8s + i/8, physical chunk i%8. ----
-    int k_voff[4], vt_voff[4];
+    // ---- tile loads (direct to LDS). A K tile is 16 slabs of 4 keys x 16
+    //      chunks, a V^T tile 16 slabs of 8 channels x 8 chunks; wave w loads
+    //      slabs 4w .. 4w+3 of each. Lane i of K slab s holds key 4s + i/16,
+    //      physical chunk i%16 = logical chunk c ^ (key & 15); lane i of V^T
+    //      slab s holds channel 8s + i/8, physical chunk i%8. ----
     const int kkey0 = lane >> 4, kp = lane & 15;
     const int vd0 = lane >> 3, vp = lane & 7;
-
+    const uint32_t lds0 = lds_addr(smem);
     int n_tiles = 0;
 #pragma unroll
     for (int s = 0; s < H3_MAX_SEGMENTS; ++s)
         if (s < a.n_seg) n_tiles += (int)((a.slen[s] + BKV - 1) / BKV);
 
-    // Position of the next tile to load: segment `seg`, key offset `seg_k0`.
-    int seg = 0;
-    int64_t seg_k0 = 0;
-    SegState nS = seg_of(a, 0);
-    auto set_offsets = [&](const SegState &S) {
+    // Two cursors over the same tile sequence: K runs two tiles ahead of the
+    // tile being finished, V^T one tile ahead.
+    Cursor kc{0, 0, seg_of(a, 0)}, vc{0, 0, seg_of(a, 0)};
+    int k_voff[4], v_voff[4];
+    auto set_k = [&]() {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int key = 4 * (4 * wave + i) + kkey0;
-            k_voff[i] = (int)((key * S.ldk + 8 * (kp ^ (key & 15))) * 2);
-            const int d = 8 * (4 * wave + i) + vd0;
-            vt_voff[i] = (int)((d * S.lpad + 8 * (vp ^ ((d ^ (d >> 3)) & 7))) * 2);
+            k_voff[i] = (int)((key * kc.S.ldk + 8 * (kp ^ (key & 15))) * 2);
         }
     };
-    set_offsets(nS);
-    auto load_tile = [&](const SegState &S, int64_t k0, int buf) {
-        const int64_t rows = min<int64_t>(S.len - k0, BKV);
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(S.k + k0 * S.ldk + head * D, ((rows - 1) * S.ldk + D) * 2);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(S.vt + (int64_t)head * D * S.lpad + k0, (D * S.lpad - k0) * 2);
+    auto set_v = [&]() {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            load_slab(rk, &k_lds[buf][64 * (4 * wave + i)], k_voff[i], 0);
-            load_slab(rv, &v_lds[buf][64 * (4 * wave + i)], vt_voff[i], 0);
+            const int d = 8 * (4 * wave + i) + vd0;
+            v_voff[i] = (int)((d * vc.S.lpad + 8 * (vp ^ ((d ^ (d >> 3)) & 7))) * 2);
         }
     };
-    auto advance = [&]() {
-        seg_k0 += BKV;
-        if (seg_k0 >= nS.len) {
-            ++seg;
-            seg_k0 = 0;
-            if (seg < a.n_seg) {
-                nS = seg_of(a, seg);
-                set_offsets(nS);
+    set_k();
+    set_v();
+    auto advance = [&](Cursor &c, bool is_k) {
+        c.k0 += BKV;
+        if (c.k0 >= c.S.len) {
+            ++c.seg;
+            c.k0 = 0;
+            if (c.seg < a.n_seg) {
+                c.S = seg_of(a, c.seg);
+                if (is_k) set_k();
+                else set_v();
             }
         }
     };
+    // Keys of the cursor's tile that exist (64 past the last tile: nothing to mask).
+    auto valid_keys = [&](const Cursor &c) -> int {
+        return c.seg < a.n_seg ? min((int)(c.S.len - c.k0), BKV) : BKV;
+    };
+    // Issue this wave's 4 slab loads of the cursor's tile into buffer b. Past
+    // the last tile the descriptor has length zero: the loads return zero and
+    // touch no memory, so every iteration issues the same loads.
+    auto issue_k = [&](int b, int half) {
+        const int rows = min((int)(kc.S.len - kc.k0), BKV);
+        i32x4_t r = raw_rsrc(kc.S.k + kc.k0 * kc.S.ldk + head * D, ((int64_t)(rows - 1) * kc.S.ldk + D) * 2);
+        if (kc.seg >= a.n_seg) r.z = 0;
+#pragma unroll
+        for (int i = 2 * half; i < 2 * half + 2; ++i)
+            dma_slab(r, lds0 + (uint32_t)((b * KB + 64 * (4 * wave + i)) * 16), k_voff[i], 0);
+    };
+    auto issue_v = [&](int b, int half) {
+        i32x4_t r = raw_rsrc(vc.S.vt + (int64_t)head * D * vc.S.lpad + vc.k0, (D * vc.S.lpad - vc.k0) * 2);
+        if (vc.seg >= a.n_seg) r.z = 0;
+#pragma unroll
+        for (int i = 2 * half; i < 2 * half + 2; ++i)
+            dma_slab(r, lds0 + (uint32_t)((2 * KB + b * VB + 64 * (4 * wave + i)) * 16), v_voff[i], 0);
+    };
 
-    load_tile(nS, 0, 0);
+    // ---- per-lane LDS read offsets (bytes); buffer and sub-tile offsets are
+    //      instruction immediates ----
+    // K operand of k-step ks: key l32 (+32 per half), logical chunk 2 ks + h.
+    int koff[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) koff[ks] = (k_pos(l32, 2 * ks + h)) * 16;
+    // V^T operand: channel 32 dt + l32, logical chunk 2 (2 hb + s2) + h; the
+    // swizzle depends on dt only through its parity.
+    int voff[2][4];
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) voff[par][c4] = (2 * KB + vt_pos(32 * par + l32, 2 * c4 + h)) * 16;
+    const char *lds_bytes = reinterpret_cast<const char *>(smem);
+    // K operand number pr = 16 hb' ... : half hb = pr / 8, k-step ks = pr % 8.
+    auto kop_read = [&](int b, int pr) -> bf16x8_t {
+        const int hb = pr >> 3, ks = pr & 7;
+        return __builtin_bit_cast(bf16x8_t,
+                                  *reinterpret_cast<const uint4 *>(lds_bytes + koff[ks] + (b * KB + hb * 512) * 16));
+    };
+    // V^T operand number pr: half hb = pr / 8, 16-key group s2 = (pr / 4) % 2,
+    // channel block dt = pr % 4.
+    auto vop_read = [&](int b, int pr) -> bf16x8_t {
+        const int hb = pr >> 3, s2 = (pr >> 2) & 1, dt = pr & 3;
+        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
+                                                lds_bytes + voff[dt & 1][2 * hb + s2] + (b * VB + (dt >> 1) * 512) * 16));
+    };
+
+    // The key loop runs over half tiles u (32 keys: tile u/2, half u%2).
+    // Scores S^T of a half tile, [query block j]: lane holds query 32 j + l32,
+    // keys 8 (v/4) + 4 h + v%4 of the half. The MFMAs accumulate them in AGPRs
+    // (sacc); the softmax works on a VGPR copy (sv).
+    f32x16_t sacc[2], sv[2];
+    auto pin_sacc = [&]() {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) asm volatile("" : "+a"(sacc[j]));
+    };
+    // Scores of keys >= valid (within the half) -> -inf; `in_agpr`: one
+    // 16-register block at a time.
+    auto mask = [&](f32x16_t (&s)[2], int valid, bool in_agpr) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int key = 8 * (v >> 2) + 4 * h + (v & 3);
+                if (key >= valid) s[j][v] = -__builtin_huge_valf();
+            }
+            if (in_agpr) asm volatile("" : "+a"(s[j]));
+        }
+    };
+    // Per-lane maximum of a half tile's raw scores, per query block.
+    float tmaxr[2];
+
+    // ---- prologue: K of tiles 0 and 1, V^T of tile 0; S of half 0 ----
+    issue_k(0, 0);
+    issue_k(0, 1);
+    advance(kc, true);
+    issue_k(1, 0);
+    issue_k(1, 1);
+    advance(kc, true);
+    issue_v(0, 0);
+    issue_v(0, 1);
+    int vk_cur = valid_keys(vc);  // valid keys of the current tile
+    int vk_next = BKV;            // ... of the next one (set when its V^T is issued)
+    advance(vc, false);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    int64_t cur_len = nS.len;  // length of the segment the current tile is in
-    int64_t cur_k0 = 0;
-    advance();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8_t kop = kop_read(0, ks);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[j][ks], ks == 0 ? f32x16_t{} : sacc[j], 0, 0,
+                                                              0);
+    }
+    pin_sacc();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sv[j] = sacc[j];
+    if (vk_cur < 32) mask(sv, vk_cur, false);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        float m = sv[j][0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) m = fmaxf(m, sv[j][v]);
+        tmaxr[j] = m;
+    }
 
     // Softmax with a per-row reference maximum m_ref (exp2 domain): p =
     // exp2(s c - m_ref) stays <= 2^kSlack while no score exceeds m_ref + kSlack,
-    // so the hot loop never rescales O. A tile whose maximum would break that
-    // bound makes the wave leave the inner loop before any P.V of the tile,
-    // rescale O and l to the new maximum and redo the tile (always at the
-    // first tile, rarely afterwards). The redone tile re-issues the same
-    // prefetch (identical bytes) and reaches the same barriers, so every wave
-    // still passes the same number of barriers.
+    // so O and l are rescaled only when a half tile's maximum breaks that
+    // bound (always at the first, rarely afterwards). The check runs before
+    // any P of the half tile is formed, so nothing is ever recomputed.
     constexpr float kSlack = 10.0f;
     float m_ref[2] = {-__builtin_huge_valf(), -__builtin_huge_valf()};
-    int it = 0;
-#pragma unroll 1
-    while (true) {
-        bool brk = false;
-        float tmax[2];
-#pragma unroll 1
-        for (; it < n_tiles; ++it) {
-            const int buf = it & 1;
-            const bool has_next = it + 1 < n_tiles;
-            const int64_t nk0 = seg_k0;
-            const int64_t nlen = nS.len;
-            if (has_next) load_tile(nS, nk0, buf ^ 1);
 
-            auto qk = [&](int hb, f32x16_t (&sacc)[2]) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) sacc[j][e] = 0.f;
-#pragma unroll
-                for (int ks = 0; ks < 8; ++ks) {
-                    const bf16x8_t kop =
-                        __builtin_bit_cast(bf16x8_t, k_lds[buf][k_pos(32 * hb + l32, 2 * ks + h)]);
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[j][ks], sacc[j], 0, 0, 0);
-                }
-            };
-            auto mask = [&](int hb, f32x16_t (&sacc)[2]) {
-                if (cur_k0 + 32 * hb + 32 > cur_len) {  // keys past the segment end
-                    const int valid = (int)(cur_len - cur_k0) - 32 * hb;
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            const int key = 8 * (v >> 2) + 4 * h + (v & 3);
-                            if (key >= valid) sacc[j][v] = -__builtin_huge_valf();
-                        }
-                }
-            };
-            auto rowmax = [&](const f32x16_t (&sacc)[2], float (&mx)[2]) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    float m = sacc[j][0];
-#pragma unroll
-                    for (int v = 1; v < 16; ++v) m = fmaxf(m, sacc[j][v]);
-                    mx[j] = m;
-                }
-            };
-            // P = exp2(s c - m_ref) packed to BF16; row sums returned in `sums`
-            // (committed to l only once the tile is known not to be redone).
-            auto expo = [&](const f32x16_t (&sacc)[2], bf16x8_t (&pop)[2][2], float (&sums)[2]) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    float p[16];
-                    float sum = 0.f;
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][v], a.scale_log2, -m_ref[j]));
-                        sum += p[v];
-                    }
-#pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2) {
-                        uint4 u;
-                        u.x = pack_bf16x2(p[8 * s2 + 0], p[8 * s2 + 1]);
-                        u.y = pack_bf16x2(p[8 * s2 + 2], p[8 * s2 + 3]);
-                        u.z = pack_bf16x2(p[8 * s2 + 4], p[8 * s2 + 5]);
-                        u.w = pack_bf16x2(p[8 * s2 + 6], p[8 * s2 + 7]);
-                        pop[j][s2] = __builtin_bit_cast(bf16x8_t, u);
-                    }
-                    sums[j] = sum;
-                }
-            };
-            auto pv = [&](int hb, const bf16x8_t (&pop)[2][2]) {
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-                    for (int dt = 0; dt < 4; ++dt) {
-                        const bf16x8_t vop =
-                            __builtin_bit_cast(bf16x8_t, v_lds[buf][vt_pos(32 * dt + l32, 2 * (2 * hb + s2) + h)]);
-#pragma unroll
-                        for (int j = 0; j < 2; ++j)
-                            oacc[dt][j] =
-                                __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[j][s2], oacc[dt][j], 0, 0, 0);
-                    }
-                }
-            };
-            // Interleave each MFMA with a few VALU instructions of the other
-            // half's softmax and the LDS operand read it needs.
-#define H3_INTERLEAVE(VALU)                                           \
-    do {                                                              \
-        _Pragma("unroll") for (int i_ = 0; i_ < 16; ++i_) {           \
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        \
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        \
-            __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);     \
-        }                                                             \
-    } while (0)
-
-            f32x16_t s0[2], s1[2];
-            bf16x8_t p0[2][2], p1[2][2];
-            float mx0[2], mx1[2], sum0[2], sum1[2];
-            qk(0, s0);                                   // A: S0
-            mask(0, s0);
-            {                                            // B: S1 || max(S0), P0
-                qk(1, s1);
-                rowmax(s0, mx0);
-                expo(s0, p0, sum0);
-                H3_INTERLEAVE(8);
-            }
-            mask(1, s1);
-            rowmax(s1, mx1);
+    // One half tile u = 2t + odd (uu = u % 4, so the tile parity tp = uu / 2
+    // and the buffers are compile-time): S of half u is in sv, its maximum in
+    // tmaxr.
+    //   check  half u's maximum against m_ref, rescale O and l if needed;
+    //   sync   even u: V^T of tile t has landed, every wave is done with V^T of
+    //          tile t-1 -> load V^T of tile t+1 into that buffer;
+    //          odd u:  K of tile t+1 has landed, every wave is done with K of
+    //          tile t -> load K of tile t+2 into that buffer.
+    //          The other operand's 4 loads may stay in flight (vmcnt 4).
+    //   X      S of half u+1 = K Q^T into sacc (16 MFMAs) || p = exp2(s c -
+    //          m_ref) in sv and BF16 P of half u || this half's 4 loads;
+    //   mask   keys past the segment end in half u+1 (last tile of a segment);
+    //   Y      O += V^T P^T of half u (16 MFMAs) || row sums of half u, then
+    //          sv = S of half u+1 and its maximum.
+    // Each phase is 16 slots of one MFMA plus its share of the other work, in
+    // a fixed order (sched_barrier); the empty asm statements keep each slot's
+    // VALU work in its slot. Past the last tile the loads return zero and the
+    // scores of half u+1 go unused.
+    auto hiter = [&](int uu) {
+        const int tp = uu >> 1, odd = uu & 1;
+        // check
+        {
             bool over = false;
+            float tm[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                float m = fmaxf(mx0[j], mx1[j]);
-                m = fmaxf(m, __shfl_xor(m, 32)) * a.scale_log2;
-                tmax[j] = m;
+                const float m = fmaxf(tmaxr[j], __shfl_xor(tmaxr[j], 32)) * a.scale_log2;
+                tm[j] = m;
                 over |= m > m_ref[j] + kSlack;
             }
-            if (__any(over)) {  // leave before any P.V of this tile
-                brk = true;
-                break;
-            }
-            {                                            // C: O += V0 P0 || P1
-                pv(0, p0);
-                expo(s1, p1, sum1);
-                H3_INTERLEAVE(7);
-            }
-            pv(1, p1);                                   // D: O += V1 P1
+            if (__any(over)) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) l_run[j] += sum0[j] + sum1[j];
-
-            if (has_next) {
-                cur_len = nlen;
-                cur_k0 = nk0;
-                advance();
+                for (int j = 0; j < 2; ++j) {
+                    const float m_new = fmaxf(m_ref[j], tm[j]);
+                    const float alpha = __builtin_amdgcn_exp2f(m_ref[j] - m_new);
+                    m_ref[j] = m_new;
+                    l_run[j] *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) oacc[dt][j][e] *= alpha;
+                        asm volatile("" : "+a"(oacc[dt][j]));
+                    }
+                }
             }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's slabs landed
-            __syncthreads();                                   // all slabs visible, buf free
         }
-        if (!brk) break;
-        // Rare path: raise the reference maximum and rescale O and l.
+        // sync
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        i32x4_t rl;
+        int voffs[4];
+        uint32_t m0b;
+        if (odd) {
+            const int rows = min((int)(kc.S.len - kc.k0), BKV);
+            rl = raw_rsrc(kc.S.k + kc.k0 * kc.S.ldk + head * D, ((int64_t)(rows - 1) * kc.S.ldk + D) * 2);
+            if (kc.seg >= a.n_seg) rl.z = 0;
+            m0b = lds0 + (uint32_t)((tp * KB + 64 * 4 * wave) * 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) voffs[i] = k_voff[i];
+        } else {
+            rl = raw_rsrc(vc.S.vt + (int64_t)head * D * vc.S.lpad + vc.k0, (D * vc.S.lpad - vc.k0) * 2);
+            if (vc.seg >= a.n_seg) rl.z = 0;
+            m0b = lds0 + (uint32_t)((2 * KB + (tp ^ 1) * VB + 64 * 4 * wave) * 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) voffs[i] = v_voff[i];
+            vk_next = valid_keys(vc);
+        }
+
+        // X: QK of half u+1 (K buffer of tile (u+1)/2, key half (u+1)%2)
+        const int kb = odd ? (tp ^ 1) : tp, khb = odd ? 0 : 1;
+        bf16x8_t pop[2][2];  // [j][s2]: keys 16 s2 .. +15 of the half, query block j
+        bf16x8_t kop[8];
+        uint32_t pk[8];
+        kop[0] = kop_read(kb, 8 * khb + 0);
+        kop[1] = kop_read(kb, 8 * khb + 1);
+#pragma unroll
+        for (int sl = 0; sl < 16; ++sl) {
+            const int ks = sl >> 1, j = sl & 1;
+            sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[j][ks], ks == 0 ? f32x16_t{} : sacc[j], 0,
+                                                              0, 0);
+            if (j == 0 && ks + 2 < 8) kop[ks + 2] = kop_read(kb, 8 * khb + ks + 2);
+            if ((sl & 3) == 1) dma_slab(rl, m0b + (uint32_t)(64 * 16 * (sl >> 2)), voffs[sl >> 2], 0);
+            {
+                const int gj = sl >> 3, e = sl & 7;
+                const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[gj][2 * e], a.scale_log2, -m_ref[gj]));
+                const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[gj][2 * e + 1], a.scale_log2, -m_ref[gj]));
+                sv[gj][2 * e] = x0;
+                sv[gj][2 * e + 1] = x1;
+                pk[e] = pack_bf16x2(x0, x1);
+                asm volatile("" : "+v"(pk[e]));
+                if (e == 7) {
+                    pop[gj][0] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+                    pop[gj][1] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[4], pk[5], pk[6], pk[7]));
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        pin_sacc();
+        if (odd) {
+            advance(kc, true);
+        } else {
+            advance(vc, false);
+        }
+
+        // mask: half u+1 is the second half of tile t (even u) or the first
+        // half of tile t+1 (odd u)
+        {
+            const int valid = odd ? min(vk_next, 32) : vk_cur - 32;
+            if (valid < 32) mask(sacc, valid, true);
+        }
+
+        // Y: PV of half u (V^T buffer of tile t, key half odd)
+        bf16x8_t vop[8];
+        vop[0] = vop_read(tp, 8 * odd + 0);
+        vop[1] = vop_read(tp, 8 * odd + 1);
+        float sm[2], mx[2];
+#pragma unroll
+        for (int sl = 0; sl < 16; ++sl) {
+            const int pr = sl >> 1, j = sl & 1, s2 = pr >> 2, dt = pr & 3;
+            oacc[dt][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[pr], pop[j][s2], oacc[dt][j], 0, 0, 0);
+            if (j == 0 && pr + 2 < 8) vop[pr + 2] = vop_read(tp, 8 * odd + pr + 2);
+            {
+                const int gj = sl >> 3, e = sl & 7;
+                const float add = sv[gj][2 * e] + sv[gj][2 * e + 1];
+                sm[gj] = e == 0 ? add : sm[gj] + add;
+                const float y0 = sacc[gj][2 * e], y1 = sacc[gj][2 * e + 1];
+                sv[gj][2 * e] = y0;
+                sv[gj][2 * e + 1] = y1;
+                mx[gj] = e == 0 ? fmaxf(y0, y1) : fmaxf(mx[gj], fmaxf(y0, y1));
+                asm volatile("" : "+v"(sm[gj]), "+v"(mx[gj]), "+v"(sv[gj][2 * e]), "+v"(sv[gj][2 * e + 1]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const float m_new = fmaxf(m_ref[j], tmax[j]);
-            const float alpha = __builtin_amdgcn_exp2f(m_ref[j] - m_new);
-            m_ref[j] = m_new;
-            l_run[j] *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) oacc[dt][j][e] *= alpha;
+            l_run[j] += sm[j];
+            tmaxr[j] = mx[j];
         }
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) asm volatile("" : "+a"(oacc[dt][j]));
+        if (odd) vk_cur = vk_next;
+    };
+
+    const int n_half = 2 * n_tiles;
+    int u = 0;
+#pragma unroll 1
+    for (; u + 4 <= n_half; u += 4) {
+        hiter(0);
+        hiter(1);
+        hiter(2);
+        hiter(3);
     }
+    if (u < n_half) {
+        hiter(0);
+        hiter(1);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads past the end
 
     // ---- normalise and store: lane holds O[q][32 dt + 8 g + 4 h + (0..3)] ----
 #pragma unroll
