@@ -77,6 +77,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
     return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, n, 0x00020000);
 }
 
+// Maximum / sum of a value over the lane pair (l, l ^ 32), in every lane
+// (v_permlane32_swap: no LDS round trip).
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // LDS layouts (16-byte chunks):
 //  K tile  [64 keys][16 chunks]: chunk c of key r at c ^ (r & 15).
 //  V^T tile [128 d][8 chunks]  : logical chunk c of row d at c ^ ((d ^ (d >> 3)) & 7);
@@ -308,59 +319,65 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
 #pragma unroll
     for (int j = 0; j < 2; ++j) sv[j] = sacc[j];
     if (vk_cur < 32) mask(sv, vk_cur, false);
+
+    // Softmax with a per-row reference maximum m_ref (exp2 domain). The
+    // scores are kept shifted, y = s c - m_ref, so p = exp2(y); while no y
+    // exceeds kSlack, p <= 2^kSlack and O and l need no rescaling. m_ref
+    // starts at the first half tile's maximum (half 0 always has a valid
+    // key); a half tile whose maximum y breaks the bound raises m_ref and
+    // rescales O, l and its own y before any of its P is formed, so nothing
+    // is ever recomputed.
+    constexpr float kSlack = 10.0f;
+    float m_ref[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         float m = sv[j][0];
 #pragma unroll
         for (int v = 1; v < 16; ++v) m = fmaxf(m, sv[j][v]);
-        tmaxr[j] = m;
+        m_ref[j] = pair_max(m) * a.scale_log2;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sv[j][v] = __builtin_fmaf(sv[j][v], a.scale_log2, -m_ref[j]);
+        tmaxr[j] = 0.f;
     }
 
-    // Softmax with a per-row reference maximum m_ref (exp2 domain): p =
-    // exp2(s c - m_ref) stays <= 2^kSlack while no score exceeds m_ref + kSlack,
-    // so O and l are rescaled only when a half tile's maximum breaks that
-    // bound (always at the first, rarely afterwards). The check runs before
-    // any P of the half tile is formed, so nothing is ever recomputed.
-    constexpr float kSlack = 10.0f;
-    float m_ref[2] = {-__builtin_huge_valf(), -__builtin_huge_valf()};
-
     // One half tile u = 2t + odd (uu = u % 4, so the tile parity tp = uu / 2
-    // and the buffers are compile-time): S of half u is in sv, its maximum in
-    // tmaxr.
-    //   check  half u's maximum against m_ref, rescale O and l if needed;
+    // and the buffers are compile-time): the shifted scores y of half u are
+    // in sv, their per-lane maximum in tmaxr.
+    //   check  half u's maximum y against kSlack, rescale if needed;
     //   sync   even u: V^T of tile t has landed, every wave is done with V^T of
     //          tile t-1 -> load V^T of tile t+1 into that buffer;
     //          odd u:  K of tile t+1 has landed, every wave is done with K of
     //          tile t -> load K of tile t+2 into that buffer.
     //          The other operand's 4 loads may stay in flight (vmcnt 4).
-    //   X      S of half u+1 = K Q^T into sacc (16 MFMAs) || p = exp2(s c -
-    //          m_ref) in sv and BF16 P of half u || this half's 4 loads;
+    //   X      S of half u+1 = K Q^T into sacc (16 MFMAs) || p = exp2(y) in sv
+    //          and BF16 P of half u || this half's 4 loads;
     //   mask   keys past the segment end in half u+1 (last tile of a segment);
     //   Y      O += V^T P^T of half u (16 MFMAs) || row sums of half u, then
-    //          sv = S of half u+1 and its maximum.
+    //          sv = y of half u+1 and its maximum.
     // Each phase is 16 slots of one MFMA plus its share of the other work, in
     // a fixed order (sched_barrier); the empty asm statements keep each slot's
     // VALU work in its slot. Past the last tile the loads return zero and the
     // scores of half u+1 go unused.
     auto hiter = [&](int uu) {
         const int tp = uu >> 1, odd = uu & 1;
-        // check
+        // check (tmaxr: per-lane maximum of half u's shifted scores)
         {
             bool over = false;
             float tm[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const float m = fmaxf(tmaxr[j], __shfl_xor(tmaxr[j], 32)) * a.scale_log2;
-                tm[j] = m;
-                over |= m > m_ref[j] + kSlack;
+                tm[j] = pair_max(tmaxr[j]);
+                over |= tm[j] > kSlack;
             }
             if (__any(over)) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const float m_new = fmaxf(m_ref[j], tm[j]);
-                    const float alpha = __builtin_amdgcn_exp2f(m_ref[j] - m_new);
-                    m_ref[j] = m_new;
+                    const float d = fmaxf(tm[j], 0.f);
+                    const float alpha = __builtin_amdgcn_exp2f(-d);
+                    m_ref[j] += d;
                     l_run[j] *= alpha;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) sv[j][v] -= d;
 #pragma unroll
                     for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
@@ -397,31 +414,44 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
         const int kb = odd ? (tp ^ 1) : tp, khb = odd ? 0 : 1;
         bf16x8_t pop[2][2];  // [j][s2]: keys 16 s2 .. +15 of the half, query block j
         bf16x8_t kop[8];
-        uint32_t pk[8];
+        // Softmax numerators p = exp2(y) of half u, staggered over the slots
+        // so no slot waits on its own results: slot w = 8 gj + e takes exp2
+        // of score pair w and the BF16 pack of pair w-1.
+        uint32_t pk[16];
+        float x[16][2];
+        auto pack_pair = [&](int w) {
+            pk[w] = pack_bf16x2(x[w][0], x[w][1]);
+            asm volatile("" : "+v"(pk[w]));
+        };
         kop[0] = kop_read(kb, 8 * khb + 0);
         kop[1] = kop_read(kb, 8 * khb + 1);
+        kop[2] = kop_read(kb, 8 * khb + 2);
 #pragma unroll
         for (int sl = 0; sl < 16; ++sl) {
             const int ks = sl >> 1, j = sl & 1;
             sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[j][ks], ks == 0 ? f32x16_t{} : sacc[j], 0,
                                                               0, 0);
-            if (j == 0 && ks + 2 < 8) kop[ks + 2] = kop_read(kb, 8 * khb + ks + 2);
+            if (j == 0 && ks + 3 < 8) kop[ks + 3] = kop_read(kb, 8 * khb + ks + 3);
             if ((sl & 3) == 1) dma_slab(rl, m0b + (uint32_t)(64 * 16 * (sl >> 2)), voffs[sl >> 2], 0);
             {
                 const int gj = sl >> 3, e = sl & 7;
-                const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[gj][2 * e], a.scale_log2, -m_ref[gj]));
-                const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[gj][2 * e + 1], a.scale_log2, -m_ref[gj]));
-                sv[gj][2 * e] = x0;
-                sv[gj][2 * e + 1] = x1;
-                pk[e] = pack_bf16x2(x0, x1);
-                asm volatile("" : "+v"(pk[e]));
-                if (e == 7) {
-                    pop[gj][0] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-                    pop[gj][1] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[4], pk[5], pk[6], pk[7]));
-                }
+                x[sl][0] = __builtin_amdgcn_exp2f(sv[gj][2 * e]);
+                x[sl][1] = __builtin_amdgcn_exp2f(sv[gj][2 * e + 1]);
+                sv[gj][2 * e] = x[sl][0];
+                sv[gj][2 * e + 1] = x[sl][1];
+                if (sl >= 1) pack_pair(sl - 1);
+                asm volatile("" : "+v"(x[sl][0]), "+v"(x[sl][1]));
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        pack_pair(15);
+#pragma unroll
+        for (int gj = 0; gj < 2; ++gj)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int w = 8 * gj + 4 * s2;
+                pop[gj][s2] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[w], pk[w + 1], pk[w + 2], pk[w + 3]));
+            }
         pin_sacc();
         if (odd) {
             advance(kc, true);
@@ -440,27 +470,46 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
         bf16x8_t vop[8];
         vop[0] = vop_read(tp, 8 * odd + 0);
         vop[1] = vop_read(tp, 8 * odd + 1);
-        float sm[2], mx[2];
+        vop[2] = vop_read(tp, 8 * odd + 2);
+        // Row sums of half u and the shifted copy / maximum of half u+1,
+        // staggered: slot w adds p pair w (two partial sums per query block),
+        // stores pair w-1 of the new scores from AGPRs into sv as y = s c -
+        // m_ref (pair w-1 was summed the slot before) and takes the maximum
+        // of pair w-2.
+        float sa[2] = {0.f, 0.f}, sb[2] = {0.f, 0.f};
+        float mx[2] = {-__builtin_huge_valf(), -__builtin_huge_valf()};
+        auto copy_pair = [&](int w) {
+            const int gj = w >> 3, e = w & 7;
+            sv[gj][2 * e] = __builtin_fmaf(sacc[gj][2 * e], a.scale_log2, -m_ref[gj]);
+            sv[gj][2 * e + 1] = __builtin_fmaf(sacc[gj][2 * e + 1], a.scale_log2, -m_ref[gj]);
+            asm volatile("" : "+v"(sv[gj][2 * e]), "+v"(sv[gj][2 * e + 1]));
+        };
+        auto max_pair = [&](int w) {
+            const int gj = w >> 3, e = w & 7;
+            mx[gj] = fmaxf(mx[gj], fmaxf(sv[gj][2 * e], sv[gj][2 * e + 1]));
+            asm volatile("" : "+v"(mx[gj]));
+        };
 #pragma unroll
         for (int sl = 0; sl < 16; ++sl) {
             const int pr = sl >> 1, j = sl & 1, s2 = pr >> 2, dt = pr & 3;
             oacc[dt][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[pr], pop[j][s2], oacc[dt][j], 0, 0, 0);
-            if (j == 0 && pr + 2 < 8) vop[pr + 2] = vop_read(tp, 8 * odd + pr + 2);
+            if (j == 0 && pr + 3 < 8) vop[pr + 3] = vop_read(tp, 8 * odd + pr + 3);
             {
                 const int gj = sl >> 3, e = sl & 7;
-                const float add = sv[gj][2 * e] + sv[gj][2 * e + 1];
-                sm[gj] = e == 0 ? add : sm[gj] + add;
-                const float y0 = sacc[gj][2 * e], y1 = sacc[gj][2 * e + 1];
-                sv[gj][2 * e] = y0;
-                sv[gj][2 * e + 1] = y1;
-                mx[gj] = e == 0 ? fmaxf(y0, y1) : fmaxf(mx[gj], fmaxf(y0, y1));
-                asm volatile("" : "+v"(sm[gj]), "+v"(mx[gj]), "+v"(sv[gj][2 * e]), "+v"(sv[gj][2 * e + 1]));
+                sa[gj] += sv[gj][2 * e];
+                sb[gj] += sv[gj][2 * e + 1];
+                asm volatile("" : "+v"(sa[gj]), "+v"(sb[gj]));
+                if (sl >= 1) copy_pair(sl - 1);
+                if (sl >= 2) max_pair(sl - 2);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        copy_pair(15);
+        max_pair(14);
+        max_pair(15);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            l_run[j] += sm[j];
+            l_run[j] += sa[j] + sb[j];
             tmaxr[j] = mx[j];
         }
         if (odd) vk_cur = vk_next;
@@ -484,7 +533,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     // ---- normalise and store: lane holds O[q][32 dt + 8 g + 4 h + (0..3)] ----
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const float l_tot = l_run[j] + __shfl_xor(l_run[j], 32);
+        const float l_tot = pair_sum(l_run[j]);
         const float inv = 1.0f / l_tot;
         const int64_t q = qw + 32 * j + l32;
         if (q < a.rows) {
