@@ -418,9 +418,9 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
         // so no slot waits on its own results: slot w = 8 gj + e takes exp2
         // of score pair w and the BF16 pack of pair w-1.
         uint32_t pk[16];
-        float x[16][2];
         auto pack_pair = [&](int w) {
-            pk[w] = pack_bf16x2(x[w][0], x[w][1]);
+            const int gj = w >> 3, e = w & 7;
+            pk[w] = pack_bf16x2(sv[gj][2 * e], sv[gj][2 * e + 1]);
             asm volatile("" : "+v"(pk[w]));
         };
         kop[0] = kop_read(kb, 8 * khb + 0);
@@ -435,12 +435,10 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
             if ((sl & 3) == 1) dma_slab(rl, m0b + (uint32_t)(64 * 16 * (sl >> 2)), voffs[sl >> 2], 0);
             {
                 const int gj = sl >> 3, e = sl & 7;
-                x[sl][0] = __builtin_amdgcn_exp2f(sv[gj][2 * e]);
-                x[sl][1] = __builtin_amdgcn_exp2f(sv[gj][2 * e + 1]);
-                sv[gj][2 * e] = x[sl][0];
-                sv[gj][2 * e + 1] = x[sl][1];
+                sv[gj][2 * e] = __builtin_amdgcn_exp2f(sv[gj][2 * e]);
+                sv[gj][2 * e + 1] = __builtin_amdgcn_exp2f(sv[gj][2 * e + 1]);
+                asm volatile("" : "+v"(sv[gj][2 * e]), "+v"(sv[gj][2 * e + 1]));
                 if (sl >= 1) pack_pair(sl - 1);
-                asm volatile("" : "+v"(x[sl][0]), "+v"(x[sl][1]));
             }
             __builtin_amdgcn_sched_barrier(0);
         }
