@@ -109,7 +109,7 @@ __device__ __forceinline__ SegState seg_of(const AttnArgs &a, int s) {
 // K / V^T tile stream: position (segment, first key) of the next tile to load.
 struct Cursor {
     int seg;
-    int64_t k0;
+    int k0, len;  // first key of the tile, keys in the segment (32-bit: scalar compares)
     SegState S;
 };
 
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
 
     // Two cursors over the same tile sequence: K runs two tiles ahead of the
     // tile being finished, V^T one tile ahead.
-    Cursor kc{0, 0, seg_of(a, 0)}, vc{0, 0, seg_of(a, 0)};
+    Cursor kc{0, 0, (int)a.slen[0], seg_of(a, 0)}, vc{0, 0, (int)a.slen[0], seg_of(a, 0)};
     int k_voff[4], v_voff[4];
     auto set_k = [&]() {
 #pragma unroll
@@ -206,11 +206,12 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     set_v();
     auto advance = [&](Cursor &c, bool is_k) {
         c.k0 += BKV;
-        if (c.k0 >= c.S.len) {
+        if (c.k0 >= c.len) {
             ++c.seg;
             c.k0 = 0;
             if (c.seg < a.n_seg) {
                 c.S = seg_of(a, c.seg);
+                c.len = (int)c.S.len;
                 if (is_k) set_k();
                 else set_v();
             }
@@ -218,21 +219,21 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     };
     // Keys of the cursor's tile that exist (64 past the last tile: nothing to mask).
     auto valid_keys = [&](const Cursor &c) -> int {
-        return c.seg < a.n_seg ? min((int)(c.S.len - c.k0), BKV) : BKV;
+        return c.seg < a.n_seg ? min(c.len - c.k0, BKV) : BKV;
     };
     // Issue this wave's 4 slab loads of the cursor's tile into buffer b. Past
     // the last tile the descriptor has length zero: the loads return zero and
     // touch no memory, so every iteration issues the same loads.
     auto issue_k = [&](int b, int half) {
-        const int rows = min((int)(kc.S.len - kc.k0), BKV);
-        i32x4_t r = raw_rsrc(kc.S.k + kc.k0 * kc.S.ldk + head * D, ((int64_t)(rows - 1) * kc.S.ldk + D) * 2);
+        const int rows = min(kc.len - kc.k0, BKV);
+        i32x4_t r = raw_rsrc(kc.S.k + (int64_t)kc.k0 * kc.S.ldk + head * D, ((int64_t)(rows - 1) * kc.S.ldk + D) * 2);
         if (kc.seg >= a.n_seg) r.z = 0;
 #pragma unroll
         for (int i = 2 * half; i < 2 * half + 2; ++i)
             dma_slab(r, lds0 + (uint32_t)((b * KB + 64 * (4 * wave + i)) * 16), k_voff[i], 0);
     };
     auto issue_v = [&](int b, int half) {
-        i32x4_t r = raw_rsrc(vc.S.vt + (int64_t)head * D * vc.S.lpad + vc.k0, (D * vc.S.lpad - vc.k0) * 2);
+        i32x4_t r = raw_rsrc(vc.S.vt + (int64_t)head * D * vc.S.lpad + vc.k0, ((int64_t)D * vc.S.lpad - vc.k0) * 2);
         if (vc.seg >= a.n_seg) r.z = 0;
 #pragma unroll
         for (int i = 2 * half; i < 2 * half + 2; ++i)
@@ -395,14 +396,14 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
         int voffs[4];
         uint32_t m0b;
         if (odd) {
-            const int rows = min((int)(kc.S.len - kc.k0), BKV);
-            rl = raw_rsrc(kc.S.k + kc.k0 * kc.S.ldk + head * D, ((int64_t)(rows - 1) * kc.S.ldk + D) * 2);
+            const int rows = min(kc.len - kc.k0, BKV);
+            rl = raw_rsrc(kc.S.k + (int64_t)kc.k0 * kc.S.ldk + head * D, ((int64_t)(rows - 1) * kc.S.ldk + D) * 2);
             if (kc.seg >= a.n_seg) rl.z = 0;
             m0b = lds0 + (uint32_t)((tp * KB + 64 * 4 * wave) * 16);
 #pragma unroll
             for (int i = 0; i < 4; ++i) voffs[i] = k_voff[i];
         } else {
-            rl = raw_rsrc(vc.S.vt + (int64_t)head * D * vc.S.lpad + vc.k0, (D * vc.S.lpad - vc.k0) * 2);
+            rl = raw_rsrc(vc.S.vt + (int64_t)head * D * vc.S.lpad + vc.k0, ((int64_t)D * vc.S.lpad - vc.k0) * 2);
             if (vc.seg >= a.n_seg) rl.z = 0;
             m0b = lds0 + (uint32_t)((2 * KB + (tp ^ 1) * VB + 64 * 4 * wave) * 16);
 #pragma unroll
