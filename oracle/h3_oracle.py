@@ -365,14 +365,16 @@ def block_forward(x, w, mod, *, heads: int, head_dim: int, ffn: int, valid_len: 
 
 def block_forward_rows(x, w, mod, rows, *, heads: int, head_dim: int, ffn: int, valid_len: int,
                        rot_dim: int = 64, theta: float = 10000.0, eps: float = 1e-6, norm_type: int = 0,
-                       pairing: int = 0, mod_idx=None, pos=None, scale=None, q_chunk: int = 64):
-    """block_forward restricted to the selected valid rows (dense attention).
+                       pairing: int = 0, mod_idx=None, pos=None, groups=None, scale=None, q_chunk: int = 64):
+    """block_forward restricted to the selected valid rows.
 
     Attention reads the keys and values of every valid row, so h, k~ and v are
     formed for all valid rows; every other step (q~, attention, the output
     projection, the FFN and the residuals) runs on the selected rows only. The
-    definitions are those of block_forward, step for step. Returns a dict of
-    [len(rows), .] arrays."""
+    definitions are those of block_forward, step for step, including its
+    grouped attention (`groups` as in block_forward: a selected row attends
+    over the segments of the group that contains it; a row outside every
+    group gets o = 0). Returns a dict of [len(rows), .] arrays."""
     x = np.asarray(x, dtype=F64)
     H = x.shape[1]
     V = int(valid_len)
@@ -392,7 +394,25 @@ def block_forward_rows(x, w, mod, rows, *, heads: int, head_dim: int, ffn: int, 
     h = h_all[rows]
     q = linear(h, w_qkv[:H], b(0))
     qn = qk_norm_rope(q, posv[rows], heads, head_dim, w['q_gain'], eps, rot_dim, theta, pairing)
-    o = attention(qn, kn, v_all, heads, head_dim, scale, q_chunk)
+    if groups is None:
+        o = attention(qn, kn, v_all, heads, head_dim, scale, q_chunk)
+    else:
+        o = np.zeros((len(rows), H), dtype=F64)
+        for (qb, qe, segs) in groups:
+            sel = np.nonzero((rows >= qb) & (rows < qe))[0]
+            if len(sel) == 0:
+                continue
+            ks, vs = [], []
+            for sg in segs:
+                if isinstance(sg[0], str):
+                    _, b0, ln = sg
+                    ks.append(kn[b0:b0 + ln])
+                    vs.append(v_all[b0:b0 + ln])
+                else:
+                    ks.append(np.asarray(sg[0], dtype=F64))
+                    vs.append(np.asarray(sg[1], dtype=F64))
+            o[sel] = attention(qn[sel], np.concatenate(ks, axis=0), np.concatenate(vs, axis=0), heads, head_dim,
+                               scale, q_chunk)
     a = linear(o, w['w_o'], w.get('b_o'))
     x1 = gated_residual(x[rows], m[:, GATE_A], a)
     h2 = modulate_norm(x1, m[:, SHIFT_F], m[:, SCALE_F], eps, norm_type)

@@ -176,3 +176,76 @@ def test_block_full_width_4096_sampled_rows():
                       ("x1", f64(b.inter(h3.H3_WS_X1)[rows])), ("h2", f64(b.inter(h3.H3_WS_H2)[rows])),
                       ("g", f64(b.inter(h3.H3_WS_G)[rows])), ("y", f64(y[rows]))):
         assert_parity(got, ref[name], name, slack=BF16_SLACK if name == "g" else 0.0)
+
+
+def _check_rows(b: Block, y, ref, rows, label):
+    H = b.s.hidden
+    qkv = f64(b.inter(h3.H3_WS_QKV)[rows])
+    for name, got in (("h", f64(b.inter(h3.H3_WS_H)[rows])), ("q", qkv[:, :H]), ("k", qkv[:, H:2 * H]),
+                      ("v", qkv[:, 2 * H:]), ("o", f64(b.inter(h3.H3_WS_O)[rows])),
+                      ("x1", f64(b.inter(h3.H3_WS_X1)[rows])), ("h2", f64(b.inter(h3.H3_WS_H2)[rows])),
+                      ("g", f64(b.inter(h3.H3_WS_G)[rows])), ("y", f64(y[rows]))):
+        assert_parity(got, ref[name], f"{label} {name}", slack=BF16_SLACK if name == "g" else 0.0)
+
+
+@pytest.mark.timeout(900)
+def test_block_full_58816_sampled_rows():
+    """The benchmarked workload itself: full width at 58,816 buffer rows with
+    58,758 valid ([text 512 | audio 1,024 | video 57,280] packed, padding
+    suffix), one h3_block_forward as bench.py launches it. The oracle forms K
+    and V for every valid row and every other step on 48 sampled rows (segment
+    boundaries and both ends included); the padding rows of y and of every
+    intermediate must be zero."""
+    print("block full 58816 (sampled rows)", flush=True)
+    s = I.FULL_58816
+    b = Block(s, tag="full3")
+    xb = I.activations(s, tag="xf3")
+    y = b.run(xb)
+    V = s.valid_len
+    rows = I.rng_for("rows58816").choice(V, size=42, replace=False)
+    rows = np.unique(np.concatenate([rows, [0, 511, 512, 1535, 1536, V - 1]]))
+    print(f"  oracle on {len(rows)} rows", flush=True)
+    ref = O.block_forward_rows(O.bf16_to_f64(xb), b.wo, b.mod.astype(np.float64), rows, heads=s.heads,
+                               head_dim=128, ffn=s.ffn, valid_len=V, rot_dim=s.rot_dim)
+    _check_rows(b, y, ref, rows, "58816")
+    for which, name in ((h3.H3_WS_H, "h"), (h3.H3_WS_QKV, "qkv"), (h3.H3_WS_O, "o"), (h3.H3_WS_X1, "x1"),
+                        (h3.H3_WS_H2, "h2"), (h3.H3_WS_G, "g")):
+        assert_zero_rows(b.inter(which), V, name)
+    assert_zero_rows(y, V, "y")
+
+
+@pytest.mark.timeout(900)
+def test_block_streaming_full_width_sampled_rows():
+    """The streaming workload at full width: current chunk [cond 256 | audio 128
+    | video 5,040] with 15,120 history rows of K/V; cond and audio attend over
+    the current chunk, video over [history ; current]. A denoise forward and
+    the refresh forward (with K/V export of the video rows) are checked on
+    sampled rows of every group; both forwards give the same y bit for bit,
+    and the exported K/V equal the refresh forward's own k~ and v."""
+    print("block streaming full width (sampled rows)", flush=True)
+    s = I.streaming_shape()
+    cond, audio, video, hist = I.STREAM_COND, I.STREAM_AUDIO, I.STREAM_VIDEO, I.STREAM_HISTORY
+    L = s.L_buf
+    b = Block(s, tag="full4")
+    xb = I.activations(s, tag="xf4")
+    hk, hv = I.history_kv(hist, s.hidden, tag="hf4")
+    tk, tv = dev_bf16(hk), dev_bf16(hv)
+    cur = ("self", 0, L)
+    groups = [(0, cond, [cur]), (cond, cond + audio, [cur]), (cond + audio, L, [(tk, tv, 0, hist), cur])]
+    pos = (np.arange(L) + hist).astype(np.int32)
+    y_denoise = bits(b.run(xb, groups=groups, pos=dev_i32(pos)))
+    ek = poison((video, s.hidden))
+    ev = poison((video, s.hidden))
+    y = b.run(xb, groups=groups, pos=dev_i32(pos), kv_export=(ek, ev, cond + audio, video))
+    np.testing.assert_array_equal(bits(y), y_denoise)
+    rows = np.unique(np.concatenate([I.rng_for("rows_stream").choice(L, size=30, replace=False),
+                                     [0, cond - 1, cond, cond + audio - 1, cond + audio, L - 1]]))
+    og = [(0, cond, [("self", 0, L)]), (cond, cond + audio, [("self", 0, L)]),
+          (cond + audio, L, [(O.bf16_to_f64(hk), O.bf16_to_f64(hv)), ("self", 0, L)])]
+    print(f"  oracle on {len(rows)} rows", flush=True)
+    ref = O.block_forward_rows(O.bf16_to_f64(xb), b.wo, b.mod.astype(np.float64), rows, heads=s.heads,
+                               head_dim=128, ffn=s.ffn, valid_len=L, rot_dim=s.rot_dim, groups=og, pos=pos)
+    _check_rows(b, y, ref, rows, "stream")
+    qkv = b.inter(h3.H3_WS_QKV)
+    np.testing.assert_array_equal(bits(ek), bits(qkv[cond + audio:, s.hidden:2 * s.hidden]))
+    np.testing.assert_array_equal(bits(ev), bits(qkv[cond + audio:, 2 * s.hidden:]))

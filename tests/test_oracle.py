@@ -463,3 +463,21 @@ def test_block_rows_equals_full_block_at_those_rows():
     part = O.block_forward_rows(x, w, mod3, rows, valid_len=V, mod_idx=idx, **kw)
     for name in ("h", "q", "k", "v", "o", "x1", "h2", "g", "y"):
         np.testing.assert_allclose(part[name], full[name][rows], rtol=1e-11, atol=1e-12)
+
+
+def test_block_rows_grouped_equals_full_grouped_block():
+    """The sampled-row block with grouped attention (history segment, current
+    chunk, a query row outside every group) equals the full grouped block at
+    those rows."""
+    s, w, x, mod, kw = _tiny_inputs()
+    V = s.valid_len
+    hk, hv = I.history_kv(96, s.hidden, tag="oracle.hist")
+    HK, HV = O.bf16_to_f64(hk), O.bf16_to_f64(hv)
+    groups = [(0, 60, [("self", 0, 60)]), (64, V, [(HK, HV), ("self", 64, V - 64)])]
+    pos = (np.arange(s.L_buf) + 96).astype(np.int32)
+    full = O.block_forward(x, w, mod, valid_len=V, groups=groups, pos=pos, **kw)
+    rows = np.array([0, 59, 61, 64, 300, V - 1])  # row 61 lies outside every group
+    part = O.block_forward_rows(x, w, mod, rows, valid_len=V, groups=groups, pos=pos, **kw)
+    for name in ("h", "q", "k", "v", "o", "x1", "h2", "g", "y"):
+        np.testing.assert_allclose(part[name], full[name][rows], rtol=1e-11, atol=1e-12)
+    assert np.all(part["o"][2] == 0)
