@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import statistics
 import os
 import sys
 import time
@@ -64,19 +65,25 @@ def counter_traffic(kernel: str, source: str):
         return None
 
 
-def time_calls(torch, fn, iters: int, warmup: int) -> float:
-    """Average ms per call with HIP events on the current stream."""
+def time_calls(torch, fn, iters: int, warmup: int, per_call: bool = False):
+    """Average ms per call with HIP events on the current stream (all `iters`
+    calls between one pair of events). With per_call, an event is also
+    recorded between consecutive calls and the per-call times are returned too."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(iters):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1 if per_call else 2)]
+    ev[0].record()
+    for i in range(iters):
         fn()
-    e.record()
+        if per_call:
+            ev[i + 1].record()
+    ev[-1].record()
     torch.cuda.synchronize()
-    return s.elapsed_time(e) / iters
+    mean = ev[0].elapsed_time(ev[-1]) / iters
+    if not per_call:
+        return mean
+    return mean, [ev[i].elapsed_time(ev[i + 1]) for i in range(iters)]
 
 
 def cpu_baseline(seconds_target: float = 20.0):
@@ -158,7 +165,7 @@ def main(argv=None) -> int:
     def step():
         h3.block_forward(dims, weights, x, y, mod, 1, V, ws)
 
-    ms = time_calls(torch, step, a.steps, a.warmup)
+    ms, step_ms = time_calls(torch, step, a.steps, a.warmup, per_call=True)
 
     # Per-kernel breakdown: the block's launches, one at a time, same buffers.
     hbuf, qkv, o, x1, h2, g = (wsv(h3.H3_WS_H, H), wsv(h3.H3_WS_QKV, 3 * H), wsv(h3.H3_WS_O, H),
@@ -181,6 +188,18 @@ def main(argv=None) -> int:
     k_ms["gemm_down_residual"] = time_calls(torch, lambda: h3.linear(
         g, w["w_down"], y, V, h3.H3_EPI_RESIDUAL, resid=x1, gate=mod[:, 5], ld_gate_group=6 * H), kit, 1)
 
+    # Measured ceilings on this GPU: a plain device copy (what the memory-bound
+    # kernels can hope for) and the vendor library's BF16 GEMM on the QKV shape
+    # (hipBLASLt through torch.matmul, no epilogue).
+    csrc = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)   # 1 GiB
+    cdst = torch.empty_like(csrc)
+    copy_ms = time_calls(torch, lambda: cdst.copy_(csrc), 5, 1)
+    copy_gbs = 2.0 * csrc.numel() * 2 / (copy_ms * 1e-3) / 1e9
+    del csrc, cdst
+    hv, wq, qv = hbuf[:V], w["w_qkv"], qkv[:V]
+    lib_ms = time_calls(torch, lambda: torch.matmul(hv, wq.t(), out=qv), 3, 1)
+    lib_tf = 2.0 * V * H * 3 * H / (lib_ms * 1e-3) / 1e12
+
     gemm_f, attn_f = block_flops(V, H, F)
     gflops = {"gemm_qkv": 2.0 * V * H * 3 * H, "gemm_out_residual": 2.0 * V * H * H,
               "gemm_up_swiglu": 2.0 * V * H * 2 * F, "gemm_down_residual": 2.0 * V * F * H, "attention": attn_f}
@@ -191,9 +210,11 @@ def main(argv=None) -> int:
         if k in gflops:
             tf = gflops[k] / (t * 1e-3) / 1e12
             d.update(tflops=round(tf, 1), frac_mfma=round(tf / PEAK_BF16_TFLOPS, 4))
+            if k.startswith("gemm"):
+                d.update(frac_library_gemm=round(tf / lib_tf, 4))
         if k in ebytes:
             gbs = ebytes[k] / (t * 1e-3) / 1e9
-            d.update(gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+            d.update(gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4), frac_copy=round(gbs / copy_gbs, 4))
         kernels[k] = d
 
     attn_tf = gflops["attention"] / (k_ms["attention"] * 1e-3) / 1e12
@@ -215,6 +236,11 @@ def main(argv=None) -> int:
         "config": {"workload": "one full-width H3 DiT block forward, 58,758 valid tokens in a 58,816-token "
                                "buffer", "hidden": H, "heads": heads, "head_dim": 128, "ffn": F, "L_buf": L,
                    "valid_len": V, "rot_dim": 64, "weights": "random-init N(0,0.02)"},
+        "step_ms": {"median": round(statistics.median(step_ms), 3), "min": round(min(step_ms), 3),
+                    "max": round(max(step_ms), 3)},
+        "ceilings": {"copy_gbs": round(copy_gbs, 1), "copy_frac_hbm": round(copy_gbs / PEAK_HBM_GBS, 4),
+                     "library_gemm_tflops": round(lib_tf, 1),
+                     "library_gemm": "hipBLASLt (torch.matmul) BF16 on the QKV shape, no epilogue"},
         "block_tflops": round(total_tf, 1),
         "block_frac_mfma": round(total_tf / PEAK_BF16_TFLOPS, 4),
         "attention_tflops": round(attn_tf, 1),
