@@ -115,6 +115,64 @@ def cpu_baseline(seconds_target: float = 20.0):
             "sample_seconds": round(dt, 3), "sample_gflops_per_s": round((g_s + a_s) / dt / 1e9, 1)}
 
 
+def lora_consumers(torch, h3, dev, gen, L, V, H, heads, F, iters):
+    """Precision-preserving LoRA consumer fusion at the block's full sizes: each
+    consumer fused (it forms bf16(base + delta) itself) against the unfused
+    sequence (a separate BF16 add that stores the sum, then the plain consumer).
+    saved_gb is the sum's HBM write + read that the fusion removes."""
+    def rnd(shape, std=1.0):
+        t = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+        t.mul_(std)
+        return t.to(torch.bfloat16)
+
+    res = {}
+    # QKV consumer: QK-norm + RoPE on q, k and packing of v
+    qkv, dq, tmp = rnd((L, 3 * H), 3.0), rnd((L, 3 * H), 0.3), torch.empty((L, 3 * H), dtype=torch.bfloat16,
+                                                                            device=dev)
+    gq = torch.ones(128, dtype=torch.bfloat16, device=dev)
+    f_ms = time_calls(torch, lambda: h3.qk_norm_rope_lora(qkv[:, :H], qkv[:, H:2 * H], dq[:, :H], dq[:, H:2 * H],
+                                                         gq, gq, V, heads, v=qkv[:, 2 * H:], dv=dq[:, 2 * H:]),
+                      iters, 1)
+
+    def unfused_qkv():
+        torch.add(qkv, dq, out=tmp)
+        h3.qk_norm_rope(tmp[:, :H], tmp[:, H:2 * H], gq, gq, V, heads)
+    u_ms = time_calls(torch, unfused_qkv, iters, 1)
+    res["qk_norm_rope"] = {"fused_ms": round(f_ms, 4), "unfused_ms": round(u_ms, 4),
+                           "saved_gb": round(2 * V * 3 * H * 2 / 1e9, 3)}
+    del qkv, dq, tmp
+    # residual-modulation consumer (out projection -> x1 and the FFN norm)
+    x, br, d = rnd((L, H)), rnd((L, H)), rnd((L, H), 0.05)
+    mod = torch.randn((1, 6, H), generator=gen, device=dev) * 0.1
+    x1, hh, tmp = (torch.empty((L, H), dtype=torch.bfloat16, device=dev) for _ in range(3))
+    f_ms = time_calls(torch, lambda: h3.fused_modulate_norm_lora(x, br, d, mod[:, 2], x1, V, shift=mod[:, 0],
+                                                                scale=mod[:, 1], h_out=hh, ld_mod_group=6 * H),
+                      iters, 1)
+
+    def unfused_mn():
+        torch.add(br, d, out=tmp)
+        h3.fused_modulate_norm(x, mod[:, 0], mod[:, 1], hh, V, branch=tmp, gate=mod[:, 2], x1_out=x1,
+                               ld_mod_group=6 * H)
+    u_ms = time_calls(torch, unfused_mn, iters, 1)
+    res["modulate_norm"] = {"fused_ms": round(f_ms, 4), "unfused_ms": round(u_ms, 4),
+                            "saved_gb": round(2 * V * H * 2 / 1e9, 3)}
+    del x, br, d, x1, hh, tmp
+    # SwiGLU consumer
+    u, du, tmp = rnd((L, 2 * F), 2.0), rnd((L, 2 * F), 0.05), torch.empty((L, 2 * F), dtype=torch.bfloat16,
+                                                                            device=dev)
+    g = torch.empty((L, F), dtype=torch.bfloat16, device=dev)
+    f_ms = time_calls(torch, lambda: h3.swiglu_lora(u, du, g, V, F), iters, 1)
+
+    def unfused_sw():
+        torch.add(u, du, out=tmp)
+        h3.swiglu(tmp, g, V, F)
+    u_ms = time_calls(torch, unfused_sw, iters, 1)
+    res["swiglu"] = {"fused_ms": round(f_ms, 4), "unfused_ms": round(u_ms, 4),
+                     "saved_gb": round(2 * V * 2 * F * 2 / 1e9, 3)}
+    del u, du, tmp, g
+    return res
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +180,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-iters", type=int, default=5)
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the measurements of the rows beyond the block (LoRA consumer fusion)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (the known-size reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -252,6 +312,8 @@ def main(argv=None) -> int:
                      "traffic_unit": "bytes per launch (FETCH_SIZE x2 + WRITE_SIZE x1, copy-calibrated)",
                      "work_per_launch": "4 * 58758^2 * 5376 = 7.424e13 flop (QK^T and PV over valid rows)"},
     }
+    if not a.no_next:
+        out["next"] = {"lora_consumer_fusion": lora_consumers(torch, h3, dev, gen, L, V, H, heads, F, kit)}
     if a.calibration_copy:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)   # 1 GiB
         dst = torch.empty_like(src)

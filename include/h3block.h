@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define H3_ABI_VERSION 1
+#define H3_ABI_VERSION 2
 #define H3_MAX_SEGMENTS 4   /* K/V segments per query group */
 #define H3_MAX_GROUPS 8     /* query groups per attention call */
 
@@ -264,6 +264,49 @@ int h3_swiglu(const uint16_t *u, int64_t ld_u, uint16_t *g, int64_t ld_g,
               int64_t L_buf, int64_t valid_len, int32_t ffn, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * Precision-preserving LoRA consumer fusion ([Sol-H3] §3.5 "Precision-
+ * preserving LoRA fusion" and Appendix B): the base projection output and the
+ * LoRA branch's output delta stay separate (the three GEMMs are unchanged) and
+ * their sum is never stored: the consumer forms s = bf16(base + delta), round
+ * to nearest even, and then runs exactly as its plain entry point does on s.
+ * The result is bit-identical to storing bf16(base + delta) and calling the
+ * plain entry point on it. delta has the shape of base, at its own row
+ * stride, and must not overlap any output. Padding rows follow the plain
+ * entry point.
+ *
+ * h3_qk_norm_rope_lora: the QKV consumer (QK normalization, RoPE, packing):
+ *   q := qk_norm_rope(bf16(q + dq)), k likewise with dk (as h3_qk_norm_rope);
+ *   v := bf16(v + dv) when v is not NULL (dv then required). q, k, v share
+ *   the row stride ld (the column blocks of a packed qkv buffer); dq, dk, dv
+ *   share ld_d.
+ * ------------------------------------------------------------------------- */
+int h3_qk_norm_rope_lora(uint16_t *q, uint16_t *k, uint16_t *v, int64_t ld,
+                         const uint16_t *dq, const uint16_t *dk, const uint16_t *dv, int64_t ld_d,
+                         const uint16_t *q_gain, const uint16_t *k_gain, const int32_t *pos,
+                         int64_t L_buf, int64_t valid_len, int32_t heads, int32_t head_dim,
+                         int32_t rot_dim, int32_t pairing, float theta, float eps, void *stream);
+
+/* h3_fused_modulate_norm_lora: the residual-modulation consumer. branch,
+ * delta and gate are required; s = bf16(branch + delta), then
+ *   gate_bf16 == 0: x1 = bf16(x + gate[i] * s)
+ *   gate_bf16 != 0: x1 = bf16(x + bf16(gate[i] * s))   (the final FFN
+ *                   consumer, which keeps the intermediate BF16 gate product)
+ *   h = bf16(norm(x1) * (1 + scale[i]) + shift[i]) as h3_fused_modulate_norm;
+ * h_out may be NULL (residual only; shift and scale are then not read). */
+int h3_fused_modulate_norm_lora(const uint16_t *x, int64_t ld_x,
+                                const uint16_t *branch, int64_t ld_b, const uint16_t *delta, int64_t ld_d,
+                                const float *shift, const float *scale, const float *gate,
+                                int64_t ld_mod_group, int32_t n_mod_groups, const int32_t *mod_idx,
+                                uint16_t *x1_out, int64_t ld_x1, uint16_t *h_out, int64_t ld_h,
+                                int64_t L_buf, int64_t valid_len, int32_t hidden, float eps,
+                                int32_t norm_type, int32_t gate_bf16, void *stream);
+
+/* h3_swiglu_lora: the SwiGLU consumer. du [L_buf, 2*ffn] at ld_du:
+ *   g[r, j] = bf16(silu(s[r, j]) * s[r, ffn + j]),  s = bf16(u + du). */
+int h3_swiglu_lora(const uint16_t *u, int64_t ld_u, const uint16_t *du, int64_t ld_du,
+                   uint16_t *g, int64_t ld_g, int64_t L_buf, int64_t valid_len, int32_t ffn, void *stream);
+
+/* ---------------------------------------------------------------------------
  * h3_linear - the block's projections as one BF16 MFMA GEMM with FP32
  * accumulation, c = a W^T (+ bias), W stored [N, K] ([Sol-H3] §3.2 packed QKV
  * projection; §3.5 group (1) gated residual and group (3) SwiGLU as epilogues):
@@ -317,6 +360,22 @@ int h3_check_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t l
                     const uint16_t *c, int64_t ldc, int64_t M_buf, int64_t M_valid,
                     int64_t N, int64_t K, int32_t epilogue, const uint16_t *resid,
                     int64_t ld_r, const float *gate, int32_t n_mod_groups);
+
+int h3_check_qk_norm_rope_lora(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t ld,
+                               const uint16_t *dq, const uint16_t *dk, const uint16_t *dv, int64_t ld_d,
+                               const uint16_t *q_gain, const uint16_t *k_gain,
+                               int64_t L_buf, int64_t valid_len, int32_t heads, int32_t head_dim,
+                               int32_t rot_dim, int32_t pairing, float theta, float eps);
+int h3_check_fused_modulate_norm_lora(const uint16_t *x, int64_t ld_x,
+                                      const uint16_t *branch, int64_t ld_b, const uint16_t *delta, int64_t ld_d,
+                                      const float *shift, const float *scale, const float *gate,
+                                      int64_t ld_mod_group, int32_t n_mod_groups,
+                                      const uint16_t *x1_out, int64_t ld_x1,
+                                      const uint16_t *h_out, int64_t ld_h,
+                                      int64_t L_buf, int64_t valid_len, int32_t hidden, float eps,
+                                      int32_t norm_type, int32_t gate_bf16);
+int h3_check_swiglu_lora(const uint16_t *u, int64_t ld_u, const uint16_t *du, int64_t ld_du,
+                         const uint16_t *g, int64_t ld_g, int64_t L_buf, int64_t valid_len, int32_t ffn);
 
 /* Human-readable name of a status code (static string). */
 const char *h3_status_string(int status);

@@ -132,6 +132,25 @@ def gated_residual(x, gate, branch):
     return x + gate * branch
 
 
+# ----------------------------------------------------------------------------
+# Precision-preserving LoRA consumer fusion (Sol-H3 report, §3.5 "Precision-
+# preserving LoRA fusion"; Appendix B "Implementation scope"). The base
+# projection and the LoRA branch each produce a BF16 output; the consumer uses
+# their sum rounded to BF16 (never the unrounded sum, never merged weights).
+# The final FFN consumer also keeps the gate product in BF16.
+# ----------------------------------------------------------------------------
+def lora_input(base, delta):
+    """bf16(base + delta): the exact sum of the two BF16 branch outputs,
+    rounded once to the nearest BF16 value, ties to even."""
+    return round_to_bf16(np.asarray(base, dtype=F64) + np.asarray(delta, dtype=F64))
+
+
+def gated_residual_bf16_product(x, gate, branch):
+    """The final FFN consumer's residual: x + bf16(gate * branch), the gate
+    product rounded to BF16 before the addition."""
+    return np.asarray(x, dtype=F64) + round_to_bf16(np.asarray(gate, dtype=F64) * np.asarray(branch, dtype=F64))
+
+
 def gather_mod(mod: np.ndarray, mod_idx, n_rows: int) -> np.ndarray:
     """Per-row modulation rows: entry mod_idx[r] of the [G, 6, H] table, or
     entry 0 for every row when no index is given (broadcast, reading R6).

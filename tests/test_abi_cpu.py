@@ -40,7 +40,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert h3.LIB.h3_abi_version() == 1
+    declared = int(re.search(r"#define H3_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert h3.LIB.h3_abi_version() == declared
     assert h3.status_string(h3.H3_ERR_ALIGN).startswith("H3_ERR_ALIGN")
     assert "unknown" in h3.status_string(99)
 
@@ -223,3 +224,47 @@ def test_elementwise_and_linear_validators():
                                1) == h3.H3_ERR_ALIAS
     assert lib.h3_check_linear(x, 256, addr(7), 256, hh, 512, L, L, 512, 256, 3, None, 0, None,
                                1) == h3.H3_ERR_UNSUPPORTED
+
+
+def test_lora_consumer_validators():
+    """The LoRA consumer variants run the plain call's checks plus: the delta is
+    required, 16-byte aligned, and overlaps no output."""
+    lib = h3.LIB
+    L, H = 64, 256
+    x, hh, sh = addr(1), addr(2), addr(3)
+    sc, gate = sh + 4 * H, sh + 8 * H
+    br, d, x1 = addr(4), addr(5), addr(6)
+    ok = lib.h3_check_fused_modulate_norm_lora(x, H, br, H, d, H, sh, sc, gate, 6 * H, 1, x1, H, hh, H, L, L, H,
+                                               1e-6, 0, 0)
+    assert ok == h3.H3_OK
+    # residual only (no h, no shift/scale)
+    assert lib.h3_check_fused_modulate_norm_lora(x, H, br, H, d, H, None, None, gate, 6 * H, 1, x1, H, None, 0, L,
+                                                 L, H, 1e-6, 0, 1) == h3.H3_OK
+    # delta missing
+    assert lib.h3_check_fused_modulate_norm_lora(x, H, br, H, None, H, sh, sc, gate, 6 * H, 1, x1, H, hh, H, L, L,
+                                                 H, 1e-6, 0, 0) == h3.H3_ERR_NULL
+    # delta misaligned
+    assert lib.h3_check_fused_modulate_norm_lora(x, H, br, H, d + 2, H, sh, sc, gate, 6 * H, 1, x1, H, hh, H, L, L,
+                                                 H, 1e-6, 0, 0) == h3.H3_ERR_ALIGN
+    # delta overlapping x1
+    assert lib.h3_check_fused_modulate_norm_lora(x, H, br, H, x1, H, sh, sc, gate, 6 * H, 1, x1, H, hh, H, L, L, H,
+                                                 1e-6, 0, 0) == h3.H3_ERR_ALIAS
+    # qk-norm: q | k | v blocks of one packed buffer, deltas in another
+    q, dq = addr(7), addr(8)
+    g = addr(9)
+    assert lib.h3_check_qk_norm_rope_lora(q, q + 2 * H, q + 4 * H, 3 * H, dq, dq + 2 * H, dq + 4 * H, 3 * H, g,
+                                          g + 256, L, L, 2, 128, 64, 0, 1e4, 1e-6) == h3.H3_OK
+    # v without dv
+    assert lib.h3_check_qk_norm_rope_lora(q, q + 2 * H, q + 4 * H, 3 * H, dq, dq + 2 * H, None, 3 * H, g, g + 256,
+                                          L, L, 2, 128, 64, 0, 1e4, 1e-6) == h3.H3_ERR_NULL
+    # no v: fine
+    assert lib.h3_check_qk_norm_rope_lora(q, q + 2 * H, None, 3 * H, dq, dq + 2 * H, None, 3 * H, g, g + 256, L, L,
+                                          2, 128, 64, 0, 1e4, 1e-6) == h3.H3_OK
+    # a delta overlapping q
+    assert lib.h3_check_qk_norm_rope_lora(q, q + 2 * H, None, 3 * H, q, dq + 2 * H, None, 3 * H, g, g + 256, L, L,
+                                          2, 128, 64, 0, 1e4, 1e-6) == h3.H3_ERR_ALIAS
+    # swiglu
+    u, du, gg = addr(10), addr(11), addr(12)
+    assert lib.h3_check_swiglu_lora(u, 2048, du, 2048, gg, 1024, L, L, 1024) == h3.H3_OK
+    assert lib.h3_check_swiglu_lora(u, 2048, None, 2048, gg, 1024, L, L, 1024) == h3.H3_ERR_NULL
+    assert lib.h3_check_swiglu_lora(u, 2048, gg, 2048, gg, 1024, L, L, 1024) == h3.H3_ERR_ALIAS

@@ -481,3 +481,38 @@ def test_block_rows_grouped_equals_full_grouped_block():
     for name in ("h", "q", "k", "v", "o", "x1", "h2", "g", "y"):
         np.testing.assert_allclose(part[name], full[name][rows], rtol=1e-11, atol=1e-12)
     assert np.all(part["o"][2] == 0)
+
+
+def test_lora_input_rounding_points():
+    """bf16(base + delta) is one round-to-nearest-even of the exact sum: delta
+    = 0 returns the base bit for bit; exact half-ulp sums round to the even
+    neighbour; an update below half an ulp rounds back to the base (the effect
+    the pages measure on merged weights)."""
+    base = O.bf16_to_f64(I.normal_bf16("lora.base", (4096,)))
+    np.testing.assert_array_equal(O.lora_input(base, np.zeros_like(base)), base)
+    # ties: BF16 spacing at 1.0 is 2^-7, so 1 + 2^-8 is halfway between 1 and 1 + 2^-7
+    assert O.lora_input(1.0, 2.0 ** -8) == 1.0                           # to even (down)
+    assert O.lora_input(1.0 + 2.0 ** -7, 2.0 ** -8) == 1.0 + 2.0 ** -6   # to even (up)
+    assert O.lora_input(-1.0, -(2.0 ** -8)) == -1.0
+    assert O.lora_input(1.0, 2.0 ** -8 + 2.0 ** -20) == 1.0 + 2.0 ** -7  # just above the tie
+    # small updates round back to the base value
+    assert O.lora_input(1.0, 1e-3) == 1.0
+    assert O.lora_input(100.0, 0.2) == 100.0                             # spacing at 100 is 0.5
+    # the result is always on the BF16 grid and within half a spacing of the exact sum
+    d = O.bf16_to_f64(I.normal_bf16("lora.delta", (4096,), 0.01))
+    r = O.lora_input(base, d)
+    np.testing.assert_array_equal(O.round_to_bf16(r), r)
+    spacing = np.ldexp(1.0, np.frexp(np.abs(base + d))[1] - 8)
+    assert np.all(np.abs(r - (base + d)) <= spacing / 2)
+
+
+def test_lora_gate_product_kept_in_bf16():
+    """x + bf16(gate * branch): with gate 1 the product is the branch itself
+    (already BF16); with gate 1/3 the product is rounded before the add."""
+    br = O.bf16_to_f64(I.normal_bf16("lora.branch", (1024,)))
+    x = O.bf16_to_f64(I.normal_bf16("lora.x", (1024,)))
+    np.testing.assert_array_equal(O.gated_residual_bf16_product(x, 1.0, br), x + br)
+    third = np.float32(1.0 / 3.0).astype(np.float64)
+    got = O.gated_residual_bf16_product(x, third, br)
+    np.testing.assert_array_equal(got, x + O.round_to_bf16(third * br))
+    assert np.any(got != x + third * br)                                  # the rounding point is visible

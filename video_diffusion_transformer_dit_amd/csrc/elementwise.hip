@@ -26,17 +26,36 @@ namespace {
 struct ModnormArgs {
     const uint16_t *x;
     const uint16_t *branch;
+    const uint16_t *delta;  // LoRA delta of the branch (LORA kernels)
     const float *shift;
     const float *scale;
     const float *gate;
     const int32_t *mod_idx;
     uint16_t *x1;
     uint16_t *h;
-    int64_t ld_x, ld_b, ld_x1, ld_h, ld_mod;
+    int64_t ld_x, ld_b, ld_x1, ld_h, ld_mod, ld_d;
+    int32_t gate_bf16;      // LORA: round the gate product to BF16 before the residual add
     int64_t L_buf, valid;
     int32_t hidden, n_groups;
     float eps;
 };
+
+// LoRA consumer input: bf16(base + delta), round to nearest even. The FP32
+// sum of two BF16 values is exact or, when the exponents are far apart, within
+// an FP32 ulp of a value nowhere near a BF16 tie, so this is the correctly
+// rounded BF16 sum (Sol-H3 report, §3.5 "Precision-preserving LoRA fusion":
+// the consumer rounds base + delta to BF16 before using it).
+__device__ __forceinline__ uint4 lora_add8(const uint4 &base, const uint4 &delta) {
+    float fb[8], fd[8];
+    unpack8(base, fb);
+    unpack8(delta, fd);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) fb[e] += fd[e];
+    return pack8(fb);
+}
+
+// Round an FP32 value to BF16 (nearest even) and back.
+__device__ __forceinline__ float bf16_round(float v) { return (float)(__bf16)v; }
 
 __device__ __forceinline__ void load_f8(const float *p, float f[8]) {
     const float4 a = *reinterpret_cast<const float4 *>(p);
@@ -45,7 +64,7 @@ __device__ __forceinline__ void load_f8(const float *p, float f[8]) {
     f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
-template <int NCH, int ROWS, bool BRANCH, int NORM>
+template <int NCH, int ROWS, bool BRANCH, int NORM, bool LORA = false>
 __global__ __launch_bounds__(256) void modnorm_kernel(ModnormArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * ROWS;
@@ -86,12 +105,20 @@ __global__ __launch_bounds__(256) void modnorm_kernel(ModnormArgs a) {
                         load_f8(a.gate + (int64_t)grp[p] * a.ld_mod + 8 * c, gv);
                         gcur = grp[p];
                     }
-                    const uint4 bw = *reinterpret_cast<const uint4 *>(a.branch + r * a.ld_b + 8 * c);
+                    uint4 bw = *reinterpret_cast<const uint4 *>(a.branch + r * a.ld_b + 8 * c);
+                    if (LORA) bw = lora_add8(bw, *reinterpret_cast<const uint4 *>(a.delta + r * a.ld_d + 8 * c));
                     float xf[8], bf[8];
                     unpack8(xw, xf);
                     unpack8(bw, bf);
+                    if (LORA && a.gate_bf16) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) xf[e] = xf[e] + gv[e] * bf[e];
+                        for (int e = 0; e < 8; ++e) xf[e] = xf[e] + bf16_round(gv[e] * bf[e]);
+                    } else {
+                        // one explicit FMA, so every instance of this kernel
+                        // forms x1 identically (contraction is not left to the compiler)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) xf[e] = __builtin_fmaf(gv[e], bf[e], xf[e]);
+                    }
                     xw = pack8(xf);
                     *reinterpret_cast<uint4 *>(a.x1 + r * a.ld_x1 + 8 * c) = xw;
                 }
@@ -148,10 +175,11 @@ __global__ __launch_bounds__(256) void modnorm_kernel(ModnormArgs a) {
                 if (!inbuf[p]) continue;
                 if (!valid[p]) {
                     const uint4 z = make_uint4(0, 0, 0, 0);
-                    *reinterpret_cast<uint4 *>(a.h + r * a.ld_h + 8 * c) = z;
+                    if (!LORA || a.h) *reinterpret_cast<uint4 *>(a.h + r * a.ld_h + 8 * c) = z;
                     if (BRANCH) *reinterpret_cast<uint4 *>(a.x1 + r * a.ld_x1 + 8 * c) = z;
                     continue;
                 }
+                if (LORA && !a.h) continue;  // residual only
                 if (grp[p] != gcur) {
                     load_f8(a.shift + (int64_t)grp[p] * a.ld_mod + 8 * c, sh);
                     load_f8(a.scale + (int64_t)grp[p] * a.ld_mod + 8 * c, sc);
@@ -168,11 +196,14 @@ __global__ __launch_bounds__(256) void modnorm_kernel(ModnormArgs a) {
 }
 
 template <int NCH>
-void modnorm_dispatch_nch(const ModnormArgs &a, bool branch, int norm, hipStream_t s) {
+void modnorm_dispatch_nch(const ModnormArgs &a, bool branch, int norm, hipStream_t s, bool lora = false) {
     constexpr int ROWS = 2;
     const int64_t waves = (a.L_buf + ROWS - 1) / ROWS;
     const dim3 grid((unsigned)((waves + 3) / 4));
-    if (branch) {
+    if (lora) {
+        if (norm == 0) modnorm_kernel<NCH, ROWS, true, 0, true><<<grid, 256, 0, s>>>(a);
+        else modnorm_kernel<NCH, ROWS, true, 1, true><<<grid, 256, 0, s>>>(a);
+    } else if (branch) {
         if (norm == 0) modnorm_kernel<NCH, ROWS, true, 0><<<grid, 256, 0, s>>>(a);
         else modnorm_kernel<NCH, ROWS, true, 1><<<grid, 256, 0, s>>>(a);
     } else {
@@ -188,6 +219,9 @@ void modnorm_dispatch_nch(const ModnormArgs &a, bool branch, int norm, hipStream
 struct QkArgs {
     uint16_t *q;
     uint16_t *k;
+    uint16_t *v;                  // LORA: v column block, packed as bf16(v + dv) (may be null)
+    const uint16_t *dq, *dk, *dv; // LORA deltas
+    int64_t ld_d;
     const uint16_t *q_gain;
     const uint16_t *k_gain;
     const int32_t *pos;
@@ -196,6 +230,7 @@ struct QkArgs {
     float theta, eps;
 };
 
+template <bool LORA = false>
 __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkArgs a) {
     __shared__ float cs_cos[64];
     __shared__ float cs_sin[64];
@@ -210,8 +245,15 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkArgs a) {
             uint16_t *base = hv < a.heads ? a.q + (int64_t)hv * 128 : a.k + (int64_t)(hv - a.heads) * 128;
             *reinterpret_cast<uint4 *>(base + r * a.ld + 8 * c) = z;
         }
+        if (LORA && a.v)
+            for (int cc = t; cc < a.heads * 16; cc += 256) *reinterpret_cast<uint4 *>(a.v + r * a.ld + 8 * cc) = z;
         return;
     }
+    if (LORA && a.v)  // packing of v: bf16(v + dv)
+        for (int cc = t; cc < a.heads * 16; cc += 256) {
+            uint4 *pv = reinterpret_cast<uint4 *>(a.v + r * a.ld + 8 * cc);
+            *pv = lora_add8(*pv, *reinterpret_cast<const uint4 *>(a.dv + r * a.ld_d + 8 * cc));
+        }
     const int p = a.pos ? a.pos[r] : (int)r;
     const bool rot = p >= 0 && a.rot_dim > 0;
     const int half = a.rot_dim >> 1;
@@ -246,7 +288,13 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkArgs a) {
         float f[8];
         if (act) {
             ptr = (is_k ? a.k + (int64_t)(hv - a.heads) * 128 : a.q + (int64_t)hv * 128) + r * a.ld + 8 * c;
-            unpack8(*reinterpret_cast<const uint4 *>(ptr), f);
+            uint4 raw = *reinterpret_cast<const uint4 *>(ptr);
+            if (LORA) {
+                const uint16_t *dp =
+                    (is_k ? a.dk + (int64_t)(hv - a.heads) * 128 : a.dq + (int64_t)hv * 128) + r * a.ld_d + 8 * c;
+                raw = lora_add8(raw, *reinterpret_cast<const uint4 *>(dp));
+            }
+            unpack8(raw, f);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) f[e] = 0.f;
@@ -291,9 +339,11 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkArgs a) {
 // SwiGLU: one thread per 8 output columns; a workgroup covers 2048 columns of
 // one row.
 // ---------------------------------------------------------------------------
+template <bool LORA = false>
 __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t *u, int64_t ld_u, uint16_t *g,
                                                      int64_t ld_g, int64_t valid, int32_t ffn,
-                                                     uint32_t blocks_per_row) {
+                                                     uint32_t blocks_per_row, const uint16_t *du = nullptr,
+                                                     int64_t ld_du = 0) {
     const uint32_t row = blockIdx.x / blocks_per_row;
     const uint32_t cb = blockIdx.x - row * blocks_per_row;
     const int c = (int)(cb * 256 + threadIdx.x) * 8;
@@ -304,9 +354,15 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t *u, int64_t 
         return;
     }
     const uint16_t *src = u + (int64_t)row * ld_u + c;
+    uint4 ua = *reinterpret_cast<const uint4 *>(src), ub = *reinterpret_cast<const uint4 *>(src + ffn);
+    if (LORA) {
+        const uint16_t *dsrc = du + (int64_t)row * ld_du + c;
+        ua = lora_add8(ua, *reinterpret_cast<const uint4 *>(dsrc));
+        ub = lora_add8(ub, *reinterpret_cast<const uint4 *>(dsrc + ffn));
+    }
     float a[8], b[8];
-    unpack8(*reinterpret_cast<const uint4 *>(src), a);
-    unpack8(*reinterpret_cast<const uint4 *>(src + ffn), b);
+    unpack8(ua, a);
+    unpack8(ub, b);
 #pragma unroll
     for (int e = 0; e < 8; ++e) a[e] = a[e] / (1.0f + __expf(-a[e])) * b[e];
     *reinterpret_cast<uint4 *>(dst) = pack8(a);
@@ -343,6 +399,7 @@ void launch_modnorm(const uint16_t *x, int64_t ld_x, const uint16_t *branch, int
     ModnormArgs a;
     a.x = x; a.branch = branch; a.shift = shift; a.scale = scale; a.gate = gate; a.mod_idx = mod_idx;
     a.x1 = x1_out; a.h = h_out;
+    a.delta = nullptr; a.ld_d = 0; a.gate_bf16 = 0;
     a.ld_x = ld_x; a.ld_b = ld_b; a.ld_x1 = ld_x1; a.ld_h = ld_h;
     a.ld_mod = n_mod_groups > 1 ? ld_mod_group : 0;
     a.L_buf = L_buf; a.valid = valid_len; a.hidden = hidden; a.n_groups = n_mod_groups; a.eps = eps;
@@ -365,13 +422,59 @@ void launch_qk_norm_rope(uint16_t *q, uint16_t *k, int64_t ld, const uint16_t *q
     a.q = q; a.k = k; a.q_gain = q_gain; a.k_gain = k_gain; a.pos = pos;
     a.ld = ld; a.L_buf = L_buf; a.valid = valid_len;
     a.heads = heads; a.rot_dim = rot_dim; a.pairing = pairing; a.theta = theta; a.eps = eps;
-    qk_norm_rope_kernel<<<dim3((unsigned)L_buf), 256, 0, stream>>>(a);
+    a.v = nullptr; a.dq = a.dk = a.dv = nullptr; a.ld_d = 0;
+    qk_norm_rope_kernel<false><<<dim3((unsigned)L_buf), 256, 0, stream>>>(a);
 }
 
 void launch_swiglu(const uint16_t *u, int64_t ld_u, uint16_t *g, int64_t ld_g, int64_t L_buf, int64_t valid_len,
                    int32_t ffn, hipStream_t stream) {
     const uint32_t bpr = (uint32_t)((ffn / 8 + 255) / 256);
-    swiglu_kernel<<<dim3((unsigned)(L_buf * bpr)), 256, 0, stream>>>(u, ld_u, g, ld_g, valid_len, ffn, bpr);
+    swiglu_kernel<false><<<dim3((unsigned)(L_buf * bpr)), 256, 0, stream>>>(u, ld_u, g, ld_g, valid_len, ffn, bpr);
+}
+
+// LoRA consumer variants: the consumer rounds base + delta to BF16 first.
+void launch_modnorm_lora(const uint16_t *x, int64_t ld_x, const uint16_t *branch, int64_t ld_b,
+                         const uint16_t *delta, int64_t ld_d, const float *shift, const float *scale,
+                         const float *gate, int64_t ld_mod_group, int32_t n_mod_groups, const int32_t *mod_idx,
+                         uint16_t *x1_out, int64_t ld_x1, uint16_t *h_out, int64_t ld_h, int64_t L_buf,
+                         int64_t valid_len, int32_t hidden, float eps, int32_t norm_type, int32_t gate_bf16,
+                         hipStream_t stream) {
+    ModnormArgs a;
+    a.x = x; a.branch = branch; a.shift = shift; a.scale = scale; a.gate = gate; a.mod_idx = mod_idx;
+    a.x1 = x1_out; a.h = h_out;
+    a.delta = delta; a.ld_d = ld_d; a.gate_bf16 = gate_bf16 ? 1 : 0;
+    a.ld_x = ld_x; a.ld_b = ld_b; a.ld_x1 = ld_x1; a.ld_h = ld_h;
+    a.ld_mod = n_mod_groups > 1 ? ld_mod_group : 0;
+    a.L_buf = L_buf; a.valid = valid_len; a.hidden = hidden; a.n_groups = n_mod_groups; a.eps = eps;
+    const int need = (hidden / 8 + 63) / 64;
+    if (need <= 1) modnorm_dispatch_nch<1>(a, true, norm_type, stream, true);
+    else if (need <= 2) modnorm_dispatch_nch<2>(a, true, norm_type, stream, true);
+    else if (need <= 4) modnorm_dispatch_nch<4>(a, true, norm_type, stream, true);
+    else if (need <= 8) modnorm_dispatch_nch<8>(a, true, norm_type, stream, true);
+    else if (need <= 11) modnorm_dispatch_nch<11>(a, true, norm_type, stream, true);
+    else if (need <= 16) modnorm_dispatch_nch<16>(a, true, norm_type, stream, true);
+    else if (need <= 24) modnorm_dispatch_nch<24>(a, true, norm_type, stream, true);
+    else modnorm_dispatch_nch<32>(a, true, norm_type, stream, true);
+}
+
+void launch_qk_norm_rope_lora(uint16_t *q, uint16_t *k, uint16_t *v, int64_t ld, const uint16_t *dq,
+                              const uint16_t *dk, const uint16_t *dv, int64_t ld_d, const uint16_t *q_gain,
+                              const uint16_t *k_gain, const int32_t *pos, int64_t L_buf, int64_t valid_len,
+                              int32_t heads, int32_t rot_dim, int32_t pairing, float theta, float eps,
+                              hipStream_t stream) {
+    QkArgs a;
+    a.q = q; a.k = k; a.q_gain = q_gain; a.k_gain = k_gain; a.pos = pos;
+    a.v = v; a.dq = dq; a.dk = dk; a.dv = dv; a.ld_d = ld_d;
+    a.ld = ld; a.L_buf = L_buf; a.valid = valid_len;
+    a.heads = heads; a.rot_dim = rot_dim; a.pairing = pairing; a.theta = theta; a.eps = eps;
+    qk_norm_rope_kernel<true><<<dim3((unsigned)L_buf), 256, 0, stream>>>(a);
+}
+
+void launch_swiglu_lora(const uint16_t *u, int64_t ld_u, const uint16_t *du, int64_t ld_du, uint16_t *g,
+                        int64_t ld_g, int64_t L_buf, int64_t valid_len, int32_t ffn, hipStream_t stream) {
+    const uint32_t bpr = (uint32_t)((ffn / 8 + 255) / 256);
+    swiglu_kernel<true><<<dim3((unsigned)(L_buf * bpr)), 256, 0, stream>>>(u, ld_u, g, ld_g, valid_len, ffn, bpr,
+                                                                           du, ld_du);
 }
 
 void launch_zero_rows(uint16_t *p, int64_t ld, int64_t cols, int64_t r0, int64_t r1, hipStream_t stream) {
@@ -428,6 +531,47 @@ int h3_swiglu(const uint16_t *u, int64_t ld_u, uint16_t *g, int64_t ld_g, int64_
     if (s != H3_OK || L_buf == 0) return s;
     if ((s = device_check()) != H3_OK) return s;
     launch_swiglu(u, ld_u, g, ld_g, L_buf, valid_len, ffn, (hipStream_t)stream);
+    return launch_status();
+}
+
+
+int h3_fused_modulate_norm_lora(const uint16_t *x, int64_t ld_x, const uint16_t *branch, int64_t ld_b,
+                                const uint16_t *delta, int64_t ld_d, const float *shift, const float *scale,
+                                const float *gate, int64_t ld_mod_group, int32_t n_mod_groups,
+                                const int32_t *mod_idx, uint16_t *x1_out, int64_t ld_x1, uint16_t *h_out,
+                                int64_t ld_h, int64_t L_buf, int64_t valid_len, int32_t hidden, float eps,
+                                int32_t norm_type, int32_t gate_bf16, void *stream) {
+    int s = h3_check_fused_modulate_norm_lora(x, ld_x, branch, ld_b, delta, ld_d, shift, scale, gate, ld_mod_group,
+                                              n_mod_groups, x1_out, ld_x1, h_out, ld_h, L_buf, valid_len, hidden,
+                                              eps, norm_type, gate_bf16);
+    if (s != H3_OK || L_buf == 0) return s;
+    if ((s = device_check()) != H3_OK) return s;
+    launch_modnorm_lora(x, ld_x, branch, ld_b, delta, ld_d, shift, scale, gate, ld_mod_group, n_mod_groups, mod_idx,
+                        x1_out, ld_x1, h_out, ld_h, L_buf, valid_len, hidden, eps, norm_type, gate_bf16,
+                        (hipStream_t)stream);
+    return launch_status();
+}
+
+int h3_qk_norm_rope_lora(uint16_t *q, uint16_t *k, uint16_t *v, int64_t ld, const uint16_t *dq,
+                         const uint16_t *dk, const uint16_t *dv, int64_t ld_d, const uint16_t *q_gain,
+                         const uint16_t *k_gain, const int32_t *pos, int64_t L_buf, int64_t valid_len,
+                         int32_t heads, int32_t head_dim, int32_t rot_dim, int32_t pairing, float theta, float eps,
+                         void *stream) {
+    int s = h3_check_qk_norm_rope_lora(q, k, v, ld, dq, dk, dv, ld_d, q_gain, k_gain, L_buf, valid_len, heads,
+                                       head_dim, rot_dim, pairing, theta, eps);
+    if (s != H3_OK || L_buf == 0) return s;
+    if ((s = device_check()) != H3_OK) return s;
+    launch_qk_norm_rope_lora(q, k, v, ld, dq, dk, dv, ld_d, q_gain, k_gain, pos, L_buf, valid_len, heads, rot_dim,
+                             pairing, theta, eps, (hipStream_t)stream);
+    return launch_status();
+}
+
+int h3_swiglu_lora(const uint16_t *u, int64_t ld_u, const uint16_t *du, int64_t ld_du, uint16_t *g,
+                   int64_t ld_g, int64_t L_buf, int64_t valid_len, int32_t ffn, void *stream) {
+    int s = h3_check_swiglu_lora(u, ld_u, du, ld_du, g, ld_g, L_buf, valid_len, ffn);
+    if (s != H3_OK || L_buf == 0) return s;
+    if ((s = device_check()) != H3_OK) return s;
+    launch_swiglu_lora(u, ld_u, du, ld_du, g, ld_g, L_buf, valid_len, ffn, (hipStream_t)stream);
     return launch_status();
 }
 

@@ -269,6 +269,84 @@ int h3_check_swiglu(const uint16_t *u, int64_t ld_u, const uint16_t *g, int64_t 
     return H3_OK;
 }
 
+int h3_check_qk_norm_rope_lora(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t ld,
+                               const uint16_t *dq, const uint16_t *dk, const uint16_t *dv, int64_t ld_d,
+                               const uint16_t *q_gain, const uint16_t *k_gain, int64_t L_buf, int64_t valid_len,
+                               int32_t heads, int32_t head_dim, int32_t rot_dim, int32_t pairing, float theta,
+                               float eps) {
+    H3_TRY(h3_check_qk_norm_rope(q, k, ld, q_gain, k_gain, L_buf, valid_len, heads, head_dim, rot_dim, pairing,
+                                 theta, eps));
+    if (L_buf == 0) return H3_OK;
+    if (!dq || !dk || (v && !dv)) return H3_ERR_NULL;
+    const int64_t H = (int64_t)heads * head_dim;
+    H3_TRY(check_bf16_mat(dq, ld_d, H));
+    H3_TRY(check_bf16_mat(dk, ld_d, H));
+    const Mat mq = mat(q, L_buf, H, ld), mk = mat(k, L_buf, H, ld), mv = mat(v, v ? L_buf : 0, H, ld);
+    if (v) {
+        H3_TRY(check_bf16_mat(v, ld, H));
+        H3_TRY(check_bf16_mat(dv, ld_d, H));
+        if (overlap(mv, mq) || overlap(mv, mk)) return H3_ERR_ALIAS;
+        const Mat gq = mat(q_gain, 1, head_dim, head_dim), gk = mat(k_gain, 1, head_dim, head_dim);
+        if (overlap(mv, gq) || overlap(mv, gk)) return H3_ERR_ALIAS;
+    }
+    const Mat mdq = mat(dq, L_buf, H, ld_d), mdk = mat(dk, L_buf, H, ld_d), mdv = mat(dv, v ? L_buf : 0, H, ld_d);
+    for (const Mat *out : {&mq, &mk, &mv})
+        for (const Mat *d : {&mdq, &mdk, &mdv})
+            if (overlap(*out, *d)) return H3_ERR_ALIAS;
+    return H3_OK;
+}
+
+int h3_check_fused_modulate_norm_lora(const uint16_t *x, int64_t ld_x, const uint16_t *branch, int64_t ld_b,
+                                      const uint16_t *delta, int64_t ld_d, const float *shift, const float *scale,
+                                      const float *gate, int64_t ld_mod_group, int32_t n_mod_groups,
+                                      const uint16_t *x1_out, int64_t ld_x1, const uint16_t *h_out, int64_t ld_h,
+                                      int64_t L_buf, int64_t valid_len, int32_t hidden, float eps,
+                                      int32_t norm_type, int32_t gate_bf16) {
+    (void)gate_bf16;
+    H3_TRY(check_rows(L_buf, valid_len));
+    if (L_buf > 0 && (!branch || !delta || !gate || !x1_out)) return H3_ERR_NULL;
+    if (h_out) {
+        H3_TRY(h3_check_fused_modulate_norm(x, ld_x, branch, ld_b, shift, scale, gate, ld_mod_group, n_mod_groups,
+                                            x1_out, ld_x1, h_out, ld_h, L_buf, valid_len, hidden, eps, norm_type));
+    } else {
+        // residual only: the plain checks with the h output and the norm table
+        // left out
+        if (hidden <= 0) return H3_ERR_SHAPE;
+        if (hidden > kMaxHidden) return H3_ERR_UNSUPPORTED;
+        if (hidden % 8 != 0) return H3_ERR_ALIGN;
+        if (norm_type != 0 && norm_type != 1) return H3_ERR_UNSUPPORTED;
+        if (L_buf == 0) return H3_OK;
+        if (!x) return H3_ERR_NULL;
+        if (n_mod_groups < 1) return H3_ERR_SHAPE;
+        if (ld_mod_group < hidden && n_mod_groups > 1) return H3_ERR_SHAPE;
+        if (ld_mod_group % 4 != 0 || !aligned16(gate)) return H3_ERR_ALIGN;
+        H3_TRY(check_bf16_mat(x, ld_x, hidden));
+        H3_TRY(check_bf16_mat(branch, ld_b, hidden));
+        H3_TRY(check_bf16_mat(x1_out, ld_x1, hidden));
+        const Mat mx = mat(x, L_buf, hidden, ld_x), mb = mat(branch, L_buf, hidden, ld_b);
+        const Mat m1 = mat(x1_out, L_buf, hidden, ld_x1);
+        const Mat mg = mat(gate, n_mod_groups, hidden, std::max<int64_t>(ld_mod_group, hidden), 4);
+        if (!same(m1, mx) && overlap(m1, mx)) return H3_ERR_ALIAS;
+        if (overlap(m1, mb) || overlap(m1, mg)) return H3_ERR_ALIAS;
+    }
+    if (L_buf == 0) return H3_OK;
+    H3_TRY(check_bf16_mat(delta, ld_d, hidden));
+    const Mat md = mat(delta, L_buf, hidden, ld_d);
+    if (overlap(mat(x1_out, L_buf, hidden, ld_x1), md)) return H3_ERR_ALIAS;
+    if (h_out && overlap(mat(h_out, L_buf, hidden, ld_h), md)) return H3_ERR_ALIAS;
+    return H3_OK;
+}
+
+int h3_check_swiglu_lora(const uint16_t *u, int64_t ld_u, const uint16_t *du, int64_t ld_du, const uint16_t *g,
+                         int64_t ld_g, int64_t L_buf, int64_t valid_len, int32_t ffn) {
+    H3_TRY(h3_check_swiglu(u, ld_u, g, ld_g, L_buf, valid_len, ffn));
+    if (L_buf == 0) return H3_OK;
+    if (!du) return H3_ERR_NULL;
+    H3_TRY(check_bf16_mat(du, ld_du, 2 * (int64_t)ffn));
+    if (overlap(mat(du, L_buf, 2 * (int64_t)ffn, ld_du), mat(g, L_buf, ffn, ld_g))) return H3_ERR_ALIAS;
+    return H3_OK;
+}
+
 int h3_check_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ldw, const uint16_t *c,
                     int64_t ldc, int64_t M_buf, int64_t M_valid, int64_t N, int64_t K, int32_t epilogue,
                     const uint16_t *resid, int64_t ld_r, const float *gate, int32_t n_mod_groups) {

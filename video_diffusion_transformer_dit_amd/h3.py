@@ -83,6 +83,14 @@ def _load():
         "h3_check_qk_norm_rope": [P, P, I64, P, P, I64, I64, I32, I32, I32, I32, F32, F32],
         "h3_swiglu": [P, I64, P, I64, I64, I64, I32, P],
         "h3_check_swiglu": [P, I64, P, I64, I64, I64, I32],
+        "h3_qk_norm_rope_lora": [P, P, P, I64, P, P, P, I64, P, P, P, I64, I64, I32, I32, I32, I32, F32, F32, P],
+        "h3_check_qk_norm_rope_lora": [P, P, P, I64, P, P, P, I64, P, P, I64, I64, I32, I32, I32, I32, F32, F32],
+        "h3_fused_modulate_norm_lora": [P, I64, P, I64, P, I64, P, P, P, I64, I32, P, P, I64, P, I64, I64, I64, I32,
+                                        F32, I32, I32, P],
+        "h3_check_fused_modulate_norm_lora": [P, I64, P, I64, P, I64, P, P, P, I64, I32, P, I64, P, I64, I64, I64,
+                                              I32, F32, I32, I32],
+        "h3_swiglu_lora": [P, I64, P, I64, P, I64, I64, I64, I32, P],
+        "h3_check_swiglu_lora": [P, I64, P, I64, P, I64, I64, I64, I32],
         "h3_linear": [P, I64, P, I64, P, P, I64, I64, I64, I64, I64, I32, P, I64, P, I64, I32, P, P],
         "h3_check_linear": [P, I64, P, I64, P, I64, I64, I64, I64, I64, I32, P, I64, P, I32],
         "h3_block_workspace_bytes": [C.POINTER(Dims), I64, C.POINTER(QGroup), I32],
@@ -105,7 +113,9 @@ LIB = _load()
 EXPORTS = ["h3_block_forward", "h3_attention", "h3_fused_modulate_norm", "h3_qk_norm_rope", "h3_swiglu",
            "h3_linear", "h3_attention_workspace_bytes", "h3_block_workspace_bytes", "h3_block_workspace_layout", "h3_status_string",
            "h3_abi_version", "h3_check_block_forward", "h3_check_attention", "h3_check_fused_modulate_norm",
-           "h3_check_qk_norm_rope", "h3_check_swiglu", "h3_check_linear"]
+           "h3_check_qk_norm_rope", "h3_check_swiglu", "h3_check_linear", "h3_qk_norm_rope_lora",
+           "h3_fused_modulate_norm_lora", "h3_swiglu_lora", "h3_check_qk_norm_rope_lora",
+           "h3_check_fused_modulate_norm_lora", "h3_check_swiglu_lora"]
 
 
 def status_string(s: int) -> str:
@@ -232,6 +242,32 @@ def qk_norm_rope(q, k, q_gain, k_gain, valid_len, heads, rot_dim=64, pairing=0, 
 def swiglu(u, g, valid_len, ffn, stream=None):
     s = LIB.h3_swiglu(_ptr(u), u.stride(0), _ptr(g), g.stride(0), u.shape[0], valid_len, ffn, _stream(stream))
     _ok(s, "h3_swiglu")
+
+
+def qk_norm_rope_lora(q, k, dq, dk, q_gain, k_gain, valid_len, heads, v=None, dv=None, rot_dim=64, pairing=0,
+                      theta=10000.0, eps=1e-6, pos=None, stream=None):
+    s = LIB.h3_qk_norm_rope_lora(_ptr(q), _ptr(k), _ptr(v), q.stride(0), _ptr(dq), _ptr(dk), _ptr(dv), dq.stride(0),
+                                 _ptr(q_gain), _ptr(k_gain), _ptr(pos), q.shape[0], valid_len, heads, 128, rot_dim,
+                                 pairing, theta, eps, _stream(stream))
+    _ok(s, "h3_qk_norm_rope_lora")
+
+
+def fused_modulate_norm_lora(x, branch, delta, gate, x1_out, valid_len, shift=None, scale=None, h_out=None,
+                             eps=1e-6, norm_type=0, gate_bf16=False, ld_mod_group=0, n_mod_groups=1, mod_idx=None,
+                             stream=None):
+    hidden = x.shape[1]
+    s = LIB.h3_fused_modulate_norm_lora(_ptr(x), x.stride(0), _ptr(branch), branch.stride(0), _ptr(delta),
+                                        delta.stride(0), _ptr(shift), _ptr(scale), _ptr(gate), ld_mod_group,
+                                        n_mod_groups, _ptr(mod_idx), _ptr(x1_out), x1_out.stride(0), _ptr(h_out),
+                                        _ld(h_out), x.shape[0], valid_len, hidden, eps, norm_type,
+                                        1 if gate_bf16 else 0, _stream(stream))
+    _ok(s, "h3_fused_modulate_norm_lora")
+
+
+def swiglu_lora(u, du, g, valid_len, ffn, stream=None):
+    s = LIB.h3_swiglu_lora(_ptr(u), u.stride(0), _ptr(du), du.stride(0), _ptr(g), g.stride(0), u.shape[0],
+                           valid_len, ffn, _stream(stream))
+    _ok(s, "h3_swiglu_lora")
 
 
 def linear(a, w, c, M_valid, epilogue=H3_EPI_STORE, bias=None, resid=None, gate=None, ld_gate_group=0,
