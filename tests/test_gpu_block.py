@@ -249,3 +249,52 @@ def test_block_streaming_full_width_sampled_rows():
     qkv = b.inter(h3.H3_WS_QKV)
     np.testing.assert_array_equal(bits(ek), bits(qkv[cond + audio:, s.hidden:2 * s.hidden]))
     np.testing.assert_array_equal(bits(ev), bits(qkv[cond + audio:, 2 * s.hidden:]))
+
+
+def _ref_cache_case(hidden, heads, ffn, n_text, n_ref, n_gen, tag):
+    """A full step over [text | reference | generation] rows exporting the
+    reference rows' K/V, then the cached step over [text | generation] rows at
+    their original positions, attending over [cached reference K/V ; own rows]."""
+    L = n_text + n_ref + n_gen
+    full_s = I.streaming_shape(hidden=hidden, heads=heads, ffn=ffn, cond=n_text, audio=n_ref, video=n_gen)
+    b_full = Block(full_s, tag=tag)
+    xb = I.activations(full_s, tag=f"{tag}.x")
+    ek, ev = poison((n_ref, hidden)), poison((n_ref, hidden))
+    y_full = b_full.run(xb, kv_export=(ek, ev, n_text, n_ref))
+    keep = np.r_[0:n_text, n_text + n_ref:L]
+    Lc = len(keep)
+    cur_s = I.streaming_shape(hidden=hidden, heads=heads, ffn=ffn, cond=n_text, audio=0, video=n_gen)
+    b_cur = Block(cur_s, tag=tag)                        # same weights (same tag), Lc rows
+    y_cur = b_cur.run(xb[keep], groups=[(0, Lc, [(ek, ev, 0, n_ref), ("self", 0, Lc)])],
+                      pos=dev_i32(keep.astype(np.int32)))
+    return b_full, b_cur, xb, keep, y_full, y_cur
+
+
+def test_block_reference_kv_cache_small():
+    """Reference K/V caching at reduced width: the cached step matches the
+    oracle's full step on every non-reference row (the two are equal in exact
+    arithmetic), and the GPU's own full step."""
+    print("block reference kv cache small", flush=True)
+    b_full, b_cur, xb, keep, y_full, y_cur = _ref_cache_case(256, 2, 1024, 32, 96, 216, "rkv0")
+    ref = b_full.oracle(xb)
+    L = b_full.s.L_buf
+    _check_all(b_full, ref, y_full, L)
+    assert_parity(f64(y_cur), ref["y"][keep], "cached y")
+    o_cur = f64(b_cur.inter(h3.H3_WS_O))
+    assert_parity(o_cur, ref["o"][keep], "cached o")
+    assert_parity(f64(y_cur), f64(y_full)[keep], "cached vs full step y")
+
+
+@pytest.mark.timeout(900)
+def test_block_reference_kv_cache_full_width_sampled_rows():
+    """Reference K/V caching at full width ([text 128 | reference 2,048 |
+    generation 3,072]): the cached step's sampled rows against the oracle's
+    full step at the same original rows, for every intermediate."""
+    print("block reference kv cache full width", flush=True)
+    b_full, b_cur, xb, keep, y_full, y_cur = _ref_cache_case(5376, 42, 21504, 128, 2048, 3072, "rkv1")
+    sel = np.unique(np.concatenate([I.rng_for("rows_rkv").choice(len(keep), size=30, replace=False),
+                                    [0, 127, 128, len(keep) - 1]]))
+    s = b_full.s
+    ref = O.block_forward_rows(O.bf16_to_f64(xb), b_full.wo, b_full.mod.astype(np.float64), keep[sel],
+                               heads=s.heads, head_dim=128, ffn=s.ffn, valid_len=s.valid_len, rot_dim=s.rot_dim)
+    _check_rows(b_cur, y_cur, ref, sel, "cached")

@@ -516,3 +516,25 @@ def test_lora_gate_product_kept_in_bf16():
     got = O.gated_residual_bf16_product(x, third, br)
     np.testing.assert_array_equal(got, x + O.round_to_bf16(third * br))
     assert np.any(got != x + third * br)                                  # the rounding point is visible
+
+
+def test_reference_kv_cache_step_equals_full_step():
+    """Reference K/V caching (Sol-H3 report, §4 "Reference KV caching
+    mechanism"): once the reference rows' K/V are cached from a full step, a
+    step over the other rows only, attending over [cached reference K/V ;
+    current rows] at their original positions, gives exactly the full step's
+    outputs on those rows (same inputs, so the cache is exact here; attention
+    does not depend on the key order)."""
+    s, w, x, mod, kw = _tiny_inputs()
+    L = 320
+    n_text, n_ref = 32, 96
+    xs = x[:L]
+    full = O.block_forward(xs, w, mod, valid_len=L, **kw)
+    keep = np.r_[0:n_text, n_text + n_ref:L]
+    ref_k, ref_v = full["k"][n_text:n_text + n_ref], full["v"][n_text:n_text + n_ref]
+    pos = keep.astype(np.int32)
+    Lc = len(keep)
+    groups = [(0, Lc, [(ref_k, ref_v), ("self", 0, Lc)])]
+    cached = O.block_forward(xs[keep], w, mod, valid_len=Lc, groups=groups, pos=pos, **kw)
+    for name in ("q", "k", "v", "o", "x1", "g", "y"):
+        np.testing.assert_allclose(cached[name], full[name][keep], rtol=1e-10, atol=1e-11)
