@@ -173,6 +173,35 @@ def lora_consumers(torch, h3, dev, gen, L, V, H, heads, F, iters):
     return res
 
 
+def reference_kv_cache(torch, h3, dev, dims, weights, mod, gen, L, V, H, n_ref=14344):
+    """Reference K/V caching at the benchmarked sequence plus one image's
+    reference tokens (14,344): the first denoising step runs the full sequence
+    [text 512 | reference | audio and video] and exports the reference rows'
+    K/V; later steps run only the generation rows at their original positions
+    and attend over [cached reference K/V ; own rows]."""
+    n_text = 512
+    Lf, Vf = L + n_ref, V + n_ref
+    xf = torch.randn((Lf, H), generator=gen, device=dev).to(torch.bfloat16)
+    yf = torch.empty_like(xf)
+    ek = torch.empty((n_ref, H), dtype=torch.bfloat16, device=dev)
+    ev = torch.empty_like(ek)
+    exp = (ek, ev, n_text, n_ref)
+    wsf = torch.empty(h3.workspace_bytes(dims, Lf), dtype=torch.uint8, device=dev)
+    full_ms = time_calls(torch, lambda: h3.block_forward(dims, weights, xf, yf, mod, 1, Vf, wsf, kv_export=exp), 2, 1)
+    del wsf
+    keep = torch.cat([torch.arange(0, n_text), torch.arange(n_text + n_ref, Lf)]).to(dev)
+    xc = xf[keep].contiguous()
+    yc = torch.empty_like(xc)
+    pos = keep.to(torch.int32)
+    groups = [(0, V, [(ek, ev, 0, n_ref), ("self", 0, V)])]
+    wsc = torch.empty(h3.workspace_bytes(dims, L, groups), dtype=torch.uint8, device=dev)
+    cached_ms = time_calls(torch, lambda: h3.block_forward(dims, weights, xc, yc, mod, 1, V, wsc, groups=groups,
+                                                           pos=pos), 2, 1)
+    del wsc, xf, yf, xc, yc
+    return {"reference_tokens": n_ref, "generation_tokens": V, "full_step_ms": round(full_ms, 3),
+            "cached_step_ms": round(cached_ms, 3), "speedup": round(full_ms / cached_ms, 3)}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -314,6 +343,7 @@ def main(argv=None) -> int:
     }
     if not a.no_next:
         out["next"] = {"lora_consumer_fusion": lora_consumers(torch, h3, dev, gen, L, V, H, heads, F, kit)}
+        out["next"]["reference_kv_cache"] = reference_kv_cache(torch, h3, dev, dims, weights, mod, gen, L, V, H)
     if a.calibration_copy:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)   # 1 GiB
         dst = torch.empty_like(src)
