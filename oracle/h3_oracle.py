@@ -24,6 +24,9 @@ Sources (cited by page title and section):
     so the head width is 128.
   - §3.4 "Safety rails": sequence packing [text | conditioning video | audio |
     target video].
+  - §3.4 "Sparse Attention": Sol-Attn block selection by the threshold
+    mu + tau * sigma per query block; prefix queries dense; prefix keys always
+    attended.
 * [vLLM-Omni H3] "MiniMax H3 on vLLM-Omni: integrating FastVideo FastH3" (blog).
   - §3.1: 58,758 valid tokens in a 58,816-token aligned buffer; the attention
     backend receives the valid length and drops the structural padding suffix.
@@ -283,6 +286,94 @@ def attention_grouped(q, groups, heads: int, head_dim: int, n_rows: int, scale=N
         kk = np.concatenate([np.asarray(s[0], dtype=F64) for s in segs], axis=0)
         vv = np.concatenate([np.asarray(s[1], dtype=F64) for s in segs], axis=0)
         out[qb:qe] = attention(q[qb:qe], kk, vv, heads, head_dim, scale)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Sol-Attn block-sparse attention (Sol-H3 §3.4 "Sparse Attention").
+#
+# The sequence is [prefix | target video]; prefix = rows [0, prefix_len).
+# Prefix queries attend densely over every valid key. Target queries are cut
+# into query blocks of q_block rows counted from prefix_len, target keys into
+# KV blocks of k_block rows counted from prefix_len (the last block of each may
+# be short). For a query block, every target KV block gets a block-level score;
+# the block is selected when its score exceeds mu + tau * sigma, mu and sigma
+# being the mean and standard deviation of that query block's scores over all
+# target KV blocks. The query block's rows attend exactly over the prefix keys
+# (always-attended sinks) plus the keys of its selected blocks.
+#
+# Readings (the pages leave these open):
+#   S1 block-level score = (mean of the block's q rows) . (mean of the KV
+#      block's k rows) * scale, per head, before any softmax; q and k are the
+#      attention inputs (after Q/K RMSNorm and RoPE).
+#   S2 sigma is the population standard deviation (divide by the number of
+#      target KV blocks); "exceed" is strict.
+#   S3 block sizes: 256 query rows and 64 keys.
+#   S4 the selection is an integer decision taken in FP32 (the kernel's
+#      precision): pooled means, scores, mu, sigma and the threshold are FP32.
+# ----------------------------------------------------------------------------
+SPARSE_Q_BLOCK = 256
+SPARSE_K_BLOCK = 64
+
+
+def _blocks(n: int, size: int):
+    return [(b, min(b + size, n)) for b in range(0, n, size)]
+
+
+def sparse_block_scores(q, k, valid_len: int, prefix_len: int, heads: int, head_dim: int,
+                        q_block: int = SPARSE_Q_BLOCK, k_block: int = SPARSE_K_BLOCK, scale=None):
+    """Block-level attention scores of the target rows (reading S1), in FP32:
+    returns [heads, n_qblocks, n_kblocks]."""
+    f32 = np.float32
+    if scale is None or scale == 0:
+        scale = 1.0 / np.sqrt(head_dim)
+    P, V = int(prefix_len), int(valid_len)
+    qb, kb = _blocks(V - P, q_block), _blocks(V - P, k_block)
+    out = np.empty((heads, len(qb), len(kb)), dtype=f32)
+    for h in range(heads):
+        sl = slice(h * head_dim, (h + 1) * head_dim)
+        qt = np.asarray(q[P:V, sl], dtype=f32)
+        kt = np.asarray(k[P:V, sl], dtype=f32)
+        qbar = np.stack([qt[a:b].mean(axis=0, dtype=f32) for a, b in qb]) if qb else np.zeros((0, head_dim), f32)
+        kbar = np.stack([kt[a:b].mean(axis=0, dtype=f32) for a, b in kb]) if kb else np.zeros((0, head_dim), f32)
+        out[h] = (qbar @ kbar.T) * f32(scale)
+    return out
+
+
+def sparse_select(scores, tau: float):
+    """Selection by the per-query-block threshold mu + tau * sigma (reading S2),
+    in FP32. scores [..., n_kblocks]. Returns (selected bool mask, threshold)."""
+    f32 = np.float32
+    s = np.asarray(scores, dtype=f32)
+    mu = s.mean(axis=-1, keepdims=True, dtype=f32)
+    sigma = np.sqrt(np.square(s - mu).mean(axis=-1, keepdims=True, dtype=f32))
+    thr = mu + f32(tau) * sigma
+    return s > thr, thr[..., 0]
+
+
+def sparse_attention(q, k, v, valid_len: int, prefix_len: int, heads: int, head_dim: int, selected,
+                     q_block: int = SPARSE_Q_BLOCK, k_block: int = SPARSE_K_BLOCK, scale=None, n_rows=None):
+    """Dense attention masked to the selected blocks (FP64). `selected`
+    [heads, n_qblocks, n_kblocks] bool. Prefix rows attend over every valid
+    key; a target query block over the prefix keys and its selected blocks.
+    Rows past valid_len give 0."""
+    P, V = int(prefix_len), int(valid_len)
+    n_rows = V if n_rows is None else int(n_rows)
+    if scale is None or scale == 0:
+        scale = 1.0 / np.sqrt(head_dim)
+    q = np.asarray(q, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    v = np.asarray(v, dtype=F64)
+    out = np.zeros((n_rows, heads * head_dim), dtype=F64)
+    kb = _blocks(V - P, k_block)
+    for h in range(heads):
+        sl = slice(h * head_dim, (h + 1) * head_dim)
+        if P > 0:
+            out[:P, sl] = attention_head(q[:P, sl], k[:V, sl], v[:V, sl], scale)
+        for bi, (a, b) in enumerate(_blocks(V - P, q_block)):
+            keys = [np.arange(P)] + [np.arange(P + c, P + d) for j, (c, d) in enumerate(kb) if selected[h, bi, j]]
+            idx = np.concatenate(keys).astype(np.int64)
+            out[P + a:P + b, sl] = attention_head(q[P + a:P + b, sl], k[idx, sl], v[idx, sl], scale)
     return out
 
 

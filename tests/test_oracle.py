@@ -519,8 +519,8 @@ def test_lora_gate_product_kept_in_bf16():
 
 
 def test_reference_kv_cache_step_equals_full_step():
-    """Reference K/V caching (Sol-H3 report, §4 "Reference KV caching
-    mechanism"): once the reference rows' K/V are cached from a full step, a
+    """Reference K/V caching (Sol-H3 report, §5 "Caching Reference Tokens for
+    Reference to Video Generation", "Reference KV caching mechanism"): once the reference rows' K/V are cached from a full step, a
     step over the other rows only, attending over [cached reference K/V ;
     current rows] at their original positions, gives exactly the full step's
     outputs on those rows (same inputs, so the cache is exact here; attention
@@ -538,3 +538,110 @@ def test_reference_kv_cache_step_equals_full_step():
     cached = O.block_forward(xs[keep], w, mod, valid_len=Lc, groups=groups, pos=pos, **kw)
     for name in ("q", "k", "v", "o", "x1", "g", "y"):
         np.testing.assert_allclose(cached[name], full[name][keep], rtol=1e-10, atol=1e-11)
+
+
+# --------------------------------------------------------------------------
+# Sol-Attn block-sparse attention (Sol-H3 report, §3.4 "Sparse Attention")
+# --------------------------------------------------------------------------
+def test_sparse_scores_equal_mean_of_pairwise_dots():
+    """A pooled score is bilinear: (mean of the q rows) . (mean of the k rows)
+    equals the mean of every pairwise q.k over the two blocks. Brute force in
+    float64 over all pairs, ragged last blocks included."""
+    heads, d, P, V = 2, 16, 5, 5 + 23
+    q = RNG.standard_normal((V, heads * d))
+    k = RNG.standard_normal((V, heads * d))
+    got = O.sparse_block_scores(q, k, V, P, heads, d, q_block=8, k_block=6)
+    assert got.shape == (heads, 3, 4) and got.dtype == np.float32
+    sc = 1 / math.sqrt(d)
+    for h in range(heads):
+        for bi, (a, b) in enumerate([(0, 8), (8, 16), (16, 23)]):
+            for bj, (c, e) in enumerate([(0, 6), (6, 12), (12, 18), (18, 23)]):
+                tot = 0.0
+                for r in range(P + a, P + b):
+                    for t in range(P + c, P + e):
+                        tot += sum(q[r, h * d + i] * k[t, h * d + i] for i in range(d))
+                ref = tot / ((b - a) * (e - c)) * sc
+                assert abs(got[h, bi, bj] - ref) <= 1e-5 * (1 + abs(ref)), (h, bi, bj)
+
+
+def test_sparse_select_closed_form():
+    """KV block j made of rows j * e0 * sqrt(d) and query rows e0: the scores
+    are exactly 0, 1, ..., n-1, so mu = (n-1)/2 and sigma = sqrt((n^2-1)/12),
+    and the selected blocks are those j > mu + tau sigma. (d = 16: the scale
+    1/4 and sqrt(d) are exact in FP32; tau = 0 and -0.5 put the threshold on an
+    integer score, which is not selected: "exceed" is strict.)"""
+    d = 16
+    for n, kb, tau in [(10, 4, 1.0), (37, 3, 1.25), (64, 2, 1.5), (9, 5, 0.0), (7, 4, -0.5)]:
+        P, T = 3, n * kb - 1                                  # the last block is one row short
+        V = P + T
+        q = np.zeros((V, d))
+        q[:, 0] = 1.0
+        k = np.zeros((V, d))
+        k[P:, 0] = np.repeat(np.arange(n), kb)[:T] * math.sqrt(d)
+        sc = O.sparse_block_scores(q, k, V, P, 1, d, q_block=16, k_block=kb)
+        np.testing.assert_array_equal(sc[0, 0], np.arange(n, dtype=np.float32))
+        sel, thr = O.sparse_select(sc, tau)
+        mu, sigma = (n - 1) / 2, math.sqrt((n * n - 1) / 12)
+        assert abs(thr[0, 0] - (mu + tau * sigma)) < 1e-5 * n
+        np.testing.assert_array_equal(sel[0, 0], np.arange(n) > mu + tau * sigma)
+
+
+def test_sparse_equal_scores_select_nothing_and_tau_nests():
+    s = np.full((2, 3, 17), 0.25, dtype=np.float32)
+    sel, _ = O.sparse_select(s, 1.0)
+    assert not sel.any()                                      # sigma = 0: no block exceeds mu
+    s = RNG.standard_normal((4, 5, 200)).astype(np.float32)
+    prev = None
+    for tau in (-1.0, 0.0, 1.0, 1.25, 1.5, 3.0):
+        sel, _ = O.sparse_select(s, tau)
+        if prev is not None:
+            assert not np.any(sel & ~prev)                    # a larger tau keeps a subset
+        prev = sel
+    # for standard-normal scores, tau = 1 keeps about P(Z > 1) = 15.9% of the blocks
+    sel, _ = O.sparse_select(RNG.standard_normal((8, 8, 4000)).astype(np.float32), 1.0)
+    assert abs(sel.mean() - 0.1587) < 0.01
+
+
+def test_sparse_attention_all_selected_is_dense():
+    heads, d, P, V = 2, 128, 37, 37 + 300
+    q = RNG.standard_normal((V, heads * d))
+    k = RNG.standard_normal((V, heads * d))
+    v = RNG.standard_normal((V, heads * d))
+    sel = np.ones((heads, 2, 5), dtype=bool)
+    got = O.sparse_attention(q, k, v, V, P, heads, d, sel)
+    np.testing.assert_allclose(got, O.attention(q, k, v, heads, d), rtol=1e-12, atol=1e-13)
+
+
+def test_sparse_attention_matches_explicit_key_lists():
+    """Brute force: each target row's softmax over the explicit list of its
+    keys (prefix rows and selected blocks), in pure-Python loops; prefix rows
+    over every valid key; rows past valid_len are zero."""
+    heads, d, P, V, n_rows = 2, 8, 3, 3 + 20, 25
+    q = RNG.standard_normal((n_rows, heads * d)) * 2
+    k = RNG.standard_normal((n_rows, heads * d)) * 2
+    v = RNG.standard_normal((n_rows, heads * d))
+    qb, kb = 7, 6                                             # target: q blocks 7,7,6; k blocks 6,6,6,2
+    sel = RNG.random((heads, 3, 4)) < 0.5
+    sel[0, 1] = False                                         # a block that attends to the prefix only
+    got = O.sparse_attention(q, k, v, V, P, heads, d, sel, q_block=qb, k_block=kb, n_rows=n_rows)
+    assert np.all(got[V:] == 0)
+    for h in range(heads):
+        sl = slice(h * d, (h + 1) * d)
+        for r in range(V):
+            if r < P:
+                keys = list(range(V))
+            else:
+                b = (r - P) // qb
+                keys = list(range(P)) + [t for t in range(P, V) if sel[h, b, (t - P) // kb]]
+            ref = _naive_attention(q[r:r + 1, sl], k[keys, sl], v[keys, sl], 1 / math.sqrt(d))
+            np.testing.assert_allclose(got[r, sl], ref[0], rtol=1e-12, atol=1e-13)
+
+
+def test_sparse_attention_nothing_selected_is_prefix_attention():
+    heads, d, P, V = 1, 128, 40, 40 + 100
+    q = RNG.standard_normal((V, d))
+    k = RNG.standard_normal((V, d))
+    v = RNG.standard_normal((V, d))
+    got = O.sparse_attention(q, k, v, V, P, heads, d, np.zeros((1, 1, 2), dtype=bool))
+    np.testing.assert_allclose(got[P:], O.attention(q[P:], k[:P], v[:P], heads, d), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(got[:P], O.attention(q[:P], k, v, heads, d), rtol=1e-12, atol=1e-13)
