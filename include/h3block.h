@@ -41,9 +41,12 @@
 extern "C" {
 #endif
 
-#define H3_ABI_VERSION 2
+#define H3_ABI_VERSION 3
 #define H3_MAX_SEGMENTS 4   /* K/V segments per query group */
 #define H3_MAX_GROUPS 8     /* query groups per attention call */
+#define H3_SPARSE_Q_BLOCK 256      /* block-sparse attention: target query block rows */
+#define H3_SPARSE_K_BLOCK 64       /* block-sparse attention: target KV block rows    */
+#define H3_SPARSE_MAX_KBLOCKS 4096 /* KV blocks per call (target rows <= 262,144)     */
 
 enum h3_status {
     H3_OK = 0,
@@ -328,6 +331,62 @@ int h3_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ldw,
               const uint16_t *resid, int64_t ld_r, const float *gate, int64_t ld_gate_group,
               int32_t n_mod_groups, const int32_t *mod_idx, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Sol-Attn block-sparse attention ([Sol-H3] §3.4 "Sparse Attention").
+ *
+ * The packed sequence is [prefix | target]: rows [0, P) are the prefix
+ * (text, conditioning video and audio), rows [P, valid_len) the target video.
+ * Target rows are cut into query blocks of H3_SPARSE_Q_BLOCK rows and target
+ * keys into KV blocks of H3_SPARSE_K_BLOCK rows, both counted from P; the
+ * last block of each may be short. n_qb = ceil(T / 256), n_kb = ceil(T / 64),
+ * T = valid_len - P <= H3_SPARSE_MAX_KBLOCKS * 64 (else H3_ERR_UNSUPPORTED).
+ * The block sizes are this library's choice; the pages do not give them.
+ *
+ * h3_sparse_select - the block selection. For head h and query block b:
+ *   s_bj = mean(q rows of b) . mean(k rows of j) / sqrt(128)  (j over the
+ *          target KV blocks; q, k after Q/K RMSNorm and RoPE)
+ *   j is selected when s_bj > mu_b + tau * sigma_b, mu_b and sigma_b being
+ *   the mean and the population standard deviation of s_b. over j.
+ * Everything is FP32. A larger tau selects fewer blocks.
+ * q, k     [valid_len, heads*128] BF16 at ld_q, ld_k (the column blocks of a
+ *          packed qkv buffer after h3_qk_norm_rope).
+ * blocks   out, uint16 [heads][n_qb][n_kb]: row (h, b) starts with the
+ *          selected j in ascending order; the rest of the row is unspecified.
+ * counts   out, int32 [heads][n_qb]: the number of selected blocks.
+ * workspace device memory of h3_sparse_select_workspace_bytes(...) bytes,
+ *          256-byte aligned (the pooled means, FP32).
+ * blocks, counts and the workspace must not overlap each other, q or k.
+ * T == 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+int h3_sparse_select(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k,
+                     int64_t valid_len, int64_t prefix_len, int32_t heads, int32_t head_dim, float tau,
+                     uint16_t *blocks, int32_t *counts, void *workspace, size_t ws_bytes, void *stream);
+/* Workspace bytes of h3_sparse_select (0 when T == 0 or on bad input). */
+size_t h3_sparse_select_workspace_bytes(int64_t valid_len, int64_t prefix_len, int32_t heads);
+
+/* h3_sparse_attention - attention with the selected blocks:
+ *   prefix rows r < P:  o[r] = softmax over every key in [0, valid_len)
+ *   target rows of query block b: o[r] = softmax over the prefix keys [0, P)
+ *       (always attended, exactly) and the keys of the KV blocks listed in
+ *       blocks[h][b][0 .. counts[h][b])
+ * i.e. dense attention masked to the selected blocks, with the arithmetic of
+ * h3_attention (FP32 scores and softmax, BF16 P). q, k, v, o and
+ * softmax_scale as in h3_attention; padding rows of o are written 0.
+ * P must be >= 1 when valid_len > P. blocks / counts as h3_sparse_select
+ * writes them (any source is accepted): counts are clamped into [0, n_kb];
+ * list entries >= n_kb contribute nothing; an entry listed twice counts twice.
+ * Lists are read, never written.
+ * workspace: h3_sparse_attention_workspace_bytes(...) bytes, 256-byte aligned
+ *          (V^T staging of the prefix and the target keys).
+ * valid_len == P falls back to dense attention over [0, valid_len).
+ * ------------------------------------------------------------------------- */
+int h3_sparse_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k,
+                        const uint16_t *v, int64_t ld_v, uint16_t *o, int64_t ld_o,
+                        int64_t L_buf, int64_t valid_len, int64_t prefix_len, int32_t heads, int32_t head_dim,
+                        float softmax_scale, const uint16_t *blocks, const int32_t *counts,
+                        void *workspace, size_t ws_bytes, void *stream);
+size_t h3_sparse_attention_workspace_bytes(int64_t valid_len, int64_t prefix_len, int32_t heads);
+
 /* Host-only validators: the same checks each entry point runs before it
  * launches anything, callable without a GPU. They return an h3_status. */
 int h3_check_block_forward(const h3_dims *dims, const h3_block_weights *w,
@@ -376,6 +435,16 @@ int h3_check_fused_modulate_norm_lora(const uint16_t *x, int64_t ld_x,
                                       int32_t norm_type, int32_t gate_bf16);
 int h3_check_swiglu_lora(const uint16_t *u, int64_t ld_u, const uint16_t *du, int64_t ld_du,
                          const uint16_t *g, int64_t ld_g, int64_t L_buf, int64_t valid_len, int32_t ffn);
+
+int h3_check_sparse_select(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k,
+                           int64_t valid_len, int64_t prefix_len, int32_t heads, int32_t head_dim, float tau,
+                           const uint16_t *blocks, const int32_t *counts, const void *workspace,
+                           size_t ws_bytes);
+int h3_check_sparse_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k,
+                              const uint16_t *v, int64_t ld_v, const uint16_t *o, int64_t ld_o,
+                              int64_t L_buf, int64_t valid_len, int64_t prefix_len, int32_t heads,
+                              int32_t head_dim, float softmax_scale, const uint16_t *blocks,
+                              const int32_t *counts, const void *workspace, size_t ws_bytes);
 
 /* Human-readable name of a status code (static string). */
 const char *h3_status_string(int status);

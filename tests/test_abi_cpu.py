@@ -268,3 +268,53 @@ def test_lora_consumer_validators():
     assert lib.h3_check_swiglu_lora(u, 2048, du, 2048, gg, 1024, L, L, 1024) == h3.H3_OK
     assert lib.h3_check_swiglu_lora(u, 2048, None, 2048, gg, 1024, L, L, 1024) == h3.H3_ERR_NULL
     assert lib.h3_check_swiglu_lora(u, 2048, gg, 2048, gg, 1024, L, L, 1024) == h3.H3_ERR_ALIAS
+
+
+def test_sparse_validators_and_workspace_sizes():
+    """Block-sparse attention (Sol-H3 report, §3.4): geometry and workspace
+    arithmetic; the checks reject a missing prefix, oversize targets, bad
+    lists and overlapping outputs."""
+    lib = h3.LIB
+    H, heads, L, V, P = 256, 2, 600, 590, 37
+    T = V - P                                               # 553 target rows: 3 query blocks, 9 KV blocks
+    assert h3.sparse_geometry(V, P) == (3, 9)
+    # selection workspace: FP32 query means, then transposed KV means padded to 256 * 4 blocks
+    qbar = heads * 3 * 128 * 4
+    assert lib.h3_sparse_select_workspace_bytes(V, P, heads) == (-(-qbar // 256) * 256) + heads * 128 * 1024 * 4
+    assert lib.h3_sparse_select_workspace_bytes(V, V, heads) == 0
+    assert lib.h3_sparse_select_workspace_bytes(V, V + 1, heads) == 0
+    # attention workspace: V^T of the prefix and of the target keys, each padded to 64
+    assert lib.h3_sparse_attention_workspace_bytes(V, P, heads) == heads * 128 * (64 + 576) * 2
+    assert lib.h3_sparse_attention_workspace_bytes(V, V, heads) == h3.attention_workspace_bytes(V, heads)
+    q = addr(1)
+    k, v = q + 2 * H, q + 4 * H
+    blocks, counts, ws = addr(2), addr(2) + 4096, addr(3)
+    sws = lib.h3_sparse_select_workspace_bytes(V, P, heads)
+    sel = lambda *a: lib.h3_check_sparse_select(*a)
+    assert sel(q, 3 * H, k, 3 * H, V, P, heads, 128, 1.0, blocks, counts, ws, sws) == h3.H3_OK
+    assert sel(q, 3 * H, k, 3 * H, V, P, heads, 128, float("nan"), blocks, counts, ws, sws) == h3.H3_ERR_SHAPE
+    assert sel(q, 3 * H, k, 3 * H, V, P, heads, 128, 1.0, blocks, counts, ws, sws - 1) == h3.H3_ERR_WORKSPACE
+    assert sel(q, 3 * H, k, 3 * H, V, P, heads, 128, 1.0, None, counts, ws, sws) == h3.H3_ERR_NULL
+    assert sel(q, 3 * H, k, 3 * H, V, P, heads, 128, 1.0, blocks + 1, counts, ws, sws) == h3.H3_ERR_ALIGN
+    assert sel(q, 3 * H, k, 3 * H, V, P, heads, 128, 1.0, blocks, blocks + 16, ws, sws) == h3.H3_ERR_ALIAS
+    assert sel(q, 3 * H, k, 3 * H, V, P, heads, 128, 1.0, q + 64, counts, ws, sws) == h3.H3_ERR_ALIAS
+    assert sel(q, 3 * H, k, 3 * H, V, P, heads, 64, 1.0, blocks, counts, ws, sws) == h3.H3_ERR_UNSUPPORTED
+    assert sel(q, 3 * H, k, 3 * H, V, V, heads, 128, 1.0, None, None, None, 0) == h3.H3_OK   # no target rows
+    big = 4096 * 64 + 1
+    assert sel(q, 3 * H, k, 3 * H, big + 1, 1, heads, 128, 1.0, blocks, counts, ws, sws) == h3.H3_ERR_UNSUPPORTED
+    o, aws = addr(4), addr(5)
+    need = lib.h3_sparse_attention_workspace_bytes(V, P, heads)
+    att = lambda *a: lib.h3_check_sparse_attention(*a)
+    args = lambda **kw: [kw.get("q", q), 3 * H, k, 3 * H, v, 3 * H, kw.get("o", o), H, L, V, kw.get("P", P), heads,
+                         128, 0.0, kw.get("b", blocks), kw.get("c", counts), kw.get("ws", aws), kw.get("n", need)]
+    assert att(*args()) == h3.H3_OK
+    assert att(*args(P=0)) == h3.H3_ERR_SHAPE                       # target rows need a prefix
+    assert att(*args(P=V + 1)) == h3.H3_ERR_SHAPE
+    assert att(*args(n=need - 1)) == h3.H3_ERR_WORKSPACE
+    assert att(*args(b=None)) == h3.H3_ERR_NULL
+    assert att(*args(c=counts + 2)) == h3.H3_ERR_ALIGN
+    assert att(*args(b=o + 128)) == h3.H3_ERR_ALIAS                 # lists overlapping the output
+    assert att(*args(o=q + 6 * H)) == h3.H3_ERR_ALIAS
+    assert att(*args(P=V, b=None, c=None)) == h3.H3_OK              # dense fallback needs no lists
+    assert lib.h3_check_sparse_attention(q, 3 * H, k, 3 * H, v, 3 * H, o, H, 0, 0, 0, heads, 128, 0.0, None, None,
+                                         None, 0) == h3.H3_OK

@@ -1,0 +1,246 @@
+"""Sol-Attn block-sparse attention (Sol-H3 report, §3.4 "Sparse Attention")
+through the C ABI, against the oracle.
+
+* Selection: the GPU's lists must equal the oracle's selection, except for a
+  block whose oracle score lies within the FP32 rounding margin of its
+  threshold (either answer is then correct). The margin bound:
+  both sides form each pooled mean from at most 256 BF16 rows and each score
+  from 128 products in FP32. A first-order bound on the difference of the two
+  scores is therefore (256 + 128 + 64) * 2^-24 * scale * sum_c |qbar_c kbar_c|
+  <= 2.7e-5 * A_b, where A_b is the largest such sum in the query block; the
+  threshold mu + tau*sigma moves by at most the same order. The tests allow
+  1e-4 * A_b.
+* Attention: with the oracle's selection handed to the kernel as lists (the
+  list format is plain index bookkeeping), the output must match the oracle's
+  masked dense attention to the parity bar, prefix rows, ragged blocks,
+  empty and full selections included; padding rows are zero.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import h3_oracle as O
+from video_diffusion_transformer_dit_amd import h3
+from video_diffusion_transformer_dit_amd import inputs as I
+
+from util import assert_parity, assert_zero_rows, dev_bf16, f64, poison
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _lists_from_mask(sel):
+    """Oracle selection [heads, n_qb, n_kb] bool -> (blocks uint16, counts int32)
+    in the library's list format."""
+    heads, nq, nk = sel.shape
+    blocks = np.zeros((heads, nq, nk), dtype=np.uint16)
+    counts = np.zeros((heads, nq), dtype=np.int32)
+    for h in range(heads):
+        for b in range(nq):
+            idx = np.nonzero(sel[h, b])[0]
+            blocks[h, b, :len(idx)] = idx
+            counts[h, b] = len(idx)
+    return blocks, counts
+
+
+def _dev_lists(blocks, counts):
+    return (torch.from_numpy(blocks.view(np.int16)).cuda(), torch.from_numpy(counts).cuda())
+
+
+def _margin(q, k, V, P, heads):
+    """A_b of the module docstring, per (head, query block)."""
+    f32 = np.float32
+    T = V - P
+    qb = [(a, min(a + 256, T)) for a in range(0, T, 256)]
+    kb = [(a, min(a + 64, T)) for a in range(0, T, 64)]
+    out = np.empty((heads, len(qb)))
+    for h in range(heads):
+        sl = slice(h * D, (h + 1) * D)
+        qt, kt = np.asarray(q[P:V, sl], f32), np.asarray(k[P:V, sl], f32)
+        qbar = np.abs(np.stack([qt[a:b].mean(0) for a, b in qb]).astype(np.float64))
+        kbar = np.abs(np.stack([kt[a:b].mean(0) for a, b in kb]).astype(np.float64))
+        out[h] = (qbar @ kbar.T).max(axis=1) / np.sqrt(D)
+    return out
+
+
+def _check_selection(blocks_t, counts_t, scores, thr, A, tag, heads_idx=None):
+    """GPU lists against the oracle's scores and thresholds; returns the mask
+    of (head, block) pairs whose selection agrees exactly."""
+    blocks = blocks_t.cpu().numpy().view(np.uint16)
+    counts = counts_t.cpu().numpy()
+    heads, nq, nk = scores.shape
+    agree = np.ones((heads, nq), dtype=bool)
+    n_tie = 0
+    for h in range(heads):
+        hh = h if heads_idx is None else heads_idx[h]
+        for b in range(nq):
+            c = int(counts[hh, b])
+            assert 0 <= c <= nk
+            lst = blocks[hh, b, :c].astype(np.int64)
+            assert np.all(np.diff(lst) > 0), f"{tag}: list ({hh},{b}) not strictly ascending"
+            assert np.all(lst < nk)
+            got = np.zeros(nk, dtype=bool)
+            got[lst] = True
+            ref = scores[h, b] > thr[h, b]
+            diff = np.nonzero(got != ref)[0]
+            if len(diff):
+                gap = np.abs(scores[h, b, diff].astype(np.float64) - float(thr[h, b]))
+                assert np.all(gap <= 1e-4 * A[h, b]), \
+                    f"{tag}: ({hh},{b}) blocks {diff[:5]} differ, |s - thr| {gap[:5]} > {1e-4 * A[h, b]:.3e}"
+                agree[h, b] = False
+                n_tie += len(diff)
+    _say(f"  {tag}: selection agrees on {agree.sum()}/{agree.size} query blocks "
+         f"({n_tie} near-threshold blocks), density {counts.sum() / max(counts.size * nk, 1):.4f}")
+    return agree
+
+
+@pytest.mark.parametrize("heads,P,T,tau", [(2, 37, 553, 1.0), (2, 300, 2000, 1.25), (1, 1, 64, 0.0),
+                                           (3, 64, 70000, 1.5), (2, 512, 262144, 1.0)])
+def test_sparse_select_matches_oracle(heads, P, T, tau):
+    """Lists and counts for ragged and aligned targets, from one KV block to
+    the 4,096-block maximum (262,144 target rows)."""
+    _say(f"sparse_select heads={heads} P={P} T={T} tau={tau}")
+    V = P + T
+    H = heads * D
+    qk = I.normal_bf16(f"sps.qk.{T}", (V, 2 * H))
+    dqk = dev_bf16(qk)
+    q, k = dqk[:, :H], dqk[:, H:]
+    nq, nk = h3.sparse_geometry(V, P)
+    blocks = torch.full((heads, nq, nk), -1, dtype=torch.int16, device="cuda")
+    counts = torch.full((heads, nq), -1, dtype=torch.int32, device="cuda")
+    h3.sparse_select(q, k, V, P, heads, tau, blocks, counts)
+    torch.cuda.synchronize()
+    qf = I.bf16_bits_to_f32(qk[:, :H])
+    kf = I.bf16_bits_to_f32(qk[:, H:])
+    scores = O.sparse_block_scores(qf, kf, V, P, heads, D)
+    _, thr = O.sparse_select(scores, tau)
+    _check_selection(blocks, counts, scores, thr, _margin(qf, kf, V, P, heads), f"T={T}")
+
+
+def _attention_case(heads, L, V, P, density, tag, edit=None):
+    H = heads * D
+    qkv = I.normal_bf16(f"spa.{tag}", (L, 3 * H), 1.0)
+    d = dev_bf16(qkv)
+    q, k, v = d[:, :H], d[:, H:2 * H], d[:, 2 * H:]
+    nq, nk = h3.sparse_geometry(V, P)
+    sel = I.rng_for(f"spa.sel.{tag}").random((heads, nq, nk)) < density
+    if nq:
+        sel[0, 0] = False                       # a query block that attends to the prefix only
+        sel[-1, -1] = True                      # and one that attends to every block
+    blocks, counts = _lists_from_mask(sel)
+    if edit is not None:
+        blocks, counts = edit(blocks, counts)
+    bt, ct = _dev_lists(blocks, counts)
+    o = poison((L, H))
+    h3.sparse_attention(q, k, v, o, V, P, heads, bt, ct)
+    torch.cuda.synchronize()
+    f = I.bf16_bits_to_f32(qkv).astype(np.float64)
+    ref = O.sparse_attention(f[:, :H], f[:, H:2 * H], f[:, 2 * H:], V, P, heads, D, sel, n_rows=V)
+    return o, ref
+
+
+@pytest.mark.parametrize("heads,L,V,P,density", [(2, 600, 590, 37, 0.3), (2, 1100, 1100, 300, 0.5),
+                                                 (1, 257, 257, 1, 0.2), (3, 2112, 2049, 513, 0.1),
+                                                 (2, 700, 650, 650, 0.5)])
+def test_sparse_attention_matches_oracle(heads, L, V, P, density):
+    """Ragged query and KV blocks, prefixes of 1 row to several query tiles,
+    a padding suffix, and P == valid_len (dense fallback)."""
+    _say(f"sparse_attention heads={heads} L={L} V={V} P={P} density={density}")
+    o, ref = _attention_case(heads, L, V, P, density, f"{L}.{V}.{P}")
+    got = f64(o)
+    assert_parity(got[:P], ref[:P], "prefix rows")
+    if V > P:
+        assert_parity(got[P:V], ref[P:V], "target rows")
+    assert_zero_rows(o, V, "o")
+
+
+def test_sparse_attention_list_edge_cases():
+    """Entries past the last block contribute nothing; counts are clamped
+    into [0, n_kb] (a negative count reads no list)."""
+    _say("sparse_attention list edge cases")
+    heads, L, V, P = 2, 600, 590, 37
+    nq, nk = h3.sparse_geometry(V, P)
+
+    def add_bad_entries(blocks, counts):
+        b, c = blocks.copy(), counts.copy()
+        for h in range(heads):
+            for i in range(nq):
+                if c[h, i] < nk:                 # append an out-of-range entry to the list
+                    b[h, i, c[h, i]] = nk + 5 + i
+                    c[h, i] += 1
+        return b, c
+
+    o, ref = _attention_case(heads, L, V, P, 0.3, "edge1", add_bad_entries)
+    assert_parity(f64(o)[:V], ref, "out-of-range entries")
+
+    def negative_counts(blocks, counts):
+        c = counts.copy()
+        c[:, :] = -7
+        return blocks, c
+
+    H = heads * D
+    o2, _ = _attention_case(heads, L, V, P, 0.3, "edge2", negative_counts)
+    qkv = I.bf16_bits_to_f32(I.normal_bf16("spa.edge2", (L, 3 * H), 1.0)).astype(np.float64)
+    ref2 = O.sparse_attention(qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:], V, P, heads, D,
+                              np.zeros((heads, nq, nk), dtype=bool), n_rows=V)
+    assert_parity(f64(o2)[:V], ref2, "negative counts = prefix only")
+
+
+@pytest.mark.timeout(900)
+def test_sparse_full_size_sampled():
+    """The benchmarked workload: 58,758 valid rows in a 58,816-row buffer,
+    42 heads, prefix 1,536 rows (512 text + 1,024 audio), tau = 1.0. The GPU
+    selects and attends; on 3 sampled heads the lists are checked against the
+    oracle, and on sampled rows of those heads (prefix rows and target rows of
+    query blocks whose selection agrees) the output against the oracle's masked
+    attention."""
+    _say("sparse full size")
+    L, V, P, heads, tau = 58816, 58758, 1536, 42, 1.0
+    H = heads * D
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20261202)
+    qkv = torch.randn((L, 3 * H), generator=gen, device="cuda").to(torch.bfloat16)
+    q, k, v = qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:]
+    nq, nk = h3.sparse_geometry(V, P)
+    blocks = torch.empty((heads, nq, nk), dtype=torch.int16, device="cuda")
+    counts = torch.empty((heads, nq), dtype=torch.int32, device="cuda")
+    h3.sparse_select(q, k, V, P, heads, tau, blocks, counts)
+    o = poison((L, H))
+    h3.sparse_attention(q, k, v, o, V, P, heads, blocks, counts)
+    torch.cuda.synchronize()
+    assert_zero_rows(o, V, "o")
+    hs = [0, 17, 41]
+    cols = np.concatenate([np.arange(h * D, (h + 1) * D) for h in hs])
+    ct = torch.from_numpy(cols).cuda()
+    qs = qkv[:V, :H].index_select(1, ct).float().cpu().numpy().astype(np.float64)
+    ks = qkv[:V, H:2 * H].index_select(1, ct).float().cpu().numpy().astype(np.float64)
+    vs = qkv[:V, 2 * H:].index_select(1, ct).float().cpu().numpy().astype(np.float64)
+    scores = O.sparse_block_scores(qs, ks, V, P, len(hs), D)
+    sel, thr = O.sparse_select(scores, tau)
+    agree = _check_selection(blocks, counts, scores, thr, _margin(qs, ks, V, P, len(hs)), "full size", hs)
+    og = o[:V].index_select(1, ct).float().cpu().numpy().astype(np.float64)
+    rng = I.rng_for("spa.full.rows")
+    rows = np.unique(np.concatenate([rng.choice(P, 6, replace=False), P + rng.choice(V - P, 40, replace=False),
+                                     [0, P - 1, P, P + 255, P + 256, V - 1]]))
+    scale = 1.0 / np.sqrt(D)
+    kb = [(a, min(a + 64, V - P)) for a in range(0, V - P, 64)]
+    got, ref = [], []
+    for i, h in enumerate(hs):
+        sl = slice(i * D, (i + 1) * D)
+        for r in rows:
+            if r < P:
+                idx = np.arange(V)
+            else:
+                b = (r - P) // 256
+                if not agree[i, b]:
+                    continue
+                idx = np.concatenate([np.arange(P)] + [np.arange(P + a, P + e) for j, (a, e) in enumerate(kb)
+                                                       if sel[i, b, j]])
+            ref.append(O.attention_head(qs[r:r + 1, sl], ks[idx, sl], vs[idx, sl], scale)[0])
+            got.append(og[r, sl])
+    assert_parity(np.array(got), np.array(ref), f"sampled rows ({len(got)} row-heads)")

@@ -59,6 +59,15 @@ struct AttnArgs {
     const uint16_t *sk[H3_MAX_SEGMENTS];   // segment row 0, head 0
     const uint16_t *svt[H3_MAX_SEGMENTS];  // segment's V^T planes [heads][128][lpad]
     int64_t sldk[H3_MAX_SEGMENTS], slpad[H3_MAX_SEGMENTS], slen[H3_MAX_SEGMENTS];
+    // Block-sparse (list) mode: q and o point at row 0; segment 0 is the
+    // prefix [0, P), segment 1 the target rows [P, P + T). Work items
+    // [0, pre_items) are prefix query tiles (dense over both segments; items
+    // past heads * pre_tiles are idle), the rest target query tiles
+    // (tiles_per_head per head), which read segment 1 through their list.
+    const uint16_t *blocks;  // [heads][tiles_per_head][n_kb] selected KV blocks
+    const int32_t *counts;   // [heads][tiles_per_head]
+    int32_t n_kb, pre_tiles, pre_items;
+    int64_t prefix_len, tgt_rows;
 };
 
 // Segment fields held in scalar registers while the segment is streamed.
@@ -107,42 +116,83 @@ __device__ __forceinline__ SegState seg_of(const AttnArgs &a, int s) {
 }
 
 // K / V^T tile stream: position (segment, first key) of the next tile to load.
+// In list mode, li is the list index of the tile and nxt (a VGPR holding a
+// wave-uniform value) the first key of the following list entry, read from
+// LDS one tile ahead so that no LDS wait sits on the load path.
 struct Cursor {
     int seg;
     int k0, len;  // first key of the tile, keys in the segment (32-bit: scalar compares)
     SegState S;
+    int li, nxt;
 };
 
+// The dense / grouped kernel (SPARSE = false) and the block-sparse list mode
+// (SPARSE = true) share every step; list mode only changes which query tile a
+// workgroup owns and which key tiles of segment 1 it visits.
+template <bool SPARSE>
 __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) {
     constexpr int KB = BKV * 16;  // 16-byte chunks per K tile buffer (16 KB)
     constexpr int VB = D * 8;     // chunks per V^T tile buffer (16 KB)
     // K buffers 0, 1 then V^T buffers 0, 1.
     __shared__ uint4 smem[2 * KB + 2 * VB];
-
-    // ---- work item: (head, group, query tile) with XCD-contiguous order ----
-    const int total = a.tiles_per_head * a.heads;
-    int bid = blockIdx.x;
-    {
-        const int q8 = total / 8, rr = total % 8;
-        const int xcd = bid % 8, local = bid / 8;
-        bid = xcd < rr ? xcd * (q8 + 1) + local : rr * (q8 + 1) + (xcd - rr) * q8 + local;
-    }
-    const int head = bid / a.tiles_per_head;
-    const int tile = bid - head * a.tiles_per_head;
-    const int64_t q0 = (int64_t)tile * BQ;
+    // List mode: the work item's selected tiles as first keys within segment 1.
+    __shared__ int lst[SPARSE ? H3_SPARSE_MAX_KBLOCKS + 1 : 1];
 
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
     const int l32 = lane & 31, h = lane >> 5;
-    const int64_t qw = q0 + wave * WQ;  // this wave's first query
+
+    // ---- work item: (head, query tile) with XCD-contiguous order ----
+    int head;
+    const uint16_t *qbase;  // the tile's first query row, head 0
+    uint16_t *obase;
+    int64_t rows_left;      // query rows from qbase to the end of the tile's group
+    bool listed = false;    // list mode, target tile: segment 1 through the list
+    int lcount = 0;
+    {
+        int bid = blockIdx.x;
+        if (SPARSE && bid < a.pre_items) {
+            if (bid >= a.heads * a.pre_tiles) return;  // idle item (whole workgroup)
+            head = bid / a.pre_tiles;
+            const int64_t q0 = (int64_t)(bid - head * a.pre_tiles) * BQ;
+            qbase = a.q + q0 * a.ld_q;
+            obase = a.o + q0 * a.ld_o;
+            rows_left = a.prefix_len - q0;
+        } else {
+            if (SPARSE) bid -= a.pre_items;  // pre_items is a multiple of 8: same XCD
+            const int total = a.tiles_per_head * a.heads;
+            const int q8 = total / 8, rr = total % 8;
+            const int xcd = bid % 8, local = bid / 8;
+            bid = xcd < rr ? xcd * (q8 + 1) + local : rr * (q8 + 1) + (xcd - rr) * q8 + local;
+            head = bid / a.tiles_per_head;
+            const int tile = bid - head * a.tiles_per_head;
+            const int64_t q0 = (SPARSE ? a.prefix_len : 0) + (int64_t)tile * BQ;
+            qbase = a.q + q0 * a.ld_q;
+            obase = a.o + q0 * a.ld_o;
+            rows_left = (SPARSE ? a.prefix_len + a.tgt_rows : a.rows) - q0;
+            if (SPARSE) {
+                listed = true;
+                const int64_t item = (int64_t)head * a.tiles_per_head + tile;
+                lcount = min(max(a.counts[item], 0), a.n_kb);
+                const uint16_t *src = a.blocks + item * a.n_kb;
+                // Entries past the last block become an empty tile at the
+                // segment end (no load, every key masked).
+                const int tl = (int)a.tgt_rows;
+                for (int i = t; i <= lcount; i += kThreads)
+                    lst[i] = i < lcount ? (src[i] < a.n_kb ? BKV * (int)src[i] : tl) : tl;
+                __syncthreads();
+            }
+        }
+    }
+    const int64_t qw = wave * WQ;  // this wave's first query, relative to qbase
 
     // ---- Q operands: qop[j][ks] = Q[qw + 32j + l32][8(2ks + h) .. +7] ----
     bf16x8_t qop[2][8];
     {
-        const int64_t rows = a.rows - qw;  // may be <= 0 for idle waves
+        const int64_t rows = rows_left - qw;  // may be <= 0 for idle waves
         const __amdgpu_buffer_rsrc_t rqb =
-            make_rsrc(a.q + qw * a.ld_q + head * D, rows > 0 ? ((min<int64_t>(rows, WQ) - 1) * a.ld_q + D) * 2 : 0);
+            make_rsrc(qbase + qw * a.ld_q + head * D, rows > 0 ? ((min<int64_t>(rows, WQ) - 1) * a.ld_q + D) * 2 : 0);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -182,11 +232,12 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     int n_tiles = 0;
 #pragma unroll
     for (int s = 0; s < H3_MAX_SEGMENTS; ++s)
-        if (s < a.n_seg) n_tiles += (int)((a.slen[s] + BKV - 1) / BKV);
+        if (s < a.n_seg && !(listed && s == 1)) n_tiles += (int)((a.slen[s] + BKV - 1) / BKV);
+    if (listed) n_tiles += lcount;
 
     // Two cursors over the same tile sequence: K runs two tiles ahead of the
     // tile being finished, V^T one tile ahead.
-    Cursor kc{0, 0, (int)a.slen[0], seg_of(a, 0)}, vc{0, 0, (int)a.slen[0], seg_of(a, 0)};
+    Cursor kc{0, 0, (int)a.slen[0], seg_of(a, 0), 0, 0}, vc{0, 0, (int)a.slen[0], seg_of(a, 0), 0, 0};
     int k_voff[4], v_voff[4];
     auto set_k = [&]() {
 #pragma unroll
@@ -205,6 +256,15 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     set_k();
     set_v();
     auto advance = [&](Cursor &c, bool is_k) {
+        if (SPARSE && listed && c.seg == 1) {  // next list entry (prefetched)
+            if (++c.li < lcount) {
+                c.k0 = __builtin_amdgcn_readfirstlane(c.nxt);
+                c.nxt = lst[c.li + 1 <= lcount ? c.li + 1 : lcount];
+            } else {
+                c.seg = a.n_seg;
+            }
+            return;
+        }
         c.k0 += BKV;
         if (c.k0 >= c.len) {
             ++c.seg;
@@ -214,6 +274,15 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
                 c.len = (int)c.S.len;
                 if (is_k) set_k();
                 else set_v();
+                if (SPARSE && listed) {  // entering segment 1: first list entry
+                    c.li = 0;
+                    if (lcount > 0) {
+                        c.k0 = __builtin_amdgcn_readfirstlane(lst[0]);
+                        c.nxt = lst[1];
+                    } else {
+                        c.seg = a.n_seg;
+                    }
+                }
             }
         }
     };
@@ -227,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     auto issue_k = [&](int b, int half) {
         const int rows = min(kc.len - kc.k0, BKV);
         i32x4_t r = raw_rsrc(kc.S.k + (int64_t)kc.k0 * kc.S.ldk + head * D, ((int64_t)(rows - 1) * kc.S.ldk + D) * 2);
-        if (kc.seg >= a.n_seg) r.z = 0;
+        if (kc.seg >= a.n_seg || rows <= 0) r.z = 0;
 #pragma unroll
         for (int i = 2 * half; i < 2 * half + 2; ++i)
             dma_slab(r, lds0 + (uint32_t)((b * KB + 64 * (4 * wave + i)) * 16), k_voff[i], 0);
@@ -398,7 +467,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
         if (odd) {
             const int rows = min(kc.len - kc.k0, BKV);
             rl = raw_rsrc(kc.S.k + (int64_t)kc.k0 * kc.S.ldk + head * D, ((int64_t)(rows - 1) * kc.S.ldk + D) * 2);
-            if (kc.seg >= a.n_seg) rl.z = 0;
+            if (kc.seg >= a.n_seg || rows <= 0) rl.z = 0;
             m0b = lds0 + (uint32_t)((tp * KB + 64 * 4 * wave) * 16);
 #pragma unroll
             for (int i = 0; i < 4; ++i) voffs[i] = k_voff[i];
@@ -535,8 +604,8 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
         const float l_tot = pair_sum(l_run[j]);
         const float inv = 1.0f / l_tot;
         const int64_t q = qw + 32 * j + l32;
-        if (q < a.rows) {
-            uint16_t *orow = a.o + q * a.ld_o + head * D;
+        if (q < rows_left) {
+            uint16_t *orow = obase + q * a.ld_o + head * D;
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -584,6 +653,17 @@ __global__ __launch_bounds__(256) void vt_transpose_kernel(const uint16_t *v, in
     }
 }
 
+// Transposed V of every segment of the plan into the workspace.
+void stage_vt(const VtPlan &plan, const uint16_t *v, int64_t ld_v, int32_t heads, uint8_t *ws, hipStream_t stream) {
+    for (int i = 0; i < plan.n; ++i) {
+        const VtSeg &e = plan.seg[i];
+        const uint16_t *src = e.own ? v + e.begin * ld_v : e.v + e.begin * e.ld;
+        const int64_t ld = e.own ? ld_v : e.ld;
+        vt_transpose_kernel<<<dim3((unsigned)(e.lpad / BKV), (unsigned)heads), 256, 0, stream>>>(
+            src, ld, e.len, reinterpret_cast<uint16_t *>(ws + e.off), e.lpad);
+    }
+}
+
 }  // namespace
 
 void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k, const uint16_t *v,
@@ -606,13 +686,7 @@ void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_
     VtPlan plan;
     vt_plan(is_dense ? nullptr : groups, is_dense ? 0 : n_groups, valid_len, heads, &plan);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    for (int i = 0; i < plan.n; ++i) {
-        const VtSeg &e = plan.seg[i];
-        const uint16_t *src = e.own ? v + e.begin * ld_v : e.v + e.begin * e.ld;
-        const int64_t ld = e.own ? ld_v : e.ld;
-        vt_transpose_kernel<<<dim3((unsigned)(e.lpad / BKV), (unsigned)heads), 256, 0, stream>>>(
-            src, ld, e.len, reinterpret_cast<uint16_t *>(ws + e.off), e.lpad);
-    }
+    stage_vt(plan, v, ld_v, heads, ws, stream);
     std::pair<int64_t, int64_t> cov[H3_MAX_GROUPS];
     int nc = 0;
     for (int gi = 0; gi < n_groups; ++gi) {
@@ -643,7 +717,7 @@ void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_
             a.slpad[s] = e.lpad;
             a.slen[s] = ss.len;
         }
-        attention_fwd_kernel<<<dim3((unsigned)(a.tiles_per_head * heads)), kThreads, 0, stream>>>(a);
+        attention_fwd_kernel<false><<<dim3((unsigned)(a.tiles_per_head * heads)), kThreads, 0, stream>>>(a);
     }
     // Zero the rows of o outside every group (the padding suffix included).
     std::sort(cov, cov + nc);
@@ -669,5 +743,70 @@ extern "C" int h3_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, 
     if ((s = device_check()) != H3_OK) return s;
     launch_attention(q, ld_q, k, ld_k, v, ld_v, o, ld_o, L_buf, valid_len, heads, softmax_scale, groups, n_groups,
                      workspace, (hipStream_t)stream);
+    return launch_status();
+}
+
+namespace h3 {
+
+void launch_sparse_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k, const uint16_t *v,
+                             int64_t ld_v, uint16_t *o, int64_t ld_o, int64_t L_buf, int64_t valid_len,
+                             int64_t prefix_len, int32_t heads, float softmax_scale, const uint16_t *blocks,
+                             const int32_t *counts, void *workspace, hipStream_t stream) {
+    if (prefix_len >= valid_len) {  // no target rows: dense attention
+        launch_attention(q, ld_q, k, ld_k, v, ld_v, o, ld_o, L_buf, valid_len, heads, softmax_scale, nullptr, 0,
+                         workspace, stream);
+        return;
+    }
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+    h3_qgroup g;
+    sparse_vt_group(valid_len, prefix_len, &g);
+    VtPlan plan;
+    vt_plan(&g, 1, valid_len, heads, &plan);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    stage_vt(plan, v, ld_v, heads, ws, stream);
+    const int64_t T = valid_len - prefix_len;
+    AttnArgs a = {};
+    a.q = q;
+    a.o = o;
+    a.ld_q = ld_q;
+    a.ld_o = ld_o;
+    a.rows = valid_len;
+    a.heads = heads;
+    a.tiles_per_head = (int32_t)((T + BQ - 1) / BQ);
+    a.n_seg = 2;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    for (int s = 0; s < 2; ++s) {
+        const VtSeg &e = plan.seg[plan.map[0][s]];
+        a.sk[s] = k + g.seg[s].begin * ld_k;
+        a.sldk[s] = ld_k;
+        a.svt[s] = reinterpret_cast<const uint16_t *>(ws + e.off);
+        a.slpad[s] = e.lpad;
+        a.slen[s] = g.seg[s].len;
+    }
+    a.blocks = blocks;
+    a.counts = counts;
+    a.n_kb = (int32_t)((T + BKV - 1) / BKV);
+    a.pre_tiles = (int32_t)((prefix_len + BQ - 1) / BQ);
+    a.pre_items = (heads * a.pre_tiles + 7) / 8 * 8;
+    a.prefix_len = prefix_len;
+    a.tgt_rows = T;
+    const unsigned grid = (unsigned)(a.pre_items + a.tiles_per_head * heads);
+    attention_fwd_kernel<true><<<dim3(grid), kThreads, 0, stream>>>(a);
+    launch_zero_rows(o, ld_o, (int64_t)heads * D, valid_len, L_buf, stream);
+}
+
+}  // namespace h3
+
+extern "C" int h3_sparse_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k,
+                                   const uint16_t *v, int64_t ld_v, uint16_t *o, int64_t ld_o, int64_t L_buf,
+                                   int64_t valid_len, int64_t prefix_len, int32_t heads, int32_t head_dim,
+                                   float softmax_scale, const uint16_t *blocks, const int32_t *counts,
+                                   void *workspace, size_t ws_bytes, void *stream) {
+    int s = h3_check_sparse_attention(q, ld_q, k, ld_k, v, ld_v, o, ld_o, L_buf, valid_len, prefix_len, heads,
+                                      head_dim, softmax_scale, blocks, counts, workspace, ws_bytes);
+    if (s != H3_OK || L_buf == 0) return s;
+    if ((s = device_check()) != H3_OK) return s;
+    launch_sparse_attention(q, ld_q, k, ld_k, v, ld_v, o, ld_o, L_buf, valid_len, prefix_len, heads, softmax_scale,
+                            blocks, counts, workspace, (hipStream_t)stream);
     return launch_status();
 }

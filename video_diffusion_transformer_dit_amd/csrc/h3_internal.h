@@ -31,6 +31,23 @@ struct VtPlan {
 // groups == NULL plans one own segment [0, dense_len).
 void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads, VtPlan *out);
 
+// Geometry of Sol-Attn block selection over target rows [P, valid_len):
+// query blocks of H3_SPARSE_Q_BLOCK rows, KV blocks of H3_SPARSE_K_BLOCK rows,
+// and the selection workspace (FP32 query-block means [heads][n_qb][128], then
+// transposed KV-block means [heads][128][n_kb_pad]).
+struct SparseGeom {
+    int64_t T;                 // target rows
+    int64_t n_qb, n_kb;        // query / KV blocks
+    int64_t per, n_kb_pad;     // KV blocks per selection thread (multiple of 4); 256 * per
+    int64_t qbar_off, kbar_off;
+    size_t ws_bytes;
+};
+void sparse_geometry(int64_t valid_len, int64_t prefix_len, int32_t heads, SparseGeom *g);
+// The block-sparse attention's two key segments as one query group over
+// [0, valid_len): own rows [0, P) and [P, valid_len). Used to plan and check
+// the V^T staging.
+void sparse_vt_group(int64_t valid_len, int64_t prefix_len, h3_qgroup *g);
+
 // Byte offsets and row strides of the block's workspace buffers.
 struct WsLayout {
     int64_t off[H3_WS_COUNT];

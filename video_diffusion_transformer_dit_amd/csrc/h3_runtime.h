@@ -40,4 +40,12 @@ void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_
                       int64_t valid_len, int32_t heads, float softmax_scale, const h3_qgroup *groups,
                       int32_t n_groups, void *workspace, hipStream_t stream);
 
+void launch_sparse_select(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k, int64_t valid_len,
+                          int64_t prefix_len, int32_t heads, float tau, uint16_t *blocks, int32_t *counts,
+                          void *workspace, hipStream_t stream);
+void launch_sparse_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k, const uint16_t *v,
+                             int64_t ld_v, uint16_t *o, int64_t ld_o, int64_t L_buf, int64_t valid_len,
+                             int64_t prefix_len, int32_t heads, float softmax_scale, const uint16_t *blocks,
+                             const int32_t *counts, void *workspace, hipStream_t stream);
+
 }  // namespace h3

@@ -31,6 +31,9 @@ Mat mat(const void *p, int64_t rows, int64_t cols, int64_t ld, int64_t elem = kB
     return Mat{reinterpret_cast<uintptr_t>(p), rows, cols, ld, elem};
 }
 
+// Byte span of a small device array (lists, counts, workspace).
+Mat bytes_of(const void *p, int64_t n) { return mat(p, 1, n, n, 1); }
+
 // True when two strided matrices can share a byte. Matrices with the same
 // row stride are compared column-block-wise (column blocks of one packed
 // buffer are disjoint); otherwise their spans are compared.
@@ -87,6 +90,30 @@ int check_dims(const h3_dims *d) {
     if (!(d->eps >= 0.0f) || !std::isfinite(d->eps)) return H3_ERR_SHAPE;
     if (!(d->rope_theta > 0.0f) || !std::isfinite(d->rope_theta)) return H3_ERR_SHAPE;
     return H3_OK;
+}
+
+void sparse_geometry(int64_t valid_len, int64_t prefix_len, int32_t heads, SparseGeom *g) {
+    const int64_t T = valid_len > prefix_len ? valid_len - prefix_len : 0;
+    g->T = T;
+    g->n_qb = (T + H3_SPARSE_Q_BLOCK - 1) / H3_SPARSE_Q_BLOCK;
+    g->n_kb = (T + H3_SPARSE_K_BLOCK - 1) / H3_SPARSE_K_BLOCK;
+    int64_t per = (g->n_kb + 255) / 256;
+    per = (per + 3) / 4 * 4;
+    g->per = per;
+    g->n_kb_pad = 256 * per;
+    g->qbar_off = 0;
+    const int64_t qbar_bytes = (int64_t)heads * g->n_qb * kHeadDim * 4;
+    g->kbar_off = (qbar_bytes + kWsAlign - 1) / kWsAlign * kWsAlign;
+    g->ws_bytes = (size_t)(g->kbar_off + (int64_t)heads * kHeadDim * g->n_kb_pad * 4);
+}
+
+void sparse_vt_group(int64_t valid_len, int64_t prefix_len, h3_qgroup *g) {
+    std::memset(g, 0, sizeof(*g));
+    g->q_begin = 0;
+    g->q_end = valid_len;
+    g->n_seg = 2;
+    g->seg[0] = h3_kv_seg{nullptr, nullptr, 0, 0, prefix_len};
+    g->seg[1] = h3_kv_seg{nullptr, nullptr, 0, prefix_len, valid_len - prefix_len};
 }
 
 void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads, VtPlan *out) {
@@ -174,6 +201,14 @@ size_t h3_attention_workspace_bytes(int64_t valid_len, int32_t heads, const h3_q
     VtPlan p;
     vt_plan(groups, n_groups, valid_len, heads, &p);
     return p.bytes;
+}
+
+size_t h3_sparse_attention_workspace_bytes(int64_t valid_len, int64_t prefix_len, int32_t heads) {
+    if (valid_len < 0 || prefix_len < 0 || prefix_len > valid_len || heads <= 0) return 0;
+    if (prefix_len == valid_len) return h3_attention_workspace_bytes(valid_len, heads, nullptr, 0);
+    h3_qgroup g;
+    sparse_vt_group(valid_len, prefix_len, &g);
+    return h3_attention_workspace_bytes(valid_len, heads, &g, 1);
 }
 
 int h3_block_workspace_layout(const h3_dims *dims, int64_t L_buf, const h3_qgroup *groups, int32_t n_groups,
@@ -525,6 +560,67 @@ int h3_check_block_forward(const h3_dims *dims, const h3_block_weights *w, const
         for (const Mat &m : weights)
             if (overlap(ek, m) || overlap(ev, m)) return H3_ERR_ALIAS;
     }
+    return H3_OK;
+}
+
+
+int h3_check_sparse_select(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k, int64_t valid_len,
+                           int64_t prefix_len, int32_t heads, int32_t head_dim, float tau, const uint16_t *blocks,
+                           const int32_t *counts, const void *workspace, size_t ws_bytes) {
+    if (valid_len < 0 || prefix_len < 0 || prefix_len > valid_len) return H3_ERR_SHAPE;
+    if (heads <= 0 || head_dim <= 0) return H3_ERR_SHAPE;
+    if (head_dim != kHeadDim) return H3_ERR_UNSUPPORTED;
+    if (!std::isfinite(tau)) return H3_ERR_SHAPE;
+    const int64_t T = valid_len - prefix_len;
+    if (T > (int64_t)H3_SPARSE_MAX_KBLOCKS * H3_SPARSE_K_BLOCK) return H3_ERR_UNSUPPORTED;
+    if (T == 0) return H3_OK;
+    if (!q || !k || !blocks || !counts) return H3_ERR_NULL;
+    const int64_t H = (int64_t)heads * head_dim;
+    H3_TRY(check_bf16_mat(q, ld_q, H));
+    H3_TRY(check_bf16_mat(k, ld_k, H));
+    if ((reinterpret_cast<uintptr_t>(blocks) & 1u) || (reinterpret_cast<uintptr_t>(counts) & 3u)) return H3_ERR_ALIGN;
+    SparseGeom g;
+    sparse_geometry(valid_len, prefix_len, heads, &g);
+    if (workspace == nullptr || ws_bytes < g.ws_bytes) return H3_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0) return H3_ERR_ALIGN;
+    const Mat outs[3] = {bytes_of(blocks, (int64_t)heads * g.n_qb * g.n_kb * 2),
+                         bytes_of(counts, (int64_t)heads * g.n_qb * 4), bytes_of(workspace, (int64_t)g.ws_bytes)};
+    const Mat mq = mat(q, valid_len, H, ld_q), mk = mat(k, valid_len, H, ld_k);
+    for (int i = 0; i < 3; ++i) {
+        if (overlap(outs[i], mq) || overlap(outs[i], mk)) return H3_ERR_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outs[j])) return H3_ERR_ALIAS;
+    }
+    return H3_OK;
+}
+
+int h3_check_sparse_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k, const uint16_t *v,
+                              int64_t ld_v, const uint16_t *o, int64_t ld_o, int64_t L_buf, int64_t valid_len,
+                              int64_t prefix_len, int32_t heads, int32_t head_dim, float softmax_scale,
+                              const uint16_t *blocks, const int32_t *counts, const void *workspace,
+                              size_t ws_bytes) {
+    H3_TRY(check_rows(L_buf, valid_len));
+    if (prefix_len < 0 || prefix_len > valid_len) return H3_ERR_SHAPE;
+    const int64_t T = valid_len - prefix_len;
+    if (T > 0 && prefix_len < 1) return H3_ERR_SHAPE;  // target rows always attend to the prefix
+    if (T > (int64_t)H3_SPARSE_MAX_KBLOCKS * H3_SPARSE_K_BLOCK) return H3_ERR_UNSUPPORTED;
+    if (T == 0)
+        return h3_check_attention(q, ld_q, k, ld_k, v, ld_v, o, ld_o, L_buf, valid_len, heads, head_dim,
+                                  softmax_scale, nullptr, 0, workspace, ws_bytes);
+    h3_qgroup g;
+    sparse_vt_group(valid_len, prefix_len, &g);
+    H3_TRY(h3_check_attention(q, ld_q, k, ld_k, v, ld_v, o, ld_o, L_buf, valid_len, heads, head_dim, softmax_scale,
+                              &g, 1, workspace, ws_bytes));
+    if (!blocks || !counts) return H3_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(blocks) & 1u) || (reinterpret_cast<uintptr_t>(counts) & 3u)) return H3_ERR_ALIGN;
+    SparseGeom sg;
+    sparse_geometry(valid_len, prefix_len, heads, &sg);
+    const int64_t H = (int64_t)heads * head_dim;
+    const Mat mo = mat(o, L_buf, H, ld_o);
+    const Mat mb = bytes_of(blocks, (int64_t)heads * sg.n_qb * sg.n_kb * 2);
+    const Mat mc = bytes_of(counts, (int64_t)heads * sg.n_qb * 4);
+    const Mat mw = bytes_of(workspace, (int64_t)h3_sparse_attention_workspace_bytes(valid_len, prefix_len, heads));
+    if (overlap(mo, mb) || overlap(mo, mc) || overlap(mw, mb) || overlap(mw, mc)) return H3_ERR_ALIAS;
     return H3_OK;
 }
 

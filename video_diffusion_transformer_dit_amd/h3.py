@@ -21,6 +21,7 @@ H3_WS_H, H3_WS_QKV, H3_WS_O, H3_WS_X1, H3_WS_H2, H3_WS_G, H3_WS_VT = range(7)
 H3_WS_COUNT = 7
 H3_MAX_SEGMENTS = 4
 H3_MAX_GROUPS = 8
+H3_SPARSE_Q_BLOCK, H3_SPARSE_K_BLOCK, H3_SPARSE_MAX_KBLOCKS = 256, 64, 4096
 
 
 class H3Error(RuntimeError):
@@ -96,6 +97,12 @@ def _load():
         "h3_block_workspace_bytes": [C.POINTER(Dims), I64, C.POINTER(QGroup), I32],
         "h3_block_workspace_layout": [C.POINTER(Dims), I64, C.POINTER(QGroup), I32, C.POINTER(I64),
                                       C.POINTER(I64)],
+        "h3_sparse_select": [P, I64, P, I64, I64, I64, I32, I32, F32, P, P, P, SZ, P],
+        "h3_check_sparse_select": [P, I64, P, I64, I64, I64, I32, I32, F32, P, P, P, SZ],
+        "h3_sparse_select_workspace_bytes": [I64, I64, I32],
+        "h3_sparse_attention": [P, I64, P, I64, P, I64, P, I64, I64, I64, I64, I32, I32, F32, P, P, P, SZ, P],
+        "h3_check_sparse_attention": [P, I64, P, I64, P, I64, P, I64, I64, I64, I64, I32, I32, F32, P, P, P, SZ],
+        "h3_sparse_attention_workspace_bytes": [I64, I64, I32],
         "h3_status_string": [C.c_int],
         "h3_abi_version": [],
     }
@@ -105,6 +112,8 @@ def _load():
         f.restype = C.c_int
     lib.h3_block_workspace_bytes.restype = C.c_size_t
     lib.h3_attention_workspace_bytes.restype = C.c_size_t
+    lib.h3_sparse_select_workspace_bytes.restype = C.c_size_t
+    lib.h3_sparse_attention_workspace_bytes.restype = C.c_size_t
     lib.h3_status_string.restype = C.c_char_p
     return lib
 
@@ -115,7 +124,9 @@ EXPORTS = ["h3_block_forward", "h3_attention", "h3_fused_modulate_norm", "h3_qk_
            "h3_abi_version", "h3_check_block_forward", "h3_check_attention", "h3_check_fused_modulate_norm",
            "h3_check_qk_norm_rope", "h3_check_swiglu", "h3_check_linear", "h3_qk_norm_rope_lora",
            "h3_fused_modulate_norm_lora", "h3_swiglu_lora", "h3_check_qk_norm_rope_lora",
-           "h3_check_fused_modulate_norm_lora", "h3_check_swiglu_lora"]
+           "h3_check_fused_modulate_norm_lora", "h3_check_swiglu_lora", "h3_sparse_select", "h3_sparse_attention",
+           "h3_sparse_select_workspace_bytes", "h3_sparse_attention_workspace_bytes", "h3_check_sparse_select",
+           "h3_check_sparse_attention"]
 
 
 def status_string(s: int) -> str:
@@ -277,3 +288,43 @@ def linear(a, w, c, M_valid, epilogue=H3_EPI_STORE, bias=None, resid=None, gate=
                       M_valid, N, K, epilogue, _ptr(resid), _ld(resid), _ptr(gate), ld_gate_group, n_mod_groups,
                       _ptr(mod_idx), _stream(stream))
     _ok(s, "h3_linear")
+
+
+def sparse_geometry(valid_len: int, prefix_len: int):
+    """(n_qb, n_kb): target query blocks and KV blocks of a block-sparse call."""
+    T = max(valid_len - prefix_len, 0)
+    return -(-T // H3_SPARSE_Q_BLOCK), -(-T // H3_SPARSE_K_BLOCK)
+
+
+def sparse_select_workspace_bytes(valid_len: int, prefix_len: int, heads: int) -> int:
+    return int(LIB.h3_sparse_select_workspace_bytes(valid_len, prefix_len, heads))
+
+
+def sparse_attention_workspace_bytes(valid_len: int, prefix_len: int, heads: int) -> int:
+    return int(LIB.h3_sparse_attention_workspace_bytes(valid_len, prefix_len, heads))
+
+
+def sparse_select(q, k, valid_len, prefix_len, heads, tau, blocks, counts, workspace=None, stream=None):
+    """blocks: uint16 (or int16) device tensor [heads, n_qb, n_kb]; counts: int32
+    [heads, n_qb]. workspace: uint8 device tensor or None (allocated here)."""
+    if workspace is None:
+        import torch
+        workspace = torch.empty(max(sparse_select_workspace_bytes(valid_len, prefix_len, heads), 1),
+                                dtype=torch.uint8, device=q.device)
+    s = LIB.h3_sparse_select(_ptr(q), q.stride(0), _ptr(k), k.stride(0), valid_len, prefix_len, heads, 128,
+                             float(tau), _ptr(blocks), _ptr(counts), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream))
+    _ok(s, "h3_sparse_select")
+
+
+def sparse_attention(q, k, v, o, valid_len, prefix_len, heads, blocks, counts, softmax_scale=0.0, workspace=None,
+                     stream=None):
+    if workspace is None:
+        import torch
+        workspace = torch.empty(max(sparse_attention_workspace_bytes(valid_len, prefix_len, heads), 1),
+                                dtype=torch.uint8, device=q.device)
+    s = LIB.h3_sparse_attention(_ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0), _ptr(o),
+                                o.stride(0), q.shape[0], valid_len, prefix_len, heads, 128, softmax_scale,
+                                _ptr(blocks), _ptr(counts), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream))
+    _ok(s, "h3_sparse_attention")
