@@ -202,6 +202,43 @@ def reference_kv_cache(torch, h3, dev, dims, weights, mod, gen, L, V, H, n_ref=1
             "cached_step_ms": round(cached_ms, 3), "speedup": round(full_ms / cached_ms, 3)}
 
 
+def block_sparse(torch, h3, dev, q, k, v, o, V, heads, dense_ms, iters, prefix=1536):
+    """Sol-Attn block-sparse attention on the block's own q~, k~, v (after
+    QK-norm and RoPE) at the pages' refinement tau schedule. The prefix is
+    the workload's 512 text + 1,024 audio rows. Reports the selection and
+    attention times, the fraction of target KV blocks selected, and the
+    attention's rate on the work it does (4 * 128 flops per query-key pair
+    actually attended)."""
+    nq, nk = h3.sparse_geometry(V, prefix)
+    T = V - prefix
+    blocks = torch.empty((heads, nq, nk), dtype=torch.int16, device=dev)
+    counts = torch.empty((heads, nq), dtype=torch.int32, device=dev)
+    sws = torch.empty(h3.sparse_select_workspace_bytes(V, prefix, heads), dtype=torch.uint8, device=dev)
+    aws = torch.empty(h3.sparse_attention_workspace_bytes(V, prefix, heads), dtype=torch.uint8, device=dev)
+    rows_b = torch.full((nq,), 256.0, dtype=torch.float64)
+    rows_b[-1] = T - 256 * (nq - 1)
+    last_len = T - 64 * (nk - 1)
+    out = {"prefix_rows": prefix, "target_rows": T, "query_block": h3.H3_SPARSE_Q_BLOCK,
+           "kv_block": h3.H3_SPARSE_K_BLOCK, "dense_attention_ms": round(dense_ms, 3), "tau": {}}
+    for tau in (1.0, 1.25, 1.5):
+        sel_ms = time_calls(torch, lambda: h3.sparse_select(q, k, V, prefix, heads, tau, blocks, counts, sws), iters, 1)
+        att_ms = time_calls(torch, lambda: h3.sparse_attention(q, k, v, o, V, prefix, heads, blocks, counts,
+                                                               workspace=aws), iters, 1)
+        c = counts.cpu().to(torch.float64)
+        # lists are ascending: the short last KV block is selected when it ends the list
+        tail = blocks.cpu().to(torch.int64).gather(2, (c.long() - 1).clamp(min=0).unsqueeze(-1)).squeeze(-1)
+        has_last = ((c > 0) & (tail == nk - 1)).to(torch.float64)
+        keys = prefix + 64.0 * c - (64 - last_len) * has_last
+        pairs = float((keys * rows_b).sum()) + heads * prefix * V
+        tf = 4.0 * 128 * pairs / (att_ms * 1e-3) / 1e12
+        out["tau"][str(tau)] = {"select_ms": round(sel_ms, 3), "attention_ms": round(att_ms, 3),
+                                "kv_block_density": round(float(c.sum()) / (heads * nq * nk), 4),
+                                "attended_fraction": round(pairs / (heads * V * V), 4),
+                                "attention_tflops_on_attended": round(tf, 1),
+                                "speedup_vs_dense": round(dense_ms / (sel_ms + att_ms), 2)}
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -343,6 +380,8 @@ def main(argv=None) -> int:
     }
     if not a.no_next:
         out["next"] = {"lora_consumer_fusion": lora_consumers(torch, h3, dev, gen, L, V, H, heads, F, kit)}
+        out["next"]["block_sparse_attention"] = block_sparse(torch, h3, dev, qkv[:, :H], qkv[:, H:2 * H],
+                                                             qkv[:, 2 * H:], o, V, heads, k_ms["attention"], kit)
         out["next"]["reference_kv_cache"] = reference_kv_cache(torch, h3, dev, dims, weights, mod, gen, L, V, H)
     if a.calibration_copy:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)   # 1 GiB

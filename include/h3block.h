@@ -387,6 +387,34 @@ int h3_sparse_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int6
                         void *workspace, size_t ws_bytes, void *stream);
 size_t h3_sparse_attention_workspace_bytes(int64_t valid_len, int64_t prefix_len, int32_t heads);
 
+/* h3_block_forward_sparse - h3_block_forward with step 4 replaced by Sol-Attn
+ * block-sparse attention ([Sol-H3] §3.4): after QK-norm and RoPE, the block
+ * runs h3_sparse_select on its own q~, k~ with threshold tau, then
+ * h3_sparse_attention with prefix_len (prefix rows dense, prefix keys always
+ * attended). The pages keep the first two layers dense and use tau 1.0, 1.25
+ * and 1.5 over the three refinement steps: that schedule belongs to the
+ * caller, which picks this entry point or h3_block_forward per layer.
+ * Arguments as h3_block_forward (no query groups, no K/V export), plus
+ * prefix_len (>= 1 when valid_len > prefix_len) and a finite tau.
+ * workspace: h3_block_sparse_workspace_bytes(dims, L_buf, valid_len,
+ *          prefix_len) bytes, 256-byte aligned. It begins with the dense
+ *          block's layout (h3_block_workspace_layout(dims, L_buf, NULL, 0)
+ *          gives the intermediates' offsets); the V^T slot may be larger,
+ *          and the selection's lists, counts and pooled means follow it. */
+int h3_block_forward_sparse(const h3_dims *dims, const h3_block_weights *w,
+                            const uint16_t *x, uint16_t *y,
+                            const float *mod, int32_t n_mod_groups, const int32_t *mod_idx,
+                            const int32_t *pos, int64_t L_buf, int64_t valid_len,
+                            int64_t prefix_len, float tau,
+                            void *workspace, size_t ws_bytes, void *stream);
+size_t h3_block_sparse_workspace_bytes(const h3_dims *dims, int64_t L_buf, int64_t valid_len,
+                                       int64_t prefix_len);
+/* Byte offsets, inside that workspace, of the selection the call made: the
+ * block lists (uint16 [heads][n_qb][n_kb]) and their counts (int32
+ * [heads][n_qb]), as h3_sparse_select documents them. */
+int h3_block_sparse_workspace_layout(const h3_dims *dims, int64_t L_buf, int64_t valid_len, int64_t prefix_len,
+                                     int64_t *blocks_off, int64_t *counts_off);
+
 /* Host-only validators: the same checks each entry point runs before it
  * launches anything, callable without a GPU. They return an h3_status. */
 int h3_check_block_forward(const h3_dims *dims, const h3_block_weights *w,
@@ -436,6 +464,11 @@ int h3_check_fused_modulate_norm_lora(const uint16_t *x, int64_t ld_x,
 int h3_check_swiglu_lora(const uint16_t *u, int64_t ld_u, const uint16_t *du, int64_t ld_du,
                          const uint16_t *g, int64_t ld_g, int64_t L_buf, int64_t valid_len, int32_t ffn);
 
+int h3_check_block_forward_sparse(const h3_dims *dims, const h3_block_weights *w,
+                                  const uint16_t *x, uint16_t *y,
+                                  const float *mod, int32_t n_mod_groups, const int32_t *mod_idx,
+                                  const int32_t *pos, int64_t L_buf, int64_t valid_len,
+                                  int64_t prefix_len, float tau, const void *workspace, size_t ws_bytes);
 int h3_check_sparse_select(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k,
                            int64_t valid_len, int64_t prefix_len, int32_t heads, int32_t head_dim, float tau,
                            const uint16_t *blocks, const int32_t *counts, const void *workspace,

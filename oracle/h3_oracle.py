@@ -403,7 +403,7 @@ def swiglu(u: np.ndarray, ffn: int) -> np.ndarray:
 def block_forward(x, w, mod, *, heads: int, head_dim: int, ffn: int, valid_len: int,
                   rot_dim: int = 64, theta: float = 10000.0, eps: float = 1e-6,
                   norm_type: int = 0, pairing: int = 0, mod_idx=None, pos=None,
-                  groups=None, scale=None, bf16_points: bool = False):
+                  groups=None, scale=None, bf16_points: bool = False, sparse=None):
     """One DiT block forward over a packed sequence of L_buf rows, valid_len valid.
 
     x      [L_buf, H] float64 (decoded BF16 values)
@@ -413,6 +413,9 @@ def block_forward(x, w, mod, *, heads: int, head_dim: int, ffn: int, valid_len: 
     groups None for dense attention over [0, valid_len); else a list of
            (q_begin, q_end, segs) where segs lists ('self', begin, len) for rows of
            this call's own K/V, or (k_array, v_array) for external (history) K/V.
+    sparse None, or (prefix_len, tau): Sol-Attn block-sparse attention (Sol-H3
+           §3.4) in place of dense attention, its blocks selected from this
+           block's own q~ and k~; the selection is returned as 'sparse_sel'.
 
     Steps (Sol-H3 §3.5 groups (1)-(3) around the projections):
       h   = modnorm(x; shift_a, scale_a)
@@ -441,7 +444,12 @@ def block_forward(x, w, mod, *, heads: int, head_dim: int, ffn: int, valid_len: 
     q, k, v = qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:3 * H]
     qn = rnd(qk_norm_rope(q, posv, heads, head_dim, w['q_gain'], eps, rot_dim, theta, pairing))
     kn = rnd(qk_norm_rope(k, posv, heads, head_dim, w['k_gain'], eps, rot_dim, theta, pairing))
-    if groups is None:
+    sel = None
+    if sparse is not None:
+        P, tau = sparse
+        sel, _ = sparse_select(sparse_block_scores(qn, kn, V, P, heads, head_dim), tau)
+        o = sparse_attention(qn, kn, v, V, P, heads, head_dim, sel, scale=scale)
+    elif groups is None:
         o = attention(qn, kn, v, heads, head_dim, scale)
     else:
         gl = []
@@ -469,8 +477,11 @@ def block_forward(x, w, mod, *, heads: int, head_dim: int, ffn: int, valid_len: 
         full[:V] = t
         return full
 
-    return {k_: pad(t_) for k_, t_ in dict(h=h, qkv=qkv, q=qn, k=kn, v=v, o=o, a=a,
-                                            x1=x1, h2=h2, u=u, g=g, f=f, y=y).items()}
+    out = {k_: pad(t_) for k_, t_ in dict(h=h, qkv=qkv, q=qn, k=kn, v=v, o=o, a=a,
+                                           x1=x1, h2=h2, u=u, g=g, f=f, y=y).items()}
+    if sel is not None:
+        out['sparse_sel'] = sel
+    return out
 
 
 def block_forward_rows(x, w, mod, rows, *, heads: int, head_dim: int, ffn: int, valid_len: int,

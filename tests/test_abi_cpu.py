@@ -318,3 +318,33 @@ def test_sparse_validators_and_workspace_sizes():
     assert att(*args(P=V, b=None, c=None)) == h3.H3_OK              # dense fallback needs no lists
     assert lib.h3_check_sparse_attention(q, 3 * H, k, 3 * H, v, 3 * H, o, H, 0, 0, 0, heads, 128, 0.0, None, None,
                                          None, 0) == h3.H3_OK
+
+
+def test_block_sparse_validator_and_layout():
+    """h3_block_forward_sparse: the dense block's checks, the prefix rules, and
+    a workspace that begins with the dense layout and then holds the lists,
+    counts and pooled means."""
+    lib = h3.LIB
+    d = TINY
+    L, V, P = 512, 500, 128
+    dense = h3.workspace_bytes(d, L)
+    need = h3.block_sparse_workspace_bytes(d, L, V, P)
+    nq, nk = h3.sparse_geometry(V, P)
+    assert (nq, nk) == (2, 6)
+    b_off, c_off = h3.block_sparse_workspace_layout(d, L, V, P)
+    assert b_off >= dense and b_off % 256 == 0 and c_off >= b_off + d.heads * nq * nk * 2 and c_off % 256 == 0
+    sel = lib.h3_sparse_select_workspace_bytes(V, P, d.heads)
+    assert need >= c_off + d.heads * nq * 4 + sel
+    w = h3.BlockWeights(*[addr(10 + i) for i in range(10)])
+    x, y, mod, ws = addr(1), addr(2), addr(3), addr(4)
+    chk = lambda **kw: lib.h3_check_block_forward_sparse(C.byref(d), C.byref(w), x, kw.get("y", y), mod, 1, None,
+                                                          None, L, V, kw.get("P", P), kw.get("tau", 1.0),
+                                                          kw.get("ws", ws), kw.get("n", need))
+    assert chk() == h3.H3_OK
+    assert chk(n=need - 1) == h3.H3_ERR_WORKSPACE
+    assert chk(P=0) == h3.H3_ERR_SHAPE
+    assert chk(P=V + 1) == h3.H3_ERR_SHAPE
+    assert chk(tau=float("inf")) == h3.H3_ERR_SHAPE
+    assert chk(y=ws + need - 1024) == h3.H3_ERR_ALIAS            # output inside the selection area
+    assert chk(P=V) == h3.H3_OK                                  # no target rows: dense block
+    assert h3.block_sparse_workspace_bytes(d, L, V, V) >= dense

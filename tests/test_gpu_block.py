@@ -298,3 +298,82 @@ def test_block_reference_kv_cache_full_width_sampled_rows():
     ref = O.block_forward_rows(O.bf16_to_f64(xb), b_full.wo, b_full.mod.astype(np.float64), keep[sel],
                                heads=s.heads, head_dim=128, ffn=s.ffn, valid_len=s.valid_len, rot_dim=s.rot_dim)
     _check_rows(b_cur, y_cur, ref, sel, "cached")
+
+
+def _run_sparse(b: Block, xb, P, tau):
+    s = b.s
+    need = h3.block_sparse_workspace_bytes(b.dims, s.L_buf, s.valid_len, P)
+    b.ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    b.off, b.lds = h3.workspace_layout(b.dims, s.L_buf)
+    x = dev_bf16(xb)
+    y = poison(x.shape)
+    h3.block_forward_sparse(b.dims, b.weights, x, y, b.md, 1, s.valid_len, P, tau, b.ws)
+    torch.cuda.synchronize()
+    return y
+
+
+def test_block_sparse_all_blocks_equals_dense_block():
+    """Sol-Attn block (Sol-H3 report, §3.4) with a tau so low that every KV
+    block is selected: every intermediate matches the oracle's dense block."""
+    print("block sparse, all blocks selected", flush=True)
+    s = I.TINY
+    b = Block(s, tag="bsp0")
+    xb = I.activations(s, tag="xsp0")
+    y = _run_sparse(b, xb, 128, -1e30)
+    _check_all(b, b.oracle(xb), y, s.valid_len)
+    nq, nk = h3.sparse_geometry(s.valid_len, 128)
+    b_off, c_off = h3.block_sparse_workspace_layout(b.dims, s.L_buf, s.valid_len, 128)
+    counts = b.ws[c_off:c_off + s.heads * nq * 4].view(torch.int32).cpu().numpy()
+    assert np.all(counts == nk)
+
+
+@pytest.mark.parametrize("tau", [1.0, 1.5])
+def test_block_sparse_matches_oracle(tau):
+    """The block with Sol-Attn attention at the pages' tau values, prefix 128
+    rows (64 text + 64 audio). The oracle runs with BF16 storage points, so
+    both sides select from the same BF16 q~ and k~ up to rounding-order
+    flips of single elements (one BF16 ulp, 2^-8 relative, each). A pooled
+    score then moves by at most 2 * 2^-8 of A_b = max_j sum_c |qbar_c kbar_c|
+    / sqrt(128), so the GPU's selection may differ from the oracle's only for
+    blocks within 8e-3 * A_b of the threshold. Rows of query blocks whose
+    selection differs in some head are left out of the output comparison;
+    every other valid row (prefix rows included) must match."""
+    print(f"block sparse tau={tau}", flush=True)
+    s = I.TINY
+    P, V, H = 128, s.valid_len, s.hidden
+    b = Block(s, tag="bsp1")
+    xb = I.activations(s, tag="xsp1")
+    y = _run_sparse(b, xb, P, tau)
+    ref = b.oracle(xb, sparse=(P, tau), bf16_points=True)
+    sel = ref["sparse_sel"]
+    nq, nk = h3.sparse_geometry(V, P)
+    b_off, c_off = h3.block_sparse_workspace_layout(b.dims, s.L_buf, V, P)
+    blocks = b.ws[b_off:b_off + s.heads * nq * nk * 2].view(torch.int16).cpu().numpy().view(np.uint16)
+    blocks = blocks.reshape(s.heads, nq, nk)
+    counts = b.ws[c_off:c_off + s.heads * nq * 4].view(torch.int32).cpu().numpy().reshape(s.heads, nq)
+    qs, ks = ref["q"][:V], ref["k"][:V]
+    scores = O.sparse_block_scores(qs, ks, V, P, s.heads, 128)
+    _, thr = O.sparse_select(scores, tau)
+    T = V - P
+    ok_rows = np.ones(V, dtype=bool)
+    for h in range(s.heads):
+        sl = slice(h * 128, (h + 1) * 128)
+        for bq in range(nq):
+            got = np.zeros(nk, dtype=bool)
+            got[blocks[h, bq, :counts[h, bq]].astype(np.int64)] = True
+            diff = np.nonzero(got != sel[h, bq])[0]
+            if len(diff):
+                a, e = P + 256 * bq, min(P + 256 * (bq + 1), V)
+                qbar = np.abs(qs[a:e, sl].mean(0))
+                A = max(np.sum(qbar * np.abs(ks[P + 64 * j:min(P + 64 * j + 64, V), sl].mean(0)))
+                        for j in range(nk)) / np.sqrt(128)
+                gap = np.abs(scores[h, bq, diff] - thr[h, bq])
+                assert np.all(gap <= 8e-3 * A), (h, bq, diff, gap, A)
+                ok_rows[a:e] = False
+    print(f"  selection differs on {np.count_nonzero(~ok_rows[P:])} of {T} target rows", flush=True)
+    assert ok_rows[:P].all()
+    qkv = f64(b.inter(h3.H3_WS_QKV))
+    for name, got, r in (("o", f64(b.inter(h3.H3_WS_O)), ref["o"]), ("y", f64(y), ref["y"]),
+                         ("x1", f64(b.inter(h3.H3_WS_X1)), ref["x1"]), ("q~", qkv[:, :H], ref["q"])):
+        assert_parity(got[:V][ok_rows], r[:V][ok_rows], name)
+    assert_zero_rows(y, V, "y")

@@ -645,3 +645,21 @@ def test_sparse_attention_nothing_selected_is_prefix_attention():
     got = O.sparse_attention(q, k, v, V, P, heads, d, np.zeros((1, 1, 2), dtype=bool))
     np.testing.assert_allclose(got[P:], O.attention(q[P:], k[:P], v[:P], heads, d), rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(got[:P], O.attention(q[:P], k, v, heads, d), rtol=1e-12, atol=1e-13)
+
+
+def test_block_sparse_all_selected_equals_dense_block_and_selection_is_exposed():
+    """The block with Sol-Attn attention: a tau so low that every block is
+    selected gives the dense block; a real tau gives a selection mask of the
+    documented geometry whose prefix rows still match the dense block's
+    attention output (prefix queries are dense)."""
+    s, w, x, mod, kw = _tiny_inputs()
+    L, V, P = 512, 500, 128
+    dense = O.block_forward(x[:L], w, mod, valid_len=V, **kw)
+    allsel = O.block_forward(x[:L], w, mod, valid_len=V, sparse=(P, -1e30), **kw)
+    assert allsel["sparse_sel"].all() and allsel["sparse_sel"].shape == (kw["heads"], 2, 6)
+    for name in ("o", "y"):
+        np.testing.assert_allclose(allsel[name], dense[name], rtol=1e-10, atol=1e-11)
+    sp = O.block_forward(x[:L], w, mod, valid_len=V, sparse=(P, 1.0), **kw)
+    assert 0 < sp["sparse_sel"].sum() < sp["sparse_sel"].size
+    np.testing.assert_allclose(sp["o"][:P], dense["o"][:P], rtol=1e-10, atol=1e-11)
+    assert np.abs(sp["o"][P:V] - dense["o"][P:V]).max() > 1e-3          # the target rows did change

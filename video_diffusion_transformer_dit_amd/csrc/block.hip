@@ -13,24 +13,25 @@
 //   8 GEMM+residual  y   = x1 + gate_f (g W_down^T (+ b))                group (1)
 //   9 KV export      (refresh forwards only) copy k~ and v rows out
 // Every kernel works on the valid rows only; padding rows of every output and
-// intermediate are written as zero.
+// intermediate are written as zero. The block-sparse variant replaces step 4
+// by the Sol-Attn block selection and the list-mode attention (Sol-H3 report,
+// §3.4 "Sparse Attention").
 #include "h3_runtime.h"
 
-using namespace h3;
+namespace h3 {
+namespace {
 
-extern "C" int h3_block_forward(const h3_dims *dims, const h3_block_weights *w, const uint16_t *x, uint16_t *y,
-                                const float *mod, int32_t n_mod_groups, const int32_t *mod_idx,
-                                const int32_t *pos, int64_t L_buf, int64_t valid_len, const h3_qgroup *groups,
-                                int32_t n_groups, const h3_kv_export *kv_export, void *workspace,
-                                size_t ws_bytes, void *stream) {
-    int s = h3_check_block_forward(dims, w, x, y, mod, n_mod_groups, mod_idx, pos, L_buf, valid_len, groups,
-                                   n_groups, kv_export, workspace, ws_bytes);
-    if (s != H3_OK || L_buf == 0) return s;
-    if ((s = device_check()) != H3_OK) return s;
-    const hipStream_t st = (hipStream_t)stream;
+struct SparseStep {
+    int64_t prefix_len;
+    float tau;
+    const BlockSparseLayout *l;
+};
 
-    WsLayout l;
-    ws_layout(dims, L_buf, groups, n_groups, &l);
+// Steps 1-9 on the caller's stream; arguments already validated.
+void block_steps(const h3_dims *dims, const h3_block_weights *w, const uint16_t *x, uint16_t *y, const float *mod,
+                 int32_t n_mod_groups, const int32_t *mod_idx, const int32_t *pos, int64_t L_buf,
+                 int64_t valid_len, const h3_qgroup *groups, int32_t n_groups, const h3_kv_export *kv_export,
+                 const WsLayout &l, void *workspace, const SparseStep *sp, hipStream_t st) {
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     uint16_t *h = reinterpret_cast<uint16_t *>(ws + l.off[H3_WS_H]);
     uint16_t *qkv = reinterpret_cast<uint16_t *>(ws + l.off[H3_WS_QKV]);
@@ -56,8 +57,17 @@ extern "C" int h3_block_forward(const h3_dims *dims, const h3_block_weights *w, 
     launch_qk_norm_rope(qkv, qkv + H, 3 * H, w->q_gain, w->k_gain, pos, L_buf, V, dims->heads, dims->rot_dim,
                         dims->rope_pairing, dims->rope_theta, dims->eps, st);
     // 4 o
-    launch_attention(qkv, 3 * H, qkv + H, 3 * H, qkv + 2 * H, 3 * H, o, H, L_buf, V, dims->heads, 0.0f, groups,
-                     n_groups, vt, st);
+    if (sp == nullptr) {
+        launch_attention(qkv, 3 * H, qkv + H, 3 * H, qkv + 2 * H, 3 * H, o, H, L_buf, V, dims->heads, 0.0f, groups,
+                         n_groups, vt, st);
+    } else {
+        uint16_t *blocks = reinterpret_cast<uint16_t *>(ws + sp->l->blocks_off);
+        int32_t *counts = reinterpret_cast<int32_t *>(ws + sp->l->counts_off);
+        launch_sparse_select(qkv, 3 * H, qkv + H, 3 * H, V, sp->prefix_len, dims->heads, sp->tau, blocks, counts,
+                             ws + sp->l->select_off, st);
+        launch_sparse_attention(qkv, 3 * H, qkv + H, 3 * H, qkv + 2 * H, 3 * H, o, H, L_buf, V, sp->prefix_len,
+                                dims->heads, 0.0f, blocks, counts, vt, st);
+    }
     // 5 x1 = x + gate_a * (o W_o^T)
     launch_linear(o, H, w->w_o, H, w->b_o, x1, H, V, H, H, H3_EPI_RESIDUAL, x, H, gate_a, ldm, n_mod_groups, mod_idx,
                   st);
@@ -79,5 +89,41 @@ extern "C" int h3_block_forward(const h3_dims *dims, const h3_block_weights *w, 
         launch_copy_rows(qkv + e.src_begin * 3 * H + H, 3 * H, e.k, e.ld, e.len, H, st);
         launch_copy_rows(qkv + e.src_begin * 3 * H + 2 * H, 3 * H, e.v, e.ld, e.len, H, st);
     }
+}
+
+}  // namespace
+}  // namespace h3
+
+using namespace h3;
+
+extern "C" int h3_block_forward(const h3_dims *dims, const h3_block_weights *w, const uint16_t *x, uint16_t *y,
+                                const float *mod, int32_t n_mod_groups, const int32_t *mod_idx,
+                                const int32_t *pos, int64_t L_buf, int64_t valid_len, const h3_qgroup *groups,
+                                int32_t n_groups, const h3_kv_export *kv_export, void *workspace,
+                                size_t ws_bytes, void *stream) {
+    int s = h3_check_block_forward(dims, w, x, y, mod, n_mod_groups, mod_idx, pos, L_buf, valid_len, groups,
+                                   n_groups, kv_export, workspace, ws_bytes);
+    if (s != H3_OK || L_buf == 0) return s;
+    if ((s = device_check()) != H3_OK) return s;
+    WsLayout l;
+    ws_layout(dims, L_buf, groups, n_groups, &l);
+    block_steps(dims, w, x, y, mod, n_mod_groups, mod_idx, pos, L_buf, valid_len, groups, n_groups, kv_export, l,
+                workspace, nullptr, (hipStream_t)stream);
+    return launch_status();
+}
+
+extern "C" int h3_block_forward_sparse(const h3_dims *dims, const h3_block_weights *w, const uint16_t *x,
+                                       uint16_t *y, const float *mod, int32_t n_mod_groups, const int32_t *mod_idx,
+                                       const int32_t *pos, int64_t L_buf, int64_t valid_len, int64_t prefix_len,
+                                       float tau, void *workspace, size_t ws_bytes, void *stream) {
+    int s = h3_check_block_forward_sparse(dims, w, x, y, mod, n_mod_groups, mod_idx, pos, L_buf, valid_len,
+                                          prefix_len, tau, workspace, ws_bytes);
+    if (s != H3_OK || L_buf == 0) return s;
+    if ((s = device_check()) != H3_OK) return s;
+    BlockSparseLayout bl;
+    block_sparse_layout(dims, L_buf, valid_len, prefix_len, &bl);
+    const SparseStep sp{prefix_len, tau, &bl};
+    block_steps(dims, w, x, y, mod, n_mod_groups, mod_idx, pos, L_buf, valid_len, nullptr, 0, nullptr, bl.base,
+                workspace, &sp, (hipStream_t)stream);
     return launch_status();
 }

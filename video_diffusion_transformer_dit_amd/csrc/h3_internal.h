@@ -57,6 +57,17 @@ struct WsLayout {
 };
 bool ws_layout(const h3_dims *d, int64_t L_buf, const h3_qgroup *groups, int n_groups, WsLayout *out);
 
+// Workspace of the block with block-sparse attention: the dense block's
+// layout (the V^T slot grown to fit the two key segments if needed), then the
+// selection lists, their counts and the selection's own workspace.
+struct BlockSparseLayout {
+    WsLayout base;
+    int64_t blocks_off, counts_off, select_off;
+    size_t total;
+};
+bool block_sparse_layout(const h3_dims *d, int64_t L_buf, int64_t valid_len, int64_t prefix_len,
+                         BlockSparseLayout *out);
+
 // Validation of dims shared by several checks.
 int check_dims(const h3_dims *d);
 

@@ -165,6 +165,35 @@ bool ws_layout(const h3_dims *d, int64_t L_buf, const h3_qgroup *groups, int n_g
     return true;
 }
 
+bool block_sparse_layout(const h3_dims *d, int64_t L_buf, int64_t valid_len, int64_t prefix_len,
+                         BlockSparseLayout *out) {
+    if (!ws_layout(d, L_buf, nullptr, 0, &out->base)) return false;
+    if (valid_len < 0 || valid_len > L_buf || prefix_len < 0 || prefix_len > valid_len) return false;
+    auto align = [](int64_t b) { return (b + (int64_t)kWsAlign - 1) / (int64_t)kWsAlign * (int64_t)kWsAlign; };
+    WsLayout &l = out->base;
+    int64_t vt = l.ld[H3_WS_VT];
+    if (valid_len > prefix_len) {
+        h3_qgroup g;
+        sparse_vt_group(valid_len, prefix_len, &g);
+        VtPlan p;
+        vt_plan(&g, 1, valid_len, d->heads, &p);
+        vt = std::max<int64_t>(vt, (int64_t)p.bytes);
+    }
+    l.ld[H3_WS_VT] = vt;
+    int64_t off = l.off[H3_WS_VT] + align(vt);
+    l.total = (size_t)off;
+    SparseGeom g;
+    sparse_geometry(valid_len, prefix_len, d->heads, &g);
+    out->blocks_off = off;
+    off += align((int64_t)d->heads * g.n_qb * g.n_kb * 2);
+    out->counts_off = off;
+    off += align((int64_t)d->heads * g.n_qb * 4);
+    out->select_off = off;
+    off += align(g.T > 0 ? (int64_t)g.ws_bytes : 0);
+    out->total = (size_t)off;
+    return true;
+}
+
 }  // namespace h3
 
 using namespace h3;
@@ -201,6 +230,23 @@ size_t h3_attention_workspace_bytes(int64_t valid_len, int32_t heads, const h3_q
     VtPlan p;
     vt_plan(groups, n_groups, valid_len, heads, &p);
     return p.bytes;
+}
+
+size_t h3_block_sparse_workspace_bytes(const h3_dims *dims, int64_t L_buf, int64_t valid_len,
+                                       int64_t prefix_len) {
+    BlockSparseLayout l;
+    if (!block_sparse_layout(dims, L_buf, valid_len, prefix_len, &l)) return 0;
+    return l.total;
+}
+
+int h3_block_sparse_workspace_layout(const h3_dims *dims, int64_t L_buf, int64_t valid_len, int64_t prefix_len,
+                                     int64_t *blocks_off, int64_t *counts_off) {
+    if (blocks_off == nullptr || counts_off == nullptr) return H3_ERR_NULL;
+    BlockSparseLayout l;
+    if (!block_sparse_layout(dims, L_buf, valid_len, prefix_len, &l)) return H3_ERR_SHAPE;
+    *blocks_off = l.blocks_off;
+    *counts_off = l.counts_off;
+    return H3_OK;
 }
 
 size_t h3_sparse_attention_workspace_bytes(int64_t valid_len, int64_t prefix_len, int32_t heads) {
@@ -621,6 +667,45 @@ int h3_check_sparse_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k
     const Mat mc = bytes_of(counts, (int64_t)heads * sg.n_qb * 4);
     const Mat mw = bytes_of(workspace, (int64_t)h3_sparse_attention_workspace_bytes(valid_len, prefix_len, heads));
     if (overlap(mo, mb) || overlap(mo, mc) || overlap(mw, mb) || overlap(mw, mc)) return H3_ERR_ALIAS;
+    return H3_OK;
+}
+
+int h3_check_block_forward_sparse(const h3_dims *dims, const h3_block_weights *w, const uint16_t *x, uint16_t *y,
+                                  const float *mod, int32_t n_mod_groups, const int32_t *mod_idx,
+                                  const int32_t *pos, int64_t L_buf, int64_t valid_len, int64_t prefix_len,
+                                  float tau, const void *workspace, size_t ws_bytes) {
+    H3_TRY(h3_check_block_forward(dims, w, x, y, mod, n_mod_groups, mod_idx, pos, L_buf, valid_len, nullptr, 0,
+                                  nullptr, workspace, ws_bytes));
+    if (prefix_len < 0 || prefix_len > valid_len) return H3_ERR_SHAPE;
+    const int64_t T = valid_len - prefix_len;
+    if (T > 0 && prefix_len < 1) return H3_ERR_SHAPE;
+    if (T > (int64_t)H3_SPARSE_MAX_KBLOCKS * H3_SPARSE_K_BLOCK) return H3_ERR_UNSUPPORTED;
+    if (!std::isfinite(tau)) return H3_ERR_SHAPE;
+    if (L_buf == 0) return H3_OK;
+    BlockSparseLayout l;
+    if (!block_sparse_layout(dims, L_buf, valid_len, prefix_len, &l)) return H3_ERR_SHAPE;
+    if (ws_bytes < l.total) return H3_ERR_WORKSPACE;
+    // The dense block's check covered the workspace's first dense-layout bytes;
+    // the rest must not overlap the inputs, the output or the weights either.
+    WsLayout dl;
+    ws_layout(dims, L_buf, nullptr, 0, &dl);
+    const int64_t H = dims->hidden, F = dims->ffn, d = dims->head_dim;
+    const Mat extra = bytes_of(static_cast<const uint8_t *>(workspace) + dl.total, (int64_t)(l.total - dl.total));
+    const Mat others[] = {mat(x, L_buf, H, H),
+                          mat(y, L_buf, H, H),
+                          mat(mod, 1, (int64_t)n_mod_groups * 6 * H, (int64_t)n_mod_groups * 6 * H, 4),
+                          mat(w->w_qkv, 3 * H, H, H),
+                          mat(w->b_qkv, w->b_qkv ? 1 : 0, 3 * H, 3 * H),
+                          mat(w->q_gain, 1, d, d),
+                          mat(w->k_gain, 1, d, d),
+                          mat(w->w_o, H, H, H),
+                          mat(w->b_o, w->b_o ? 1 : 0, H, H),
+                          mat(w->w_up, 2 * F, H, H),
+                          mat(w->b_up, w->b_up ? 1 : 0, 2 * F, 2 * F),
+                          mat(w->w_down, H, F, F),
+                          mat(w->b_down, w->b_down ? 1 : 0, H, H)};
+    for (const Mat &m : others)
+        if (overlap(extra, m)) return H3_ERR_ALIAS;
     return H3_OK;
 }
 

@@ -97,6 +97,12 @@ def _load():
         "h3_block_workspace_bytes": [C.POINTER(Dims), I64, C.POINTER(QGroup), I32],
         "h3_block_workspace_layout": [C.POINTER(Dims), I64, C.POINTER(QGroup), I32, C.POINTER(I64),
                                       C.POINTER(I64)],
+        "h3_block_forward_sparse": [C.POINTER(Dims), C.POINTER(BlockWeights), P, P, P, I32, P, P, I64, I64, I64,
+                                    F32, P, SZ, P],
+        "h3_check_block_forward_sparse": [C.POINTER(Dims), C.POINTER(BlockWeights), P, P, P, I32, P, P, I64, I64,
+                                          I64, F32, P, SZ],
+        "h3_block_sparse_workspace_bytes": [C.POINTER(Dims), I64, I64, I64],
+        "h3_block_sparse_workspace_layout": [C.POINTER(Dims), I64, I64, I64, C.POINTER(I64), C.POINTER(I64)],
         "h3_sparse_select": [P, I64, P, I64, I64, I64, I32, I32, F32, P, P, P, SZ, P],
         "h3_check_sparse_select": [P, I64, P, I64, I64, I64, I32, I32, F32, P, P, P, SZ],
         "h3_sparse_select_workspace_bytes": [I64, I64, I32],
@@ -113,6 +119,7 @@ def _load():
     lib.h3_block_workspace_bytes.restype = C.c_size_t
     lib.h3_attention_workspace_bytes.restype = C.c_size_t
     lib.h3_sparse_select_workspace_bytes.restype = C.c_size_t
+    lib.h3_block_sparse_workspace_bytes.restype = C.c_size_t
     lib.h3_sparse_attention_workspace_bytes.restype = C.c_size_t
     lib.h3_status_string.restype = C.c_char_p
     return lib
@@ -126,7 +133,9 @@ EXPORTS = ["h3_block_forward", "h3_attention", "h3_fused_modulate_norm", "h3_qk_
            "h3_fused_modulate_norm_lora", "h3_swiglu_lora", "h3_check_qk_norm_rope_lora",
            "h3_check_fused_modulate_norm_lora", "h3_check_swiglu_lora", "h3_sparse_select", "h3_sparse_attention",
            "h3_sparse_select_workspace_bytes", "h3_sparse_attention_workspace_bytes", "h3_check_sparse_select",
-           "h3_check_sparse_attention"]
+           "h3_check_sparse_attention", "h3_block_forward_sparse", "h3_block_sparse_workspace_bytes",
+           "h3_check_block_forward_sparse",
+           "h3_block_sparse_workspace_layout"]
 
 
 def status_string(s: int) -> str:
@@ -217,6 +226,26 @@ def block_forward(dims: Dims, weights: BlockWeights, x, y, mod, n_mod_groups, va
                              C.byref(exp) if exp is not None else None, _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream(stream))
     _ok(s, "h3_block_forward")
+
+
+def block_sparse_workspace_bytes(dims: Dims, L_buf: int, valid_len: int, prefix_len: int) -> int:
+    return int(LIB.h3_block_sparse_workspace_bytes(C.byref(dims), L_buf, valid_len, prefix_len))
+
+
+def block_sparse_workspace_layout(dims: Dims, L_buf: int, valid_len: int, prefix_len: int):
+    """(blocks_off, counts_off): where the block's selection lies in its workspace."""
+    b, c = C.c_int64(), C.c_int64()
+    _ok(LIB.h3_block_sparse_workspace_layout(C.byref(dims), L_buf, valid_len, prefix_len, C.byref(b), C.byref(c)),
+        "h3_block_sparse_workspace_layout")
+    return b.value, c.value
+
+
+def block_forward_sparse(dims: Dims, weights: BlockWeights, x, y, mod, n_mod_groups, valid_len, prefix_len, tau,
+                         workspace, mod_idx=None, pos=None, stream=None):
+    s = LIB.h3_block_forward_sparse(C.byref(dims), C.byref(weights), _ptr(x), _ptr(y), _ptr(mod), n_mod_groups,
+                                    _ptr(mod_idx), _ptr(pos), x.shape[0], valid_len, prefix_len, float(tau),
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _ok(s, "h3_block_forward_sparse")
 
 
 def attention(q, k, v, o, valid_len, heads, softmax_scale=0.0, groups=None, workspace=None, stream=None):
