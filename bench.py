@@ -202,7 +202,7 @@ def reference_kv_cache(torch, h3, dev, dims, weights, mod, gen, L, V, H, n_ref=1
             "cached_step_ms": round(cached_ms, 3), "speedup": round(full_ms / cached_ms, 3)}
 
 
-def block_sparse(torch, h3, dev, q, k, v, o, V, heads, dense_ms, iters, prefix=1536):
+def block_sparse(torch, h3, dev, q, k, v, o, V, heads, dense_ms, iters, block, prefix=1536):
     """Sol-Attn block-sparse attention on the block's own q~, k~, v (after
     QK-norm and RoPE) at the pages' refinement tau schedule. The prefix is
     the workload's 512 text + 1,024 audio rows. Reports the selection and
@@ -236,6 +236,15 @@ def block_sparse(torch, h3, dev, q, k, v, o, V, heads, dense_ms, iters, prefix=1
                                 "attended_fraction": round(pairs / (heads * V * V), 4),
                                 "attention_tflops_on_attended": round(tf, 1),
                                 "speedup_vs_dense": round(dense_ms / (sel_ms + att_ms), 2)}
+    # the whole block with Sol-Attn attention (tau = 1.0), against the dense block
+    dims, weights, x, y, mod, dense_block_ms = block
+    L = x.shape[0]
+    wsb = torch.empty(h3.block_sparse_workspace_bytes(dims, L, V, prefix), dtype=torch.uint8, device=dev)
+    blk_ms = time_calls(torch, lambda: h3.block_forward_sparse(dims, weights, x, y, mod, 1, V, prefix, 1.0, wsb),
+                        iters, 1)
+    del wsb
+    out["block_tau_1.0"] = {"block_ms": round(blk_ms, 3), "dense_block_ms": round(dense_block_ms, 3),
+                            "speedup": round(dense_block_ms / blk_ms, 3)}
     return out
 
 
@@ -372,16 +381,17 @@ def main(argv=None) -> int:
         "attention_tflops": round(attn_tf, 1),
         "gemm_tflops": round(gemm_f / (gemm_ms * 1e-3) / 1e12, 1),
         "kernels": kernels,
-        "roofline": {"kernel": "attention_fwd_kernel", "bound": "mfma", "achieved": round(attn_tf, 1),
+        "roofline": {"kernel": "attention_fwd_kernel<false> (dense)", "bound": "mfma", "achieved": round(attn_tf, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": counter_traffic("attention_fwd_kernel", "attention.hip"),
+                     "traffic": counter_traffic("void attention_fwd_kernel<false>", "attention.hip"),
                      "traffic_unit": "bytes per launch (FETCH_SIZE x2 + WRITE_SIZE x1, copy-calibrated)",
                      "work_per_launch": "4 * 58758^2 * 5376 = 7.424e13 flop (QK^T and PV over valid rows)"},
     }
     if not a.no_next:
         out["next"] = {"lora_consumer_fusion": lora_consumers(torch, h3, dev, gen, L, V, H, heads, F, kit)}
         out["next"]["block_sparse_attention"] = block_sparse(torch, h3, dev, qkv[:, :H], qkv[:, H:2 * H],
-                                                             qkv[:, 2 * H:], o, V, heads, k_ms["attention"], kit)
+                                                             qkv[:, 2 * H:], o, V, heads, k_ms["attention"], kit,
+                                                             (dims, weights, x, y, mod, ms))
         out["next"]["reference_kv_cache"] = reference_kv_cache(torch, h3, dev, dims, weights, mod, gen, L, V, H)
     if a.calibration_copy:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)   # 1 GiB
