@@ -24,6 +24,8 @@ Sources (cited by page title and section):
     so the head width is 128.
   - §3.4 "Safety rails": sequence packing [text | conditioning video | audio |
     target video].
+  - §3.3 "Compute Quantization" ("MXFP8 GEMM computation"): E4M3 values with one E8M0 scale per 32
+    values along the reduction dimension, written by the producers.
   - §3.4 "Sparse Attention": Sol-Attn block selection by the threshold
     mu + tau * sigma per query block; prefix queries dense; prefix keys always
     attended.
@@ -375,6 +377,98 @@ def sparse_attention(q, k, v, valid_len: int, prefix_len: int, heads: int, head_
             idx = np.concatenate(keys).astype(np.int64)
             out[P + a:P + b, sl] = attention_head(q[P + a:P + b, sl], k[idx, sl], v[idx, sl], scale)
     return out
+
+
+# ----------------------------------------------------------------------------
+# MXFP8 (Sol-H3 §3.3 "Compute Quantization", "MXFP8 GEMM computation"): E4M3 values with one E8M0
+# scale per 32 consecutive values along the reduction dimension.
+#
+# Readings (the pages name the formats, not the rule that picks a scale):
+#   M1 E4M3 is the 8-bit float with 1 sign, 4 exponent (bias 7) and 3
+#      mantissa bits, no infinities, one NaN pattern per sign (S.1111.111):
+#      largest finite 448, smallest normal 2^-6, subnormal step 2^-9.
+#      E8M0 is an unsigned biased exponent: code c stands for 2^(c - 127).
+#   M2 the scale of a group of 32 is the microscaling rule: with amax the
+#      group's largest magnitude, the shared exponent is floor(log2 amax)
+#      minus 8 (the exponent of E4M3's largest binade), clamped to
+#      [-127, 127]; a group of zeros takes the smallest scale, 2^-127.
+#   M3 an element is v / 2^shared rounded to the nearest E4M3 value, ties to
+#      the even code, with magnitudes above 448 saturating to 448.
+#   M4 a GEMM on MXFP8 operands multiplies the scaled values exactly and
+#      accumulates; the oracle dequantizes and multiplies in FP64.
+# ----------------------------------------------------------------------------
+MX_BLOCK = 32
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """E4M3 bit patterns (uint8) -> float64 values (reading M1; NaN for the NaN patterns)."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(F64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(F64) - 7.0))
+    mag = np.where((e == 15) & ((c & 7) == 7), np.nan, mag)
+    return sign * mag
+
+
+def e4m3_round(v) -> np.ndarray:
+    """Nearest E4M3 value of each real v, ties to even, saturating at +-448
+    (reading M3). Returns float64 values (exactly representable in E4M3)."""
+    v = np.asarray(v, dtype=F64)
+    a = np.abs(v)
+    with np.errstate(divide='ignore'):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)                       # below 2^-6 the step is fixed (subnormals)
+    step = np.exp2(e - 3.0)
+    q = np.round(a / step) * step                 # np.round: half to even
+    q = np.minimum(q, E4M3_MAX)
+    return np.sign(v) * q
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """E4M3 bit patterns of values that are exactly representable (the output
+    of e4m3_round); -0.0 and 0.0 both encode to 0x00 (sign of zero dropped)."""
+    v = np.asarray(v, dtype=F64)
+    table = e4m3_decode(np.arange(128))
+    a = np.abs(v)
+    idx = np.searchsorted(table[:127], a)
+    assert np.all(table[np.minimum(idx, 126)] == a), "value not representable in E4M3"
+    return (idx + np.where((v < 0) & (a > 0), 128, 0)).astype(np.uint8)
+
+
+def mx_scale_exponent(amax) -> np.ndarray:
+    """Shared exponent of a group from its largest magnitude (reading M2)."""
+    amax = np.asarray(amax, dtype=F64)
+    with np.errstate(divide='ignore'):
+        e = np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8.0
+    e = np.where(amax > 0, e, -127.0)
+    return np.clip(e, -127.0, 127.0)
+
+
+def mx_quantize(x, block: int = MX_BLOCK):
+    """MXFP8 quantization of x [rows, K] along K in groups of 32 (K a multiple
+    of 32). Returns (elements [rows, K] as float64 E4M3 values, shared
+    exponents [rows, K/32] as float64 integers). The dequantized matrix is
+    elements * 2^exponent, group by group."""
+    x = np.asarray(x, dtype=F64)
+    r, K = x.shape
+    assert K % block == 0
+    g = x.reshape(r, K // block, block)
+    e = mx_scale_exponent(np.max(np.abs(g), axis=2))
+    q = e4m3_round(g / np.exp2(e)[:, :, None])
+    return q.reshape(r, K), e
+
+
+def mx_dequantize(q, e, block: int = MX_BLOCK) -> np.ndarray:
+    q = np.asarray(q, dtype=F64)
+    r, K = q.shape
+    return (q.reshape(r, K // block, block) * np.exp2(np.asarray(e, dtype=F64))[:, :, None]).reshape(r, K)
+
+
+def linear_mxfp8(a_q, a_e, w_q, w_e, b=None) -> np.ndarray:
+    """y = dequant(a) dequant(w)^T (+ b) in FP64 (reading M4)."""
+    return linear(mx_dequantize(a_q, a_e), mx_dequantize(w_q, w_e), b)
 
 
 # ----------------------------------------------------------------------------

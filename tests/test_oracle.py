@@ -663,3 +663,111 @@ def test_block_sparse_all_selected_equals_dense_block_and_selection_is_exposed()
     assert 0 < sp["sparse_sel"].sum() < sp["sparse_sel"].size
     np.testing.assert_allclose(sp["o"][:P], dense["o"][:P], rtol=1e-10, atol=1e-11)
     assert np.abs(sp["o"][P:V] - dense["o"][P:V]).max() > 1e-3          # the target rows did change
+
+
+# --------------------------------------------------------------------------
+# MXFP8 (Sol-H3 report, §3.3 "Compute Quantization", "MXFP8 GEMM computation")
+# --------------------------------------------------------------------------
+def _finite_e4m3():
+    """All finite E4M3 values with their codes, from torch's float8_e4m3fn."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    vals = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return np.arange(256), vals
+
+
+def test_e4m3_decode_matches_torch_float8():
+    codes, vals = _finite_e4m3()
+    got = O.e4m3_decode(codes)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(vals))
+    ok = ~np.isnan(vals)
+    np.testing.assert_array_equal(got[ok], vals[ok])
+    assert got[0x7E] == 448.0 and got[0x08] == 2.0 ** -6 and got[0x01] == 2.0 ** -9 and got[0x38] == 1.0
+
+
+def test_e4m3_round_matches_torch_in_range_and_saturates():
+    rng = np.random.default_rng(7)
+    v = np.concatenate([rng.standard_normal(20000) * 30, rng.standard_normal(5000) * 1e-3,
+                        rng.uniform(-464, 464, 5000)]).astype(np.float32)
+    # ties: midpoints between neighbouring E4M3 values (subnormal and normal)
+    _, vals = _finite_e4m3()
+    pos = np.unique(vals[(vals >= 0) & ~np.isnan(vals)])
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    v = np.concatenate([v, mids, -mids, [0.0, -0.0, 448.0, 464.0, -464.0]]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.e4m3_round(v.astype(np.float64)), ref)
+    # saturation above 448 (torch's cast gives NaN there)
+    big = np.array([464.5, 480.0, 1e6, -500.0])
+    np.testing.assert_array_equal(O.e4m3_round(big), [448.0, 448.0, 448.0, -448.0])
+    q = O.e4m3_round(v.astype(np.float64))
+    np.testing.assert_array_equal(O.e4m3_decode(O.e4m3_encode(q)), q)
+
+
+def test_mx_scale_exponent_closed_forms():
+    a = np.array([1.0, 448.0, 255.99, 256.0, 511.9, 512.0, 2.0 ** -130, 0.0, 3.0, 2.0 ** 140])
+    np.testing.assert_array_equal(O.mx_scale_exponent(a), [-8, 0, -1, 0, 0, 1, -127, -127, -7, 127])
+
+
+def _mx_quantize_brute(x):
+    """Group by group with math.frexp for the exponent and an exhaustive
+    nearest-value search (ties to the even code) for the elements."""
+    codes, vals = _finite_e4m3()
+    fin = [(c, v) for c, v in zip(codes, vals) if not math.isnan(v)]
+    r, K = x.shape
+    q = np.zeros_like(x)
+    e = np.zeros((r, K // 32))
+    for i in range(r):
+        for g in range(K // 32):
+            grp = x[i, 32 * g:32 * g + 32]
+            amax = max(abs(t) for t in grp)
+            if amax == 0:
+                ex = -127
+            else:
+                ex = math.frexp(amax)[1] - 1 - 8          # frexp: amax = m 2^k, m in [0.5, 1)
+                ex = min(max(ex, -127), 127)
+            e[i, g] = ex
+            for j, t in enumerate(grp):
+                y = t / 2.0 ** ex
+                if abs(y) >= 448:
+                    q[i, 32 * g + j] = math.copysign(448.0, y)
+                    continue
+                best = min(fin, key=lambda cv: (abs(cv[1] - y), cv[0] & 1))
+                q[i, 32 * g + j] = best[1]
+    return q, e
+
+
+def test_mx_quantize_matches_brute_force_and_error_bound():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((3, 128)) * np.exp2(rng.integers(-12, 12, size=(3, 1)))
+    x[1, 32:64] = 0.0                                          # a zero group
+    x[2, 64] = 1000.0                                          # a group whose amax sets a large scale
+    x[0, :32] = O.round_to_bf16(x[0, :32])
+    q, e = O.mx_quantize(x)
+    qb, eb = _mx_quantize_brute(x)
+    np.testing.assert_array_equal(e, eb)
+    np.testing.assert_array_equal(q, qb)
+    d = O.mx_dequantize(q, e)
+    # below 448 after scaling, |error| <= half a step: 2^-4 |x| (normal range)
+    # or 2^(e - 10) (subnormal range); from 448 up (the top of the group's
+    # binade, below 512) the element saturates to 448 * 2^e
+    E = np.repeat(e, 32, axis=1)
+    scaled = np.abs(x) / np.exp2(E)
+    bound = np.where(scaled >= 2 ** -6, 2.0 ** -4 * np.abs(x), np.exp2(E - 10))
+    sat = scaled >= 448
+    assert np.all(np.abs(d - x)[~sat] <= bound[~sat])
+    np.testing.assert_array_equal(d[sat], np.sign(x[sat]) * 448 * np.exp2(E[sat]))
+    assert np.all(scaled < 512) and np.all(np.max(scaled.reshape(3, 4, 32), axis=2)[e > -127] >= 256)
+
+
+def test_linear_mxfp8_is_the_product_of_dequantized_operands():
+    rng = np.random.default_rng(12)
+    a = rng.standard_normal((4, 64))
+    w = rng.standard_normal((3, 64)) * 0.02
+    aq, ae = O.mx_quantize(a)
+    wq, we = O.mx_quantize(w)
+    da, dw = _mx_quantize_brute(a), _mx_quantize_brute(w)
+    A = da[0] * np.exp2(np.repeat(da[1], 32, axis=1))
+    W = dw[0] * np.exp2(np.repeat(dw[1], 32, axis=1))
+    ref = np.array([[sum(A[i, k] * W[j, k] for k in range(64)) for j in range(3)] for i in range(4)])
+    np.testing.assert_allclose(O.linear_mxfp8(aq, ae, wq, we), ref, rtol=1e-12, atol=1e-14)
+    # operands already in MXFP8 (E4M3 values times powers of two) quantize to themselves
+    np.testing.assert_array_equal(O.mx_dequantize(*O.mx_quantize(A)), A)
