@@ -415,6 +415,48 @@ size_t h3_block_sparse_workspace_bytes(const h3_dims *dims, int64_t L_buf, int64
 int h3_block_sparse_workspace_layout(const h3_dims *dims, int64_t L_buf, int64_t valid_len, int64_t prefix_len,
                                      int64_t *blocks_off, int64_t *counts_off);
 
+/* ---------------------------------------------------------------------------
+ * MXFP8 GEMMs ([Sol-H3] §3.3 "Compute Quantization", "MXFP8 GEMM
+ * computation"): E4M3 values with one E8M0 scale per 32 consecutive values
+ * along the reduction dimension K. The pages name the formats; the scale of
+ * a group is chosen by the microscaling rule (this library's reading): with
+ * amax the group's largest magnitude, the shared exponent is
+ * e = floor(log2 amax) - 8 (clamped to >= -127; an all-zero group takes
+ * -127), the scale code is e + 127, and each element is x * 2^-e rounded to
+ * the nearest E4M3 value (ties to even) with magnitudes above 448 saturating
+ * to 448. E4M3 is the 1-4-3 format with bias 7, no infinities, largest
+ * finite value 448.
+ *
+ * MXFP8 matrix [rows, K] (K a multiple of 128): codes, uint8 [rows][ld]
+ * (ld >= K, a multiple of 16, 16-byte aligned base), plus scales, uint8
+ * [K / 128][scale_rows][4] (4-byte aligned): byte (g / 4, r, g % 4) is the
+ * scale code of row r's k group g (k in [32 g, 32 g + 32)). scale_rows is the
+ * row count of the scale array (>= the rows in use). The pages' scale
+ * buffers use cuBLASLt's SWIZZLE_32_4_4 layout; this layout instead puts one
+ * K stage's scales for a tile of rows in one contiguous run, which is what
+ * the gfx950 kernel loads.
+ *
+ * h3_mxfp8_quantize: x [rows_buf, K] BF16 at ld_x -> codes q at ld_q and
+ * scales (scale_rows = rows_buf). Rows [rows_valid, rows_buf) get zero codes
+ * and zero scale codes; x's padding rows are not read. K % 128 != 0 is
+ * H3_ERR_UNSUPPORTED. Outputs must not overlap x or each other.
+ * ------------------------------------------------------------------------- */
+int h3_mxfp8_quantize(const uint16_t *x, int64_t ld_x, int64_t rows_buf, int64_t rows_valid, int64_t K,
+                      uint8_t *q, int64_t ld_q, uint8_t *scales, void *stream);
+
+/* h3_linear_mxfp8: c = dequant(a) dequant(w)^T (+ bias) with h3_linear's
+ * epilogues (STORE, RESIDUAL, SWIGLU; same arguments, BF16 output, rows
+ * [M_valid, M_buf) of c written 0). a: MXFP8 [M_buf, K] with scale_rows
+ * a_scale_rows (>= M_valid); w: MXFP8 [N, K] with scale_rows N. Products are
+ * exact and accumulated in FP32 on gfx950's scaled MFMA. K must be a
+ * multiple of 128 (else H3_ERR_UNSUPPORTED); N a multiple of 8 (16 for
+ * SwiGLU). c must not overlap any input but resid (which may equal it). */
+int h3_linear_mxfp8(const uint8_t *a, int64_t lda, const uint8_t *a_scales, int64_t a_scale_rows,
+                    const uint8_t *w, int64_t ldw, const uint8_t *w_scales, const uint16_t *bias,
+                    uint16_t *c, int64_t ldc, int64_t M_buf, int64_t M_valid, int64_t N, int64_t K,
+                    int32_t epilogue, const uint16_t *resid, int64_t ld_r, const float *gate,
+                    int64_t ld_gate_group, int32_t n_mod_groups, const int32_t *mod_idx, void *stream);
+
 /* Host-only validators: the same checks each entry point runs before it
  * launches anything, callable without a GPU. They return an h3_status. */
 int h3_check_block_forward(const h3_dims *dims, const h3_block_weights *w,
@@ -478,6 +520,14 @@ int h3_check_sparse_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k
                               int64_t L_buf, int64_t valid_len, int64_t prefix_len, int32_t heads,
                               int32_t head_dim, float softmax_scale, const uint16_t *blocks,
                               const int32_t *counts, const void *workspace, size_t ws_bytes);
+
+int h3_check_mxfp8_quantize(const uint16_t *x, int64_t ld_x, int64_t rows_buf, int64_t rows_valid, int64_t K,
+                            const uint8_t *q, int64_t ld_q, const uint8_t *scales);
+int h3_check_linear_mxfp8(const uint8_t *a, int64_t lda, const uint8_t *a_scales, int64_t a_scale_rows,
+                          const uint8_t *w, int64_t ldw, const uint8_t *w_scales, const uint16_t *bias,
+                          const uint16_t *c, int64_t ldc, int64_t M_buf, int64_t M_valid, int64_t N, int64_t K,
+                          int32_t epilogue, const uint16_t *resid, int64_t ld_r, const float *gate,
+                          int64_t ld_gate_group, int32_t n_mod_groups);
 
 /* Human-readable name of a status code (static string). */
 const char *h3_status_string(int status);

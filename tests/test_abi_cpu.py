@@ -348,3 +348,30 @@ def test_block_sparse_validator_and_layout():
     assert chk(y=ws + need - 1024) == h3.H3_ERR_ALIAS            # output inside the selection area
     assert chk(P=V) == h3.H3_OK                                  # no target rows: dense block
     assert h3.block_sparse_workspace_bytes(d, L, V, V) >= dense
+
+
+def test_mxfp8_validators():
+    """MXFP8 quantize and GEMM checks (Sol-H3 report, §3.3): K a multiple of
+    128, 16-byte code rows, 4-byte scale arrays, no overlapping outputs."""
+    lib = h3.LIB
+    M_buf, M, K, N = 300, 291, 256, 512
+    x, q, s = addr(1), addr(2), addr(3)
+    chk_q = lambda **kw: lib.h3_check_mxfp8_quantize(kw.get("x", x), K, M_buf, kw.get("M", M), kw.get("K", K),
+                                                     kw.get("q", q), kw.get("ldq", K), kw.get("s", s))
+    assert chk_q() == h3.H3_OK
+    assert chk_q(K=96) == h3.H3_ERR_UNSUPPORTED
+    assert chk_q(ldq=K + 8) == h3.H3_ERR_ALIGN
+    assert chk_q(s=s + 2) == h3.H3_ERR_ALIGN
+    assert chk_q(q=None) == h3.H3_ERR_NULL
+    assert chk_q(s=x + 64) == h3.H3_ERR_ALIAS
+    assert chk_q(M=0, x=None) == h3.H3_OK                          # only padding rows: x is not read
+    a, as_, w, ws, c = addr(4), addr(5), addr(6), addr(7), addr(8)
+    chk = lambda **kw: lib.h3_check_linear_mxfp8(a, K, kw.get("as_", as_), kw.get("srows", M_buf), w, K, ws, None,
+                                                 kw.get("c", c), N, M_buf, M, N, kw.get("K", K), kw.get("epi", 0),
+                                                 None, 0, None, 0, 1)
+    assert chk() == h3.H3_OK
+    assert chk(K=192) == h3.H3_ERR_UNSUPPORTED
+    assert chk(srows=M - 1) == h3.H3_ERR_SHAPE
+    assert chk(as_=as_ + 1) == h3.H3_ERR_ALIGN
+    assert chk(c=ws) == h3.H3_ERR_ALIAS
+    assert chk(epi=1) == h3.H3_ERR_NULL                           # residual without resid / gate

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libh3block.so")
 
-SOURCES = ["validate.cpp", "runtime.hip", "elementwise.hip", "gemm.hip", "attention.hip", "sparse.hip", "block.hip"]
+SOURCES = ["validate.cpp", "runtime.hip", "elementwise.hip", "gemm.hip", "attention.hip", "sparse.hip", "gemm_mxfp8.hip", "mx_quant.hip", "block.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -26,6 +26,7 @@
 // walks a contiguous range of a grouped tile order, keeping the operand
 // K-slices its 32 CUs share in that XCD's L2.
 #include "h3_device.h"
+#include "h3_gemm_epilogue.h"
 #include "h3_runtime.h"
 
 namespace h3 {
@@ -59,29 +60,13 @@ struct GemmArgs {
 // see 8 distinct chunk positions, so the 16 reads hit distinct banks.
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kChunksPerRow + (chunk ^ ((row >> 1) & 7)); }
 
-// Map a linear workgroup id to (tile_m, tile_n): XCD-contiguous ranges of a
-// grouped (group_m tile-rows at a time, column by column) order.
-__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int group_m, int &tm, int &tn) {
-    const int T = tiles_m * tiles_n;
-    const int q = T / 8, rr = T % 8;
-    const int xcd = bid % 8, local = bid / 8;
-    const int lin = xcd < rr ? xcd * (q + 1) + local : rr * (q + 1) + (xcd - rr) * q + local;
-    const int per_group = group_m * tiles_n;
-    const int group = lin / per_group;
-    const int first_m = group * group_m;
-    const int gsz = min(tiles_m - first_m, group_m);
-    const int in_group = lin - group * per_group;
-    tm = first_m + in_group % gsz;
-    tn = in_group / gsz;
-}
-
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
     // LDS: two stage slots of [W tile, A tile], 32 KB each (128 KB).
     __shared__ uint4 smem[2 * 2 * kTileChunks];
 
     int tm, tn;
-    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    gemm_tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
@@ -234,72 +219,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
     // can end.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // Epilogue: in each 32 x 32 sub-tile the lane holds row m = lane & 31 and,
-    // for register group q (0..3), the 4 columns 8 q + 4 (lane >> 5) + (0..3).
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t m = (int64_t)tm * BM + wm * 128 + j * 32 + r32;
-        if (m >= p.M) continue;
-        uint16_t *crow = p.c + m * p.ldc;
-        if (EPI == H3_EPI_SWIGLU) {
-            // W sub-tile i holds the gate block (rows 0-15, q = 0, 1) and the up
-            // block (rows 16-31, q = 2, 3) of output columns (wn*4 + i)*16 + 0..15.
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const int64_t col = (int64_t)tn * (BN / 2) + (wn * 4 + i) * 16 + 8 * q + 4 * g2;
-                    if (col >= p.ffn) continue;
-                    float gb[4] = {0.f, 0.f, 0.f, 0.f}, ub[4] = {0.f, 0.f, 0.f, 0.f};
-                    if (p.bias) {
-                        const uint2 bg = *reinterpret_cast<const uint2 *>(p.bias + col);
-                        const uint2 bu = *reinterpret_cast<const uint2 *>(p.bias + p.ffn + col);
-                        gb[0] = bf16_lo(bg.x); gb[1] = bf16_hi(bg.x); gb[2] = bf16_lo(bg.y); gb[3] = bf16_hi(bg.y);
-                        ub[0] = bf16_lo(bu.x); ub[1] = bf16_hi(bu.x); ub[2] = bf16_lo(bu.y); ub[3] = bf16_hi(bu.y);
-                    }
-                    float o[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float zg = acc[i][j][4 * q + e] + gb[e];
-                        o[e] = zg / (1.0f + __expf(-zg)) * (acc[i][j][4 * (q + 2) + e] + ub[e]);
-                    }
-                    *reinterpret_cast<uint2 *>(crow + col) =
-                        make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-                }
-            }
-        } else {
-            const float *grow = nullptr;
-            const uint16_t *rrow = nullptr;
-            if (EPI == H3_EPI_RESIDUAL) {
-                int g = 0;
-                if (p.mod_idx) g = min(max(p.mod_idx[m], 0), p.n_groups - 1);
-                grow = p.gate + (int64_t)g * p.ld_gate;
-                rrow = p.resid + m * p.ld_r;
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int64_t n = (int64_t)tn * BN + wn * 128 + i * 32 + 8 * q + 4 * g2;
-                    if (n >= p.N) continue;
-                    float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                    if (p.bias) {
-                        const uint2 b = *reinterpret_cast<const uint2 *>(p.bias + n);
-                        v[0] += bf16_lo(b.x); v[1] += bf16_hi(b.x); v[2] += bf16_lo(b.y); v[3] += bf16_hi(b.y);
-                    }
-                    if (EPI == H3_EPI_RESIDUAL) {
-                        const float4 gv = *reinterpret_cast<const float4 *>(grow + n);
-                        const uint2 rv = *reinterpret_cast<const uint2 *>(rrow + n);
-                        v[0] = bf16_lo(rv.x) + gv.x * v[0];
-                        v[1] = bf16_hi(rv.x) + gv.y * v[1];
-                        v[2] = bf16_lo(rv.y) + gv.z * v[2];
-                        v[3] = bf16_hi(rv.y) + gv.w * v[3];
-                    }
-                    *reinterpret_cast<uint2 *>(crow + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                }
-            }
-        }
-    }
+    gemm_epilogue<EPI>(p, acc, tm, tn, wm, wn, r32, g2);
 }
 
 }  // namespace

@@ -48,6 +48,36 @@ __device__ __forceinline__ void dma_slab(i32x4_t rsrc, uint32_t lds, int voff, i
         : "memory", "m0");
 }
 
+// Direct global -> LDS load of 4 bytes per lane: lane i's dword (descriptor
+// rsrc, byte offset voff + soff) lands at LDS address lds + 4 i. Same
+// ordering contract as dma_slab.
+__device__ __forceinline__ void dma_dword(i32x4_t rsrc, uint32_t lds, int voff, int soff) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %1, %2, %3 offen lds"
+        :
+        : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+        : "memory", "m0");
+}
+
+// GEMM tile order: map a linear workgroup id to (tile_m, tile_n) so that each
+// XCD (workgroups are dealt round-robin over 8 XCDs) walks a contiguous range
+// of a grouped order (group_m tile rows at a time, column by column).
+__device__ __forceinline__ void gemm_tile_coords(int bid, int tiles_m, int tiles_n, int group_m, int &tm, int &tn) {
+    const int T = tiles_m * tiles_n;
+    const int q = T / 8, rr = T % 8;
+    const int xcd = bid % 8, local = bid / 8;
+    const int lin = xcd < rr ? xcd * (q + 1) + local : rr * (q + 1) + (xcd - rr) * q + local;
+    const int per_group = group_m * tiles_n;
+    const int group = lin / per_group;
+    const int first_m = group * group_m;
+    const int gsz = min(tiles_m - first_m, group_m);
+    const int in_group = lin - group * per_group;
+    tm = first_m + in_group % gsz;
+    tn = in_group / gsz;
+}
+
 // BF16 bit pattern -> float (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

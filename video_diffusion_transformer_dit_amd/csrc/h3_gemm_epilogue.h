@@ -1,0 +1,90 @@
+// Epilogue shared by the block's GEMM kernels (BF16 and MXFP8 operands):
+// the FP32 accumulators of one 256 x 256 output tile, held by 4 wavefronts
+// of 128 x 128 as 4 x 4 MFMA sub-tiles of 32 x 32 (weight tile = MFMA A
+// operand, activation tile = B operand), become BF16 outputs.
+//   H3_EPI_STORE     c = acc + bias
+//   H3_EPI_RESIDUAL  c = resid + gate[i] * (acc + bias)   (Sol-H3 report, §3.5
+//                    "Kernel Fusion", group (1): residual with indexed gating)
+//   H3_EPI_SWIGLU    c = silu(acc_gate + b) * (acc_up + b)   (group (3)); the
+//                    weight tile interleaves 16-row gate and up blocks
+#pragma once
+
+#include "h3_device.h"
+#include "h3block.h"
+
+namespace h3 {
+
+// In each 32 x 32 sub-tile the lane holds row m = lane & 31 and, for register
+// group q (0..3), the 4 columns 8 q + 4 (lane >> 5) + (0..3). Args provides
+// M, N, ffn, c/ldc, bias, resid/ld_r, gate/ld_gate, mod_idx and n_groups.
+template <int EPI, typename Args>
+__device__ __forceinline__ void gemm_epilogue(const Args &p, f32x16_t (&acc)[4][4], int tm, int tn, int wm, int wn,
+                                              int r32, int g2) {
+    constexpr int BM = 256, BN = 256;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t m = (int64_t)tm * BM + wm * 128 + j * 32 + r32;
+        if (m >= p.M) continue;
+        uint16_t *crow = p.c + m * p.ldc;
+        if (EPI == H3_EPI_SWIGLU) {
+            // W sub-tile i holds the gate block (rows 0-15, q = 0, 1) and the up
+            // block (rows 16-31, q = 2, 3) of output columns (wn*4 + i)*16 + 0..15.
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int64_t col = (int64_t)tn * (BN / 2) + (wn * 4 + i) * 16 + 8 * q + 4 * g2;
+                    if (col >= p.ffn) continue;
+                    float gb[4] = {0.f, 0.f, 0.f, 0.f}, ub[4] = {0.f, 0.f, 0.f, 0.f};
+                    if (p.bias) {
+                        const uint2 bg = *reinterpret_cast<const uint2 *>(p.bias + col);
+                        const uint2 bu = *reinterpret_cast<const uint2 *>(p.bias + p.ffn + col);
+                        gb[0] = bf16_lo(bg.x); gb[1] = bf16_hi(bg.x); gb[2] = bf16_lo(bg.y); gb[3] = bf16_hi(bg.y);
+                        ub[0] = bf16_lo(bu.x); ub[1] = bf16_hi(bu.x); ub[2] = bf16_lo(bu.y); ub[3] = bf16_hi(bu.y);
+                    }
+                    float o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float zg = acc[i][j][4 * q + e] + gb[e];
+                        o[e] = zg / (1.0f + __expf(-zg)) * (acc[i][j][4 * (q + 2) + e] + ub[e]);
+                    }
+                    *reinterpret_cast<uint2 *>(crow + col) =
+                        make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+                }
+            }
+        } else {
+            const float *grow = nullptr;
+            const uint16_t *rrow = nullptr;
+            if (EPI == H3_EPI_RESIDUAL) {
+                int g = 0;
+                if (p.mod_idx) g = min(max(p.mod_idx[m], 0), p.n_groups - 1);
+                grow = p.gate + (int64_t)g * p.ld_gate;
+                rrow = p.resid + m * p.ld_r;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t n = (int64_t)tn * BN + wn * 128 + i * 32 + 8 * q + 4 * g2;
+                    if (n >= p.N) continue;
+                    float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    if (p.bias) {
+                        const uint2 b = *reinterpret_cast<const uint2 *>(p.bias + n);
+                        v[0] += bf16_lo(b.x); v[1] += bf16_hi(b.x); v[2] += bf16_lo(b.y); v[3] += bf16_hi(b.y);
+                    }
+                    if (EPI == H3_EPI_RESIDUAL) {
+                        const float4 gv = *reinterpret_cast<const float4 *>(grow + n);
+                        const uint2 rv = *reinterpret_cast<const uint2 *>(rrow + n);
+                        v[0] = bf16_lo(rv.x) + gv.x * v[0];
+                        v[1] = bf16_hi(rv.x) + gv.y * v[1];
+                        v[2] = bf16_lo(rv.y) + gv.z * v[2];
+                        v[3] = bf16_hi(rv.y) + gv.w * v[3];
+                    }
+                    *reinterpret_cast<uint2 *>(crow + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                }
+            }
+        }
+    }
+}
+
+}  // namespace h3

@@ -709,4 +709,56 @@ int h3_check_block_forward_sparse(const h3_dims *dims, const h3_block_weights *w
     return H3_OK;
 }
 
+int h3_check_mxfp8_quantize(const uint16_t *x, int64_t ld_x, int64_t rows_buf, int64_t rows_valid, int64_t K,
+                            const uint8_t *q, int64_t ld_q, const uint8_t *scales) {
+    H3_TRY(check_rows(rows_buf, rows_valid));
+    if (K <= 0) return H3_ERR_SHAPE;
+    if (K % 128 != 0) return H3_ERR_UNSUPPORTED;  // scales are stored per 128-wide slab
+    if (rows_buf == 0) return H3_OK;
+    if (!q || !scales || (rows_valid > 0 && !x)) return H3_ERR_NULL;
+    if (rows_valid > 0) H3_TRY(check_bf16_mat(x, ld_x, K));
+    if (ld_q < K) return H3_ERR_SHAPE;
+    if (!aligned16(q) || (ld_q % 16) != 0 || (reinterpret_cast<uintptr_t>(scales) & 3u)) return H3_ERR_ALIGN;
+    const Mat mx = mat(x, rows_valid, K, ld_x), mq = mat(q, rows_buf, K, ld_q, 1);
+    const Mat ms = bytes_of(scales, rows_buf * (K / 32));
+    if (overlap(mq, mx) || overlap(ms, mx) || overlap(ms, mq)) return H3_ERR_ALIAS;
+    return H3_OK;
+}
+
+int h3_check_linear_mxfp8(const uint8_t *a, int64_t lda, const uint8_t *a_scales, int64_t a_scale_rows,
+                          const uint8_t *w, int64_t ldw, const uint8_t *w_scales, const uint16_t *bias,
+                          const uint16_t *c, int64_t ldc, int64_t M_buf, int64_t M_valid, int64_t N, int64_t K,
+                          int32_t epilogue, const uint16_t *resid, int64_t ld_r, const float *gate,
+                          int64_t ld_gate_group, int32_t n_mod_groups) {
+    H3_TRY(check_rows(M_buf, M_valid));
+    if (N <= 0 || K <= 0) return H3_ERR_SHAPE;
+    if (epilogue < H3_EPI_STORE || epilogue > H3_EPI_SWIGLU) return H3_ERR_UNSUPPORTED;
+    if (N % 8 != 0) return H3_ERR_ALIGN;
+    if (K % 128 != 0) return H3_ERR_UNSUPPORTED;  // the kernel's K stage and the scale slabs
+    if (epilogue == H3_EPI_SWIGLU && (N % 16) != 0) return H3_ERR_ALIGN;
+    if (M_buf == 0) return H3_OK;
+    if (!a || !w || !c || !a_scales || !w_scales) return H3_ERR_NULL;
+    if (a_scale_rows < M_valid) return H3_ERR_SHAPE;
+    if (lda < K || ldw < K) return H3_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(w) || (lda % 16) != 0 || (ldw % 16) != 0) return H3_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(a_scales) & 3u) || (reinterpret_cast<uintptr_t>(w_scales) & 3u))
+        return H3_ERR_ALIGN;
+    if (bias && !aligned16(bias)) return H3_ERR_ALIGN;
+    const int64_t Nc = epilogue == H3_EPI_SWIGLU ? N / 2 : N;
+    H3_TRY(check_bf16_mat(c, ldc, Nc));
+    const Mat ma = mat(a, M_buf, K, lda, 1), mw = mat(w, N, K, ldw, 1), mc = mat(c, M_buf, Nc, ldc);
+    const Mat mas = bytes_of(a_scales, a_scale_rows * (K / 32)), mws = bytes_of(w_scales, N * (K / 32));
+    if (overlap(mc, ma) || overlap(mc, mw) || overlap(mc, mas) || overlap(mc, mws)) return H3_ERR_ALIAS;
+    if (epilogue == H3_EPI_RESIDUAL) {
+        if (!resid || !gate) return H3_ERR_NULL;
+        if (n_mod_groups < 1) return H3_ERR_SHAPE;
+        if (!aligned16(gate)) return H3_ERR_ALIGN;
+        if (n_mod_groups > 1 && (ld_gate_group % 4) != 0) return H3_ERR_ALIGN;
+        H3_TRY(check_bf16_mat(resid, ld_r, N));
+        const Mat mr = mat(resid, M_buf, N, ld_r);
+        if (!same(mr, mc) && overlap(mr, mc)) return H3_ERR_ALIAS;
+    }
+    return H3_OK;
+}
+
 }  // extern "C"

@@ -109,6 +109,12 @@ def _load():
         "h3_sparse_attention": [P, I64, P, I64, P, I64, P, I64, I64, I64, I64, I32, I32, F32, P, P, P, SZ, P],
         "h3_check_sparse_attention": [P, I64, P, I64, P, I64, P, I64, I64, I64, I64, I32, I32, F32, P, P, P, SZ],
         "h3_sparse_attention_workspace_bytes": [I64, I64, I32],
+        "h3_mxfp8_quantize": [P, I64, I64, I64, I64, P, I64, P, P],
+        "h3_check_mxfp8_quantize": [P, I64, I64, I64, I64, P, I64, P],
+        "h3_linear_mxfp8": [P, I64, P, I64, P, I64, P, P, P, I64, I64, I64, I64, I64, I32, P, I64, P, I64, I32, P,
+                            P],
+        "h3_check_linear_mxfp8": [P, I64, P, I64, P, I64, P, P, P, I64, I64, I64, I64, I64, I32, P, I64, P, I64,
+                                  I32],
         "h3_status_string": [C.c_int],
         "h3_abi_version": [],
     }
@@ -135,7 +141,8 @@ EXPORTS = ["h3_block_forward", "h3_attention", "h3_fused_modulate_norm", "h3_qk_
            "h3_sparse_select_workspace_bytes", "h3_sparse_attention_workspace_bytes", "h3_check_sparse_select",
            "h3_check_sparse_attention", "h3_block_forward_sparse", "h3_block_sparse_workspace_bytes",
            "h3_check_block_forward_sparse",
-           "h3_block_sparse_workspace_layout"]
+           "h3_block_sparse_workspace_layout", "h3_mxfp8_quantize", "h3_linear_mxfp8", "h3_check_mxfp8_quantize",
+           "h3_check_linear_mxfp8"]
 
 
 def status_string(s: int) -> str:
@@ -357,3 +364,26 @@ def sparse_attention(q, k, v, o, valid_len, prefix_len, heads, blocks, counts, s
                                 _ptr(blocks), _ptr(counts), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(stream))
     _ok(s, "h3_sparse_attention")
+
+
+def mx_scales_shape(rows: int, K: int):
+    """Shape of an MXFP8 scale array: [K / 128, rows, 4] uint8."""
+    return (K // 128, rows, 4)
+
+
+def mxfp8_quantize(x, valid_len, q, scales, stream=None):
+    """x [rows_buf, K] BF16 -> q [rows_buf, K] uint8 codes, scales [K/128, rows_buf, 4] uint8."""
+    s = LIB.h3_mxfp8_quantize(_ptr(x), x.stride(0), x.shape[0], valid_len, x.shape[1], _ptr(q), q.stride(0),
+                              _ptr(scales), _stream(stream))
+    _ok(s, "h3_mxfp8_quantize")
+
+
+def linear_mxfp8(a, a_scales, w, w_scales, c, M_valid, epilogue=H3_EPI_STORE, bias=None, resid=None, gate=None,
+                 ld_gate_group=0, n_mod_groups=1, mod_idx=None, stream=None):
+    """a [M_buf, K] / w [N, K] uint8 codes with scales [K/128, rows, 4]."""
+    N, K = w.shape
+    s = LIB.h3_linear_mxfp8(_ptr(a), a.stride(0), _ptr(a_scales), a_scales.shape[1], _ptr(w), w.stride(0),
+                            _ptr(w_scales), _ptr(bias), _ptr(c), c.stride(0), a.shape[0], M_valid, N, K, epilogue,
+                            _ptr(resid), _ld(resid), _ptr(gate), ld_gate_group, n_mod_groups, _ptr(mod_idx),
+                            _stream(stream))
+    _ok(s, "h3_linear_mxfp8")
