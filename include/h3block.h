@@ -457,6 +457,66 @@ int h3_linear_mxfp8(const uint8_t *a, int64_t lda, const uint8_t *a_scales, int6
                     int32_t epilogue, const uint16_t *resid, int64_t ld_r, const float *gate,
                     int64_t ld_gate_group, int32_t n_mod_groups, const int32_t *mod_idx, void *stream);
 
+/* h3_fused_modulate_norm_mxfp8: h3_fused_modulate_norm whose output h is
+ * written as MXFP8 straight from its FP32 values (the fused quantizing
+ * producer of [Sol-H3] §3.3): codes hq [L_buf, hidden] at ld_hq and scales
+ * hs with L_buf scale rows; no BF16 h exists. hidden must be a multiple of
+ * 128 (else H3_ERR_UNSUPPORTED). Padding rows get zero codes and scale
+ * codes. The optional residual (branch, gate, x1_out) is as in
+ * h3_fused_modulate_norm. */
+int h3_fused_modulate_norm_mxfp8(const uint16_t *x, int64_t ld_x, const uint16_t *branch, int64_t ld_b,
+                                 const float *shift, const float *scale, const float *gate,
+                                 int64_t ld_mod_group, int32_t n_mod_groups, const int32_t *mod_idx,
+                                 uint16_t *x1_out, int64_t ld_x1, uint8_t *hq, int64_t ld_hq, uint8_t *hs,
+                                 int64_t L_buf, int64_t valid_len, int32_t hidden, float eps,
+                                 int32_t norm_type, void *stream);
+
+/* Weights of one block in MXFP8 (each made by h3_mxfp8_quantize of the BF16
+ * weight with rows_buf = rows_valid = its row count): codes with row stride
+ * equal to K, scales with scale_rows equal to the weight's row count.
+ * Biases and QK-norm gains stay BF16. */
+typedef struct {
+    const uint8_t *w_qkv, *s_qkv;   /* [3H, H] */
+    const uint8_t *w_o, *s_o;       /* [H, H] */
+    const uint8_t *w_up, *s_up;     /* [2F, H], gate | up */
+    const uint8_t *w_down, *s_down; /* [H, F] */
+    const uint16_t *b_qkv, *b_o, *b_up, *b_down;  /* or NULL */
+    const uint16_t *q_gain, *k_gain;
+} h3_block_weights_mxfp8;
+
+/* h3_block_forward_mxfp8 - the block of h3_block_forward with its four
+ * projections as MXFP8 GEMMs ([Sol-H3] §3.3: attention and FFN projections in
+ * MXFP8, fed by fused quantizing producers):
+ *   hq  = MXFP8(modnorm(x))            (fused producer, from FP32 values)
+ *   qkv = bf16(dequant(hq) dequant(W_qkv)^T + b)
+ *   q~, k~ as h3_block_forward; o = attention (BF16)
+ *   oq  = MXFP8(o)                     (h3_mxfp8_quantize of the BF16 o)
+ *   x1  = bf16(x + gate_a * (dequant(oq) dequant(W_o)^T + b))
+ *   h2q = MXFP8(modnorm(x1))           (fused producer)
+ *   gq  = MXFP8(silu(u_gate) * u_up), u = dequant(h2q) dequant(W_up)^T + b
+ *                                      (fused into the up-projection epilogue)
+ *   y   = bf16(x1 + gate_f * (dequant(gq) dequant(W_down)^T + b)); 0 on padding
+ * Dense attention only (no query groups, no K/V export). hidden and ffn must be
+ * multiples of 128. Other arguments as h3_block_forward. The quantization is
+ * approximate: the result differs from the BF16 block by the MXFP8 rounding
+ * of the four GEMMs' operands.
+ * workspace: h3_block_mxfp8_workspace_bytes(dims, L_buf) bytes, 256-byte
+ *          aligned; h3_block_mxfp8_workspace_layout gives the offsets of the
+ *          intermediates it holds after the call. */
+enum { H3_MXWS_HQ = 0, H3_MXWS_HS = 1, H3_MXWS_QKV = 2, H3_MXWS_O = 3, H3_MXWS_OQ = 4, H3_MXWS_OS = 5,
+       H3_MXWS_X1 = 6, H3_MXWS_H2Q = 7, H3_MXWS_H2S = 8, H3_MXWS_GQ = 9, H3_MXWS_GS = 10, H3_MXWS_VT = 11,
+       H3_MXWS_COUNT = 12 };
+int h3_block_forward_mxfp8(const h3_dims *dims, const h3_block_weights_mxfp8 *w,
+                           const uint16_t *x, uint16_t *y,
+                           const float *mod, int32_t n_mod_groups, const int32_t *mod_idx,
+                           const int32_t *pos, int64_t L_buf, int64_t valid_len,
+                           void *workspace, size_t ws_bytes, void *stream);
+size_t h3_block_mxfp8_workspace_bytes(const h3_dims *dims, int64_t L_buf);
+/* Byte offsets of the intermediates (codes [L_buf, cols] with row stride
+ * cols; scales [cols / 128][L_buf][4]; BF16 qkv [L_buf, 3H], o and x1
+ * [L_buf, H] with row strides 3H and H; the V^T staging area last). */
+int h3_block_mxfp8_workspace_layout(const h3_dims *dims, int64_t L_buf, int64_t offsets[H3_MXWS_COUNT]);
+
 /* Host-only validators: the same checks each entry point runs before it
  * launches anything, callable without a GPU. They return an h3_status. */
 int h3_check_block_forward(const h3_dims *dims, const h3_block_weights *w,
@@ -528,6 +588,18 @@ int h3_check_linear_mxfp8(const uint8_t *a, int64_t lda, const uint8_t *a_scales
                           const uint16_t *c, int64_t ldc, int64_t M_buf, int64_t M_valid, int64_t N, int64_t K,
                           int32_t epilogue, const uint16_t *resid, int64_t ld_r, const float *gate,
                           int64_t ld_gate_group, int32_t n_mod_groups);
+
+int h3_check_fused_modulate_norm_mxfp8(const uint16_t *x, int64_t ld_x, const uint16_t *branch, int64_t ld_b,
+                                       const float *shift, const float *scale, const float *gate,
+                                       int64_t ld_mod_group, int32_t n_mod_groups, const uint16_t *x1_out,
+                                       int64_t ld_x1, const uint8_t *hq, int64_t ld_hq, const uint8_t *hs,
+                                       int64_t L_buf, int64_t valid_len, int32_t hidden, float eps,
+                                       int32_t norm_type);
+int h3_check_block_forward_mxfp8(const h3_dims *dims, const h3_block_weights_mxfp8 *w,
+                                 const uint16_t *x, const uint16_t *y,
+                                 const float *mod, int32_t n_mod_groups, const int32_t *mod_idx,
+                                 const int32_t *pos, int64_t L_buf, int64_t valid_len,
+                                 const void *workspace, size_t ws_bytes);
 
 /* Human-readable name of a status code (static string). */
 const char *h3_status_string(int status);

@@ -396,6 +396,10 @@ def sparse_attention(q, k, v, valid_len: int, prefix_len: int, heads: int, head_
 #      the even code, with magnitudes above 448 saturating to 448.
 #   M4 a GEMM on MXFP8 operands multiplies the scaled values exactly and
 #      accumulates; the oracle dequantizes and multiplies in FP64.
+#   M5 in the block, the quantizing producers quantize their exact outputs
+#      (h, h2 from the norm, g from SwiGLU), with no BF16 step in between;
+#      the attention output o is quantized from its BF16 value, since the
+#      attention kernel returns BF16.
 # ----------------------------------------------------------------------------
 MX_BLOCK = 32
 E4M3_MAX = 448.0
@@ -497,7 +501,7 @@ def swiglu(u: np.ndarray, ffn: int) -> np.ndarray:
 def block_forward(x, w, mod, *, heads: int, head_dim: int, ffn: int, valid_len: int,
                   rot_dim: int = 64, theta: float = 10000.0, eps: float = 1e-6,
                   norm_type: int = 0, pairing: int = 0, mod_idx=None, pos=None,
-                  groups=None, scale=None, bf16_points: bool = False, sparse=None):
+                  groups=None, scale=None, bf16_points: bool = False, sparse=None, mxfp8: bool = False):
     """One DiT block forward over a packed sequence of L_buf rows, valid_len valid.
 
     x      [L_buf, H] float64 (decoded BF16 values)
@@ -510,6 +514,11 @@ def block_forward(x, w, mod, *, heads: int, head_dim: int, ffn: int, valid_len: 
     sparse None, or (prefix_len, tau): Sol-Attn block-sparse attention (Sol-H3
            §3.4) in place of dense attention, its blocks selected from this
            block's own q~ and k~; the selection is returned as 'sparse_sel'.
+    mxfp8  the four projections on MXFP8 operands (Sol-H3 §3.3, readings
+           M1-M5): the weights are quantized; h and h2 are quantized from the
+           norm's exact values and g from the SwiGLU's (fused producers), o
+           from its BF16 rounding (attention returns BF16). The dequantized
+           operands are returned as h_q, o_q, h2_q and g_q.
 
     Steps (Sol-H3 §3.5 groups (1)-(3) around the projections):
       h   = modnorm(x; shift_a, scale_a)
@@ -533,8 +542,17 @@ def block_forward(x, w, mod, *, heads: int, head_dim: int, ffn: int, valid_len: 
     else:
         posv = np.asarray(pos[:V], dtype=F64)
 
-    h = rnd(modulate_norm(xv, m[:, SHIFT_A], m[:, SCALE_A], eps, norm_type))
-    qkv = rnd(linear(h, w['w_qkv'], w.get('b_qkv')))
+    if mxfp8:
+        wmx = {k_: mx_dequantize(*mx_quantize(w[k_])) for k_ in ('w_qkv', 'w_o', 'w_up', 'w_down')}
+        mxq = lambda t: mx_dequantize(*mx_quantize(t))
+    h_exact = modulate_norm(xv, m[:, SHIFT_A], m[:, SCALE_A], eps, norm_type)
+    h = rnd(h_exact)
+    extra = {}
+    if mxfp8:
+        extra['h_q'] = mxq(h_exact)
+        qkv = rnd(linear(extra['h_q'], wmx['w_qkv'], w.get('b_qkv')))
+    else:
+        qkv = rnd(linear(h, w['w_qkv'], w.get('b_qkv')))
     q, k, v = qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:3 * H]
     qn = rnd(qk_norm_rope(q, posv, heads, head_dim, w['q_gain'], eps, rot_dim, theta, pairing))
     kn = rnd(qk_norm_rope(k, posv, heads, head_dim, w['k_gain'], eps, rot_dim, theta, pairing))
@@ -558,12 +576,25 @@ def block_forward(x, w, mod, *, heads: int, head_dim: int, ffn: int, valid_len: 
             gl.append((qb, qe, ss))
         o = attention_grouped(qn, gl, heads, head_dim, V, scale)
     o = rnd(o)
-    a = linear(o, w['w_o'], w.get('b_o'))
+    if mxfp8:
+        extra['o_q'] = mxq(round_to_bf16(o))
+        a = linear(extra['o_q'], wmx['w_o'], w.get('b_o'))
+    else:
+        a = linear(o, w['w_o'], w.get('b_o'))
     x1 = rnd(gated_residual(xv, m[:, GATE_A], a))
-    h2 = rnd(modulate_norm(x1, m[:, SHIFT_F], m[:, SCALE_F], eps, norm_type))
-    u = linear(h2, w['w_up'], w.get('b_up'))
-    g = rnd(swiglu(u, ffn))
-    f = linear(g, w['w_down'], w.get('b_down'))
+    h2_exact = modulate_norm(x1, m[:, SHIFT_F], m[:, SCALE_F], eps, norm_type)
+    h2 = rnd(h2_exact)
+    if mxfp8:
+        extra['h2_q'] = mxq(h2_exact)
+        u = linear(extra['h2_q'], wmx['w_up'], w.get('b_up'))
+        g_exact = swiglu(u, ffn)
+        g = rnd(g_exact)
+        extra['g_q'] = mxq(g_exact)
+        f = linear(extra['g_q'], wmx['w_down'], w.get('b_down'))
+    else:
+        u = linear(h2, w['w_up'], w.get('b_up'))
+        g = rnd(swiglu(u, ffn))
+        f = linear(g, w['w_down'], w.get('b_down'))
     y = rnd(gated_residual(x1, m[:, GATE_F], f))
 
     def pad(t):
@@ -572,7 +603,7 @@ def block_forward(x, w, mod, *, heads: int, head_dim: int, ffn: int, valid_len: 
         return full
 
     out = {k_: pad(t_) for k_, t_ in dict(h=h, qkv=qkv, q=qn, k=kn, v=v, o=o, a=a,
-                                           x1=x1, h2=h2, u=u, g=g, f=f, y=y).items()}
+                                           x1=x1, h2=h2, u=u, g=g, f=f, y=y, **extra).items()}
     if sel is not None:
         out['sparse_sel'] = sel
     return out

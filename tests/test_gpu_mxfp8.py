@@ -198,3 +198,166 @@ def test_mxfp8_quantize_full_size_sampled_rows():
     np.testing.assert_array_equal(O.e4m3_decode(q[rt].cpu().numpy()), ref_q)
     np.testing.assert_array_equal(_scales_from_layout(s[:, rt].cpu().numpy()), ref_e)
     assert torch.count_nonzero(q[M:]).item() == 0 and torch.count_nonzero(s[:, M:]).item() == 0
+
+
+def _dequant(codes, scales_layout):
+    return O.mx_dequantize(O.e4m3_decode(codes), _scales_from_layout(scales_layout))
+
+
+def _check_mx_against(got_codes, got_scales, exact, name, max_frac=1e-3):
+    """Quantized GPU values against the oracle's quantization of the exact
+    (FP64) values. The GPU quantizes its FP32 values, so an element may land
+    on the other side of a rounding point, and a group may take the other
+    scale when its amax is at a power of two; both are allowed only within
+    1e-5 (relative) of that point, and only for a small fraction."""
+    ref_q, ref_e = O.mx_quantize(exact)
+    got_e = _scales_from_layout(got_scales)
+    got = _dequant(got_codes, got_scales)
+    ref = O.mx_dequantize(ref_q, ref_e)
+    bad = got != ref
+    rows, K = exact.shape
+    E = np.repeat(ref_e, 32, axis=1)
+    y = np.abs(exact) / np.exp2(E)
+    # distance of y to the nearest E4M3 rounding point (midpoint of two neighbours)
+    vals = np.unique(np.abs(O.e4m3_decode(np.arange(127))))
+    mids = (vals[:-1] + vals[1:]) / 2
+    idx = np.clip(np.searchsorted(mids, y), 1, len(mids) - 1)
+    near_mid = np.minimum(np.abs(y - mids[idx - 1]), np.abs(y - mids[idx])) <= 1e-5 * np.maximum(y, 2.0 ** -9)
+    amax = np.max(np.abs(exact).reshape(rows, K // 32, 32), axis=2)
+    near_pow2 = np.abs(amax / np.exp2(np.round(np.log2(np.maximum(amax, 1e-300)))) - 1) <= 1e-5
+    scale_flip = np.repeat((got_e != ref_e) & near_pow2, 32, axis=1)
+    assert np.all((got_e == ref_e) | near_pow2), f"{name}: a group scale differs away from a power of two"
+    unexplained = bad & ~near_mid & ~scale_flip
+    assert not unexplained.any(), f"{name}: {unexplained.sum()} quantized values differ away from a rounding point"
+    frac = bad.mean()
+    _say(f"  {name}: {bad.sum()} of {bad.size} quantized values at a rounding point differ ({frac:.2e})")
+    assert frac <= max_frac
+    return got
+
+
+@pytest.mark.parametrize("H,L,V,branch", [(256, 300, 291, False), (5376, 70, 67, True), (1024, 64, 64, True)])
+def test_modnorm_mxfp8_producer(H, L, V, branch):
+    """The fused quantizing producer: MXFP8 h from the norm's FP32 values; the
+    optional residual x1 is bit-identical to the plain kernel's."""
+    _say(f"modnorm_mxfp8 H={H} L={L} V={V} branch={branch}")
+    G = 3
+    xb = I.normal_bf16("mnx.x", (L, H))
+    bb = I.normal_bf16("mnx.b", (L, H))
+    mod = I.normal_f32("mnx.mod", (G, 6, H), 0.3)
+    idx = I.rng_for("mnx.idx").integers(0, G, size=L).astype(np.int32)
+    x, md, ix = dev_bf16(xb), dev_f32(mod), dev_i32(idx)
+    hq = torch.full((L, H), 0x7F, dtype=torch.uint8, device="cuda")
+    hs = torch.full(h3.mx_scales_shape(L, H), 0xEE, dtype=torch.uint8, device="cuda")
+    kw = {}
+    if branch:
+        x1 = poison((L, H))
+        kw = dict(branch=dev_bf16(bb), gate=md[:, 2], x1_out=x1)
+    h3.fused_modulate_norm_mxfp8(x, md[:, 0], md[:, 1], hq, hs, V, ld_mod_group=6 * H, n_mod_groups=G, mod_idx=ix,
+                                 **kw)
+    torch.cuda.synchronize()
+    m = O.gather_mod(mod.astype(np.float64), idx, V)
+    xv = O.bf16_to_f64(xb[:V])
+    if branch:
+        x1_ref, h_ref = poison((L, H)), poison((L, H))
+        h3.fused_modulate_norm(x, md[:, 0], md[:, 1], h_ref, V, branch=dev_bf16(bb), gate=md[:, 2], x1_out=x1_ref,
+                               ld_mod_group=6 * H, n_mod_groups=G, mod_idx=ix)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(x1.view(torch.int16).cpu().numpy(), x1_ref.view(torch.int16).cpu().numpy())
+        xv = f64(x1)[:V]
+    exact = O.modulate_norm(xv, m[:, O.SHIFT_A], m[:, O.SCALE_A], 1e-6, 0)
+    got = _check_mx_against(hq.cpu().numpy()[:V], hs.cpu().numpy()[:, :V], exact, "hq")
+    # the quantization error itself: below E4M3's relative step on average; a
+    # group's largest element may saturate (448 of up to 512), so no max bound
+    assert_parity(got, exact, "h (MXFP8 vs exact)", rel_tol=0.05, max_tol=np.inf)
+    assert np.all(hq.cpu().numpy()[V:] == 0) and np.all(hs.cpu().numpy()[:, V:] == 0)
+
+
+class MxBlock:
+    def __init__(self, shape, tag):
+        self.s = shape
+        wb = I.block_weights(shape, tag)
+        self.wo = {k: O.bf16_to_f64(v) for k, v in wb.items()}
+        self.w = {k: dev_bf16(v) for k, v in wb.items()}
+        self.mod = I.mod_table(shape, 1, tag=f"{tag}.mod")
+        self.md = dev_f32(self.mod)
+        self.dims = h3.make_dims(shape.hidden, shape.heads, shape.ffn, rot_dim=shape.rot_dim, rope_theta=shape.theta,
+                                 eps=shape.eps)
+        wq = {}
+        for k in ("w_qkv", "w_o", "w_up", "w_down"):
+            t = self.w[k]
+            q = torch.empty(t.shape, dtype=torch.uint8, device="cuda")
+            sc = torch.empty(h3.mx_scales_shape(t.shape[0], t.shape[1]), dtype=torch.uint8, device="cuda")
+            h3.mxfp8_quantize(t, t.shape[0], q, sc)
+            wq[k] = (q, sc)
+        wq.update({k: self.w[k] for k in ("q_gain", "k_gain")})
+        self.wq = wq
+        self.weights = h3.make_weights_mx(wq)
+
+    def run(self, xb):
+        s = self.s
+        self.ws = torch.empty(h3.block_mxfp8_workspace_bytes(self.dims, s.L_buf), dtype=torch.uint8, device="cuda")
+        self.off = h3.block_mxfp8_workspace_layout(self.dims, s.L_buf)
+        x = dev_bf16(xb)
+        y = poison(x.shape)
+        h3.block_forward_mxfp8(self.dims, self.weights, x, y, self.md, 1, s.valid_len, self.ws)
+        torch.cuda.synchronize()
+        return y
+
+    def buf(self, which, nbytes):
+        return self.ws[self.off[which]:self.off[which] + nbytes]
+
+    def bf16(self, which, cols):
+        L = self.s.L_buf
+        return self.buf(which, L * cols * 2).view(torch.bfloat16).view(L, cols)
+
+    def mx(self, q, sc, cols):
+        L = self.s.L_buf
+        return (self.buf(q, L * cols).view(L, cols).cpu().numpy(),
+                self.buf(sc, L * cols // 32).view(cols // 128, L, 4).cpu().numpy())
+
+
+def test_block_mxfp8_tiny():
+    """The MXFP8 block (Sol-H3 report, §3.3) against the oracle's MXFP8 block
+    with the same quantization points, every intermediate; and its distance
+    to the exact (unquantized) block, which is the approximation itself."""
+    _say("block mxfp8 tiny")
+    s = I.TINY
+    V, H, F = s.valid_len, s.hidden, s.ffn
+    b = MxBlock(s, "mxb0")
+    xb = I.activations(s, tag="xmx0")
+    y = b.run(xb)
+    kw = dict(heads=s.heads, head_dim=s.head_dim, ffn=F, valid_len=V, rot_dim=s.rot_dim, theta=s.theta, eps=s.eps)
+    x64 = O.bf16_to_f64(xb)
+    ref = O.block_forward(x64, b.wo, b.mod.astype(np.float64), mxfp8=True, bf16_points=True, **kw)
+    exact_h = O.modulate_norm(x64[:V], b.mod[0, O.SHIFT_A].astype(np.float64), b.mod[0, O.SCALE_A].astype(np.float64),
+                              s.eps, 0)
+    hqc, hqs = b.mx(h3.H3_MXWS_HQ, h3.H3_MXWS_HS, H)
+    _check_mx_against(hqc[:V], hqs[:, :V], exact_h, "hq")
+    qkv = f64(b.bf16(h3.H3_MXWS_QKV, 3 * H))
+    for name, got, r in (("q~", qkv[:, :H], ref["q"]), ("k~", qkv[:, H:2 * H], ref["k"]),
+                         ("v", qkv[:, 2 * H:], ref["v"]), ("o", f64(b.bf16(h3.H3_MXWS_O, H)), ref["o"]),
+                         ("x1", f64(b.bf16(h3.H3_MXWS_X1, H)), ref["x1"]), ("y", f64(y), ref["y"])):
+        assert_parity(got[:V], r[:V], name)
+    for q, sc, cols, name in ((h3.H3_MXWS_OQ, h3.H3_MXWS_OS, H, "o_q"), (h3.H3_MXWS_H2Q, h3.H3_MXWS_H2S, H, "h2_q"),
+                              (h3.H3_MXWS_GQ, h3.H3_MXWS_GS, F, "g_q")):
+        codes, scales = b.mx(q, sc, cols)
+        got = _dequant(codes[:V], scales[:, :V])
+        # Each side quantizes its own values of this operand (BF16 o, FP32 h2
+        # and g on the GPU; FP64 in the oracle), which differ in their last
+        # bits. Where that moves an element across a rounding point it changes
+        # by one E4M3 step, and where it moves a group's amax across a power of
+        # two the group changes scale: each at most 1/8 of the group's amax,
+        # so every element is within amax / 4 (plus the input difference,
+        # itself far below it); the bulk must still meet the parity bar.
+        r = ref[name][:V]
+        amax = np.repeat(np.max(np.abs(r).reshape(V, cols // 32, 32), axis=2), 32, axis=1)
+        diff = np.abs(got - r)
+        assert np.all(diff <= amax / 4 * (1 + 1e-2)), f"{name}: a value moved by more than a quantization step"
+        _say(f"  {name}: {np.count_nonzero(diff)} of {diff.size} quantized values differ")
+        assert_parity(got, r, name, max_tol=np.inf)
+        assert np.all(codes[V:] == 0) and np.all(scales[:, V:] == 0), f"{name}: padding rows"
+    assert_zero_rows(y, V, "y")
+    exact = O.block_forward(x64, b.wo, b.mod.astype(np.float64), **kw)
+    rel = np.linalg.norm(f64(y)[:V] - exact["y"][:V]) / np.linalg.norm(exact["y"][:V])
+    _say(f"  MXFP8 block vs exact block: y rel_fro={rel:.3e}")
+    assert rel < 0.05

@@ -771,3 +771,24 @@ def test_linear_mxfp8_is_the_product_of_dequantized_operands():
     np.testing.assert_allclose(O.linear_mxfp8(aq, ae, wq, we), ref, rtol=1e-12, atol=1e-14)
     # operands already in MXFP8 (E4M3 values times powers of two) quantize to themselves
     np.testing.assert_array_equal(O.mx_dequantize(*O.mx_quantize(A)), A)
+
+
+def test_block_mxfp8_structure():
+    """The MXFP8 block: its quantized operands are what mx_quantize makes of
+    the producers' values; its output stays within the MXFP8 rounding of the
+    exact block (each operand element within 2^-4 relative before saturation,
+    so the output within a few percent)."""
+    s, w, x, mod, kw = _tiny_inputs()
+    V = s.valid_len
+    ex = O.block_forward(x, w, mod, valid_len=V, **kw)
+    mx = O.block_forward(x, w, mod, valid_len=V, mxfp8=True, **kw)
+    np.testing.assert_array_equal(mx["h_q"][:V], O.mx_dequantize(*O.mx_quantize(
+        O.modulate_norm(x[:V], mod[0, O.SHIFT_A], mod[0, O.SCALE_A], 1e-6, 0))))
+    np.testing.assert_array_equal(mx["o_q"][:V], O.mx_dequantize(*O.mx_quantize(O.round_to_bf16(mx["o"][:V]))))
+    for name in ("h_q", "h2_q", "g_q"):
+        base = {"h_q": ex["h"], "h2_q": mx["h2"], "g_q": mx["g"]}[name][:V]
+        rel = np.linalg.norm(mx[name][:V] - base) / np.linalg.norm(base)
+        assert 1e-3 < rel < 0.05, (name, rel)          # quantized, and within E4M3's relative step
+    rel_y = np.linalg.norm(mx["y"][:V] - ex["y"][:V]) / np.linalg.norm(ex["y"][:V])
+    assert rel_y < 0.05
+    assert np.all(mx["y"][V:] == 0)

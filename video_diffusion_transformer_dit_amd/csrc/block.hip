@@ -16,6 +16,7 @@
 // intermediate are written as zero. The block-sparse variant replaces step 4
 // by the Sol-Attn block selection and the list-mode attention (Sol-H3 report,
 // §3.4 "Sparse Attention").
+#include "h3_gemm_epilogue.h"
 #include "h3_runtime.h"
 
 namespace h3 {
@@ -125,5 +126,67 @@ extern "C" int h3_block_forward_sparse(const h3_dims *dims, const h3_block_weigh
     const SparseStep sp{prefix_len, tau, &bl};
     block_steps(dims, w, x, y, mod, n_mod_groups, mod_idx, pos, L_buf, valid_len, nullptr, 0, nullptr, bl.base,
                 workspace, &sp, (hipStream_t)stream);
+    return launch_status();
+}
+
+// The MXFP8 block: the same steps with the four projections on MXFP8
+// operands (Sol-H3 report, §3.3 "MXFP8 GEMM computation"), fed by the fused
+// quantizing producers (modulate-norm and the SwiGLU epilogue) and, for the
+// output projection, by a quantization of the BF16 attention output.
+extern "C" int h3_block_forward_mxfp8(const h3_dims *dims, const h3_block_weights_mxfp8 *w, const uint16_t *x,
+                                      uint16_t *y, const float *mod, int32_t n_mod_groups, const int32_t *mod_idx,
+                                      const int32_t *pos, int64_t L_buf, int64_t valid_len, void *workspace,
+                                      size_t ws_bytes, void *stream) {
+    int s = h3_check_block_forward_mxfp8(dims, w, x, y, mod, n_mod_groups, mod_idx, pos, L_buf, valid_len, workspace,
+                                         ws_bytes);
+    if (s != H3_OK || L_buf == 0) return s;
+    if ((s = device_check()) != H3_OK) return s;
+    const hipStream_t st = (hipStream_t)stream;
+    MxWsLayout l;
+    mx_ws_layout(dims, L_buf, &l);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    uint8_t *hq = ws + l.off[H3_MXWS_HQ], *hs = ws + l.off[H3_MXWS_HS];
+    uint16_t *qkv = reinterpret_cast<uint16_t *>(ws + l.off[H3_MXWS_QKV]);
+    uint16_t *o = reinterpret_cast<uint16_t *>(ws + l.off[H3_MXWS_O]);
+    uint8_t *oq = ws + l.off[H3_MXWS_OQ], *os = ws + l.off[H3_MXWS_OS];
+    uint16_t *x1 = reinterpret_cast<uint16_t *>(ws + l.off[H3_MXWS_X1]);
+    uint8_t *h2q = ws + l.off[H3_MXWS_H2Q], *h2s = ws + l.off[H3_MXWS_H2S];
+    uint8_t *gq = ws + l.off[H3_MXWS_GQ], *gs = ws + l.off[H3_MXWS_GS];
+    void *vt = ws + l.off[H3_MXWS_VT];
+
+    const int64_t H = dims->hidden, F = dims->ffn, V = valid_len;
+    const int64_t ldm = 6 * H;
+    const float *shift_a = mod, *scale_a = mod + H, *gate_a = mod + 2 * H;
+    const float *shift_f = mod + 3 * H, *scale_f = mod + 4 * H, *gate_f = mod + 5 * H;
+
+    // 1 hq = MXFP8(modnorm(x))
+    launch_modnorm_mx(x, H, nullptr, 0, shift_a, scale_a, nullptr, ldm, n_mod_groups, mod_idx, nullptr, 0, hq, H, hs,
+                      L_buf, V, (int32_t)H, dims->eps, dims->norm_type, st);
+    // 2 qkv
+    launch_linear_mxfp8(hq, H, hs, L_buf, w->w_qkv, H, w->s_qkv, w->b_qkv, qkv, 3 * H, V, 3 * H, H, H3_EPI_STORE,
+                        nullptr, 0, nullptr, 0, 1, nullptr, st);
+    launch_zero_rows(qkv, 3 * H, 3 * H, V, L_buf, st);
+    // 3 q~, k~
+    launch_qk_norm_rope(qkv, qkv + H, 3 * H, w->q_gain, w->k_gain, pos, L_buf, V, dims->heads, dims->rot_dim,
+                        dims->rope_pairing, dims->rope_theta, dims->eps, st);
+    // 4 o, then oq = MXFP8(o)
+    launch_attention(qkv, 3 * H, qkv + H, 3 * H, qkv + 2 * H, 3 * H, o, H, L_buf, V, dims->heads, 0.0f, nullptr, 0,
+                     vt, st);
+    launch_mx_quantize(o, H, L_buf, V, H, oq, H, os, st);
+    // 5 x1 = x + gate_a * (oq W_o^T)
+    launch_linear_mxfp8(oq, H, os, L_buf, w->w_o, H, w->s_o, w->b_o, x1, H, V, H, H, H3_EPI_RESIDUAL, x, H, gate_a,
+                        ldm, n_mod_groups, mod_idx, st);
+    launch_zero_rows(x1, H, H, V, L_buf, st);
+    // 6 h2q = MXFP8(modnorm(x1))
+    launch_modnorm_mx(x1, H, nullptr, 0, shift_f, scale_f, nullptr, ldm, n_mod_groups, mod_idx, nullptr, 0, h2q, H,
+                      h2s, L_buf, V, (int32_t)H, dims->eps, dims->norm_type, st);
+    // 7 gq = MXFP8(silu(gate) * up), in the up-projection's epilogue
+    launch_linear_mxfp8(h2q, H, h2s, L_buf, w->w_up, H, w->s_up, w->b_up, nullptr, 0, V, 2 * F, H, kEpiSwigluMx,
+                        nullptr, 0, nullptr, 0, 1, nullptr, st, gq, F, gs, L_buf);
+    launch_mx_zero_rows(gq, F, F, gs, L_buf, V, L_buf, st);
+    // 8 y = x1 + gate_f * (gq W_down^T)
+    launch_linear_mxfp8(gq, F, gs, L_buf, w->w_down, F, w->s_down, w->b_down, y, H, V, H, F, H3_EPI_RESIDUAL, x1, H,
+                        gate_f, ldm, n_mod_groups, mod_idx, st);
+    launch_zero_rows(y, H, H, V, L_buf, st);
     return launch_status();
 }

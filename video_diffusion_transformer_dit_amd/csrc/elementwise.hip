@@ -35,6 +35,9 @@ struct ModnormArgs {
     uint16_t *h;
     int64_t ld_x, ld_b, ld_x1, ld_h, ld_mod, ld_d;
     int32_t gate_bf16;      // LORA: round the gate product to BF16 before the residual add
+    uint8_t *hq;            // MX: h as E4M3 codes [L_buf, hidden] at ld_hq ...
+    uint8_t *hs;            // ... and E8M0 scales [hidden / 128][L_buf][4]
+    int64_t ld_hq;
     int64_t L_buf, valid;
     int32_t hidden, n_groups;
     float eps;
@@ -64,7 +67,11 @@ __device__ __forceinline__ void load_f8(const float *p, float f[8]) {
     f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
-template <int NCH, int ROWS, bool BRANCH, int NORM, bool LORA = false>
+// MX: instead of BF16 h, write h as MXFP8 straight from its FP32 values (the
+// fused quantizing producer of Sol-H3 report, §3.3 "MXFP8 GEMM computation").
+// A 32-wide group is the 4 consecutive chunks of 4 consecutive lanes; the 4
+// groups of a 128-wide scale slab are the chunks of 16 consecutive lanes.
+template <int NCH, int ROWS, bool BRANCH, int NORM, bool LORA = false, bool MX = false>
 __global__ __launch_bounds__(256) void modnorm_kernel(ModnormArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * ROWS;
@@ -175,7 +182,12 @@ __global__ __launch_bounds__(256) void modnorm_kernel(ModnormArgs a) {
                 if (!inbuf[p]) continue;
                 if (!valid[p]) {
                     const uint4 z = make_uint4(0, 0, 0, 0);
-                    if (!LORA || a.h) *reinterpret_cast<uint4 *>(a.h + r * a.ld_h + 8 * c) = z;
+                    if (MX) {
+                        *reinterpret_cast<uint2 *>(a.hq + r * a.ld_hq + 8 * c) = make_uint2(0, 0);
+                        if ((c & 15) == 0) *reinterpret_cast<uint32_t *>(a.hs + ((int64_t)(c >> 4) * a.L_buf + r) * 4) = 0;
+                    } else if (!LORA || a.h) {
+                        *reinterpret_cast<uint4 *>(a.h + r * a.ld_h + 8 * c) = z;
+                    }
                     if (BRANCH) *reinterpret_cast<uint4 *>(a.x1 + r * a.ld_x1 + 8 * c) = z;
                     continue;
                 }
@@ -189,18 +201,45 @@ __global__ __launch_bounds__(256) void modnorm_kernel(ModnormArgs a) {
                 unpack8(xv[p][i], xf);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) xf[e] = (xf[e] - mean[p]) * inv[p] * (1.f + sc[e]) + sh[e];
-                *reinterpret_cast<uint4 *>(a.h + r * a.ld_h + 8 * c) = pack8(xf);
+                if (MX) {
+                    float amax = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(xf[e]));
+                    amax = fmaxf(amax, __shfl_xor(amax, 1));
+                    amax = fmaxf(amax, __shfl_xor(amax, 2));
+                    const int ex = mx_shared_exponent(amax);
+                    const float is = mx_inv_scale(ex);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) xf[e] *= is;
+                    *reinterpret_cast<uint2 *>(a.hq + r * a.ld_hq + 8 * c) = e4m3x8(xf);
+                    const uint32_t code = (uint32_t)(ex + 127);
+                    const uint32_t c1 = __shfl_down(code, 4), c2 = __shfl_down(code, 8), c3 = __shfl_down(code, 12);
+                    if ((c & 15) == 0)
+                        *reinterpret_cast<uint32_t *>(a.hs + ((int64_t)(c >> 4) * a.L_buf + r) * 4) =
+                            code | (c1 << 8) | (c2 << 16) | (c3 << 24);
+                } else {
+                    *reinterpret_cast<uint4 *>(a.h + r * a.ld_h + 8 * c) = pack8(xf);
+                }
             }
         }
     }
 }
 
 template <int NCH>
-void modnorm_dispatch_nch(const ModnormArgs &a, bool branch, int norm, hipStream_t s, bool lora = false) {
+void modnorm_dispatch_nch(const ModnormArgs &a, bool branch, int norm, hipStream_t s, bool lora = false,
+                          bool mx = false) {
     constexpr int ROWS = 2;
     const int64_t waves = (a.L_buf + ROWS - 1) / ROWS;
     const dim3 grid((unsigned)((waves + 3) / 4));
-    if (lora) {
+    if (mx) {
+        if (branch) {
+            if (norm == 0) modnorm_kernel<NCH, ROWS, true, 0, false, true><<<grid, 256, 0, s>>>(a);
+            else modnorm_kernel<NCH, ROWS, true, 1, false, true><<<grid, 256, 0, s>>>(a);
+        } else {
+            if (norm == 0) modnorm_kernel<NCH, ROWS, false, 0, false, true><<<grid, 256, 0, s>>>(a);
+            else modnorm_kernel<NCH, ROWS, false, 1, false, true><<<grid, 256, 0, s>>>(a);
+        }
+    } else if (lora) {
         if (norm == 0) modnorm_kernel<NCH, ROWS, true, 0, true><<<grid, 256, 0, s>>>(a);
         else modnorm_kernel<NCH, ROWS, true, 1, true><<<grid, 256, 0, s>>>(a);
     } else if (branch) {
@@ -432,6 +471,32 @@ void launch_swiglu(const uint16_t *u, int64_t ld_u, uint16_t *g, int64_t ld_g, i
     swiglu_kernel<false><<<dim3((unsigned)(L_buf * bpr)), 256, 0, stream>>>(u, ld_u, g, ld_g, valid_len, ffn, bpr);
 }
 
+// Quantizing producer: h written as MXFP8 (codes hq at ld_hq, scales hs with
+// L_buf scale rows) instead of BF16.
+void launch_modnorm_mx(const uint16_t *x, int64_t ld_x, const uint16_t *branch, int64_t ld_b, const float *shift,
+                       const float *scale, const float *gate, int64_t ld_mod_group, int32_t n_mod_groups,
+                       const int32_t *mod_idx, uint16_t *x1_out, int64_t ld_x1, uint8_t *hq, int64_t ld_hq,
+                       uint8_t *hs, int64_t L_buf, int64_t valid_len, int32_t hidden, float eps, int32_t norm_type,
+                       hipStream_t stream) {
+    ModnormArgs a;
+    a.x = x; a.branch = branch; a.shift = shift; a.scale = scale; a.gate = gate; a.mod_idx = mod_idx;
+    a.x1 = x1_out; a.h = nullptr; a.hq = hq; a.hs = hs; a.ld_hq = ld_hq;
+    a.delta = nullptr; a.ld_d = 0; a.gate_bf16 = 0;
+    a.ld_x = ld_x; a.ld_b = ld_b; a.ld_x1 = ld_x1; a.ld_h = 0;
+    a.ld_mod = n_mod_groups > 1 ? ld_mod_group : 0;
+    a.L_buf = L_buf; a.valid = valid_len; a.hidden = hidden; a.n_groups = n_mod_groups; a.eps = eps;
+    const int need = (hidden / 8 + 63) / 64;
+    const bool b = branch != nullptr;
+    if (need <= 1) modnorm_dispatch_nch<1>(a, b, norm_type, stream, false, true);
+    else if (need <= 2) modnorm_dispatch_nch<2>(a, b, norm_type, stream, false, true);
+    else if (need <= 4) modnorm_dispatch_nch<4>(a, b, norm_type, stream, false, true);
+    else if (need <= 8) modnorm_dispatch_nch<8>(a, b, norm_type, stream, false, true);
+    else if (need <= 11) modnorm_dispatch_nch<11>(a, b, norm_type, stream, false, true);
+    else if (need <= 16) modnorm_dispatch_nch<16>(a, b, norm_type, stream, false, true);
+    else if (need <= 24) modnorm_dispatch_nch<24>(a, b, norm_type, stream, false, true);
+    else modnorm_dispatch_nch<32>(a, b, norm_type, stream, false, true);
+}
+
 // LoRA consumer variants: the consumer rounds base + delta to BF16 first.
 void launch_modnorm_lora(const uint16_t *x, int64_t ld_x, const uint16_t *branch, int64_t ld_b,
                          const uint16_t *delta, int64_t ld_d, const float *shift, const float *scale,
@@ -576,3 +641,19 @@ int h3_swiglu_lora(const uint16_t *u, int64_t ld_u, const uint16_t *du, int64_t 
 }
 
 }  // extern "C"
+
+extern "C" int h3_fused_modulate_norm_mxfp8(const uint16_t *x, int64_t ld_x, const uint16_t *branch, int64_t ld_b,
+                                            const float *shift, const float *scale, const float *gate,
+                                            int64_t ld_mod_group, int32_t n_mod_groups, const int32_t *mod_idx,
+                                            uint16_t *x1_out, int64_t ld_x1, uint8_t *hq, int64_t ld_hq, uint8_t *hs,
+                                            int64_t L_buf, int64_t valid_len, int32_t hidden, float eps,
+                                            int32_t norm_type, void *stream) {
+    int s = h3_check_fused_modulate_norm_mxfp8(x, ld_x, branch, ld_b, shift, scale, gate, ld_mod_group, n_mod_groups,
+                                               x1_out, ld_x1, hq, ld_hq, hs, L_buf, valid_len, hidden, eps,
+                                               norm_type);
+    if (s != H3_OK || L_buf == 0) return s;
+    if ((s = device_check()) != H3_OK) return s;
+    launch_modnorm_mx(x, ld_x, branch, ld_b, shift, scale, gate, ld_mod_group, n_mod_groups, mod_idx, x1_out, ld_x1,
+                      hq, ld_hq, hs, L_buf, valid_len, hidden, eps, norm_type, (hipStream_t)stream);
+    return launch_status();
+}

@@ -60,6 +60,10 @@ struct MxGemmArgs {
     int32_t tiles_m, tiles_n;
     int32_t group_m;
     int32_t ffn;
+    uint8_t *cq;          // kEpiSwigluMx: MXFP8 output codes ...
+    int64_t ld_cq;
+    uint8_t *cs;          // ... and scales
+    int64_t cs_rows;
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kChunksPerRow + (chunk ^ ((row >> 1) & 7)); }
@@ -83,8 +87,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(MxGemmArgs p) {
     const int KT = (int)(p.K / BK);
     const i32x4_t rs_a = raw_rsrc(p.a + m_first * p.lda, (a_rows - 1) * p.lda + p.K);
     i32x4_t rs_w, rs_w2;
+    constexpr bool kSwiglu = EPI == H3_EPI_SWIGLU || EPI == kEpiSwigluMx;
     int64_t w_first;  // first weight row of the tile (gate block for SwiGLU)
-    if (EPI == H3_EPI_SWIGLU) {
+    if (kSwiglu) {
         w_first = (int64_t)tn * (BN / 2);
         const int64_t w_rows = min<int64_t>(p.ffn - w_first, BN / 2);
         rs_w = raw_rsrc(p.w + w_first * p.ldw, (w_rows - 1) * p.ldw + p.K);
@@ -106,7 +111,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(MxGemmArgs p) {
         const int row = 8 * slab + (lane >> 3);
         const int c = (lane & 7) ^ ((row >> 1) & 7);
         a_voff[i] = (int)(row * p.lda + 16 * c);
-        if (EPI == H3_EPI_SWIGLU) {
+        if (kSwiglu) {
             const int col = 16 * (slab >> 2) + 8 * (slab & 1) + (lane >> 3);
             w_voff[i] = (int)(col * p.ldw + 16 * c);
         } else {
@@ -116,7 +121,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(MxGemmArgs p) {
     const int srow = 64 * wave + lane;  // tile row whose scale dword this lane loads
     const int as_voff = (int)((m_first + srow) * 4);
     int64_t w_srow;
-    if (EPI == H3_EPI_SWIGLU) w_srow = ((srow & 16) ? p.ffn : 0) + w_first + 16 * (srow >> 5) + (srow & 15);
+    if (kSwiglu) w_srow = ((srow & 16) ? p.ffn : 0) + w_first + 16 * (srow >> 5) + (srow & 15);
     else w_srow = w_first + srow;
     const int ws_voff = (int)(w_srow * 4);
     i32x4_t rs_none = rs_a;
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(MxGemmArgs p) {
         if (d < 16) {
             const int i = d >> 1, op = d & 1;
             const int slab = 8 * wave + i;
-            i32x4_t r = op ? rs_a : ((EPI == H3_EPI_SWIGLU && ((slab >> 1) & 1)) ? rs_w2 : rs_w);
+            i32x4_t r = op ? rs_a : ((kSwiglu && ((slab >> 1) & 1)) ? rs_w2 : rs_w);
             if (past) r = rs_none;
             dma_slab(r, slot_base + (uint32_t)((op * kTileChunks + 64 * slab) * 16), op ? a_voff[i] : w_voff[i],
                      kt * BK);
@@ -269,9 +274,11 @@ void launch_linear_mxfp8(const uint8_t *a, int64_t lda, const uint8_t *a_scales,
                          const uint8_t *w, int64_t ldw, const uint8_t *w_scales, const uint16_t *bias, uint16_t *c,
                          int64_t ldc, int64_t M_valid, int64_t N, int64_t K, int32_t epilogue,
                          const uint16_t *resid, int64_t ld_r, const float *gate, int64_t ld_gate_group,
-                         int32_t n_mod_groups, const int32_t *mod_idx, hipStream_t stream) {
+                         int32_t n_mod_groups, const int32_t *mod_idx, hipStream_t stream, uint8_t *cq,
+                         int64_t ld_cq, uint8_t *cs, int64_t cs_rows) {
     if (M_valid <= 0) return;
     MxGemmArgs p;
+    p.cq = cq; p.ld_cq = ld_cq; p.cs = cs; p.cs_rows = cs_rows;
     p.a = a; p.w = w; p.as = a_scales; p.ws = w_scales;
     p.a_srows = a_scale_rows; p.w_srows = N;
     p.bias = bias; p.c = c; p.resid = resid; p.gate = gate; p.mod_idx = mod_idx;
@@ -281,12 +288,14 @@ void launch_linear_mxfp8(const uint8_t *a, int64_t lda, const uint8_t *a_scales,
     p.n_groups = n_mod_groups > 0 ? n_mod_groups : 1;
     p.ffn = (int32_t)(N / 2);
     p.tiles_m = (int32_t)((M_valid + BM - 1) / BM);
-    p.tiles_n = epilogue == H3_EPI_SWIGLU ? (int32_t)((N / 2 + BN / 2 - 1) / (BN / 2)) : (int32_t)((N + BN - 1) / BN);
+    const bool swiglu = epilogue == H3_EPI_SWIGLU || epilogue == kEpiSwigluMx;
+    p.tiles_n = swiglu ? (int32_t)((N / 2 + BN / 2 - 1) / (BN / 2)) : (int32_t)((N + BN - 1) / BN);
     p.group_m = p.tiles_n >= 128 ? 8 : 2;
     const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
     switch (epilogue) {
         case H3_EPI_RESIDUAL: gemm_mxfp8_kernel<H3_EPI_RESIDUAL><<<grid, kThreads, 0, stream>>>(p); break;
         case H3_EPI_SWIGLU: gemm_mxfp8_kernel<H3_EPI_SWIGLU><<<grid, kThreads, 0, stream>>>(p); break;
+        case kEpiSwigluMx: gemm_mxfp8_kernel<kEpiSwigluMx><<<grid, kThreads, 0, stream>>>(p); break;
         default: gemm_mxfp8_kernel<H3_EPI_STORE><<<grid, kThreads, 0, stream>>>(p); break;
     }
 }

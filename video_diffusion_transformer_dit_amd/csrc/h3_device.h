@@ -78,6 +78,35 @@ __device__ __forceinline__ void gemm_tile_coords(int bid, int tiles_m, int tiles
     tn = in_group / gsz;
 }
 
+// ---- MXFP8 (E4M3 elements, one E8M0 scale per 32 values) ----
+// Shared exponent of a group from its largest magnitude: floor(log2 amax) - 8,
+// read from amax's FP32 exponent field, clamped below at -127 (zero and FP32
+// subnormal groups get -127). The scale code is this + 127.
+__device__ __forceinline__ int mx_shared_exponent(float amax) {
+    const int eb = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+    return max(eb - 127 - 8, -127);
+}
+// 2^-e as a float, exact for the exponents mx_shared_exponent returns.
+__device__ __forceinline__ float mx_inv_scale(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+// 8 floats, already divided by the group scale, -> 8 E4M3 codes: saturate to
+// +-448, then the hardware conversion (round to nearest, ties to even).
+__device__ __forceinline__ uint2 e4m3x8(const float y[8]) {
+    float c[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = fminf(fmaxf(y[e], -448.0f), 448.0f);
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], hi, true);
+    return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(a, -448.0f), 448.0f), fminf(fmaxf(b, -448.0f), 448.0f), 0,
+                                            false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(c, -448.0f), 448.0f), fminf(fmaxf(d, -448.0f), 448.0f), v, true);
+    return (uint32_t)v;
+}
+
 // BF16 bit pattern -> float (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

@@ -14,6 +14,11 @@
 
 namespace h3 {
 
+// Internal epilogue: SwiGLU with its output written as MXFP8 (E4M3 codes at
+// p.cq / p.ld_cq, scale codes at p.cs with p.cs_rows scale rows), the fused
+// quantizing SwiGLU producer of Sol-H3 report, §3.3 "MXFP8 GEMM computation".
+constexpr int kEpiSwigluMx = 3;
+
 // In each 32 x 32 sub-tile the lane holds row m = lane & 31 and, for register
 // group q (0..3), the 4 columns 8 q + 4 (lane >> 5) + (0..3). Args provides
 // M, N, ffn, c/ldc, bias, resid/ld_r, gate/ld_gate, mod_idx and n_groups.
@@ -25,8 +30,51 @@ __device__ __forceinline__ void gemm_epilogue(const Args &p, f32x16_t (&acc)[4][
     for (int j = 0; j < 4; ++j) {
         const int64_t m = (int64_t)tm * BM + wm * 128 + j * 32 + r32;
         if (m >= p.M) continue;
-        uint16_t *crow = p.c + m * p.ldc;
-        if (EPI == H3_EPI_SWIGLU) {
+        uint16_t *crow = EPI == kEpiSwigluMx ? nullptr : p.c + m * p.ldc;
+        if constexpr (EPI == kEpiSwigluMx) {
+            // A 32-wide output group is W sub-tiles i = 2 ip, 2 ip + 1: 16
+            // values in this lane (4 columns x q x 2 sub-tiles) and 16 in lane
+            // ^ 32 (the other 4-column halves).
+#pragma unroll
+            for (int ip = 0; ip < 2; ++ip) {
+                const int64_t col0 = (int64_t)tn * (BN / 2) + (wn * 4 + 2 * ip) * 16;
+                if (col0 >= p.ffn) continue;
+                float o[2][2][4];
+                float amax = 0.f;
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii) {
+                    const int i = 2 * ip + ii;
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const int64_t col = col0 + 16 * ii + 8 * q + 4 * g2;
+                        float gb[4] = {0.f, 0.f, 0.f, 0.f}, ub[4] = {0.f, 0.f, 0.f, 0.f};
+                        if (p.bias) {
+                            const uint2 bg = *reinterpret_cast<const uint2 *>(p.bias + col);
+                            const uint2 bu = *reinterpret_cast<const uint2 *>(p.bias + p.ffn + col);
+                            gb[0] = bf16_lo(bg.x); gb[1] = bf16_hi(bg.x); gb[2] = bf16_lo(bg.y); gb[3] = bf16_hi(bg.y);
+                            ub[0] = bf16_lo(bu.x); ub[1] = bf16_hi(bu.x); ub[2] = bf16_lo(bu.y); ub[3] = bf16_hi(bu.y);
+                        }
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float zg = acc[i][j][4 * q + e] + gb[e];
+                            o[ii][q][e] = zg / (1.0f + __expf(-zg)) * (acc[i][j][4 * (q + 2) + e] + ub[e]);
+                            amax = fmaxf(amax, fabsf(o[ii][q][e]));
+                        }
+                    }
+                }
+                amax = fmaxf(amax, __shfl_xor(amax, 32));
+                const int ex = mx_shared_exponent(amax);
+                const float is = mx_inv_scale(ex);
+                uint8_t *qrow = p.cq + m * p.ld_cq;
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+                        *reinterpret_cast<uint32_t *>(qrow + col0 + 16 * ii + 8 * q + 4 * g2) =
+                            e4m3x4(o[ii][q][0] * is, o[ii][q][1] * is, o[ii][q][2] * is, o[ii][q][3] * is);
+                if (g2 == 0) p.cs[((col0 >> 7) * p.cs_rows + m) * 4 + ((col0 >> 5) & 3)] = (uint8_t)(ex + 127);
+            }
+        } else if (EPI == H3_EPI_SWIGLU) {
             // W sub-tile i holds the gate block (rows 0-15, q = 0, 1) and the up
             // block (rows 16-31, q = 2, 3) of output columns (wn*4 + i)*16 + 0..15.
 #pragma unroll

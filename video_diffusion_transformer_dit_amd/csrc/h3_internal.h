@@ -68,6 +68,13 @@ struct BlockSparseLayout {
 bool block_sparse_layout(const h3_dims *d, int64_t L_buf, int64_t valid_len, int64_t prefix_len,
                          BlockSparseLayout *out);
 
+// Workspace of the MXFP8 block: byte offsets of the H3_MXWS_* buffers.
+struct MxWsLayout {
+    int64_t off[H3_MXWS_COUNT];
+    size_t total;
+};
+bool mx_ws_layout(const h3_dims *d, int64_t L_buf, MxWsLayout *out);
+
 // Validation of dims shared by several checks.
 int check_dims(const h3_dims *d);
 

@@ -20,18 +20,6 @@
 namespace h3 {
 namespace {
 
-// 8 floats, already scaled, -> 8 E4M3 codes (saturating at +-448).
-__device__ __forceinline__ uint2 to_e4m3x8(const float y[8]) {
-    float c[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) c[e] = fminf(fmaxf(y[e], -448.0f), 448.0f);
-    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
-    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], hi, true);
-    return make_uint2((uint32_t)lo, (uint32_t)hi);
-}
-
 __global__ __launch_bounds__(256) void mx_quantize_kernel(const uint16_t *x, int64_t ld_x, int64_t rows_buf,
                                                           int64_t rows_valid, int32_t slabs, uint8_t *q,
                                                           int64_t ld_q, uint8_t *scales) {
@@ -49,13 +37,12 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const uint16_t *x, int
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
     amax = fmaxf(amax, __shfl_xor(amax, 1));
     amax = fmaxf(amax, __shfl_xor(amax, 2));
-    const int eb = (int)((__float_as_uint(amax) >> 23) & 0xFF);
-    const int ex = max(eb - 127 - 8, -127);
-    const float inv = __uint_as_float((uint32_t)(127 - ex) << 23);  // 2^-ex, exact
+    const int ex = mx_shared_exponent(amax);
+    const float inv = mx_inv_scale(ex);
     float y[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = f[e] * inv;
-    *reinterpret_cast<uint2 *>(q + row * ld_q + col) = to_e4m3x8(y);
+    *reinterpret_cast<uint2 *>(q + row * ld_q + col) = e4m3x8(y);
     // scale codes of the slab's 4 groups (lanes 0, 4, 8, 12 of the team)
     const uint32_t code = (uint32_t)(ex + 127);
     const uint32_t c1 = __shfl_down(code, 4), c2 = __shfl_down(code, 8), c3 = __shfl_down(code, 12);
@@ -64,7 +51,26 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const uint16_t *x, int
             code | (c1 << 8) | (c2 << 16) | (c3 << 24);
 }
 
+// Zero codes and scale codes of rows [r0, r1) of an MXFP8 matrix with `slabs`
+// 128-wide scale slabs and rows_buf scale rows.
+__global__ __launch_bounds__(256) void mx_zero_rows_kernel(uint8_t *q, int64_t ld_q, int32_t slabs, uint8_t *scales,
+                                                           int64_t rows_buf, int64_t r0, int64_t r1) {
+    const int64_t r = r0 + blockIdx.x;
+    if (r >= r1) return;
+    for (int c = threadIdx.x; c < slabs * 8; c += blockDim.x)
+        *reinterpret_cast<uint4 *>(q + r * ld_q + 16 * c) = make_uint4(0, 0, 0, 0);
+    for (int k = threadIdx.x; k < slabs; k += blockDim.x)
+        *reinterpret_cast<uint32_t *>(scales + ((int64_t)k * rows_buf + r) * 4) = 0;
+}
+
 }  // namespace
+
+void launch_mx_zero_rows(uint8_t *q, int64_t ld_q, int64_t K, uint8_t *scales, int64_t rows_buf, int64_t r0,
+                         int64_t r1, hipStream_t stream) {
+    if (r1 <= r0) return;
+    mx_zero_rows_kernel<<<dim3((unsigned)(r1 - r0)), 256, 0, stream>>>(q, ld_q, (int32_t)(K / 128), scales, rows_buf,
+                                                                      r0, r1);
+}
 
 void launch_mx_quantize(const uint16_t *x, int64_t ld_x, int64_t rows_buf, int64_t rows_valid, int64_t K, uint8_t *q,
                         int64_t ld_q, uint8_t *scales, hipStream_t stream) {

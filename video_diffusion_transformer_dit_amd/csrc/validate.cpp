@@ -194,6 +194,25 @@ bool block_sparse_layout(const h3_dims *d, int64_t L_buf, int64_t valid_len, int
     return true;
 }
 
+bool mx_ws_layout(const h3_dims *d, int64_t L_buf, MxWsLayout *out) {
+    if (check_dims(d) != H3_OK || L_buf < 0) return false;
+    if (d->hidden % 128 != 0 || d->ffn % 128 != 0) return false;
+    const int64_t H = d->hidden, F = d->ffn;
+    auto align = [](int64_t b) { return (b + (int64_t)kWsAlign - 1) / (int64_t)kWsAlign * (int64_t)kWsAlign; };
+    VtPlan p;
+    vt_plan(nullptr, 0, L_buf, d->heads, &p);
+    const int64_t bytes[H3_MXWS_COUNT] = {L_buf * H,     L_buf * H / 32, L_buf * 3 * H * 2, L_buf * H * 2,
+                                          L_buf * H,     L_buf * H / 32, L_buf * H * 2,     L_buf * H,
+                                          L_buf * H / 32, L_buf * F,     L_buf * F / 32,    (int64_t)p.bytes};
+    int64_t off = 0;
+    for (int i = 0; i < H3_MXWS_COUNT; ++i) {
+        out->off[i] = off;
+        off += align(bytes[i]);
+    }
+    out->total = (size_t)off;
+    return true;
+}
+
 }  // namespace h3
 
 using namespace h3;
@@ -758,6 +777,114 @@ int h3_check_linear_mxfp8(const uint8_t *a, int64_t lda, const uint8_t *a_scales
         const Mat mr = mat(resid, M_buf, N, ld_r);
         if (!same(mr, mc) && overlap(mr, mc)) return H3_ERR_ALIAS;
     }
+    return H3_OK;
+}
+
+int h3_check_fused_modulate_norm_mxfp8(const uint16_t *x, int64_t ld_x, const uint16_t *branch, int64_t ld_b,
+                                       const float *shift, const float *scale, const float *gate,
+                                       int64_t ld_mod_group, int32_t n_mod_groups, const uint16_t *x1_out,
+                                       int64_t ld_x1, const uint8_t *hq, int64_t ld_hq, const uint8_t *hs,
+                                       int64_t L_buf, int64_t valid_len, int32_t hidden, float eps,
+                                       int32_t norm_type) {
+    H3_TRY(check_rows(L_buf, valid_len));
+    if (hidden <= 0) return H3_ERR_SHAPE;
+    if (hidden > kMaxHidden) return H3_ERR_UNSUPPORTED;
+    if (hidden % 128 != 0) return H3_ERR_UNSUPPORTED;  // whole 128-wide scale slabs
+    if (norm_type != 0 && norm_type != 1) return H3_ERR_UNSUPPORTED;
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return H3_ERR_SHAPE;
+    if (L_buf == 0) return H3_OK;
+    if (!x || !hq || !hs || !shift || !scale) return H3_ERR_NULL;
+    if (branch && (!gate || !x1_out)) return H3_ERR_NULL;
+    if (n_mod_groups < 1) return H3_ERR_SHAPE;
+    if (ld_mod_group < hidden && n_mod_groups > 1) return H3_ERR_SHAPE;
+    if (ld_mod_group % 4 != 0) return H3_ERR_ALIGN;
+    if (!aligned16(shift) || !aligned16(scale) || (gate && !aligned16(gate))) return H3_ERR_ALIGN;
+    H3_TRY(check_bf16_mat(x, ld_x, hidden));
+    if (ld_hq < hidden) return H3_ERR_SHAPE;
+    if (!aligned16(hq) || (ld_hq % 16) != 0 || (reinterpret_cast<uintptr_t>(hs) & 3u)) return H3_ERR_ALIGN;
+    if (branch) {
+        H3_TRY(check_bf16_mat(branch, ld_b, hidden));
+        H3_TRY(check_bf16_mat(x1_out, ld_x1, hidden));
+    }
+    const Mat mx = mat(x, L_buf, hidden, ld_x), mq = mat(hq, L_buf, hidden, ld_hq, 1);
+    const Mat ms = bytes_of(hs, L_buf * (hidden / 32));
+    const Mat mb = mat(branch, branch ? L_buf : 0, hidden, ld_b);
+    const Mat m1 = mat(x1_out, branch ? L_buf : 0, hidden, ld_x1);
+    const int64_t lm = std::max<int64_t>(ld_mod_group, hidden);
+    const Mat msh = mat(shift, n_mod_groups, hidden, lm, 4), msc = mat(scale, n_mod_groups, hidden, lm, 4);
+    const Mat mg = mat(gate, gate ? n_mod_groups : 0, hidden, lm, 4);
+    for (const Mat *out : {&mq, &ms})
+        for (const Mat *in : {&mx, &mb, &msh, &msc, &mg, &m1})
+            if (overlap(*out, *in)) return H3_ERR_ALIAS;
+    if (overlap(mq, ms)) return H3_ERR_ALIAS;
+    if (branch) {
+        if (!same(m1, mx) && overlap(m1, mx)) return H3_ERR_ALIAS;
+        for (const Mat *in : {&mb, &msh, &msc, &mg})
+            if (overlap(m1, *in)) return H3_ERR_ALIAS;
+    }
+    return H3_OK;
+}
+
+size_t h3_block_mxfp8_workspace_bytes(const h3_dims *dims, int64_t L_buf) {
+    MxWsLayout l;
+    if (!mx_ws_layout(dims, L_buf, &l)) return 0;
+    return l.total;
+}
+
+int h3_block_mxfp8_workspace_layout(const h3_dims *dims, int64_t L_buf, int64_t offsets[H3_MXWS_COUNT]) {
+    if (offsets == nullptr) return H3_ERR_NULL;
+    H3_TRY(check_dims(dims));
+    if (L_buf < 0) return H3_ERR_SHAPE;
+    MxWsLayout l;
+    if (!mx_ws_layout(dims, L_buf, &l)) return H3_ERR_UNSUPPORTED;
+    for (int i = 0; i < H3_MXWS_COUNT; ++i) offsets[i] = l.off[i];
+    return H3_OK;
+}
+
+int h3_check_block_forward_mxfp8(const h3_dims *dims, const h3_block_weights_mxfp8 *w, const uint16_t *x,
+                                 const uint16_t *y, const float *mod, int32_t n_mod_groups, const int32_t *mod_idx,
+                                 const int32_t *pos, int64_t L_buf, int64_t valid_len, const void *workspace,
+                                 size_t ws_bytes) {
+    (void)mod_idx;
+    (void)pos;
+    H3_TRY(check_dims(dims));
+    if (dims->hidden % 128 != 0 || dims->ffn % 128 != 0) return H3_ERR_UNSUPPORTED;
+    H3_TRY(check_rows(L_buf, valid_len));
+    if (w == nullptr) return H3_ERR_NULL;
+    if (L_buf == 0) return H3_OK;
+    const int64_t H = dims->hidden, F = dims->ffn, d = dims->head_dim;
+    if (!x || !y || !mod) return H3_ERR_NULL;
+    if (!w->w_qkv || !w->s_qkv || !w->w_o || !w->s_o || !w->w_up || !w->s_up || !w->w_down || !w->s_down ||
+        !w->q_gain || !w->k_gain)
+        return H3_ERR_NULL;
+    if (n_mod_groups < 1) return H3_ERR_SHAPE;
+    if (!aligned16(mod)) return H3_ERR_ALIGN;
+    H3_TRY(check_bf16_mat(x, H, H));
+    H3_TRY(check_bf16_mat(y, H, H));
+    for (const uint8_t *p : {w->w_qkv, w->w_o, w->w_up, w->w_down})
+        if (!aligned16(p)) return H3_ERR_ALIGN;
+    for (const uint8_t *p : {w->s_qkv, w->s_o, w->s_up, w->s_down})
+        if (reinterpret_cast<uintptr_t>(p) & 3u) return H3_ERR_ALIGN;
+    for (const uint16_t *p : {w->b_qkv, w->b_o, w->b_up, w->b_down, w->q_gain, w->k_gain})
+        if (p && !aligned16(p)) return H3_ERR_ALIGN;
+    MxWsLayout l;
+    if (!mx_ws_layout(dims, L_buf, &l)) return H3_ERR_SHAPE;
+    if (workspace == nullptr || ws_bytes < l.total) return H3_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0) return H3_ERR_ALIGN;
+    const Mat mx = mat(x, L_buf, H, H), my = mat(y, L_buf, H, H);
+    const Mat mws = bytes_of(workspace, (int64_t)l.total);
+    const Mat mmod = mat(mod, 1, (int64_t)n_mod_groups * 6 * H, (int64_t)n_mod_groups * 6 * H, 4);
+    const Mat weights[] = {mat(w->w_qkv, 3 * H, H, H, 1), bytes_of(w->s_qkv, 3 * H * H / 32),
+                           mat(w->w_o, H, H, H, 1),       bytes_of(w->s_o, H * H / 32),
+                           mat(w->w_up, 2 * F, H, H, 1),  bytes_of(w->s_up, 2 * F * H / 32),
+                           mat(w->w_down, H, F, F, 1),    bytes_of(w->s_down, H * F / 32),
+                           mat(w->b_qkv, w->b_qkv ? 1 : 0, 3 * H, 3 * H), mat(w->b_o, w->b_o ? 1 : 0, H, H),
+                           mat(w->b_up, w->b_up ? 1 : 0, 2 * F, 2 * F),   mat(w->b_down, w->b_down ? 1 : 0, H, H),
+                           mat(w->q_gain, 1, d, d),       mat(w->k_gain, 1, d, d)};
+    if (!same(mx, my) && overlap(mx, my)) return H3_ERR_ALIAS;
+    if (overlap(my, mws) || overlap(mx, mws) || overlap(my, mmod) || overlap(mws, mmod)) return H3_ERR_ALIAS;
+    for (const Mat &m : weights)
+        if (overlap(my, m) || overlap(mws, m)) return H3_ERR_ALIAS;
     return H3_OK;
 }
 

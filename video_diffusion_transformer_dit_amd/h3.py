@@ -19,6 +19,9 @@ H3_OK, H3_ERR_NULL, H3_ERR_SHAPE, H3_ERR_UNSUPPORTED, H3_ERR_ALIGN, H3_ERR_ALIAS
 H3_EPI_STORE, H3_EPI_RESIDUAL, H3_EPI_SWIGLU = range(3)
 H3_WS_H, H3_WS_QKV, H3_WS_O, H3_WS_X1, H3_WS_H2, H3_WS_G, H3_WS_VT = range(7)
 H3_WS_COUNT = 7
+H3_MXWS_HQ, H3_MXWS_HS, H3_MXWS_QKV, H3_MXWS_O, H3_MXWS_OQ, H3_MXWS_OS, H3_MXWS_X1, H3_MXWS_H2Q, H3_MXWS_H2S, \
+    H3_MXWS_GQ, H3_MXWS_GS, H3_MXWS_VT = range(12)
+H3_MXWS_COUNT = 12
 H3_MAX_SEGMENTS = 4
 H3_MAX_GROUPS = 8
 H3_SPARSE_Q_BLOCK, H3_SPARSE_K_BLOCK, H3_SPARSE_MAX_KBLOCKS = 256, 64, 4096
@@ -39,6 +42,11 @@ class Dims(C.Structure):
 class BlockWeights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("w_qkv", "b_qkv", "q_gain", "k_gain", "w_o", "b_o", "w_up", "b_up",
                                           "w_down", "b_down")]
+
+
+class BlockWeightsMx(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("w_qkv", "s_qkv", "w_o", "s_o", "w_up", "s_up", "w_down", "s_down",
+                                          "b_qkv", "b_o", "b_up", "b_down", "q_gain", "k_gain")]
 
 
 class KvSeg(C.Structure):
@@ -115,6 +123,16 @@ def _load():
                             P],
         "h3_check_linear_mxfp8": [P, I64, P, I64, P, I64, P, P, P, I64, I64, I64, I64, I64, I32, P, I64, P, I64,
                                   I32],
+        "h3_fused_modulate_norm_mxfp8": [P, I64, P, I64, P, P, P, I64, I32, P, P, I64, P, I64, P, I64, I64, I32, F32,
+                                         I32, P],
+        "h3_check_fused_modulate_norm_mxfp8": [P, I64, P, I64, P, P, P, I64, I32, P, I64, P, I64, P, I64, I64, I32,
+                                               F32, I32],
+        "h3_block_forward_mxfp8": [C.POINTER(Dims), C.POINTER(BlockWeightsMx), P, P, P, I32, P, P, I64, I64, P, SZ,
+                                   P],
+        "h3_check_block_forward_mxfp8": [C.POINTER(Dims), C.POINTER(BlockWeightsMx), P, P, P, I32, P, P, I64, I64, P,
+                                         SZ],
+        "h3_block_mxfp8_workspace_bytes": [C.POINTER(Dims), I64],
+        "h3_block_mxfp8_workspace_layout": [C.POINTER(Dims), I64, C.POINTER(I64)],
         "h3_status_string": [C.c_int],
         "h3_abi_version": [],
     }
@@ -126,6 +144,7 @@ def _load():
     lib.h3_attention_workspace_bytes.restype = C.c_size_t
     lib.h3_sparse_select_workspace_bytes.restype = C.c_size_t
     lib.h3_block_sparse_workspace_bytes.restype = C.c_size_t
+    lib.h3_block_mxfp8_workspace_bytes.restype = C.c_size_t
     lib.h3_sparse_attention_workspace_bytes.restype = C.c_size_t
     lib.h3_status_string.restype = C.c_char_p
     return lib
@@ -142,7 +161,9 @@ EXPORTS = ["h3_block_forward", "h3_attention", "h3_fused_modulate_norm", "h3_qk_
            "h3_check_sparse_attention", "h3_block_forward_sparse", "h3_block_sparse_workspace_bytes",
            "h3_check_block_forward_sparse",
            "h3_block_sparse_workspace_layout", "h3_mxfp8_quantize", "h3_linear_mxfp8", "h3_check_mxfp8_quantize",
-           "h3_check_linear_mxfp8"]
+           "h3_check_linear_mxfp8", "h3_fused_modulate_norm_mxfp8", "h3_check_fused_modulate_norm_mxfp8",
+           "h3_block_forward_mxfp8", "h3_check_block_forward_mxfp8", "h3_block_mxfp8_workspace_bytes",
+           "h3_block_mxfp8_workspace_layout"]
 
 
 def status_string(s: int) -> str:
@@ -387,3 +408,41 @@ def linear_mxfp8(a, a_scales, w, w_scales, c, M_valid, epilogue=H3_EPI_STORE, bi
                             _ptr(resid), _ld(resid), _ptr(gate), ld_gate_group, n_mod_groups, _ptr(mod_idx),
                             _stream(stream))
     _ok(s, "h3_linear_mxfp8")
+
+
+def fused_modulate_norm_mxfp8(x, shift, scale, hq, hs, valid_len, eps=1e-6, norm_type=0, branch=None, gate=None,
+                              x1_out=None, ld_mod_group=0, n_mod_groups=1, mod_idx=None, stream=None):
+    """h written as MXFP8: hq [L_buf, hidden] uint8, hs [hidden/128, L_buf, 4] uint8."""
+    s = LIB.h3_fused_modulate_norm_mxfp8(_ptr(x), x.stride(0), _ptr(branch), _ld(branch), _ptr(shift), _ptr(scale),
+                                         _ptr(gate), ld_mod_group, n_mod_groups, _ptr(mod_idx), _ptr(x1_out),
+                                         _ld(x1_out), _ptr(hq), hq.stride(0), _ptr(hs), x.shape[0], valid_len,
+                                         x.shape[1], eps, norm_type, _stream(stream))
+    _ok(s, "h3_fused_modulate_norm_mxfp8")
+
+
+def make_weights_mx(wq: dict) -> BlockWeightsMx:
+    """wq: w_qkv / w_o / w_up / w_down -> (codes, scales) pairs; b_* and q_gain / k_gain BF16 tensors."""
+    f = {}
+    for n, sname in (("w_qkv", "s_qkv"), ("w_o", "s_o"), ("w_up", "s_up"), ("w_down", "s_down")):
+        f[n], f[sname] = _ptr(wq[n][0]), _ptr(wq[n][1])
+    for n in ("b_qkv", "b_o", "b_up", "b_down", "q_gain", "k_gain"):
+        f[n] = _ptr(wq.get(n))
+    return BlockWeightsMx(**f)
+
+
+def block_mxfp8_workspace_bytes(dims: Dims, L_buf: int) -> int:
+    return int(LIB.h3_block_mxfp8_workspace_bytes(C.byref(dims), L_buf))
+
+
+def block_mxfp8_workspace_layout(dims: Dims, L_buf: int):
+    off = (C.c_int64 * H3_MXWS_COUNT)()
+    _ok(LIB.h3_block_mxfp8_workspace_layout(C.byref(dims), L_buf, off), "h3_block_mxfp8_workspace_layout")
+    return list(off)
+
+
+def block_forward_mxfp8(dims: Dims, weights: BlockWeightsMx, x, y, mod, n_mod_groups, valid_len, workspace,
+                        mod_idx=None, pos=None, stream=None):
+    s = LIB.h3_block_forward_mxfp8(C.byref(dims), C.byref(weights), _ptr(x), _ptr(y), _ptr(mod), n_mod_groups,
+                                   _ptr(mod_idx), _ptr(pos), x.shape[0], valid_len, _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream))
+    _ok(s, "h3_block_forward_mxfp8")
