@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense BF16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 (and MXFP8) MFMA, published
 SEED = 20260903
 
 
@@ -248,6 +249,65 @@ def block_sparse(torch, h3, dev, q, k, v, o, V, heads, dense_ms, iters, block, p
     return out
 
 
+def mxfp8_gemms(torch, h3, dev, w, bufs, mod, L, V, H, F, bf16_ms, iters, dims, block_ms):
+    """The block's four projections as MXFP8 GEMMs (E4M3 with one E8M0 scale
+    per 32 along K) at the benchmark's shapes, on the block's own
+    activations. Weights are quantized once, outside the timing (they are
+    constants of the model); activations by h3_mxfp8_quantize, timed
+    separately."""
+    hbuf, o, x, x1, h2, g, y = bufs
+
+    def quant(t, rows_valid):
+        rows, K = t.shape
+        q = torch.empty((rows, K), dtype=torch.uint8, device=dev)
+        sc = torch.empty(h3.mx_scales_shape(rows, K), dtype=torch.uint8, device=dev)
+        h3.mxfp8_quantize(t, rows_valid, q, sc)
+        return q, sc
+
+    wq = {k: quant(w[k], w[k].shape[0]) for k in ("w_qkv", "w_o", "w_up", "w_down")}
+    aq = {"h": quant(hbuf, V), "o": quant(o, V), "h2": quant(h2, V), "g": quant(g, V)}
+    qkv = torch.empty((L, 3 * H), dtype=torch.bfloat16, device=dev)
+    gout = torch.empty((L, F), dtype=torch.bfloat16, device=dev)
+    x1o = torch.empty((L, H), dtype=torch.bfloat16, device=dev)
+    yo = torch.empty((L, H), dtype=torch.bfloat16, device=dev)
+    calls = {
+        "gemm_qkv": (lambda: h3.linear_mxfp8(*aq["h"], *wq["w_qkv"], qkv, V), 2.0 * V * H * 3 * H),
+        "gemm_out_residual": (lambda: h3.linear_mxfp8(*aq["o"], *wq["w_o"], x1o, V, h3.H3_EPI_RESIDUAL, resid=x,
+                                                      gate=mod[:, 2], ld_gate_group=6 * H), 2.0 * V * H * H),
+        "gemm_up_swiglu": (lambda: h3.linear_mxfp8(*aq["h2"], *wq["w_up"], gout, V, h3.H3_EPI_SWIGLU),
+                           2.0 * V * H * 2 * F),
+        "gemm_down_residual": (lambda: h3.linear_mxfp8(*aq["g"], *wq["w_down"], yo, V, h3.H3_EPI_RESIDUAL, resid=x1,
+                                                       gate=mod[:, 5], ld_gate_group=6 * H), 2.0 * V * F * H),
+    }
+    out = {"peak_fp8_tflops": PEAK_FP8_TFLOPS, "gemms": {}}
+    tot_mx, tot_bf = 0.0, 0.0
+    for k, (fn, fl) in calls.items():
+        t = time_calls(torch, fn, iters, 1)
+        tf = fl / (t * 1e-3) / 1e12
+        out["gemms"][k] = {"ms": round(t, 4), "tflops": round(tf, 1), "frac_fp8_mfma": round(tf / PEAK_FP8_TFLOPS, 4),
+                           "bf16_ms": round(bf16_ms[k], 4), "speedup_vs_bf16": round(bf16_ms[k] / t, 3)}
+        tot_mx += t
+        tot_bf += bf16_ms[k]
+    qt = {}
+    for name, t in (("h", hbuf), ("g", g)):
+        q, sc = aq[name]
+        qt[name] = round(time_calls(torch, lambda: h3.mxfp8_quantize(t, V, q, sc), iters, 1), 4)
+    out["quantize_ms"] = qt
+    out["gemm_total_ms"] = round(tot_mx, 3)
+    out["bf16_gemm_total_ms"] = round(tot_bf, 3)
+    # the whole MXFP8 block (fused producers, same attention)
+    wmx = dict(wq)
+    wmx.update({k: w[k] for k in ("q_gain", "k_gain")})
+    weights_mx = h3.make_weights_mx(wmx)
+    wsm = torch.empty(h3.block_mxfp8_workspace_bytes(dims, L), dtype=torch.uint8, device=dev)
+    blk = time_calls(torch, lambda: h3.block_forward_mxfp8(dims, weights_mx, x, y, mod, 1, V, wsm), iters, 1)
+    del wsm
+    out["block_ms"] = round(blk, 3)
+    out["dense_bf16_block_ms"] = round(block_ms, 3)
+    out["block_speedup"] = round(block_ms / blk, 3)
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -392,6 +452,8 @@ def main(argv=None) -> int:
         out["next"]["block_sparse_attention"] = block_sparse(torch, h3, dev, qkv[:, :H], qkv[:, H:2 * H],
                                                              qkv[:, 2 * H:], o, V, heads, k_ms["attention"], kit,
                                                              (dims, weights, x, y, mod, ms))
+        out["next"]["mxfp8_gemms"] = mxfp8_gemms(torch, h3, dev, w, (hbuf, o, x, x1, h2, g, y), mod, L, V, H, F,
+                                                 k_ms, kit, dims, ms)
         out["next"]["reference_kv_cache"] = reference_kv_cache(torch, h3, dev, dims, weights, mod, gen, L, V, H)
     if a.calibration_copy:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)   # 1 GiB
