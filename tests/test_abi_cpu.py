@@ -25,6 +25,16 @@ def addr(i):
     return A + i * 64 * MB
 
 
+def _align(b):
+    return -(-b // 256) * 256
+
+
+def attention_extra(heads, qrows):
+    """Bytes the attention workspace holds after the V^T planes: the per-head
+    key norm maxima and one int32 per workgroup of a launch."""
+    return _align(heads * 4) + _align(((qrows + 255) // 256 + 1) * heads * 4 + 8 * 4)
+
+
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
@@ -56,8 +66,9 @@ def test_workspace_layout_is_disjoint_and_aligned():
         total = h3.workspace_bytes(d, L)
         cols = [d.hidden, 3 * d.hidden, d.hidden, d.hidden, d.hidden, d.ffn]
         assert lds[:6] == cols
-        # V^T staging: heads x 128 x round_up(L, 64) BF16 for the dense case
-        assert lds[6] == d.heads * 128 * (-(-L // 64) * 64) * 2
+        # V^T staging: heads x 128 x round_up(L, 64) BF16 for the dense case,
+        # then the key norm maxima and the workgroup flags
+        assert lds[6] == d.heads * 128 * (-(-L // 64) * 64) * 2 + attention_extra(d.heads, L)
         ends = [o + L * c * 2 for o, c in zip(off, cols)] + [off[6] + lds[6]]
         for i in range(7):
             assert off[i] % 256 == 0
@@ -161,7 +172,7 @@ def test_attention_validator():
     o = addr(2)
     ws = addr(3)
     need = h3.attention_workspace_bytes(500, 2)
-    assert need == 2 * 128 * 512 * 2
+    assert need == 2 * 128 * 512 * 2 + attention_extra(2, 500)
     ok = h3.LIB.h3_check_attention(q, 3 * H, k, 3 * H, v, 3 * H, o, H, L, 500, 2, 128, 0.0, None, 0, ws, need)
     assert ok == h3.H3_OK
     assert h3.LIB.h3_check_attention(q, 3 * H, k, 3 * H, v, 3 * H, o, H, L, 500, 2, 128, 0.0, None, 0, ws,
@@ -284,7 +295,7 @@ def test_sparse_validators_and_workspace_sizes():
     assert lib.h3_sparse_select_workspace_bytes(V, V, heads) == 0
     assert lib.h3_sparse_select_workspace_bytes(V, V + 1, heads) == 0
     # attention workspace: V^T of the prefix and of the target keys, each padded to 64
-    assert lib.h3_sparse_attention_workspace_bytes(V, P, heads) == heads * 128 * (64 + 576) * 2
+    assert lib.h3_sparse_attention_workspace_bytes(V, P, heads) == heads * 128 * (64 + 576) * 2 + attention_extra(heads, V)
     assert lib.h3_sparse_attention_workspace_bytes(V, V, heads) == h3.attention_workspace_bytes(V, heads)
     q = addr(1)
     k, v = q + 2 * H, q + 4 * H

@@ -203,6 +203,31 @@ def test_attention_dense(heads, L, V, q_scale, packed):
     assert_zero_rows(o, V, "o")
 
 
+def test_attention_fixed_and_online_workgroups_in_one_call():
+    """Query tiles whose score bound |q| max|k| allows a fixed softmax
+    reference and tiles whose bound does not (their q scaled by 8) in one
+    call: the first are done by the fixed-reference kernel instance, the
+    others by the online one; every row must match the oracle."""
+    heads, L, V = 2, 1100, 1090
+    H = heads * 128
+    _say(f"attention fixed + online heads={heads} L={L} V={V}")
+    qb, kb, vb = _qkv(L, heads, "amix")
+    q = O.bf16_to_f64(qb)
+    q[256:512] *= 8.0                       # query tile 1: bound far above the fixed range
+    q[1000:1010] *= 8.0                     # a few rows of the last tile
+    qb = I.f32_to_bf16_bits(q.astype(np.float32))
+    o = poison((L, H))
+    h3.attention(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), o, V, heads)
+    torch.cuda.synchronize()
+    ref = O.attention(O.bf16_to_f64(qb[:V]), O.bf16_to_f64(kb[:V]), O.bf16_to_f64(vb[:V]), heads, 128)
+    got = f64(o)
+    # compared by kind of row (the max-error bar is relative to the slice's
+    # RMS, and sharp rows, q x 8, have much larger outputs than soft ones)
+    for a, b in ((0, 256), (256, 512), (512, 768), (768, 1000), (1000, 1010), (1010, 1024), (1024, V)):
+        assert_parity(got[a:b], ref[a:b], f"o[{a}:{b}]")
+    assert_zero_rows(o, V, "o")
+
+
 def test_attention_single_key_is_exact():
     """One valid key: softmax weight exactly 1, so o equals that key's value bit for bit."""
     heads, L = 2, 64

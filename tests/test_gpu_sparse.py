@@ -122,9 +122,13 @@ def test_sparse_select_matches_oracle(heads, P, T, tau):
     _check_selection(blocks, counts, scores, thr, _margin(qf, kf, V, P, heads), f"T={T}")
 
 
-def _attention_case(heads, L, V, P, density, tag, edit=None):
+def _attention_case(heads, L, V, P, density, tag, edit=None, big_rows=None):
     H = heads * D
     qkv = I.normal_bf16(f"spa.{tag}", (L, 3 * H), 1.0)
+    if big_rows is not None:             # rows whose score bound needs the online softmax
+        f = I.bf16_bits_to_f32(qkv)
+        f[big_rows[0]:big_rows[1], :H] *= 8.0
+        qkv = I.f32_to_bf16_bits(f)
     d = dev_bf16(qkv)
     q, k, v = d[:, :H], d[:, H:2 * H], d[:, 2 * H:]
     nq, nk = h3.sparse_geometry(V, P)
@@ -157,6 +161,17 @@ def test_sparse_attention_matches_oracle(heads, L, V, P, density):
     if V > P:
         assert_parity(got[P:V], ref[P:V], "target rows")
     assert_zero_rows(o, V, "o")
+
+
+def test_sparse_attention_online_workgroups():
+    """List mode with prefix and target tiles whose score bound is too large
+    for the fixed softmax reference (q scaled by 8): the online instance."""
+    _say("sparse_attention online workgroups")
+    heads, L, V, P = 2, 1100, 1100, 300
+    o, ref = _attention_case(heads, L, V, P, 0.4, "online", big_rows=(200, 700))
+    got = f64(o)
+    assert_parity(got[:P], ref[:P], "prefix rows")
+    assert_parity(got[P:V], ref[P:V], "target rows")
 
 
 def test_sparse_attention_list_edge_cases():

@@ -23,9 +23,18 @@
 //  * In V^T the keys of every 16-key group are permuted (bits 2 and 3 of the
 //    key index swapped) so each lane's 8 keys of a P.V k-step are one 16-byte
 //    LDS read.
-//  * Online softmax in FP32 in the exp2 domain (scale * log2 e folded into one
-//    FMA); the O accumulator is rescaled only when some row maximum grew.
-//    P is rounded to BF16 for the P.V MFMA.
+//  * Softmax in FP32 in the exp2 domain (scale * log2 e folded into one FMA),
+//    against a per-row reference m: p = exp2(s c - m). By Cauchy-Schwarz every
+//    score obeys |s c| <= B = |q| max|k| c, so when B <= 60 the reference is
+//    fixed at m = B: no p exceeds 1, none falls below 2^-120 (normal in FP32
+//    and BF16), and no running maximum or rescaling is needed. |q| comes from
+//    the workgroup's own Q registers, max|k| from a small pre-pass over the
+//    call's keys. The two forms are two instances of the kernel, launched
+//    back to back on the same grid: the fixed-reference instance handles
+//    every workgroup whose rows all have B <= 60 and flags the others, which
+//    the online instance then handles (m starts at the first half tile's
+//    maximum and O is rescaled only when some row maximum grew); it exits at
+//    once for the rest. P is rounded to BF16 for the P.V MFMA.
 //  * Workgroups are dealt round-robin over the 8 XCDs; work items are remapped
 //    so each XCD walks a contiguous range (consecutive query tiles of one
 //    head), so the workgroups resident on an XCD stream the same K/V through
@@ -59,6 +68,8 @@ struct AttnArgs {
     const uint16_t *sk[H3_MAX_SEGMENTS];   // segment row 0, head 0
     const uint16_t *svt[H3_MAX_SEGMENTS];  // segment's V^T planes [heads][128][lpad]
     int64_t sldk[H3_MAX_SEGMENTS], slpad[H3_MAX_SEGMENTS], slen[H3_MAX_SEGMENTS];
+    const float *kmax2;      // [heads] largest squared key norm over all segments
+    int32_t *flags;          // per workgroup: 1 = left to the online instance
     // Block-sparse (list) mode: q and o point at row 0; segment 0 is the
     // prefix [0, P), segment 1 the target rows [P, P + T). Work items
     // [0, pre_items) are prefix query tiles (dense over both segments; items
@@ -129,8 +140,9 @@ struct Cursor {
 // The dense / grouped kernel (SPARSE = false) and the block-sparse list mode
 // (SPARSE = true) share every step; list mode only changes which query tile a
 // workgroup owns and which key tiles of segment 1 it visits.
-template <bool SPARSE>
+template <bool SPARSE, bool FIXED>
 __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) {
+    if (!FIXED && a.flags[blockIdx.x] == 0) return;  // done by the fixed-reference instance
     constexpr int KB = BKV * 16;  // 16-byte chunks per K tile buffer (16 KB)
     constexpr int VB = D * 8;     // chunks per V^T tile buffer (16 KB)
     // K buffers 0, 1 then V^T buffers 0, 1.
@@ -153,7 +165,10 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     {
         int bid = blockIdx.x;
         if (SPARSE && bid < a.pre_items) {
-            if (bid >= a.heads * a.pre_tiles) return;  // idle item (whole workgroup)
+            if (bid >= a.heads * a.pre_tiles) {  // idle item (whole workgroup)
+                if (FIXED && threadIdx.x == 0) a.flags[blockIdx.x] = 0;
+                return;
+            }
             head = bid / a.pre_tiles;
             const int64_t q0 = (int64_t)(bid - head * a.pre_tiles) * BQ;
             qbase = a.q + q0 * a.ld_q;
@@ -200,6 +215,37 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
                 qop[j][ks] = __builtin_bit_cast(
                     bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
                                   rqb, (int)(((32 * j + l32) * a.ld_q + 8 * (2 * ks + h)) * 2), 0, 0));
+    }
+    // Score bound per query row (exp2 domain): B = |q| max|k| scale log2(e),
+    // with a 2^-10 margin for the FP32 rounding of the norms. The lane pair
+    // (l, l ^ 32) holds the two halves of a row.
+    constexpr float kFixedMax = 60.0f;
+    float bound[2];
+    {
+        const float km = a.kmax2[head];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            float s2 = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const uint4 u = __builtin_bit_cast(uint4, qop[j][ks]);
+                float f[8];
+                unpack8(u, f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s2 = __builtin_fmaf(f[e], f[e], s2);
+            }
+            bound[j] = sqrtf(pair_sum(s2) * km) * a.scale_log2 * (1.0f + 1.0f / 1024.0f);
+        }
+    }
+    if (FIXED) {
+        // the workgroup takes the fixed reference only if all its rows allow it
+        __shared__ int vote[4];
+        const int ok = __all(bound[0] <= kFixedMax && bound[1] <= kFixedMax);
+        if (lane == 0) vote[wave] = ok;
+        __syncthreads();
+        const bool wg_ok = vote[0] && vote[1] && vote[2] && vote[3];
+        if (t == 0) a.flags[blockIdx.x] = wg_ok ? 0 : 1;
+        if (!wg_ok) return;
     }
     // Register-class hints (empty asm, no instruction): Q and O live in AGPRs,
     // which the MFMA reads directly, leaving the VGPRs for scores and P.
@@ -401,10 +447,14 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     float m_ref[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        float m = sv[j][0];
+        if (FIXED) {
+            m_ref[j] = bound[j];
+        } else {
+            float m = sv[j][0];
 #pragma unroll
-        for (int v = 1; v < 16; ++v) m = fmaxf(m, sv[j][v]);
-        m_ref[j] = pair_max(m) * a.scale_log2;
+            for (int v = 1; v < 16; ++v) m = fmaxf(m, sv[j][v]);
+            m_ref[j] = pair_max(m) * a.scale_log2;
+        }
 #pragma unroll
         for (int v = 0; v < 16; ++v) sv[j][v] = __builtin_fmaf(sv[j][v], a.scale_log2, -m_ref[j]);
         tmaxr[j] = 0.f;
@@ -428,10 +478,11 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     // a fixed order (sched_barrier); the empty asm statements keep each slot's
     // VALU work in its slot. Past the last tile the loads return zero and the
     // scores of half u+1 go unused.
-    auto hiter = [&](int uu) {
+    auto hiter = [&](int uu, bool fixed) {
         const int tp = uu >> 1, odd = uu & 1;
-        // check (tmaxr: per-lane maximum of half u's shifted scores)
-        {
+        // check (tmaxr: per-lane maximum of half u's shifted scores); with a
+        // fixed reference no score can exceed it
+        if (!fixed) {
             bool over = false;
             float tm[2];
 #pragma unroll
@@ -568,17 +619,19 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
                 sb[gj] += sv[gj][2 * e + 1];
                 asm volatile("" : "+v"(sa[gj]), "+v"(sb[gj]));
                 if (sl >= 1) copy_pair(sl - 1);
-                if (sl >= 2) max_pair(sl - 2);
+                if (!fixed && sl >= 2) max_pair(sl - 2);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
         copy_pair(15);
-        max_pair(14);
-        max_pair(15);
+        if (!fixed) {
+            max_pair(14);
+            max_pair(15);
+        }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             l_run[j] += sa[j] + sb[j];
-            tmaxr[j] = mx[j];
+            if (!fixed) tmaxr[j] = mx[j];
         }
         if (odd) vk_cur = vk_next;
     };
@@ -587,14 +640,14 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     int u = 0;
 #pragma unroll 1
     for (; u + 4 <= n_half; u += 4) {
-        hiter(0);
-        hiter(1);
-        hiter(2);
-        hiter(3);
+        hiter(0, FIXED);
+        hiter(1, FIXED);
+        hiter(2, FIXED);
+        hiter(3, FIXED);
     }
     if (u < n_half) {
-        hiter(0);
-        hiter(1);
+        hiter(0, FIXED);
+        hiter(1, FIXED);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads past the end
 
@@ -617,6 +670,33 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
                 }
         }
     }
+}
+
+// Largest squared key norm per head over rows [0, rows) of k, merged into
+// kmax2[head] (non-negative FP32 bit patterns compare like unsigned integers,
+// so an integer atomic maximum merges them). 16 lanes per 128-channel key,
+// 256 rows per workgroup, one atomic per wave.
+__global__ __launch_bounds__(256) void key_norm_max_kernel(const uint16_t *k, int64_t ld, int64_t rows,
+                                                           uint32_t *kmax2) {
+    const int head = blockIdx.y;
+    const int t = threadIdx.x, c = t & 15;
+    const int64_t r_end = min<int64_t>((int64_t)(blockIdx.x + 1) * 256, rows);
+    float m = 0.f;
+    for (int64_t r = (int64_t)blockIdx.x * 256 + (t >> 4); r < r_end; r += 16) {
+        float f[8];
+        unpack8(*reinterpret_cast<const uint4 *>(k + r * ld + head * D + 8 * c), f);
+        float s2 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s2 = __builtin_fmaf(f[e], f[e], s2);
+        s2 += __shfl_xor(s2, 8);
+        s2 += __shfl_xor(s2, 4);
+        s2 += __shfl_xor(s2, 2);
+        s2 += __shfl_xor(s2, 1);
+        m = fmaxf(m, s2);
+    }
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    if ((t & 63) == 0) atomicMax(kmax2 + head, __float_as_uint(m));
 }
 
 // V -> V^T staging for one segment: tile of 64 keys x 128 channels of one head
@@ -653,8 +733,20 @@ __global__ __launch_bounds__(256) void vt_transpose_kernel(const uint16_t *v, in
     }
 }
 
-// Transposed V of every segment of the plan into the workspace.
-void stage_vt(const VtPlan &plan, const uint16_t *v, int64_t ld_v, int32_t heads, uint8_t *ws, hipStream_t stream) {
+// Transposed V of every segment of the plan into the workspace, and the
+// largest squared key norm per head over all segments.
+void stage_vt(const VtPlan &plan, const uint16_t *k, int64_t ld_k, const uint16_t *v, int64_t ld_v, int32_t heads,
+              uint8_t *ws, hipStream_t stream) {
+    if (plan.n == 0) return;
+    uint32_t *kmax2 = reinterpret_cast<uint32_t *>(ws + plan.kmax_off);
+    const int64_t kcols = (int64_t)(plan.bytes - plan.kmax_off) / 2;  // the 256-byte aligned area, as BF16 slots
+    launch_zero_rows(reinterpret_cast<uint16_t *>(kmax2), kcols, kcols, 0, 1, stream);
+    for (int i = 0; i < plan.n; ++i) {
+        const VtSeg &e = plan.seg[i];
+        const uint16_t *ks = e.own ? k + e.begin * ld_k : e.k + e.begin * e.ld;
+        key_norm_max_kernel<<<dim3((unsigned)((e.len + 255) / 256), (unsigned)heads), 256, 0, stream>>>(
+            ks, e.own ? ld_k : e.ld, e.len, kmax2);
+    }
     for (int i = 0; i < plan.n; ++i) {
         const VtSeg &e = plan.seg[i];
         const uint16_t *src = e.own ? v + e.begin * ld_v : e.v + e.begin * e.ld;
@@ -686,7 +778,7 @@ void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_
     VtPlan plan;
     vt_plan(is_dense ? nullptr : groups, is_dense ? 0 : n_groups, valid_len, heads, &plan);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    stage_vt(plan, v, ld_v, heads, ws, stream);
+    stage_vt(plan, k, ld_k, v, ld_v, heads, ws, stream);
     std::pair<int64_t, int64_t> cov[H3_MAX_GROUPS];
     int nc = 0;
     for (int gi = 0; gi < n_groups; ++gi) {
@@ -703,6 +795,8 @@ void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_
         a.tiles_per_head = (int32_t)((a.rows + BQ - 1) / BQ);
         a.n_seg = g.n_seg;
         a.scale_log2 = scale * 1.4426950408889634f;
+        a.kmax2 = reinterpret_cast<const float *>(ws + plan.kmax_off);
+        a.flags = reinterpret_cast<int32_t *>(ws + plan.flags_off);
         for (int s = 0; s < g.n_seg; ++s) {
             const h3_kv_seg &ss = g.seg[s];
             const VtSeg &e = plan.seg[plan.map[gi][s]];
@@ -717,7 +811,9 @@ void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_
             a.slpad[s] = e.lpad;
             a.slen[s] = ss.len;
         }
-        attention_fwd_kernel<false><<<dim3((unsigned)(a.tiles_per_head * heads)), kThreads, 0, stream>>>(a);
+        const dim3 grid((unsigned)(a.tiles_per_head * heads));
+        attention_fwd_kernel<false, true><<<grid, kThreads, 0, stream>>>(a);
+        attention_fwd_kernel<false, false><<<grid, kThreads, 0, stream>>>(a);
     }
     // Zero the rows of o outside every group (the padding suffix included).
     std::sort(cov, cov + nc);
@@ -763,7 +859,7 @@ void launch_sparse_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k,
     VtPlan plan;
     vt_plan(&g, 1, valid_len, heads, &plan);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    stage_vt(plan, v, ld_v, heads, ws, stream);
+    stage_vt(plan, k, ld_k, v, ld_v, heads, ws, stream);
     const int64_t T = valid_len - prefix_len;
     AttnArgs a = {};
     a.q = q;
@@ -775,6 +871,8 @@ void launch_sparse_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k,
     a.tiles_per_head = (int32_t)((T + BQ - 1) / BQ);
     a.n_seg = 2;
     a.scale_log2 = scale * 1.4426950408889634f;
+    a.kmax2 = reinterpret_cast<const float *>(ws + plan.kmax_off);
+    a.flags = reinterpret_cast<int32_t *>(ws + plan.flags_off);
     for (int s = 0; s < 2; ++s) {
         const VtSeg &e = plan.seg[plan.map[0][s]];
         a.sk[s] = k + g.seg[s].begin * ld_k;
@@ -791,7 +889,8 @@ void launch_sparse_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k,
     a.prefix_len = prefix_len;
     a.tgt_rows = T;
     const unsigned grid = (unsigned)(a.pre_items + a.tiles_per_head * heads);
-    attention_fwd_kernel<true><<<dim3(grid), kThreads, 0, stream>>>(a);
+    attention_fwd_kernel<true, true><<<dim3(grid), kThreads, 0, stream>>>(a);
+    attention_fwd_kernel<true, false><<<dim3(grid), kThreads, 0, stream>>>(a);
     launch_zero_rows(o, ld_o, (int64_t)heads * D, valid_len, L_buf, stream);
 }
 

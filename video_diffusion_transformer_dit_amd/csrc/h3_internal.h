@@ -16,8 +16,13 @@ constexpr size_t kWsAlign = 256;
 // Attention stages each distinct K/V segment's V transposed per head in the
 // workspace: [heads][128][lpad] BF16 with lpad = len rounded up to 64.
 // Segments are identified by (own rows or external pointer, stride, begin, len).
+// After the segments come one FP32 per head, the largest squared norm of the
+// call's keys (it bounds every score), and one int32 per attention
+// workgroup, which tells the online kernel instance which workgroups the
+// fixed-reference instance left to it (see the attention kernel).
 struct VtSeg {
     int own;              // rows of the call's own K/V
+    const uint16_t *k;    // external K (own == 0)
     const uint16_t *v;    // external V (own == 0)
     int64_t ld, begin, len, lpad;
     int64_t off;          // byte offset inside the V^T staging area
@@ -26,6 +31,8 @@ struct VtPlan {
     int n;
     VtSeg seg[H3_MAX_GROUPS * H3_MAX_SEGMENTS];
     int map[H3_MAX_GROUPS][H3_MAX_SEGMENTS];  // (group, segment) -> seg index
+    int64_t kmax_off;     // byte offset of the per-head key norm maxima
+    int64_t flags_off;    // byte offset of one int32 per attention workgroup
     size_t bytes;
 };
 // groups == NULL plans one own segment [0, dense_len).

@@ -119,27 +119,44 @@ void sparse_vt_group(int64_t valid_len, int64_t prefix_len, h3_qgroup *g) {
 void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads, VtPlan *out) {
     out->n = 0;
     out->bytes = 0;
-    auto add = [&](int own, const uint16_t *v, int64_t ld, int64_t begin, int64_t len) {
+    out->kmax_off = 0;
+    auto add = [&](int own, const uint16_t *k, const uint16_t *v, int64_t ld, int64_t begin, int64_t len) {
         for (int i = 0; i < out->n; ++i) {
             const VtSeg &e = out->seg[i];
             if (e.own == own && e.v == v && e.ld == ld && e.begin == begin && e.len == len) return i;
         }
         VtSeg &e = out->seg[out->n];
-        e.own = own; e.v = v; e.ld = ld; e.begin = begin; e.len = len;
+        e.own = own; e.k = k; e.v = v; e.ld = ld; e.begin = begin; e.len = len;
         e.lpad = (len + 63) / 64 * 64;
         e.off = (int64_t)out->bytes;
         out->bytes += (size_t)heads * kHeadDim * e.lpad * 2;
         return out->n++;
     };
+    int64_t qrows = 0;  // longest query range of one launch
     if (groups == nullptr) {
-        if (dense_len > 0) out->map[0][0] = add(1, nullptr, 0, 0, dense_len);
-        return;
-    }
-    for (int g = 0; g < n_groups && g < H3_MAX_GROUPS; ++g)
-        for (int s = 0; s < groups[g].n_seg && s < H3_MAX_SEGMENTS; ++s) {
-            const h3_kv_seg &x = groups[g].seg[s];
-            out->map[g][s] = x.k == nullptr ? add(1, nullptr, 0, x.begin, x.len) : add(0, x.v, x.ld, x.begin, x.len);
+        if (dense_len > 0) out->map[0][0] = add(1, nullptr, nullptr, 0, 0, dense_len);
+        qrows = dense_len;
+    } else {
+        for (int g = 0; g < n_groups && g < H3_MAX_GROUPS; ++g) {
+            qrows = std::max<int64_t>(qrows, groups[g].q_end - groups[g].q_begin);
+            for (int s = 0; s < groups[g].n_seg && s < H3_MAX_SEGMENTS; ++s) {
+                const h3_kv_seg &x = groups[g].seg[s];
+                out->map[g][s] = x.k == nullptr ? add(1, nullptr, nullptr, 0, x.begin, x.len)
+                                                : add(0, x.k, x.v, x.ld, x.begin, x.len);
+            }
         }
+    }
+    out->flags_off = 0;
+    if (out->n > 0) {
+        auto align = [](size_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; };
+        out->kmax_off = (int64_t)out->bytes;
+        out->bytes += align((size_t)heads * 4);
+        // workgroups of one launch: query tiles of 256 rows per head, plus the
+        // block-sparse launch's split of the rows into prefix and target tiles
+        // (at most one more tile per head) and its padding to a multiple of 8
+        out->flags_off = (int64_t)out->bytes;
+        out->bytes += align((size_t)(((qrows + 255) / 256 + 1) * heads + 8) * 4);
+    }
 }
 
 bool ws_layout(const h3_dims *d, int64_t L_buf, const h3_qgroup *groups, int n_groups, WsLayout *out) {
@@ -536,7 +553,9 @@ int h3_check_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64
             return H3_ERR_ALIAS;
         for (int i = 0; i < plan.n; ++i) {
             const VtSeg &e = plan.seg[i];
-            if (!e.own && overlap(mw, mat(e.v + e.begin * e.ld, e.len, H, e.ld))) return H3_ERR_ALIAS;
+            if (!e.own && (overlap(mw, mat(e.v + e.begin * e.ld, e.len, H, e.ld)) ||
+                           overlap(mw, mat(e.k + e.begin * e.ld, e.len, H, e.ld))))
+                return H3_ERR_ALIAS;
         }
     }
     return H3_OK;
