@@ -496,26 +496,33 @@ typedef struct {
  *   gq  = MXFP8(silu(u_gate) * u_up), u = dequant(h2q) dequant(W_up)^T + b
  *                                      (fused into the up-projection epilogue)
  *   y   = bf16(x1 + gate_f * (dequant(gq) dequant(W_down)^T + b)); 0 on padding
- * Dense attention only (no query groups, no K/V export). hidden and ffn must be
- * multiples of 128. Other arguments as h3_block_forward. The quantization is
- * approximate: the result differs from the BF16 block by the MXFP8 rounding
- * of the four GEMMs' operands.
- * workspace: h3_block_mxfp8_workspace_bytes(dims, L_buf) bytes, 256-byte
- *          aligned; h3_block_mxfp8_workspace_layout gives the offsets of the
- *          intermediates it holds after the call. */
+ * Attention: dense over [0, valid_len) when prefix_len < 0; otherwise Sol-Attn
+ * block-sparse attention as in h3_block_forward_sparse (prefix rows
+ * [0, prefix_len) dense, target rows block-sparse with threshold tau): the
+ * pages run their refinement blocks with both. No query groups, no K/V
+ * export. hidden and ffn must be multiples of 128. Other arguments as
+ * h3_block_forward. The quantization is approximate: the result differs from
+ * the BF16 block by the MXFP8 rounding of the four GEMMs' operands.
+ * workspace: h3_block_mxfp8_workspace_bytes(dims, L_buf, valid_len,
+ *          prefix_len) bytes, 256-byte aligned; h3_block_mxfp8_workspace_layout
+ *          gives the offsets of the intermediates it holds after the call. */
 enum { H3_MXWS_HQ = 0, H3_MXWS_HS = 1, H3_MXWS_QKV = 2, H3_MXWS_O = 3, H3_MXWS_OQ = 4, H3_MXWS_OS = 5,
        H3_MXWS_X1 = 6, H3_MXWS_H2Q = 7, H3_MXWS_H2S = 8, H3_MXWS_GQ = 9, H3_MXWS_GS = 10, H3_MXWS_VT = 11,
-       H3_MXWS_COUNT = 12 };
+       H3_MXWS_BLOCKS = 12, H3_MXWS_COUNTS = 13, H3_MXWS_SELECT = 14, H3_MXWS_COUNT = 15 };
 int h3_block_forward_mxfp8(const h3_dims *dims, const h3_block_weights_mxfp8 *w,
                            const uint16_t *x, uint16_t *y,
                            const float *mod, int32_t n_mod_groups, const int32_t *mod_idx,
                            const int32_t *pos, int64_t L_buf, int64_t valid_len,
+                           int64_t prefix_len, float tau,
                            void *workspace, size_t ws_bytes, void *stream);
-size_t h3_block_mxfp8_workspace_bytes(const h3_dims *dims, int64_t L_buf);
+size_t h3_block_mxfp8_workspace_bytes(const h3_dims *dims, int64_t L_buf, int64_t valid_len, int64_t prefix_len);
 /* Byte offsets of the intermediates (codes [L_buf, cols] with row stride
  * cols; scales [cols / 128][L_buf][4]; BF16 qkv [L_buf, 3H], o and x1
- * [L_buf, H] with row strides 3H and H; the V^T staging area last). */
-int h3_block_mxfp8_workspace_layout(const h3_dims *dims, int64_t L_buf, int64_t offsets[H3_MXWS_COUNT]);
+ * [L_buf, H] with row strides 3H and H; the V^T staging area; with sparse
+ * attention the selection's lists and counts, as h3_sparse_select writes
+ * them, and its pooled means). */
+int h3_block_mxfp8_workspace_layout(const h3_dims *dims, int64_t L_buf, int64_t valid_len, int64_t prefix_len,
+                                    int64_t offsets[H3_MXWS_COUNT]);
 
 /* Host-only validators: the same checks each entry point runs before it
  * launches anything, callable without a GPU. They return an h3_status. */
@@ -599,6 +606,7 @@ int h3_check_block_forward_mxfp8(const h3_dims *dims, const h3_block_weights_mxf
                                  const uint16_t *x, const uint16_t *y,
                                  const float *mod, int32_t n_mod_groups, const int32_t *mod_idx,
                                  const int32_t *pos, int64_t L_buf, int64_t valid_len,
+                                 int64_t prefix_len, float tau,
                                  const void *workspace, size_t ws_bytes);
 
 /* Human-readable name of a status code (static string). */

@@ -293,13 +293,15 @@ class MxBlock:
         self.wq = wq
         self.weights = h3.make_weights_mx(wq)
 
-    def run(self, xb):
+    def run(self, xb, prefix_len=-1, tau=0.0):
         s = self.s
-        self.ws = torch.empty(h3.block_mxfp8_workspace_bytes(self.dims, s.L_buf), dtype=torch.uint8, device="cuda")
-        self.off = h3.block_mxfp8_workspace_layout(self.dims, s.L_buf)
+        self.ws = torch.empty(h3.block_mxfp8_workspace_bytes(self.dims, s.L_buf, s.valid_len, prefix_len),
+                              dtype=torch.uint8, device="cuda")
+        self.off = h3.block_mxfp8_workspace_layout(self.dims, s.L_buf, s.valid_len, prefix_len)
         x = dev_bf16(xb)
         y = poison(x.shape)
-        h3.block_forward_mxfp8(self.dims, self.weights, x, y, self.md, 1, s.valid_len, self.ws)
+        h3.block_forward_mxfp8(self.dims, self.weights, x, y, self.md, 1, s.valid_len, self.ws, prefix_len=prefix_len,
+                               tau=tau)
         torch.cuda.synchronize()
         return y
 
@@ -361,3 +363,45 @@ def test_block_mxfp8_tiny():
     rel = np.linalg.norm(f64(y)[:V] - exact["y"][:V]) / np.linalg.norm(exact["y"][:V])
     _say(f"  MXFP8 block vs exact block: y rel_fro={rel:.3e}")
     assert rel < 0.05
+
+
+def test_block_mxfp8_sparse_tiny():
+    """The pages' refinement block: MXFP8 projections and Sol-Attn block-sparse
+    attention (tau 1.0, prefix 128 rows) in one call, against the oracle block
+    with both options. The selection is checked as in the BF16 sparse block
+    (disagreements only within the rounding margin of the threshold); rows of
+    query blocks whose selection differs in some head are left out."""
+    _say("block mxfp8 + sparse tiny")
+    s = I.TINY
+    V, H, F, P, tau = s.valid_len, s.hidden, s.ffn, 128, 1.0
+    b = MxBlock(s, "mxb1")
+    xb = I.activations(s, tag="xmx1")
+    y = b.run(xb, prefix_len=P, tau=tau)
+    kw = dict(heads=s.heads, head_dim=s.head_dim, ffn=F, valid_len=V, rot_dim=s.rot_dim, theta=s.theta, eps=s.eps)
+    ref = O.block_forward(O.bf16_to_f64(xb), b.wo, b.mod.astype(np.float64), mxfp8=True, bf16_points=True,
+                          sparse=(P, tau), **kw)
+    nq, nk = h3.sparse_geometry(V, P)
+    blocks = b.buf(h3.H3_MXWS_BLOCKS, s.heads * nq * nk * 2).view(torch.int16).cpu().numpy().view(np.uint16)
+    blocks = blocks.reshape(s.heads, nq, nk)
+    counts = b.buf(h3.H3_MXWS_COUNTS, s.heads * nq * 4).view(torch.int32).cpu().numpy().reshape(s.heads, nq)
+    scores = O.sparse_block_scores(ref["q"][:V], ref["k"][:V], V, P, s.heads, 128)
+    _, thr = O.sparse_select(scores, tau)
+    ok = np.ones(V, dtype=bool)
+    for h in range(s.heads):
+        sl = slice(h * 128, (h + 1) * 128)
+        for bq in range(nq):
+            got = np.zeros(nk, dtype=bool)
+            got[blocks[h, bq, :counts[h, bq]].astype(np.int64)] = True
+            diff = np.nonzero(got != ref["sparse_sel"][h, bq])[0]
+            if len(diff):
+                a, e = P + 256 * bq, min(P + 256 * (bq + 1), V)
+                qbar = np.abs(ref["q"][a:e, sl].mean(0))
+                A = max(np.sum(qbar * np.abs(ref["k"][P + 64 * j:min(P + 64 * j + 64, V), sl].mean(0)))
+                        for j in range(nk)) / np.sqrt(128)
+                assert np.all(np.abs(scores[h, bq, diff] - thr[h, bq]) <= 8e-3 * A), (h, bq, diff)
+                ok[a:e] = False
+    _say(f"  selection differs on {np.count_nonzero(~ok)} of {V - P} target rows")
+    for name, got, r in (("o", f64(b.bf16(h3.H3_MXWS_O, H)), ref["o"]), ("x1", f64(b.bf16(h3.H3_MXWS_X1, H)), ref["x1"]),
+                         ("y", f64(y), ref["y"])):
+        assert_parity(got[:V][ok], r[:V][ok], name)
+    assert_zero_rows(y, V, "y")

@@ -135,15 +135,15 @@ extern "C" int h3_block_forward_sparse(const h3_dims *dims, const h3_block_weigh
 // output projection, by a quantization of the BF16 attention output.
 extern "C" int h3_block_forward_mxfp8(const h3_dims *dims, const h3_block_weights_mxfp8 *w, const uint16_t *x,
                                       uint16_t *y, const float *mod, int32_t n_mod_groups, const int32_t *mod_idx,
-                                      const int32_t *pos, int64_t L_buf, int64_t valid_len, void *workspace,
-                                      size_t ws_bytes, void *stream) {
-    int s = h3_check_block_forward_mxfp8(dims, w, x, y, mod, n_mod_groups, mod_idx, pos, L_buf, valid_len, workspace,
-                                         ws_bytes);
+                                      const int32_t *pos, int64_t L_buf, int64_t valid_len, int64_t prefix_len,
+                                      float tau, void *workspace, size_t ws_bytes, void *stream) {
+    int s = h3_check_block_forward_mxfp8(dims, w, x, y, mod, n_mod_groups, mod_idx, pos, L_buf, valid_len, prefix_len,
+                                         tau, workspace, ws_bytes);
     if (s != H3_OK || L_buf == 0) return s;
     if ((s = device_check()) != H3_OK) return s;
     const hipStream_t st = (hipStream_t)stream;
     MxWsLayout l;
-    mx_ws_layout(dims, L_buf, &l);
+    mx_ws_layout(dims, L_buf, valid_len, prefix_len, &l);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     uint8_t *hq = ws + l.off[H3_MXWS_HQ], *hs = ws + l.off[H3_MXWS_HS];
     uint16_t *qkv = reinterpret_cast<uint16_t *>(ws + l.off[H3_MXWS_QKV]);
@@ -169,9 +169,18 @@ extern "C" int h3_block_forward_mxfp8(const h3_dims *dims, const h3_block_weight
     // 3 q~, k~
     launch_qk_norm_rope(qkv, qkv + H, 3 * H, w->q_gain, w->k_gain, pos, L_buf, V, dims->heads, dims->rot_dim,
                         dims->rope_pairing, dims->rope_theta, dims->eps, st);
-    // 4 o, then oq = MXFP8(o)
-    launch_attention(qkv, 3 * H, qkv + H, 3 * H, qkv + 2 * H, 3 * H, o, H, L_buf, V, dims->heads, 0.0f, nullptr, 0,
-                     vt, st);
+    // 4 o (dense, or selection + list-mode attention), then oq = MXFP8(o)
+    if (prefix_len >= 0 && prefix_len < V) {
+        uint16_t *blocks = reinterpret_cast<uint16_t *>(ws + l.off[H3_MXWS_BLOCKS]);
+        int32_t *counts = reinterpret_cast<int32_t *>(ws + l.off[H3_MXWS_COUNTS]);
+        launch_sparse_select(qkv, 3 * H, qkv + H, 3 * H, V, prefix_len, dims->heads, tau, blocks, counts,
+                             ws + l.off[H3_MXWS_SELECT], st);
+        launch_sparse_attention(qkv, 3 * H, qkv + H, 3 * H, qkv + 2 * H, 3 * H, o, H, L_buf, V, prefix_len,
+                                dims->heads, 0.0f, blocks, counts, vt, st);
+    } else {
+        launch_attention(qkv, 3 * H, qkv + H, 3 * H, qkv + 2 * H, 3 * H, o, H, L_buf, V, dims->heads, 0.0f, nullptr,
+                         0, vt, st);
+    }
     launch_mx_quantize(o, H, L_buf, V, H, oq, H, os, st);
     // 5 x1 = x + gate_a * (oq W_o^T)
     launch_linear_mxfp8(oq, H, os, L_buf, w->w_o, H, w->s_o, w->b_o, x1, H, V, H, H, H3_EPI_RESIDUAL, x, H, gate_a,

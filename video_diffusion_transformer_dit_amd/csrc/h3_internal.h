@@ -80,7 +80,9 @@ struct MxWsLayout {
     int64_t off[H3_MXWS_COUNT];
     size_t total;
 };
-bool mx_ws_layout(const h3_dims *d, int64_t L_buf, MxWsLayout *out);
+// prefix_len < 0 (or >= valid_len): dense attention, the selection entries
+// are empty.
+bool mx_ws_layout(const h3_dims *d, int64_t L_buf, int64_t valid_len, int64_t prefix_len, MxWsLayout *out);
 
 // Validation of dims shared by several checks.
 int check_dims(const h3_dims *d);

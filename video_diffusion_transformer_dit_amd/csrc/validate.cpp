@@ -211,16 +211,31 @@ bool block_sparse_layout(const h3_dims *d, int64_t L_buf, int64_t valid_len, int
     return true;
 }
 
-bool mx_ws_layout(const h3_dims *d, int64_t L_buf, MxWsLayout *out) {
+bool mx_ws_layout(const h3_dims *d, int64_t L_buf, int64_t valid_len, int64_t prefix_len, MxWsLayout *out) {
     if (check_dims(d) != H3_OK || L_buf < 0) return false;
     if (d->hidden % 128 != 0 || d->ffn % 128 != 0) return false;
+    if (valid_len < 0 || valid_len > L_buf) return false;
     const int64_t H = d->hidden, F = d->ffn;
     auto align = [](int64_t b) { return (b + (int64_t)kWsAlign - 1) / (int64_t)kWsAlign * (int64_t)kWsAlign; };
     VtPlan p;
     vt_plan(nullptr, 0, L_buf, d->heads, &p);
-    const int64_t bytes[H3_MXWS_COUNT] = {L_buf * H,     L_buf * H / 32, L_buf * 3 * H * 2, L_buf * H * 2,
-                                          L_buf * H,     L_buf * H / 32, L_buf * H * 2,     L_buf * H,
-                                          L_buf * H / 32, L_buf * F,     L_buf * F / 32,    (int64_t)p.bytes};
+    int64_t vt = (int64_t)p.bytes;
+    const bool sparse = prefix_len >= 0 && prefix_len < valid_len;
+    SparseGeom g = {};
+    if (sparse) {
+        h3_qgroup grp;
+        sparse_vt_group(valid_len, prefix_len, &grp);
+        VtPlan ps;
+        vt_plan(&grp, 1, valid_len, d->heads, &ps);
+        vt = std::max<int64_t>(vt, (int64_t)ps.bytes);
+        sparse_geometry(valid_len, prefix_len, d->heads, &g);
+    }
+    const int64_t bytes[H3_MXWS_COUNT] = {L_buf * H,      L_buf * H / 32, L_buf * 3 * H * 2, L_buf * H * 2,
+                                          L_buf * H,      L_buf * H / 32, L_buf * H * 2,     L_buf * H,
+                                          L_buf * H / 32, L_buf * F,      L_buf * F / 32,    vt,
+                                          sparse ? (int64_t)d->heads * g.n_qb * g.n_kb * 2 : 0,
+                                          sparse ? (int64_t)d->heads * g.n_qb * 4 : 0,
+                                          sparse ? (int64_t)g.ws_bytes : 0};
     int64_t off = 0;
     for (int i = 0; i < H3_MXWS_COUNT; ++i) {
         out->off[i] = off;
@@ -844,31 +859,39 @@ int h3_check_fused_modulate_norm_mxfp8(const uint16_t *x, int64_t ld_x, const ui
     return H3_OK;
 }
 
-size_t h3_block_mxfp8_workspace_bytes(const h3_dims *dims, int64_t L_buf) {
+size_t h3_block_mxfp8_workspace_bytes(const h3_dims *dims, int64_t L_buf, int64_t valid_len, int64_t prefix_len) {
     MxWsLayout l;
-    if (!mx_ws_layout(dims, L_buf, &l)) return 0;
+    if (!mx_ws_layout(dims, L_buf, valid_len, prefix_len, &l)) return 0;
     return l.total;
 }
 
-int h3_block_mxfp8_workspace_layout(const h3_dims *dims, int64_t L_buf, int64_t offsets[H3_MXWS_COUNT]) {
+int h3_block_mxfp8_workspace_layout(const h3_dims *dims, int64_t L_buf, int64_t valid_len, int64_t prefix_len,
+                                    int64_t offsets[H3_MXWS_COUNT]) {
     if (offsets == nullptr) return H3_ERR_NULL;
     H3_TRY(check_dims(dims));
-    if (L_buf < 0) return H3_ERR_SHAPE;
+    if (L_buf < 0 || valid_len < 0 || valid_len > L_buf) return H3_ERR_SHAPE;
     MxWsLayout l;
-    if (!mx_ws_layout(dims, L_buf, &l)) return H3_ERR_UNSUPPORTED;
+    if (!mx_ws_layout(dims, L_buf, valid_len, prefix_len, &l)) return H3_ERR_UNSUPPORTED;
     for (int i = 0; i < H3_MXWS_COUNT; ++i) offsets[i] = l.off[i];
     return H3_OK;
 }
 
 int h3_check_block_forward_mxfp8(const h3_dims *dims, const h3_block_weights_mxfp8 *w, const uint16_t *x,
                                  const uint16_t *y, const float *mod, int32_t n_mod_groups, const int32_t *mod_idx,
-                                 const int32_t *pos, int64_t L_buf, int64_t valid_len, const void *workspace,
-                                 size_t ws_bytes) {
+                                 const int32_t *pos, int64_t L_buf, int64_t valid_len, int64_t prefix_len, float tau,
+                                 const void *workspace, size_t ws_bytes) {
     (void)mod_idx;
     (void)pos;
     H3_TRY(check_dims(dims));
     if (dims->hidden % 128 != 0 || dims->ffn % 128 != 0) return H3_ERR_UNSUPPORTED;
     H3_TRY(check_rows(L_buf, valid_len));
+    if (prefix_len >= 0) {
+        if (prefix_len > valid_len) return H3_ERR_SHAPE;
+        const int64_t T = valid_len - prefix_len;
+        if (T > 0 && prefix_len < 1) return H3_ERR_SHAPE;
+        if (T > (int64_t)H3_SPARSE_MAX_KBLOCKS * H3_SPARSE_K_BLOCK) return H3_ERR_UNSUPPORTED;
+        if (!std::isfinite(tau)) return H3_ERR_SHAPE;
+    }
     if (w == nullptr) return H3_ERR_NULL;
     if (L_buf == 0) return H3_OK;
     const int64_t H = dims->hidden, F = dims->ffn, d = dims->head_dim;
@@ -887,7 +910,7 @@ int h3_check_block_forward_mxfp8(const h3_dims *dims, const h3_block_weights_mxf
     for (const uint16_t *p : {w->b_qkv, w->b_o, w->b_up, w->b_down, w->q_gain, w->k_gain})
         if (p && !aligned16(p)) return H3_ERR_ALIGN;
     MxWsLayout l;
-    if (!mx_ws_layout(dims, L_buf, &l)) return H3_ERR_SHAPE;
+    if (!mx_ws_layout(dims, L_buf, valid_len, prefix_len, &l)) return H3_ERR_SHAPE;
     if (workspace == nullptr || ws_bytes < l.total) return H3_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0) return H3_ERR_ALIGN;
     const Mat mx = mat(x, L_buf, H, H), my = mat(y, L_buf, H, H);

@@ -20,8 +20,8 @@ H3_EPI_STORE, H3_EPI_RESIDUAL, H3_EPI_SWIGLU = range(3)
 H3_WS_H, H3_WS_QKV, H3_WS_O, H3_WS_X1, H3_WS_H2, H3_WS_G, H3_WS_VT = range(7)
 H3_WS_COUNT = 7
 H3_MXWS_HQ, H3_MXWS_HS, H3_MXWS_QKV, H3_MXWS_O, H3_MXWS_OQ, H3_MXWS_OS, H3_MXWS_X1, H3_MXWS_H2Q, H3_MXWS_H2S, \
-    H3_MXWS_GQ, H3_MXWS_GS, H3_MXWS_VT = range(12)
-H3_MXWS_COUNT = 12
+    H3_MXWS_GQ, H3_MXWS_GS, H3_MXWS_VT, H3_MXWS_BLOCKS, H3_MXWS_COUNTS, H3_MXWS_SELECT = range(15)
+H3_MXWS_COUNT = 15
 H3_MAX_SEGMENTS = 4
 H3_MAX_GROUPS = 8
 H3_SPARSE_Q_BLOCK, H3_SPARSE_K_BLOCK, H3_SPARSE_MAX_KBLOCKS = 256, 64, 4096
@@ -127,12 +127,12 @@ def _load():
                                          I32, P],
         "h3_check_fused_modulate_norm_mxfp8": [P, I64, P, I64, P, P, P, I64, I32, P, I64, P, I64, P, I64, I64, I32,
                                                F32, I32],
-        "h3_block_forward_mxfp8": [C.POINTER(Dims), C.POINTER(BlockWeightsMx), P, P, P, I32, P, P, I64, I64, P, SZ,
-                                   P],
-        "h3_check_block_forward_mxfp8": [C.POINTER(Dims), C.POINTER(BlockWeightsMx), P, P, P, I32, P, P, I64, I64, P,
-                                         SZ],
-        "h3_block_mxfp8_workspace_bytes": [C.POINTER(Dims), I64],
-        "h3_block_mxfp8_workspace_layout": [C.POINTER(Dims), I64, C.POINTER(I64)],
+        "h3_block_forward_mxfp8": [C.POINTER(Dims), C.POINTER(BlockWeightsMx), P, P, P, I32, P, P, I64, I64, I64,
+                                   F32, P, SZ, P],
+        "h3_check_block_forward_mxfp8": [C.POINTER(Dims), C.POINTER(BlockWeightsMx), P, P, P, I32, P, P, I64, I64,
+                                         I64, F32, P, SZ],
+        "h3_block_mxfp8_workspace_bytes": [C.POINTER(Dims), I64, I64, I64],
+        "h3_block_mxfp8_workspace_layout": [C.POINTER(Dims), I64, I64, I64, C.POINTER(I64)],
         "h3_status_string": [C.c_int],
         "h3_abi_version": [],
     }
@@ -430,19 +430,23 @@ def make_weights_mx(wq: dict) -> BlockWeightsMx:
     return BlockWeightsMx(**f)
 
 
-def block_mxfp8_workspace_bytes(dims: Dims, L_buf: int) -> int:
-    return int(LIB.h3_block_mxfp8_workspace_bytes(C.byref(dims), L_buf))
+def block_mxfp8_workspace_bytes(dims: Dims, L_buf: int, valid_len=None, prefix_len: int = -1) -> int:
+    valid_len = L_buf if valid_len is None else valid_len
+    return int(LIB.h3_block_mxfp8_workspace_bytes(C.byref(dims), L_buf, valid_len, prefix_len))
 
 
-def block_mxfp8_workspace_layout(dims: Dims, L_buf: int):
+def block_mxfp8_workspace_layout(dims: Dims, L_buf: int, valid_len=None, prefix_len: int = -1):
+    valid_len = L_buf if valid_len is None else valid_len
     off = (C.c_int64 * H3_MXWS_COUNT)()
-    _ok(LIB.h3_block_mxfp8_workspace_layout(C.byref(dims), L_buf, off), "h3_block_mxfp8_workspace_layout")
+    _ok(LIB.h3_block_mxfp8_workspace_layout(C.byref(dims), L_buf, valid_len, prefix_len, off),
+        "h3_block_mxfp8_workspace_layout")
     return list(off)
 
 
 def block_forward_mxfp8(dims: Dims, weights: BlockWeightsMx, x, y, mod, n_mod_groups, valid_len, workspace,
-                        mod_idx=None, pos=None, stream=None):
+                        mod_idx=None, pos=None, prefix_len: int = -1, tau: float = 0.0, stream=None):
+    """prefix_len < 0: dense attention; else Sol-Attn block-sparse attention with threshold tau."""
     s = LIB.h3_block_forward_mxfp8(C.byref(dims), C.byref(weights), _ptr(x), _ptr(y), _ptr(mod), n_mod_groups,
-                                   _ptr(mod_idx), _ptr(pos), x.shape[0], valid_len, _ptr(workspace),
-                                   workspace.numel() * workspace.element_size(), _stream(stream))
+                                   _ptr(mod_idx), _ptr(pos), x.shape[0], valid_len, prefix_len, float(tau),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _ok(s, "h3_block_forward_mxfp8")
