@@ -447,9 +447,9 @@ def main(argv=None) -> int:
         "attention_tflops": round(attn_tf, 1),
         "gemm_tflops": round(gemm_f / (gemm_ms * 1e-3) / 1e12, 1),
         "kernels": kernels,
-        "roofline": {"kernel": "attention_fwd_kernel<false> (dense)", "bound": "mfma", "achieved": round(attn_tf, 1),
+        "roofline": {"kernel": "attention_fwd_kernel<false, true> (dense, fixed softmax reference)", "bound": "mfma", "achieved": round(attn_tf, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": counter_traffic("void attention_fwd_kernel<false>", "attention.hip"),
+                     "traffic": counter_traffic("void attention_fwd_kernel<false, true>", "attention.hip"),
                      "traffic_unit": "bytes per launch (FETCH_SIZE x2 + WRITE_SIZE x1, copy-calibrated)",
                      "work_per_launch": "4 * 58758^2 * 5376 = 7.424e13 flop (QK^T and PV over valid rows)"},
     }

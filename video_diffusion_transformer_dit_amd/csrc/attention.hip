@@ -674,29 +674,45 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
 
 // Largest squared key norm per head over rows [0, rows) of k, merged into
 // kmax2[head] (non-negative FP32 bit patterns compare like unsigned integers,
-// so an integer atomic maximum merges them). 16 lanes per 128-channel key,
-// 256 rows per workgroup, one atomic per wave.
-__global__ __launch_bounds__(256) void key_norm_max_kernel(const uint16_t *k, int64_t ld, int64_t rows,
+// so an integer atomic maximum merges them). A workgroup owns 64 whole rows;
+// thread t takes the 16-byte chunks t, t + 256, ... of every row, so the
+// loads are coalesced across all heads, and the 16 chunks of one head are 16
+// consecutive lanes. One atomic per head and workgroup.
+constexpr int kNormRows = 64;
+__global__ __launch_bounds__(256) void key_norm_max_kernel(const uint16_t *k, int64_t ld, int64_t rows, int32_t heads,
                                                            uint32_t *kmax2) {
-    const int head = blockIdx.y;
-    const int t = threadIdx.x, c = t & 15;
-    const int64_t r_end = min<int64_t>((int64_t)(blockIdx.x + 1) * 256, rows);
-    float m = 0.f;
-    for (int64_t r = (int64_t)blockIdx.x * 256 + (t >> 4); r < r_end; r += 16) {
-        float f[8];
-        unpack8(*reinterpret_cast<const uint4 *>(k + r * ld + head * D + 8 * c), f);
-        float s2 = 0.f;
+    const int t = threadIdx.x;
+    const int nch = heads * 16;
+    const int64_t r0 = (int64_t)blockIdx.x * kNormRows;
+    const int nr = (int)min<int64_t>(kNormRows, rows - r0);
+    for (int c = t; c < nch; c += 256) {
+        const uint16_t *p = k + r0 * ld + 8 * c;
+        float m = 0.f;
+        int r = 0;
+        for (; r + 4 <= nr; r += 4) {
+            uint4 u[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s2 = __builtin_fmaf(f[e], f[e], s2);
-        s2 += __shfl_xor(s2, 8);
-        s2 += __shfl_xor(s2, 4);
-        s2 += __shfl_xor(s2, 2);
-        s2 += __shfl_xor(s2, 1);
-        m = fmaxf(m, s2);
+            for (int i = 0; i < 4; ++i) u[i] = *reinterpret_cast<const uint4 *>(p + (int64_t)(r + i) * ld);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float f[8];
+                unpack8(u[i], f);
+                float s2 = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s2 = __builtin_fmaf(f[e], f[e], s2);
+                m = fmaxf(m, sum16(s2));
+            }
+        }
+        for (; r < nr; ++r) {
+            float f[8];
+            unpack8(*reinterpret_cast<const uint4 *>(p + (int64_t)r * ld), f);
+            float s2 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s2 = __builtin_fmaf(f[e], f[e], s2);
+            m = fmaxf(m, sum16(s2));
+        }
+        if ((c & 15) == 0) atomicMax(kmax2 + (c >> 4), __float_as_uint(m));
     }
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
-    if ((t & 63) == 0) atomicMax(kmax2 + head, __float_as_uint(m));
 }
 
 // V -> V^T staging for one segment: tile of 64 keys x 128 channels of one head
@@ -744,8 +760,8 @@ void stage_vt(const VtPlan &plan, const uint16_t *k, int64_t ld_k, const uint16_
     for (int i = 0; i < plan.n; ++i) {
         const VtSeg &e = plan.seg[i];
         const uint16_t *ks = e.own ? k + e.begin * ld_k : e.k + e.begin * e.ld;
-        key_norm_max_kernel<<<dim3((unsigned)((e.len + 255) / 256), (unsigned)heads), 256, 0, stream>>>(
-            ks, e.own ? ld_k : e.ld, e.len, kmax2);
+        key_norm_max_kernel<<<dim3((unsigned)((e.len + kNormRows - 1) / kNormRows)), 256, 0, stream>>>(
+            ks, e.own ? ld_k : e.ld, e.len, heads, kmax2);
     }
     for (int i = 0; i < plan.n; ++i) {
         const VtSeg &e = plan.seg[i];
