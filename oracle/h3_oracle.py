@@ -399,7 +399,10 @@ def sparse_attention(q, k, v, valid_len: int, prefix_len: int, heads: int, head_
 #   M5 in the block, the quantizing producers quantize their exact outputs
 #      (h, h2 from the norm, g from SwiGLU), with no BF16 step in between;
 #      the attention output o is quantized from its BF16 value, since the
-#      attention kernel returns BF16.
+#      attention kernel returns BF16, and the residual stream x1 is taken at
+#      its BF16 value (the block stores it in BF16) before the FFN-side norm
+#      and residual. Quantization turns a last-bit difference of its input into
+#      a whole E4M3 step, so these storage points are part of the definition.
 # ----------------------------------------------------------------------------
 MX_BLOCK = 32
 E4M3_MAX = 448.0
@@ -582,6 +585,8 @@ def block_forward(x, w, mod, *, heads: int, head_dim: int, ffn: int, valid_len: 
     else:
         a = linear(o, w['w_o'], w.get('b_o'))
     x1 = rnd(gated_residual(xv, m[:, GATE_A], a))
+    if mxfp8:
+        x1 = round_to_bf16(x1)
     h2_exact = modulate_norm(x1, m[:, SHIFT_F], m[:, SCALE_F], eps, norm_type)
     h2 = rnd(h2_exact)
     if mxfp8:
@@ -611,7 +616,8 @@ def block_forward(x, w, mod, *, heads: int, head_dim: int, ffn: int, valid_len: 
 
 def block_forward_rows(x, w, mod, rows, *, heads: int, head_dim: int, ffn: int, valid_len: int,
                        rot_dim: int = 64, theta: float = 10000.0, eps: float = 1e-6, norm_type: int = 0,
-                       pairing: int = 0, mod_idx=None, pos=None, groups=None, scale=None, q_chunk: int = 64):
+                       pairing: int = 0, mod_idx=None, pos=None, groups=None, scale=None, q_chunk: int = 64,
+                       mxfp8: bool = False):
     """block_forward restricted to the selected valid rows.
 
     Attention reads the keys and values of every valid row, so h, k~ and v are
@@ -620,7 +626,9 @@ def block_forward_rows(x, w, mod, rows, *, heads: int, head_dim: int, ffn: int, 
     definitions are those of block_forward, step for step, including its
     grouped attention (`groups` as in block_forward: a selected row attends
     over the segments of the group that contains it; a row outside every
-    group gets o = 0). Returns a dict of [len(rows), .] arrays."""
+    group gets o = 0). With mxfp8, the projections take MXFP8 operands at the
+    quantization points of block_forward's mxfp8 option. Returns a dict of
+    [len(rows), .] arrays."""
     x = np.asarray(x, dtype=F64)
     H = x.shape[1]
     V = int(valid_len)
@@ -630,6 +638,13 @@ def block_forward_rows(x, w, mod, rows, *, heads: int, head_dim: int, ffn: int, 
 
     h_all = modulate_norm(x[:V], m_all[:, SHIFT_A], m_all[:, SCALE_A], eps, norm_type)
     w_qkv = np.asarray(w['w_qkv'], dtype=F64)
+    if mxfp8:
+        mxq = lambda t: mx_dequantize(*mx_quantize(t))
+        w = dict(w)
+        w_qkv = mxq(w_qkv)
+        for k_ in ('w_o', 'w_up', 'w_down'):
+            w[k_] = mxq(np.asarray(w[k_], dtype=F64))
+        h_all = mxq(h_all)
     b_qkv = w.get('b_qkv')
     b = (lambda i: None) if b_qkv is None else (lambda i: np.asarray(b_qkv, dtype=F64)[i * H:(i + 1) * H])
     k_all = linear(h_all, w_qkv[H:2 * H], b(1))
@@ -659,11 +674,13 @@ def block_forward_rows(x, w, mod, rows, *, heads: int, head_dim: int, ffn: int, 
                     vs.append(np.asarray(sg[1], dtype=F64))
             o[sel] = attention(qn[sel], np.concatenate(ks, axis=0), np.concatenate(vs, axis=0), heads, head_dim,
                                scale, q_chunk)
-    a = linear(o, w['w_o'], w.get('b_o'))
+    a = linear(mxq(round_to_bf16(o)) if mxfp8 else o, w['w_o'], w.get('b_o'))
     x1 = gated_residual(x[rows], m[:, GATE_A], a)
+    if mxfp8:
+        x1 = round_to_bf16(x1)
     h2 = modulate_norm(x1, m[:, SHIFT_F], m[:, SCALE_F], eps, norm_type)
-    u = linear(h2, w['w_up'], w.get('b_up'))
+    u = linear(mxq(h2) if mxfp8 else h2, w['w_up'], w.get('b_up'))
     g = swiglu(u, ffn)
-    f = linear(g, w['w_down'], w.get('b_down'))
+    f = linear(mxq(g) if mxfp8 else g, w['w_down'], w.get('b_down'))
     y = gated_residual(x1, m[:, GATE_F], f)
     return dict(h=h, q=qn, k=kn[rows], v=v_all[rows], o=o, a=a, x1=x1, h2=h2, g=g, f=f, y=y)

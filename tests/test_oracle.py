@@ -792,3 +792,13 @@ def test_block_mxfp8_structure():
     rel_y = np.linalg.norm(mx["y"][:V] - ex["y"][:V]) / np.linalg.norm(ex["y"][:V])
     assert rel_y < 0.05
     assert np.all(mx["y"][V:] == 0)
+
+
+def test_block_rows_mxfp8_equals_full_mxfp8_block_at_those_rows():
+    s, w, x, mod, kw = _tiny_inputs()
+    V = s.valid_len
+    full = O.block_forward(x, w, mod, valid_len=V, mxfp8=True, **kw)
+    rows = np.array([0, 5, 63, 64, 200, 383, V - 1])
+    part = O.block_forward_rows(x, w, mod, rows, valid_len=V, mxfp8=True, **kw)
+    for name in ("q", "k", "v", "o", "x1", "g", "y"):
+        np.testing.assert_allclose(part[name], full[name][rows], rtol=1e-10, atol=1e-11)
