@@ -239,11 +239,12 @@ def _check_mx_against(got_codes, got_scales, exact, name, max_frac=1e-3):
     return got
 
 
-@pytest.mark.parametrize("H,L,V,branch", [(256, 300, 291, False), (5376, 70, 67, True), (1024, 64, 64, True)])
-def test_modnorm_mxfp8_producer(H, L, V, branch):
+@pytest.mark.parametrize("H,L,V,branch,norm", [(256, 300, 291, False, 0), (5376, 70, 67, True, 0), (1024, 64, 64, True, 0),
+                                                (512, 40, 37, True, 1)])
+def test_modnorm_mxfp8_producer(H, L, V, branch, norm):
     """The fused quantizing producer: MXFP8 h from the norm's FP32 values; the
     optional residual x1 is bit-identical to the plain kernel's."""
-    _say(f"modnorm_mxfp8 H={H} L={L} V={V} branch={branch}")
+    _say(f"modnorm_mxfp8 H={H} L={L} V={V} branch={branch} norm={norm}")
     G = 3
     xb = I.normal_bf16("mnx.x", (L, H))
     bb = I.normal_bf16("mnx.b", (L, H))
@@ -256,19 +257,19 @@ def test_modnorm_mxfp8_producer(H, L, V, branch):
     if branch:
         x1 = poison((L, H))
         kw = dict(branch=dev_bf16(bb), gate=md[:, 2], x1_out=x1)
-    h3.fused_modulate_norm_mxfp8(x, md[:, 0], md[:, 1], hq, hs, V, ld_mod_group=6 * H, n_mod_groups=G, mod_idx=ix,
-                                 **kw)
+    h3.fused_modulate_norm_mxfp8(x, md[:, 0], md[:, 1], hq, hs, V, norm_type=norm, ld_mod_group=6 * H, n_mod_groups=G,
+                                 mod_idx=ix, **kw)
     torch.cuda.synchronize()
     m = O.gather_mod(mod.astype(np.float64), idx, V)
     xv = O.bf16_to_f64(xb[:V])
     if branch:
         x1_ref, h_ref = poison((L, H)), poison((L, H))
-        h3.fused_modulate_norm(x, md[:, 0], md[:, 1], h_ref, V, branch=dev_bf16(bb), gate=md[:, 2], x1_out=x1_ref,
-                               ld_mod_group=6 * H, n_mod_groups=G, mod_idx=ix)
+        h3.fused_modulate_norm(x, md[:, 0], md[:, 1], h_ref, V, norm_type=norm, branch=dev_bf16(bb), gate=md[:, 2],
+                               x1_out=x1_ref, ld_mod_group=6 * H, n_mod_groups=G, mod_idx=ix)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(x1.view(torch.int16).cpu().numpy(), x1_ref.view(torch.int16).cpu().numpy())
         xv = f64(x1)[:V]
-    exact = O.modulate_norm(xv, m[:, O.SHIFT_A], m[:, O.SCALE_A], 1e-6, 0)
+    exact = O.modulate_norm(xv, m[:, O.SHIFT_A], m[:, O.SCALE_A], 1e-6, norm)
     got = _check_mx_against(hq.cpu().numpy()[:V], hs.cpu().numpy()[:, :V], exact, "hq")
     # the quantization error itself: below E4M3's relative step on average; a
     # group's largest element may saturate (448 of up to 512), so no max bound
