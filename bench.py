@@ -314,6 +314,106 @@ def mxfp8_gemms(torch, h3, dev, w, bufs, mod, L, V, H, F, bf16_ms, iters, dims, 
     return out
 
 
+def progress(msg: str) -> None:
+    """One line on stderr per finished section (stdout carries only the JSON)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def streaming_chunk(torch, h3, dev, gen, dims, weights, H, heads, F, iters):
+    """The chunked streaming variant at full width: a current chunk of
+    [cond 256 | audio 128 | video 5 x 1,008] rows whose video queries also
+    attend to 15,120 history rows of K/V; cond and audio attend over the
+    current chunk only. One chunk is 4 denoise forwards plus 1 refresh forward
+    that exports the video rows' k~ and v. Also times the grouped attention
+    alone (2.27 TFLOP per forward)."""
+    cond, audio, video, hist = 256, 128, 5040, 15120
+    L = cond + audio + video
+    x = torch.randn((L, H), generator=gen, device=dev).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    hk = torch.randn((hist, H), generator=gen, device=dev).to(torch.bfloat16)
+    hv = torch.randn((hist, H), generator=gen, device=dev).to(torch.bfloat16)
+    mod = (0.1 * torch.randn((1, 6, H), generator=gen, device=dev)).float()
+    ek = torch.empty((video, H), dtype=torch.bfloat16, device=dev)
+    ev = torch.empty_like(ek)
+    cur = ("self", 0, L)
+    groups = [(0, cond, [cur]), (cond, cond + audio, [cur]), (cond + audio, L, [(hk, hv, 0, hist), cur])]
+    pos = (torch.arange(L, device=dev) + hist).to(torch.int32)
+    ws = torch.empty(h3.workspace_bytes(dims, L, groups), dtype=torch.uint8, device=dev)
+
+    def chunk():
+        for _ in range(4):
+            h3.block_forward(dims, weights, x, y, mod, 1, L, ws, groups=groups, pos=pos)
+        h3.block_forward(dims, weights, x, y, mod, 1, L, ws, groups=groups, pos=pos,
+                         kv_export=(ek, ev, cond + audio, video))
+
+    chunk_ms = time_calls(torch, chunk, iters, 1)
+    off, lds = h3.workspace_layout(dims, L, groups)
+    qkv = ws[off[h3.H3_WS_QKV]:off[h3.H3_WS_QKV] + L * 3 * H * 2].view(torch.bfloat16).view(L, 3 * H)
+    o = ws[off[h3.H3_WS_O]:off[h3.H3_WS_O] + L * H * 2].view(torch.bfloat16).view(L, H)
+    aws = torch.empty(h3.attention_workspace_bytes(L, heads, groups), dtype=torch.uint8, device=dev)
+    attn_ms = time_calls(torch, lambda: h3.attention(qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:], o, L, heads,
+                                                     groups=groups, workspace=aws), iters, 1)
+    attn_f = 4.0 * H * (video * (hist + L) + (cond + audio) * L)
+    gemm_f = 2.0 * L * H * (4 * H + 3 * F)
+    fwd_ms = chunk_ms / 5
+    del ws, aws, x, y, hk, hv
+    return {"workload": "streaming chunk [cond 256 | audio 128 | video 5 x 1,008] over 15,120 history rows, "
+                        "4 denoise + 1 refresh forward (one block)",
+            "chunk_ms": round(chunk_ms, 3), "forward_ms": round(fwd_ms, 3),
+            "forward_tflops": round((gemm_f + attn_f) / (fwd_ms * 1e-3) / 1e12, 1),
+            "grouped_attention": {"ms": round(attn_ms, 4), "tflop": round(attn_f / 1e12, 3),
+                                  "tflops": round(attn_f / (attn_ms * 1e-3) / 1e12, 1),
+                                  "frac_mfma": round(attn_f / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}}
+
+
+def stacked_denoise(torch, h3, dev, dims, x, L, V, H, F, n_blocks=50, n_steps=4):
+    """The stacked denoise loop: n_blocks random-init blocks (46 GB of BF16
+    weights at 50) resident at once, n_steps denoising steps at the
+    benchmarked sequence, each step one h3_stack_forward over all blocks with
+    that step's slice of an FP32 AdaLN table [blocks][steps][6][H]. Reports
+    DiT forwards per second (one forward = all blocks once) over the whole
+    loop, timed once after a one-block warmup."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(SEED + 1)
+
+    def draw(shape, std, mean=0.0):
+        t = torch.randn(shape, generator=g, device=dev, dtype=torch.float32).mul_(std)
+        if mean:
+            t.add_(mean)
+        return t.to(torch.bfloat16)
+
+    blocks = [{"w_qkv": draw((3 * H, H), 0.02), "w_o": draw((H, H), 0.02), "w_up": draw((2 * F, H), 0.02),
+               "w_down": draw((H, F), 0.02), "q_gain": draw((128,), 0.02, 1.0), "k_gain": draw((128,), 0.02, 1.0)}
+              for _ in range(n_blocks)]
+    wbytes = sum(t.numel() * 2 for b in blocks for t in b.values())
+    arr = h3.make_weight_stack([h3.make_weights(b) for b in blocks])
+    mod = (0.1 * torch.randn((n_blocks, n_steps, 6, H), generator=g, device=dev)).float()
+    ws = torch.empty(h3.workspace_bytes(dims, L), dtype=torch.uint8, device=dev)
+    xs = x.clone()
+    ld_blk = n_steps * 6 * H
+    h3.stack_forward(dims, h3.make_weight_stack([h3.make_weights(blocks[0])]), xs, mod[0, 0], 0, 1, V, ws)
+    xs.copy_(x)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for s in range(n_steps):
+        h3.stack_forward(dims, arr, xs, mod[0, s], ld_blk, 1, V, ws)
+    t1.record()
+    torch.cuda.synchronize()
+    loop_ms = t0.elapsed_time(t1)
+    gemm_f, attn_f = block_flops(V, H, F)
+    per_block = loop_ms / (n_blocks * n_steps)
+    out = {"workload": f"{n_blocks} resident blocks, {n_steps} denoising steps, 58,758 valid tokens in 58,816",
+           "resident_weight_gb": round(wbytes / 1e9, 2), "loop_s": round(loop_ms / 1e3, 3),
+           "dit_forwards_per_s": round(n_steps / (loop_ms * 1e-3), 4), "ms_per_block": round(per_block, 3),
+           "tflops": round((gemm_f + attn_f) / (per_block * 1e-3) / 1e12, 1),
+           "finite": bool(torch.isfinite(xs[:V].float()).all().item())}
+    del blocks, ws, xs, mod
+    torch.cuda.empty_cache()
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -323,6 +423,8 @@ def main(argv=None) -> int:
     ap.add_argument("--kernel-iters", type=int, default=5)
     ap.add_argument("--no-next", action="store_true",
                     help="skip the measurements of the rows beyond the block (LoRA consumer fusion)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (streaming chunk, 50-block stacked denoise loop)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (the known-size reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -367,6 +469,7 @@ def main(argv=None) -> int:
         h3.block_forward(dims, weights, x, y, mod, 1, V, ws)
 
     ms, step_ms = time_calls(torch, step, a.steps, a.warmup, per_call=True)
+    progress(f"block timed: {ms:.3f} ms over {a.steps} steps")
 
     # Per-kernel breakdown: the block's launches, one at a time, same buffers.
     hbuf, qkv, o, x1, h2, g = (wsv(h3.H3_WS_H, H), wsv(h3.H3_WS_QKV, 3 * H), wsv(h3.H3_WS_O, H),
@@ -389,6 +492,7 @@ def main(argv=None) -> int:
     k_ms["gemm_down_residual"] = time_calls(torch, lambda: h3.linear(
         g, w["w_down"], y, V, h3.H3_EPI_RESIDUAL, resid=x1, gate=mod[:, 5], ld_gate_group=6 * H), kit, 1)
 
+    progress("per-kernel breakdown timed")
     # Measured ceilings on this GPU: a plain device copy (what the memory-bound
     # kernels can hope for) and the vendor library's BF16 GEMM on the QKV shape
     # (hipBLASLt through torch.matmul, no epilogue).
@@ -453,14 +557,24 @@ def main(argv=None) -> int:
                      "traffic_unit": "bytes per launch (FETCH_SIZE x2 + WRITE_SIZE x1, copy-calibrated)",
                      "work_per_launch": "4 * 58758^2 * 5376 = 7.424e13 flop (QK^T and PV over valid rows)"},
     }
+    if not a.no_configs:
+        out["configs"] = {"streaming_chunk": streaming_chunk(torch, h3, dev, gen, dims, weights, H, heads, F, kit)}
+        progress("streaming chunk timed")
     if not a.no_next:
         out["next"] = {"lora_consumer_fusion": lora_consumers(torch, h3, dev, gen, L, V, H, heads, F, kit)}
+        progress("LoRA consumer fusion timed")
         out["next"]["block_sparse_attention"] = block_sparse(torch, h3, dev, qkv[:, :H], qkv[:, H:2 * H],
                                                              qkv[:, 2 * H:], o, V, heads, k_ms["attention"], kit,
                                                              (dims, weights, x, y, mod, ms))
+        progress("block-sparse attention timed")
         out["next"]["mxfp8_gemms"] = mxfp8_gemms(torch, h3, dev, w, (hbuf, o, x, x1, h2, g, y), mod, L, V, H, F,
                                                  k_ms, kit, dims, ms)
+        progress("MXFP8 GEMMs timed")
         out["next"]["reference_kv_cache"] = reference_kv_cache(torch, h3, dev, dims, weights, mod, gen, L, V, H)
+        progress("reference K/V caching timed")
+    if not a.no_configs:
+        out["configs"]["stacked_denoise"] = stacked_denoise(torch, h3, dev, dims, x, L, V, H, F)
+        progress("stacked denoise loop timed")
     if a.calibration_copy:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)   # 1 GiB
         dst = torch.empty_like(src)
@@ -470,6 +584,7 @@ def main(argv=None) -> int:
         out["calibration_copy_bytes"] = int(src.numel() * 2)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
+        progress("CPU oracle sample timed")
     print(json.dumps(out), flush=True)
     return 0
 

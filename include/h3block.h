@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define H3_ABI_VERSION 3
+#define H3_ABI_VERSION 4
 #define H3_MAX_SEGMENTS 4   /* K/V segments per query group */
 #define H3_MAX_GROUPS 8     /* query groups per attention call */
 #define H3_SPARSE_Q_BLOCK 256      /* block-sparse attention: target query block rows */
@@ -167,6 +167,32 @@ int h3_block_forward(const h3_dims *dims, const h3_block_weights *w,
                      const int32_t *pos, int64_t L_buf, int64_t valid_len,
                      const h3_qgroup *groups, int32_t n_groups,
                      const h3_kv_export *kv_export,
+                     void *workspace, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * h3_stack_forward - n_blocks DiT blocks applied in order to one packed
+ * sequence, in place: x <- block_{n-1}( ... block_1(block_0(x)) ), each block
+ * exactly as h3_block_forward with dense attention over [0, valid_len). This
+ * is one denoiser forward of a step; the step's modulation comes from the
+ * precomputed AdaLN table cached per (block, step) ([Sol-H3] §4.1 "AdaLN
+ * precompute"), of which the caller passes the step's slice.
+ *
+ * w        [n_blocks] weight sets (block b uses w[b]).
+ * x        [L_buf, hidden], ld = hidden; input and, on return, output.
+ * mod      block b reads its FP32 table [n_mod_groups, 6, hidden] at
+ *          mod + b * ld_mod_block (floats); ld_mod_block >= 0 and a multiple
+ *          of 4 (16-byte aligned tables). For a table [blocks][steps][6][H],
+ *          step s passes mod + s * 6H and ld_mod_block = steps * 6H.
+ * mod_idx, pos, L_buf, valid_len: as h3_block_forward, shared by every block.
+ * workspace h3_block_workspace_bytes(dims, L_buf, NULL, 0) bytes, reused by
+ *          every block; on return it holds the last block's intermediates.
+ * Every block's arguments are checked before the first launch, so a rejected
+ * call writes nothing. n_blocks == 0 returns H3_OK without work.
+ * ------------------------------------------------------------------------- */
+int h3_stack_forward(const h3_dims *dims, const h3_block_weights *w, int32_t n_blocks,
+                     uint16_t *x, const float *mod, int64_t ld_mod_block,
+                     int32_t n_mod_groups, const int32_t *mod_idx,
+                     const int32_t *pos, int64_t L_buf, int64_t valid_len,
                      void *workspace, size_t ws_bytes, void *stream);
 
 /* Workspace size of h3_block_forward for L_buf rows and the given query groups
@@ -532,6 +558,11 @@ int h3_check_block_forward(const h3_dims *dims, const h3_block_weights *w,
                            const int32_t *pos, int64_t L_buf, int64_t valid_len,
                            const h3_qgroup *groups, int32_t n_groups,
                            const h3_kv_export *kv_export,
+                           const void *workspace, size_t ws_bytes);
+int h3_check_stack_forward(const h3_dims *dims, const h3_block_weights *w, int32_t n_blocks,
+                           const uint16_t *x, const float *mod, int64_t ld_mod_block,
+                           int32_t n_mod_groups, const int32_t *mod_idx,
+                           const int32_t *pos, int64_t L_buf, int64_t valid_len,
                            const void *workspace, size_t ws_bytes);
 int h3_check_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k,
                        const uint16_t *v, int64_t ld_v, const uint16_t *o, int64_t ld_o,

@@ -134,6 +134,33 @@ def test_block_validator_accepts_good_call_and_rejects_bad():
     assert check_block(*_block_args(d=d)) == h3.H3_ERR_UNSUPPORTED
 
 
+def test_stack_validator_checks_every_block_before_any_launch():
+    d, L, V = TINY, 512, 500
+    good = h3.BlockWeights(addr(1), None, addr(2), addr(2) + 4096, addr(3), None, addr(4), None, addr(5), None)
+    bad = h3.BlockWeights(addr(1), None, addr(2), addr(2) + 4096, None, None, addr(4), None, addr(5), None)
+    ws_bytes = h3.workspace_bytes(d, L)
+    x, mod, ws = addr(6), addr(8), addr(10)
+    ld_tbl = 4 * 6 * d.hidden            # a [blocks][4 steps][6][H] table
+
+    def chk(ws_list, ld=ld_tbl, x_=x, mod_=mod, n=None, wsb=ws_bytes):
+        arr = h3.make_weight_stack(ws_list) if ws_list else None
+        n = len(ws_list) if n is None else n
+        return h3.LIB.h3_check_stack_forward(C.byref(d), arr, n, x_, mod_, ld, 1, None, None, L, V, ws, wsb)
+
+    assert chk([good] * 50) == h3.H3_OK
+    assert chk([], n=0) == h3.H3_OK                                    # no blocks: nothing to do
+    assert chk([good] * 49 + [bad]) == h3.H3_ERR_NULL                  # the last block's missing W_o
+    assert chk([good] * 3, ld=-4) == h3.H3_ERR_SHAPE
+    assert chk([good] * 3, ld=6 * d.hidden + 2) == h3.H3_ERR_ALIGN      # tables 16-byte aligned
+    assert chk([good] * 3, ld=0) == h3.H3_OK                           # every block shares one table
+    assert chk([good] * 3, mod_=None) == h3.H3_ERR_NULL
+    assert chk([good] * 3, wsb=ws_bytes - 1) == h3.H3_ERR_WORKSPACE
+    # a later block's table running into x is an alias (x is written in place)
+    assert chk([good] * 3, mod_=addr(6) - 2 * ld_tbl * 4 - 64) == h3.H3_ERR_ALIAS
+    assert chk([good] * 2, mod_=addr(6) - 2 * ld_tbl * 4 - 64) == h3.H3_OK
+    assert chk([good] * 3, n=-1) == h3.H3_ERR_SHAPE
+
+
 def test_block_validator_groups():
     V = 500
     g, n = h3.make_groups([(0, 100, [("self", 0, V)]), (100, V, [("self", 0, 300)])])

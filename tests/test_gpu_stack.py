@@ -1,0 +1,121 @@
+"""The stacked denoise loop: 50 full-width blocks (hidden 5376, 42 x 128 heads,
+F 21504; 46 GB of BF16 weights) resident in HBM at once, run for 4 denoising
+steps, each step reading its own slice of an FP32 AdaLN table cached per
+(block, step) (Sol-H3 report §4.1 "AdaLN precompute"), at 2,048 tokens.
+
+* h3_stack_forward over all 50 blocks equals 50 separate h3_block_forward
+  calls bit for bit, at every step (each step consumes the previous step's
+  output), so the stack applies block b with table (b, step) and nothing else.
+* Per-block parity on 2 seeded-sampled layers at a seeded-sampled step: the
+  resident layer with its (layer, step) table against the FP64 oracle on a
+  seeded input, every intermediate on sampled rows.
+
+The weights are drawn on the GPU with a seeded torch generator (the 46 GB
+would take minutes to draw on the host); the two checked layers are copied
+back for the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import h3_oracle as O
+from video_diffusion_transformer_dit_amd import h3
+from video_diffusion_transformer_dit_amd import inputs as I
+
+from util import BF16_SLACK, assert_parity, bits, dev_bf16, f64
+
+pytestmark = pytest.mark.gpu
+
+N_BLOCKS, N_STEPS, TOKENS = 50, 4, 2048
+H, HEADS, F = 5376, 42, 21504
+
+
+def _draw(gen, shape, std, mean=0.0, dtype=torch.bfloat16):
+    t = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32)
+    t.mul_(std)
+    if mean:
+        t.add_(mean)
+    return t.to(dtype)
+
+
+@pytest.fixture(scope="module")
+def stack():
+    print(f"stack: drawing {N_BLOCKS} full-width blocks on the GPU", flush=True)
+    gen = torch.Generator(device="cuda")
+    blocks = []
+    for b in range(N_BLOCKS):
+        gen.manual_seed(I.MASTER_SEED + 1000 + b)
+        blocks.append({"w_qkv": _draw(gen, (3 * H, H), 0.02), "w_o": _draw(gen, (H, H), 0.02),
+                       "w_up": _draw(gen, (2 * F, H), 0.02), "w_down": _draw(gen, (H, F), 0.02),
+                       "q_gain": _draw(gen, (128,), 0.02, 1.0), "k_gain": _draw(gen, (128,), 0.02, 1.0)})
+    gen.manual_seed(I.MASTER_SEED + 999)
+    mod = _draw(gen, (N_BLOCKS, N_STEPS, 6, H), 0.1, dtype=torch.float32)   # [block][step][6][H]
+    dims = h3.make_dims(H, HEADS, F)
+    wsets = [h3.make_weights(w) for w in blocks]
+    arr = h3.make_weight_stack(wsets)
+    ws = torch.empty(h3.workspace_bytes(dims, TOKENS), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    print(f"stack: {torch.cuda.memory_allocated() / 2**30:.1f} GiB resident", flush=True)
+    yield dict(blocks=blocks, mod=mod, dims=dims, wsets=wsets, arr=arr, ws=ws)
+    del blocks, mod, ws
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+def test_stack_equals_blockwise_calls_bit_for_bit(stack):
+    dims, mod, ws = stack["dims"], stack["mod"], stack["ws"]
+    L, V = TOKENS, TOKENS - 37          # a padding suffix, as in the benchmarked workload
+    x0 = dev_bf16(I.normal_bf16("stack.x0", (L, H)))
+    xa = x0.clone()
+    xb = x0.clone()
+    ld_blk = N_STEPS * 6 * H
+    for s in range(N_STEPS):
+        print(f"  step {s}: stack of {N_BLOCKS} vs {N_BLOCKS} block calls", flush=True)
+        h3.stack_forward(dims, stack["arr"], xa, mod[0, s], ld_blk, 1, V, ws)
+        for b in range(N_BLOCKS):
+            h3.block_forward(dims, stack["wsets"][b], xb, xb, mod[b, s], 1, V, ws)
+        torch.cuda.synchronize()
+        ba, bb = bits(xa), bits(xb)
+        np.testing.assert_array_equal(ba, bb)
+        assert np.all(ba[V:] == 0), "padding rows of the stack's output are not +0.0"
+        assert torch.isfinite(xa[:V].float()).all()
+    # the loop changed x: 200 blocks were applied, not zero
+    assert not np.array_equal(bits(x0)[:V], bits(xa)[:V])
+    # n_blocks == 0 leaves x alone
+    xc = xa.clone()
+    h3.stack_forward(dims, h3.make_weight_stack([]), xc, mod[0, 0], ld_blk, 1, V, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(xc), bits(xa))
+
+
+@pytest.mark.timeout(900)
+def test_stack_sampled_layers_match_oracle(stack):
+    dims, mod, ws = stack["dims"], stack["mod"], stack["ws"]
+    L = V = TOKENS
+    pick = I.rng_for("stack.layers")
+    layers = np.sort(pick.choice(N_BLOCKS, size=2, replace=False))
+    steps = pick.integers(0, N_STEPS, size=2)
+    off, lds = h3.workspace_layout(dims, L)
+
+    def inter(which):
+        return ws[off[which]:off[which] + L * lds[which] * 2].view(torch.bfloat16).view(L, lds[which])
+
+    for layer, step in zip(layers.tolist(), steps.tolist()):
+        print(f"  layer {layer} step {step}: block vs the oracle on sampled rows", flush=True)
+        xb_bits = I.normal_bf16(f"stack.x.{layer}", (L, H))
+        x = dev_bf16(xb_bits)
+        y = torch.full_like(x, float("nan"))
+        # one block of the stack: n_blocks = 1 starting at the layer, out of place via a copy
+        y.copy_(x)
+        h3.stack_forward(dims, h3.make_weight_stack([stack["wsets"][layer]]), y, mod[layer, step], 0, 1, V, ws)
+        torch.cuda.synchronize()
+        w = {k: O.bf16_to_f64(bits(t)) for k, t in stack["blocks"][layer].items()}
+        m = mod[layer, step].double().cpu().numpy()[None]
+        rows = np.unique(np.concatenate([pick.choice(V, size=40, replace=False), [0, V - 1]]))
+        ref = O.block_forward_rows(O.bf16_to_f64(xb_bits), w, m, rows, heads=HEADS, head_dim=128, ffn=F,
+                                   valid_len=V)
+        qkv = f64(inter(h3.H3_WS_QKV)[rows])
+        for name, got in (("h", f64(inter(h3.H3_WS_H)[rows])), ("q", qkv[:, :H]), ("k", qkv[:, H:2 * H]),
+                          ("v", qkv[:, 2 * H:]), ("o", f64(inter(h3.H3_WS_O)[rows])),
+                          ("x1", f64(inter(h3.H3_WS_X1)[rows])), ("h2", f64(inter(h3.H3_WS_H2)[rows])),
+                          ("g", f64(inter(h3.H3_WS_G)[rows])), ("y", f64(y[rows]))):
+            assert_parity(got, ref[name], f"layer {layer} {name}", slack=BF16_SLACK if name == "g" else 0.0)

@@ -113,6 +113,27 @@ extern "C" int h3_block_forward(const h3_dims *dims, const h3_block_weights *w, 
     return launch_status();
 }
 
+// A stack of blocks in place on x: every block's arguments are checked first,
+// then the blocks run one after another on the stream, sharing the workspace
+// (the AdaLN table cached per (block, step), Sol-H3 report §4.1).
+extern "C" int h3_stack_forward(const h3_dims *dims, const h3_block_weights *w, int32_t n_blocks, uint16_t *x,
+                                const float *mod, int64_t ld_mod_block, int32_t n_mod_groups,
+                                const int32_t *mod_idx, const int32_t *pos, int64_t L_buf, int64_t valid_len,
+                                void *workspace, size_t ws_bytes, void *stream) {
+    int s = h3_check_stack_forward(dims, w, n_blocks, x, mod, ld_mod_block, n_mod_groups, mod_idx, pos, L_buf,
+                                   valid_len, workspace, ws_bytes);
+    if (s != H3_OK || L_buf == 0 || n_blocks == 0) return s;
+    if ((s = device_check()) != H3_OK) return s;
+    WsLayout l;
+    ws_layout(dims, L_buf, nullptr, 0, &l);
+    for (int32_t b = 0; b < n_blocks; ++b) {
+        block_steps(dims, w + b, x, x, mod + (int64_t)b * ld_mod_block, n_mod_groups, mod_idx, pos, L_buf,
+                    valid_len, nullptr, 0, nullptr, l, workspace, nullptr, (hipStream_t)stream);
+        if ((s = launch_status()) != H3_OK) return s;
+    }
+    return H3_OK;
+}
+
 extern "C" int h3_block_forward_sparse(const h3_dims *dims, const h3_block_weights *w, const uint16_t *x,
                                        uint16_t *y, const float *mod, int32_t n_mod_groups, const int32_t *mod_idx,
                                        const int32_t *pos, int64_t L_buf, int64_t valid_len, int64_t prefix_len,

@@ -723,6 +723,23 @@ int h3_check_sparse_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k
     return H3_OK;
 }
 
+int h3_check_stack_forward(const h3_dims *dims, const h3_block_weights *w, int32_t n_blocks, const uint16_t *x,
+                           const float *mod, int64_t ld_mod_block, int32_t n_mod_groups, const int32_t *mod_idx,
+                           const int32_t *pos, int64_t L_buf, int64_t valid_len, const void *workspace,
+                           size_t ws_bytes) {
+    H3_TRY(check_dims(dims));
+    H3_TRY(check_rows(L_buf, valid_len));
+    if (n_blocks < 0 || ld_mod_block < 0 || ld_mod_block > (int64_t(1) << 40)) return H3_ERR_SHAPE;
+    if (ld_mod_block % 4 != 0) return H3_ERR_ALIGN;
+    if (n_blocks == 0) return H3_OK;
+    if (w == nullptr || mod == nullptr) return H3_ERR_NULL;
+    uint16_t *xm = const_cast<uint16_t *>(x);  // the stack writes x in place
+    for (int32_t b = 0; b < n_blocks; ++b)
+        H3_TRY(h3_check_block_forward(dims, w + b, x, xm, mod + (int64_t)b * ld_mod_block, n_mod_groups, mod_idx,
+                                      pos, L_buf, valid_len, nullptr, 0, nullptr, workspace, ws_bytes));
+    return H3_OK;
+}
+
 int h3_check_block_forward_sparse(const h3_dims *dims, const h3_block_weights *w, const uint16_t *x, uint16_t *y,
                                   const float *mod, int32_t n_mod_groups, const int32_t *mod_idx,
                                   const int32_t *pos, int64_t L_buf, int64_t valid_len, int64_t prefix_len,

@@ -102,6 +102,10 @@ def _load():
         "h3_check_swiglu_lora": [P, I64, P, I64, P, I64, I64, I64, I32],
         "h3_linear": [P, I64, P, I64, P, P, I64, I64, I64, I64, I64, I32, P, I64, P, I64, I32, P, P],
         "h3_check_linear": [P, I64, P, I64, P, I64, I64, I64, I64, I64, I32, P, I64, P, I32],
+        "h3_stack_forward": [C.POINTER(Dims), C.POINTER(BlockWeights), I32, P, P, I64, I32, P, P, I64, I64, P, SZ,
+                             P],
+        "h3_check_stack_forward": [C.POINTER(Dims), C.POINTER(BlockWeights), I32, P, P, I64, I32, P, P, I64, I64, P,
+                                   SZ],
         "h3_block_workspace_bytes": [C.POINTER(Dims), I64, C.POINTER(QGroup), I32],
         "h3_block_workspace_layout": [C.POINTER(Dims), I64, C.POINTER(QGroup), I32, C.POINTER(I64),
                                       C.POINTER(I64)],
@@ -163,7 +167,7 @@ EXPORTS = ["h3_block_forward", "h3_attention", "h3_fused_modulate_norm", "h3_qk_
            "h3_block_sparse_workspace_layout", "h3_mxfp8_quantize", "h3_linear_mxfp8", "h3_check_mxfp8_quantize",
            "h3_check_linear_mxfp8", "h3_fused_modulate_norm_mxfp8", "h3_check_fused_modulate_norm_mxfp8",
            "h3_block_forward_mxfp8", "h3_check_block_forward_mxfp8", "h3_block_mxfp8_workspace_bytes",
-           "h3_block_mxfp8_workspace_layout"]
+           "h3_block_mxfp8_workspace_layout", "h3_stack_forward", "h3_check_stack_forward"]
 
 
 def status_string(s: int) -> str:
@@ -254,6 +258,25 @@ def block_forward(dims: Dims, weights: BlockWeights, x, y, mod, n_mod_groups, va
                              C.byref(exp) if exp is not None else None, _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream(stream))
     _ok(s, "h3_block_forward")
+
+
+def make_weight_stack(weight_sets) -> "C.Array":
+    """ctypes array of BlockWeights, one per block, for stack_forward."""
+    arr = (BlockWeights * len(weight_sets))()
+    for i, w in enumerate(weight_sets):
+        arr[i] = w
+    return arr
+
+
+def stack_forward(dims: Dims, weight_stack, x, mod, ld_mod_block, n_mod_groups, valid_len, workspace,
+                  mod_idx=None, pos=None, stream=None):
+    """h3_stack_forward: len(weight_stack) blocks in place on x; block b reads
+    its modulation table at mod + b * ld_mod_block floats."""
+    n = len(weight_stack)
+    s = LIB.h3_stack_forward(C.byref(dims), weight_stack if n else None, n, _ptr(x), _ptr(mod), ld_mod_block,
+                             n_mod_groups, _ptr(mod_idx), _ptr(pos), x.shape[0], valid_len, _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream))
+    _ok(s, "h3_stack_forward")
 
 
 def block_sparse_workspace_bytes(dims: Dims, L_buf: int, valid_len: int, prefix_len: int) -> int:
