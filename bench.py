@@ -89,7 +89,9 @@ def time_calls(torch, fn, iters: int, warmup: int, per_call: bool = False):
 
 def cpu_baseline(seconds_target: float = 20.0):
     """FP64 oracle on a bounded sample: the full-width block at L tokens, scaled
-    to ms per block at the 58,758-token workload by algorithmic flops."""
+    to ms per block at the 58,758-token workload by algorithmic flops. A
+    1,024-token probe sizes the sample: L grows (in steps of 64 rows, at most
+    8,192) until the sample takes about `seconds_target` on this host."""
     from oracle import h3_oracle as O
     from video_diffusion_transformer_dit_amd import inputs as I
     try:
@@ -97,23 +99,30 @@ def cpu_baseline(seconds_target: float = 20.0):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    L = 1024
-    s = I.scaled(I.FULL_4096, L, name=f"full-{L}")
-    wb = I.block_weights(s, "cpu0")
-    w = {k: O.bf16_to_f64(v) for k, v in wb.items()}
-    x = O.bf16_to_f64(I.activations(s, tag="cpu0.x"))
-    mod = I.mod_table(s, 1, tag="cpu0.mod").astype(np.float64)
-    t0 = time.perf_counter()
-    O.block_forward(x, w, mod, heads=s.heads, head_dim=128, ffn=s.ffn, valid_len=L, rot_dim=s.rot_dim)
-    dt = time.perf_counter() - t0
-    g_s, a_s = block_flops(L, s.hidden, s.ffn)
+
+    def run(L):
+        s = I.scaled(I.FULL_4096, L, name=f"full-{L}")
+        wb = I.block_weights(s, "cpu0")
+        w = {k: O.bf16_to_f64(v) for k, v in wb.items()}
+        x = O.bf16_to_f64(I.activations(s, tag="cpu0.x"))
+        mod = I.mod_table(s, 1, tag="cpu0.mod").astype(np.float64)
+        t0 = time.perf_counter()
+        O.block_forward(x, w, mod, heads=s.heads, head_dim=128, ffn=s.ffn, valid_len=L, rot_dim=s.rot_dim)
+        return time.perf_counter() - t0
+
+    L, dt = 1024, run(1024)
+    if dt < seconds_target / 3:
+        L = int(min(8192, max(1024, 1024 * seconds_target / dt)) // 64 * 64)
+        if L > 1024:
+            dt = run(L)
+    g_s, a_s = block_flops(L, 5376, 21504)
     g_f, a_f = block_flops(58758, 5376, 21504)
     ms_full = dt * 1e3 * (g_f + a_f) / (g_s + a_s)
     return {"value": round(ms_full, 1), "unit": "ms/block", "cores": int(threads), "kind": "oracle",
             "sample": f"FP64 numpy oracle, one full-width block (H 5376, 42x128, F 21504) at {L} tokens: "
                       f"{dt:.2f} s for {(g_s + a_s) / 1e12:.3f} TFLOP, scaled by algorithmic flops to the "
                       f"58,758-token block ({(g_f + a_f) / 1e12:.1f} TFLOP)",
-            "sample_seconds": round(dt, 3), "sample_gflops_per_s": round((g_s + a_s) / dt / 1e9, 1)}
+            "sample_tokens": L, "sample_seconds": round(dt, 3), "sample_gflops_per_s": round((g_s + a_s) / dt / 1e9, 1)}
 
 
 def lora_consumers(torch, h3, dev, gen, L, V, H, heads, F, iters):
@@ -551,9 +560,9 @@ def main(argv=None) -> int:
         "attention_tflops": round(attn_tf, 1),
         "gemm_tflops": round(gemm_f / (gemm_ms * 1e-3) / 1e12, 1),
         "kernels": kernels,
-        "roofline": {"kernel": "attention_fwd_kernel<false, true> (dense, fixed softmax reference)", "bound": "mfma", "achieved": round(attn_tf, 1),
+        "roofline": {"kernel": "attention_fwd_kernel<false, true, false> (dense, fixed softmax reference)", "bound": "mfma", "achieved": round(attn_tf, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": counter_traffic("void attention_fwd_kernel<false, true>", "attention.hip"),
+                     "traffic": counter_traffic("void attention_fwd_kernel<false, true, false>", "attention.hip"),
                      "traffic_unit": "bytes per launch (FETCH_SIZE x2 + WRITE_SIZE x1, copy-calibrated)",
                      "work_per_launch": "4 * 58758^2 * 5376 = 7.424e13 flop (QK^T and PV over valid rows)"},
     }

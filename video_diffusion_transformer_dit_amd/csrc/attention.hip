@@ -54,20 +54,31 @@ constexpr int WQ = 64;          // queries per wavefront
 constexpr int BKV = 64;         // keys per tile
 constexpr int kThreads = 256;
 
-// One launch per query group: rows [0, rows) of q/o (already offset to the
-// group's first row) attend over n_seg K/V segments in order.
-struct AttnArgs {
+// A query group: rows [0, rows) of q/o (offset to the group's first row)
+// attend over n_seg K/V segments in order.
+struct AttnGroup {
     const uint16_t *q;
     uint16_t *o;
-    int64_t ld_q, ld_o;
     int64_t rows;
-    int32_t heads;
     int32_t tiles_per_head;  // ceil(rows / BQ)
     int32_t n_seg;
-    float scale_log2;        // softmax scale * log2(e)
     const uint16_t *sk[H3_MAX_SEGMENTS];   // segment row 0, head 0
     const uint16_t *svt[H3_MAX_SEGMENTS];  // segment's V^T planes [heads][128][lpad]
     int64_t sldk[H3_MAX_SEGMENTS], slpad[H3_MAX_SEGMENTS], slen[H3_MAX_SEGMENTS];
+};
+
+// One launch covers every query group of a call: group i owns the work items
+// [item_end[i-1], item_end[i]) (heads x query tiles, padded to a multiple of
+// 8 so that a group's items start on XCD 0). Groups are ordered by the keys
+// one of their items reads, longest first, so short groups fill the tail of
+// the long ones instead of running as launches of their own.
+struct AttnArgs {
+    int64_t ld_q, ld_o;
+    int32_t heads;
+    float scale_log2;        // softmax scale * log2(e)
+    int32_t n_groups;
+    int32_t item_end[H3_MAX_GROUPS];
+    AttnGroup grp[H3_MAX_GROUPS];
     const float *kmax2;      // [heads] largest squared key norm over all segments
     int32_t *flags;          // per workgroup: 1 = left to the online instance
     // Block-sparse (list) mode: q and o point at row 0; segment 0 is the
@@ -118,7 +129,7 @@ __device__ __forceinline__ int kperm(int k) { return (k & ~12) | ((k & 4) << 1) 
 
 // Fields of segment s, read from the kernel arguments at static offsets
 // under a uniform condition (dynamic indexing would go through memory).
-__device__ __forceinline__ SegState seg_of(const AttnArgs &a, int s) {
+__device__ __forceinline__ SegState seg_of(const AttnGroup &a, int s) {
     SegState r{a.sk[0], a.svt[0], a.sldk[0], a.slpad[0], a.slen[0]};
 #pragma unroll
     for (int j = 1; j < H3_MAX_SEGMENTS; ++j)
@@ -140,8 +151,12 @@ struct Cursor {
 // The dense / grouped kernel (SPARSE = false) and the block-sparse list mode
 // (SPARSE = true) share every step; list mode only changes which query tile a
 // workgroup owns and which key tiles of segment 1 it visits.
-template <bool SPARSE, bool FIXED>
+template <bool SPARSE, bool FIXED, bool MULTI>
 __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) {
+    int gi = 0;  // the workgroup's query group (wave-uniform; group 0 unless MULTI)
+    if (MULTI)
+        while (gi + 1 < a.n_groups && (int)blockIdx.x >= a.item_end[gi]) ++gi;
+    const AttnGroup &G = a.grp[gi];
     if (!FIXED && a.flags[blockIdx.x] == 0) return;  // done by the fixed-reference instance
     constexpr int KB = BKV * 16;  // 16-byte chunks per K tile buffer (16 KB)
     constexpr int VB = D * 8;     // chunks per V^T tile buffer (16 KB)
@@ -171,24 +186,36 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
             }
             head = bid / a.pre_tiles;
             const int64_t q0 = (int64_t)(bid - head * a.pre_tiles) * BQ;
-            qbase = a.q + q0 * a.ld_q;
-            obase = a.o + q0 * a.ld_o;
+            qbase = G.q + q0 * a.ld_q;
+            obase = G.o + q0 * a.ld_o;
             rows_left = a.prefix_len - q0;
         } else {
-            if (SPARSE) bid -= a.pre_items;  // pre_items is a multiple of 8: same XCD
-            const int total = a.tiles_per_head * a.heads;
-            const int q8 = total / 8, rr = total % 8;
-            const int xcd = bid % 8, local = bid / 8;
-            bid = xcd < rr ? xcd * (q8 + 1) + local : rr * (q8 + 1) + (xcd - rr) * q8 + local;
-            head = bid / a.tiles_per_head;
-            const int tile = bid - head * a.tiles_per_head;
+            const int total = G.tiles_per_head * a.heads;
+            if (!MULTI) {
+                if (SPARSE) bid -= a.pre_items;  // pre_items is a multiple of 8: same XCD
+                const int q8 = total / 8, rr = total % 8;
+                const int xcd = bid % 8, local = bid / 8;
+                bid = xcd < rr ? xcd * (q8 + 1) + local : rr * (q8 + 1) + (xcd - rr) * q8 + local;
+            } else {
+                // the group's items start at a multiple of 8 and span a multiple of 8
+                const int item0 = gi > 0 ? a.item_end[gi - 1] : 0;
+                const int span = a.item_end[gi] - item0;
+                const int local = bid - item0;
+                bid = (local % 8) * (span / 8) + local / 8;
+                if (bid >= total) {  // padding item (whole workgroup)
+                    if (FIXED && threadIdx.x == 0) a.flags[blockIdx.x] = 0;
+                    return;
+                }
+            }
+            head = bid / G.tiles_per_head;
+            const int tile = bid - head * G.tiles_per_head;
             const int64_t q0 = (SPARSE ? a.prefix_len : 0) + (int64_t)tile * BQ;
-            qbase = a.q + q0 * a.ld_q;
-            obase = a.o + q0 * a.ld_o;
-            rows_left = (SPARSE ? a.prefix_len + a.tgt_rows : a.rows) - q0;
+            qbase = G.q + q0 * a.ld_q;
+            obase = G.o + q0 * a.ld_o;
+            rows_left = (SPARSE ? a.prefix_len + a.tgt_rows : G.rows) - q0;
             if (SPARSE) {
                 listed = true;
-                const int64_t item = (int64_t)head * a.tiles_per_head + tile;
+                const int64_t item = (int64_t)head * G.tiles_per_head + tile;
                 lcount = min(max(a.counts[item], 0), a.n_kb);
                 const uint16_t *src = a.blocks + item * a.n_kb;
                 // Entries past the last block become an empty tile at the
@@ -278,12 +305,12 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     int n_tiles = 0;
 #pragma unroll
     for (int s = 0; s < H3_MAX_SEGMENTS; ++s)
-        if (s < a.n_seg && !(listed && s == 1)) n_tiles += (int)((a.slen[s] + BKV - 1) / BKV);
+        if (s < G.n_seg && !(listed && s == 1)) n_tiles += (int)((G.slen[s] + BKV - 1) / BKV);
     if (listed) n_tiles += lcount;
 
     // Two cursors over the same tile sequence: K runs two tiles ahead of the
     // tile being finished, V^T one tile ahead.
-    Cursor kc{0, 0, (int)a.slen[0], seg_of(a, 0), 0, 0}, vc{0, 0, (int)a.slen[0], seg_of(a, 0), 0, 0};
+    Cursor kc{0, 0, (int)G.slen[0], seg_of(G, 0), 0, 0}, vc{0, 0, (int)G.slen[0], seg_of(G, 0), 0, 0};
     int k_voff[4], v_voff[4];
     auto set_k = [&]() {
 #pragma unroll
@@ -307,7 +334,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
                 c.k0 = __builtin_amdgcn_readfirstlane(c.nxt);
                 c.nxt = lst[c.li + 1 <= lcount ? c.li + 1 : lcount];
             } else {
-                c.seg = a.n_seg;
+                c.seg = G.n_seg;
             }
             return;
         }
@@ -315,8 +342,8 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
         if (c.k0 >= c.len) {
             ++c.seg;
             c.k0 = 0;
-            if (c.seg < a.n_seg) {
-                c.S = seg_of(a, c.seg);
+            if (c.seg < G.n_seg) {
+                c.S = seg_of(G, c.seg);
                 c.len = (int)c.S.len;
                 if (is_k) set_k();
                 else set_v();
@@ -326,7 +353,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
                         c.k0 = __builtin_amdgcn_readfirstlane(lst[0]);
                         c.nxt = lst[1];
                     } else {
-                        c.seg = a.n_seg;
+                        c.seg = G.n_seg;
                     }
                 }
             }
@@ -334,7 +361,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     };
     // Keys of the cursor's tile that exist (64 past the last tile: nothing to mask).
     auto valid_keys = [&](const Cursor &c) -> int {
-        return c.seg < a.n_seg ? min(c.len - c.k0, BKV) : BKV;
+        return c.seg < G.n_seg ? min(c.len - c.k0, BKV) : BKV;
     };
     // Issue this wave's 4 slab loads of the cursor's tile into buffer b. Past
     // the last tile the descriptor has length zero: the loads return zero and
@@ -342,14 +369,14 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     auto issue_k = [&](int b, int half) {
         const int rows = min(kc.len - kc.k0, BKV);
         i32x4_t r = raw_rsrc(kc.S.k + (int64_t)kc.k0 * kc.S.ldk + head * D, ((int64_t)(rows - 1) * kc.S.ldk + D) * 2);
-        if (kc.seg >= a.n_seg || rows <= 0) r.z = 0;
+        if (kc.seg >= G.n_seg || rows <= 0) r.z = 0;
 #pragma unroll
         for (int i = 2 * half; i < 2 * half + 2; ++i)
             dma_slab(r, lds0 + (uint32_t)((b * KB + 64 * (4 * wave + i)) * 16), k_voff[i], 0);
     };
     auto issue_v = [&](int b, int half) {
         i32x4_t r = raw_rsrc(vc.S.vt + (int64_t)head * D * vc.S.lpad + vc.k0, ((int64_t)D * vc.S.lpad - vc.k0) * 2);
-        if (vc.seg >= a.n_seg) r.z = 0;
+        if (vc.seg >= G.n_seg) r.z = 0;
 #pragma unroll
         for (int i = 2 * half; i < 2 * half + 2; ++i)
             dma_slab(r, lds0 + (uint32_t)((2 * KB + b * VB + 64 * (4 * wave + i)) * 16), v_voff[i], 0);
@@ -518,13 +545,13 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
         if (odd) {
             const int rows = min(kc.len - kc.k0, BKV);
             rl = raw_rsrc(kc.S.k + (int64_t)kc.k0 * kc.S.ldk + head * D, ((int64_t)(rows - 1) * kc.S.ldk + D) * 2);
-            if (kc.seg >= a.n_seg || rows <= 0) rl.z = 0;
+            if (kc.seg >= G.n_seg || rows <= 0) rl.z = 0;
             m0b = lds0 + (uint32_t)((tp * KB + 64 * 4 * wave) * 16);
 #pragma unroll
             for (int i = 0; i < 4; ++i) voffs[i] = k_voff[i];
         } else {
             rl = raw_rsrc(vc.S.vt + (int64_t)head * D * vc.S.lpad + vc.k0, ((int64_t)D * vc.S.lpad - vc.k0) * 2);
-            if (vc.seg >= a.n_seg) rl.z = 0;
+            if (vc.seg >= G.n_seg) rl.z = 0;
             m0b = lds0 + (uint32_t)((2 * KB + (tp ^ 1) * VB + 64 * 4 * wave) * 16);
 #pragma unroll
             for (int i = 0; i < 4; ++i) voffs[i] = v_voff[i];
@@ -797,39 +824,60 @@ void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_
     stage_vt(plan, k, ld_k, v, ld_v, heads, ws, stream);
     std::pair<int64_t, int64_t> cov[H3_MAX_GROUPS];
     int nc = 0;
+    // Non-empty groups, longest item first (key tiles one work item reads).
+    int order[H3_MAX_GROUPS];
+    int64_t key_tiles[H3_MAX_GROUPS];
     for (int gi = 0; gi < n_groups; ++gi) {
         const h3_qgroup &g = groups[gi];
         if (g.q_end <= g.q_begin) continue;
-        cov[nc++] = {g.q_begin, g.q_end};
-        AttnArgs a = {};
-        a.q = q + g.q_begin * ld_q;
-        a.o = o + g.q_begin * ld_o;
-        a.ld_q = ld_q;
-        a.ld_o = ld_o;
-        a.rows = g.q_end - g.q_begin;
-        a.heads = heads;
-        a.tiles_per_head = (int32_t)((a.rows + BQ - 1) / BQ);
-        a.n_seg = g.n_seg;
-        a.scale_log2 = scale * 1.4426950408889634f;
-        a.kmax2 = reinterpret_cast<const float *>(ws + plan.kmax_off);
-        a.flags = reinterpret_cast<int32_t *>(ws + plan.flags_off);
+        cov[nc] = {g.q_begin, g.q_end};
+        key_tiles[gi] = 0;
+        for (int s = 0; s < g.n_seg; ++s) key_tiles[gi] += (g.seg[s].len + BKV - 1) / BKV;
+        order[nc++] = gi;
+    }
+    std::stable_sort(order, order + nc, [&](int x, int y) { return key_tiles[x] > key_tiles[y]; });
+    AttnArgs a = {};
+    a.ld_q = ld_q;
+    a.ld_o = ld_o;
+    a.heads = heads;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.kmax2 = reinterpret_cast<const float *>(ws + plan.kmax_off);
+    a.flags = reinterpret_cast<int32_t *>(ws + plan.flags_off);
+    a.n_groups = nc;
+    int32_t items = 0;
+    for (int oi = 0; oi < nc; ++oi) {
+        const int gi = order[oi];
+        const h3_qgroup &g = groups[gi];
+        AttnGroup &G = a.grp[oi];
+        G.q = q + g.q_begin * ld_q;
+        G.o = o + g.q_begin * ld_o;
+        G.rows = g.q_end - g.q_begin;
+        G.tiles_per_head = (int32_t)((G.rows + BQ - 1) / BQ);
+        G.n_seg = g.n_seg;
         for (int s = 0; s < g.n_seg; ++s) {
             const h3_kv_seg &ss = g.seg[s];
             const VtSeg &e = plan.seg[plan.map[gi][s]];
             if (ss.k == nullptr) {
-                a.sk[s] = k + ss.begin * ld_k;
-                a.sldk[s] = ld_k;
+                G.sk[s] = k + ss.begin * ld_k;
+                G.sldk[s] = ld_k;
             } else {
-                a.sk[s] = ss.k + ss.begin * ss.ld;
-                a.sldk[s] = ss.ld;
+                G.sk[s] = ss.k + ss.begin * ss.ld;
+                G.sldk[s] = ss.ld;
             }
-            a.svt[s] = reinterpret_cast<const uint16_t *>(ws + e.off);
-            a.slpad[s] = e.lpad;
-            a.slen[s] = ss.len;
+            G.svt[s] = reinterpret_cast<const uint16_t *>(ws + e.off);
+            G.slpad[s] = e.lpad;
+            G.slen[s] = ss.len;
         }
-        const dim3 grid((unsigned)(a.tiles_per_head * heads));
-        attention_fwd_kernel<false, true><<<grid, kThreads, 0, stream>>>(a);
-        attention_fwd_kernel<false, false><<<grid, kThreads, 0, stream>>>(a);
+        // a group's items start on XCD 0 (one group alone needs no padding)
+        items += nc > 1 ? (G.tiles_per_head * heads + 7) / 8 * 8 : G.tiles_per_head * heads;
+        a.item_end[oi] = items;
+    }
+    if (nc > 1) {
+        attention_fwd_kernel<false, true, true><<<dim3((unsigned)items), kThreads, 0, stream>>>(a);
+        attention_fwd_kernel<false, false, true><<<dim3((unsigned)items), kThreads, 0, stream>>>(a);
+    } else if (nc == 1) {
+        attention_fwd_kernel<false, true, false><<<dim3((unsigned)items), kThreads, 0, stream>>>(a);
+        attention_fwd_kernel<false, false, false><<<dim3((unsigned)items), kThreads, 0, stream>>>(a);
     }
     // Zero the rows of o outside every group (the padding suffix included).
     std::sort(cov, cov + nc);
@@ -878,35 +926,38 @@ void launch_sparse_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k,
     stage_vt(plan, k, ld_k, v, ld_v, heads, ws, stream);
     const int64_t T = valid_len - prefix_len;
     AttnArgs a = {};
-    a.q = q;
-    a.o = o;
+    AttnGroup &G = a.grp[0];
+    G.q = q;
+    G.o = o;
     a.ld_q = ld_q;
     a.ld_o = ld_o;
-    a.rows = valid_len;
+    G.rows = valid_len;
     a.heads = heads;
-    a.tiles_per_head = (int32_t)((T + BQ - 1) / BQ);
-    a.n_seg = 2;
+    G.tiles_per_head = (int32_t)((T + BQ - 1) / BQ);
+    G.n_seg = 2;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.kmax2 = reinterpret_cast<const float *>(ws + plan.kmax_off);
     a.flags = reinterpret_cast<int32_t *>(ws + plan.flags_off);
     for (int s = 0; s < 2; ++s) {
         const VtSeg &e = plan.seg[plan.map[0][s]];
-        a.sk[s] = k + g.seg[s].begin * ld_k;
-        a.sldk[s] = ld_k;
-        a.svt[s] = reinterpret_cast<const uint16_t *>(ws + e.off);
-        a.slpad[s] = e.lpad;
-        a.slen[s] = g.seg[s].len;
+        G.sk[s] = k + g.seg[s].begin * ld_k;
+        G.sldk[s] = ld_k;
+        G.svt[s] = reinterpret_cast<const uint16_t *>(ws + e.off);
+        G.slpad[s] = e.lpad;
+        G.slen[s] = g.seg[s].len;
     }
     a.blocks = blocks;
     a.counts = counts;
     a.n_kb = (int32_t)((T + BKV - 1) / BKV);
     a.pre_tiles = (int32_t)((prefix_len + BQ - 1) / BQ);
     a.pre_items = (heads * a.pre_tiles + 7) / 8 * 8;
+    a.n_groups = 1;
     a.prefix_len = prefix_len;
     a.tgt_rows = T;
-    const unsigned grid = (unsigned)(a.pre_items + a.tiles_per_head * heads);
-    attention_fwd_kernel<true, true><<<dim3(grid), kThreads, 0, stream>>>(a);
-    attention_fwd_kernel<true, false><<<dim3(grid), kThreads, 0, stream>>>(a);
+    const unsigned grid = (unsigned)(a.pre_items + G.tiles_per_head * heads);
+    a.item_end[0] = (int32_t)grid;
+    attention_fwd_kernel<true, true, false><<<dim3(grid), kThreads, 0, stream>>>(a);
+    attention_fwd_kernel<true, false, false><<<dim3(grid), kThreads, 0, stream>>>(a);
     launch_zero_rows(o, ld_o, (int64_t)heads * D, valid_len, L_buf, stream);
 }
 

@@ -132,13 +132,15 @@ void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads
         out->bytes += (size_t)heads * kHeadDim * e.lpad * 2;
         return out->n++;
     };
-    int64_t qrows = 0;  // longest query range of one launch
+    int64_t qtiles = 0;  // 256-row query tiles over all groups
+    int n_launch_groups = 1;
     if (groups == nullptr) {
         if (dense_len > 0) out->map[0][0] = add(1, nullptr, nullptr, 0, 0, dense_len);
-        qrows = dense_len;
+        qtiles = (dense_len + 255) / 256;
     } else {
+        n_launch_groups = std::max(1, std::min(n_groups, H3_MAX_GROUPS));
         for (int g = 0; g < n_groups && g < H3_MAX_GROUPS; ++g) {
-            qrows = std::max<int64_t>(qrows, groups[g].q_end - groups[g].q_begin);
+            qtiles += (std::max<int64_t>(groups[g].q_end - groups[g].q_begin, 0) + 255) / 256;
             for (int s = 0; s < groups[g].n_seg && s < H3_MAX_SEGMENTS; ++s) {
                 const h3_kv_seg &x = groups[g].seg[s];
                 out->map[g][s] = x.k == nullptr ? add(1, nullptr, nullptr, 0, x.begin, x.len)
@@ -151,11 +153,12 @@ void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads
         auto align = [](size_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; };
         out->kmax_off = (int64_t)out->bytes;
         out->bytes += align((size_t)heads * 4);
-        // workgroups of one launch: query tiles of 256 rows per head, plus the
-        // block-sparse launch's split of the rows into prefix and target tiles
-        // (at most one more tile per head) and its padding to a multiple of 8
+        // workgroups of the launch: query tiles of 256 rows per head and group,
+        // each group padded to a multiple of 8, plus the block-sparse launch's
+        // split of the rows into prefix and target tiles (at most one more tile
+        // per head)
         out->flags_off = (int64_t)out->bytes;
-        out->bytes += align((size_t)(((qrows + 255) / 256 + 1) * heads + 8) * 4);
+        out->bytes += align((size_t)((qtiles + 1) * heads + 8 * n_launch_groups) * 4);
     }
 }
 
