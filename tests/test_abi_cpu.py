@@ -29,10 +29,16 @@ def _align(b):
     return -(-b // 256) * 256
 
 
-def attention_extra(heads, qrows):
-    """Bytes the attention workspace holds after the V^T planes: the per-head
-    key norm maxima and one int32 per workgroup of a launch."""
-    return _align(heads * 4) + _align(((qrows + 255) // 256 + 1) * heads * 4 + 8 * 4)
+def attention_extra(heads, qrows, n_groups=1, qtiles=None):
+    """Bytes the attention workspace holds after the V^T planes: partial
+    records for query tiles cut into key-range pieces (fewer than 512, at most
+    4 per tile, 256 rows of 128 FP32 plus (m, l) each), the per-head key norm
+    maxima and one int32 per workgroup of a launch (tiles, the block-sparse
+    launch's extra tile per head, range padding and pieces)."""
+    qtiles = (qrows + 255) // 256 if qtiles is None else qtiles
+    records = min(511, 4 * qtiles * heads)
+    return (_align(records * 256 * 130 * 4) + _align(heads * 4)
+            + _align(((qtiles + 1) * heads + 8 * (n_groups + 1) + 512) * 4))
 
 
 def declared_functions():
@@ -206,9 +212,9 @@ def test_attention_validator():
                                      need - 1) == h3.H3_ERR_WORKSPACE
     assert h3.LIB.h3_check_attention(q, 3 * H, k, 3 * H, v, 3 * H, o, H, L, 500, 2, 128, 0.0, None, 0, o,
                                      need) == h3.H3_ERR_ALIAS
-    # groups sharing one segment stage its V^T once
+    # groups sharing one segment stage its V^T once (query tiles: 1 + 2)
     g, n = h3.make_groups([(0, 100, [("self", 0, 500)]), (100, 500, [("self", 0, 500)])])
-    assert h3.LIB.h3_attention_workspace_bytes(500, 2, g, n) == need
+    assert h3.LIB.h3_attention_workspace_bytes(500, 2, g, n) == 2 * 128 * 512 * 2 + attention_extra(2, 0, 2, 3)
     # o overlapping the packed qkv
     assert h3.LIB.h3_check_attention(q, 3 * H, k, 3 * H, v, 3 * H, base + 6 * H, H, L, 500, 2, 128, 0.0, None,
                                      0, ws, need) == h3.H3_ERR_ALIAS

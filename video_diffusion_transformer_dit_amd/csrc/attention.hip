@@ -67,17 +67,23 @@ struct AttnGroup {
     int64_t sldk[H3_MAX_SEGMENTS], slpad[H3_MAX_SEGMENTS], slen[H3_MAX_SEGMENTS];
 };
 
-// One launch covers every query group of a call: group i owns the work items
-// [item_end[i-1], item_end[i]) (heads x query tiles, padded to a multiple of
-// 8 so that a group's items start on XCD 0). Groups are ordered by the keys
-// one of their items reads, longest first, so short groups fill the tail of
-// the long ones instead of running as launches of their own.
+// One launch covers every query group of a call, as ranges of work items
+// (the host's attention schedule): range i owns the items [end[i-1], end[i])
+// and covers count[i] (head, tile) items of group grp[group[i]] from item
+// first[i] on, each cut into split[i] pieces by key range. Pieces write
+// unnormalised partial results (O in FP32 and the row's reference m and sum
+// l) to `part`, which the merge pass combines. The longest items run first,
+// so short groups and pieces fill the tail instead of running as launches of
+// their own.
 struct AttnArgs {
     int64_t ld_q, ld_o;
     int32_t heads;
     float scale_log2;        // softmax scale * log2(e)
-    int32_t n_groups;
-    int32_t item_end[H3_MAX_GROUPS];
+    int32_t n_ranges;
+    int32_t rng_end[H3_MAX_GROUPS + 1], rng_group[H3_MAX_GROUPS + 1], rng_first[H3_MAX_GROUPS + 1],
+        rng_count[H3_MAX_GROUPS + 1], rng_split[H3_MAX_GROUPS + 1];
+    float *part;             // [records][256][128] FP32 O, then [records][256] (m, l)
+    int32_t part_records;
     AttnGroup grp[H3_MAX_GROUPS];
     const float *kmax2;      // [heads] largest squared key norm over all segments
     int32_t *flags;          // per workgroup: 1 = left to the online instance
@@ -153,10 +159,10 @@ struct Cursor {
 // workgroup owns and which key tiles of segment 1 it visits.
 template <bool SPARSE, bool FIXED, bool MULTI>
 __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) {
-    int gi = 0;  // the workgroup's query group (wave-uniform; group 0 unless MULTI)
+    int ri = 0;  // the workgroup's range (wave-uniform; range 0 unless MULTI)
     if (MULTI)
-        while (gi + 1 < a.n_groups && (int)blockIdx.x >= a.item_end[gi]) ++gi;
-    const AttnGroup &G = a.grp[gi];
+        while (ri + 1 < a.n_ranges && (int)blockIdx.x >= a.rng_end[ri]) ++ri;
+    const AttnGroup &G = a.grp[MULTI ? a.rng_group[ri] : 0];
     if (!FIXED && a.flags[blockIdx.x] == 0) return;  // done by the fixed-reference instance
     constexpr int KB = BKV * 16;  // 16-byte chunks per K tile buffer (16 KB)
     constexpr int VB = D * 8;     // chunks per V^T tile buffer (16 KB)
@@ -177,6 +183,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     int64_t rows_left;      // query rows from qbase to the end of the tile's group
     bool listed = false;    // list mode, target tile: segment 1 through the list
     int lcount = 0;
+    int pieces = 1, piece = 0, rec = 0;  // key-range pieces of the item; this one; its partial record
     {
         int bid = blockIdx.x;
         if (SPARSE && bid < a.pre_items) {
@@ -197,15 +204,19 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
                 const int xcd = bid % 8, local = bid / 8;
                 bid = xcd < rr ? xcd * (q8 + 1) + local : rr * (q8 + 1) + (xcd - rr) * q8 + local;
             } else {
-                // the group's items start at a multiple of 8 and span a multiple of 8
-                const int item0 = gi > 0 ? a.item_end[gi - 1] : 0;
-                const int span = a.item_end[gi] - item0;
+                // the range's items start at a multiple of 8 and span a multiple of 8
+                const int item0 = ri > 0 ? a.rng_end[ri - 1] : 0;
+                const int span = a.rng_end[ri] - item0;
                 const int local = bid - item0;
-                bid = (local % 8) * (span / 8) + local / 8;
-                if (bid >= total) {  // padding item (whole workgroup)
+                const int idx = (local % 8) * (span / 8) + local / 8;
+                pieces = a.rng_split[ri];
+                if (idx >= a.rng_count[ri] * pieces) {  // padding item (whole workgroup)
                     if (FIXED && threadIdx.x == 0) a.flags[blockIdx.x] = 0;
                     return;
                 }
+                piece = idx % pieces;
+                rec = idx;
+                bid = a.rng_first[ri] + idx / pieces;
             }
             head = bid / G.tiles_per_head;
             const int tile = bid - head * G.tiles_per_head;
@@ -307,10 +318,26 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     for (int s = 0; s < H3_MAX_SEGMENTS; ++s)
         if (s < G.n_seg && !(listed && s == 1)) n_tiles += (int)((G.slen[s] + BKV - 1) / BKV);
     if (listed) n_tiles += lcount;
+    // A piece covers key tiles [kt0, kt1) of the group's key sequence.
+    int seg0 = 0, t0 = 0;
+    if (MULTI && pieces > 1) {
+        const int kt0 = piece * n_tiles / pieces;
+        n_tiles = (piece + 1) * n_tiles / pieces - kt0;
+        t0 = kt0;
+#pragma unroll
+        for (int s = 0; s < H3_MAX_SEGMENTS; ++s) {
+            const int ts = (int)((G.slen[s] + BKV - 1) / BKV);
+            if (seg0 == s && s + 1 < G.n_seg && t0 >= ts) {
+                t0 -= ts;
+                seg0 = s + 1;
+            }
+        }
+    }
 
     // Two cursors over the same tile sequence: K runs two tiles ahead of the
     // tile being finished, V^T one tile ahead.
-    Cursor kc{0, 0, (int)G.slen[0], seg_of(G, 0), 0, 0}, vc{0, 0, (int)G.slen[0], seg_of(G, 0), 0, 0};
+    const SegState S0 = seg_of(G, seg0);
+    Cursor kc{seg0, BKV * t0, (int)S0.len, S0, 0, 0}, vc{seg0, BKV * t0, (int)S0.len, S0, 0, 0};
     int k_voff[4], v_voff[4];
     auto set_k = [&]() {
 #pragma unroll
@@ -678,6 +705,28 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads past the end
 
+    if (MULTI && pieces > 1) {
+        // ---- a piece: unnormalised O rows and (m, l) into its partial record ----
+        float *po = a.part + (int64_t)rec * BQ * D;
+        float2 *pml = reinterpret_cast<float2 *>(a.part + (int64_t)a.part_records * BQ * D) + (int64_t)rec * BQ;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float l_tot = pair_sum(l_run[j]);
+            const int r = (int)qw + 32 * j + l32;
+            if (r < rows_left) {
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        *reinterpret_cast<float4 *>(po + (int64_t)r * D + 32 * dt + 8 * g + 4 * h) =
+                            make_float4(oacc[dt][j][4 * g], oacc[dt][j][4 * g + 1], oacc[dt][j][4 * g + 2],
+                                        oacc[dt][j][4 * g + 3]);
+                if (h == 0) pml[r] = make_float2(m_ref[j], l_tot);
+            }
+        }
+        return;
+    }
+
     // ---- normalise and store: lane holds O[q][32 dt + 8 g + 4 h + (0..3)] ----
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -776,6 +825,38 @@ __global__ __launch_bounds__(256) void vt_transpose_kernel(const uint16_t *v, in
     }
 }
 
+// Combines the partial results of (head, tile) items cut into key-range
+// pieces: per query row, o = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M)
+// with M the largest m_s, rounded to BF16. Workgroup (item, quarter): 64 rows
+// of one item, one wave per row at a time, two channels per lane.
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float *part, int32_t records, int32_t pieces,
+                                                         int32_t first, int32_t tiles_per_head, int64_t rows,
+                                                         uint16_t *o, int64_t ld_o) {
+    const int item = blockIdx.x;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int hti = first + item;
+    const int head = hti / tiles_per_head, tile = hti - head * tiles_per_head;
+    const float2 *ml = reinterpret_cast<const float2 *>(part + (int64_t)records * BQ * D);
+    for (int r = blockIdx.y * 64 + wave; r < (int)blockIdx.y * 64 + 64; r += 4) {
+        const int64_t q = (int64_t)tile * BQ + r;
+        if (q >= rows) break;
+        float M = -__builtin_huge_valf();
+        for (int s = 0; s < pieces; ++s) M = fmaxf(M, ml[(int64_t)(item * pieces + s) * BQ + r].x);
+        float l = 0.f, o0 = 0.f, o1 = 0.f;
+        for (int s = 0; s < pieces; ++s) {
+            const int64_t rec = (int64_t)item * pieces + s;
+            const float2 e = ml[rec * BQ + r];
+            const float w = __builtin_amdgcn_exp2f(e.x - M);
+            const float2 v = *reinterpret_cast<const float2 *>(part + (rec * BQ + r) * D + 2 * lane);
+            l += w * e.y;
+            o0 += w * v.x;
+            o1 += w * v.y;
+        }
+        const float inv = 1.0f / l;
+        *reinterpret_cast<uint32_t *>(o + q * ld_o + head * D + 2 * lane) = pack_bf16x2(o0 * inv, o1 * inv);
+    }
+}
+
 // Transposed V of every segment of the plan into the workspace, and the
 // largest squared key norm per head over all segments.
 void stage_vt(const VtPlan &plan, const uint16_t *k, int64_t ld_k, const uint16_t *v, int64_t ld_v, int32_t heads,
@@ -824,18 +905,10 @@ void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_
     stage_vt(plan, k, ld_k, v, ld_v, heads, ws, stream);
     std::pair<int64_t, int64_t> cov[H3_MAX_GROUPS];
     int nc = 0;
-    // Non-empty groups, longest item first (key tiles one work item reads).
-    int order[H3_MAX_GROUPS];
-    int64_t key_tiles[H3_MAX_GROUPS];
-    for (int gi = 0; gi < n_groups; ++gi) {
-        const h3_qgroup &g = groups[gi];
-        if (g.q_end <= g.q_begin) continue;
-        cov[nc] = {g.q_begin, g.q_end};
-        key_tiles[gi] = 0;
-        for (int s = 0; s < g.n_seg; ++s) key_tiles[gi] += (g.seg[s].len + BKV - 1) / BKV;
-        order[nc++] = gi;
-    }
-    std::stable_sort(order, order + nc, [&](int x, int y) { return key_tiles[x] > key_tiles[y]; });
+    for (int gi = 0; gi < n_groups; ++gi)
+        if (groups[gi].q_end > groups[gi].q_begin) cov[nc++] = {groups[gi].q_begin, groups[gi].q_end};
+    AttnSchedule sch;
+    attn_schedule(is_dense ? nullptr : groups, is_dense ? 0 : n_groups, valid_len, heads, &sch);
     AttnArgs a = {};
     a.ld_q = ld_q;
     a.ld_o = ld_o;
@@ -843,12 +916,13 @@ void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_
     a.scale_log2 = scale * 1.4426950408889634f;
     a.kmax2 = reinterpret_cast<const float *>(ws + plan.kmax_off);
     a.flags = reinterpret_cast<int32_t *>(ws + plan.flags_off);
-    a.n_groups = nc;
-    int32_t items = 0;
-    for (int oi = 0; oi < nc; ++oi) {
-        const int gi = order[oi];
+    a.part = reinterpret_cast<float *>(ws + plan.part_off);
+    a.part_records = sch.split_items * sch.pieces;
+    a.n_ranges = sch.n;
+    for (int gi = 0; gi < n_groups; ++gi) {
         const h3_qgroup &g = groups[gi];
-        AttnGroup &G = a.grp[oi];
+        if (g.q_end <= g.q_begin) continue;
+        AttnGroup &G = a.grp[gi];
         G.q = q + g.q_begin * ld_q;
         G.o = o + g.q_begin * ld_o;
         G.rows = g.q_end - g.q_begin;
@@ -868,16 +942,32 @@ void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_
             G.slpad[s] = e.lpad;
             G.slen[s] = ss.len;
         }
-        // a group's items start on XCD 0 (one group alone needs no padding)
-        items += nc > 1 ? (G.tiles_per_head * heads + 7) / 8 * 8 : G.tiles_per_head * heads;
-        a.item_end[oi] = items;
     }
-    if (nc > 1) {
-        attention_fwd_kernel<false, true, true><<<dim3((unsigned)items), kThreads, 0, stream>>>(a);
-        attention_fwd_kernel<false, false, true><<<dim3((unsigned)items), kThreads, 0, stream>>>(a);
-    } else if (nc == 1) {
-        attention_fwd_kernel<false, true, false><<<dim3((unsigned)items), kThreads, 0, stream>>>(a);
-        attention_fwd_kernel<false, false, false><<<dim3((unsigned)items), kThreads, 0, stream>>>(a);
+    int split_range = -1;
+    for (int i = 0; i < sch.n; ++i) {
+        a.rng_end[i] = sch.end[i];
+        a.rng_group[i] = sch.group[i];
+        a.rng_first[i] = sch.first[i];
+        a.rng_count[i] = sch.count[i];
+        a.rng_split[i] = sch.split[i];
+        if (sch.split[i] > 1) split_range = i;
+    }
+    const dim3 grid((unsigned)sch.items);
+    if (sch.n == 1 && split_range < 0 && sch.group[0] != 0) {  // the single-range kernel reads grp[0]
+        a.grp[0] = a.grp[sch.group[0]];
+        a.rng_group[0] = 0;
+    }
+    if (sch.n > 1 || split_range >= 0) {
+        attention_fwd_kernel<false, true, true><<<grid, kThreads, 0, stream>>>(a);
+        attention_fwd_kernel<false, false, true><<<grid, kThreads, 0, stream>>>(a);
+    } else if (sch.n == 1) {
+        attention_fwd_kernel<false, true, false><<<grid, kThreads, 0, stream>>>(a);
+        attention_fwd_kernel<false, false, false><<<grid, kThreads, 0, stream>>>(a);
+    }
+    if (split_range >= 0) {
+        const AttnGroup &G = a.grp[sch.group[split_range]];
+        attn_merge_kernel<<<dim3((unsigned)sch.split_items, BQ / 64), 256, 0, stream>>>(
+            a.part, a.part_records, sch.pieces, sch.first[split_range], G.tiles_per_head, G.rows, G.o, ld_o);
     }
     // Zero the rows of o outside every group (the padding suffix included).
     std::sort(cov, cov + nc);
@@ -951,11 +1041,12 @@ void launch_sparse_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k,
     a.n_kb = (int32_t)((T + BKV - 1) / BKV);
     a.pre_tiles = (int32_t)((prefix_len + BQ - 1) / BQ);
     a.pre_items = (heads * a.pre_tiles + 7) / 8 * 8;
-    a.n_groups = 1;
+    a.n_ranges = 1;
+    a.rng_split[0] = 1;
     a.prefix_len = prefix_len;
     a.tgt_rows = T;
     const unsigned grid = (unsigned)(a.pre_items + G.tiles_per_head * heads);
-    a.item_end[0] = (int32_t)grid;
+    a.rng_end[0] = (int32_t)grid;
     attention_fwd_kernel<true, true, false><<<dim3(grid), kThreads, 0, stream>>>(a);
     attention_fwd_kernel<true, false, false><<<dim3(grid), kThreads, 0, stream>>>(a);
     launch_zero_rows(o, ld_o, (int64_t)heads * D, valid_len, L_buf, stream);

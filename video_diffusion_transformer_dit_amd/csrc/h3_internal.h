@@ -27,10 +27,35 @@ struct VtSeg {
     int64_t ld, begin, len, lpad;
     int64_t off;          // byte offset inside the V^T staging area
 };
+// Work schedule of one attention launch. A work item is one 256-row query
+// tile of one head of one group ("(head, tile) item"), or a piece of one: its
+// keys cut into `split` consecutive ranges of key tiles whose partial
+// results a merge pass combines. Ranges of items are dispatched in order:
+// the group whose items read the most keys first; if it fills less than
+// four rounds of the chip's 256 workgroup slots, its last, partial round is
+// cut into pieces (2 to 4, at least 4 key tiles each) so the round is full;
+// then the other groups, longest items first. With more than one range, each
+// range is padded to a multiple of 8 items so that it starts on XCD 0 (also
+// a single range cut into pieces).
+constexpr int kAttnSlots = 256;
+struct AttnSchedule {
+    int n;                                // ranges
+    int group[H3_MAX_GROUPS + 1];         // caller's group index of each range
+    int32_t first[H3_MAX_GROUPS + 1];     // first (head, tile) item of the group in the range
+    int32_t count[H3_MAX_GROUPS + 1];     // (head, tile) items in the range
+    int32_t split[H3_MAX_GROUPS + 1];     // pieces per item (1: whole)
+    int32_t end[H3_MAX_GROUPS + 1];       // exclusive end of the range's work items
+    int32_t items;                        // work items of the launch
+    int32_t split_items, pieces;          // (head, tile) items cut into pieces, pieces per item
+};
+// groups == NULL schedules one dense group of dense_len rows over keys [0, dense_len).
+void attn_schedule(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads, AttnSchedule *out);
+
 struct VtPlan {
     int n;
     VtSeg seg[H3_MAX_GROUPS * H3_MAX_SEGMENTS];
     int map[H3_MAX_GROUPS][H3_MAX_SEGMENTS];  // (group, segment) -> seg index
+    int64_t part_off;     // byte offset of the split items' partial results (FP32 O, then (m, l) per row)
     int64_t kmax_off;     // byte offset of the per-head key norm maxima
     int64_t flags_off;    // byte offset of one int32 per attention workgroup
     size_t bytes;

@@ -116,6 +116,67 @@ void sparse_vt_group(int64_t valid_len, int64_t prefix_len, h3_qgroup *g) {
     g->seg[1] = h3_kv_seg{nullptr, nullptr, 0, prefix_len, valid_len - prefix_len};
 }
 
+void attn_schedule(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads, AttnSchedule *out) {
+    std::memset(out, 0, sizeof(*out));
+    int order[H3_MAX_GROUPS];
+    int64_t rows[H3_MAX_GROUPS], kt[H3_MAX_GROUPS];
+    int nc = 0;
+    if (groups == nullptr) {
+        if (dense_len > 0) {
+            rows[0] = dense_len;
+            kt[0] = (dense_len + 63) / 64;
+            order[nc++] = 0;
+        }
+    } else {
+        for (int g = 0; g < n_groups && g < H3_MAX_GROUPS; ++g) {
+            rows[g] = groups[g].q_end - groups[g].q_begin;
+            if (rows[g] <= 0) continue;
+            kt[g] = 0;
+            for (int s = 0; s < groups[g].n_seg && s < H3_MAX_SEGMENTS; ++s)
+                kt[g] += (std::max<int64_t>(groups[g].seg[s].len, 0) + 63) / 64;
+            order[nc++] = g;
+        }
+    }
+    std::stable_sort(order, order + nc, [&](int x, int y) { return kt[x] > kt[y]; });
+    auto add = [&](int g, int32_t first, int32_t count, int32_t split) {
+        out->group[out->n] = g;
+        out->first[out->n] = first;
+        out->count[out->n] = count;
+        out->split[out->n] = split;
+        ++out->n;
+    };
+    for (int oi = 0; oi < nc; ++oi) {
+        const int g = order[oi];
+        const int32_t n = (int32_t)((rows[g] + 255) / 256) * heads;
+        int32_t pieces = 1, full = n;
+        if (oi == 0 && n < 4 * kAttnSlots) {
+            full = n / kAttnSlots * kAttnSlots;
+            const int32_t tail = n - full;
+            if (tail > 0) {
+                pieces = (int32_t)std::min<int64_t>({4, (kAttnSlots + tail - 1) / tail, kt[g] / 4});
+                if (pieces < 2) {
+                    pieces = 1;
+                    full = n;
+                }
+            }
+        }
+        if (full > 0) add(g, 0, full, 1);
+        if (pieces > 1) {
+            add(g, full, n - full, pieces);
+            out->split_items = n - full;
+            out->pieces = pieces;
+        }
+    }
+    int32_t items = 0;
+    const bool multi = out->n > 1 || out->pieces > 1;
+    for (int i = 0; i < out->n; ++i) {
+        const int32_t c = out->count[i] * out->split[i];
+        items += multi ? (c + 7) / 8 * 8 : c;
+        out->end[i] = items;
+    }
+    out->items = items;
+}
+
 void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads, VtPlan *out) {
     out->n = 0;
     out->bytes = 0;
@@ -149,16 +210,26 @@ void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads
         }
     }
     out->flags_off = 0;
+    out->part_off = 0;
     if (out->n > 0) {
         auto align = [](size_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; };
+        // Partial results of the items cut into pieces: a partial round has
+        // fewer than 256 items, each cut into at most ceil(256 / items)
+        // pieces, so fewer than 512 records of 256 rows in all, and at most 4
+        // per item. Reserved from the row count alone so that the size never
+        // shrinks as rows grow (a dense plan for the buffer rows also fits
+        // any valid length below them).
+        const int64_t records = std::min<int64_t>(511, 4 * qtiles * heads);
+        out->part_off = (int64_t)out->bytes;
+        out->bytes += align((size_t)records * 256 * (kHeadDim + 2) * 4);
         out->kmax_off = (int64_t)out->bytes;
         out->bytes += align((size_t)heads * 4);
         // workgroups of the launch: query tiles of 256 rows per head and group,
-        // each group padded to a multiple of 8, plus the block-sparse launch's
-        // split of the rows into prefix and target tiles (at most one more tile
-        // per head)
+        // plus the block-sparse launch's split of the rows into prefix and
+        // target tiles (at most one more tile per head)
+        // (pieces add fewer than 512 items; every range may be padded by 7)
         out->flags_off = (int64_t)out->bytes;
-        out->bytes += align((size_t)((qtiles + 1) * heads + 8 * n_launch_groups) * 4);
+        out->bytes += align((size_t)((qtiles + 1) * heads + 8 * (n_launch_groups + 1) + 512) * 4);
     }
 }
 
