@@ -19,9 +19,12 @@ namespace h3 {
 namespace {
 
 // ---------------------------------------------------------------------------
-// modulate-norm: one wavefront owns ROWS rows; lane i holds 16-byte chunks
-// i, i+64, ... of each row in registers (NCH chunks max), so x (and the
-// branch) are read once and h (and x1) written once.
+// modulate-norm: SPAN lanes own ROWS rows (SPAN 64: one wavefront, ROWS rows;
+// SPAN 256: the whole workgroup, one row); lane i holds 16-byte chunks
+// i, i+SPAN, ... of each row in registers (NCH chunks max), so x (and the
+// branch) are read once and h (and x1) written once. Wide rows take a
+// workgroup each: the row's loads then leave every wave at once instead of
+// one wave issuing them chunk after chunk.
 // ---------------------------------------------------------------------------
 struct ModnormArgs {
     const uint16_t *x;
@@ -71,11 +74,30 @@ __device__ __forceinline__ void load_f8(const float *p, float f[8]) {
 // fused quantizing producer of Sol-H3 report, §3.3 "MXFP8 GEMM computation").
 // A 32-wide group is the 4 consecutive chunks of 4 consecutive lanes; the 4
 // groups of a 128-wide scale slab are the chunks of 16 consecutive lanes.
-template <int NCH, int ROWS, bool BRANCH, int NORM, bool LORA = false, bool MX = false>
+// Row sum of the per-lane partial sums v[0..3], in one association for both
+// spans, so that every instance gives the same bits: with SPAN 256, thread
+// 64 w + l holds the chunks w * 64 + l + 256 i in v[0]; with SPAN 64, lane l
+// holds the chunks l + 64 (4 i + w) in v[w]. Either way the result is
+// (S_0 + S_1) + (S_2 + S_3), S_w the wave sum of the chunks with
+// (c / 64) % 4 == w, each lane adding its chunks in increasing order.
+template <int SPAN>
+__device__ __forceinline__ float row_sum(const float (&v)[4], float *red) {
+    if (SPAN == 64)
+        return (wave_sum(v[0]) + wave_sum(v[1])) + (wave_sum(v[2]) + wave_sum(v[3]));
+    const float w = wave_sum(v[0]);
+    __syncthreads();  // red may still be read by a previous sum
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = w;
+    __syncthreads();
+    return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+template <int NCH, int ROWS, bool BRANCH, int NORM, bool LORA = false, bool MX = false, int SPAN = 64>
 __global__ __launch_bounds__(256) void modnorm_kernel(ModnormArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * ROWS;
-    if (r0 >= a.L_buf) return;
+    static_assert(SPAN == 64 || (SPAN == 256 && ROWS == 1), "a workgroup-wide row span owns one row");
+    __shared__ float red[4];
+    const int lane = SPAN == 64 ? (int)(threadIdx.x & 63) : (int)threadIdx.x;  // chunk lane within the row
+    const int64_t r0 = SPAN == 64 ? ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * ROWS : (int64_t)blockIdx.x;
+    if (r0 >= a.L_buf) return;  // uniform over the row's lanes
     const int nch = a.hidden >> 3;
 
     uint4 xv[ROWS][NCH];
@@ -93,12 +115,15 @@ __global__ __launch_bounds__(256) void modnorm_kernel(ModnormArgs a) {
 
     // Pass 1: load rows (forming x1 = x + gate * branch), accumulate the sum of
     // squares (RMSNorm) or the sum (LayerNorm).
-    float acc[ROWS];
+    float acc[ROWS][4];
 #pragma unroll
-    for (int p = 0; p < ROWS; ++p) acc[p] = 0.f;
+    for (int p = 0; p < ROWS; ++p)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc[p][w] = 0.f;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-        const int c = lane + 64 * i;
+        const int c = lane + SPAN * i;
+        const int w = SPAN == 64 ? (i & 3) : 0;  // partial sum of the chunk (see row_sum)
         if (c < nch) {
             float gv[8];
             int gcur = -1;
@@ -133,24 +158,27 @@ __global__ __launch_bounds__(256) void modnorm_kernel(ModnormArgs a) {
                 float xf[8];
                 unpack8(xw, xf);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[p] += NORM == 0 ? xf[e] * xf[e] : xf[e];
+                for (int e = 0; e < 8; ++e) acc[p][w] += NORM == 0 ? xf[e] * xf[e] : xf[e];
             }
         }
     }
     float mean[ROWS], inv[ROWS];
 #pragma unroll
     for (int p = 0; p < ROWS; ++p) {
-        const float s = wave_sum(acc[p]);
+        const float s = row_sum<SPAN>(acc[p], red);
         mean[p] = NORM == 0 ? 0.f : s / (float)a.hidden;
         if (NORM == 0) inv[p] = rsqrtf(s / (float)a.hidden + a.eps);
     }
     if (NORM == 1) {
         // two-pass population variance from the register copy
 #pragma unroll
-        for (int p = 0; p < ROWS; ++p) acc[p] = 0.f;
+        for (int p = 0; p < ROWS; ++p)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) acc[p][w] = 0.f;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
-            const int c = lane + 64 * i;
+            const int c = lane + SPAN * i;
+            const int w = SPAN == 64 ? (i & 3) : 0;
             if (c < nch) {
 #pragma unroll
                 for (int p = 0; p < ROWS; ++p) {
@@ -160,19 +188,19 @@ __global__ __launch_bounds__(256) void modnorm_kernel(ModnormArgs a) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const float dlt = xf[e] - mean[p];
-                        acc[p] += dlt * dlt;
+                        acc[p][w] += dlt * dlt;
                     }
                 }
             }
         }
 #pragma unroll
-        for (int p = 0; p < ROWS; ++p) inv[p] = rsqrtf(wave_sum(acc[p]) / (float)a.hidden + a.eps);
+        for (int p = 0; p < ROWS; ++p) inv[p] = rsqrtf(row_sum<SPAN>(acc[p], red) / (float)a.hidden + a.eps);
     }
 
     // Pass 2: h = n * (1 + scale) + shift; padding rows are written as zero.
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-        const int c = lane + 64 * i;
+        const int c = lane + SPAN * i;
         if (c < nch) {
             float sh[8], sc[8];
             int gcur = -1;
@@ -225,29 +253,55 @@ __global__ __launch_bounds__(256) void modnorm_kernel(ModnormArgs a) {
     }
 }
 
-template <int NCH>
+template <int NCH, int SPAN = 64>
 void modnorm_dispatch_nch(const ModnormArgs &a, bool branch, int norm, hipStream_t s, bool lora = false,
                           bool mx = false) {
-    constexpr int ROWS = 2;
+    constexpr int ROWS = SPAN == 64 ? 2 : 1;
     const int64_t waves = (a.L_buf + ROWS - 1) / ROWS;
-    const dim3 grid((unsigned)((waves + 3) / 4));
+    const dim3 grid((unsigned)(SPAN == 64 ? (waves + 3) / 4 : a.L_buf));
     if (mx) {
         if (branch) {
-            if (norm == 0) modnorm_kernel<NCH, ROWS, true, 0, false, true><<<grid, 256, 0, s>>>(a);
-            else modnorm_kernel<NCH, ROWS, true, 1, false, true><<<grid, 256, 0, s>>>(a);
+            if (norm == 0) modnorm_kernel<NCH, ROWS, true, 0, false, true, SPAN><<<grid, 256, 0, s>>>(a);
+            else modnorm_kernel<NCH, ROWS, true, 1, false, true, SPAN><<<grid, 256, 0, s>>>(a);
         } else {
-            if (norm == 0) modnorm_kernel<NCH, ROWS, false, 0, false, true><<<grid, 256, 0, s>>>(a);
-            else modnorm_kernel<NCH, ROWS, false, 1, false, true><<<grid, 256, 0, s>>>(a);
+            if (norm == 0) modnorm_kernel<NCH, ROWS, false, 0, false, true, SPAN><<<grid, 256, 0, s>>>(a);
+            else modnorm_kernel<NCH, ROWS, false, 1, false, true, SPAN><<<grid, 256, 0, s>>>(a);
         }
     } else if (lora) {
-        if (norm == 0) modnorm_kernel<NCH, ROWS, true, 0, true><<<grid, 256, 0, s>>>(a);
-        else modnorm_kernel<NCH, ROWS, true, 1, true><<<grid, 256, 0, s>>>(a);
+        if (norm == 0) modnorm_kernel<NCH, ROWS, true, 0, true, false, SPAN><<<grid, 256, 0, s>>>(a);
+        else modnorm_kernel<NCH, ROWS, true, 1, true, false, SPAN><<<grid, 256, 0, s>>>(a);
     } else if (branch) {
-        if (norm == 0) modnorm_kernel<NCH, ROWS, true, 0><<<grid, 256, 0, s>>>(a);
-        else modnorm_kernel<NCH, ROWS, true, 1><<<grid, 256, 0, s>>>(a);
+        if (norm == 0) modnorm_kernel<NCH, ROWS, true, 0, false, false, SPAN><<<grid, 256, 0, s>>>(a);
+        else modnorm_kernel<NCH, ROWS, true, 1, false, false, SPAN><<<grid, 256, 0, s>>>(a);
     } else {
-        if (norm == 0) modnorm_kernel<NCH, ROWS, false, 0><<<grid, 256, 0, s>>>(a);
-        else modnorm_kernel<NCH, ROWS, false, 1><<<grid, 256, 0, s>>>(a);
+        if (norm == 0) modnorm_kernel<NCH, ROWS, false, 0, false, false, SPAN><<<grid, 256, 0, s>>>(a);
+        else modnorm_kernel<NCH, ROWS, false, 1, false, false, SPAN><<<grid, 256, 0, s>>>(a);
+    }
+}
+
+// Plain modulate-norm rows of 2,048 channels or more take a workgroup each
+// (SPAN 256: 0.35 -> 0.29 ms at 58,758 x 5,376); with the residual branch,
+// which moves twice the bytes per row, two rows per wavefront (SPAN 64) stay
+// faster (0.51 vs 0.58 ms), as do narrow rows. NCH covers the row's chunks.
+void modnorm_dispatch(const ModnormArgs &a, bool branch, int norm, hipStream_t s, bool lora, bool mx) {
+    const int nch = a.hidden / 8;
+    if (!branch && nch >= 256) {
+        const int need = (nch + 255) / 256;
+        if (need <= 1) modnorm_dispatch_nch<1, 256>(a, branch, norm, s, lora, mx);
+        else if (need <= 2) modnorm_dispatch_nch<2, 256>(a, branch, norm, s, lora, mx);
+        else if (need <= 3) modnorm_dispatch_nch<3, 256>(a, branch, norm, s, lora, mx);
+        else if (need <= 4) modnorm_dispatch_nch<4, 256>(a, branch, norm, s, lora, mx);
+        else modnorm_dispatch_nch<8, 256>(a, branch, norm, s, lora, mx);
+    } else {
+        const int need = (nch + 63) / 64;
+        if (need <= 1) modnorm_dispatch_nch<1>(a, branch, norm, s, lora, mx);
+        else if (need <= 2) modnorm_dispatch_nch<2>(a, branch, norm, s, lora, mx);
+        else if (need <= 4) modnorm_dispatch_nch<4>(a, branch, norm, s, lora, mx);
+        else if (need <= 8) modnorm_dispatch_nch<8>(a, branch, norm, s, lora, mx);
+        else if (need <= 11) modnorm_dispatch_nch<11>(a, branch, norm, s, lora, mx);
+        else if (need <= 16) modnorm_dispatch_nch<16>(a, branch, norm, s, lora, mx);
+        else if (need <= 24) modnorm_dispatch_nch<24>(a, branch, norm, s, lora, mx);
+        else modnorm_dispatch_nch<32>(a, branch, norm, s, lora, mx);
     }
 }
 
@@ -442,16 +496,8 @@ void launch_modnorm(const uint16_t *x, int64_t ld_x, const uint16_t *branch, int
     a.ld_x = ld_x; a.ld_b = ld_b; a.ld_x1 = ld_x1; a.ld_h = ld_h;
     a.ld_mod = n_mod_groups > 1 ? ld_mod_group : 0;
     a.L_buf = L_buf; a.valid = valid_len; a.hidden = hidden; a.n_groups = n_mod_groups; a.eps = eps;
-    const int need = (hidden / 8 + 63) / 64;
     const bool b = branch != nullptr;
-    if (need <= 1) modnorm_dispatch_nch<1>(a, b, norm_type, stream);
-    else if (need <= 2) modnorm_dispatch_nch<2>(a, b, norm_type, stream);
-    else if (need <= 4) modnorm_dispatch_nch<4>(a, b, norm_type, stream);
-    else if (need <= 8) modnorm_dispatch_nch<8>(a, b, norm_type, stream);
-    else if (need <= 11) modnorm_dispatch_nch<11>(a, b, norm_type, stream);
-    else if (need <= 16) modnorm_dispatch_nch<16>(a, b, norm_type, stream);
-    else if (need <= 24) modnorm_dispatch_nch<24>(a, b, norm_type, stream);
-    else modnorm_dispatch_nch<32>(a, b, norm_type, stream);
+    modnorm_dispatch(a, b, norm_type, stream, false, false);
 }
 
 void launch_qk_norm_rope(uint16_t *q, uint16_t *k, int64_t ld, const uint16_t *q_gain, const uint16_t *k_gain,
@@ -485,16 +531,8 @@ void launch_modnorm_mx(const uint16_t *x, int64_t ld_x, const uint16_t *branch, 
     a.ld_x = ld_x; a.ld_b = ld_b; a.ld_x1 = ld_x1; a.ld_h = 0;
     a.ld_mod = n_mod_groups > 1 ? ld_mod_group : 0;
     a.L_buf = L_buf; a.valid = valid_len; a.hidden = hidden; a.n_groups = n_mod_groups; a.eps = eps;
-    const int need = (hidden / 8 + 63) / 64;
     const bool b = branch != nullptr;
-    if (need <= 1) modnorm_dispatch_nch<1>(a, b, norm_type, stream, false, true);
-    else if (need <= 2) modnorm_dispatch_nch<2>(a, b, norm_type, stream, false, true);
-    else if (need <= 4) modnorm_dispatch_nch<4>(a, b, norm_type, stream, false, true);
-    else if (need <= 8) modnorm_dispatch_nch<8>(a, b, norm_type, stream, false, true);
-    else if (need <= 11) modnorm_dispatch_nch<11>(a, b, norm_type, stream, false, true);
-    else if (need <= 16) modnorm_dispatch_nch<16>(a, b, norm_type, stream, false, true);
-    else if (need <= 24) modnorm_dispatch_nch<24>(a, b, norm_type, stream, false, true);
-    else modnorm_dispatch_nch<32>(a, b, norm_type, stream, false, true);
+    modnorm_dispatch(a, b, norm_type, stream, false, true);
 }
 
 // LoRA consumer variants: the consumer rounds base + delta to BF16 first.
@@ -511,15 +549,7 @@ void launch_modnorm_lora(const uint16_t *x, int64_t ld_x, const uint16_t *branch
     a.ld_x = ld_x; a.ld_b = ld_b; a.ld_x1 = ld_x1; a.ld_h = ld_h;
     a.ld_mod = n_mod_groups > 1 ? ld_mod_group : 0;
     a.L_buf = L_buf; a.valid = valid_len; a.hidden = hidden; a.n_groups = n_mod_groups; a.eps = eps;
-    const int need = (hidden / 8 + 63) / 64;
-    if (need <= 1) modnorm_dispatch_nch<1>(a, true, norm_type, stream, true);
-    else if (need <= 2) modnorm_dispatch_nch<2>(a, true, norm_type, stream, true);
-    else if (need <= 4) modnorm_dispatch_nch<4>(a, true, norm_type, stream, true);
-    else if (need <= 8) modnorm_dispatch_nch<8>(a, true, norm_type, stream, true);
-    else if (need <= 11) modnorm_dispatch_nch<11>(a, true, norm_type, stream, true);
-    else if (need <= 16) modnorm_dispatch_nch<16>(a, true, norm_type, stream, true);
-    else if (need <= 24) modnorm_dispatch_nch<24>(a, true, norm_type, stream, true);
-    else modnorm_dispatch_nch<32>(a, true, norm_type, stream, true);
+    modnorm_dispatch(a, true, norm_type, stream, true, false);
 }
 
 void launch_qk_norm_rope_lora(uint16_t *q, uint16_t *k, uint16_t *v, int64_t ld, const uint16_t *dq,
