@@ -119,3 +119,35 @@ def test_stack_sampled_layers_match_oracle(stack):
                           ("x1", f64(inter(h3.H3_WS_X1)[rows])), ("h2", f64(inter(h3.H3_WS_H2)[rows])),
                           ("g", f64(inter(h3.H3_WS_G)[rows])), ("y", f64(y[rows]))):
             assert_parity(got, ref[name], f"layer {layer} {name}", slack=BF16_SLACK if name == "g" else 0.0)
+
+
+def test_stack_tiny_chain_matches_chained_oracle():
+    """The stack's semantics end to end at reduced width: 4 blocks x 2 steps,
+    each step's output feeding the next step, block b of step s reading table
+    entry (b, s); the oracle chains its own FP64 outputs the same way. After 8
+    blocks the GPU's BF16 rounding has compounded, so the bar is the per-block
+    one scaled by the number of blocks (8 x 1e-2 relative Frobenius)."""
+    s = I.TINY
+    nb, ns = 4, 2
+    blocks = [I.block_weights(s, f"stk{b}") for b in range(nb)]
+    mod = I.normal_f32("stk.mod", (nb, ns, 6, s.hidden), 0.1)
+    dims = h3.make_dims(s.hidden, s.heads, s.ffn, rot_dim=s.rot_dim, rope_theta=s.theta, eps=s.eps)
+    dev_w = [{k: dev_bf16(v) for k, v in w.items()} for w in blocks]
+    arr = h3.make_weight_stack([h3.make_weights(w) for w in dev_w])
+    md = torch.from_numpy(mod).cuda()
+    ws = torch.empty(h3.workspace_bytes(dims, s.L_buf), dtype=torch.uint8, device="cuda")
+    xb = I.activations(s, tag="stk.x")
+    x = dev_bf16(xb)
+    for st in range(ns):
+        h3.stack_forward(dims, arr, x, md[0, st], ns * 6 * s.hidden, 1, s.valid_len, ws)
+    torch.cuda.synchronize()
+    ref = O.bf16_to_f64(xb)
+    wo = [{k: O.bf16_to_f64(v) for k, v in w.items()} for w in blocks]
+    for st in range(ns):
+        for b in range(nb):
+            ref = O.block_forward(ref, wo[b], mod[b, st][None].astype(np.float64), heads=s.heads,
+                                  head_dim=s.head_dim, ffn=s.ffn, valid_len=s.valid_len, rot_dim=s.rot_dim,
+                                  theta=s.theta, eps=s.eps)["y"]
+    got = f64(x)
+    assert np.all(bits(x)[s.valid_len:] == 0)
+    assert_parity(got[:s.valid_len], ref[:s.valid_len], "stack y", rel_tol=nb * ns * 1e-2, max_tol=nb * ns * 5e-2)
