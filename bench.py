@@ -502,6 +502,15 @@ def main(argv=None) -> int:
         g, w["w_down"], y, V, h3.H3_EPI_RESIDUAL, resid=x1, gate=mod[:, 5], ld_gate_group=6 * H), kit, 1)
 
     progress("per-kernel breakdown timed")
+    # The online-softmax form on the same shape: q scaled by 8 puts every
+    # workgroup's score bound above the fixed-reference range (as trained
+    # models with large QK-norm gains would).
+    q8 = torch.empty_like(qkv[:, :H])
+    q8.copy_(qkv[:, :H]).mul_(8.0)
+    k_ms["attention_online"] = time_calls(torch, lambda: h3.attention(
+        q8, qkv[:, H:2 * H], qkv[:, 2 * H:], o, V, heads, workspace=vt_ws), kit, 1)
+    del q8
+    h3.attention(qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:], o, V, heads, workspace=vt_ws)  # o back to the block's
     # Measured ceilings on this GPU: a plain device copy (what the memory-bound
     # kernels can hope for) and the vendor library's BF16 GEMM on the QKV shape
     # (hipBLASLt through torch.matmul, no epilogue).
@@ -516,7 +525,8 @@ def main(argv=None) -> int:
 
     gemm_f, attn_f = block_flops(V, H, F)
     gflops = {"gemm_qkv": 2.0 * V * H * 3 * H, "gemm_out_residual": 2.0 * V * H * H,
-              "gemm_up_swiglu": 2.0 * V * H * 2 * F, "gemm_down_residual": 2.0 * V * F * H, "attention": attn_f}
+              "gemm_up_swiglu": 2.0 * V * H * 2 * F, "gemm_down_residual": 2.0 * V * F * H, "attention": attn_f,
+              "attention_online": attn_f}
     ebytes = elementwise_bytes(V, H, F)
     kernels = {}
     for k, t in k_ms.items():
