@@ -240,6 +240,36 @@ def test_attention_single_key_is_exact():
     assert_zero_rows(o, 1, "o")
 
 
+@pytest.mark.parametrize("segs,q_scale", [((320, 300), 1.0), ((130, 260, 70), 1.0), ((130, 260, 70), 8.0),
+                                          ((64, 64, 64, 300), 1.0), ((500, 524), 1.0), ((500, 524), 8.0)])
+def test_attention_key_range_pieces(segs, q_scale):
+    """One query tile whose keys are several segments: the work schedule cuts
+    it into key-range pieces (a piece may start exactly at a segment boundary
+    or inside a segment, and end on a segment's ragged last tile), merged by
+    the merge pass; also with peaked scores (q x 8: the online form, pieces
+    with different row maxima)."""
+    heads, rows = 1, 200
+    H = heads * 128
+    tiles = sum((n + 63) // 64 for n in segs)
+    _say(f"attention pieces segs={segs} key tiles={tiles} q_scale={q_scale}")
+    Lk = sum(segs)
+    qb = I.normal_bf16("apc.q", (rows, H), q_scale)
+    kb = I.normal_bf16("apc.k", (Lk, H))
+    vb = I.normal_bf16("apc.v", (Lk, H))
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    # external segments of one K/V buffer, consecutive
+    seg_list, begin = [], 0
+    for n in segs:
+        seg_list.append((k, v, begin, n))
+        begin += n
+    o = poison((rows, H))
+    h3.attention(q, q, q, o, rows, heads, groups=[(0, rows, seg_list)])
+    torch.cuda.synchronize()
+    K, Vv = O.bf16_to_f64(kb), O.bf16_to_f64(vb)
+    ref = O.attention_grouped(O.bf16_to_f64(qb), [(0, rows, [(K, Vv)])], heads, 128, rows)
+    assert_parity(f64(o), ref, "o")
+
+
 def test_attention_grouped_with_history():
     """Query groups over [external history ; own keys] segments; rows outside
     every group are zero (the streaming chunk's structure, scaled down)."""
