@@ -19,6 +19,7 @@ import argparse
 import json
 import statistics
 import os
+import platform
 import sys
 import time
 
@@ -118,7 +119,13 @@ def cpu_baseline(seconds_target: float = 20.0):
     g_s, a_s = block_flops(L, 5376, 21504)
     g_f, a_f = block_flops(58758, 5376, 21504)
     ms_full = dt * 1e3 * (g_f + a_f) / (g_s + a_s)
-    return {"value": round(ms_full, 1), "unit": "ms/block", "cores": int(threads), "kind": "oracle",
+    cpu = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
+    except OSError:  # pragma: no cover
+        pass
+    return {"value": round(ms_full, 1), "unit": "ms/block", "cores": int(threads), "cpu": cpu, "kind": "oracle",
             "sample": f"FP64 numpy oracle, one full-width block (H 5376, 42x128, F 21504) at {L} tokens: "
                       f"{dt:.2f} s for {(g_s + a_s) / 1e12:.3f} TFLOP, scaled by algorithmic flops to the "
                       f"58,758-token block ({(g_f + a_f) / 1e12:.1f} TFLOP)",
