@@ -446,7 +446,7 @@ def main(argv=None) -> int:
                          "FETCH_SIZE / WRITE_SIZE counters)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); the library has no multi-GPU path.",
               file=sys.stderr)
         return 2
 
