@@ -194,6 +194,35 @@ def test_rope_invariants():
     np.testing.assert_allclose(s1, s2, rtol=1e-9, atol=1e-9)
 
 
+def test_qk_norm_rope_composition():
+    """QK-norm then RoPE (readings R6-R8), pinned through cases with a closed
+    form: a head holding only channels 0 and R/2 normalises to (3, 4) / rms
+    times its gains and then turns by the angle pos * theta^0 = pos
+    (rotate-half pairing); position 0 leaves the plain per-head norm; with unit
+    gains every head keeps RMS 1 at any position, since the rotation preserves
+    the norm."""
+    heads, d, R, eps = 2, 128, 64, 1e-6
+    g = 1.0 + 0.25 * np.arange(d) / d       # distinct gain per channel: gain before rotation is visible
+    t = np.zeros((1, heads * d))
+    t[0, 0], t[0, R // 2] = 3.0, 4.0
+    p = 0.7
+    out = O.qk_norm_rope(t, np.array([p]), heads, d, g, eps, R, 1e4)
+    rms = math.sqrt((9.0 + 16.0) / d + eps)
+    a, b = 3.0 / rms * g[0], 4.0 / rms * g[R // 2]
+    np.testing.assert_allclose(out[0, 0], a * math.cos(p) - b * math.sin(p), rtol=1e-14)
+    np.testing.assert_allclose(out[0, R // 2], a * math.sin(p) + b * math.cos(p), rtol=1e-14)
+    others = np.delete(np.arange(heads * d), [0, R // 2])
+    np.testing.assert_array_equal(out[0, others], 0.0)
+    # position 0: no rotation
+    L = 8
+    x = RNG.standard_normal((L, heads * d))
+    np.testing.assert_array_equal(O.qk_norm_rope(x, np.zeros(L), heads, d, g, eps, R, 1e4),
+                                  O.head_rms_norm(x, heads, d, g, eps))
+    # unit gains: RMS 1 per head after the rotation, at arbitrary positions
+    y = O.qk_norm_rope(x * 7.5, np.arange(L) * 4099, heads, d, np.ones(d), 0.0, R, 1e4)
+    np.testing.assert_allclose(np.sqrt(np.mean(y.reshape(L, heads, d) ** 2, axis=-1)), 1.0, rtol=1e-13)
+
+
 # --------------------------------------------------------------------------
 # attention
 # --------------------------------------------------------------------------
