@@ -93,6 +93,15 @@ def test_modulation_special_cases():
     # gate = 0 leaves the residual stream unchanged, exactly
     br = RNG.standard_normal((4, 64)) * 1e3
     np.testing.assert_array_equal(O.gated_residual(x, np.zeros(64), br), x)
+    # gate = 1 adds the branch; gate = -1 on branch = x cancels the stream; the
+    # gate is per channel
+    np.testing.assert_array_equal(O.gated_residual(x, np.ones(64), br), x + br)
+    np.testing.assert_array_equal(O.gated_residual(x, -np.ones(64), x), np.zeros_like(x))
+    gch = np.zeros(64)
+    gch[7] = 2.0
+    out = O.gated_residual(x, gch, br)
+    np.testing.assert_array_equal(out[:, 7], x[:, 7] + 2.0 * br[:, 7])
+    np.testing.assert_array_equal(np.delete(out, 7, axis=1), np.delete(x, 7, axis=1))
 
 
 def test_gather_mod_indexing():
