@@ -203,6 +203,25 @@ def test_attention_dense(heads, L, V, q_scale, packed):
     assert_zero_rows(o, V, "o")
 
 
+@pytest.mark.parametrize("V", [2, 31, 32, 33, 63, 64, 65, 95, 96, 97, 255, 256, 257, 511, 513])
+@pytest.mark.parametrize("q_scale", [1.0, 8.0])
+def test_attention_lengths_at_tile_boundaries(V, q_scale):
+    """Valid lengths on both sides of every boundary the kernel has: 32-key
+    half tiles, 64-key K/V tiles and 256-query workgroup tiles (the last tile
+    of a length is partly masked, or exactly full), for the fixed-reference
+    (q x 1) and the online (q x 8) form, in a buffer 7 rows longer."""
+    heads, L = 2, V + 7
+    _say(f"attention lengths heads={heads} L={L} V={V} q_scale={q_scale}")
+    H = heads * 128
+    qb, kb, vb = _qkv(L, heads, f"alen{V}", q_scale)
+    o = poison((L, H))
+    h3.attention(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), o, V, heads)
+    torch.cuda.synchronize()
+    ref = O.attention(O.bf16_to_f64(qb[:V]), O.bf16_to_f64(kb[:V]), O.bf16_to_f64(vb[:V]), heads, 128)
+    assert_parity(f64(o)[:V], ref, "o")
+    assert_zero_rows(o, V, "o")
+
+
 def test_attention_fixed_and_online_workgroups_in_one_call():
     """Query tiles whose score bound |q| max|k| allows a fixed softmax
     reference and tiles whose bound does not (their q scaled by 8) in one
