@@ -584,9 +584,10 @@ int h3_check_qk_norm_rope(const uint16_t *q, const uint16_t *k, int64_t ld,
 int h3_check_swiglu(const uint16_t *u, int64_t ld_u, const uint16_t *g, int64_t ld_g,
                     int64_t L_buf, int64_t valid_len, int32_t ffn);
 int h3_check_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ldw,
-                    const uint16_t *c, int64_t ldc, int64_t M_buf, int64_t M_valid,
-                    int64_t N, int64_t K, int32_t epilogue, const uint16_t *resid,
-                    int64_t ld_r, const float *gate, int32_t n_mod_groups);
+                    const uint16_t *bias, const uint16_t *c, int64_t ldc, int64_t M_buf,
+                    int64_t M_valid, int64_t N, int64_t K, int32_t epilogue,
+                    const uint16_t *resid, int64_t ld_r, const float *gate,
+                    int64_t ld_gate_group, int32_t n_mod_groups);
 
 int h3_check_qk_norm_rope_lora(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t ld,
                                const uint16_t *dq, const uint16_t *dk, const uint16_t *dv, int64_t ld_d,

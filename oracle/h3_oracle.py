@@ -159,11 +159,15 @@ def gated_residual_bf16_product(x, gate, branch):
 def gather_mod(mod: np.ndarray, mod_idx, n_rows: int) -> np.ndarray:
     """Per-row modulation rows: entry mod_idx[r] of the [G, 6, H] table, or
     entry 0 for every row when no index is given (broadcast, reading R6).
+    An index outside [0, G) selects the nearest end of the table (entry 0 or
+    entry G - 1): the interface's rule for out-of-range indices, which the
+    pages leave open (reading R5).
     Returns [n_rows, 6, H] float64."""
     mod = np.asarray(mod, dtype=F64)
     if mod_idx is None:
         return np.broadcast_to(mod[0], (n_rows,) + mod.shape[1:])
-    return mod[np.asarray(mod_idx[:n_rows], dtype=np.int64)]
+    idx = np.clip(np.asarray(mod_idx[:n_rows], dtype=np.int64), 0, mod.shape[0] - 1)
+    return mod[idx]
 
 
 # ----------------------------------------------------------------------------

@@ -256,18 +256,42 @@ def test_elementwise_and_linear_validators():
     # swiglu
     assert lib.h3_check_swiglu(x, 2048, hh, 1024, L, L, 1024) == h3.H3_OK
     assert lib.h3_check_swiglu(x, 2048, x + 2048, 1024, L, L, 1024) == h3.H3_ERR_ALIAS
-    # linear
-    assert lib.h3_check_linear(x, 256, addr(7), 256, hh, 512, L, L, 512, 256, 0, None, 0, None, 1) == h3.H3_OK
-    assert lib.h3_check_linear(x, 256, addr(7), 256, hh, 512, L, L, 512, 204, 0, None, 0, None,
+    # linear (bias and the gate table's stride are checked by the twin too)
+    assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 256, 0, None, 0, None, 0,
+                               1) == h3.H3_OK
+    assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 204, 0, None, 0, None, 0,
                                1) == h3.H3_ERR_ALIGN
-    assert lib.h3_check_linear(x, 256, addr(7), 256, hh, 512, L, L, 512, 264, 0, None, 0, None,
+    assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 264, 0, None, 0, None, 0,
                                1) == h3.H3_ERR_UNSUPPORTED
-    assert lib.h3_check_linear(x, 256, addr(7), 256, hh, 512, L, L, 512, 256, 1, None, 0, None,
+    assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 256, 1, None, 0, None, 0,
                                1) == h3.H3_ERR_NULL
-    assert lib.h3_check_linear(x, 256, addr(7), 256, x, 512, L, L, 512, 256, 0, None, 0, None,
+    assert lib.h3_check_linear(x, 256, addr(7), 256, None, x, 512, L, L, 512, 256, 0, None, 0, None, 0,
                                1) == h3.H3_ERR_ALIAS
-    assert lib.h3_check_linear(x, 256, addr(7), 256, hh, 512, L, L, 512, 256, 3, None, 0, None,
+    assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 256, 3, None, 0, None, 0,
                                1) == h3.H3_ERR_UNSUPPORTED
+    # bias: 16-byte aligned, not inside c
+    assert lib.h3_check_linear(x, 256, addr(7), 256, addr(8), hh, 512, L, L, 512, 256, 0, None, 0, None, 0,
+                               1) == h3.H3_OK
+    assert lib.h3_check_linear(x, 256, addr(7), 256, addr(8) + 2, hh, 512, L, L, 512, 256, 0, None, 0, None, 0,
+                               1) == h3.H3_ERR_ALIGN
+    assert lib.h3_check_linear(x, 256, addr(7), 256, hh + 512 * 4, hh, 512, L, L, 512, 256, 0, None, 0, None, 0,
+                               1) == h3.H3_ERR_ALIAS
+    # gated residual: a table of G entries of N floats, ld_gate_group >= N apart
+    r, gt = addr(9), addr(10)
+    assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 256, 1, r, 512, gt, 6 * 512,
+                               3) == h3.H3_OK
+    assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 256, 1, r, 512, gt, 256,
+                               3) == h3.H3_ERR_SHAPE
+    assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 256, 1, r, 512, gt, -6 * 512,
+                               3) == h3.H3_ERR_SHAPE
+    assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 256, 1, r, 512, gt, 6 * 512 + 2,
+                               3) == h3.H3_ERR_ALIGN
+    # one table entry: the stride is unused
+    assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 256, 1, r, 512, gt, 0,
+                               1) == h3.H3_OK
+    # the gate table may not overlap c
+    assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 256, 1, r, 512, hh + 64, 6 * 512,
+                               3) == h3.H3_ERR_ALIAS
 
 
 def test_lora_consumer_validators():

@@ -23,8 +23,9 @@ from util import assert_parity, assert_zero_rows, dev_bf16, dev_f32, dev_i32, f6
 
 pytestmark = pytest.mark.gpu
 
-# Element-wise bar for outputs downstream of MXFP8 quantization points: one
-# E4M3 step relative to the element (2^-3), in place of the BF16 path's 5e-2.
+# Element-wise bar for the block output y, downstream of quantizers whose
+# inputs differ by a BF16 last bit between the GPU and the oracle: one E4M3
+# step (2^-3 of the RMS), in place of the BF16 path's 5e-2.
 MX_MAX = 2.0 ** -3
 
 
@@ -416,13 +417,18 @@ def test_block_mxfp8_sparse_tiny():
 def test_block_mxfp8_full_58816_sampled_rows():
     """The MXFP8 block at the benchmarked workload (58,758 valid rows in a
     58,816-row buffer, full width): the oracle forms the MXFP8 K and V of every
-    valid row and every other step on sampled rows. The BF16 intermediates
-    (q~, k~, v, o, x1) and y must meet the parity bar's relative Frobenius
-    error. Element-wise, a quantizing step turns a last-bit difference of its
-    input into a whole E4M3 step (at most 2^-3 of the element) on a few
-    elements, and three such steps feed y, so the max-error bar for the
-    MXFP8 path is one E4M3 step, 2^-3 of the RMS, instead of 5e-2. Padding
-    rows are zero."""
+    valid row and every other step on sampled rows. Every output must meet
+    the parity bar's relative Frobenius error. Element-wise, the BF16 bar
+    (5e-2 of the RMS) holds for q~, k~, v and o, whose only quantized inputs
+    are h and the weights (FP32 on the GPU, FP64 in the oracle: they round to
+    different E4M3 codes only when they straddle a rounding point within an
+    FP32 ulp), and for x1, where the quantized o enters through the small
+    attention gate. y is the one output fed by quantizers of values that
+    differ by a BF16 last bit between the two sides (o, and through x1 the
+    FFN-side h2 and g): there a last-bit difference becomes a whole E4M3 step
+    (at most 2^-3 of the element) on a few percent of the elements, and the
+    gated FFN branch carries them into y at full weight, so y's max-error
+    bar is one E4M3 step, 2^-3 of the RMS. Padding rows are zero."""
     _say("block mxfp8 full 58816 (sampled rows)")
     s = I.FULL_58816
     V, H = s.valid_len, s.hidden
@@ -440,5 +446,5 @@ def test_block_mxfp8_full_58816_sampled_rows():
                       ("o", b.bf16(h3.H3_MXWS_O, H)[rt].float().cpu().numpy().astype(np.float64)),
                       ("x1", b.bf16(h3.H3_MXWS_X1, H)[rt].float().cpu().numpy().astype(np.float64)),
                       ("y", y[rt].float().cpu().numpy().astype(np.float64))):
-        assert_parity(got, ref[name], f"mx58816 {name}", max_tol=MX_MAX)
+        assert_parity(got, ref[name], f"mx58816 {name}", max_tol=MX_MAX if name == "y" else 5e-2)
     assert_zero_rows(y, V, "y")

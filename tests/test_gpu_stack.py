@@ -124,9 +124,11 @@ def test_stack_sampled_layers_match_oracle(stack):
 def test_stack_tiny_chain_matches_chained_oracle():
     """The stack's semantics end to end at reduced width: 4 blocks x 2 steps,
     each step's output feeding the next step, block b of step s reading table
-    entry (b, s); the oracle chains its own FP64 outputs the same way. After 8
-    blocks the GPU's BF16 rounding has compounded, so the bar is the per-block
-    one scaled by the number of blocks (8 x 1e-2 relative Frobenius)."""
+    entry (b, s); the oracle chains its own FP64 outputs the same way. Each
+    step's output is held to the per-block bar (1e-2 relative Frobenius,
+    5e-2 max/rms): the BF16 rounding does not compound past it over these 8
+    blocks (the modulated norms rescale every block's input, and the gated
+    branches add to the residual stream rather than multiply it)."""
     s = I.TINY
     nb, ns = 4, 2
     blocks = [I.block_weights(s, f"stk{b}") for b in range(nb)]
@@ -138,16 +140,15 @@ def test_stack_tiny_chain_matches_chained_oracle():
     ws = torch.empty(h3.workspace_bytes(dims, s.L_buf), dtype=torch.uint8, device="cuda")
     xb = I.activations(s, tag="stk.x")
     x = dev_bf16(xb)
-    for st in range(ns):
-        h3.stack_forward(dims, arr, x, md[0, st], ns * 6 * s.hidden, 1, s.valid_len, ws)
-    torch.cuda.synchronize()
     ref = O.bf16_to_f64(xb)
     wo = [{k: O.bf16_to_f64(v) for k, v in w.items()} for w in blocks]
     for st in range(ns):
+        h3.stack_forward(dims, arr, x, md[0, st], ns * 6 * s.hidden, 1, s.valid_len, ws)
+        torch.cuda.synchronize()
         for b in range(nb):
             ref = O.block_forward(ref, wo[b], mod[b, st][None].astype(np.float64), heads=s.heads,
                                   head_dim=s.head_dim, ffn=s.ffn, valid_len=s.valid_len, rot_dim=s.rot_dim,
                                   theta=s.theta, eps=s.eps)["y"]
-    got = f64(x)
-    assert np.all(bits(x)[s.valid_len:] == 0)
-    assert_parity(got[:s.valid_len], ref[:s.valid_len], "stack y", rel_tol=nb * ns * 1e-2, max_tol=nb * ns * 5e-2)
+        got = f64(x)
+        assert np.all(bits(x)[s.valid_len:] == 0)
+        assert_parity(got[:s.valid_len], ref[:s.valid_len], f"stack y after step {st}")

@@ -105,14 +105,27 @@ def test_modulation_special_cases():
 
 
 def test_gather_mod_indexing():
-    mod = RNG.standard_normal((3, 6, 8))
-    idx = np.array([2, 0, 1, 1, 2], dtype=np.int32)
-    g = O.gather_mod(mod, idx, 5)
-    for r in range(5):
-        np.testing.assert_array_equal(g[r], mod[idx[r]])
+    """Against another route to the same selection: a one-hot row matrix times
+    the flattened table (exact, since each row has a single 1), with the
+    one-hot column of an out-of-range index set by the interface rule
+    written out case by case (below 0 -> entry 0, G or above -> entry G - 1)."""
+    G = 3
+    mod = RNG.standard_normal((G, 6, 8))
+    idx = np.array([2, 0, 1, 1, 2, -1, 3, -2147483648, 2147483647, 1000], dtype=np.int32)
+    n = len(idx)
+    onehot = np.zeros((n, G))
+    for r, i in enumerate(idx.tolist()):
+        if i < 0:
+            onehot[r, 0] = 1.0
+        elif i >= G:
+            onehot[r, G - 1] = 1.0
+        else:
+            onehot[r, i] = 1.0
+    want = (onehot @ mod.reshape(G, -1)).reshape(n, 6, 8)
+    np.testing.assert_array_equal(O.gather_mod(mod, idx, n), want)
+    np.testing.assert_array_equal(O.gather_mod(mod, idx, 4), want[:4])
     g0 = O.gather_mod(mod, None, 5)
-    for r in range(5):
-        np.testing.assert_array_equal(g0[r], mod[0])
+    np.testing.assert_array_equal(g0, np.broadcast_to(mod[0], (5, 6, 8)))
 
 
 # --------------------------------------------------------------------------

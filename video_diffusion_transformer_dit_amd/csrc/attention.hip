@@ -24,17 +24,20 @@
 //    key index swapped) so each lane's 8 keys of a P.V k-step are one 16-byte
 //    LDS read.
 //  * Softmax in FP32 in the exp2 domain (scale * log2 e folded into one FMA),
-//    against a per-row reference m: p = exp2(s c - m). By Cauchy-Schwarz every
-//    score obeys |s c| <= B = |q| max|k| c, so when B <= 60 the reference is
-//    fixed at m = B: no p exceeds 1, none falls below 2^-120 (normal in FP32
-//    and BF16), and no running maximum or rescaling is needed. |q| comes from
-//    the workgroup's own Q registers, max|k| from a small pre-pass over the
-//    call's keys. The two forms are two instances of the kernel, launched
+//    against a per-row reference m: p = exp2(s c - m), with m the row's
+//    largest scaled score in the first half tile of keys. By Cauchy-Schwarz
+//    every score obeys |s c| <= B = |q| max|k| c, so when B <= 30 every
+//    later s c - m lies in [-2B, 2B]: no p leaves [2^-60, 2^60] (normal in
+//    FP32 and BF16), and m stays fixed, with no running maximum, check or
+//    rescaling. |q| comes from the workgroup's own Q registers, max|k| from
+//    the call's keys. The two forms are two instances of the kernel, launched
 //    back to back on the same grid: the fixed-reference instance handles
-//    every workgroup whose rows all have B <= 60 and flags the others, which
-//    the online instance then handles (m starts at the first half tile's
-//    maximum and O is rescaled only when some row maximum grew); it exits at
-//    once for the rest. P is rounded to BF16 for the P.V MFMA.
+//    every workgroup whose rows all have B <= 30 and flags the others, which
+//    the online instance then handles (m starts the same way and is raised,
+//    with O rescaled, only when some row maximum grew); it exits at once for
+//    the rest. P is rounded to BF16 for the P.V MFMA. The key that sets m
+//    gets p within 2^-19 of 1, so BF16(p) = 1: with one valid key both forms
+//    return that key's value exactly.
 //  * Workgroups are dealt round-robin over the 8 XCDs; work items are remapped
 //    so each XCD walks a contiguous range (consecutive query tiles of one
 //    head), so the workgroups resident on an XCD stream the same K/V through
@@ -256,8 +259,9 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     }
     // Score bound per query row (exp2 domain): B = |q| max|k| scale log2(e),
     // with a 2^-10 margin for the FP32 rounding of the norms. The lane pair
-    // (l, l ^ 32) holds the two halves of a row.
-    constexpr float kFixedMax = 60.0f;
+    // (l, l ^ 32) holds the two halves of a row. With B <= 30 and the
+    // reference taken from the first half tile, p stays in [2^-60, 2^60].
+    constexpr float kFixedMax = 30.0f;
     float bound[2];
     {
         const float km = a.kmax2[head];
@@ -491,19 +495,18 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     if (vk_cur < 32) mask(sv, vk_cur, false);
 
     // Softmax with a per-row reference maximum m_ref (exp2 domain). The
-    // scores are kept shifted, y = s c - m_ref, so p = exp2(y); while no y
-    // exceeds kSlack, p <= 2^kSlack and O and l need no rescaling. m_ref
-    // starts at the first half tile's maximum (half 0 always has a valid
-    // key); a half tile whose maximum y breaks the bound raises m_ref and
-    // rescales O, l and its own y before any of its P is formed, so nothing
-    // is ever recomputed.
+    // scores are kept shifted, y = s c - m_ref, so p = exp2(y). m_ref starts
+    // at the first half tile's maximum (half 0 always has a valid key), in
+    // both forms. In the online form, while no y exceeds kSlack, p <= 2^kSlack
+    // and O and l need no rescaling; a half tile whose maximum y breaks the
+    // bound raises m_ref and rescales O, l and its own y before any of its P
+    // is formed, so nothing is ever recomputed. In the fixed form the score
+    // bound already keeps every y in [-60, 60].
     constexpr float kSlack = 10.0f;
     float m_ref[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        if (FIXED) {
-            m_ref[j] = bound[j];
-        } else {
+        {
             float m = sv[j][0];
 #pragma unroll
             for (int v = 1; v < 16; ++v) m = fmaxf(m, sv[j][v]);

@@ -257,11 +257,9 @@ extern "C" int h3_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int6
                          uint16_t *c, int64_t ldc, int64_t M_buf, int64_t M_valid, int64_t N, int64_t K,
                          int32_t epilogue, const uint16_t *resid, int64_t ld_r, const float *gate,
                          int64_t ld_gate_group, int32_t n_mod_groups, const int32_t *mod_idx, void *stream) {
-    int s = h3_check_linear(a, lda, w, ldw, c, ldc, M_buf, M_valid, N, K, epilogue, resid, ld_r, gate,
-                            n_mod_groups);
+    int s = h3_check_linear(a, lda, w, ldw, bias, c, ldc, M_buf, M_valid, N, K, epilogue, resid, ld_r, gate,
+                            ld_gate_group, n_mod_groups);
     if (s != H3_OK || M_buf == 0) return s;
-    if (bias && (reinterpret_cast<uintptr_t>(bias) & 15u)) return H3_ERR_ALIGN;
-    if (epilogue == H3_EPI_RESIDUAL && n_mod_groups > 1 && (ld_gate_group % 4) != 0) return H3_ERR_ALIGN;
     if ((s = device_check()) != H3_OK) return s;
     const hipStream_t st = (hipStream_t)stream;
     launch_linear(a, lda, w, ldw, bias, c, ldc, M_valid, N, K, epilogue, resid, ld_r, gate, ld_gate_group,

@@ -553,9 +553,10 @@ int h3_check_swiglu_lora(const uint16_t *u, int64_t ld_u, const uint16_t *du, in
     return H3_OK;
 }
 
-int h3_check_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ldw, const uint16_t *c,
-                    int64_t ldc, int64_t M_buf, int64_t M_valid, int64_t N, int64_t K, int32_t epilogue,
-                    const uint16_t *resid, int64_t ld_r, const float *gate, int32_t n_mod_groups) {
+int h3_check_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ldw, const uint16_t *bias,
+                    const uint16_t *c, int64_t ldc, int64_t M_buf, int64_t M_valid, int64_t N, int64_t K,
+                    int32_t epilogue, const uint16_t *resid, int64_t ld_r, const float *gate,
+                    int64_t ld_gate_group, int32_t n_mod_groups) {
     H3_TRY(check_rows(M_buf, M_valid));
     if (N <= 0 || K <= 0) return H3_ERR_SHAPE;
     if (epilogue < H3_EPI_STORE || epilogue > H3_EPI_SWIGLU) return H3_ERR_UNSUPPORTED;
@@ -570,10 +571,19 @@ int h3_check_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t l
     H3_TRY(check_bf16_mat(c, ldc, Nc));
     const Mat ma = mat(a, M_buf, K, lda), mw = mat(w, N, K, ldw), mc = mat(c, M_buf, Nc, ldc);
     if (overlap(mc, ma) || overlap(mc, mw)) return H3_ERR_ALIAS;
+    if (bias) {
+        if (!aligned16(bias)) return H3_ERR_ALIGN;
+        if (overlap(mc, mat(bias, 1, N, N))) return H3_ERR_ALIAS;
+    }
     if (epilogue == H3_EPI_RESIDUAL) {
         if (!resid || !gate) return H3_ERR_NULL;
         if (n_mod_groups < 1) return H3_ERR_SHAPE;
         if (!aligned16(gate)) return H3_ERR_ALIGN;
+        // the gate table: n_mod_groups entries of N floats, ld_gate_group apart
+        if (n_mod_groups > 1 && ld_gate_group < N) return H3_ERR_SHAPE;
+        if (n_mod_groups > 1 && (ld_gate_group % 4) != 0) return H3_ERR_ALIGN;
+        const Mat mg = mat(gate, n_mod_groups, N, n_mod_groups > 1 ? ld_gate_group : N, 4);
+        if (overlap(mg, mc)) return H3_ERR_ALIAS;
         H3_TRY(check_bf16_mat(resid, ld_r, N));
         const Mat mr = mat(resid, M_buf, N, ld_r);
         if (!same(mr, mc) && overlap(mr, mc)) return H3_ERR_ALIAS;
@@ -897,7 +907,9 @@ int h3_check_linear_mxfp8(const uint8_t *a, int64_t lda, const uint8_t *a_scales
         if (!resid || !gate) return H3_ERR_NULL;
         if (n_mod_groups < 1) return H3_ERR_SHAPE;
         if (!aligned16(gate)) return H3_ERR_ALIGN;
+        if (n_mod_groups > 1 && ld_gate_group < N) return H3_ERR_SHAPE;
         if (n_mod_groups > 1 && (ld_gate_group % 4) != 0) return H3_ERR_ALIGN;
+        if (overlap(mat(gate, n_mod_groups, N, n_mod_groups > 1 ? ld_gate_group : N, 4), mc)) return H3_ERR_ALIAS;
         H3_TRY(check_bf16_mat(resid, ld_r, N));
         const Mat mr = mat(resid, M_buf, N, ld_r);
         if (!same(mr, mc) && overlap(mr, mc)) return H3_ERR_ALIAS;

@@ -101,7 +101,7 @@ def _load():
         "h3_swiglu_lora": [P, I64, P, I64, P, I64, I64, I64, I32, P],
         "h3_check_swiglu_lora": [P, I64, P, I64, P, I64, I64, I64, I32],
         "h3_linear": [P, I64, P, I64, P, P, I64, I64, I64, I64, I64, I32, P, I64, P, I64, I32, P, P],
-        "h3_check_linear": [P, I64, P, I64, P, I64, I64, I64, I64, I64, I32, P, I64, P, I32],
+        "h3_check_linear": [P, I64, P, I64, P, P, I64, I64, I64, I64, I64, I32, P, I64, P, I64, I32],
         "h3_stack_forward": [C.POINTER(Dims), C.POINTER(BlockWeights), I32, P, P, I64, I32, P, P, I64, I64, P, SZ,
                              P],
         "h3_check_stack_forward": [C.POINTER(Dims), C.POINTER(BlockWeights), I32, P, P, I64, I32, P, P, I64, I64, P,
