@@ -243,6 +243,29 @@ size_t h3_attention_workspace_bytes(int64_t valid_len, int32_t heads,
                                     const h3_qgroup *groups, int32_t n_groups);
 
 /* ---------------------------------------------------------------------------
+ * h3_attention_noalloc - h3_attention for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments and result, with no workspace
+ * argument. The workspace is a fixed device array inside the library, one per
+ * GPU, of H3_ATTENTION_SCRATCH_BYTES bytes, held until the process ends.
+ * The call allocates nothing and calls no allocating routine.
+ *
+ * Limit: h3_attention_workspace_bytes(valid_len, heads, groups, n_groups)
+ * must not exceed H3_ATTENTION_SCRATCH_BYTES (128 MiB: at 42 heads, dense
+ * attention up to 6,144 valid rows, e.g. the 4,096-token full-width block),
+ * else H3_ERR_WORKSPACE and nothing is launched. Other errors as h3_attention.
+ * Every call on one GPU uses that GPU's one array, which keeps the last call's
+ * contents: calls that overlap on one GPU (on different streams, or from
+ * different threads without ordering) race and give undefined results.
+ * ------------------------------------------------------------------------- */
+#define H3_ATTENTION_SCRATCH_BYTES (128ll << 20)
+int h3_attention_noalloc(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k,
+                         const uint16_t *v, int64_t ld_v, uint16_t *o, int64_t ld_o,
+                         int64_t L_buf, int64_t valid_len, int32_t heads, int32_t head_dim,
+                         float softmax_scale, const h3_qgroup *groups, int32_t n_groups,
+                         void *stream);
+
+/* ---------------------------------------------------------------------------
  * h3_fused_modulate_norm - operator group (1) of [Sol-H3] §3.5 (residual
  * addition with indexed gating, RMSNorm, indexed scale/shift modulation), the
  * merged FP32 modulation + norm + residual of [vLLM-H3] §3.2:

@@ -4,7 +4,8 @@
 * The host validators reject malformed calls before anything could launch
   (fail-closed: a rejected call writes nothing).
 * Workspace size and layout arithmetic.
-No compute entry point is called here.
+No compute entry point runs here (the allocation-free attention is only called
+with arguments it rejects before any HIP call).
 """
 import ctypes as C
 import os
@@ -225,6 +226,28 @@ def test_attention_validator():
     assert h3.LIB.h3_check_attention(q, 3 * H + 4, k, 3 * H, v, 3 * H, o, H, L, 500, 2, 128, 0.0, None,
                                      0, ws, need) == h3.H3_ERR_ALIGN
     assert h3.LIB.h3_check_attention(q, 3 * H, k, 3 * H, v, 3 * H, o, H, 0, 0, 2, 128, 0.0, None, 0, None, 0) == h3.H3_OK
+
+
+def test_noalloc_attention_rejects_on_the_host():
+    """h3_attention_noalloc checks its arguments and the size limit of its
+    fixed device workspace before any HIP call, so rejected calls return here
+    without a GPU (fake addresses, never dereferenced)."""
+    H = 42 * 128
+    base = addr(1)
+    q, k, v, o = base, base + 2 * H, base + 4 * H, addr(40)
+    L = 8192
+    assert h3.attention_workspace_bytes(L, 42) > h3.H3_ATTENTION_SCRATCH_BYTES
+    assert h3.LIB.h3_attention_noalloc(q, 3 * H, k, 3 * H, v, 3 * H, o, H, L, L, 42, 128, 0.0, None, 0,
+                                       None) == h3.H3_ERR_WORKSPACE
+    # the largest dense length that fits at 42 heads: 6,144 rows
+    assert h3.attention_workspace_bytes(6144, 42) <= h3.H3_ATTENTION_SCRATCH_BYTES
+    assert h3.attention_workspace_bytes(6208, 42) > h3.H3_ATTENTION_SCRATCH_BYTES
+    assert h3.LIB.h3_attention_noalloc(q, 3 * H, k, 3 * H, v, 3 * H, o, H, 512, 500, 42, 64, 0.0, None, 0,
+                                       None) == h3.H3_ERR_UNSUPPORTED
+    assert h3.LIB.h3_attention_noalloc(q, 3 * H, k, 3 * H, v, 3 * H, q, H, 512, 500, 42, 128, 0.0, None, 0,
+                                       None) == h3.H3_ERR_ALIAS
+    assert h3.LIB.h3_attention_noalloc(q, 3 * H, k, 3 * H, v, 3 * H, o, H, 0, 0, 42, 128, 0.0, None, 0,
+                                       None) == h3.H3_OK
 
 
 def test_elementwise_and_linear_validators():

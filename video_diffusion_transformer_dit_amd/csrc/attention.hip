@@ -43,6 +43,8 @@
 //    head), so the workgroups resident on an XCD stream the same K/V through
 //    its L2.
 #include <algorithm>
+#include <atomic>
+#include <cstdio>
 #include <utility>
 
 #include "h3_device.h"
@@ -996,6 +998,76 @@ extern "C" int h3_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, 
     if ((s = device_check()) != H3_OK) return s;
     launch_attention(q, ld_q, k, ld_k, v, ld_v, o, ld_o, L_buf, valid_len, heads, softmax_scale, groups, n_groups,
                      workspace, (hipStream_t)stream);
+    return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// h3_attention_noalloc: h3_attention with its workspace in a fixed device array
+// of this library instead of a caller buffer, for callers that cannot allocate.
+// The array has static storage: every GPU the library runs on holds its own
+// copy until the process ends. Host code only ever uses the device address
+// hipGetSymbolAddress returns for the current device (the array's name is a
+// host-side stand-in there). The kernels need nothing cleared in it: the
+// key-norm maxima are zeroed by a fill kernel inside the call, the V^T planes,
+// partial records and workgroup flags are written before they are read.
+// ---------------------------------------------------------------------------
+namespace h3 {
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[H3_ATTENTION_SCRATCH_BYTES];
+
+constexpr int kScratchDevices = 64;
+std::atomic<uintptr_t> g_scratch_addr[kScratchDevices];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+int scratch_address(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        std::fprintf(stderr, "libh3block: hipGetDevice failed: %s (%d)\n", hipGetErrorString(e), (int)e);
+        return H3_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kScratchDevices) return H3_ERR_DEVICE;
+    uintptr_t a = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (a == 0) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            std::fprintf(stderr, "libh3block: hipGetSymbolAddress(scratch) failed: %s (%d)\n",
+                         hipGetErrorString(e), (int)e);
+            return H3_ERR_HIP;
+        }
+        a = reinterpret_cast<uintptr_t>(p);
+        g_scratch_addr[dev].store(a, std::memory_order_release);
+    }
+    *out = reinterpret_cast<void *>(a);
+    return H3_OK;
+}
+
+}  // namespace
+}  // namespace h3
+
+extern "C" int h3_attention_noalloc(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k,
+                                    const uint16_t *v, int64_t ld_v, uint16_t *o, int64_t ld_o, int64_t L_buf,
+                                    int64_t valid_len, int32_t heads, int32_t head_dim, float softmax_scale,
+                                    const h3_qgroup *groups, int32_t n_groups, void *stream) {
+    // Every check but the workspace's first (no workspace given yet), then the
+    // size limit, then the full check against the device array.
+    int s = h3_check_attention(q, ld_q, k, ld_k, v, ld_v, o, ld_o, L_buf, valid_len, heads, head_dim,
+                               softmax_scale, groups, n_groups, nullptr, 0);
+    if (s != H3_OK && s != H3_ERR_WORKSPACE) return s;
+    if (L_buf == 0) return H3_OK;
+    if (h3_attention_workspace_bytes(valid_len, heads, groups, n_groups) > (size_t)H3_ATTENTION_SCRATCH_BYTES)
+        return H3_ERR_WORKSPACE;
+    if ((s = device_check()) != H3_OK) return s;
+    void *ws = nullptr;
+    if ((s = scratch_address(&ws)) != H3_OK) return s;
+    s = h3_check_attention(q, ld_q, k, ld_k, v, ld_v, o, ld_o, L_buf, valid_len, heads, head_dim, softmax_scale,
+                           groups, n_groups, ws, (size_t)H3_ATTENTION_SCRATCH_BYTES);
+    if (s != H3_OK) return s;
+    launch_attention(q, ld_q, k, ld_k, v, ld_v, o, ld_o, L_buf, valid_len, heads, softmax_scale, groups, n_groups,
+                     ws, (hipStream_t)stream);
     return launch_status();
 }
 

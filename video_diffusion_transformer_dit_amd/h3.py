@@ -25,6 +25,7 @@ H3_MXWS_COUNT = 15
 H3_MAX_SEGMENTS = 4
 H3_MAX_GROUPS = 8
 H3_SPARSE_Q_BLOCK, H3_SPARSE_K_BLOCK, H3_SPARSE_MAX_KBLOCKS = 256, 64, 4096
+H3_ATTENTION_SCRATCH_BYTES = 128 << 20
 
 
 class H3Error(RuntimeError):
@@ -85,6 +86,8 @@ def _load():
         "h3_check_attention": [P, I64, P, I64, P, I64, P, I64, I64, I64, I32, I32, F32, C.POINTER(QGroup), I32,
                                P, SZ],
         "h3_attention_workspace_bytes": [I64, I32, C.POINTER(QGroup), I32],
+        "h3_attention_noalloc": [P, I64, P, I64, P, I64, P, I64, I64, I64, I32, I32, F32, C.POINTER(QGroup), I32,
+                                 P],
         "h3_fused_modulate_norm": [P, I64, P, I64, P, P, P, I64, I32, P, P, I64, P, I64, I64, I64, I32, F32, I32, P],
         "h3_check_fused_modulate_norm": [P, I64, P, I64, P, P, P, I64, I32, P, I64, P, I64, I64, I64, I32, F32,
                                          I32],
@@ -167,7 +170,8 @@ EXPORTS = ["h3_block_forward", "h3_attention", "h3_fused_modulate_norm", "h3_qk_
            "h3_block_sparse_workspace_layout", "h3_mxfp8_quantize", "h3_linear_mxfp8", "h3_check_mxfp8_quantize",
            "h3_check_linear_mxfp8", "h3_fused_modulate_norm_mxfp8", "h3_check_fused_modulate_norm_mxfp8",
            "h3_block_forward_mxfp8", "h3_check_block_forward_mxfp8", "h3_block_mxfp8_workspace_bytes",
-           "h3_block_mxfp8_workspace_layout", "h3_stack_forward", "h3_check_stack_forward"]
+           "h3_block_mxfp8_workspace_layout", "h3_stack_forward", "h3_check_stack_forward",
+           "h3_attention_noalloc"]
 
 
 def status_string(s: int) -> str:
@@ -311,6 +315,16 @@ def attention(q, k, v, o, valid_len, heads, softmax_scale=0.0, groups=None, work
                          q.shape[0], valid_len, heads, 128, softmax_scale, garr, ng, _ptr(workspace),
                          workspace.numel() * workspace.element_size(), _stream(stream))
     _ok(s, "h3_attention")
+
+
+def attention_noalloc(q, k, v, o, valid_len, heads, softmax_scale=0.0, groups=None, stream=None):
+    """h3_attention with the library's own fixed device workspace (no
+    allocation anywhere, on either side of the boundary)."""
+    garr, ng = make_groups(groups)
+    s = LIB.h3_attention_noalloc(_ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0), _ptr(o),
+                                 o.stride(0), q.shape[0], valid_len, heads, 128, softmax_scale, garr, ng,
+                                 _stream(stream))
+    _ok(s, "h3_attention_noalloc")
 
 
 def fused_modulate_norm(x, shift, scale, h_out, valid_len, eps=1e-6, norm_type=0, branch=None, gate=None,
