@@ -863,27 +863,20 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float *part, int3
 }
 
 // Transposed V of every segment of the plan into the workspace, and the
-// largest squared key norm per head over all segments. With own_prestaged,
-// the plan's own-rows plane and its key norms are already in place (the
-// fused QKV epilogue wrote them and zeroed kmax2 first): only the other
-// segments are staged, their norms merged into kmax2.
+// largest squared key norm per head over all segments.
 void stage_vt(const VtPlan &plan, const uint16_t *k, int64_t ld_k, const uint16_t *v, int64_t ld_v, int32_t heads,
-              uint8_t *ws, hipStream_t stream, bool own_prestaged) {
+              uint8_t *ws, hipStream_t stream) {
     if (plan.n == 0) return;
     uint32_t *kmax2 = reinterpret_cast<uint32_t *>(ws + plan.kmax_off);
-    if (!own_prestaged) {
-        const int64_t kcols = (int64_t)(plan.bytes - plan.kmax_off) / 2;  // the 256-byte aligned area, as BF16 slots
-        launch_zero_rows(reinterpret_cast<uint16_t *>(kmax2), kcols, kcols, 0, 1, stream);
-    }
+    const int64_t kcols = (int64_t)(plan.bytes - plan.kmax_off) / 2;  // the 256-byte aligned area, as BF16 slots
+    launch_zero_rows(reinterpret_cast<uint16_t *>(kmax2), kcols, kcols, 0, 1, stream);
     for (int i = 0; i < plan.n; ++i) {
-        if (own_prestaged && i == plan.own_full) continue;
         const VtSeg &e = plan.seg[i];
         const uint16_t *ks = e.own ? k + e.begin * ld_k : e.k + e.begin * e.ld;
         key_norm_max_kernel<<<dim3((unsigned)((e.len + kNormRows - 1) / kNormRows)), 256, 0, stream>>>(
             ks, e.own ? ld_k : e.ld, e.len, heads, kmax2);
     }
     for (int i = 0; i < plan.n; ++i) {
-        if (own_prestaged && i == plan.own_full) continue;
         const VtSeg &e = plan.seg[i];
         const uint16_t *src = e.own ? v + e.begin * ld_v : e.v + e.begin * e.ld;
         const int64_t ld = e.own ? ld_v : e.ld;
@@ -897,7 +890,7 @@ void stage_vt(const VtPlan &plan, const uint16_t *k, int64_t ld_k, const uint16_
 void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k, const uint16_t *v,
                       int64_t ld_v, uint16_t *o, int64_t ld_o, int64_t L_buf, int64_t valid_len, int32_t heads,
                       float softmax_scale, const h3_qgroup *groups, int32_t n_groups, void *workspace,
-                      hipStream_t stream, bool own_prestaged) {
+                      hipStream_t stream) {
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
     // The dense case is one group over [0, valid_len) attending to keys [0, valid_len).
     h3_qgroup dense = {};
@@ -912,10 +905,9 @@ void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_
     }
     // Stage V^T once per distinct segment.
     VtPlan plan;
-    vt_plan(is_dense ? nullptr : groups, is_dense ? 0 : n_groups, valid_len, heads, &plan,
-            own_prestaged ? valid_len : 0);
+    vt_plan(is_dense ? nullptr : groups, is_dense ? 0 : n_groups, valid_len, heads, &plan);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    stage_vt(plan, k, ld_k, v, ld_v, heads, ws, stream, own_prestaged);
+    stage_vt(plan, k, ld_k, v, ld_v, heads, ws, stream);
     std::pair<int64_t, int64_t> cov[H3_MAX_GROUPS];
     int nc = 0;
     for (int gi = 0; gi < n_groups; ++gi)
@@ -951,7 +943,7 @@ void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_
                 G.sk[s] = ss.k + ss.begin * ss.ld;
                 G.sldk[s] = ss.ld;
             }
-            G.svt[s] = reinterpret_cast<const uint16_t *>(ws + e.off) + plan.koff[gi][s];
+            G.svt[s] = reinterpret_cast<const uint16_t *>(ws + e.off);
             G.slpad[s] = e.lpad;
             G.slen[s] = ss.len;
         }
@@ -1084,19 +1076,19 @@ namespace h3 {
 void launch_sparse_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k, const uint16_t *v,
                              int64_t ld_v, uint16_t *o, int64_t ld_o, int64_t L_buf, int64_t valid_len,
                              int64_t prefix_len, int32_t heads, float softmax_scale, const uint16_t *blocks,
-                             const int32_t *counts, void *workspace, hipStream_t stream, bool own_prestaged) {
+                             const int32_t *counts, void *workspace, hipStream_t stream) {
     if (prefix_len >= valid_len) {  // no target rows: dense attention
         launch_attention(q, ld_q, k, ld_k, v, ld_v, o, ld_o, L_buf, valid_len, heads, softmax_scale, nullptr, 0,
-                         workspace, stream, own_prestaged);
+                         workspace, stream);
         return;
     }
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
     h3_qgroup g;
     sparse_vt_group(valid_len, prefix_len, &g);
     VtPlan plan;
-    vt_plan(&g, 1, valid_len, heads, &plan, own_prestaged ? valid_len : 0);
+    vt_plan(&g, 1, valid_len, heads, &plan);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    stage_vt(plan, k, ld_k, v, ld_v, heads, ws, stream, own_prestaged);
+    stage_vt(plan, k, ld_k, v, ld_v, heads, ws, stream);
     const int64_t T = valid_len - prefix_len;
     AttnArgs a = {};
     AttnGroup &G = a.grp[0];
@@ -1115,7 +1107,7 @@ void launch_sparse_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k,
         const VtSeg &e = plan.seg[plan.map[0][s]];
         G.sk[s] = k + g.seg[s].begin * ld_k;
         G.sldk[s] = ld_k;
-        G.svt[s] = reinterpret_cast<const uint16_t *>(ws + e.off) + plan.koff[0][s];
+        G.svt[s] = reinterpret_cast<const uint16_t *>(ws + e.off);
         G.slpad[s] = e.lpad;
         G.slen[s] = g.seg[s].len;
     }

@@ -4,9 +4,8 @@
 // vLLM-Omni H3 blog, §3.1-3.2).
 //
 //   1 modnorm        h   = RMSNorm(x) (1 + scale_a) + shift_a           group (1)
-//   2 GEMM           qkv = h W_qkv^T (+ b), packed QKV, with group (2) in
-//   3 (epilogue)     its epilogue: q~, k~ = RoPE(RMSNorm_head(.) gain); v
-//                    also into attention's V^T plane, key norm maxima
+//   2 GEMM           qkv = h W_qkv^T (+ b)                               packed QKV
+//   3 qk-norm+RoPE   q~, k~ in place in qkv                              group (2)
 //   4 attention      o   = softmax(q~ k~^T / sqrt(128)) v
 //   5 GEMM+residual  x1  = x + gate_a (o W_o^T (+ b))                    group (1)
 //   6 modnorm        h2  = RMSNorm(x1) (1 + scale_f) + shift_f           group (1)
@@ -51,39 +50,24 @@ void block_steps(const h3_dims *dims, const h3_block_weights *w, const uint16_t 
     // 1 h
     launch_modnorm(x, H, nullptr, 0, shift_a, scale_a, nullptr, ldm, n_mod_groups, mod_idx, nullptr, 0, h, H, L_buf,
                    V, (int32_t)H, dims->eps, dims->norm_type, st);
-    // 2+3 qkv with q~, k~ in place, the own rows' V^T plane and key norm
-    // maxima, where the attention call below (planned the same way) expects
-    // them; the RoPE table first (it also zeroes the maxima)
-    if (V > 0) {
-        VtPlan plan;
-        if (sp != nullptr && sp->prefix_len < V) {
-            h3_qgroup sg;
-            sparse_vt_group(V, sp->prefix_len, &sg);
-            vt_plan(&sg, 1, V, dims->heads, &plan, V);
-        } else {
-            vt_plan(sp == nullptr ? groups : nullptr, sp == nullptr ? n_groups : 0, V, dims->heads, &plan, V);
-        }
-        uint8_t *vtb = static_cast<uint8_t *>(vt);
-        uint32_t *kmax2 = reinterpret_cast<uint32_t *>(vtb + plan.kmax_off);
-        float *rope = reinterpret_cast<float *>(ws + l.rope_off);
-        launch_rope_table(pos, V, dims->rot_dim, dims->rope_theta, rope, kmax2, dims->heads, st);
-        launch_linear_qkv(h, H, w->w_qkv, H, w->b_qkv, qkv, 3 * H, V, H, w->q_gain, w->k_gain, rope,
-                          dims->rot_dim / 2, dims->rope_pairing, dims->eps,
-                          reinterpret_cast<uint16_t *>(vtb + plan.seg[plan.own_full].off),
-                          plan.seg[plan.own_full].lpad, kmax2, st);
-    }
+    // 2 qkv
+    launch_linear(h, H, w->w_qkv, H, w->b_qkv, qkv, 3 * H, V, 3 * H, H, H3_EPI_STORE, nullptr, 0, nullptr, 0, 1,
+                  nullptr, st);
     launch_zero_rows(qkv, 3 * H, 3 * H, V, L_buf, st);
+    // 3 q~, k~ (also zeroes their padding rows)
+    launch_qk_norm_rope(qkv, qkv + H, 3 * H, w->q_gain, w->k_gain, pos, L_buf, V, dims->heads, dims->rot_dim,
+                        dims->rope_pairing, dims->rope_theta, dims->eps, st);
     // 4 o
     if (sp == nullptr) {
         launch_attention(qkv, 3 * H, qkv + H, 3 * H, qkv + 2 * H, 3 * H, o, H, L_buf, V, dims->heads, 0.0f, groups,
-                         n_groups, vt, st, true);
+                         n_groups, vt, st);
     } else {
         uint16_t *blocks = reinterpret_cast<uint16_t *>(ws + sp->l->blocks_off);
         int32_t *counts = reinterpret_cast<int32_t *>(ws + sp->l->counts_off);
         launch_sparse_select(qkv, 3 * H, qkv + H, 3 * H, V, sp->prefix_len, dims->heads, sp->tau, blocks, counts,
                              ws + sp->l->select_off, st);
         launch_sparse_attention(qkv, 3 * H, qkv + H, 3 * H, qkv + 2 * H, 3 * H, o, H, L_buf, V, sp->prefix_len,
-                                dims->heads, 0.0f, blocks, counts, vt, st, true);
+                                dims->heads, 0.0f, blocks, counts, vt, st);
     }
     // 5 x1 = x + gate_a * (o W_o^T)
     launch_linear(o, H, w->w_o, H, w->b_o, x1, H, V, H, H, H3_EPI_RESIDUAL, x, H, gate_a, ldm, n_mod_groups, mod_idx,

@@ -461,34 +461,6 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t *u, int64_t 
     *reinterpret_cast<uint4 *>(dst) = pack8(a);
 }
 
-// RoPE cos/sin table for the fused QKV epilogue: row r holds cos(pos_r w_i)
-// for i < half, then sin(pos_r w_i), w_i = theta^(-2i/rot_dim), with the
-// angle and its sine and cosine in FP64 rounded to FP32, exactly as
-// qk_norm_rope_kernel forms them; rows with a negative position hold cos 1,
-// sin 0 (no rotation). The first `heads` threads also zero the per-head key
-// norm maxima the epilogue merges into.
-__global__ __launch_bounds__(256) void rope_table_kernel(const int32_t *pos, int64_t rows, int32_t half,
-                                                         int32_t rot_dim, float theta, float *tab, uint32_t *kmax2,
-                                                         int32_t heads) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < heads) kmax2[i] = 0u;
-    if (half <= 0) return;
-    const int64_t r = i / half;
-    const int f = (int)(i - r * half);
-    if (r >= rows) return;
-    const int p = pos ? pos[r] : (int)r;
-    float c = 1.0f, sn = 0.0f;
-    if (p >= 0) {
-        const double w = pow((double)theta, -2.0 * (double)f / (double)rot_dim);
-        double sd, cd;
-        sincos((double)p * w, &sd, &cd);
-        c = (float)cd;
-        sn = (float)sd;
-    }
-    tab[r * 2 * half + f] = c;
-    tab[r * 2 * half + half + f] = sn;
-}
-
 __global__ __launch_bounds__(256) void zero_rows_kernel(uint16_t *p, int64_t ld, int32_t chunks, int64_t r0,
                                                         int64_t rows) {
     const int64_t n = rows * chunks;
@@ -537,14 +509,6 @@ void launch_qk_norm_rope(uint16_t *q, uint16_t *k, int64_t ld, const uint16_t *q
     a.heads = heads; a.rot_dim = rot_dim; a.pairing = pairing; a.theta = theta; a.eps = eps;
     a.v = nullptr; a.dq = a.dk = a.dv = nullptr; a.ld_d = 0;
     qk_norm_rope_kernel<false><<<dim3((unsigned)L_buf), 256, 0, stream>>>(a);
-}
-
-void launch_rope_table(const int32_t *pos, int64_t rows, int32_t rot_dim, float theta, float *tab, uint32_t *kmax2,
-                       int32_t heads, hipStream_t stream) {
-    const int32_t half = rot_dim / 2;
-    const int64_t n = std::max<int64_t>(half > 0 ? rows * half : 0, heads);
-    rope_table_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, stream>>>(pos, rows, half, rot_dim, theta, tab,
-                                                                            kmax2, heads);
 }
 
 void launch_swiglu(const uint16_t *u, int64_t ld_u, uint16_t *g, int64_t ld_g, int64_t L_buf, int64_t valid_len,

@@ -52,14 +52,6 @@ struct GemmArgs {
     int32_t tiles_m, tiles_n;
     int32_t group_m;      // tile rows per group of the tile order
     int32_t ffn;          // SwiGLU output width
-    // packed-QKV epilogue (kEpiQkv): QK-norm + RoPE, V^T plane, key norms
-    const uint16_t *q_gain, *k_gain;
-    const float *rope;
-    int32_t rope_half, rope_pairing, hidden;
-    float eps;
-    uint16_t *vt;
-    int64_t vt_lpad;
-    uint32_t *kmax2;
 };
 
 // LDS operand tile: row r holds 8 chunks of 16 B (64 k values); chunk c of
@@ -227,12 +219,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
     // can end.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    if constexpr (EPI == kEpiQkv) {
-        __syncthreads();  // every wave is done reading the last stage: LDS is free
-        gemm_epilogue_qkv(p, acc, tm, tn, wm, wn, r32, g2, reinterpret_cast<uint16_t *>(smem) + wave * 16384);
-    } else {
-        gemm_epilogue<EPI>(p, acc, tm, tn, wm, wn, r32, g2);
-    }
+    gemm_epilogue<EPI>(p, acc, tm, tn, wm, wn, r32, g2);
 }
 
 }  // namespace
@@ -247,8 +234,6 @@ void launch_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ld
     p.lda = lda; p.ldw = ldw; p.ldc = ldc; p.ld_r = ld_r;
     p.ld_gate = n_mod_groups > 1 ? ld_gate_group : 0;
     p.M = M_valid; p.N = N; p.K = K;
-    p.q_gain = p.k_gain = nullptr; p.rope = nullptr; p.rope_half = p.rope_pairing = p.hidden = 0; p.eps = 0.f;
-    p.vt = nullptr; p.vt_lpad = 0; p.kmax2 = nullptr;
     p.n_groups = n_mod_groups > 0 ? n_mod_groups : 1;
     p.ffn = (int32_t)(N / 2);
     p.tiles_m = (int32_t)((M_valid + BM - 1) / BM);
@@ -262,24 +247,6 @@ void launch_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ld
         case H3_EPI_SWIGLU: gemm_bf16_kernel<H3_EPI_SWIGLU><<<grid, kThreads, 0, stream>>>(p); break;
         default: gemm_bf16_kernel<H3_EPI_STORE><<<grid, kThreads, 0, stream>>>(p); break;
     }
-}
-
-void launch_linear_qkv(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ldw, const uint16_t *bias,
-                       uint16_t *qkv, int64_t ldc, int64_t M_valid, int64_t hidden, const uint16_t *q_gain,
-                       const uint16_t *k_gain, const float *rope, int32_t rope_half, int32_t rope_pairing, float eps,
-                       uint16_t *vt, int64_t vt_lpad, uint32_t *kmax2, hipStream_t stream) {
-    if (M_valid <= 0) return;
-    GemmArgs p = {};
-    p.a = a; p.w = w; p.bias = bias; p.c = qkv;
-    p.lda = lda; p.ldw = ldw; p.ldc = ldc;
-    p.M = M_valid; p.N = 3 * hidden; p.K = hidden;
-    p.n_groups = 1;
-    p.tiles_m = (int32_t)((M_valid + BM - 1) / BM);
-    p.tiles_n = (int32_t)((p.N + BN - 1) / BN);
-    p.group_m = p.tiles_n >= 128 ? 8 : 2;
-    p.q_gain = q_gain; p.k_gain = k_gain; p.rope = rope; p.rope_half = rope_half; p.rope_pairing = rope_pairing;
-    p.hidden = (int32_t)hidden; p.eps = eps; p.vt = vt; p.vt_lpad = vt_lpad; p.kmax2 = kmax2;
-    gemm_bf16_kernel<kEpiQkv><<<dim3((unsigned)(p.tiles_m * p.tiles_n)), kThreads, 0, stream>>>(p);
 }
 
 }  // namespace h3

@@ -55,18 +55,13 @@ struct VtPlan {
     int n;
     VtSeg seg[H3_MAX_GROUPS * H3_MAX_SEGMENTS];
     int map[H3_MAX_GROUPS][H3_MAX_SEGMENTS];  // (group, segment) -> seg index
-    int64_t koff[H3_MAX_GROUPS][H3_MAX_SEGMENTS];  // first key of (group, segment) inside its seg's plane
-    int own_full;         // seg index of the own rows' full plane, or -1
     int64_t part_off;     // byte offset of the split items' partial results (FP32 O, then (m, l) per row)
     int64_t kmax_off;     // byte offset of the per-head key norm maxima
     int64_t flags_off;    // byte offset of one int32 per attention workgroup
     size_t bytes;
 };
-// groups == NULL plans one own segment [0, dense_len). own_full_len > 0 puts
-// the plane of the own rows [0, own_full_len) first, and own segments that
-// start on a 64-key boundary inside it read it (koff = their first key).
-void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads, VtPlan *out,
-             int64_t own_full_len = 0);
+// groups == NULL plans one own segment [0, dense_len).
+void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads, VtPlan *out);
 
 // Geometry of Sol-Attn block selection over target rows [P, valid_len):
 // query blocks of H3_SPARSE_Q_BLOCK rows, KV blocks of H3_SPARSE_K_BLOCK rows,
@@ -90,7 +85,6 @@ struct WsLayout {
     int64_t off[H3_WS_COUNT];
     int64_t ld[H3_WS_COUNT];
     int64_t cols[H3_WS_COUNT];
-    int64_t rope_off;  // FP32 [L_buf][rot_dim] RoPE table of the fused QKV epilogue
     size_t total;
 };
 bool ws_layout(const h3_dims *d, int64_t L_buf, const h3_qgroup *groups, int n_groups, WsLayout *out);

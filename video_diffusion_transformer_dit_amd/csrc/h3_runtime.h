@@ -22,10 +22,6 @@ void launch_qk_norm_rope(uint16_t *q, uint16_t *k, int64_t ld, const uint16_t *q
                          const uint16_t *k_gain, const int32_t *pos, int64_t L_buf, int64_t valid_len,
                          int32_t heads, int32_t rot_dim, int32_t pairing, float theta, float eps,
                          hipStream_t stream);
-// RoPE cos/sin table [rows][2][rot_dim / 2] FP32 for the fused QKV epilogue,
-// and kmax2[0 .. heads) zeroed.
-void launch_rope_table(const int32_t *pos, int64_t rows, int32_t rot_dim, float theta, float *tab, uint32_t *kmax2,
-                       int32_t heads, hipStream_t stream);
 void launch_swiglu(const uint16_t *u, int64_t ld_u, uint16_t *g, int64_t ld_g, int64_t L_buf,
                    int64_t valid_len, int32_t ffn, hipStream_t stream);
 void launch_modnorm_mx(const uint16_t *x, int64_t ld_x, const uint16_t *branch, int64_t ld_b, const float *shift,
@@ -54,22 +50,10 @@ void launch_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ld
                    const uint16_t *resid, int64_t ld_r, const float *gate, int64_t ld_gate_group,
                    int32_t n_mod_groups, const int32_t *mod_idx, hipStream_t stream);
 
-// Packed QKV projection with the fused epilogue (QK-norm + RoPE from the
-// table, v also written into the V^T plane [heads][128][vt_lpad] of the own
-// rows [0, M_valid), per-head key norm maxima merged into kmax2).
-void launch_linear_qkv(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ldw, const uint16_t *bias,
-                       uint16_t *qkv, int64_t ldc, int64_t M_valid, int64_t hidden, const uint16_t *q_gain,
-                       const uint16_t *k_gain, const float *rope, int32_t rope_half, int32_t rope_pairing, float eps,
-                       uint16_t *vt, int64_t vt_lpad, uint32_t *kmax2, hipStream_t stream);
-
-// own_prestaged: the call's own rows [0, valid_len) already have their V^T
-// plane at the plan's first segment and their key norm maxima in kmax2 (the
-// fused QKV epilogue): own segments it covers are not staged again and kmax2
-// is not cleared. The plan must then be made with own_full_len = valid_len.
 void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k,
                       const uint16_t *v, int64_t ld_v, uint16_t *o, int64_t ld_o, int64_t L_buf,
                       int64_t valid_len, int32_t heads, float softmax_scale, const h3_qgroup *groups,
-                      int32_t n_groups, void *workspace, hipStream_t stream, bool own_prestaged = false);
+                      int32_t n_groups, void *workspace, hipStream_t stream);
 
 void launch_sparse_select(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k, int64_t valid_len,
                           int64_t prefix_len, int32_t heads, float tau, uint16_t *blocks, int32_t *counts,
@@ -77,6 +61,6 @@ void launch_sparse_select(const uint16_t *q, int64_t ld_q, const uint16_t *k, in
 void launch_sparse_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k, const uint16_t *v,
                              int64_t ld_v, uint16_t *o, int64_t ld_o, int64_t L_buf, int64_t valid_len,
                              int64_t prefix_len, int32_t heads, float softmax_scale, const uint16_t *blocks,
-                             const int32_t *counts, void *workspace, hipStream_t stream, bool own_prestaged = false);
+                             const int32_t *counts, void *workspace, hipStream_t stream);
 
 }  // namespace h3

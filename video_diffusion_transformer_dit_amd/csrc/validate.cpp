@@ -177,12 +177,10 @@ void attn_schedule(const h3_qgroup *groups, int n_groups, int64_t dense_len, int
     out->items = items;
 }
 
-void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads, VtPlan *out,
-             int64_t own_full_len) {
+void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads, VtPlan *out) {
     out->n = 0;
     out->bytes = 0;
     out->kmax_off = 0;
-    out->own_full = -1;
     auto add = [&](int own, const uint16_t *k, const uint16_t *v, int64_t ld, int64_t begin, int64_t len) {
         for (int i = 0; i < out->n; ++i) {
             const VtSeg &e = out->seg[i];
@@ -195,23 +193,10 @@ void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads
         out->bytes += (size_t)heads * kHeadDim * e.lpad * 2;
         return out->n++;
     };
-    // The plane of the own rows [0, own_full_len), first in the area; an own
-    // segment starting on a 64-key tile boundary inside it reads that plane
-    // from its first key on instead of a plane of its own.
-    if (own_full_len > 0) out->own_full = add(1, nullptr, nullptr, 0, 0, own_full_len);
-    auto add_own = [&](int g, int s, int64_t begin, int64_t len) {
-        if (out->own_full >= 0 && begin % 64 == 0 && begin >= 0 && begin + len <= own_full_len) {
-            out->map[g][s] = out->own_full;
-            out->koff[g][s] = begin;
-        } else {
-            out->map[g][s] = add(1, nullptr, nullptr, 0, begin, len);
-            out->koff[g][s] = 0;
-        }
-    };
     int64_t qtiles = 0;  // 256-row query tiles over all groups
     int n_launch_groups = 1;
     if (groups == nullptr) {
-        if (dense_len > 0) add_own(0, 0, 0, dense_len);
+        if (dense_len > 0) out->map[0][0] = add(1, nullptr, nullptr, 0, 0, dense_len);
         qtiles = (dense_len + 255) / 256;
     } else {
         n_launch_groups = std::max(1, std::min(n_groups, H3_MAX_GROUPS));
@@ -219,12 +204,8 @@ void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads
             qtiles += (std::max<int64_t>(groups[g].q_end - groups[g].q_begin, 0) + 255) / 256;
             for (int s = 0; s < groups[g].n_seg && s < H3_MAX_SEGMENTS; ++s) {
                 const h3_kv_seg &x = groups[g].seg[s];
-                if (x.k == nullptr) {
-                    add_own(g, s, x.begin, x.len);
-                } else {
-                    out->map[g][s] = add(0, x.k, x.v, x.ld, x.begin, x.len);
-                    out->koff[g][s] = 0;
-                }
+                out->map[g][s] = x.k == nullptr ? add(1, nullptr, nullptr, 0, x.begin, x.len)
+                                                : add(0, x.k, x.v, x.ld, x.begin, x.len);
             }
         }
     }
@@ -265,16 +246,12 @@ bool ws_layout(const h3_dims *d, int64_t L_buf, const h3_qgroup *groups, int n_g
         out->cols[i] = cols[i];
         off += align(L_buf * cols[i] * kBf16);
     }
-    // the QKV projection stages the own rows' V^T plane itself (own_full)
     VtPlan p;
-    vt_plan(groups, n_groups, L_buf, d->heads, &p, L_buf);
+    vt_plan(groups, n_groups, L_buf, d->heads, &p);
     out->off[H3_WS_VT] = off;
     out->ld[H3_WS_VT] = (int64_t)p.bytes;
     out->cols[H3_WS_VT] = 0;
     off += align((int64_t)p.bytes);
-    // RoPE cos/sin table of the fused QKV epilogue, FP32 [L_buf][rot_dim]
-    out->rope_off = off;
-    off += align(L_buf * (int64_t)d->rot_dim * 4);
     out->total = (size_t)off;
     return true;
 }
@@ -290,13 +267,11 @@ bool block_sparse_layout(const h3_dims *d, int64_t L_buf, int64_t valid_len, int
         h3_qgroup g;
         sparse_vt_group(valid_len, prefix_len, &g);
         VtPlan p;
-        vt_plan(&g, 1, valid_len, d->heads, &p, valid_len);
+        vt_plan(&g, 1, valid_len, d->heads, &p);
         vt = std::max<int64_t>(vt, (int64_t)p.bytes);
     }
     l.ld[H3_WS_VT] = vt;
     int64_t off = l.off[H3_WS_VT] + align(vt);
-    l.rope_off = off;
-    off += align(L_buf * (int64_t)d->rot_dim * 4);
     l.total = (size_t)off;
     SparseGeom g;
     sparse_geometry(valid_len, prefix_len, d->heads, &g);
