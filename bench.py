@@ -88,7 +88,7 @@ def time_calls(torch, fn, iters: int, warmup: int, per_call: bool = False):
     return mean, [ev[i].elapsed_time(ev[i + 1]) for i in range(iters)]
 
 
-def cpu_baseline(seconds_target: float = 20.0):
+def cpu_baseline(seconds_target: float = 20.0, configs: bool = True):
     """FP64 oracle on a bounded sample: the full-width block at L tokens, scaled
     to ms per block at the 58,758-token workload by algorithmic flops. A
     1,024-token probe sizes the sample: L grows (in steps of 64 rows, at most
@@ -119,17 +119,87 @@ def cpu_baseline(seconds_target: float = 20.0):
     g_s, a_s = block_flops(L, 5376, 21504)
     g_f, a_f = block_flops(58758, 5376, 21504)
     ms_full = dt * 1e3 * (g_f + a_f) / (g_s + a_s)
-    cpu = platform.processor() or "unknown"
+    out = {"value": round(ms_full, 1), "unit": "ms/block", "cores": int(threads), "cpu": cpu_model(),
+           "kind": "oracle", "extrapolated": True,
+           "sample": f"FP64 numpy oracle, one full-width block (H 5376, 42x128, F 21504) at {L} tokens: "
+                     f"{dt:.2f} s for {(g_s + a_s) / 1e12:.3f} TFLOP, scaled by algorithmic flops to the "
+                     f"58,758-token block ({(g_f + a_f) / 1e12:.1f} TFLOP)",
+           "sample_tokens": L, "sample_seconds": round(dt, 3), "sample_gflops_per_s": round((g_s + a_s) / dt / 1e9, 1)}
+    if configs:
+        out["configs"] = cpu_oracle_configs(threads)
+        # the same extrapolation from the 4,096-token block: a second sample size
+        c2 = out["configs"]["full_4096"]
+        g4, a4 = block_flops(4096, 5376, 21504)
+        out["extrapolation_from_4096_tokens_ms"] = round(c2["s"] * 1e3 * (g_f + a_f) / (g4 + a4), 1)
+    return out
+
+
+def cpu_model():
+    """Host CPU: /proc/cpuinfo's model name with its family / model / stepping
+    numbers (the name alone can be generic), logical CPUs and usable ones."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
-            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
+            for ln in f:
+                if ":" in ln:
+                    k, v = (t.strip() for t in ln.split(":", 1))
+                    info.setdefault(k, v)
+                if not ln.strip() and info:
+                    break
     except OSError:  # pragma: no cover
         pass
-    return {"value": round(ms_full, 1), "unit": "ms/block", "cores": int(threads), "cpu": cpu, "kind": "oracle",
-            "sample": f"FP64 numpy oracle, one full-width block (H 5376, 42x128, F 21504) at {L} tokens: "
-                      f"{dt:.2f} s for {(g_s + a_s) / 1e12:.3f} TFLOP, scaled by algorithmic flops to the "
-                      f"58,758-token block ({(g_f + a_f) / 1e12:.1f} TFLOP)",
-            "sample_tokens": L, "sample_seconds": round(dt, 3), "sample_gflops_per_s": round((g_s + a_s) / dt / 1e9, 1)}
+    name = info.get("model name") or platform.processor() or "unknown"
+    fms = "/".join(info.get(k, "?") for k in ("cpu family", "model", "stepping"))
+    return (f"{name} (family/model/stepping {fms}; {os.cpu_count()} logical CPUs, "
+            f"{len(os.sched_getaffinity(0))} usable)")
+
+
+def cpu_oracle_configs(threads: int):
+    """The FP64 oracle timed once per workload that fits a bounded CPU run
+    (wall clock of the oracle call alone, inputs generated before): the tiny
+    block, the full-width block at 4,096 tokens, one forward of the streaming
+    chunk (its 4 denoise forwards and the refresh forward are the same work;
+    the chunk is 5 of them) and the stacked loop's check of 2 layers at 2,048
+    tokens. The 58,758-token block is not run; cpu_baseline extrapolates it."""
+    from oracle import h3_oracle as O
+    from video_diffusion_transformer_dit_amd import inputs as I
+
+    def timed(s, groups=None, pos=None, tag="cpu"):
+        wb = I.block_weights(s, tag)
+        w = {k: O.bf16_to_f64(v) for k, v in wb.items()}
+        x = O.bf16_to_f64(I.activations(s, tag=f"{tag}.x"))
+        mod = I.mod_table(s, 1, tag=f"{tag}.mod").astype(np.float64)
+        t0 = time.perf_counter()
+        O.block_forward(x, w, mod, heads=s.heads, head_dim=128, ffn=s.ffn, valid_len=s.valid_len,
+                        rot_dim=s.rot_dim, groups=groups, pos=pos)
+        return time.perf_counter() - t0
+
+    out = {"cores": int(threads), "kind": "oracle", "unit": "s"}
+    t = timed(I.TINY, tag="cpu.tiny")
+    out["tiny_block"] = {"workload": "tiny block, 512 rows (500 valid), H 256, 2x128, F 1024", "s": round(t, 3)}
+    progress(f"CPU oracle: tiny block {t:.2f} s")
+    t = timed(I.FULL_4096, tag="cpu.c2")
+    g, a = block_flops(4096, 5376, 21504)
+    out["full_4096"] = {"workload": "full-width block at 4,096 valid tokens", "s": round(t, 3),
+                        "gflops_per_s": round((g + a) / t / 1e9, 1)}
+    progress(f"CPU oracle: 4,096-token block {t:.2f} s")
+    s = I.streaming_shape()
+    hk, hv = I.history_kv(I.STREAM_HISTORY, s.hidden, tag="cpu.hist")
+    c, au, L = I.STREAM_COND, I.STREAM_AUDIO, s.L_buf
+    cur = ("self", 0, L)
+    groups = [(0, c, [cur]), (c, c + au, [cur]), (c + au, L, [(O.bf16_to_f64(hk), O.bf16_to_f64(hv)), cur])]
+    pos = np.arange(L, dtype=np.int64) + I.STREAM_HISTORY
+    t = timed(s, groups=groups, pos=pos, tag="cpu.c4")
+    out["streaming_forward"] = {"workload": "one streaming forward: [cond 256 | audio 128 | video 5,040] over "
+                                            "15,120 history rows, full width", "s": round(t, 3),
+                                "chunk_s_5_forwards": round(5 * t, 3)}
+    progress(f"CPU oracle: streaming forward {t:.2f} s")
+    s = I.scaled(I.FULL_4096, 2048, name="full-2048")
+    t = sum(timed(s, tag=f"cpu.c5.{i}") for i in range(2))
+    out["stacked_two_layers_2048"] = {"workload": "2 full-width blocks at 2,048 tokens (the stacked loop's "
+                                                  "per-layer check)", "s": round(t, 3)}
+    progress(f"CPU oracle: 2 layers at 2,048 tokens {t:.2f} s")
+    return out
 
 
 def lora_consumers(torch, h3, dev, gen, L, V, H, heads, F, iters):
@@ -382,6 +452,56 @@ def streaming_chunk(torch, h3, dev, gen, dims, weights, H, heads, F, iters):
                                   "frac_mfma": round(attn_f / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}}
 
 
+def full_4096(torch, h3, dev, gen, dims, weights, w, H, heads, F, iters, n_rot=4):
+    """The full-width block at 4,096 valid tokens (no padding). Its
+    activations (44 MB) would stay in the 256 MB last-level cache between
+    calls, so the block is timed over n_rot input/output sets in turn. Also
+    the four projections and attention alone, on the block's own buffers."""
+    L = V = 4096
+    xs = [torch.randn((L, H), generator=gen, device=dev).to(torch.bfloat16) for _ in range(n_rot)]
+    ys = [torch.empty_like(xs[0]) for _ in range(n_rot)]
+    mod = (0.1 * torch.randn((1, 6, H), generator=gen, device=dev)).float()
+    ws = torch.empty(h3.workspace_bytes(dims, L), dtype=torch.uint8, device=dev)
+    turn = [0]
+
+    def block():
+        i = turn[0] % n_rot
+        turn[0] += 1
+        h3.block_forward(dims, weights, xs[i], ys[i], mod, 1, V, ws)
+
+    blk = time_calls(torch, block, 4 * iters, n_rot)
+    off, lds = h3.workspace_layout(dims, L)
+
+    def wsv(i, cols):
+        return ws[off[i]:off[i] + L * cols * 2].view(torch.bfloat16).view(L, cols)
+
+    hbuf, qkv, o, x1, h2, g = (wsv(h3.H3_WS_H, H), wsv(h3.H3_WS_QKV, 3 * H), wsv(h3.H3_WS_O, H),
+                               wsv(h3.H3_WS_X1, H), wsv(h3.H3_WS_H2, H), wsv(h3.H3_WS_G, F))
+    vt_ws = ws[off[h3.H3_WS_VT]:off[h3.H3_WS_VT] + lds[h3.H3_WS_VT]]
+    x, y = xs[0], ys[0]
+    calls = {
+        "gemm_qkv": (lambda: h3.linear(hbuf, w["w_qkv"], qkv, V), 2.0 * V * H * 3 * H),
+        "attention": (lambda: h3.attention(qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:], o, V, heads,
+                                           workspace=vt_ws), 4.0 * V * V * H),
+        "gemm_out_residual": (lambda: h3.linear(o, w["w_o"], x1, V, h3.H3_EPI_RESIDUAL, resid=x, gate=mod[:, 2],
+                                                ld_gate_group=6 * H), 2.0 * V * H * H),
+        "gemm_up_swiglu": (lambda: h3.linear(h2, w["w_up"], g, V, h3.H3_EPI_SWIGLU), 2.0 * V * H * 2 * F),
+        "gemm_down_residual": (lambda: h3.linear(g, w["w_down"], y, V, h3.H3_EPI_RESIDUAL, resid=x1,
+                                                 gate=mod[:, 5], ld_gate_group=6 * H), 2.0 * V * F * H),
+    }
+    kern = {}
+    for k, (fn, fl) in calls.items():
+        t = time_calls(torch, fn, iters, 1)
+        tf = fl / (t * 1e-3) / 1e12
+        kern[k] = {"ms": round(t, 4), "tflops": round(tf, 1), "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4)}
+    gemm_f, attn_f = block_flops(V, H, F)
+    tf = (gemm_f + attn_f) / (blk * 1e-3) / 1e12
+    del xs, ys, ws
+    return {"workload": "one full-width H3 DiT block forward at 4,096 valid tokens (no padding)",
+            "block_ms": round(blk, 4), "tflop": round((gemm_f + attn_f) / 1e12, 3), "tflops": round(tf, 1),
+            "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4), "input_sets_rotated": n_rot, "kernels": kern}
+
+
 def stacked_denoise(torch, h3, dev, dims, x, L, V, H, F, n_blocks=50, n_steps=4):
     """The stacked denoise loop: n_blocks random-init blocks (46 GB of BF16
     weights at 50) resident at once, n_steps denoising steps at the
@@ -584,7 +704,9 @@ def main(argv=None) -> int:
                      "work_per_launch": "4 * 58758^2 * 5376 = 7.424e13 flop (QK^T and PV over valid rows)"},
     }
     if not a.no_configs:
-        out["configs"] = {"streaming_chunk": streaming_chunk(torch, h3, dev, gen, dims, weights, H, heads, F, kit)}
+        out["configs"] = {"full_4096": full_4096(torch, h3, dev, gen, dims, weights, w, H, heads, F, kit)}
+        progress("4,096-token block timed")
+        out["configs"]["streaming_chunk"] = streaming_chunk(torch, h3, dev, gen, dims, weights, H, heads, F, kit)
         progress("streaming chunk timed")
     if not a.no_next:
         out["next"] = {"lora_consumer_fusion": lora_consumers(torch, h3, dev, gen, L, V, H, heads, F, kit)}
@@ -609,7 +731,7 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         out["calibration_copy_bytes"] = int(src.numel() * 2)
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline()
+        out["cpu_baseline"] = cpu_baseline(configs=not a.no_configs)
         progress("CPU oracle sample timed")
     print(json.dumps(out), flush=True)
     return 0

@@ -1,0 +1,362 @@
+"""Guard-band canaries: every output of every C-ABI call is written into a view
+inside a larger allocation whose every byte starts as a sentinel pattern:
+rows before and after the view and, where the call takes a row stride, the
+columns between the view's width and its stride. Workspaces get sentinel
+bytes before and after them, and the block's workspace is filled too, so the
+alignment gaps between its intermediates must survive. After each call every
+margin is compared bit for bit with the sentinel: a write outside the view
+fails the test. Ragged tails (valid rows not a multiple of any tile, widths
+that leave partial column tiles) and the full 58,816-row block."""
+import numpy as np
+import pytest
+import torch
+
+from video_diffusion_transformer_dit_amd import h3
+from video_diffusion_transformer_dit_amd import inputs as I
+
+from util import dev_bf16, dev_f32
+
+pytestmark = pytest.mark.gpu
+
+PAD = 3          # sentinel rows before and after each view
+WS_PAD = 512     # sentinel bytes before and after each workspace (keeps 256-byte alignment)
+SENT = {torch.bfloat16: 0x7FA5, torch.int16: 0x7FA5, torch.uint8: 0xA5, torch.int32: 0x7FA5A5A5,
+        torch.float32: 0x7FA5A5A5}
+RAW = {torch.bfloat16: torch.int16, torch.int16: torch.int16, torch.uint8: torch.uint8, torch.int32: torch.int32,
+       torch.float32: torch.int32}
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _sentinel(dtype):
+    v = SENT[dtype]
+    return v - (1 << 32) if RAW[dtype] == torch.int32 and v >= (1 << 31) else v
+
+
+class Guard:
+    """A [rows, cols] view with row stride ld >= cols inside [rows + 2 PAD, ld]."""
+
+    def __init__(self, rows, cols, ld=None, dtype=torch.bfloat16, init=None):
+        self.rows, self.cols, self.ld, self.dtype = rows, cols, ld or cols, dtype
+        raw = torch.full((rows + 2 * PAD, self.ld), _sentinel(dtype), dtype=RAW[dtype], device="cuda")
+        self.base = raw.view(dtype)
+        self.view = self.base[PAD:PAD + rows, :cols]
+        if init is not None:
+            self.view.copy_(init)
+
+    def check(self, name):
+        b = self.base.view(RAW[self.dtype]).cpu()
+        s = _sentinel(self.dtype)
+        assert bool((b[:PAD] == s).all()), f"{name}: rows before the view written"
+        assert bool((b[PAD + self.rows:] == s).all()), f"{name}: rows after the view written"
+        if self.ld > self.cols:
+            assert bool((b[PAD:PAD + self.rows, self.cols:] == s).all()), f"{name}: columns past the view written"
+
+
+class WsGuard:
+    """n bytes of workspace with WS_PAD sentinel bytes on each side; with
+    fill, the workspace itself starts as the sentinel too."""
+
+    def __init__(self, n, fill=False):
+        self.n = n
+        self.base = torch.full((n + 2 * WS_PAD,), SENT[torch.uint8], dtype=torch.uint8, device="cuda")
+        self.view = self.base[WS_PAD:WS_PAD + n]
+        if not fill:
+            self.view.zero_()
+
+    def check(self, name, unused=()):
+        b = self.base.cpu().numpy()
+        assert np.all(b[:WS_PAD] == 0xA5), f"{name}: bytes before the workspace written"
+        assert np.all(b[WS_PAD + self.n:] == 0xA5), f"{name}: bytes after the workspace written"
+        for lo, hi in unused:
+            assert np.all(b[WS_PAD + lo:WS_PAD + hi] == 0xA5), f"{name}: workspace bytes [{lo}, {hi}) written"
+
+
+def test_guard_modnorm_and_lora_consumer():
+    H, L, V = 5376, 130, 117
+    _say(f"guard modnorm H={H} L={L} V={V}")
+    x = dev_bf16(I.normal_bf16("gd.x", (L, H)))
+    br = dev_bf16(I.normal_bf16("gd.b", (L, H)))
+    dl = dev_bf16(I.normal_bf16("gd.d", (L, H), 0.05))
+    mod = dev_f32(I.normal_f32("gd.mod", (1, 6, H), 0.1))
+    x1, hh = Guard(L, H, H + 24), Guard(L, H, H + 8)
+    h3.fused_modulate_norm(x, mod[:, 0], mod[:, 1], hh.view, V, branch=br, gate=mod[:, 2], x1_out=x1.view,
+                           ld_mod_group=6 * H)
+    torch.cuda.synchronize()
+    x1.check("modnorm x1")
+    hh.check("modnorm h")
+    x1, hh = Guard(L, H, H + 8), Guard(L, H, H + 16)
+    h3.fused_modulate_norm_lora(x, br, dl, mod[:, 2], x1.view, V, shift=mod[:, 0], scale=mod[:, 1], h_out=hh.view,
+                                ld_mod_group=6 * H)
+    torch.cuda.synchronize()
+    x1.check("modnorm lora x1")
+    hh.check("modnorm lora h")
+
+
+def test_guard_modnorm_mxfp8_producer():
+    H, L, V = 1024, 77, 70
+    _say(f"guard modnorm mxfp8 H={H} L={L} V={V}")
+    x = dev_bf16(I.normal_bf16("gdm.x", (L, H)))
+    mod = dev_f32(I.normal_f32("gdm.mod", (1, 6, H), 0.1))
+    hq = Guard(L, H, H + 32, torch.uint8)
+    nsc = int(np.prod(h3.mx_scales_shape(L, H)))
+    hs = Guard(1, nsc, None, torch.uint8)
+    h3.fused_modulate_norm_mxfp8(x, mod[:, 0], mod[:, 1], hq.view, hs.view.view(h3.mx_scales_shape(L, H)), V,
+                                 ld_mod_group=6 * H)
+    torch.cuda.synchronize()
+    hq.check("modnorm mxfp8 codes")
+    hs.check("modnorm mxfp8 scales")
+
+
+@pytest.mark.parametrize("lora", [False, True])
+def test_guard_qk_norm_rope_in_packed_buffer(lora):
+    heads, L, V = 3, 150, 141
+    H = heads * 128
+    _say(f"guard qk_norm_rope heads={heads} L={L} V={V} lora={lora}")
+    qkv0 = torch.from_numpy(I.normal_bf16("gq.qkv", (L, 3 * H)).view(np.int16)).cuda().view(torch.bfloat16)
+    g = Guard(L, 3 * H, 3 * H + 16, init=qkv0)
+    gain = dev_bf16(I.normal_bf16("gq.g", (128,), 0.02, 1.0))
+    q, k, v = g.view[:, :H], g.view[:, H:2 * H], g.view[:, 2 * H:]
+    if lora:
+        d = Guard(L, 3 * H, 3 * H + 8, init=dev_bf16(I.normal_bf16("gq.d", (L, 3 * H), 0.05)))
+        h3.qk_norm_rope_lora(q, k, d.view[:, :H], d.view[:, H:2 * H], gain, gain, V, heads, v=v,
+                             dv=d.view[:, 2 * H:])
+    else:
+        h3.qk_norm_rope(q, k, gain, gain, V, heads)
+    torch.cuda.synchronize()
+    g.check("packed qkv")
+    if not lora:
+        assert torch.equal(v.view(torch.int16), qkv0[:, 2 * H:].view(torch.int16)), "v columns changed"
+
+
+@pytest.mark.parametrize("lora", [False, True])
+def test_guard_swiglu(lora):
+    F, L, V = 1000, 90, 83
+    _say(f"guard swiglu F={F} L={L} V={V} lora={lora}")
+    u = dev_bf16(I.normal_bf16("gs.u", (L, 2 * F)))
+    g = Guard(L, F, F + 24)
+    if lora:
+        h3.swiglu_lora(u, dev_bf16(I.normal_bf16("gs.d", (L, 2 * F), 0.05)), g.view, V, F)
+    else:
+        h3.swiglu(u, g.view, V, F)
+    torch.cuda.synchronize()
+    g.check("swiglu g")
+
+
+@pytest.mark.parametrize("epi", [h3.H3_EPI_STORE, h3.H3_EPI_RESIDUAL, h3.H3_EPI_SWIGLU])
+def test_guard_linear(epi):
+    M, Mv, N, K = 300, 291, 400, 320
+    _say(f"guard linear epi={epi} M={M} Mv={Mv} N={N} K={K}")
+    a = dev_bf16(I.normal_bf16("gl.a", (M, K)))
+    w = dev_bf16(I.normal_bf16("gl.w", (N, K), 0.05))
+    cols = N // 2 if epi == h3.H3_EPI_SWIGLU else N
+    c = Guard(M, cols, cols + 40)
+    kw = {}
+    if epi == h3.H3_EPI_RESIDUAL:
+        mod = dev_f32(I.normal_f32("gl.mod", (1, 6, N), 0.5))
+        kw = dict(resid=dev_bf16(I.normal_bf16("gl.r", (M, N))), gate=mod[:, 2], ld_gate_group=6 * N)
+    h3.linear(a, w, c.view, Mv, epi, **kw)
+    torch.cuda.synchronize()
+    c.check("linear c")
+
+
+@pytest.mark.parametrize("epi", [h3.H3_EPI_STORE, h3.H3_EPI_RESIDUAL, h3.H3_EPI_SWIGLU])
+def test_guard_mxfp8_quantize_and_linear(epi):
+    M, Mv, N, K = 300, 289, 512, 384
+    _say(f"guard mxfp8 epi={epi} M={M} Mv={Mv} N={N} K={K}")
+    a_bf = dev_bf16(I.normal_bf16("gx.a", (M, K)))
+    w_bf = dev_bf16(I.normal_bf16("gx.w", (N, K), 0.05))
+    aq = Guard(M, K, K + 16, torch.uint8)
+    as_ = Guard(1, int(np.prod(h3.mx_scales_shape(M, K))), None, torch.uint8)
+    h3.mxfp8_quantize(a_bf, Mv, aq.view, as_.view.view(h3.mx_scales_shape(M, K)))
+    wq = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(h3.mx_scales_shape(N, K), dtype=torch.uint8, device="cuda")
+    h3.mxfp8_quantize(w_bf, N, wq, ws)
+    torch.cuda.synchronize()
+    aq.check("mxfp8 codes")
+    as_.check("mxfp8 scales")
+    cols = N // 2 if epi == h3.H3_EPI_SWIGLU else N
+    c = Guard(M, cols, cols + 8)
+    kw = {}
+    if epi == h3.H3_EPI_RESIDUAL:
+        mod = dev_f32(I.normal_f32("gx.mod", (1, 6, N), 0.5))
+        kw = dict(resid=dev_bf16(I.normal_bf16("gx.r", (M, N))), gate=mod[:, 2], ld_gate_group=6 * N)
+    h3.linear_mxfp8(aq.view, as_.view.view(h3.mx_scales_shape(M, K)), wq, ws, c.view, Mv, epi, **kw)
+    torch.cuda.synchronize()
+    c.check("linear mxfp8 c")
+
+
+def _qkv(L, heads, tag):
+    H = heads * 128
+    return dev_bf16(np.concatenate([I.normal_bf16(f"{tag}.q", (L, H)), I.normal_bf16(f"{tag}.k", (L, H)),
+                                    I.normal_bf16(f"{tag}.v", (L, H))], axis=1))
+
+
+@pytest.mark.parametrize("grouped", [False, True])
+def test_guard_attention(grouped):
+    heads, L, V = 3, 777, 700
+    H = heads * 128
+    _say(f"guard attention heads={heads} L={L} V={V} grouped={grouped}")
+    qkv = _qkv(L, heads, "ga")
+    groups = [(0, 100, [("self", 0, 100)]), (100, 650, [("self", 0, 700)])] if grouped else None
+    o = Guard(L, H, H + 8)
+    w = WsGuard(h3.attention_workspace_bytes(V, heads, groups))
+    h3.attention(qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:], o.view, V, heads, groups=groups, workspace=w.view)
+    torch.cuda.synchronize()
+    o.check("attention o")
+    w.check("attention workspace")
+    o = Guard(L, H, H + 16)
+    h3.attention_noalloc(qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:], o.view, V, heads, groups=groups)
+    torch.cuda.synchronize()
+    o.check("attention_noalloc o")
+
+
+def test_guard_sparse_select_and_attention():
+    heads, L, V, P = 2, 1300, 1250, 100
+    H = heads * 128
+    _say(f"guard sparse heads={heads} L={L} V={V} P={P}")
+    qkv = _qkv(L, heads, "gsp")
+    nq, nk = h3.sparse_geometry(V, P)
+    # lists [heads][nq][nk] and counts [heads][nq] are dense: guarded as a whole
+    bl = Guard(1, heads * nq * nk, None, torch.int16)
+    counts = Guard(1, heads * nq, None, torch.int32)
+    sw = WsGuard(h3.sparse_select_workspace_bytes(V, P, heads))
+    h3.sparse_select(qkv[:, :H], qkv[:, H:2 * H], V, P, heads, 1.0, bl.view.view(heads, nq, nk),
+                     counts.view.view(heads, nq), sw.view)
+    torch.cuda.synchronize()
+    counts.check("sparse counts")
+    sw.check("sparse select workspace")
+    o = Guard(L, H, H + 8)
+    aw = WsGuard(h3.sparse_attention_workspace_bytes(V, P, heads))
+    h3.sparse_attention(qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:], o.view, V, P, heads,
+                        bl.view.view(heads, nq, nk), counts.view.view(heads, nq), workspace=aw.view)
+    torch.cuda.synchronize()
+    bl.check("sparse lists")
+    o.check("sparse attention o")
+    aw.check("sparse attention workspace")
+
+
+class _Tiny:
+    def __init__(self, tag, shape=I.TINY):
+        s = self.s = shape
+        wb = I.block_weights(s, tag)
+        self.w = {k: dev_bf16(v) for k, v in wb.items()}
+        self.weights = h3.make_weights(self.w)
+        self.x = dev_bf16(I.activations(s, tag=f"{tag}.x"))
+        self.mod = dev_f32(I.mod_table(s, 1, tag=f"{tag}.mod"))
+        self.dims = h3.make_dims(s.hidden, s.heads, s.ffn, rot_dim=s.rot_dim)
+
+
+def _ws_gaps(dims, L, groups=None):
+    """Byte ranges of a block workspace outside every intermediate (the
+    alignment gaps between them and after the V^T area)."""
+    off, lds = h3.workspace_layout(dims, L, groups)
+    H, F = dims.hidden, dims.ffn
+    size = [L * H * 2, L * 3 * H * 2, L * H * 2, L * H * 2, L * H * 2, L * F * 2, lds[h3.H3_WS_VT]]
+    total = h3.workspace_bytes(dims, L, groups)
+    ends = [o + n for o, n in zip(off, size)]
+    starts = off[1:] + [total]
+    return [(e, s) for e, s in zip(ends, starts) if s > e]
+
+
+@pytest.mark.parametrize("sparse", [False, True])
+def test_guard_block_and_workspace(sparse):
+    b = _Tiny("gb")
+    s, L, V = b.s, b.s.L_buf, b.s.valid_len
+    _say(f"guard block L={L} V={V} sparse={sparse}")
+    y = Guard(L, s.hidden)
+    if sparse:
+        w = WsGuard(h3.block_sparse_workspace_bytes(b.dims, L, V, 128), fill=True)
+        h3.block_forward_sparse(b.dims, b.weights, b.x, y.view, b.mod, 1, V, 128, 1.0, w.view)
+        gaps = []
+    else:
+        w = WsGuard(h3.workspace_bytes(b.dims, L), fill=True)
+        h3.block_forward(b.dims, b.weights, b.x, y.view, b.mod, 1, V, w.view)
+        gaps = _ws_gaps(b.dims, L)
+    torch.cuda.synchronize()
+    y.check("block y")
+    w.check("block workspace", gaps)
+
+
+def test_guard_streaming_block_with_export():
+    s = I.streaming_shape(hidden=256, heads=2, ffn=1024, cond=64, audio=32, video=200)
+    b = _Tiny("gst", s)
+    L, H = s.L_buf, s.hidden
+    hist = 150
+    hk, hv = (dev_bf16(t) for t in I.history_kv(hist, H, tag="gst.h"))
+    groups = [(0, 64, [("self", 0, L)]), (64, 96, [("self", 0, L)]), (96, L, [(hk, hv, 0, hist), ("self", 0, L)])]
+    _say(f"guard streaming block L={L} history={hist}")
+    y = Guard(L, H)
+    ek, ev = Guard(200, H, H + 8), Guard(200, H, H + 8)
+    w = WsGuard(h3.workspace_bytes(b.dims, L, groups), fill=True)
+    pos = torch.arange(hist, hist + L, dtype=torch.int32, device="cuda")
+    h3.block_forward(b.dims, b.weights, b.x, y.view, b.mod, 1, L, w.view, groups=groups, pos=pos,
+                     kv_export=(ek.view, ev.view, 96, 200))
+    torch.cuda.synchronize()
+    y.check("streaming y")
+    ek.check("export k")
+    ev.check("export v")
+    w.check("streaming workspace", _ws_gaps(b.dims, L, groups))
+
+
+def test_guard_stack_in_place():
+    b = _Tiny("gsk")
+    s, L, V = b.s, b.s.L_buf, b.s.valid_len
+    _say(f"guard stack L={L} V={V}")
+    x = Guard(L, s.hidden, init=b.x)
+    w = WsGuard(h3.workspace_bytes(b.dims, L), fill=True)
+    arr = h3.make_weight_stack([b.weights, b.weights])
+    mods = torch.stack([b.mod, b.mod]).contiguous()
+    h3.stack_forward(b.dims, arr, x.view, mods, 6 * s.hidden, 1, V, w.view)
+    torch.cuda.synchronize()
+    x.check("stack x")
+    w.check("stack workspace", _ws_gaps(b.dims, L))
+
+
+def test_guard_block_mxfp8():
+    b = _Tiny("gbm", I.scaled(I.TINY, 512, 500, name="tiny-mx"))
+    s, L, V = b.s, b.s.L_buf, b.s.valid_len
+    _say(f"guard block mxfp8 L={L} V={V}")
+    wq = {}
+    for n in ("w_qkv", "w_o", "w_up", "w_down"):
+        t = b.w[n]
+        q = torch.empty(t.shape, dtype=torch.uint8, device="cuda")
+        sc = torch.empty(h3.mx_scales_shape(*t.shape), dtype=torch.uint8, device="cuda")
+        h3.mxfp8_quantize(t, t.shape[0], q, sc)
+        wq[n] = (q, sc)
+    wq.update({k: b.w[k] for k in ("q_gain", "k_gain")})
+    y = Guard(L, s.hidden)
+    w = WsGuard(h3.block_mxfp8_workspace_bytes(b.dims, L, V, 128), fill=True)
+    h3.block_forward_mxfp8(b.dims, h3.make_weights_mx(wq), b.x, y.view, b.mod, 1, V, w.view, prefix_len=128,
+                           tau=1.0)
+    torch.cuda.synchronize()
+    y.check("block mxfp8 y")
+    w.check("block mxfp8 workspace")
+
+
+def test_guard_block_full_58816():
+    """The benchmark shape: y and the 7 GB workspace inside sentinel margins."""
+    s = I.FULL_58816
+    L, V, H, F = s.L_buf, s.valid_len, s.hidden, s.ffn
+    _say(f"guard full block L={L} V={V}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    w = {"w_qkv": (torch.randn((3 * H, H), generator=g, device="cuda") * 0.02).to(torch.bfloat16),
+         "w_o": (torch.randn((H, H), generator=g, device="cuda") * 0.02).to(torch.bfloat16),
+         "w_up": (torch.randn((2 * F, H), generator=g, device="cuda") * 0.02).to(torch.bfloat16),
+         "w_down": (torch.randn((H, F), generator=g, device="cuda") * 0.02).to(torch.bfloat16),
+         "q_gain": torch.ones(128, dtype=torch.bfloat16, device="cuda"),
+         "k_gain": torch.ones(128, dtype=torch.bfloat16, device="cuda")}
+    x = torch.randn((L, H), generator=g, device="cuda").to(torch.bfloat16)
+    mod = (0.1 * torch.randn((1, 6, H), generator=g, device="cuda")).float()
+    dims = h3.make_dims(H, s.heads, F)
+    y = Guard(L, H)
+    ws = WsGuard(h3.workspace_bytes(dims, L), fill=True)
+    h3.block_forward(dims, h3.make_weights(w), x, y.view, mod, 1, V, ws.view)
+    torch.cuda.synchronize()
+    y.check("full block y")
+    ws.check("full block workspace", _ws_gaps(dims, L))
+    del ws, w, x
+    torch.cuda.empty_cache()
