@@ -479,15 +479,18 @@ def full_4096(torch, h3, dev, gen, dims, weights, w, H, heads, F, iters, n_rot=4
                                wsv(h3.H3_WS_X1, H), wsv(h3.H3_WS_H2, H), wsv(h3.H3_WS_G, F))
     vt_ws = ws[off[h3.H3_WS_VT]:off[h3.H3_WS_VT] + lds[h3.H3_WS_VT]]
     x, y = xs[0], ys[0]
+    lws = torch.empty(128 << 20, dtype=torch.uint8, device=dev)  # stream-K partial sums
     calls = {
-        "gemm_qkv": (lambda: h3.linear(hbuf, w["w_qkv"], qkv, V), 2.0 * V * H * 3 * H),
+        "gemm_qkv": (lambda: h3.linear(hbuf, w["w_qkv"], qkv, V, workspace=lws), 2.0 * V * H * 3 * H),
         "attention": (lambda: h3.attention(qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:], o, V, heads,
                                            workspace=vt_ws), 4.0 * V * V * H),
         "gemm_out_residual": (lambda: h3.linear(o, w["w_o"], x1, V, h3.H3_EPI_RESIDUAL, resid=x, gate=mod[:, 2],
-                                                ld_gate_group=6 * H), 2.0 * V * H * H),
-        "gemm_up_swiglu": (lambda: h3.linear(h2, w["w_up"], g, V, h3.H3_EPI_SWIGLU), 2.0 * V * H * 2 * F),
+                                                ld_gate_group=6 * H, workspace=lws), 2.0 * V * H * H),
+        "gemm_up_swiglu": (lambda: h3.linear(h2, w["w_up"], g, V, h3.H3_EPI_SWIGLU, workspace=lws),
+                           2.0 * V * H * 2 * F),
         "gemm_down_residual": (lambda: h3.linear(g, w["w_down"], y, V, h3.H3_EPI_RESIDUAL, resid=x1,
-                                                 gate=mod[:, 5], ld_gate_group=6 * H), 2.0 * V * F * H),
+                                                 gate=mod[:, 5], ld_gate_group=6 * H, workspace=lws),
+                               2.0 * V * F * H),
     }
     kern = {}
     for k, (fn, fl) in calls.items():
@@ -614,19 +617,22 @@ def main(argv=None) -> int:
     k_ms = {}
     k_ms["modnorm"] = time_calls(torch, lambda: h3.fused_modulate_norm(
         x, mod[:, 0], mod[:, 1], hbuf, V, ld_mod_group=6 * H), kit, 1)
-    k_ms["gemm_qkv"] = time_calls(torch, lambda: h3.linear(hbuf, w["w_qkv"], qkv, V), kit, 1)
+    lws = torch.empty(128 << 20, dtype=torch.uint8, device=dev)  # stream-K partial sums (at most 128 MiB)
+    k_ms["gemm_qkv"] = time_calls(torch, lambda: h3.linear(hbuf, w["w_qkv"], qkv, V, workspace=lws), kit, 1)
     k_ms["qk_norm_rope"] = time_calls(torch, lambda: h3.qk_norm_rope(
         qkv[:, :H], qkv[:, H:2 * H], w["q_gain"], w["k_gain"], V, heads), kit, 1)
     vt_ws = ws[off[h3.H3_WS_VT]:off[h3.H3_WS_VT] + lds[h3.H3_WS_VT]]
     k_ms["attention"] = time_calls(torch, lambda: h3.attention(
         qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:], o, V, heads, workspace=vt_ws), kit, 1)
     k_ms["gemm_out_residual"] = time_calls(torch, lambda: h3.linear(
-        o, w["w_o"], x1, V, h3.H3_EPI_RESIDUAL, resid=x, gate=mod[:, 2], ld_gate_group=6 * H), kit, 1)
+        o, w["w_o"], x1, V, h3.H3_EPI_RESIDUAL, resid=x, gate=mod[:, 2], ld_gate_group=6 * H, workspace=lws), kit, 1)
     k_ms["modnorm2"] = time_calls(torch, lambda: h3.fused_modulate_norm(
         x1, mod[:, 3], mod[:, 4], h2, V, ld_mod_group=6 * H), kit, 1)
-    k_ms["gemm_up_swiglu"] = time_calls(torch, lambda: h3.linear(h2, w["w_up"], g, V, h3.H3_EPI_SWIGLU), kit, 1)
+    k_ms["gemm_up_swiglu"] = time_calls(torch, lambda: h3.linear(h2, w["w_up"], g, V, h3.H3_EPI_SWIGLU,
+                                                                 workspace=lws), kit, 1)
     k_ms["gemm_down_residual"] = time_calls(torch, lambda: h3.linear(
-        g, w["w_down"], y, V, h3.H3_EPI_RESIDUAL, resid=x1, gate=mod[:, 5], ld_gate_group=6 * H), kit, 1)
+        g, w["w_down"], y, V, h3.H3_EPI_RESIDUAL, resid=x1, gate=mod[:, 5], ld_gate_group=6 * H, workspace=lws),
+        kit, 1)
 
     progress("per-kernel breakdown timed")
     # The online-softmax form on the same shape: q scaled by 8 puts every

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define H3_ABI_VERSION 4
+#define H3_ABI_VERSION 5
 #define H3_MAX_SEGMENTS 4   /* K/V segments per query group */
 #define H3_MAX_GROUPS 8     /* query groups per attention call */
 #define H3_SPARSE_Q_BLOCK 256      /* block-sparse attention: target query block rows */
@@ -207,9 +207,13 @@ size_t h3_block_workspace_bytes(const h3_dims *dims, int64_t L_buf,
  *   H3_WS_X1  x1  (cols H)      H3_WS_H2  h2  (cols H)
  *   H3_WS_G   g   (cols F)
  *   H3_WS_VT  attention's V^T staging (see h3_attention_workspace_bytes);
- *             its "row stride" entry holds its size in bytes.              */
+ *             its "row stride" entry holds its size in bytes.
+ *   H3_WS_GEMM the projections' stream-K partial sums (see
+ *             h3_linear_workspace_bytes), the largest any of the four needs
+ *             at up to L_buf rows; its "row stride" entry holds its size in
+ *             bytes (0 when none would split).                           */
 enum { H3_WS_H = 0, H3_WS_QKV = 1, H3_WS_O = 2, H3_WS_X1 = 3, H3_WS_H2 = 4, H3_WS_G = 5,
-       H3_WS_VT = 6, H3_WS_COUNT = 7 };
+       H3_WS_VT = 6, H3_WS_GEMM = 7, H3_WS_COUNT = 8 };
 int h3_block_workspace_layout(const h3_dims *dims, int64_t L_buf,
                               const h3_qgroup *groups, int32_t n_groups,
                               int64_t offsets[H3_WS_COUNT], int64_t lds[H3_WS_COUNT]);
@@ -378,7 +382,18 @@ int h3_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ldw,
               const uint16_t *bias, uint16_t *c, int64_t ldc,
               int64_t M_buf, int64_t M_valid, int64_t N, int64_t K, int32_t epilogue,
               const uint16_t *resid, int64_t ld_r, const float *gate, int64_t ld_gate_group,
-              int32_t n_mod_groups, const int32_t *mod_idx, void *stream);
+              int32_t n_mod_groups, const int32_t *mod_idx,
+              void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes h3_linear uses to split its last, partial round of output
+ * tiles (stream-K tail) for M_valid rows: 0 when no split applies. With a
+ * workspace of at least this size (256-byte aligned, overlapping no operand)
+ * the tiles of a last round that fills at most 4/5 of the chip's 256
+ * workgroup slots are cut into equal ranges of K stages over all slots; each
+ * range leaves FP32 partial sums there and a fix-up pass adds them in K
+ * order and applies the epilogue. workspace NULL: one workgroup per tile.
+ * A non-NULL workspace smaller than this size is H3_ERR_WORKSPACE. */
+size_t h3_linear_workspace_bytes(int64_t M_valid, int64_t N, int64_t K, int32_t epilogue);
 
 /* ---------------------------------------------------------------------------
  * Sol-Attn block-sparse attention ([Sol-H3] §3.4 "Sparse Attention").
@@ -610,7 +625,8 @@ int h3_check_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t l
                     const uint16_t *bias, const uint16_t *c, int64_t ldc, int64_t M_buf,
                     int64_t M_valid, int64_t N, int64_t K, int32_t epilogue,
                     const uint16_t *resid, int64_t ld_r, const float *gate,
-                    int64_t ld_gate_group, int32_t n_mod_groups);
+                    int64_t ld_gate_group, int32_t n_mod_groups,
+                    const void *workspace, size_t ws_bytes);
 
 int h3_check_qk_norm_rope_lora(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t ld,
                                const uint16_t *dq, const uint16_t *dk, const uint16_t *dv, int64_t ld_d,

@@ -76,8 +76,14 @@ def test_workspace_layout_is_disjoint_and_aligned():
         # V^T staging: heads x 128 x round_up(L, 64) BF16 for the dense case,
         # then the key norm maxima and the workgroup flags
         assert lds[6] == d.heads * 128 * (-(-L // 64) * 64) * 2 + attention_extra(d.heads, L)
-        ends = [o + L * c * 2 for o, c in zip(off, cols)] + [off[6] + lds[6]]
-        for i in range(7):
+        # the projections' stream-K partial sums: the largest any of the four
+        # needs at up to L rows (two 256 x 256 FP32 slots per K range)
+        H, F = d.hidden, d.ffn
+        part = max(max(h3.linear_workspace_bytes(m, n, k, e) for m in range(256, L + 256, 256))
+                   for n, k, e in ((3 * H, H, 0), (H, H, 1), (2 * F, H, 2), (H, F, 1)))
+        assert lds[7] == part
+        ends = [o + L * c * 2 for o, c in zip(off, cols)] + [off[6] + lds[6], off[7] + lds[7]]
+        for i in range(8):
             assert off[i] % 256 == 0
             if i:
                 assert off[i] >= ends[i - 1]
@@ -281,40 +287,81 @@ def test_elementwise_and_linear_validators():
     assert lib.h3_check_swiglu(x, 2048, x + 2048, 1024, L, L, 1024) == h3.H3_ERR_ALIAS
     # linear (bias and the gate table's stride are checked by the twin too)
     assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 256, 0, None, 0, None, 0,
-                               1) == h3.H3_OK
+                               1, None, 0) == h3.H3_OK
     assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 204, 0, None, 0, None, 0,
-                               1) == h3.H3_ERR_ALIGN
+                               1, None, 0) == h3.H3_ERR_ALIGN
     assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 264, 0, None, 0, None, 0,
-                               1) == h3.H3_ERR_UNSUPPORTED
+                               1, None, 0) == h3.H3_ERR_UNSUPPORTED
     assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 256, 1, None, 0, None, 0,
-                               1) == h3.H3_ERR_NULL
+                               1, None, 0) == h3.H3_ERR_NULL
     assert lib.h3_check_linear(x, 256, addr(7), 256, None, x, 512, L, L, 512, 256, 0, None, 0, None, 0,
-                               1) == h3.H3_ERR_ALIAS
+                               1, None, 0) == h3.H3_ERR_ALIAS
     assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 256, 3, None, 0, None, 0,
-                               1) == h3.H3_ERR_UNSUPPORTED
+                               1, None, 0) == h3.H3_ERR_UNSUPPORTED
     # bias: 16-byte aligned, not inside c
     assert lib.h3_check_linear(x, 256, addr(7), 256, addr(8), hh, 512, L, L, 512, 256, 0, None, 0, None, 0,
-                               1) == h3.H3_OK
+                               1, None, 0) == h3.H3_OK
     assert lib.h3_check_linear(x, 256, addr(7), 256, addr(8) + 2, hh, 512, L, L, 512, 256, 0, None, 0, None, 0,
-                               1) == h3.H3_ERR_ALIGN
+                               1, None, 0) == h3.H3_ERR_ALIGN
     assert lib.h3_check_linear(x, 256, addr(7), 256, hh + 512 * 4, hh, 512, L, L, 512, 256, 0, None, 0, None, 0,
-                               1) == h3.H3_ERR_ALIAS
+                               1, None, 0) == h3.H3_ERR_ALIAS
     # gated residual: a table of G entries of N floats, ld_gate_group >= N apart
     r, gt = addr(9), addr(10)
     assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 256, 1, r, 512, gt, 6 * 512,
-                               3) == h3.H3_OK
+                               3, None, 0) == h3.H3_OK
     assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 256, 1, r, 512, gt, 256,
-                               3) == h3.H3_ERR_SHAPE
+                               3, None, 0) == h3.H3_ERR_SHAPE
     assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 256, 1, r, 512, gt, -6 * 512,
-                               3) == h3.H3_ERR_SHAPE
+                               3, None, 0) == h3.H3_ERR_SHAPE
     assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 256, 1, r, 512, gt, 6 * 512 + 2,
-                               3) == h3.H3_ERR_ALIGN
+                               3, None, 0) == h3.H3_ERR_ALIGN
     # one table entry: the stride is unused
     assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 256, 1, r, 512, gt, 0,
-                               1) == h3.H3_OK
+                               1, None, 0) == h3.H3_OK
     # the gate table may not overlap c
     assert lib.h3_check_linear(x, 256, addr(7), 256, None, hh, 512, L, L, 512, 256, 1, r, 512, hh + 64, 6 * 512,
-                               3) == h3.H3_ERR_ALIAS
+                               3, None, 0) == h3.H3_ERR_ALIAS
+
+
+def test_linear_stream_k_plan_and_workspace_checks():
+    """The stream-K tail of h3_linear: which shapes split their last round of
+    tiles (a tail of at most 4/5 of the 256 slots whose idle share, in K
+    stages, is worth at least 100 stages), the partial-sum area that needs
+    (two 256 x 256 FP32 slots per range), and the workspace checks."""
+    MB256 = 256 * 256 * 4
+    # 4,096 rows x 5,376 columns: 16 x 21 = 336 tiles, a tail of 80 tiles.
+    # K 21,504 (the down projection, 336 stages): 336 x 176/256 = 231 stages
+    # idle -> split, 80 x 336 units in all 256 slots
+    assert h3.linear_workspace_bytes(4096, 5376, 21504, h3.H3_EPI_RESIDUAL) == 256 * 2 * MB256
+    # K 5,376 (84 stages): 58 stages idle -> not worth a split
+    assert h3.linear_workspace_bytes(4096, 5376, 5376, h3.H3_EPI_RESIDUAL) == 0
+    # a tail of more than 4/5 of the slots is not split: 58,758 rows x 5,376 = 230 x 21 = 4,830 tiles, tail 222
+    assert h3.linear_workspace_bytes(58758, 5376, 21504, h3.H3_EPI_RESIDUAL) == 0
+    # whole rounds: 2,048 rows x 8,192 columns = 8 x 32 = 256 tiles
+    assert h3.linear_workspace_bytes(2048, 8192, 21504, h3.H3_EPI_STORE) == 0
+    # fewer tiles than slots: 1,000 x 2,048 = 32 tiles, K 7,552 = 118 stages: 3,776 units in 256 ranges
+    assert h3.linear_workspace_bytes(1000, 2048, 7552, h3.H3_EPI_STORE) == 256 * 2 * MB256
+    # ... K 1,024: 14 stages idle -> no split
+    assert h3.linear_workspace_bytes(1000, 2048, 1024, h3.H3_EPI_STORE) == 0
+    # one round plus a tail of 8: 2,600 x 6,144 = 11 x 24 = 264 tiles, K 6,656 = 104 stages: 832 units in
+    # 104 ranges of 8 stages
+    assert h3.linear_workspace_bytes(2600, 6144, 6656, h3.H3_EPI_STORE) == 104 * 2 * MB256
+    # SwiGLU tiles are 128 output columns: F = 1,024 -> 8 tile columns
+    assert h3.linear_workspace_bytes(1000, 2048, 7552, h3.H3_EPI_SWIGLU) == 256 * 2 * MB256
+    lib = h3.LIB
+    L, need = 1000, 256 * 2 * MB256
+    a, w, c, ws = addr(1), addr(2), addr(3), addr(20)
+    assert lib.h3_check_linear(a, 7552, w, 7552, None, c, 2048, L, L, 2048, 7552, 0, None, 0, None, 0, 1, ws,
+                               need) == h3.H3_OK
+    assert lib.h3_check_linear(a, 7552, w, 7552, None, c, 2048, L, L, 2048, 7552, 0, None, 0, None, 0, 1, ws,
+                               need - 1) == h3.H3_ERR_WORKSPACE
+    assert lib.h3_check_linear(a, 7552, w, 7552, None, c, 2048, L, L, 2048, 7552, 0, None, 0, None, 0, 1, ws + 64,
+                               need) == h3.H3_ERR_ALIGN
+    assert lib.h3_check_linear(a, 7552, w, 7552, None, c, 2048, L, L, 2048, 7552, 0, None, 0, None, 0, 1, c,
+                               need) == h3.H3_ERR_ALIAS
+    # NULL workspace: allowed (no split)
+    assert lib.h3_check_linear(a, 7552, w, 7552, None, c, 2048, L, L, 2048, 7552, 0, None, 0, None, 0, 1, None,
+                               0) == h3.H3_OK
 
 
 def test_lora_consumer_validators():

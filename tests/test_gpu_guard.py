@@ -163,6 +163,26 @@ def test_guard_linear(epi):
 
 
 @pytest.mark.parametrize("epi", [h3.H3_EPI_STORE, h3.H3_EPI_RESIDUAL, h3.H3_EPI_SWIGLU])
+def test_guard_linear_stream_k(epi):
+    M, Mv, N, K = 1024, 1000, 2048, 7552
+    _say(f"guard linear stream-K epi={epi} M={M} Mv={Mv} N={N} K={K}")
+    a = dev_bf16(I.normal_bf16("glk.a", (M, K)))
+    w = dev_bf16(I.normal_bf16("glk.w", (N, K), 0.05))
+    cols = N // 2 if epi == h3.H3_EPI_SWIGLU else N
+    c = Guard(M, cols, cols + 24)
+    ws = WsGuard(h3.linear_workspace_bytes(Mv, N, K, epi))
+    assert ws.n > 0
+    kw = {}
+    if epi == h3.H3_EPI_RESIDUAL:
+        mod = dev_f32(I.normal_f32("glk.mod", (1, 6, N), 0.5))
+        kw = dict(resid=dev_bf16(I.normal_bf16("glk.r", (M, N))), gate=mod[:, 2], ld_gate_group=6 * N)
+    h3.linear(a, w, c.view, Mv, epi, workspace=ws.view, **kw)
+    torch.cuda.synchronize()
+    c.check("linear stream-K c")
+    ws.check("linear stream-K workspace")
+
+
+@pytest.mark.parametrize("epi", [h3.H3_EPI_STORE, h3.H3_EPI_RESIDUAL, h3.H3_EPI_SWIGLU])
 def test_guard_mxfp8_quantize_and_linear(epi):
     M, Mv, N, K = 300, 289, 512, 384
     _say(f"guard mxfp8 epi={epi} M={M} Mv={Mv} N={N} K={K}")
@@ -254,7 +274,8 @@ def _ws_gaps(dims, L, groups=None):
     alignment gaps between them and after the V^T area)."""
     off, lds = h3.workspace_layout(dims, L, groups)
     H, F = dims.hidden, dims.ffn
-    size = [L * H * 2, L * 3 * H * 2, L * H * 2, L * H * 2, L * H * 2, L * F * 2, lds[h3.H3_WS_VT]]
+    size = [L * H * 2, L * 3 * H * 2, L * H * 2, L * H * 2, L * H * 2, L * F * 2, lds[h3.H3_WS_VT],
+            lds[h3.H3_WS_GEMM]]
     total = h3.workspace_bytes(dims, L, groups)
     ends = [o + n for o, n in zip(off, size)]
     starts = off[1:] + [total]

@@ -241,6 +241,51 @@ def test_linear_swiglu(M, Mv, F, K, bias):
     assert_zero_rows(g, Mv, "g")
 
 
+@pytest.mark.parametrize("epi,M,Mv,N,K", [(h3.H3_EPI_STORE, 1024, 1000, 2048, 7552),
+                                          (h3.H3_EPI_RESIDUAL, 2700, 2600, 6144, 6656),
+                                          (h3.H3_EPI_SWIGLU, 1024, 1000, 2048, 7552)])
+def test_linear_stream_k_tail(epi, M, Mv, N, K):
+    """Shapes whose last round of output tiles is split into K ranges
+    (stream-K tail): 32 tiles of 118 stages cut into 256 ranges of 14-15
+    stages (ranges straddle tiles), and 264 tiles = one whole round plus a
+    tail of 8 tiles of 104 stages cut into 104 ranges of 8. Against the
+    oracle, and against the unsplit call (a different FP32 summation order
+    only)."""
+    _say(f"linear stream-K epi={epi} M={M} Mv={Mv} N={N} K={K}")
+    need = h3.linear_workspace_bytes(Mv, N, K, epi)
+    assert need > 0, "the shape must take the split path"
+    ab = I.normal_bf16("lk.a", (M, K))
+    wb = I.normal_bf16("lk.w", (N, K), 0.05)
+    bb = I.normal_bf16("lk.b", (N,), 0.5)
+    cols = N // 2 if epi == h3.H3_EPI_SWIGLU else N
+    kw = {"bias": dev_bf16(bb)}
+    G = 3
+    if epi == h3.H3_EPI_RESIDUAL:
+        rb = I.normal_bf16("lk.r", (M, N))
+        mod = I.normal_f32("lk.mod", (G, 6, N), 0.5)
+        idx = I.rng_for("lk.idx").integers(0, G, size=M).astype(np.int32)
+        md = dev_f32(mod)
+        kw.update(resid=dev_bf16(rb), gate=md[:, 2], ld_gate_group=6 * N, n_mod_groups=G, mod_idx=dev_i32(idx))
+    a, w = dev_bf16(ab), dev_bf16(wb)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")  # stale contents must not matter
+    c = poison((M, cols))
+    h3.linear(a, w, c, Mv, epi, workspace=ws, **kw)
+    c0 = poison((M, cols))
+    h3.linear(a, w, c0, Mv, epi, **kw)
+    torch.cuda.synchronize()
+    u = O.linear(O.bf16_to_f64(ab[:Mv]), O.bf16_to_f64(wb), O.bf16_to_f64(bb))
+    if epi == h3.H3_EPI_STORE:
+        ref, slack = u, 0.0
+    elif epi == h3.H3_EPI_SWIGLU:
+        ref, slack = O.swiglu(u, N // 2), BF16_SLACK
+    else:
+        m = O.gather_mod(mod.astype(np.float64), idx, Mv)
+        ref, slack = O.gated_residual(O.bf16_to_f64(rb[:Mv]), m[:, O.GATE_A], u), 0.0
+    assert_parity(f64(c)[:Mv], ref, "c (split tail)", slack=slack)
+    assert_parity(f64(c)[:Mv], f64(c0)[:Mv], "c split vs unsplit", slack=slack)
+    assert_zero_rows(c, Mv, "c")
+
+
 # ---------------------------------------------------------------------------
 # attention
 # ---------------------------------------------------------------------------

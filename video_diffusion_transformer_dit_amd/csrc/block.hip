@@ -41,6 +41,7 @@ void block_steps(const h3_dims *dims, const h3_block_weights *w, const uint16_t 
     uint16_t *h2 = reinterpret_cast<uint16_t *>(ws + l.off[H3_WS_H2]);
     uint16_t *g = reinterpret_cast<uint16_t *>(ws + l.off[H3_WS_G]);
     void *vt = ws + l.off[H3_WS_VT];
+    void *part = ws + l.off[H3_WS_GEMM];  // the projections' stream-K partial sums
 
     const int64_t H = dims->hidden, F = dims->ffn, V = valid_len;
     const int64_t ldm = 6 * H;  // floats between modulation-table entries
@@ -52,7 +53,7 @@ void block_steps(const h3_dims *dims, const h3_block_weights *w, const uint16_t 
                    V, (int32_t)H, dims->eps, dims->norm_type, st);
     // 2 qkv
     launch_linear(h, H, w->w_qkv, H, w->b_qkv, qkv, 3 * H, V, 3 * H, H, H3_EPI_STORE, nullptr, 0, nullptr, 0, 1,
-                  nullptr, st);
+                  nullptr, st, part);
     launch_zero_rows(qkv, 3 * H, 3 * H, V, L_buf, st);
     // 3 q~, k~ (also zeroes their padding rows)
     launch_qk_norm_rope(qkv, qkv + H, 3 * H, w->q_gain, w->k_gain, pos, L_buf, V, dims->heads, dims->rot_dim,
@@ -71,18 +72,18 @@ void block_steps(const h3_dims *dims, const h3_block_weights *w, const uint16_t 
     }
     // 5 x1 = x + gate_a * (o W_o^T)
     launch_linear(o, H, w->w_o, H, w->b_o, x1, H, V, H, H, H3_EPI_RESIDUAL, x, H, gate_a, ldm, n_mod_groups, mod_idx,
-                  st);
+                  st, part);
     launch_zero_rows(x1, H, H, V, L_buf, st);
     // 6 h2
     launch_modnorm(x1, H, nullptr, 0, shift_f, scale_f, nullptr, ldm, n_mod_groups, mod_idx, nullptr, 0, h2, H,
                    L_buf, V, (int32_t)H, dims->eps, dims->norm_type, st);
     // 7 g = silu(gate) * up
     launch_linear(h2, H, w->w_up, H, w->b_up, g, F, V, 2 * F, H, H3_EPI_SWIGLU, nullptr, 0, nullptr, 0, 1, nullptr,
-                  st);
+                  st, part);
     launch_zero_rows(g, F, F, V, L_buf, st);
     // 8 y = x1 + gate_f * (g W_down^T)
     launch_linear(g, F, w->w_down, F, w->b_down, y, H, V, H, F, H3_EPI_RESIDUAL, x1, H, gate_f, ldm, n_mod_groups,
-                  mod_idx, st);
+                  mod_idx, st, part);
     launch_zero_rows(y, H, H, V, L_buf, st);
     // 9 KV refresh export
     if (kv_export && kv_export->len > 0) {

@@ -52,6 +52,12 @@ struct GemmArgs {
     int32_t tiles_m, tiles_n;
     int32_t group_m;      // tile rows per group of the tile order
     int32_t ffn;          // SwiGLU output width
+    // Stream-K tail: workgroups [0, dp_tiles) each own a whole tile; the last
+    // sk_tiles tiles of the order are cut into sk_groups equal ranges of
+    // (tile, K stage) units, whose FP32 partial sums go to `part` (two
+    // 256 x 256 slots per range) for the fix-up pass.
+    int32_t dp_tiles, sk_tiles, sk_groups;
+    float *part;
 };
 
 // LDS operand tile: row r holds 8 chunks of 16 B (64 k values); chunk c of
@@ -60,13 +66,12 @@ struct GemmArgs {
 // see 8 distinct chunk positions, so the 16 reads hit distinct banks.
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kChunksPerRow + (chunk ^ ((row >> 1) & 7)); }
 
-template <int EPI>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
-    // LDS: two stage slots of [W tile, A tile], 32 KB each (128 KB).
-    __shared__ uint4 smem[2 * 2 * kTileChunks];
-
-    int tm, tn;
-    gemm_tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+// One output tile (tm, tn) over the K stages [k0, k1): the whole tile with
+// its epilogue, or (PARTIAL) a range of its stages whose FP32 partial sums go
+// to `part` (stream-K tail). smem: the two 64 KB stage slots.
+template <int EPI, bool PARTIAL>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &p, uint4 *smem, int tm, int tn, int k0, int k1,
+                                          float *part) {
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
@@ -112,9 +117,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
             w_voff[i] = (int)((row * p.ldw + 8 * c) * 2);
         }
     }
-    // Stages past the end of K load through a zero-length descriptor: the
-    // loads return zero without touching memory, so every stage issues the
-    // same 16 loads and the vmcnt arithmetic below is constant.
+    // Stages past the end of the range load through a zero-length descriptor:
+    // the loads return zero without touching memory, so every stage issues
+    // the same 16 loads and the vmcnt arithmetic below is constant.
     i32x4_t rs_none = rs_a;
     rs_none.z = 0;
     // LDS byte address of this wave's first slab of slot 0's W tile.
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
         const int i = d >> 1, op = (d & 1) ? 1 : 0;
         const int slab = 8 * wave + i;
         i32x4_t r = op ? rs_a : ((EPI == H3_EPI_SWIGLU && ((slab >> 1) & 1)) ? rs_w2 : rs_w);
-        if (kt >= (int)(p.K / BK)) r = rs_none;
+        if (kt >= k1) r = rs_none;
         const uint32_t m0 = lds_wave + (uint32_t)(((slot * 2 + op) * kTileChunks + 64 * i) * 16);
         dma_slab(r, m0, op ? a_voff[i] : w_voff[i], kt * BK * 2);
     };
@@ -138,7 +143,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    const int KT = (int)(p.K / BK);
     const int r32 = lane & 31, g2 = lane >> 5;
     // This wave's MFMA operands of one 16-wide k-step: 4 W and 4 A sub-tiles.
     struct Ops {
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
         }
     };
     // One k-step (16 MFMAs) of stage kt, whose operands `cur` already holds.
-    // Stage kt lives in slot kt & 1. Per k-step:
+    // Stage kt lives in slot (kt - k0) & 1. Per k-step:
     //  ks 0..2: read k-step ks+1 of stage kt into `nxt`;
     //  ks 3:    wait for stage kt+1 (its 16 loads are the only ones in
     //           flight), make sure this wave's reads of stage kt are done,
@@ -168,7 +172,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
     // The loads and reads sit between the MFMAs in a fixed order, so issuing
     // them never leaves the matrix pipe idle. Raw barrier: __syncthreads()'s
     // fences would wait for every outstanding load. Reads of a stage at or
-    // past KT see stale or zero data and are never used.
+    // past k1 see stale or zero data and are never used.
     auto kstep = [&](int kt, int ks, int slot, const Ops &cur, Ops &nxt) {
         if (ks == 3) {
             asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
@@ -196,29 +200,125 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
         kstep(kt, 3, slot, r1, r0);
     };
 
-    // Prologue: stage 0 and the first half of stage 1 in flight; stage 0's
-    // first k-step in registers.
+    // Prologue: stage k0 and the first half of stage k0+1 in flight; stage
+    // k0's first k-step in registers.
 #pragma unroll
-    for (int d = 0; d < 16; ++d) dma(0, d, 0);
+    for (int d = 0; d < 16; ++d) dma(0, d, k0);
 #pragma unroll
-    for (int d = 0; d < 8; ++d) dma(1, d, 1);
+    for (int d = 0; d < 8; ++d) dma(1, d, k0 + 1);
     Ops opa, opb;
     asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int r = 0; r < 8; ++r) read(0, 0, r, opa);
-    int kt = 0;
+    int kt = k0;
 #pragma unroll 1
-    for (; kt + 2 <= KT; kt += 2) {
+    for (; kt + 2 <= k1; kt += 2) {
         stage(kt, 0, opa, opb);
         stage(kt + 1, 1, opa, opb);
     }
-    if (kt < KT) stage(kt, 0, opa, opb);  // odd KT
-    // Drain the loads still in flight (stages past K) before the workgroup
-    // can end.
+    if (kt < k1) stage(kt, 0, opa, opb);  // odd stage count
+    // Drain the loads still in flight (stages past the range) before the
+    // workgroup can end or reuse the LDS slots.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+    if constexpr (!PARTIAL) {
+        gemm_epilogue<EPI>(p, acc, tm, tn, wm, wn, r32, g2);
+    } else {
+        // FP32 partial sums, register-major: float4 q of thread t at
+        // part[(q * 256 + t) * 4], q = (4 i + j) * 4 + e / 4.
+        float4 *dst = reinterpret_cast<float4 *>(part);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; e += 4)
+                    dst[((4 * i + j) * 4 + e / 4) * kThreads + t] =
+                        make_float4(acc[i][j][e], acc[i][j][e + 1], acc[i][j][e + 2], acc[i][j][e + 3]);
+    }
+}
+
+// Data-parallel tiles: one whole tile per workgroup, the first dp_tiles tiles
+// of the grouped order, XCD-contiguous.
+template <int EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
+    // LDS: two stage slots of [W tile, A tile], 32 KB each (128 KB).
+    __shared__ uint4 smem[2 * 2 * kTileChunks];
+    int tm, tn;
+    gemm_tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, p.dp_tiles, tm, tn);
+    gemm_tile<EPI, false>(p, smem, tm, tn, 0, (int)(p.K / BK), nullptr);
+}
+
+// Stream-K tail: workgroup w takes the units [w U / G, (w + 1) U / G) of the
+// tail's U = sk_tiles * (K / 64) (tile, stage) units, G = sk_groups; a range
+// is shorter than a tile, so it touches at most two tiles, and leaves FP32
+// partial sums for each in its two slots of `part`.
+template <int EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_sk_kernel(GemmArgs p) {
+    __shared__ uint4 smem[2 * 2 * kTileChunks];
+    const int KT = (int)(p.K / BK);
+    const int w = blockIdx.x;
+    const int64_t U = (int64_t)p.sk_tiles * KT;
+    const int u0 = (int)(w * U / p.sk_groups), u1 = (int)((w + 1) * U / p.sk_groups);
+    const int t0 = u0 / KT, t1 = (u1 - 1) / KT;
+#pragma unroll 1
+    for (int tile = t0; tile <= t1; ++tile) {
+        int tm, tn;
+        gemm_grouped_coords(p.dp_tiles + tile, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+        const int k0 = tile == t0 ? u0 - tile * KT : 0;
+        const int k1 = tile == t1 ? u1 - tile * KT : KT;
+        if (tile > t0) __syncthreads();  // every wave is done with the LDS slots
+        gemm_tile<EPI, true>(p, smem, tm, tn, k0, k1, p.part + ((int64_t)w * 2 + (tile - t0)) * (BM * BN));
+    }
+}
+
+
+// Stream-K fix-up: one wavefront per (tail tile, 128 x 128 quarter) sums, in
+// K order, the partial sums of the workgroups whose unit ranges cover the
+// tile, then applies the epilogue exactly as the main kernel's wave would.
+template <int EPI>
+__global__ __launch_bounds__(64) void gemm_fixup_kernel(GemmArgs p) {
+    const int lane = threadIdx.x;
+    const int wave = blockIdx.x & 3;  // the quarter: the main kernel's wave
+    const int tile = blockIdx.x >> 2;
+    const int t = wave * 64 + lane;   // the main kernel's thread
+    const int wm = wave >> 1, wn = wave & 1;
+    const int r32 = lane & 31, g2 = lane >> 5;
+    const int KT = (int)(p.K / BK);
+    const int64_t U = (int64_t)p.sk_tiles * KT, G = p.sk_groups;
+    const int64_t tb = (int64_t)tile * KT, te = tb + KT;
+    // workgroup w covers units [w U / G, (w + 1) U / G)
+    int64_t w = (tb * G) / U;
+    while (w > 0 && (w * U) / G > tb) --w;
+    while (((w + 1) * U) / G <= tb) ++w;
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    for (; w < G && (w * U) / G < te; ++w) {
+        const int64_t ws = (w * U) / G;
+        const int sg = ws / KT == tile ? 0 : 1;  // this tile is the workgroup's first or second segment
+        const float4 *src = reinterpret_cast<const float4 *>(p.part + (w * 2 + sg) * (BM * BN));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; e += 4) {
+                    const float4 v = src[((4 * i + j) * 4 + e / 4) * kThreads + t];
+                    acc[i][j][e] += v.x;
+                    acc[i][j][e + 1] += v.y;
+                    acc[i][j][e + 2] += v.z;
+                    acc[i][j][e + 3] += v.w;
+                }
+    }
+    int tm, tn;
+    gemm_grouped_coords(p.dp_tiles + tile, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     gemm_epilogue<EPI>(p, acc, tm, tn, wm, wn, r32, g2);
 }
 
@@ -227,7 +327,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
 void launch_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ldw, const uint16_t *bias,
                    uint16_t *c, int64_t ldc, int64_t M_valid, int64_t N, int64_t K, int32_t epilogue,
                    const uint16_t *resid, int64_t ld_r, const float *gate, int64_t ld_gate_group,
-                   int32_t n_mod_groups, const int32_t *mod_idx, hipStream_t stream) {
+                   int32_t n_mod_groups, const int32_t *mod_idx, hipStream_t stream, void *workspace) {
     if (M_valid <= 0) return;
     GemmArgs p;
     p.a = a; p.w = w; p.bias = bias; p.c = c; p.resid = resid; p.gate = gate; p.mod_idx = mod_idx;
@@ -236,16 +336,37 @@ void launch_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ld
     p.M = M_valid; p.N = N; p.K = K;
     p.n_groups = n_mod_groups > 0 ? n_mod_groups : 1;
     p.ffn = (int32_t)(N / 2);
-    p.tiles_m = (int32_t)((M_valid + BM - 1) / BM);
-    p.tiles_n = epilogue == H3_EPI_SWIGLU ? (int32_t)((N / 2 + BN / 2 - 1) / (BN / 2)) : (int32_t)((N + BN - 1) / BN);
+    const GemmPlan plan = gemm_plan(M_valid, N, K, epilogue);
+    p.tiles_m = plan.tiles_m;
+    p.tiles_n = plan.tiles_n;
     // Measured on the block's projections: narrow grids keep the L2 best
     // with 2 tile rows per group, wide ones (the SwiGLU FFN) with 8.
     p.group_m = p.tiles_n >= 128 ? 8 : 2;
-    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
+    const bool sk = workspace != nullptr && plan.sk_groups > 0;
+    p.dp_tiles = sk ? plan.dp_tiles : plan.tiles;
+    p.sk_tiles = sk ? plan.sk_tiles : 0;
+    p.sk_groups = sk ? plan.sk_groups : 0;
+    p.part = static_cast<float *>(workspace);
+    const dim3 grid((unsigned)p.dp_tiles);
+    if (p.dp_tiles > 0) {
+        switch (epilogue) {
+            case H3_EPI_RESIDUAL: gemm_bf16_kernel<H3_EPI_RESIDUAL><<<grid, kThreads, 0, stream>>>(p); break;
+            case H3_EPI_SWIGLU: gemm_bf16_kernel<H3_EPI_SWIGLU><<<grid, kThreads, 0, stream>>>(p); break;
+            default: gemm_bf16_kernel<H3_EPI_STORE><<<grid, kThreads, 0, stream>>>(p); break;
+        }
+    }
+    if (!sk) return;
+    const dim3 sgrid((unsigned)p.sk_groups);
     switch (epilogue) {
-        case H3_EPI_RESIDUAL: gemm_bf16_kernel<H3_EPI_RESIDUAL><<<grid, kThreads, 0, stream>>>(p); break;
-        case H3_EPI_SWIGLU: gemm_bf16_kernel<H3_EPI_SWIGLU><<<grid, kThreads, 0, stream>>>(p); break;
-        default: gemm_bf16_kernel<H3_EPI_STORE><<<grid, kThreads, 0, stream>>>(p); break;
+        case H3_EPI_RESIDUAL: gemm_bf16_sk_kernel<H3_EPI_RESIDUAL><<<sgrid, kThreads, 0, stream>>>(p); break;
+        case H3_EPI_SWIGLU: gemm_bf16_sk_kernel<H3_EPI_SWIGLU><<<sgrid, kThreads, 0, stream>>>(p); break;
+        default: gemm_bf16_sk_kernel<H3_EPI_STORE><<<sgrid, kThreads, 0, stream>>>(p); break;
+    }
+    const dim3 fgrid((unsigned)p.sk_tiles * 4);
+    switch (epilogue) {
+        case H3_EPI_RESIDUAL: gemm_fixup_kernel<H3_EPI_RESIDUAL><<<fgrid, 64, 0, stream>>>(p); break;
+        case H3_EPI_SWIGLU: gemm_fixup_kernel<H3_EPI_SWIGLU><<<fgrid, 64, 0, stream>>>(p); break;
+        default: gemm_fixup_kernel<H3_EPI_STORE><<<fgrid, 64, 0, stream>>>(p); break;
     }
 }
 
@@ -256,14 +377,15 @@ using namespace h3;
 extern "C" int h3_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ldw, const uint16_t *bias,
                          uint16_t *c, int64_t ldc, int64_t M_buf, int64_t M_valid, int64_t N, int64_t K,
                          int32_t epilogue, const uint16_t *resid, int64_t ld_r, const float *gate,
-                         int64_t ld_gate_group, int32_t n_mod_groups, const int32_t *mod_idx, void *stream) {
+                         int64_t ld_gate_group, int32_t n_mod_groups, const int32_t *mod_idx, void *workspace,
+                         size_t ws_bytes, void *stream) {
     int s = h3_check_linear(a, lda, w, ldw, bias, c, ldc, M_buf, M_valid, N, K, epilogue, resid, ld_r, gate,
-                            ld_gate_group, n_mod_groups);
+                            ld_gate_group, n_mod_groups, workspace, ws_bytes);
     if (s != H3_OK || M_buf == 0) return s;
     if ((s = device_check()) != H3_OK) return s;
     const hipStream_t st = (hipStream_t)stream;
     launch_linear(a, lda, w, ldw, bias, c, ldc, M_valid, N, K, epilogue, resid, ld_r, gate, ld_gate_group,
-                  n_mod_groups, mod_idx, st);
+                  n_mod_groups, mod_idx, st, workspace);
     launch_zero_rows(c, ldc, epilogue == H3_EPI_SWIGLU ? N / 2 : N, M_valid, M_buf, st);
     return launch_status();
 }

@@ -61,14 +61,10 @@ __device__ __forceinline__ void dma_dword(i32x4_t rsrc, uint32_t lds, int voff, 
         : "memory", "m0");
 }
 
-// GEMM tile order: map a linear workgroup id to (tile_m, tile_n) so that each
-// XCD (workgroups are dealt round-robin over 8 XCDs) walks a contiguous range
-// of a grouped order (group_m tile rows at a time, column by column).
-__device__ __forceinline__ void gemm_tile_coords(int bid, int tiles_m, int tiles_n, int group_m, int &tm, int &tn) {
-    const int T = tiles_m * tiles_n;
-    const int q = T / 8, rr = T % 8;
-    const int xcd = bid % 8, local = bid / 8;
-    const int lin = xcd < rr ? xcd * (q + 1) + local : rr * (q + 1) + (xcd - rr) * q + local;
+// GEMM tile order. The grouped order walks group_m tile rows at a time,
+// column by column; gemm_grouped_coords maps a position in it to (tile_m,
+// tile_n).
+__device__ __forceinline__ void gemm_grouped_coords(int lin, int tiles_m, int tiles_n, int group_m, int &tm, int &tn) {
     const int per_group = group_m * tiles_n;
     const int group = lin / per_group;
     const int first_m = group * group_m;
@@ -76,6 +72,19 @@ __device__ __forceinline__ void gemm_tile_coords(int bid, int tiles_m, int tiles
     const int in_group = lin - group * per_group;
     tm = first_m + in_group % gsz;
     tn = in_group / gsz;
+}
+// Workgroup id -> tile among the first T tiles of the grouped order, such that
+// each XCD (workgroups are dealt round-robin over 8 XCDs) walks a contiguous
+// range of that order.
+__device__ __forceinline__ void gemm_tile_coords(int bid, int tiles_m, int tiles_n, int group_m, int T, int &tm,
+                                                 int &tn) {
+    const int q = T / 8, rr = T % 8;
+    const int xcd = bid % 8, local = bid / 8;
+    const int lin = xcd < rr ? xcd * (q + 1) + local : rr * (q + 1) + (xcd - rr) * q + local;
+    gemm_grouped_coords(lin, tiles_m, tiles_n, group_m, tm, tn);
+}
+__device__ __forceinline__ void gemm_tile_coords(int bid, int tiles_m, int tiles_n, int group_m, int &tm, int &tn) {
+    gemm_tile_coords(bid, tiles_m, tiles_n, group_m, tiles_m * tiles_n, tm, tn);
 }
 
 // ---- MXFP8 (E4M3 elements, one E8M0 scale per 32 values) ----

@@ -80,6 +80,27 @@ void sparse_geometry(int64_t valid_len, int64_t prefix_len, int32_t heads, Spars
 // the V^T staging.
 void sparse_vt_group(int64_t valid_len, int64_t prefix_len, h3_qgroup *g);
 
+// Launch plan of one BF16 GEMM (h3_linear): 256 x 256 output tiles in the
+// grouped order, K in stages of 64. When the last round of tiles fills at
+// most 4/5 of the chip's 256 workgroup slots and leaves the equivalent of at
+// least kSkWorthStages stages idle (stages x idle share), that tail
+// (sk_tiles tiles) is
+// cut into sk_groups equal ranges of (tile, stage) units, at least
+// kSkMinStages stages each and less than one tile (so a range touches at
+// most two tiles), whose FP32 partial sums a fix-up pass adds; the other
+// dp_tiles tiles run one per workgroup. sk_groups == 0: no tail split.
+constexpr int kGemmSlots = 256;
+constexpr int kSkMinStages = 8;
+constexpr int kSkWorthStages = 100;
+struct GemmPlan {
+    int32_t tiles_m, tiles_n, tiles, stages;
+    int32_t dp_tiles, sk_tiles, sk_groups;
+    size_t part_bytes;  // 2 slots of 256 x 256 FP32 per range
+};
+GemmPlan gemm_plan(int64_t M_valid, int64_t N, int64_t K, int32_t epilogue);
+// Largest part_bytes of any plan with at most M_buf rows, for these (N, K, epilogue).
+size_t gemm_part_bytes_max(int64_t M_buf, int64_t N, int64_t K, int32_t epilogue);
+
 // Byte offsets and row strides of the block's workspace buffers.
 struct WsLayout {
     int64_t off[H3_WS_COUNT];

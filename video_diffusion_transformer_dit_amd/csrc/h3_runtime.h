@@ -45,10 +45,12 @@ void launch_zero_rows(uint16_t *p, int64_t ld, int64_t cols, int64_t r0, int64_t
 void launch_copy_rows(const uint16_t *src, int64_t ld_src, uint16_t *dst, int64_t ld_dst, int64_t rows,
                       int64_t cols, hipStream_t stream);
 
+// workspace: NULL, or at least gemm_plan(...).part_bytes bytes for the
+// stream-K tail's partial sums (then the tail is split when the plan says so).
 void launch_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ldw, const uint16_t *bias,
                    uint16_t *c, int64_t ldc, int64_t M_valid, int64_t N, int64_t K, int32_t epilogue,
                    const uint16_t *resid, int64_t ld_r, const float *gate, int64_t ld_gate_group,
-                   int32_t n_mod_groups, const int32_t *mod_idx, hipStream_t stream);
+                   int32_t n_mod_groups, const int32_t *mod_idx, hipStream_t stream, void *workspace = nullptr);
 
 void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k,
                       const uint16_t *v, int64_t ld_v, uint16_t *o, int64_t ld_o, int64_t L_buf,

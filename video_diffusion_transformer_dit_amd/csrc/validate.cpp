@@ -177,6 +177,41 @@ void attn_schedule(const h3_qgroup *groups, int n_groups, int64_t dense_len, int
     out->items = items;
 }
 
+GemmPlan gemm_plan(int64_t M_valid, int64_t N, int64_t K, int32_t epilogue) {
+    GemmPlan g = {};
+    g.tiles_m = (int32_t)((std::max<int64_t>(M_valid, 0) + 255) / 256);
+    g.tiles_n = epilogue == H3_EPI_SWIGLU ? (int32_t)((N / 2 + 127) / 128) : (int32_t)((N + 255) / 256);
+    g.tiles = g.tiles_m * g.tiles_n;
+    g.stages = (int32_t)(K / 64);
+    g.dp_tiles = g.tiles;
+    const int32_t tail = g.tiles % kGemmSlots;
+    if (tail == 0 || 5 * tail > 4 * kGemmSlots) return g;
+    // The split costs about as much as 100 stages of the last round (the
+    // partial sums' traffic, the fix-up pass, two more launches): take it only
+    // where the idle share of the last round is worth more.
+    if ((int64_t)g.stages * (kGemmSlots - tail) < (int64_t)kSkWorthStages * kGemmSlots) return g;
+    const int64_t units = (int64_t)tail * g.stages;
+    const int32_t groups = (int32_t)std::min<int64_t>(kGemmSlots, units / kSkMinStages);
+    if (groups <= tail) return g;  // no range would be shorter than a tile
+    g.dp_tiles = g.tiles - tail;
+    g.sk_tiles = tail;
+    g.sk_groups = groups;
+    g.part_bytes = (size_t)groups * 2 * 256 * 256 * 4;
+    return g;
+}
+
+size_t gemm_part_bytes_max(int64_t M_buf, int64_t N, int64_t K, int32_t epilogue) {
+    // part_bytes grows with the tail's units, at most kGemmSlots ranges: bound
+    // it by the plan of every tile count up to M_buf's.
+    const int64_t tm_max = (std::max<int64_t>(M_buf, 0) + 255) / 256;
+    size_t best = 0;
+    for (int64_t tm = 1; tm <= tm_max; ++tm) {
+        best = std::max(best, gemm_plan(tm * 256, N, K, epilogue).part_bytes);
+        if (best >= (size_t)kGemmSlots * 2 * 256 * 256 * 4) break;
+    }
+    return best;
+}
+
 void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads, VtPlan *out) {
     out->n = 0;
     out->bytes = 0;
@@ -233,14 +268,23 @@ void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads
     }
 }
 
+// Partial-sum area for the block's four projections (run one after another).
+static size_t block_gemm_part_bytes(const h3_dims *d, int64_t L_buf) {
+    const int64_t H = d->hidden, F = d->ffn;
+    return std::max({gemm_part_bytes_max(L_buf, 3 * H, H, H3_EPI_STORE),
+                     gemm_part_bytes_max(L_buf, H, H, H3_EPI_RESIDUAL),
+                     gemm_part_bytes_max(L_buf, 2 * F, H, H3_EPI_SWIGLU),
+                     gemm_part_bytes_max(L_buf, H, F, H3_EPI_RESIDUAL)});
+}
+
 bool ws_layout(const h3_dims *d, int64_t L_buf, const h3_qgroup *groups, int n_groups, WsLayout *out) {
     if (check_dims(d) != H3_OK || L_buf < 0) return false;
     if (groups != nullptr && (n_groups < 1 || n_groups > H3_MAX_GROUPS)) return false;
     const int64_t H = d->hidden, F = d->ffn;
-    const int64_t cols[H3_WS_COUNT - 1] = {H, 3 * H, H, H, H, F};
+    const int64_t cols[H3_WS_VT] = {H, 3 * H, H, H, H, F};
     int64_t off = 0;
     auto align = [](int64_t b) { return (b + (int64_t)kWsAlign - 1) / (int64_t)kWsAlign * (int64_t)kWsAlign; };
-    for (int i = 0; i < H3_WS_COUNT - 1; ++i) {
+    for (int i = 0; i < H3_WS_VT; ++i) {
         out->off[i] = off;
         out->ld[i] = cols[i];
         out->cols[i] = cols[i];
@@ -252,6 +296,11 @@ bool ws_layout(const h3_dims *d, int64_t L_buf, const h3_qgroup *groups, int n_g
     out->ld[H3_WS_VT] = (int64_t)p.bytes;
     out->cols[H3_WS_VT] = 0;
     off += align((int64_t)p.bytes);
+    const int64_t part = (int64_t)block_gemm_part_bytes(d, L_buf);
+    out->off[H3_WS_GEMM] = off;
+    out->ld[H3_WS_GEMM] = part;
+    out->cols[H3_WS_GEMM] = 0;
+    off += align(part);
     out->total = (size_t)off;
     return true;
 }
@@ -272,6 +321,8 @@ bool block_sparse_layout(const h3_dims *d, int64_t L_buf, int64_t valid_len, int
     }
     l.ld[H3_WS_VT] = vt;
     int64_t off = l.off[H3_WS_VT] + align(vt);
+    l.off[H3_WS_GEMM] = off;
+    off += align(l.ld[H3_WS_GEMM]);
     l.total = (size_t)off;
     SparseGeom g;
     sparse_geometry(valid_len, prefix_len, d->heads, &g);
@@ -553,10 +604,15 @@ int h3_check_swiglu_lora(const uint16_t *u, int64_t ld_u, const uint16_t *du, in
     return H3_OK;
 }
 
+size_t h3_linear_workspace_bytes(int64_t M_valid, int64_t N, int64_t K, int32_t epilogue) {
+    if (M_valid < 0 || N <= 0 || K <= 0 || epilogue < H3_EPI_STORE || epilogue > H3_EPI_SWIGLU) return 0;
+    return gemm_plan(M_valid, N, K, epilogue).part_bytes;
+}
+
 int h3_check_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ldw, const uint16_t *bias,
                     const uint16_t *c, int64_t ldc, int64_t M_buf, int64_t M_valid, int64_t N, int64_t K,
                     int32_t epilogue, const uint16_t *resid, int64_t ld_r, const float *gate,
-                    int64_t ld_gate_group, int32_t n_mod_groups) {
+                    int64_t ld_gate_group, int32_t n_mod_groups, const void *workspace, size_t ws_bytes) {
     H3_TRY(check_rows(M_buf, M_valid));
     if (N <= 0 || K <= 0) return H3_ERR_SHAPE;
     if (epilogue < H3_EPI_STORE || epilogue > H3_EPI_SWIGLU) return H3_ERR_UNSUPPORTED;
@@ -587,6 +643,20 @@ int h3_check_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t l
         H3_TRY(check_bf16_mat(resid, ld_r, N));
         const Mat mr = mat(resid, M_buf, N, ld_r);
         if (!same(mr, mc) && overlap(mr, mc)) return H3_ERR_ALIAS;
+    }
+    if (workspace != nullptr) {
+        const size_t need = gemm_plan(M_valid, N, K, epilogue).part_bytes;
+        if (ws_bytes < need) return H3_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0) return H3_ERR_ALIGN;
+        if (need > 0) {
+            const Mat mws = mat(workspace, 1, (int64_t)need, (int64_t)need, 1);
+            if (overlap(mws, ma) || overlap(mws, mw) || overlap(mws, mc)) return H3_ERR_ALIAS;
+            if (bias && overlap(mws, mat(bias, 1, N, N))) return H3_ERR_ALIAS;
+            if (epilogue == H3_EPI_RESIDUAL &&
+                (overlap(mws, mat(resid, M_buf, N, ld_r)) ||
+                 overlap(mws, mat(gate, n_mod_groups, N, n_mod_groups > 1 ? ld_gate_group : N, 4))))
+                return H3_ERR_ALIAS;
+        }
     }
     return H3_OK;
 }

@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(_PKG, "libh3block.so")
 H3_OK, H3_ERR_NULL, H3_ERR_SHAPE, H3_ERR_UNSUPPORTED, H3_ERR_ALIGN, H3_ERR_ALIAS, \
     H3_ERR_WORKSPACE, H3_ERR_DEVICE, H3_ERR_HIP = range(9)
 H3_EPI_STORE, H3_EPI_RESIDUAL, H3_EPI_SWIGLU = range(3)
-H3_WS_H, H3_WS_QKV, H3_WS_O, H3_WS_X1, H3_WS_H2, H3_WS_G, H3_WS_VT = range(7)
-H3_WS_COUNT = 7
+H3_WS_H, H3_WS_QKV, H3_WS_O, H3_WS_X1, H3_WS_H2, H3_WS_G, H3_WS_VT, H3_WS_GEMM = range(8)
+H3_WS_COUNT = 8
 H3_MXWS_HQ, H3_MXWS_HS, H3_MXWS_QKV, H3_MXWS_O, H3_MXWS_OQ, H3_MXWS_OS, H3_MXWS_X1, H3_MXWS_H2Q, H3_MXWS_H2S, \
     H3_MXWS_GQ, H3_MXWS_GS, H3_MXWS_VT, H3_MXWS_BLOCKS, H3_MXWS_COUNTS, H3_MXWS_SELECT = range(15)
 H3_MXWS_COUNT = 15
@@ -103,8 +103,9 @@ def _load():
                                               I32, F32, I32, I32],
         "h3_swiglu_lora": [P, I64, P, I64, P, I64, I64, I64, I32, P],
         "h3_check_swiglu_lora": [P, I64, P, I64, P, I64, I64, I64, I32],
-        "h3_linear": [P, I64, P, I64, P, P, I64, I64, I64, I64, I64, I32, P, I64, P, I64, I32, P, P],
-        "h3_check_linear": [P, I64, P, I64, P, P, I64, I64, I64, I64, I64, I32, P, I64, P, I64, I32],
+        "h3_linear": [P, I64, P, I64, P, P, I64, I64, I64, I64, I64, I32, P, I64, P, I64, I32, P, P, SZ, P],
+        "h3_check_linear": [P, I64, P, I64, P, P, I64, I64, I64, I64, I64, I32, P, I64, P, I64, I32, P, SZ],
+        "h3_linear_workspace_bytes": [I64, I64, I64, I32],
         "h3_stack_forward": [C.POINTER(Dims), C.POINTER(BlockWeights), I32, P, P, I64, I32, P, P, I64, I64, P, SZ,
                              P],
         "h3_check_stack_forward": [C.POINTER(Dims), C.POINTER(BlockWeights), I32, P, P, I64, I32, P, P, I64, I64, P,
@@ -149,6 +150,7 @@ def _load():
         f.restype = C.c_int
     lib.h3_block_workspace_bytes.restype = C.c_size_t
     lib.h3_attention_workspace_bytes.restype = C.c_size_t
+    lib.h3_linear_workspace_bytes.restype = C.c_size_t
     lib.h3_sparse_select_workspace_bytes.restype = C.c_size_t
     lib.h3_block_sparse_workspace_bytes.restype = C.c_size_t
     lib.h3_block_mxfp8_workspace_bytes.restype = C.c_size_t
@@ -171,7 +173,7 @@ EXPORTS = ["h3_block_forward", "h3_attention", "h3_fused_modulate_norm", "h3_qk_
            "h3_check_linear_mxfp8", "h3_fused_modulate_norm_mxfp8", "h3_check_fused_modulate_norm_mxfp8",
            "h3_block_forward_mxfp8", "h3_check_block_forward_mxfp8", "h3_block_mxfp8_workspace_bytes",
            "h3_block_mxfp8_workspace_layout", "h3_stack_forward", "h3_check_stack_forward",
-           "h3_attention_noalloc"]
+           "h3_attention_noalloc", "h3_linear_workspace_bytes"]
 
 
 def status_string(s: int) -> str:
@@ -375,12 +377,19 @@ def swiglu_lora(u, du, g, valid_len, ffn, stream=None):
     _ok(s, "h3_swiglu_lora")
 
 
+def linear_workspace_bytes(M_valid: int, N: int, K: int, epilogue: int = H3_EPI_STORE) -> int:
+    return int(LIB.h3_linear_workspace_bytes(M_valid, N, K, epilogue))
+
+
 def linear(a, w, c, M_valid, epilogue=H3_EPI_STORE, bias=None, resid=None, gate=None, ld_gate_group=0,
-           n_mod_groups=1, mod_idx=None, stream=None):
+           n_mod_groups=1, mod_idx=None, workspace=None, stream=None):
+    """workspace: None (one workgroup per output tile) or a uint8 device tensor
+    of at least linear_workspace_bytes(...) bytes for the stream-K tail."""
     N, K = w.shape
     s = LIB.h3_linear(_ptr(a), a.stride(0), _ptr(w), w.stride(0), _ptr(bias), _ptr(c), c.stride(0), a.shape[0],
                       M_valid, N, K, epilogue, _ptr(resid), _ld(resid), _ptr(gate), ld_gate_group, n_mod_groups,
-                      _ptr(mod_idx), _stream(stream))
+                      _ptr(mod_idx), _ptr(workspace),
+                      0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
     _ok(s, "h3_linear")
 
 
