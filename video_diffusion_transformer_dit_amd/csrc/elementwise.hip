@@ -80,23 +80,33 @@ __device__ __forceinline__ void load_f8(const float *p, float f[8]) {
 // holds the chunks l + 64 (4 i + w) in v[w]. Either way the result is
 // (S_0 + S_1) + (S_2 + S_3), S_w the wave sum of the chunks with
 // (c / 64) % 4 == w, each lane adding its chunks in increasing order.
-template <int SPAN>
-__device__ __forceinline__ float row_sum(const float (&v)[4], float *red) {
-    if (SPAN == 64)
-        return (wave_sum(v[0]) + wave_sum(v[1])) + (wave_sum(v[2]) + wave_sum(v[3]));
-    const float w = wave_sum(v[0]);
+// The sums of ROWS rows at once (SPAN 256: one pair of barriers for all of
+// them; red holds 4 floats per row).
+template <int SPAN, int ROWS>
+__device__ __forceinline__ void row_sums(const float (&v)[ROWS][4], float *red, float (&out)[ROWS]) {
+    if (SPAN == 64) {
+#pragma unroll
+        for (int p = 0; p < ROWS; ++p)
+            out[p] = (wave_sum(v[p][0]) + wave_sum(v[p][1])) + (wave_sum(v[p][2]) + wave_sum(v[p][3]));
+        return;
+    }
+    float w[ROWS];
+#pragma unroll
+    for (int p = 0; p < ROWS; ++p) w[p] = wave_sum(v[p][0]);
     __syncthreads();  // red may still be read by a previous sum
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = w;
+    if ((threadIdx.x & 63) == 0)
+#pragma unroll
+        for (int p = 0; p < ROWS; ++p) red[4 * p + (threadIdx.x >> 6)] = w[p];
     __syncthreads();
-    return (red[0] + red[1]) + (red[2] + red[3]);
+#pragma unroll
+    for (int p = 0; p < ROWS; ++p) out[p] = (red[4 * p] + red[4 * p + 1]) + (red[4 * p + 2] + red[4 * p + 3]);
 }
 
 template <int NCH, int ROWS, bool BRANCH, int NORM, bool LORA = false, bool MX = false, int SPAN = 64>
 __global__ __launch_bounds__(256) void modnorm_kernel(ModnormArgs a) {
-    static_assert(SPAN == 64 || (SPAN == 256 && ROWS == 1), "a workgroup-wide row span owns one row");
-    __shared__ float red[4];
+    __shared__ float red[4 * ROWS];
     const int lane = SPAN == 64 ? (int)(threadIdx.x & 63) : (int)threadIdx.x;  // chunk lane within the row
-    const int64_t r0 = SPAN == 64 ? ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * ROWS : (int64_t)blockIdx.x;
+    const int64_t r0 = SPAN == 64 ? ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * ROWS : (int64_t)blockIdx.x * ROWS;
     if (r0 >= a.L_buf) return;  // uniform over the row's lanes
     const int nch = a.hidden >> 3;
 
@@ -131,13 +141,13 @@ __global__ __launch_bounds__(256) void modnorm_kernel(ModnormArgs a) {
             for (int p = 0; p < ROWS; ++p) {
                 if (!valid[p]) continue;
                 const int64_t r = r0 + p;
-                uint4 xw = *reinterpret_cast<const uint4 *>(a.x + r * a.ld_x + 8 * c);
+                uint4 xw = load_nt(a.x + r * a.ld_x + 8 * c);
                 if (BRANCH) {
                     if (grp[p] != gcur) {
                         load_f8(a.gate + (int64_t)grp[p] * a.ld_mod + 8 * c, gv);
                         gcur = grp[p];
                     }
-                    uint4 bw = *reinterpret_cast<const uint4 *>(a.branch + r * a.ld_b + 8 * c);
+                    uint4 bw = load_nt(a.branch + r * a.ld_b + 8 * c);
                     if (LORA) bw = lora_add8(bw, *reinterpret_cast<const uint4 *>(a.delta + r * a.ld_d + 8 * c));
                     float xf[8], bf[8];
                     unpack8(xw, xf);
@@ -152,7 +162,7 @@ __global__ __launch_bounds__(256) void modnorm_kernel(ModnormArgs a) {
                         for (int e = 0; e < 8; ++e) xf[e] = __builtin_fmaf(gv[e], bf[e], xf[e]);
                     }
                     xw = pack8(xf);
-                    *reinterpret_cast<uint4 *>(a.x1 + r * a.ld_x1 + 8 * c) = xw;
+                    store_nt(a.x1 + r * a.ld_x1 + 8 * c, xw);
                 }
                 xv[p][i] = xw;
                 float xf[8];
@@ -162,10 +172,11 @@ __global__ __launch_bounds__(256) void modnorm_kernel(ModnormArgs a) {
             }
         }
     }
-    float mean[ROWS], inv[ROWS];
+    float mean[ROWS], inv[ROWS], sums[ROWS];
+    row_sums<SPAN, ROWS>(acc, red, sums);
 #pragma unroll
     for (int p = 0; p < ROWS; ++p) {
-        const float s = row_sum<SPAN>(acc[p], red);
+        const float s = sums[p];
         mean[p] = NORM == 0 ? 0.f : s / (float)a.hidden;
         if (NORM == 0) inv[p] = rsqrtf(s / (float)a.hidden + a.eps);
     }
@@ -193,8 +204,9 @@ __global__ __launch_bounds__(256) void modnorm_kernel(ModnormArgs a) {
                 }
             }
         }
+        row_sums<SPAN, ROWS>(acc, red, sums);
 #pragma unroll
-        for (int p = 0; p < ROWS; ++p) inv[p] = rsqrtf(row_sum<SPAN>(acc[p], red) / (float)a.hidden + a.eps);
+        for (int p = 0; p < ROWS; ++p) inv[p] = rsqrtf(sums[p] / (float)a.hidden + a.eps);
     }
 
     // Pass 2: h = n * (1 + scale) + shift; padding rows are written as zero.
@@ -246,19 +258,19 @@ __global__ __launch_bounds__(256) void modnorm_kernel(ModnormArgs a) {
                         *reinterpret_cast<uint32_t *>(a.hs + ((int64_t)(c >> 4) * a.L_buf + r) * 4) =
                             code | (c1 << 8) | (c2 << 16) | (c3 << 24);
                 } else {
-                    *reinterpret_cast<uint4 *>(a.h + r * a.ld_h + 8 * c) = pack8(xf);
+                    store_nt(a.h + r * a.ld_h + 8 * c, pack8(xf));
                 }
             }
         }
     }
 }
 
-template <int NCH, int SPAN = 64>
+template <int NCH, int SPAN = 64, int WG_ROWS = 1>
 void modnorm_dispatch_nch(const ModnormArgs &a, bool branch, int norm, hipStream_t s, bool lora = false,
                           bool mx = false) {
-    constexpr int ROWS = SPAN == 64 ? 2 : 1;
+    constexpr int ROWS = SPAN == 64 ? 2 : WG_ROWS;
     const int64_t waves = (a.L_buf + ROWS - 1) / ROWS;
-    const dim3 grid((unsigned)(SPAN == 64 ? (waves + 3) / 4 : a.L_buf));
+    const dim3 grid((unsigned)(SPAN == 64 ? (waves + 3) / 4 : (a.L_buf + ROWS - 1) / ROWS));
     if (mx) {
         if (branch) {
             if (norm == 0) modnorm_kernel<NCH, ROWS, true, 0, false, true, SPAN><<<grid, 256, 0, s>>>(a);
@@ -280,7 +292,11 @@ void modnorm_dispatch_nch(const ModnormArgs &a, bool branch, int norm, hipStream
 }
 
 // Plain modulate-norm rows of 2,048 channels or more take a workgroup each
-// (SPAN 256: 0.35 -> 0.29 ms at 58,758 x 5,376); with the residual branch,
+// (SPAN 256: 0.35 -> 0.29 ms at 58,758 x 5,376), two rows per workgroup for
+// rows of 513-768 chunks (one pair of reductions and one read of the modulation
+// vectors for both rows, loads of both in flight at once: 0.30 -> 0.26 ms,
+// 0.24 ms with non-temporal loads and stores; four rows were slower);
+// with the residual branch,
 // which moves twice the bytes per row, two rows per wavefront (SPAN 64) stay
 // faster (0.51 vs 0.58 ms), as do narrow rows. NCH covers the row's chunks.
 void modnorm_dispatch(const ModnormArgs &a, bool branch, int norm, hipStream_t s, bool lora, bool mx) {
@@ -289,7 +305,7 @@ void modnorm_dispatch(const ModnormArgs &a, bool branch, int norm, hipStream_t s
         const int need = (nch + 255) / 256;
         if (need <= 1) modnorm_dispatch_nch<1, 256>(a, branch, norm, s, lora, mx);
         else if (need <= 2) modnorm_dispatch_nch<2, 256>(a, branch, norm, s, lora, mx);
-        else if (need <= 3) modnorm_dispatch_nch<3, 256>(a, branch, norm, s, lora, mx);
+        else if (need <= 3) modnorm_dispatch_nch<3, 256, 2>(a, branch, norm, s, lora, mx);
         else if (need <= 4) modnorm_dispatch_nch<4, 256>(a, branch, norm, s, lora, mx);
         else modnorm_dispatch_nch<8, 256>(a, branch, norm, s, lora, mx);
     } else {
@@ -381,7 +397,7 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkArgs a) {
         float f[8];
         if (act) {
             ptr = (is_k ? a.k + (int64_t)(hv - a.heads) * 128 : a.q + (int64_t)hv * 128) + r * a.ld + 8 * c;
-            uint4 raw = *reinterpret_cast<const uint4 *>(ptr);
+            uint4 raw = load_nt(ptr);
             if (LORA) {
                 const uint16_t *dp =
                     (is_k ? a.dk + (int64_t)(hv - a.heads) * 128 : a.dq + (int64_t)hv * 128) + r * a.ld_d + 8 * c;
@@ -424,7 +440,7 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkArgs a) {
                 }
             }
         }
-        if (act) *reinterpret_cast<uint4 *>(ptr) = pack8(f);
+        if (act) store_nt(ptr, pack8(f));
     }
 }
 
@@ -447,7 +463,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t *u, int64_t 
         return;
     }
     const uint16_t *src = u + (int64_t)row * ld_u + c;
-    uint4 ua = *reinterpret_cast<const uint4 *>(src), ub = *reinterpret_cast<const uint4 *>(src + ffn);
+    uint4 ua = load_nt(src), ub = load_nt(src + ffn);
     if (LORA) {
         const uint16_t *dsrc = du + (int64_t)row * ld_du + c;
         ua = lora_add8(ua, *reinterpret_cast<const uint4 *>(dsrc));
@@ -458,7 +474,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t *u, int64_t 
     unpack8(ub, b);
 #pragma unroll
     for (int e = 0; e < 8; ++e) a[e] = a[e] / (1.0f + __expf(-a[e])) * b[e];
-    *reinterpret_cast<uint4 *>(dst) = pack8(a);
+    store_nt(dst, pack8(a));
 }
 
 __global__ __launch_bounds__(256) void zero_rows_kernel(uint16_t *p, int64_t ld, int32_t chunks, int64_t r0,

@@ -116,6 +116,18 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
     return (uint32_t)v;
 }
 
+// 16-byte global load / store with the non-temporal hint, for data a kernel
+// streams once (measured on the modulate-norm pass: 4.9 -> 5.2 TB/s).
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt(const void *p) {
+    const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_nt(void *p, const uint4 &v) {
+    const u32x4_nt w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_nt *>(p));
+}
+
 // BF16 bit pattern -> float (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
