@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define H3_ABI_VERSION 5
+#define H3_ABI_VERSION 6
 #define H3_MAX_SEGMENTS 4   /* K/V segments per query group */
 #define H3_MAX_GROUPS 8     /* query groups per attention call */
 #define H3_SPARSE_Q_BLOCK 256      /* block-sparse attention: target query block rows */
@@ -99,13 +99,20 @@ typedef struct {
  * k == NULL selects rows [begin, begin+len) of the call's own K/V; otherwise
  * rows [begin, begin+len) of k and v, each [rows, heads*head_dim] with row
  * stride ld. Attention is non-causal; a group's keys are the concatenation of
- * its segments in order. */
+ * its segments in order.
+ * vt, kmax2: NULL, or (external segments only) the segment's V and key norms
+ * already staged by h3_kv_stage over exactly these rows ([SolarWM] stage 3:
+ * the history is prepared once at the KV refresh and reused by the chunk's
+ * forwards); attention then reads them instead of staging V again. Both or
+ * neither; the caller keeps them consistent with k and v. */
 typedef struct {
     const uint16_t *k;
     const uint16_t *v;
     int64_t ld;
     int64_t begin;
     int64_t len;
+    const uint16_t *vt;   /* [heads][128][round_up(len, 64)] BF16, 16-byte aligned */
+    const float *kmax2;   /* [heads], 4-byte aligned */
 } h3_kv_seg;
 
 /* A query group: rows [q_begin, q_end) attend over n_seg segments. Groups must
@@ -245,6 +252,24 @@ int h3_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_
  * valid rows), heads * 128 * round_up(len, 64) BF16 values. 0 on bad input. */
 size_t h3_attention_workspace_bytes(int64_t valid_len, int32_t heads,
                                     const h3_qgroup *groups, int32_t n_groups);
+
+/* ---------------------------------------------------------------------------
+ * h3_kv_stage - prepare an external K/V segment once for the attention calls
+ * that will read it ([SolarWM] stage 3: the KV refresh prepares the history
+ * K/V for the following chunk's forwards): rows [0, len) of k and v
+ * ([len, heads*128] at row stride ld) give
+ *   vt     [heads][128][round_up(len, 64)] BF16: V transposed per head, keys
+ *          permuted inside each 16-key group and zero past len, exactly as
+ *          attention stages V itself (h3_kv_stage_bytes(len, heads) bytes);
+ *   kmax2  [heads] FP32: the largest squared norm of a key row per head.
+ * Pass them in an h3_kv_seg (with k + begin * ld ... as that segment's rows)
+ * as vt and kmax2. vt and kmax2 must not overlap k, v or each other.
+ * ------------------------------------------------------------------------- */
+int h3_kv_stage(const uint16_t *k, const uint16_t *v, int64_t ld, int64_t len, int32_t heads, int32_t head_dim,
+                uint16_t *vt, float *kmax2, void *stream);
+size_t h3_kv_stage_bytes(int64_t len, int32_t heads);
+int h3_check_kv_stage(const uint16_t *k, const uint16_t *v, int64_t ld, int64_t len, int32_t heads,
+                      int32_t head_dim, const uint16_t *vt, const float *kmax2);
 
 /* ---------------------------------------------------------------------------
  * h3_attention_noalloc - h3_attention for callers that cannot allocate device

@@ -192,10 +192,21 @@ def test_block_validator_groups():
     # external history segment inside the workspace is rejected
     arr = (h3.QGroup * 1)()
     arr[0].q_begin, arr[0].q_end, arr[0].n_seg = 0, 10, 1
-    arr[0].seg[0] = h3.KvSeg(addr(10), addr(10) + 1 * MB, 256, 0, 100)
+    arr[0].seg[0] = h3.KvSeg(addr(10), addr(10) + 1 * MB, 256, 0, 100, None, None)
     assert check_block(*_block_args(groups=arr, n_groups=1)) == h3.H3_ERR_ALIAS
-    arr[0].seg[0] = h3.KvSeg(addr(20), addr(21), 256, 0, 100)
+    arr[0].seg[0] = h3.KvSeg(addr(20), addr(21), 256, 0, 100, None, None)
     assert check_block(*_block_args(groups=arr, n_groups=1)) == h3.H3_OK
+    # a staged segment: V^T plane and key norms both or neither, aligned, outside y and the workspace
+    arr[0].seg[0] = h3.KvSeg(addr(20), addr(21), 256, 0, 100, addr(24), addr(25))
+    assert check_block(*_block_args(groups=arr, n_groups=1)) == h3.H3_OK
+    arr[0].seg[0] = h3.KvSeg(addr(20), addr(21), 256, 0, 100, addr(24), None)
+    assert check_block(*_block_args(groups=arr, n_groups=1)) == h3.H3_ERR_NULL
+    arr[0].seg[0] = h3.KvSeg(addr(20), addr(21), 256, 0, 100, addr(24) + 8, addr(25))
+    assert check_block(*_block_args(groups=arr, n_groups=1)) == h3.H3_ERR_ALIGN
+    arr[0].seg[0] = h3.KvSeg(addr(20), addr(21), 256, 0, 100, addr(10), addr(25))
+    assert check_block(*_block_args(groups=arr, n_groups=1)) == h3.H3_ERR_ALIAS
+    arr[0].seg[0] = h3.KvSeg(None, None, 0, 0, 100, addr(24), addr(25))   # own rows are never pre-staged
+    assert check_block(*_block_args(groups=arr, n_groups=1)) == h3.H3_ERR_UNSUPPORTED
     # KV export range and aliasing
     e = h3.KvExport(addr(22), addr(23), 256, 400, 100)
     assert check_block(*_block_args(exp=C.byref(e))) == h3.H3_OK
@@ -232,6 +243,25 @@ def test_attention_validator():
     assert h3.LIB.h3_check_attention(q, 3 * H + 4, k, 3 * H, v, 3 * H, o, H, L, 500, 2, 128, 0.0, None,
                                      0, ws, need) == h3.H3_ERR_ALIGN
     assert h3.LIB.h3_check_attention(q, 3 * H, k, 3 * H, v, 3 * H, o, H, 0, 0, 2, 128, 0.0, None, 0, None, 0) == h3.H3_OK
+
+
+def test_kv_stage_validator_and_sizes():
+    """h3_kv_stage: a V^T plane of heads x 128 x round_up(len, 64) BF16 and
+    one FP32 per head, neither overlapping k, v or each other."""
+    lib = h3.LIB
+    H = 42 * 128
+    k, v, vt, km = addr(1), addr(4), addr(7), addr(12)   # 15,120 rows of K or V span 163 MB
+    assert h3.kv_stage_bytes(15120, 42) == 42 * 128 * 15168 * 2
+    assert h3.kv_stage_bytes(64, 2) == 2 * 128 * 64 * 2
+    assert lib.h3_check_kv_stage(k, v, H, 15120, 42, 128, vt, km) == h3.H3_OK
+    assert lib.h3_check_kv_stage(k, v, H, 15120, 42, 64, vt, km) == h3.H3_ERR_UNSUPPORTED
+    assert lib.h3_check_kv_stage(k, v, H, 15120, 42, 128, None, km) == h3.H3_ERR_NULL
+    assert lib.h3_check_kv_stage(k, v, H, 15120, 42, 128, vt + 2, km) == h3.H3_ERR_ALIGN
+    assert lib.h3_check_kv_stage(k, v, H, 15120, 42, 128, vt, km + 2) == h3.H3_ERR_ALIGN
+    assert lib.h3_check_kv_stage(k, v, H + 4, 15120, 42, 128, vt, km) == h3.H3_ERR_ALIGN
+    assert lib.h3_check_kv_stage(k, v, H, 15120, 42, 128, k + 1024, km) == h3.H3_ERR_ALIAS
+    assert lib.h3_check_kv_stage(k, v, H, 15120, 42, 128, vt, vt + 1024) == h3.H3_ERR_ALIAS
+    assert lib.h3_check_kv_stage(k, v, H, 0, 42, 128, None, None) == h3.H3_OK
 
 
 def test_noalloc_attention_rejects_on_the_host():

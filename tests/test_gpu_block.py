@@ -234,6 +234,10 @@ def test_block_streaming_full_width_sampled_rows():
     groups = [(0, cond, [cur]), (cond, cond + audio, [cur]), (cond + audio, L, [(tk, tv, 0, hist), cur])]
     pos = (np.arange(L) + hist).astype(np.int32)
     y_denoise = bits(b.run(xb, groups=groups, pos=dev_i32(pos)))
+    # the history staged once (h3_kv_stage) and read in place: the same bits
+    staged = h3.kv_stage(tk, tv, s.heads)
+    groups_st = [(0, cond, [cur]), (cond, cond + audio, [cur]), (cond + audio, L, [(tk, tv, 0, hist, staged), cur])]
+    np.testing.assert_array_equal(bits(b.run(xb, groups=groups_st, pos=dev_i32(pos))), y_denoise)
     ek = poison((video, s.hidden))
     ev = poison((video, s.hidden))
     y = b.run(xb, groups=groups, pos=dev_i32(pos), kv_export=(ek, ev, cond + audio, video))

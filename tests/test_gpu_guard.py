@@ -233,6 +233,20 @@ def test_guard_attention(grouped):
     o.check("attention_noalloc o")
 
 
+def test_guard_kv_stage():
+    heads, Lh = 3, 700
+    H = heads * 128
+    _say(f"guard kv_stage heads={heads} rows={Lh}")
+    hk = dev_bf16(I.normal_bf16("gks.k", (Lh, H)))
+    hv = dev_bf16(I.normal_bf16("gks.v", (Lh, H)))
+    vt = Guard(1, h3.kv_stage_bytes(Lh, heads) // 2)
+    km = Guard(1, heads, None, torch.float32)
+    h3.kv_stage(hk, hv, heads, vt=vt.view, kmax2=km.view)
+    torch.cuda.synchronize()
+    vt.check("kv_stage V^T")
+    km.check("kv_stage key norms")
+
+
 def test_guard_sparse_select_and_attention():
     heads, L, V, P = 2, 1300, 1250, 100
     H = heads * 128

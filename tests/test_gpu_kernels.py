@@ -471,3 +471,41 @@ def test_attention_grouped_with_history():
     for (a, b) in ((100, 150), (560, 570)):
         assert np.all(bits(o[a:b]) == 0), f"rows {a}:{b} outside every group must be zero"
     assert_zero_rows(o, V, "o")
+    # the same history segments staged once by h3_kv_stage and read in place:
+    # the same V^T planes and key norm maxima, so the same bits
+    st = {(b, n): h3.kv_stage(tk[b:b + n], tv[b:b + n], heads) for (b, n) in ((20, 280), (0, 1), (299, 1))}
+    groups_st = [(a, e, [(x[0], x[1], x[2], x[3], st[(x[2], x[3])]) if not isinstance(x[0], str) else x
+                          for x in segs]) for (a, e, segs) in groups]
+    o2 = poison((L, H))
+    h3.attention(q, k, v, o2, V, heads, groups=groups_st)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(o2), bits(o))
+
+
+@pytest.mark.parametrize("q_scale", [1.0, 8.0])
+def test_kv_stage_matches_attention_staging(q_scale):
+    """h3_kv_stage's V^T plane and key norms equal what attention stages
+    itself: a group reading only a staged external segment (longer than a
+    K/V tile, ragged) gives the same bits as the unstaged call, on the fixed
+    and the online softmax form, and matches the oracle."""
+    heads, L, Lh = 3, 300, 777
+    H = heads * 128
+    qb = I.normal_bf16("kst.q", (L, H), q_scale)
+    hk = I.normal_bf16("kst.hk", (Lh, H))
+    hv = I.normal_bf16("kst.hv", (Lh, H))
+    q, tk, tv = dev_bf16(qb), dev_bf16(hk), dev_bf16(hv)
+    dummy = torch.zeros((L, H), dtype=torch.bfloat16, device="cuda")
+    vt, km = h3.kv_stage(tk[5:705], tv[5:705], heads)
+    torch.cuda.synchronize()
+    # the key norm maxima: the largest squared norm of the BF16 key rows, per head
+    kk = O.bf16_to_f64(hk[5:705]).reshape(700, heads, 128)
+    np.testing.assert_allclose(km.cpu().numpy(), (kk ** 2).sum(-1).max(0), rtol=1e-5)
+    outs = []
+    for seg in ((tk, tv, 5, 700), (tk, tv, 5, 700, (vt, km))):
+        o = poison((L, H))
+        h3.attention(q, dummy, dummy, o, L, heads, groups=[(0, L, [seg])])
+        torch.cuda.synchronize()
+        outs.append(bits(o))
+    np.testing.assert_array_equal(outs[1], outs[0])
+    ref = O.attention(O.bf16_to_f64(qb), O.bf16_to_f64(hk[5:705]), O.bf16_to_f64(hv[5:705]), heads, 128)
+    assert_parity(I.bf16_bits_to_f32(outs[1]).astype(np.float64), ref, "o (staged history)")

@@ -864,12 +864,29 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float *part, int3
 
 // Transposed V of every segment of the plan into the workspace, and the
 // largest squared key norm per head over all segments.
+__global__ __launch_bounds__(64) void zero_u32_kernel(uint32_t *p, int32_t n) {
+    const int i = blockIdx.x * 64 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// Per-head maxima of a segment staged by h3_kv_stage merged into the call's.
+__global__ __launch_bounds__(64) void kmax_merge_kernel(uint32_t *kmax2, const float *seg_kmax2, int32_t heads) {
+    const int h = blockIdx.x * 64 + threadIdx.x;
+    if (h < heads) atomicMax(kmax2 + h, __float_as_uint(seg_kmax2[h]));
+}
+
 void stage_vt(const VtPlan &plan, const uint16_t *k, int64_t ld_k, const uint16_t *v, int64_t ld_v, int32_t heads,
-              uint8_t *ws, hipStream_t stream) {
-    if (plan.n == 0) return;
+              uint8_t *ws, hipStream_t stream, const h3_qgroup *groups = nullptr, int32_t n_groups = 0) {
+    if (plan.bytes == 0) return;
     uint32_t *kmax2 = reinterpret_cast<uint32_t *>(ws + plan.kmax_off);
     const int64_t kcols = (int64_t)(plan.bytes - plan.kmax_off) / 2;  // the 256-byte aligned area, as BF16 slots
     launch_zero_rows(reinterpret_cast<uint16_t *>(kmax2), kcols, kcols, 0, 1, stream);
+    for (int gi = 0; gi < n_groups; ++gi)
+        for (int s = 0; s < groups[gi].n_seg; ++s) {
+            const h3_kv_seg &x = groups[gi].seg[s];
+            if (x.k != nullptr && x.vt != nullptr)
+                kmax_merge_kernel<<<dim3((unsigned)((heads + 63) / 64)), 64, 0, stream>>>(kmax2, x.kmax2, heads);
+        }
     for (int i = 0; i < plan.n; ++i) {
         const VtSeg &e = plan.seg[i];
         const uint16_t *ks = e.own ? k + e.begin * ld_k : e.k + e.begin * e.ld;
@@ -899,7 +916,7 @@ void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_
         dense.q_begin = 0;
         dense.q_end = valid_len;
         dense.n_seg = 1;
-        dense.seg[0] = h3_kv_seg{nullptr, nullptr, 0, 0, valid_len};
+        dense.seg[0] = h3_kv_seg{nullptr, nullptr, 0, 0, valid_len, nullptr, nullptr};
         groups = &dense;
         n_groups = valid_len > 0 ? 1 : 0;
     }
@@ -907,7 +924,7 @@ void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_
     VtPlan plan;
     vt_plan(is_dense ? nullptr : groups, is_dense ? 0 : n_groups, valid_len, heads, &plan);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    stage_vt(plan, k, ld_k, v, ld_v, heads, ws, stream);
+    stage_vt(plan, k, ld_k, v, ld_v, heads, ws, stream, is_dense ? nullptr : groups, is_dense ? 0 : n_groups);
     std::pair<int64_t, int64_t> cov[H3_MAX_GROUPS];
     int nc = 0;
     for (int gi = 0; gi < n_groups; ++gi)
@@ -935,6 +952,14 @@ void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_
         G.n_seg = g.n_seg;
         for (int s = 0; s < g.n_seg; ++s) {
             const h3_kv_seg &ss = g.seg[s];
+            if (ss.k != nullptr && ss.vt != nullptr) {  // staged by h3_kv_stage
+                G.sk[s] = ss.k + ss.begin * ss.ld;
+                G.sldk[s] = ss.ld;
+                G.svt[s] = ss.vt;
+                G.slpad[s] = (ss.len + 63) / 64 * 64;
+                G.slen[s] = ss.len;
+                continue;
+            }
             const VtSeg &e = plan.seg[plan.map[gi][s]];
             if (ss.k == nullptr) {
                 G.sk[s] = k + ss.begin * ld_k;
@@ -998,6 +1023,23 @@ extern "C" int h3_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, 
     if ((s = device_check()) != H3_OK) return s;
     launch_attention(q, ld_q, k, ld_k, v, ld_v, o, ld_o, L_buf, valid_len, heads, softmax_scale, groups, n_groups,
                      workspace, (hipStream_t)stream);
+    return launch_status();
+}
+
+// SolarWM H3 Realtime, stage 3: an external K/V segment staged once (V^T plane
+// and per-head key norm maxima, the same kernels attention stages with) for
+// the attention calls that read it.
+extern "C" int h3_kv_stage(const uint16_t *k, const uint16_t *v, int64_t ld, int64_t len, int32_t heads,
+                           int32_t head_dim, uint16_t *vt, float *kmax2, void *stream) {
+    int s = h3_check_kv_stage(k, v, ld, len, heads, head_dim, vt, kmax2);
+    if (s != H3_OK || len == 0) return s;
+    if ((s = device_check()) != H3_OK) return s;
+    const hipStream_t st = (hipStream_t)stream;
+    const int64_t lpad = (len + 63) / 64 * 64;
+    uint32_t *km = reinterpret_cast<uint32_t *>(kmax2);
+    zero_u32_kernel<<<dim3((unsigned)((heads + 63) / 64)), 64, 0, st>>>(km, heads);
+    key_norm_max_kernel<<<dim3((unsigned)((len + kNormRows - 1) / kNormRows)), 256, 0, st>>>(k, ld, len, heads, km);
+    vt_transpose_kernel<<<dim3((unsigned)(lpad / BKV), (unsigned)heads), 256, 0, st>>>(v, ld, len, vt, lpad);
     return launch_status();
 }
 

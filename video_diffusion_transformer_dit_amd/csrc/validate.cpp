@@ -112,8 +112,8 @@ void sparse_vt_group(int64_t valid_len, int64_t prefix_len, h3_qgroup *g) {
     g->q_begin = 0;
     g->q_end = valid_len;
     g->n_seg = 2;
-    g->seg[0] = h3_kv_seg{nullptr, nullptr, 0, 0, prefix_len};
-    g->seg[1] = h3_kv_seg{nullptr, nullptr, 0, prefix_len, valid_len - prefix_len};
+    g->seg[0] = h3_kv_seg{nullptr, nullptr, 0, 0, prefix_len, nullptr, nullptr};
+    g->seg[1] = h3_kv_seg{nullptr, nullptr, 0, prefix_len, valid_len - prefix_len, nullptr, nullptr};
 }
 
 void attn_schedule(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads, AttnSchedule *out) {
@@ -230,6 +230,7 @@ void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads
     };
     int64_t qtiles = 0;  // 256-row query tiles over all groups
     int n_launch_groups = 1;
+    bool staged = false;  // a segment staged by h3_kv_stage (no plane here)
     if (groups == nullptr) {
         if (dense_len > 0) out->map[0][0] = add(1, nullptr, nullptr, 0, 0, dense_len);
         qtiles = (dense_len + 255) / 256;
@@ -239,6 +240,11 @@ void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads
             qtiles += (std::max<int64_t>(groups[g].q_end - groups[g].q_begin, 0) + 255) / 256;
             for (int s = 0; s < groups[g].n_seg && s < H3_MAX_SEGMENTS; ++s) {
                 const h3_kv_seg &x = groups[g].seg[s];
+                if (x.k != nullptr && x.vt != nullptr) {
+                    out->map[g][s] = -1;  // staged by h3_kv_stage: read in place
+                    staged = true;
+                    continue;
+                }
                 out->map[g][s] = x.k == nullptr ? add(1, nullptr, nullptr, 0, x.begin, x.len)
                                                 : add(0, x.k, x.v, x.ld, x.begin, x.len);
             }
@@ -246,7 +252,7 @@ void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads
     }
     out->flags_off = 0;
     out->part_off = 0;
-    if (out->n > 0) {
+    if (out->n > 0 || staged) {
         auto align = [](size_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; };
         // Partial results of the items cut into pieces: a partial round has
         // fewer than 256 items, each cut into at most ceil(256 / items)
@@ -661,6 +667,42 @@ int h3_check_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t l
     return H3_OK;
 }
 
+// The staged V^T plane and key norms of an external segment (h3_kv_stage).
+static int check_staged_seg(const h3_kv_seg &s, int64_t heads, std::vector<Mat> &planes) {
+    if ((s.vt == nullptr) != (s.kmax2 == nullptr)) return H3_ERR_NULL;
+    if (s.vt == nullptr) return H3_OK;
+    if (s.k == nullptr) return H3_ERR_UNSUPPORTED;  // own rows are staged by the call itself
+    if (!aligned16(s.vt) || (reinterpret_cast<uintptr_t>(s.kmax2) & 3u)) return H3_ERR_ALIGN;
+    const int64_t bytes = heads * kHeadDim * ((s.len + 63) / 64 * 64) * 2;
+    planes.push_back(mat(s.vt, 1, bytes, bytes, 1));
+    planes.push_back(mat(s.kmax2, 1, heads, heads, 4));
+    return H3_OK;
+}
+
+size_t h3_kv_stage_bytes(int64_t len, int32_t heads) {
+    if (len < 0 || heads <= 0) return 0;
+    return (size_t)heads * kHeadDim * ((len + 63) / 64 * 64) * 2;
+}
+
+int h3_check_kv_stage(const uint16_t *k, const uint16_t *v, int64_t ld, int64_t len, int32_t heads,
+                      int32_t head_dim, const uint16_t *vt, const float *kmax2) {
+    if (heads <= 0 || len < 0) return H3_ERR_SHAPE;
+    if (head_dim != kHeadDim) return H3_ERR_UNSUPPORTED;
+    if ((int64_t)heads * head_dim > kMaxHidden) return H3_ERR_SHAPE;
+    if (len == 0) return H3_OK;
+    if (!k || !v || !vt || !kmax2) return H3_ERR_NULL;
+    const int64_t H = (int64_t)heads * head_dim;
+    H3_TRY(check_bf16_mat(k, ld, H));
+    H3_TRY(check_bf16_mat(v, ld, H));
+    if (!aligned16(vt) || (reinterpret_cast<uintptr_t>(kmax2) & 3u)) return H3_ERR_ALIGN;
+    const int64_t bytes = (int64_t)h3_kv_stage_bytes(len, heads);
+    const Mat mvt = mat(vt, 1, bytes, bytes, 1), mk2 = mat(kmax2, 1, heads, heads, 4);
+    const Mat mk = mat(k, len, H, ld), mv = mat(v, len, H, ld);
+    if (overlap(mvt, mk) || overlap(mvt, mv) || overlap(mk2, mk) || overlap(mk2, mv) || overlap(mvt, mk2))
+        return H3_ERR_ALIAS;
+    return H3_OK;
+}
+
 int h3_check_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_k,
                        const uint16_t *v, int64_t ld_v, const uint16_t *o, int64_t ld_o, int64_t L_buf,
                        int64_t valid_len, int32_t heads, int32_t head_dim, float softmax_scale,
@@ -703,6 +745,13 @@ int h3_check_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64
                     const Mat sk = mat(s.k + s.begin * s.ld, s.len, H, s.ld);
                     const Mat sv = mat(s.v + s.begin * s.ld, s.len, H, s.ld);
                     if (overlap(mo, sk) || overlap(mo, sv)) return H3_ERR_ALIAS;
+                }
+                std::vector<Mat> staged;
+                H3_TRY(check_staged_seg(s, heads, staged));
+                for (const Mat &m : staged) {
+                    if (overlap(m, mo)) return H3_ERR_ALIAS;
+                    if (workspace != nullptr && overlap(m, mat(workspace, 1, (int64_t)ws_bytes, (int64_t)ws_bytes, 1)))
+                        return H3_ERR_ALIAS;
                 }
             }
         }
@@ -794,6 +843,10 @@ int h3_check_block_forward(const h3_dims *dims, const h3_block_weights *w, const
                     if (overlap(my, sk) || overlap(my, sv) || overlap(mws, sk) || overlap(mws, sv))
                         return H3_ERR_ALIAS;
                 }
+                std::vector<Mat> staged;
+                H3_TRY(check_staged_seg(s, dims->heads, staged));
+                for (const Mat &m : staged)
+                    if (overlap(m, my) || overlap(m, mws)) return H3_ERR_ALIAS;
             }
         }
         std::sort(spans.begin(), spans.end());

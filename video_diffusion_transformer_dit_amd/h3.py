@@ -52,7 +52,7 @@ class BlockWeightsMx(C.Structure):
 
 class KvSeg(C.Structure):
     _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("ld", C.c_int64), ("begin", C.c_int64),
-                ("len", C.c_int64)]
+                ("len", C.c_int64), ("vt", C.c_void_p), ("kmax2", C.c_void_p)]
 
 
 class QGroup(C.Structure):
@@ -86,6 +86,9 @@ def _load():
         "h3_check_attention": [P, I64, P, I64, P, I64, P, I64, I64, I64, I32, I32, F32, C.POINTER(QGroup), I32,
                                P, SZ],
         "h3_attention_workspace_bytes": [I64, I32, C.POINTER(QGroup), I32],
+        "h3_kv_stage": [P, P, I64, I64, I32, I32, P, P, P],
+        "h3_check_kv_stage": [P, P, I64, I64, I32, I32, P, P],
+        "h3_kv_stage_bytes": [I64, I32],
         "h3_attention_noalloc": [P, I64, P, I64, P, I64, P, I64, I64, I64, I32, I32, F32, C.POINTER(QGroup), I32,
                                  P],
         "h3_fused_modulate_norm": [P, I64, P, I64, P, P, P, I64, I32, P, P, I64, P, I64, I64, I64, I32, F32, I32, P],
@@ -151,6 +154,7 @@ def _load():
     lib.h3_block_workspace_bytes.restype = C.c_size_t
     lib.h3_attention_workspace_bytes.restype = C.c_size_t
     lib.h3_linear_workspace_bytes.restype = C.c_size_t
+    lib.h3_kv_stage_bytes.restype = C.c_size_t
     lib.h3_sparse_select_workspace_bytes.restype = C.c_size_t
     lib.h3_block_sparse_workspace_bytes.restype = C.c_size_t
     lib.h3_block_mxfp8_workspace_bytes.restype = C.c_size_t
@@ -173,7 +177,8 @@ EXPORTS = ["h3_block_forward", "h3_attention", "h3_fused_modulate_norm", "h3_qk_
            "h3_check_linear_mxfp8", "h3_fused_modulate_norm_mxfp8", "h3_check_fused_modulate_norm_mxfp8",
            "h3_block_forward_mxfp8", "h3_check_block_forward_mxfp8", "h3_block_mxfp8_workspace_bytes",
            "h3_block_mxfp8_workspace_layout", "h3_stack_forward", "h3_check_stack_forward",
-           "h3_attention_noalloc", "h3_linear_workspace_bytes"]
+           "h3_attention_noalloc", "h3_linear_workspace_bytes", "h3_kv_stage", "h3_check_kv_stage",
+           "h3_kv_stage_bytes"]
 
 
 def status_string(s: int) -> str:
@@ -219,7 +224,9 @@ def make_weights(w: dict) -> BlockWeights:
 
 def make_groups(groups):
     """groups: list of (q_begin, q_end, segs) with segs a list of
-    ('self', begin, len) or (k_tensor, v_tensor, begin, len)."""
+    ('self', begin, len), (k_tensor, v_tensor, begin, len), or
+    (k_tensor, v_tensor, begin, len, (vt, kmax2)) for a segment whose rows
+    [begin, begin+len) were staged by kv_stage."""
     if groups is None:
         return None, 0
     arr = (QGroup * len(groups))()
@@ -227,10 +234,11 @@ def make_groups(groups):
         arr[i].q_begin, arr[i].q_end, arr[i].n_seg = qb, qe, len(segs)
         for j, s in enumerate(segs):
             if isinstance(s[0], str):
-                arr[i].seg[j] = KvSeg(None, None, 0, s[1], s[2])
+                arr[i].seg[j] = KvSeg(None, None, 0, s[1], s[2], None, None)
             else:
-                k, v, b, ln = s
-                arr[i].seg[j] = KvSeg(_ptr(k), _ptr(v), k.stride(0), b, ln)
+                k, v, b, ln = s[:4]
+                vt, km = s[4] if len(s) > 4 else (None, None)
+                arr[i].seg[j] = KvSeg(_ptr(k), _ptr(v), k.stride(0), b, ln, _ptr(vt), _ptr(km))
     return arr, len(groups)
 
 
@@ -317,6 +325,25 @@ def attention(q, k, v, o, valid_len, heads, softmax_scale=0.0, groups=None, work
                          q.shape[0], valid_len, heads, 128, softmax_scale, garr, ng, _ptr(workspace),
                          workspace.numel() * workspace.element_size(), _stream(stream))
     _ok(s, "h3_attention")
+
+
+def kv_stage_bytes(length: int, heads: int) -> int:
+    return int(LIB.h3_kv_stage_bytes(length, heads))
+
+
+def kv_stage(k, v, heads, vt=None, kmax2=None, stream=None):
+    """Stage rows [0, k.shape[0]) of an external K/V segment once: returns
+    (vt, kmax2) device tensors (allocated here unless given) to pass as a
+    segment's staged form."""
+    import torch
+    n = k.shape[0]
+    if vt is None:
+        vt = torch.empty(max(kv_stage_bytes(n, heads), 16) // 2, dtype=torch.bfloat16, device=k.device)
+    if kmax2 is None:
+        kmax2 = torch.empty(heads, dtype=torch.float32, device=k.device)
+    s = LIB.h3_kv_stage(_ptr(k), _ptr(v), k.stride(0), n, heads, 128, _ptr(vt), _ptr(kmax2), _stream(stream))
+    _ok(s, "h3_kv_stage")
+    return vt, kmax2
 
 
 def attention_noalloc(q, k, v, o, valid_len, heads, softmax_scale=0.0, groups=None, stream=None):
