@@ -755,45 +755,51 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
 
 // Largest squared key norm per head over rows [0, rows) of k, merged into
 // kmax2[head] (non-negative FP32 bit patterns compare like unsigned integers,
-// so an integer atomic maximum merges them). A workgroup owns 64 whole rows;
-// thread t takes the 16-byte chunks t, t + 256, ... of every row, so the
-// loads are coalesced across all heads, and the 16 chunks of one head are 16
-// consecutive lanes. One atomic per head and workgroup.
-constexpr int kNormRows = 64;
+// so an integer atomic maximum merges them). Workgroup (x, y) owns the rows
+// [x per, (x + 1) per) of heads [8 y, 8 y + 8): 128 chunks of 16 bytes per
+// row. Thread t takes chunk t & 127 of the rows of parity t >> 7, 8 rows in
+// flight; the 16 chunks of one head are 16 consecutive lanes. `per`
+// (norm_rows_per_wg) keeps the row blocks at about 128 or fewer, so each
+// head's maximum takes at most about 256 atomics.
+constexpr int kNormHeads = 8;
+int norm_rows_per_wg(int64_t rows) {
+    const int64_t r = ((rows + 127) / 128 + 15) / 16 * 16;
+    return (int)std::min<int64_t>(std::max<int64_t>(r, 64), 512);
+}
 __global__ __launch_bounds__(256) void key_norm_max_kernel(const uint16_t *k, int64_t ld, int64_t rows, int32_t heads,
-                                                           uint32_t *kmax2) {
+                                                           int32_t per, uint32_t *kmax2) {
     const int t = threadIdx.x;
-    const int nch = heads * 16;
-    const int64_t r0 = (int64_t)blockIdx.x * kNormRows;
-    const int nr = (int)min<int64_t>(kNormRows, rows - r0);
-    for (int c = t; c < nch; c += 256) {
-        const uint16_t *p = k + r0 * ld + 8 * c;
-        float m = 0.f;
-        int r = 0;
-        for (; r + 4 <= nr; r += 4) {
-            uint4 u[4];
+    const int c = (int)blockIdx.y * (kNormHeads * 16) + (t & 127);
+    const int head = c >> 4;  // uniform over 16 consecutive lanes
+    if (head >= heads) return;
+    const int64_t r0 = (int64_t)blockIdx.x * per;
+    const int nr = (int)min<int64_t>(per, rows - r0);
+    const uint16_t *p = k + r0 * ld + 8 * c;
+    float m = 0.f;
+    int r = t >> 7;
+    for (; r + 14 < nr; r += 16) {
+        uint4 u[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) u[i] = *reinterpret_cast<const uint4 *>(p + (int64_t)(r + i) * ld);
+        for (int i = 0; i < 8; ++i) u[i] = *reinterpret_cast<const uint4 *>(p + (int64_t)(r + 2 * i) * ld);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float f[8];
-                unpack8(u[i], f);
-                float s2 = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) s2 = __builtin_fmaf(f[e], f[e], s2);
-                m = fmaxf(m, sum16(s2));
-            }
-        }
-        for (; r < nr; ++r) {
+        for (int i = 0; i < 8; ++i) {
             float f[8];
-            unpack8(*reinterpret_cast<const uint4 *>(p + (int64_t)r * ld), f);
+            unpack8(u[i], f);
             float s2 = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) s2 = __builtin_fmaf(f[e], f[e], s2);
             m = fmaxf(m, sum16(s2));
         }
-        if ((c & 15) == 0) atomicMax(kmax2 + (c >> 4), __float_as_uint(m));
     }
+    for (; r < nr; r += 2) {
+        float f[8];
+        unpack8(*reinterpret_cast<const uint4 *>(p + (int64_t)r * ld), f);
+        float s2 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s2 = __builtin_fmaf(f[e], f[e], s2);
+        m = fmaxf(m, sum16(s2));
+    }
+    if ((t & 15) == 0) atomicMax(kmax2 + head, __float_as_uint(m));
 }
 
 // V -> V^T staging for one segment: tile of 64 keys x 128 channels of one head
@@ -831,34 +837,53 @@ __global__ __launch_bounds__(256) void vt_transpose_kernel(const uint16_t *v, in
 }
 
 // Combines the partial results of (head, tile) items cut into key-range
-// pieces: per query row, o = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M)
-// with M the largest m_s, rounded to BF16. Workgroup (item, quarter): 64 rows
-// of one item, one wave per row at a time, two channels per lane.
+// pieces (at most 4, as the work schedule cuts them): per query row,
+// o = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M) with M the largest m_s,
+// rounded to BF16. Workgroup (item, quarter): 64 rows of one item, 16 rows at
+// a time, 16 lanes per row with 8 channels each; every piece's loads of a row
+// are issued before any of them is used.
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float *part, int32_t records, int32_t pieces,
                                                          int32_t first, int32_t tiles_per_head, int64_t rows,
                                                          uint16_t *o, int64_t ld_o) {
+    constexpr int kMaxPieces = 4;
     const int item = blockIdx.x;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int sub = threadIdx.x >> 4, cl = threadIdx.x & 15;
     const int hti = first + item;
     const int head = hti / tiles_per_head, tile = hti - head * tiles_per_head;
     const float2 *ml = reinterpret_cast<const float2 *>(part + (int64_t)records * BQ * D);
-    for (int r = blockIdx.y * 64 + wave; r < (int)blockIdx.y * 64 + 64; r += 4) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int r = (int)blockIdx.y * 64 + it * 16 + sub;
         const int64_t q = (int64_t)tile * BQ + r;
-        if (q >= rows) break;
+        if (q >= rows) continue;
+        float2 e[kMaxPieces];
+        float4 v[kMaxPieces][2];
+#pragma unroll
+        for (int s = 0; s < kMaxPieces; ++s)
+            if (s < pieces) {
+                const int64_t rec = (int64_t)item * pieces + s;
+                e[s] = ml[rec * BQ + r];
+                const float4 *src = reinterpret_cast<const float4 *>(part + (rec * BQ + r) * D + 8 * cl);
+                v[s][0] = src[0];
+                v[s][1] = src[1];
+            }
         float M = -__builtin_huge_valf();
-        for (int s = 0; s < pieces; ++s) M = fmaxf(M, ml[(int64_t)(item * pieces + s) * BQ + r].x);
-        float l = 0.f, o0 = 0.f, o1 = 0.f;
-        for (int s = 0; s < pieces; ++s) {
-            const int64_t rec = (int64_t)item * pieces + s;
-            const float2 e = ml[rec * BQ + r];
-            const float w = __builtin_amdgcn_exp2f(e.x - M);
-            const float2 v = *reinterpret_cast<const float2 *>(part + (rec * BQ + r) * D + 2 * lane);
-            l += w * e.y;
-            o0 += w * v.x;
-            o1 += w * v.y;
-        }
+#pragma unroll
+        for (int s = 0; s < kMaxPieces; ++s)
+            if (s < pieces) M = fmaxf(M, e[s].x);
+        float l = 0.f, a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < kMaxPieces; ++s)
+            if (s < pieces) {
+                const float w = __builtin_amdgcn_exp2f(e[s].x - M);
+                l += w * e[s].y;
+                a[0] += w * v[s][0].x; a[1] += w * v[s][0].y; a[2] += w * v[s][0].z; a[3] += w * v[s][0].w;
+                a[4] += w * v[s][1].x; a[5] += w * v[s][1].y; a[6] += w * v[s][1].z; a[7] += w * v[s][1].w;
+            }
         const float inv = 1.0f / l;
-        *reinterpret_cast<uint32_t *>(o + q * ld_o + head * D + 2 * lane) = pack_bf16x2(o0 * inv, o1 * inv);
+        *reinterpret_cast<uint4 *>(o + q * ld_o + head * D + 8 * cl) =
+            make_uint4(pack_bf16x2(a[0] * inv, a[1] * inv), pack_bf16x2(a[2] * inv, a[3] * inv),
+                       pack_bf16x2(a[4] * inv, a[5] * inv), pack_bf16x2(a[6] * inv, a[7] * inv));
     }
 }
 
@@ -890,8 +915,10 @@ void stage_vt(const VtPlan &plan, const uint16_t *k, int64_t ld_k, const uint16_
     for (int i = 0; i < plan.n; ++i) {
         const VtSeg &e = plan.seg[i];
         const uint16_t *ks = e.own ? k + e.begin * ld_k : e.k + e.begin * e.ld;
-        key_norm_max_kernel<<<dim3((unsigned)((e.len + kNormRows - 1) / kNormRows)), 256, 0, stream>>>(
-            ks, e.own ? ld_k : e.ld, e.len, heads, kmax2);
+        const int per = norm_rows_per_wg(e.len);
+        key_norm_max_kernel<<<dim3((unsigned)((e.len + per - 1) / per), (unsigned)((heads + kNormHeads - 1) / kNormHeads)),
+                              256, 0, stream>>>(
+            ks, e.own ? ld_k : e.ld, e.len, heads, per, kmax2);
     }
     for (int i = 0; i < plan.n; ++i) {
         const VtSeg &e = plan.seg[i];
@@ -1038,7 +1065,9 @@ extern "C" int h3_kv_stage(const uint16_t *k, const uint16_t *v, int64_t ld, int
     const int64_t lpad = (len + 63) / 64 * 64;
     uint32_t *km = reinterpret_cast<uint32_t *>(kmax2);
     zero_u32_kernel<<<dim3((unsigned)((heads + 63) / 64)), 64, 0, st>>>(km, heads);
-    key_norm_max_kernel<<<dim3((unsigned)((len + kNormRows - 1) / kNormRows)), 256, 0, st>>>(k, ld, len, heads, km);
+    const int per = norm_rows_per_wg(len);
+    key_norm_max_kernel<<<dim3((unsigned)((len + per - 1) / per), (unsigned)((heads + kNormHeads - 1) / kNormHeads)), 256,
+                          0, st>>>(k, ld, len, heads, per, km);
     vt_transpose_kernel<<<dim3((unsigned)(lpad / BKV), (unsigned)heads), 256, 0, st>>>(v, ld, len, vt, lpad);
     return launch_status();
 }

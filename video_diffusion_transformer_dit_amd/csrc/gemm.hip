@@ -275,15 +275,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_sk_kernel(GemmArgs p) {
 }
 
 
-// Stream-K fix-up: one wavefront per (tail tile, 128 x 128 quarter) sums, in
-// K order, the partial sums of the workgroups whose unit ranges cover the
-// tile, then applies the epilogue exactly as the main kernel's wave would.
-template <int EPI>
-__global__ __launch_bounds__(64) void gemm_fixup_kernel(GemmArgs p) {
-    const int lane = threadIdx.x;
-    const int wave = blockIdx.x & 3;  // the quarter: the main kernel's wave
-    const int tile = blockIdx.x >> 2;
-    const int t = wave * 64 + lane;   // the main kernel's thread
+// Stream-K fix-up: one wavefront per (tail tile, 128 x 128 quarter, 32-row
+// block j of the quarter) sums, in K order, the partial sums of the
+// workgroups whose unit ranges cover the tile, then applies the epilogue to
+// those rows exactly as the main kernel's wave would. A wave reads 16 float4
+// per partial slot, so the pass has many loads in flight across 16 waves per
+// tile.
+template <int EPI, int J>
+__device__ __forceinline__ void gemm_fixup_rows(const GemmArgs &p, int tile, int wave, int lane) {
+    const int t = wave * 64 + lane;           // the main kernel's thread
     const int wm = wave >> 1, wn = wave & 1;
     const int r32 = lane & 31, g2 = lane >> 5;
     const int KT = (int)(p.K / BK);
@@ -293,33 +293,46 @@ __global__ __launch_bounds__(64) void gemm_fixup_kernel(GemmArgs p) {
     int64_t w = (tb * G) / U;
     while (w > 0 && (w * U) / G > tb) --w;
     while (((w + 1) * U) / G <= tb) ++w;
-    f32x16_t acc[4][4];
+    f32x16_t acc[4][4];  // only the column J is used
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+        for (int e = 0; e < 16; ++e) acc[i][J][e] = 0.f;
     for (; w < G && (w * U) / G < te; ++w) {
         const int64_t ws = (w * U) / G;
         const int sg = ws / KT == tile ? 0 : 1;  // this tile is the workgroup's first or second segment
         const float4 *src = reinterpret_cast<const float4 *>(p.part + (w * 2 + sg) * (BM * BN));
+        float4 v[4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int q = 0; q < 4; ++q) v[i][q] = src[((4 * i + J) * 4 + q) * kThreads + t];
 #pragma unroll
-                for (int e = 0; e < 16; e += 4) {
-                    const float4 v = src[((4 * i + j) * 4 + e / 4) * kThreads + t];
-                    acc[i][j][e] += v.x;
-                    acc[i][j][e + 1] += v.y;
-                    acc[i][j][e + 2] += v.z;
-                    acc[i][j][e + 3] += v.w;
-                }
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[i][J][4 * q] += v[i][q].x;
+                acc[i][J][4 * q + 1] += v[i][q].y;
+                acc[i][J][4 * q + 2] += v[i][q].z;
+                acc[i][J][4 * q + 3] += v[i][q].w;
+            }
     }
     int tm, tn;
     gemm_grouped_coords(p.dp_tiles + tile, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-    gemm_epilogue<EPI>(p, acc, tm, tn, wm, wn, r32, g2);
+    gemm_epilogue_rows<EPI, J>(p, acc, tm, tn, wm, wn, r32, g2);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(64) void gemm_fixup_kernel(GemmArgs p) {
+    const int lane = threadIdx.x;
+    const int wave = (blockIdx.x >> 2) & 3;   // the quarter: the main kernel's wave
+    const int tile = blockIdx.x >> 4;
+    switch (blockIdx.x & 3) {                 // 32-row block of the quarter
+        case 0: gemm_fixup_rows<EPI, 0>(p, tile, wave, lane); break;
+        case 1: gemm_fixup_rows<EPI, 1>(p, tile, wave, lane); break;
+        case 2: gemm_fixup_rows<EPI, 2>(p, tile, wave, lane); break;
+        default: gemm_fixup_rows<EPI, 3>(p, tile, wave, lane); break;
+    }
 }
 
 }  // namespace
@@ -362,7 +375,7 @@ void launch_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ld
         case H3_EPI_SWIGLU: gemm_bf16_sk_kernel<H3_EPI_SWIGLU><<<sgrid, kThreads, 0, stream>>>(p); break;
         default: gemm_bf16_sk_kernel<H3_EPI_STORE><<<sgrid, kThreads, 0, stream>>>(p); break;
     }
-    const dim3 fgrid((unsigned)p.sk_tiles * 4);
+    const dim3 fgrid((unsigned)p.sk_tiles * 16);
     switch (epilogue) {
         case H3_EPI_RESIDUAL: gemm_fixup_kernel<H3_EPI_RESIDUAL><<<fgrid, 64, 0, stream>>>(p); break;
         case H3_EPI_SWIGLU: gemm_fixup_kernel<H3_EPI_SWIGLU><<<fgrid, 64, 0, stream>>>(p); break;

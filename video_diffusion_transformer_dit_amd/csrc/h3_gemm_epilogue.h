@@ -22,14 +22,16 @@ constexpr int kEpiSwigluMx = 3;
 // In each 32 x 32 sub-tile the lane holds row m = lane & 31 and, for register
 // group q (0..3), the 4 columns 8 q + 4 (lane >> 5) + (0..3). Args provides
 // M, N, ffn, c/ldc, bias, resid/ld_r, gate/ld_gate, mod_idx and n_groups.
-template <int EPI, typename Args>
-__device__ __forceinline__ void gemm_epilogue(const Args &p, f32x16_t (&acc)[4][4], int tm, int tn, int wm, int wn,
-                                              int r32, int g2) {
+// gemm_epilogue_rows handles the wave's 32-row block J, sub-tiles acc[i][J]
+// (the other entries of acc are not read).
+template <int EPI, int J, typename Args>
+__device__ __forceinline__ void gemm_epilogue_rows(const Args &p, f32x16_t (&acc)[4][4], int tm, int tn, int wm,
+                                                   int wn, int r32, int g2) {
     constexpr int BM = 256, BN = 256;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    constexpr int j = J;
+    {
         const int64_t m = (int64_t)tm * BM + wm * 128 + j * 32 + r32;
-        if (m >= p.M) continue;
+        if (m >= p.M) return;
         uint16_t *crow = EPI == kEpiSwigluMx ? nullptr : p.c + m * p.ldc;
         if constexpr (EPI == kEpiSwigluMx) {
             // A 32-wide output group is W sub-tiles i = 2 ip, 2 ip + 1: 16
@@ -133,6 +135,16 @@ __device__ __forceinline__ void gemm_epilogue(const Args &p, f32x16_t (&acc)[4][
             }
         }
     }
+}
+
+// The whole wave's 128 x 128: acc[i][j] is sub-tile (i, j).
+template <int EPI, typename Args>
+__device__ __forceinline__ void gemm_epilogue(const Args &p, f32x16_t (&acc)[4][4], int tm, int tn, int wm, int wn,
+                                              int r32, int g2) {
+    gemm_epilogue_rows<EPI, 0>(p, acc, tm, tn, wm, wn, r32, g2);
+    gemm_epilogue_rows<EPI, 1>(p, acc, tm, tn, wm, wn, r32, g2);
+    gemm_epilogue_rows<EPI, 2>(p, acc, tm, tn, wm, wn, r32, g2);
+    gemm_epilogue_rows<EPI, 3>(p, acc, tm, tn, wm, wn, r32, g2);
 }
 
 }  // namespace h3

@@ -33,7 +33,8 @@ struct VtSeg {
 // results a merge pass combines. Ranges of items are dispatched in order:
 // the group whose items read the most keys first; if it fills less than
 // four rounds of the chip's 256 workgroup slots, its last, partial round is
-// cut into pieces (2 to 4, at least 4 key tiles each) so the round is full;
+// cut into pieces (2 to 4, at least 4 key tiles each; the count that ends
+// the tail soonest in rounds of whole items, if any beats 1);
 // then the other groups, longest items first. With more than one range, each
 // range is padded to a multiple of 8 items so that it starts on XCD 0 (also
 // a single range cut into pieces).
@@ -91,7 +92,7 @@ void sparse_vt_group(int64_t valid_len, int64_t prefix_len, h3_qgroup *g);
 // dp_tiles tiles run one per workgroup. sk_groups == 0: no tail split.
 constexpr int kGemmSlots = 256;
 constexpr int kSkMinStages = 8;
-constexpr int kSkWorthStages = 100;
+constexpr int kSkWorthStages = 45;
 struct GemmPlan {
     int32_t tiles_m, tiles_n, tiles, stages;
     int32_t dp_tiles, sk_tiles, sk_groups;

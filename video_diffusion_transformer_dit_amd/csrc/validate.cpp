@@ -153,11 +153,20 @@ void attn_schedule(const h3_qgroup *groups, int n_groups, int64_t dense_len, int
             full = n / kAttnSlots * kAttnSlots;
             const int32_t tail = n - full;
             if (tail > 0) {
-                pieces = (int32_t)std::min<int64_t>({4, (kAttnSlots + tail - 1) / tail, kt[g] / 4});
-                if (pieces < 2) {
-                    pieces = 1;
-                    full = n;
+                // The piece count p that finishes the tail soonest, counted in
+                // rounds of whole items: ceil(tail p / 256) rounds of pieces
+                // 1/p long. Each piece keeps at least 4 key tiles, and the
+                // tail's pieces stay under 512 partial records.
+                int32_t rounds_best = 1;
+                for (int32_t p = 2; p <= 4; ++p) {
+                    if ((int64_t)tail * p > 511 || kt[g] / p < 4) break;
+                    const int32_t r = (int32_t)(((int64_t)tail * p + kAttnSlots - 1) / kAttnSlots);
+                    if ((int64_t)r * pieces < (int64_t)rounds_best * p) {
+                        pieces = p;
+                        rounds_best = r;
+                    }
                 }
+                if (pieces < 2) full = n;
             }
         }
         if (full > 0) add(g, 0, full, 1);
@@ -186,9 +195,10 @@ GemmPlan gemm_plan(int64_t M_valid, int64_t N, int64_t K, int32_t epilogue) {
     g.dp_tiles = g.tiles;
     const int32_t tail = g.tiles % kGemmSlots;
     if (tail == 0 || 5 * tail > 4 * kGemmSlots) return g;
-    // The split costs about as much as 100 stages of the last round (the
-    // partial sums' traffic, the fix-up pass, two more launches): take it only
-    // where the idle share of the last round is worth more.
+    // The split costs about as much as 45 stages of the last round (the
+    // partial sums' traffic, the fix-up pass, two more launches; measured on
+    // the block's projections at 4,096 and 5,424 rows): take it only where the
+    // idle share of the last round is worth more.
     if ((int64_t)g.stages * (kGemmSlots - tail) < (int64_t)kSkWorthStages * kGemmSlots) return g;
     const int64_t units = (int64_t)tail * g.stages;
     const int32_t groups = (int32_t)std::min<int64_t>(kGemmSlots, units / kSkMinStages);
@@ -255,9 +265,8 @@ void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads
     if (out->n > 0 || staged) {
         auto align = [](size_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; };
         // Partial results of the items cut into pieces: a partial round has
-        // fewer than 256 items, each cut into at most ceil(256 / items)
-        // pieces, so fewer than 512 records of 256 rows in all, and at most 4
-        // per item. Reserved from the row count alone so that the size never
+        // fewer than 256 items, cut into at most 4 pieces each and fewer than
+        // 512 records of 256 rows in all. Reserved from the row count alone so that the size never
         // shrinks as rows grow (a dense plan for the buffer rows also fits
         // any valid length below them).
         const int64_t records = std::min<int64_t>(511, 4 * qtiles * heads);
