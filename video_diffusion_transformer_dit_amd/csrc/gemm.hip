@@ -122,16 +122,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, uint4 *smem, int tm
     // the same 16 loads and the vmcnt arithmetic below is constant.
     i32x4_t rs_none = rs_a;
     rs_none.z = 0;
-    // LDS byte address of this wave's first slab of slot 0's W tile.
+    // LDS holds a ring of 5 operand tiles of 32 KB ("halves" of a stage).
+    // Stage s (counted from k0) keeps its W tile in half b = 2 s mod 5 and
+    // its A tile in half b + 1 (mod 5); stage s + 1 sits in halves b + 2 and
+    // b + 3, and half b + 4 (stage s - 1's A tile) is free while stage s is
+    // consumed. So the W tile of stage s + 2 streams into half b + 4 about two
+    // stages before it is read, and its A tile into half b as soon as stage s
+    // is consumed, one stage ahead. (Two full 64 KB slots, the most the LDS
+    // holds, would give both only one stage.)
+    // LDS byte address of this wave's first slab of half 0.
     const uint32_t lds_wave = lds_addr(smem) + (uint32_t)(8 * wave * 64 * 16);
-    // Direct load number d (0..15) of stage kt into slot `slot`: slab
-    // 8 wave + d/2 of the A tile (d odd) or the W tile (d even).
-    auto dma = [&](int slot, int d, int kt) {
-        const int i = d >> 1, op = (d & 1) ? 1 : 0;
+    // Direct load of slab 8 wave + i of stage kt's W (op 0) or A (op 1) tile
+    // into half h.
+    auto dma = [&](int h, int op, int i, int kt) {
         const int slab = 8 * wave + i;
         i32x4_t r = op ? rs_a : ((EPI == H3_EPI_SWIGLU && ((slab >> 1) & 1)) ? rs_w2 : rs_w);
         if (kt >= k1) r = rs_none;
-        const uint32_t m0 = lds_wave + (uint32_t)(((slot * 2 + op) * kTileChunks + 64 * i) * 16);
+        const uint32_t m0 = lds_wave + (uint32_t)((h * kTileChunks + 64 * i) * 16);
         dma_slab(r, m0, op ? a_voff[i] : w_voff[i], kt * BK * 2);
     };
 
@@ -148,34 +155,35 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, uint4 *smem, int tm
     struct Ops {
         bf16x8_t a[4], w[4];
     };
-    // LDS read number r (0..7) of k-step ks of the stage in `slot`, in the
-    // order the MFMAs consume the operands: W[0], A[0..3], W[1..3].
-    auto read = [&](int slot, int ks, int r, Ops &o) {
-        const uint4 *base = smem + slot * 2 * kTileChunks;
+    // LDS read number r (0..7) of k-step ks of the stage whose W and A tiles
+    // are in halves hw and ha, in the order the MFMAs consume the operands:
+    // W[0], A[0..3], W[1..3].
+    auto read = [&](int hw, int ha, int ks, int r, Ops &o) {
         if (r >= 1 && r <= 4)
-            o.a[r - 1] = __builtin_bit_cast(bf16x8_t, base[kTileChunks + swz(wm * 128 + (r - 1) * 32 + r32, ks * 2 + g2)]);
+            o.a[r - 1] = __builtin_bit_cast(
+                bf16x8_t, smem[ha * kTileChunks + swz(wm * 128 + (r - 1) * 32 + r32, ks * 2 + g2)]);
         else {
             const int i = r == 0 ? 0 : r - 4;
-            o.w[i] = __builtin_bit_cast(bf16x8_t, base[swz(wn * 128 + i * 32 + r32, ks * 2 + g2)]);
+            o.w[i] = __builtin_bit_cast(bf16x8_t, smem[hw * kTileChunks + swz(wn * 128 + i * 32 + r32, ks * 2 + g2)]);
         }
     };
-    // One k-step (16 MFMAs) of stage kt, whose operands `cur` already holds.
-    // Stage kt lives in slot (kt - k0) & 1. Per k-step:
+    // One k-step (16 MFMAs) of stage kt, whose ring base is b (compile time)
+    // and whose operands `cur` already holds. Per k-step:
     //  ks 0..2: read k-step ks+1 of stage kt into `nxt`;
-    //  ks 3:    wait for stage kt+1 (its 16 loads are the only ones in
-    //           flight), make sure this wave's reads of stage kt are done,
-    //           barrier (all of stage kt+1 visible, slot kt & 1 free), then
-    //           read k-step 0 of stage kt+1 and issue the first 8 loads of
-    //           stage kt+2 into slot kt & 1;
-    //  ks 0:    issue the other 8 loads of stage kt+1 (begun at k-step 3 of
-    //           stage kt-1).
+    //  ks 0:    also issue the W tile of stage kt+2 into half b+4;
+    //  ks 3:    wait for stage kt+1 (only the 8 loads of stage kt+2's W tile
+    //           may stay in flight), make sure this wave's reads of stage kt
+    //           are done, barrier (stage kt+1 visible, stage kt's halves
+    //           free), then read k-step 0 of stage kt+1 and issue the A tile
+    //           of stage kt+2 into half b.
     // The loads and reads sit between the MFMAs in a fixed order, so issuing
     // them never leaves the matrix pipe idle. Raw barrier: __syncthreads()'s
     // fences would wait for every outstanding load. Reads of a stage at or
     // past k1 see stale or zero data and are never used.
-    auto kstep = [&](int kt, int ks, int slot, const Ops &cur, Ops &nxt) {
+    auto kstep = [&](int kt, int ks, int b, const Ops &cur, Ops &nxt) {
+        const int hw = b, ha = (b + 1) % 5, hw1 = (b + 2) % 5, ha1 = (b + 3) % 5, hfree = (b + 4) % 5;
         if (ks == 3) {
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -184,43 +192,55 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, uint4 *smem, int tm
             const int i = t >> 2, j = t & 3;
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.w[i], cur.a[j], acc[i][j], 0, 0, 0);
             if (t & 1) {
-                if (ks == 3) dma(slot, t >> 1, kt + 2);
-                if (ks == 0) dma(slot ^ 1, 8 + (t >> 1), kt + 1);
+                if (ks == 0) dma(hfree, 0, t >> 1, kt + 2);
+                if (ks == 3) dma(hw, 1, t >> 1, kt + 2);
             } else {
-                if (ks < 3) read(slot, ks + 1, t >> 1, nxt);
-                else read(slot ^ 1, 0, t >> 1, nxt);
+                if (ks < 3) read(hw, ha, ks + 1, t >> 1, nxt);
+                else read(hw1, ha1, 0, t >> 1, nxt);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    auto stage = [&](int kt, int slot, Ops &r0, Ops &r1) {
-        kstep(kt, 0, slot, r0, r1);
-        kstep(kt, 1, slot, r1, r0);
-        kstep(kt, 2, slot, r0, r1);
-        kstep(kt, 3, slot, r1, r0);
+    auto stage = [&](int kt, int b, Ops &r0, Ops &r1) {
+        kstep(kt, 0, b, r0, r1);
+        kstep(kt, 1, b, r1, r0);
+        kstep(kt, 2, b, r0, r1);
+        kstep(kt, 3, b, r1, r0);
     };
 
-    // Prologue: stage k0 and the first half of stage k0+1 in flight; stage
-    // k0's first k-step in registers.
+    // Prologue: stages k0 (halves 0, 1) and k0+1 (halves 2, 3) in flight;
+    // stage k0's first k-step in registers.
 #pragma unroll
-    for (int d = 0; d < 16; ++d) dma(0, d, k0);
+    for (int i = 0; i < kSlabsPerWave; ++i) dma(0, 0, i, k0);
 #pragma unroll
-    for (int d = 0; d < 8; ++d) dma(1, d, k0 + 1);
+    for (int i = 0; i < kSlabsPerWave; ++i) dma(1, 1, i, k0);
+#pragma unroll
+    for (int i = 0; i < kSlabsPerWave; ++i) dma(2, 0, i, k0 + 1);
+#pragma unroll
+    for (int i = 0; i < kSlabsPerWave; ++i) dma(3, 1, i, k0 + 1);
     Ops opa, opb;
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) read(0, 0, r, opa);
+    for (int r = 0; r < 8; ++r) read(0, 1, 0, r, opa);
+    // Five stages per iteration bring the ring base back to 0 (b = 0, 2, 4,
+    // 1, 3); the remaining 0..4 stages follow with their own bases.
     int kt = k0;
 #pragma unroll 1
-    for (; kt + 2 <= k1; kt += 2) {
+    for (; kt + 5 <= k1; kt += 5) {
         stage(kt, 0, opa, opb);
-        stage(kt + 1, 1, opa, opb);
+        stage(kt + 1, 2, opa, opb);
+        stage(kt + 2, 4, opa, opb);
+        stage(kt + 3, 1, opa, opb);
+        stage(kt + 4, 3, opa, opb);
     }
-    if (kt < k1) stage(kt, 0, opa, opb);  // odd stage count
+    if (kt < k1) stage(kt, 0, opa, opb);
+    if (kt + 1 < k1) stage(kt + 1, 2, opa, opb);
+    if (kt + 2 < k1) stage(kt + 2, 4, opa, opb);
+    if (kt + 3 < k1) stage(kt + 3, 1, opa, opb);
     // Drain the loads still in flight (stages past the range) before the
-    // workgroup can end or reuse the LDS slots.
+    // workgroup can end or reuse the LDS.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     if constexpr (!PARTIAL) {
@@ -244,8 +264,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, uint4 *smem, int tm
 // of the grouped order, XCD-contiguous.
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
-    // LDS: two stage slots of [W tile, A tile], 32 KB each (128 KB).
-    __shared__ uint4 smem[2 * 2 * kTileChunks];
+    // LDS: the ring of five 32 KB operand tiles (160 KB).
+    __shared__ uint4 smem[5 * kTileChunks];
     int tm, tn;
     gemm_tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, p.dp_tiles, tm, tn);
     gemm_tile<EPI, false>(p, smem, tm, tn, 0, (int)(p.K / BK), nullptr);
@@ -257,7 +277,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
 // partial sums for each in its two slots of `part`.
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_sk_kernel(GemmArgs p) {
-    __shared__ uint4 smem[2 * 2 * kTileChunks];
+    __shared__ uint4 smem[5 * kTileChunks];
     const int KT = (int)(p.K / BK);
     const int w = blockIdx.x;
     const int64_t U = (int64_t)p.sk_tiles * KT;
@@ -352,9 +372,10 @@ void launch_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ld
     const GemmPlan plan = gemm_plan(M_valid, N, K, epilogue);
     p.tiles_m = plan.tiles_m;
     p.tiles_n = plan.tiles_n;
-    // Measured on the block's projections: narrow grids keep the L2 best
-    // with 2 tile rows per group, wide ones (the SwiGLU FFN) with 8.
-    p.group_m = p.tiles_n >= 128 ? 8 : 2;
+    // Tile rows per group, measured on the block's projections: wide grids
+    // (the SwiGLU FFN) keep the L2 best with 8; narrow ones with 2 at 58,816
+    // rows (230 tile rows), 4 at 5,424 (22) and 8 at 4,096 (16).
+    p.group_m = (p.tiles_n >= 128 || p.tiles_m <= 16) ? 8 : p.tiles_m <= 32 ? 4 : 2;
     const bool sk = workspace != nullptr && plan.sk_groups > 0;
     p.dp_tiles = sk ? plan.dp_tiles : plan.tiles;
     p.sk_tiles = sk ? plan.sk_tiles : 0;
