@@ -170,7 +170,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, uint4 *smem, int tm
     // One k-step (16 MFMAs) of stage kt, whose ring base is b (compile time)
     // and whose operands `cur` already holds. Per k-step:
     //  ks 0..2: read k-step ks+1 of stage kt into `nxt`;
-    //  ks 0:    also issue the W tile of stage kt+2 into half b+4;
+    //  ks 0, 1: also issue the W tile of stage kt+2 into half b+4 (4
+    //           loads each, every fourth slot);
     //  ks 3:    wait for stage kt+1 (only the 8 loads of stage kt+2's W tile
     //           may stay in flight), make sure this wave's reads of stage kt
     //           are done, barrier (stage kt+1 visible, stage kt's halves
@@ -192,7 +193,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, uint4 *smem, int tm
             const int i = t >> 2, j = t & 3;
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.w[i], cur.a[j], acc[i][j], 0, 0, 0);
             if (t & 1) {
-                if (ks == 0) dma(hfree, 0, t >> 1, kt + 2);
+                if (ks < 2 && (t & 3) == 1) dma(hfree, 0, 4 * ks + (t >> 2), kt + 2);
                 if (ks == 3) dma(hw, 1, t >> 1, kt + 2);
             } else {
                 if (ks < 3) read(hw, ha, ks + 1, t >> 1, nxt);
