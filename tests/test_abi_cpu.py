@@ -356,7 +356,7 @@ def test_elementwise_and_linear_validators():
 def test_linear_stream_k_plan_and_workspace_checks():
     """The stream-K tail of h3_linear: which shapes split their last round of
     tiles (a tail of at most 4/5 of the 256 slots whose idle share, in K
-    stages, is worth at least 45 stages), the partial-sum area that needs
+    stages, is worth at least 55 stages), the partial-sum area that needs
     (two 256 x 256 FP32 slots per range), and the workspace checks."""
     MB256 = 256 * 256 * 4
     # 4,096 rows x 5,376 columns: 16 x 21 = 336 tiles, a tail of 80 tiles.
@@ -365,8 +365,8 @@ def test_linear_stream_k_plan_and_workspace_checks():
     assert h3.linear_workspace_bytes(4096, 5376, 21504, h3.H3_EPI_RESIDUAL) == 256 * 2 * MB256
     # K 5,376 (84 stages): 58 stages idle -> split, 6,720 units in 256 ranges
     assert h3.linear_workspace_bytes(4096, 5376, 5376, h3.H3_EPI_RESIDUAL) == 256 * 2 * MB256
-    # 5,424 rows, SwiGLU up projection: 22 x 168 = 3,696 tiles, tail 112, 84 x 144/256 = 47 stages idle -> split
-    assert h3.linear_workspace_bytes(5424, 43008, 5376, h3.H3_EPI_SWIGLU) == 256 * 2 * MB256
+    # 5,424 rows, QKV projection: 22 x 63 = 1,386 tiles, tail 106, 84 x 150/256 = 49 stages idle -> no split
+    assert h3.linear_workspace_bytes(5424, 16128, 5376, h3.H3_EPI_STORE) == 0
     # 4,096 rows, the same: 16 x 168 = 2,688 tiles, tail 128, 84 x 128/256 = 42 stages idle -> no split
     assert h3.linear_workspace_bytes(4096, 43008, 5376, h3.H3_EPI_SWIGLU) == 0
     # a tail of more than 4/5 of the slots is not split: 58,758 rows x 5,376 = 230 x 21 = 4,830 tiles, tail 222

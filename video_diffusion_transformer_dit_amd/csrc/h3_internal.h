@@ -92,7 +92,7 @@ void sparse_vt_group(int64_t valid_len, int64_t prefix_len, h3_qgroup *g);
 // dp_tiles tiles run one per workgroup. sk_groups == 0: no tail split.
 constexpr int kGemmSlots = 256;
 constexpr int kSkMinStages = 8;
-constexpr int kSkWorthStages = 45;
+constexpr int kSkWorthStages = 55;
 struct GemmPlan {
     int32_t tiles_m, tiles_n, tiles, stages;
     int32_t dp_tiles, sk_tiles, sk_groups;

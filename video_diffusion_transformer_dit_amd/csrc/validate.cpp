@@ -195,7 +195,7 @@ GemmPlan gemm_plan(int64_t M_valid, int64_t N, int64_t K, int32_t epilogue) {
     g.dp_tiles = g.tiles;
     const int32_t tail = g.tiles % kGemmSlots;
     if (tail == 0 || 5 * tail > 4 * kGemmSlots) return g;
-    // The split costs about as much as 45 stages of the last round (the
+    // The split costs about as much as 55 stages of the last round (the
     // partial sums' traffic, the fix-up pass, two more launches; measured on
     // the block's projections at 4,096 and 5,424 rows): take it only where the
     // idle share of the last round is worth more.
