@@ -157,6 +157,24 @@ def test_linear_store(M, Mv, N, K, bias):
     assert_zero_rows(c, Mv, "c")
 
 
+@pytest.mark.parametrize("stages", list(range(1, 12)))
+def test_linear_every_stage_count(stages):
+    """K = 64 x 1..11: the main loop runs five K stages per iteration over a
+    ring of five LDS operand tiles, then the remaining 0-4 stages each from its
+    own ring position; every loop count and remainder against the oracle, on a
+    ragged 2 x 2 tile grid."""
+    M, Mv, N, K = 260, 258, 264, 64 * stages
+    _say(f"linear stages={stages} M={M} Mv={Mv} N={N} K={K}")
+    ab = I.normal_bf16(f"lst{stages}.a", (M, K))
+    wb = I.normal_bf16(f"lst{stages}.w", (N, K), 0.05)
+    c = poison((M, N))
+    h3.linear(dev_bf16(ab), dev_bf16(wb), c, Mv, h3.H3_EPI_STORE)
+    torch.cuda.synchronize()
+    ref = O.linear(O.bf16_to_f64(ab[:Mv]), O.bf16_to_f64(wb), None)
+    assert_parity(f64(c)[:Mv], ref, "c")
+    assert_zero_rows(c, Mv, "c")
+
+
 @pytest.mark.parametrize("M,Mv,N,K,G", [(300, 291, 512, 256, 1), (520, 515, 5376, 512, 3),
                                            (70, 66, 256, 320, 2)])
 def test_linear_gated_residual(M, Mv, N, K, G):

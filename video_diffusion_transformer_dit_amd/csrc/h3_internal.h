@@ -33,12 +33,19 @@ struct VtSeg {
 // results a merge pass combines. Ranges of items are dispatched in order:
 // the group whose items read the most keys first; if it fills less than
 // four rounds of the chip's 256 workgroup slots, its last, partial round is
-// cut into pieces (2 to 4, at least 4 key tiles each; the count that ends
-// the tail soonest in rounds of whole items, if any beats 1);
+// cut into pieces (2 to 4, at least 4 key tiles each: the count whose tail,
+// with the other groups' items after it, finishes soonest under list
+// scheduling, if any beats 1);
 // then the other groups, longest items first. With more than one range, each
 // range is padded to a multiple of 8 items so that it starts on XCD 0 (also
 // a single range cut into pieces).
 constexpr int kAttnSlots = 256;
+// Fixed cost of one work item (Q loads, the first tiles' latency, the
+// epilogue), in key tiles of the steady loop: about 15 us against 1.8 us per
+// tile, measured on full rounds of short items.
+constexpr int64_t kAttnItemTiles = 8;
+// At most this many of the other groups' items enter the tail's estimate.
+constexpr int64_t kAttnSimUnits = 2048;
 struct AttnSchedule {
     int n;                                // ranges
     int group[H3_MAX_GROUPS + 1];         // caller's group index of each range

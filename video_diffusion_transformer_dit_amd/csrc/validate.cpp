@@ -8,6 +8,8 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <functional>
+#include <queue>
 #include <vector>
 
 #include "h3_internal.h"
@@ -116,6 +118,23 @@ void sparse_vt_group(int64_t valid_len, int64_t prefix_len, h3_qgroup *g) {
     g->seg[1] = h3_kv_seg{nullptr, nullptr, 0, prefix_len, valid_len - prefix_len, nullptr, nullptr};
 }
 
+// Finish time of list scheduling on kAttnSlots identical workgroup slots, all
+// free at time 0: each unit (a length in key tiles) goes, in order, to the
+// slot that frees first. This is how the dispatcher hands out a launch's
+// workgroups once its full rounds are done.
+static int64_t list_makespan(const std::vector<int64_t> &units) {
+    std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
+    for (int i = 0; i < kAttnSlots; ++i) free_at.push(0);
+    int64_t end = 0;
+    for (const int64_t u : units) {
+        const int64_t t = free_at.top() + u;
+        free_at.pop();
+        free_at.push(t);
+        end = std::max(end, t);
+    }
+    return end;
+}
+
 void attn_schedule(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads, AttnSchedule *out) {
     std::memset(out, 0, sizeof(*out));
     int order[H3_MAX_GROUPS];
@@ -153,17 +172,31 @@ void attn_schedule(const h3_qgroup *groups, int n_groups, int64_t dense_len, int
             full = n / kAttnSlots * kAttnSlots;
             const int32_t tail = n - full;
             if (tail > 0) {
-                // The piece count p that finishes the tail soonest, counted in
-                // rounds of whole items: ceil(tail p / 256) rounds of pieces
-                // 1/p long. Each piece keeps at least 4 key tiles, and the
-                // tail's pieces stay under 512 partial records.
-                int32_t rounds_best = 1;
-                for (int32_t p = 2; p <= 4; ++p) {
-                    if ((int64_t)tail * p > 511 || kt[g] / p < 4) break;
-                    const int32_t r = (int32_t)(((int64_t)tail * p + kAttnSlots - 1) / kAttnSlots);
-                    if ((int64_t)r * pieces < (int64_t)rounds_best * p) {
+                // The piece count p (1-4) whose tail finishes soonest: list
+                // scheduling of the tail's pieces, then the other groups'
+                // items (longest group first, as they are dispatched), each
+                // unit costing its key tiles plus kAttnItemTiles for the
+                // item's fixed work. Each piece keeps at least 4 key tiles,
+                // and the tail's pieces stay under 512 partial records.
+                std::vector<int64_t> rest;
+                for (int oj = 1; oj < nc && (int64_t)rest.size() < kAttnSimUnits; ++oj) {
+                    const int64_t cnt = (rows[order[oj]] + 255) / 256 * heads;
+                    for (int64_t i = 0; i < cnt && (int64_t)rest.size() < kAttnSimUnits; ++i)
+                        rest.push_back(kt[order[oj]] + kAttnItemTiles);
+                }
+                int64_t best = -1;
+                for (int32_t p = 1; p <= 4; ++p) {
+                    if (p > 1 && ((int64_t)tail * p > 511 || kt[g] / p < 4)) break;
+                    std::vector<int64_t> units;
+                    units.reserve((size_t)tail * p + rest.size());
+                    for (int32_t i = 0; i < tail; ++i)
+                        for (int32_t q = 0; q < p; ++q)
+                            units.push_back((q + 1) * kt[g] / p - q * kt[g] / p + kAttnItemTiles);
+                    units.insert(units.end(), rest.begin(), rest.end());
+                    const int64_t t = list_makespan(units);
+                    if (best < 0 || t < best) {
+                        best = t;
                         pieces = p;
-                        rounds_best = r;
                     }
                 }
                 if (pieces < 2) full = n;
