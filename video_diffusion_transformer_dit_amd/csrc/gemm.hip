@@ -68,95 +68,6 @@ struct GemmArgs {
 // see 8 distinct chunk positions, so the 16 reads hit distinct banks.
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kChunksPerRow + (chunk ^ ((row >> 1) & 7)); }
 
-// Epilogue through LDS. In the MFMA register layout a lane holds 4 columns of
-// one row per register group, so a wave's global accesses would touch 32 rows
-// in 8- or 16-byte pieces. Instead each wave writes its 128 x 128 results to
-// its own 32 KB of the (now idle) stage ring and reads them back row by row,
-// so every global load and store is 16 bytes per lane along a row (whole
-// 128-byte lines per 8 lanes). Same arithmetic per element as gemm_epilogue.
-// The FP32 accumulators go half the wave's rows at a time ([64 rows][32
-// chunks of 4 floats], chunk k of row r at k ^ (r & 15)); a lane then takes
-// 8 columns of one row, 4 rows per step. Store and gated-residual epilogues
-// (measured 2-4% faster on the projections that use them); the SwiGLU tile,
-// half as wide at the output, measured the same either way and keeps the
-// register-layout epilogue.
-template <int EPI>
-__device__ __forceinline__ void gemm_epilogue_lds(const GemmArgs &p, f32x16_t (&acc)[4][4], int tm, int tn, int wm,
-                                                  int wn, int lane, uint4 *lw) {
-    const int r32 = lane & 31, g2 = lane >> 5;
-    const int64_t row0 = (int64_t)tm * BM + wm * 128;
-    const int c8 = lane & 15;
-    const int64_t n = (int64_t)tn * BN + wn * 128 + 8 * c8;
-    const bool col_ok = n < p.N;
-    float bias8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (p.bias && col_ok) unpack8(*reinterpret_cast<const uint4 *>(p.bias + n), bias8);
-    // one gate row for every row unless the rows pick modulation groups
-    const bool gate_per_row = EPI == H3_EPI_RESIDUAL && p.mod_idx != nullptr;
-    float gate8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (EPI == H3_EPI_RESIDUAL && !gate_per_row && col_ok) {
-        const float4 g0 = *reinterpret_cast<const float4 *>(p.gate + n);
-        const float4 g1 = *reinterpret_cast<const float4 *>(p.gate + n + 4);
-        gate8[0] = g0.x; gate8[1] = g0.y; gate8[2] = g0.z; gate8[3] = g0.w;
-        gate8[4] = g1.x; gate8[5] = g1.y; gate8[6] = g1.z; gate8[7] = g1.w;
-    }
-    float4 *lf = reinterpret_cast<float4 *>(lw);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int j = 2 * h + jj;
-            const int row = jj * 32 + r32;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int chunk = 8 * i + 2 * q + g2;
-                    lf[row * 32 + (chunk ^ (row & 15))] = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                                                                      acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-                }
-        }
-        // the residual rows of this half first: loads issued after the
-        // stores below would each wait out a latency (possible aliasing)
-        uint4 rv[16];
-        if (EPI == H3_EPI_RESIDUAL) {
-#pragma unroll
-            for (int it = 0; it < 16; ++it) {
-                const int64_t m = row0 + 64 * h + it * 4 + (lane >> 4);
-                if (m < p.M && col_ok) rv[it] = *reinterpret_cast<const uint4 *>(p.resid + m * p.ld_r + n);
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < 16; ++it) {
-            const int row = it * 4 + (lane >> 4);
-            const int64_t m = row0 + 64 * h + row;
-            const float4 a = lf[row * 32 + ((2 * c8) ^ (row & 15))];
-            const float4 b = lf[row * 32 + ((2 * c8 + 1) ^ (row & 15))];
-            if (m >= p.M || !col_ok) continue;
-            float v[8] = {a.x + bias8[0], a.y + bias8[1], a.z + bias8[2], a.w + bias8[3],
-                          b.x + bias8[4], b.y + bias8[5], b.z + bias8[6], b.w + bias8[7]};
-            if (EPI == H3_EPI_RESIDUAL) {
-                float g[8];
-                if (gate_per_row) {
-                    const int grp = min(max(p.mod_idx[m], 0), p.n_groups - 1);
-                    const float *gr = p.gate + (int64_t)grp * p.ld_gate + n;
-                    const float4 g0 = *reinterpret_cast<const float4 *>(gr);
-                    const float4 g1 = *reinterpret_cast<const float4 *>(gr + 4);
-                    g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
-                    g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) g[e] = gate8[e];
-                }
-                float r[8];
-                unpack8(rv[it], r);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = r[e] + g[e] * v[e];
-            }
-            *reinterpret_cast<uint4 *>(p.c + m * p.ldc + n) = pack8(v);
-        }
-    }
-}
-
 // One output tile (tm, tn) over the K stages [k0, k1): the whole tile with
 // its epilogue, or (PARTIAL) a range of its stages whose FP32 partial sums go
 // to `part` (stream-K tail). smem: the 160 KB ring of operand tiles.

@@ -265,7 +265,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(MxGemmArgs p) {
     if (kt < KT) stage(kt, 0, opa, opb, sca, scb);  // odd KT
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    gemm_epilogue<EPI>(p, acc, tm, tn, wm, wn, r32, g2);
+    if constexpr (EPI == H3_EPI_STORE || EPI == H3_EPI_RESIDUAL) {
+        __syncthreads();  // every wave is done with the stage slots before they hold the epilogue's tiles
+        gemm_epilogue_lds<EPI>(p, acc, tm, tn, wm, wn, lane, smem + wave * kTileChunks);
+    } else {
+        gemm_epilogue<EPI>(p, acc, tm, tn, wm, wn, r32, g2);
+    }
 }
 
 }  // namespace
