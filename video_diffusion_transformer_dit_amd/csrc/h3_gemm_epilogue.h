@@ -111,6 +111,25 @@ __device__ __forceinline__ void gemm_epilogue_rows(const Args &p, f32x16_t (&acc
                 grow = p.gate + (int64_t)g * p.ld_gate;
                 rrow = p.resid + m * p.ld_r;
             }
+            // Every load of the row first, then the stores: a load after a
+            // store that might alias it would wait out a memory latency. (The
+            // GEMM kernels' own store / residual epilogue is gemm_epilogue_lds;
+            // this path serves the stream-K fix-up, which has registers to
+            // spare.)
+            uint2 bv[4][4], rv[4][4];
+            float4 gv[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t n = (int64_t)tn * BN + wn * 128 + i * 32 + 8 * q + 4 * g2;
+                    if (n >= p.N) continue;
+                    if (p.bias) bv[i][q] = *reinterpret_cast<const uint2 *>(p.bias + n);
+                    if (EPI == H3_EPI_RESIDUAL) {
+                        gv[i][q] = *reinterpret_cast<const float4 *>(grow + n);
+                        rv[i][q] = *reinterpret_cast<const uint2 *>(rrow + n);
+                    }
+                }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -119,16 +138,16 @@ __device__ __forceinline__ void gemm_epilogue_rows(const Args &p, f32x16_t (&acc
                     if (n >= p.N) continue;
                     float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
                     if (p.bias) {
-                        const uint2 b = *reinterpret_cast<const uint2 *>(p.bias + n);
+                        const uint2 b = bv[i][q];
                         v[0] += bf16_lo(b.x); v[1] += bf16_hi(b.x); v[2] += bf16_lo(b.y); v[3] += bf16_hi(b.y);
                     }
                     if (EPI == H3_EPI_RESIDUAL) {
-                        const float4 gv = *reinterpret_cast<const float4 *>(grow + n);
-                        const uint2 rv = *reinterpret_cast<const uint2 *>(rrow + n);
-                        v[0] = bf16_lo(rv.x) + gv.x * v[0];
-                        v[1] = bf16_hi(rv.x) + gv.y * v[1];
-                        v[2] = bf16_lo(rv.y) + gv.z * v[2];
-                        v[3] = bf16_hi(rv.y) + gv.w * v[3];
+                        const float4 g4 = gv[i][q];
+                        const uint2 r2 = rv[i][q];
+                        v[0] = bf16_lo(r2.x) + g4.x * v[0];
+                        v[1] = bf16_hi(r2.x) + g4.y * v[1];
+                        v[2] = bf16_lo(r2.y) + g4.z * v[2];
+                        v[3] = bf16_hi(r2.y) + g4.w * v[3];
                     }
                     *reinterpret_cast<uint2 *>(crow + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                 }
