@@ -414,7 +414,9 @@ int h3_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ldw,
  * tiles (stream-K tail) for M_valid rows: 0 when no split applies. With a
  * workspace of at least this size (256-byte aligned, overlapping no operand)
  * the tiles of a last round that fills at most 4/5 of the chip's 256
- * workgroup slots are cut into equal ranges of K stages over all slots; each
+ * workgroup slots, and leaves idle slot time worth at least 55 K stages of
+ * 64 (K/64 x the idle share), are cut into equal ranges of K stages over all
+ * slots; each
  * range leaves FP32 partial sums there and a fix-up pass adds them in K
  * order and applies the epilogue. workspace NULL: one workgroup per tile.
  * A non-NULL workspace smaller than this size is H3_ERR_WORKSPACE. */
