@@ -473,7 +473,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t *u, int64_t 
     unpack8(ua, a);
     unpack8(ub, b);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) a[e] = a[e] / (1.0f + __expf(-a[e])) * b[e];
+    for (int e = 0; e < 8; ++e) a[e] = silu(a[e]) * b[e];
     store_nt(dst, pack8(a));
 }
 

@@ -133,6 +133,13 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // Two floats -> packed BF16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+// SiLU, x / (1 + e^-x), with the hardware reciprocal (v_rcp_f32, within 1 ulp)
+// in place of an IEEE divide (about ten instructions): every caller rounds the
+// result to BF16 or E4M3 right after, far coarser than that ulp. A large
+// negative x (e^-x overflowing to inf) gives a reciprocal of 0 and a product
+// of -0, as the divide would; NaN propagates.
+__device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     bf16x2_t r;

@@ -59,7 +59,7 @@ __device__ __forceinline__ void gemm_epilogue_rows(const Args &p, f32x16_t (&acc
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const float zg = acc[i][j][4 * q + e] + gb[e];
-                            o[ii][q][e] = zg / (1.0f + __expf(-zg)) * (acc[i][j][4 * (q + 2) + e] + ub[e]);
+                            o[ii][q][e] = silu(zg) * (acc[i][j][4 * (q + 2) + e] + ub[e]);
                             amax = fmaxf(amax, fabsf(o[ii][q][e]));
                         }
                     }
@@ -96,7 +96,7 @@ __device__ __forceinline__ void gemm_epilogue_rows(const Args &p, f32x16_t (&acc
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float zg = acc[i][j][4 * q + e] + gb[e];
-                        o[e] = zg / (1.0f + __expf(-zg)) * (acc[i][j][4 * (q + 2) + e] + ub[e]);
+                        o[e] = silu(zg) * (acc[i][j][4 * (q + 2) + e] + ub[e]);
                     }
                     *reinterpret_cast<uint2 *>(crow + col) =
                         make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
