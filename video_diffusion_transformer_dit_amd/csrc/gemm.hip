@@ -125,13 +125,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, uint4 *smem, int tm
     i32x4_t rs_none = rs_a;
     rs_none.z = 0;
     // LDS holds a ring of 5 operand tiles of 32 KB ("halves" of a stage).
-    // Stage s (counted from k0) keeps its W tile in half b = 2 s mod 5 and
-    // its A tile in half b + 1 (mod 5); stage s + 1 sits in halves b + 2 and
-    // b + 3, and half b + 4 (stage s - 1's A tile) is free while stage s is
-    // consumed. So the W tile of stage s + 2 streams into half b + 4 about two
-    // stages before it is read, and its A tile into half b as soon as stage s
-    // is consumed, one stage ahead. (Two full 64 KB slots, the most the LDS
-    // holds, would give both only one stage.)
+    // Stage s (counted from k0) keeps one tile (the long-lead one) in half
+    // b = 2 s mod 5 and the other in half b + 1 (mod 5); stage s + 1 sits in
+    // halves b + 2 and b + 3, and half b + 4 (stage s - 1's second tile) is
+    // free while stage s is consumed. So the long-lead tile of stage s + 2
+    // streams into half b + 4 about two stages before it is read, and the
+    // other into half b as soon as stage s is consumed, one stage ahead. (Two
+    // full 64 KB slots, the most the LDS holds, would give both only one
+    // stage.) The activation tile leads for the store and residual
+    // projections, the weight tile for the SwiGLU projection (each measured
+    // about 1% ahead of the other choice on the block's shapes).
+    constexpr bool kALong = EPI != H3_EPI_SWIGLU;
+    constexpr int kLongOp = kALong ? 1 : 0;  // dma operand index: 0 W, 1 A
     // LDS byte address of this wave's first slab of half 0.
     const uint32_t lds_wave = lds_addr(smem) + (uint32_t)(8 * wave * 64 * 16);
     // Direct load of slab 8 wave + i of stage kt's W (op 0) or A (op 1) tile
@@ -172,19 +177,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, uint4 *smem, int tm
     // One k-step (16 MFMAs) of stage kt, whose ring base is b (compile time)
     // and whose operands `cur` already holds. Per k-step:
     //  ks 0..2: read k-step ks+1 of stage kt into `nxt`;
-    //  ks 0, 1: also issue the W tile of stage kt+2 into half b+4 (4
-    //           loads each, every fourth slot);
-    //  ks 3:    wait for stage kt+1 (only the 8 loads of stage kt+2's W tile
-    //           may stay in flight), make sure this wave's reads of stage kt
-    //           are done, barrier (stage kt+1 visible, stage kt's halves
-    //           free), then read k-step 0 of stage kt+1 and issue the A tile
-    //           of stage kt+2 into half b.
+    //  ks 0, 1: also issue the long-lead tile of stage kt+2 into half b+4
+    //           (4 loads each, every fourth slot);
+    //  ks 3:    wait for stage kt+1 (only the 8 loads of stage kt+2's
+    //           long-lead tile may stay in flight), make sure this wave's
+    //           reads of stage kt are done, barrier (stage kt+1 visible,
+    //           stage kt's halves free), then read k-step 0 of stage kt+1 and
+    //           issue the other tile of stage kt+2 into half b.
     // The loads and reads sit between the MFMAs in a fixed order, so issuing
     // them never leaves the matrix pipe idle. Raw barrier: __syncthreads()'s
     // fences would wait for every outstanding load. Reads of a stage at or
     // past k1 see stale or zero data and are never used.
     auto kstep = [&](int kt, int ks, int b, const Ops &cur, Ops &nxt) {
-        const int hw = b, ha = (b + 1) % 5, hw1 = (b + 2) % 5, ha1 = (b + 3) % 5, hfree = (b + 4) % 5;
+        // the long-lead tile in half b, the other in b + 1 (stage kt + 1: b + 2, b + 3)
+        const int hw = kALong ? (b + 1) % 5 : b, ha = kALong ? b : (b + 1) % 5;
+        const int hw1 = kALong ? (b + 3) % 5 : (b + 2) % 5, ha1 = kALong ? (b + 2) % 5 : (b + 3) % 5;
+        const int hfree = (b + 4) % 5;
         if (ks == 3) {
             asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
@@ -195,8 +203,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, uint4 *smem, int tm
             const int i = t >> 2, j = t & 3;
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.w[i], cur.a[j], acc[i][j], 0, 0, 0);
             if (t & 1) {
-                if (ks < 2 && (t & 3) == 1) dma(hfree, 0, 4 * ks + (t >> 2), kt + 2);
-                if (ks == 3) dma(hw, 1, t >> 1, kt + 2);
+                if (ks < 2 && (t & 3) == 1) dma(hfree, kLongOp, 4 * ks + (t >> 2), kt + 2);
+                if (ks == 3) dma(b, 1 - kLongOp, t >> 1, kt + 2);
             } else {
                 if (ks < 3) read(hw, ha, ks + 1, t >> 1, nxt);
                 else read(hw1, ha1, 0, t >> 1, nxt);
@@ -214,19 +222,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, uint4 *smem, int tm
     // Prologue: stages k0 (halves 0, 1) and k0+1 (halves 2, 3) in flight;
     // stage k0's first k-step in registers.
 #pragma unroll
-    for (int i = 0; i < kSlabsPerWave; ++i) dma(0, 0, i, k0);
+    for (int i = 0; i < kSlabsPerWave; ++i) dma(0, kLongOp, i, k0);
 #pragma unroll
-    for (int i = 0; i < kSlabsPerWave; ++i) dma(1, 1, i, k0);
+    for (int i = 0; i < kSlabsPerWave; ++i) dma(1, 1 - kLongOp, i, k0);
 #pragma unroll
-    for (int i = 0; i < kSlabsPerWave; ++i) dma(2, 0, i, k0 + 1);
+    for (int i = 0; i < kSlabsPerWave; ++i) dma(2, kLongOp, i, k0 + 1);
 #pragma unroll
-    for (int i = 0; i < kSlabsPerWave; ++i) dma(3, 1, i, k0 + 1);
+    for (int i = 0; i < kSlabsPerWave; ++i) dma(3, 1 - kLongOp, i, k0 + 1);
     Ops opa, opb;
     asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) read(0, 1, 0, r, opa);
+    for (int r = 0; r < 8; ++r) read(kALong ? 1 : 0, kALong ? 0 : 1, 0, r, opa);
     // Five stages per iteration bring the ring base back to 0 (b = 0, 2, 4,
     // 1, 3); the remaining 0..4 stages follow with their own bases.
     int kt = k0;
