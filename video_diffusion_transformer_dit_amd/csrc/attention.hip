@@ -732,23 +732,59 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
         return;
     }
 
-    // ---- normalise and store: lane holds O[q][32 dt + 8 g + 4 h + (0..3)] ----
+    // ---- normalise and store: lane holds O[q][32 dt + 8 g + 4 h + (0..3)].
+    //      Launches of several ranges (short items: query groups, key-range
+    //      pieces) store through LDS: each wave writes its 64 rows x 128
+    //      channels in BF16 to its own 16 KB of the now idle K / V^T buffers
+    //      ([64 rows][16 chunks of 8 channels], chunk c of row r at c ^
+    //      (r & 15)) and stores them back row by row, 16 bytes per lane, which
+    //      shortens a short item's tail (measured -1 to -2% at 4,096 keys).
+    //      The one-range dense instance keeps direct stores: there the LDS path
+    //      moved the key loop's register allocation and cost 0.5%. ----
+    if constexpr (MULTI) {
+        __syncthreads();  // every wave is done with the K / V^T buffers
+        uint2 *lo = reinterpret_cast<uint2 *>(smem + wave * (D * 8));
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const float l_tot = pair_sum(l_run[j]);
-        const float inv = 1.0f / l_tot;
-        const int64_t q = qw + 32 * j + l32;
-        if (q < rows_left) {
-            uint16_t *orow = obase + q * a.ld_o + head * D;
+        for (int j = 0; j < 2; ++j) {
+            const float inv = 1.0f / pair_sum(l_run[j]);
+            const int row = 32 * j + l32;
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int d = 32 * dt + 8 * g + 4 * h;
-                    *reinterpret_cast<uint2 *>(orow + d) =
+                    const int chunk = 4 * dt + g;
+                    lo[(row * 16 + (chunk ^ (row & 15))) * 2 + h] =
                         make_uint2(pack_bf16x2(oacc[dt][j][4 * g] * inv, oacc[dt][j][4 * g + 1] * inv),
                                    pack_bf16x2(oacc[dt][j][4 * g + 2] * inv, oacc[dt][j][4 * g + 3] * inv));
                 }
+        }
+        const uint4 *li = smem + wave * (D * 8);
+        const int c = lane & 15;
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+            const int row = it * 4 + (lane >> 4);
+            const int64_t q = qw + row;
+            const uint4 val = li[row * 16 + (c ^ (row & 15))];
+            if (q < rows_left) *reinterpret_cast<uint4 *>(obase + q * a.ld_o + head * D + 8 * c) = val;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float l_tot = pair_sum(l_run[j]);
+            const float inv = 1.0f / l_tot;
+            const int64_t q = qw + 32 * j + l32;
+            if (q < rows_left) {
+                uint16_t *orow = obase + q * a.ld_o + head * D;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int d = 32 * dt + 8 * g + 4 * h;
+                        *reinterpret_cast<uint2 *>(orow + d) =
+                            make_uint2(pack_bf16x2(oacc[dt][j][4 * g] * inv, oacc[dt][j][4 * g + 1] * inv),
+                                       pack_bf16x2(oacc[dt][j][4 * g + 2] * inv, oacc[dt][j][4 * g + 3] * inv));
+                    }
+            }
         }
     }
 }
