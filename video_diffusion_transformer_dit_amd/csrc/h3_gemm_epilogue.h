@@ -156,6 +156,85 @@ __device__ __forceinline__ void gemm_epilogue_rows(const Args &p, f32x16_t (&acc
     }
 }
 
+// Gated-residual epilogue through LDS: the wave's residual block (128 rows x
+// 128 columns, BF16, [128 rows][16 chunks of 8], chunk c of row r at
+// c ^ (r & 15)) streams into its 32 KB of LDS with direct loads, one latency
+// for the whole block; each lane then reads its 4-column pieces there, forms
+// resid + gate * (acc + bias), writes the BF16 result back in place, and the
+// block leaves row by row with 16-byte stores. The caller has made the LDS
+// free (barrier); everything after is wave-local.
+template <typename Args>
+__device__ __forceinline__ void gemm_epilogue_residual_lds(const Args &p, f32x16_t (&acc)[4][4], int tm, int tn,
+                                                           int wm, int wn, int lane, uint4 *lw) {
+    constexpr int BM = 256, BN = 256;
+    const int r32 = lane & 31, g2 = lane >> 5;
+    const int64_t row0 = (int64_t)tm * BM + wm * 128;
+    const int64_t col0 = (int64_t)tn * BN + wn * 128;
+    const int64_t rows = min<int64_t>(p.M - row0, 128);
+    if (rows <= 0 || col0 >= p.N) return;
+    const int64_t cols = min<int64_t>(p.N - col0, 128);
+    // residual block -> LDS: slab s (1 KB) is rows 4 s .. 4 s + 3; lane i
+    // lands at physical chunk i & 15 of row 4 s + i / 16 and so loads that
+    // row's logical chunk (i & 15) ^ (row & 15). Rows past M read zero.
+    const i32x4_t rs = raw_rsrc(p.resid + row0 * p.ld_r + col0, ((rows - 1) * p.ld_r + cols) * 2);
+    const uint32_t lds_w = lds_addr(lw);
+#pragma unroll
+    for (int sl = 0; sl < 32; ++sl) {
+        const int row = 4 * sl + (lane >> 4);
+        const int c = (lane & 15) ^ (row & 15);
+        dma_slab(rs, lds_w + (uint32_t)(sl * 1024), (int)((row * p.ld_r + 8 * c) * 2), 0);
+    }
+    // per-column operands, the same for every row unless rows pick gate groups
+    const bool gate_per_row = p.mod_idx != nullptr;
+    float4 gv[4][4];
+    uint2 bv[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t n = col0 + i * 32 + 8 * q + 4 * g2;
+            gv[i][q] = make_float4(0.f, 0.f, 0.f, 0.f);
+            bv[i][q] = make_uint2(0u, 0u);
+            if (n < p.N) {
+                if (!gate_per_row) gv[i][q] = *reinterpret_cast<const float4 *>(p.gate + n);
+                if (p.bias) bv[i][q] = *reinterpret_cast<const uint2 *>(p.bias + n);
+            }
+        }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the residual block is in LDS
+    uint2 *lh = reinterpret_cast<uint2 *>(lw);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = j * 32 + r32;
+        const float *grow = p.gate;
+        if (gate_per_row && row < rows) {
+            const int g = min(max(p.mod_idx[row0 + row], 0), p.n_groups - 1);
+            grow = p.gate + (int64_t)g * p.ld_gate;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = col0 + i * 32 + 8 * q + 4 * g2;
+                const int at = (row * 16 + ((4 * i + q) ^ (row & 15))) * 2 + g2;
+                const uint2 r2 = lh[at];
+                float4 g4 = gv[i][q];
+                if (gate_per_row && row < rows && n < p.N) g4 = *reinterpret_cast<const float4 *>(grow + n);
+                const uint2 b = bv[i][q];
+                const float v0 = acc[i][j][4 * q] + bf16_lo(b.x), v1 = acc[i][j][4 * q + 1] + bf16_hi(b.x);
+                const float v2 = acc[i][j][4 * q + 2] + bf16_lo(b.y), v3 = acc[i][j][4 * q + 3] + bf16_hi(b.y);
+                lh[at] = make_uint2(pack_bf16x2(bf16_lo(r2.x) + g4.x * v0, bf16_hi(r2.x) + g4.y * v1),
+                                    pack_bf16x2(bf16_lo(r2.y) + g4.z * v2, bf16_hi(r2.y) + g4.w * v3));
+            }
+    }
+    const int c = lane & 15;
+#pragma unroll
+    for (int it = 0; it < 32; ++it) {
+        const int row = it * 4 + (lane >> 4);
+        const uint4 val = lw[row * 16 + (c ^ (row & 15))];
+        if (row < rows && 8 * c < cols) *reinterpret_cast<uint4 *>(p.c + (row0 + row) * p.ldc + col0 + 8 * c) = val;
+    }
+}
+
 // Epilogue through LDS. In the MFMA register layout a lane holds 4 columns of
 // one row per register group, so a wave's global accesses would touch 32 rows
 // in 8- or 16-byte pieces. Instead each wave writes its 128 x 128 results to
@@ -172,6 +251,10 @@ __device__ __forceinline__ void gemm_epilogue_rows(const Args &p, f32x16_t (&acc
 template <int EPI, typename Args>
 __device__ __forceinline__ void gemm_epilogue_lds(const Args &p, f32x16_t (&acc)[4][4], int tm, int tn, int wm,
                                                   int wn, int lane, uint4 *lw) {
+    if constexpr (EPI == H3_EPI_RESIDUAL) {
+        gemm_epilogue_residual_lds(p, acc, tm, tn, wm, wn, lane, lw);
+        return;
+    }
     constexpr int BM = 256, BN = 256;
     const int r32 = lane & 31, g2 = lane >> 5;
     const int64_t row0 = (int64_t)tm * BM + wm * 128;
