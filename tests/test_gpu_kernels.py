@@ -244,6 +244,33 @@ def test_mod_idx_out_of_range_is_clamped():
     assert_parity(f64(c)[:V], ref, "x1 (GEMM epilogue)")
 
 
+@pytest.mark.parametrize("in_place", [False, True])
+def test_linear_gated_residual_bias_ragged(in_place):
+    """The residual epilogue with a bias, a ragged column tile (N = 264: the
+    last tile's second wave has no valid column, its first wave 8) and ragged
+    rows, indexed gates; also in place (c is the residual buffer, which the
+    epilogue reads into LDS before it stores)."""
+    M, Mv, N, K, G = 300, 291, 264, 128, 2
+    _say(f"linear residual bias ragged in_place={in_place}")
+    ab = I.normal_bf16("lrb.a", (M, K))
+    wb = I.normal_bf16("lrb.w", (N, K), 0.05)
+    bb = I.normal_bf16("lrb.b", (N,), 0.5)
+    rb = I.normal_bf16("lrb.r", (M, N))
+    mod = I.normal_f32("lrb.mod", (G, 6, N), 0.5)
+    idx = I.rng_for("lrb.idx").integers(0, G, size=M).astype(np.int32)
+    md = dev_f32(mod)
+    r = dev_bf16(rb)
+    c = r if in_place else poison((M, N))
+    h3.linear(dev_bf16(ab), dev_bf16(wb), c, Mv, h3.H3_EPI_RESIDUAL, bias=dev_bf16(bb), resid=r, gate=md[:, 2],
+              ld_gate_group=6 * N, n_mod_groups=G, mod_idx=dev_i32(idx))
+    torch.cuda.synchronize()
+    m = O.gather_mod(mod.astype(np.float64), idx, Mv)
+    branch = O.linear(O.bf16_to_f64(ab[:Mv]), O.bf16_to_f64(wb), O.bf16_to_f64(bb))
+    ref = O.gated_residual(O.bf16_to_f64(rb[:Mv]), m[:, O.GATE_A], branch)
+    assert_parity(f64(c)[:Mv], ref, "x1")
+    assert_zero_rows(c, Mv, "x1")
+
+
 @pytest.mark.parametrize("M,Mv,F,K", [(300, 291, 512, 256), (260, 257, 1040, 512)])
 @pytest.mark.parametrize("bias", [False, True])
 def test_linear_swiglu(M, Mv, F, K, bias):
