@@ -408,6 +408,62 @@ def test_attention_fixed_and_online_workgroups_in_one_call():
     assert_zero_rows(o, V, "o")
 
 
+def _rescale_count(q_rows, k_rows, slack=40.0):
+    """Per (row, head): how often the online form must raise its softmax
+    reference, restated from its rule: the reference starts at the row's
+    largest scaled score among the first 32 keys, and each later 32-key half
+    tile whose largest score exceeds the reference by more than the slack
+    moves the reference up to that score."""
+    c = np.log2(np.e) / np.sqrt(128.0)
+    nq, nk = q_rows.shape[0], k_rows.shape[0]
+    qh = q_rows.reshape(nq, -1, 128).transpose(1, 0, 2)
+    kh = k_rows.reshape(nk, -1, 128).transpose(1, 0, 2)
+    s = np.matmul(qh, kh.transpose(0, 2, 1)) * c          # [heads, nq, nk]
+    halves = [s[:, :, i:i + 32].max(axis=-1) for i in range(0, nk, 32)]
+    ref, count = halves[0], np.zeros(halves[0].shape, np.int64)
+    for m in halves[1:]:
+        up = m - ref > slack
+        count += up
+        ref = np.where(up, m, ref)
+    return count
+
+
+@pytest.mark.parametrize("pieces", [False, True])
+def test_attention_online_rescales(pieces):
+    """The online form's rescale path: keys whose norms ramp up 4x along the
+    sequence (and a last stretch 12x), against peaked queries, so that each
+    row's largest score climbs far beyond its first half tile's and the
+    softmax reference is raised several times per row, in different half
+    tiles for different rows of a wave (checked on the inputs first). Either
+    one query tile over all keys (pieces=False, 700 keys) or a query tile
+    whose 1,024 keys the schedule cuts into key-range pieces merged
+    afterwards."""
+    heads, rows = 2, 200
+    H = heads * 128
+    nk = 1024 if pieces else 700
+    _say(f"attention online rescales pieces={pieces} keys={nk}")
+    qb = I.normal_bf16("aresc.q", (rows, H), 8.0)
+    k = O.bf16_to_f64(I.normal_bf16("aresc.k", (nk, H)))
+    ramp = 1.0 + 3.0 * np.arange(nk) / nk
+    ramp[-40:] *= 3.0
+    kb = I.f32_to_bf16_bits((k * ramp[:, None]).astype(np.float32))
+    vb = I.normal_bf16("aresc.v", (nk, H))
+    cnt = _rescale_count(O.bf16_to_f64(qb), O.bf16_to_f64(kb))
+    assert (cnt >= 2).mean() > 0.5 and cnt.max() >= 3, f"too few rescales: {np.bincount(cnt.ravel())}"
+    assert _score_bound(O.bf16_to_f64(qb), O.bf16_to_f64(kb)) > 30.0
+    q, k_d, v_d = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    o = poison((rows, H))
+    if pieces:
+        half = nk // 2
+        h3.attention(q, q, q, o, rows, heads, groups=[(0, rows, [(k_d, v_d, 0, half), (k_d, v_d, half, nk - half)])])
+    else:
+        h3.attention(q, q, q, o, rows, heads, groups=[(0, rows, [(k_d, v_d, 0, nk)])])
+    torch.cuda.synchronize()
+    ref = O.attention_grouped(O.bf16_to_f64(qb), [(0, rows, [(O.bf16_to_f64(kb), O.bf16_to_f64(vb))])], heads, 128,
+                              rows)
+    assert_parity(f64(o), ref, "o")
+
+
 def _score_bound(q_rows, k_rows):
     """The kernel's per-workgroup form choice, restated from its definition:
     |q| max|k| / sqrt(128) * log2(e) for the largest-norm query row. At most
