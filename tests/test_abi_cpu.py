@@ -39,7 +39,7 @@ def attention_extra(heads, qrows, n_groups=1, qtiles=None):
     qtiles = (qrows + 255) // 256 if qtiles is None else qtiles
     records = min(511, 4 * qtiles * heads)
     return (_align(records * 256 * 130 * 4) + _align(heads * 4)
-            + _align(((qtiles + 1) * heads + 8 * (n_groups + 1) + 512) * 4))
+            + _align(((qtiles + 1) * heads + 8 * (n_groups + 1) + 512) * 4) + _align(16 * 4))
 
 
 def declared_functions():

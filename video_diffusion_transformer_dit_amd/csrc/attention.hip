@@ -38,10 +38,12 @@
 //    the rest. P is rounded to BF16 for the P.V MFMA. The key that sets m
 //    gets p within 2^-19 of 1, so BF16(p) = 1: with one valid key both forms
 //    return that key's value exactly.
-//  * Workgroups are dealt round-robin over the 8 XCDs; work items are remapped
-//    so each XCD walks a contiguous range (consecutive query tiles of one
-//    head), so the workgroups resident on an XCD stream the same K/V through
-//    its L2.
+//  * Workgroups are dealt round-robin over the 8 XCDs, and each claims its
+//    work item from its XCD's ticket counter: an XCD walks a contiguous range
+//    of items (consecutive query tiles of one head), so the workgroups
+//    resident on it stream the same K/V through its L2. The grid holds more
+//    workgroups than items, so an XCD that runs ahead takes over what is left
+//    of the others' ranges at the end instead of idling.
 #include <algorithm>
 #include <atomic>
 #include <cstdio>
@@ -91,7 +93,10 @@ struct AttnArgs {
     int32_t part_records;
     AttnGroup grp[H3_MAX_GROUPS];
     const float *kmax2;      // [heads] largest squared key norm over all segments
-    int32_t *flags;          // per workgroup: 1 = left to the online instance
+    int32_t *flags;          // items the fixed-reference instance left to the online one (queue word 8 of them)
+    int32_t *queue;          // kAttnQueueWords work-queue words, zero when the fixed-reference instance starts
+    int32_t n_items;         // work items of the launch
+    int32_t static_tickets;  // per XCD: tickets dealt by workgroup index; later ones are drawn from the counter
     // Block-sparse (list) mode: q and o point at row 0; segment 0 is the
     // prefix [0, P), segment 1 the target rows [P, P + T). Work items
     // [0, pre_items) are prefix query tiles (dense over both segments; items
@@ -102,6 +107,24 @@ struct AttnArgs {
     int32_t n_kb, pre_tiles, pre_items;
     int64_t prefix_len, tgt_rows;
 };
+
+// Work-queue words: [0, 8) the ticket counter of each XCD, then the count of
+// items left to the online instance, then the online instance's counter.
+constexpr int kQueueDeferred = 8, kQueueOnline = 9;
+static_assert(kAttnQueueWords >= 10, "work-queue words");
+// Work-item dealing of a launch of n items. Launches of fewer than 8 rounds
+// of the chip's slots deal every item by workgroup index (the grid is the n
+// items). Longer ones deal all but the last 96 tickets of each XCD (3 rounds
+// of its 32 slots) that way and let the rest be drawn from the counters, with
+// up to 64 surplus workgroups per XCD: XCDs differ in speed by a few percent
+// under load, which over a long launch adds up to more than an item.
+struct AttnDeal {
+    int grid, static_tickets;
+};
+inline AttnDeal attn_deal(int n) {
+    if (n < 8 * kAttnSlots) return {n, (n + 7) / 8};
+    return {n + std::min(512, (n + 7) / 8 * 8), n / 8 - 96};
+}
 
 // Segment fields held in scalar registers while the segment is streamed.
 struct SegState {
@@ -159,16 +182,64 @@ struct Cursor {
     int li, nxt;
 };
 
+// The work item a workgroup on XCD `xcd` draws (-1: none left); thread 0
+// only. The fixed-reference instance draws its own XCD's items first (word
+// xcd counts the tickets drawn past the static ones; ticket i is item
+// 8 i + xcd), then what is left of the other XCDs' (their counters are read
+// at once, then one with items left is drawn from). The online instance walks the list of items the fixed
+// one left to it, and reads the counts before it draws, so that when nothing
+// was left (the usual case) its workgroups leave without an atomic.
+template <bool FIXED>
+__device__ __forceinline__ int attn_claim(const AttnArgs &a, int xcd) {
+    const int n = a.n_items, s0 = a.static_tickets;
+    if (FIXED) {
+        int item = 8 * (s0 + atomicAdd(a.queue + xcd, 1)) + xcd;
+        if (item < n) return item;
+        int c[8];
+#pragma unroll
+        for (int y = 0; y < 8; ++y)
+            c[y] = __hip_atomic_load(a.queue + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int d = 1; d < 8; ++d) {
+            const int y = (xcd + d) & 7;
+            if (8 * (s0 + c[y]) + y >= n) continue;
+            item = 8 * (s0 + atomicAdd(a.queue + y, 1)) + y;
+            if (item < n) return item;
+        }
+        return -1;
+    }
+    const int left = __hip_atomic_load(a.queue + kQueueDeferred, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int drawn = __hip_atomic_load(a.queue + kQueueOnline, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (drawn >= left) return -1;
+    const int i = atomicAdd(a.queue + kQueueOnline, 1);
+    return i < left ? a.flags[i] : -1;
+}
+
 // The dense / grouped kernel (SPARSE = false) and the block-sparse list mode
 // (SPARSE = true) share every step; list mode only changes which query tile a
 // workgroup owns and which key tiles of segment 1 it visits.
+//
+// A workgroup takes one work item as it starts. Workgroups are dealt
+// round-robin over the 8 XCDs, so workgroup b is the (b / 8)-th of XCD b % 8.
+// In the fixed-reference instance, the first static_tickets of each XCD take
+// ticket b / 8 (item b) at once; later ones draw theirs. With surplus
+// workgroups, an XCD that runs ahead starts its next workgroups sooner and
+// takes over the items of slower ones; the surplus finds nothing left and
+// leaves. No workgroup waits on another.
 template <bool SPARSE, bool FIXED, bool MULTI>
 __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) {
-    int ri = 0;  // the workgroup's range (wave-uniform; range 0 unless MULTI)
+    int item = blockIdx.x;
+    if (!FIXED || (int)(blockIdx.x >> 3) >= a.static_tickets) {
+        __shared__ int claimed;
+        if (threadIdx.x == 0) claimed = attn_claim<FIXED>(a, blockIdx.x & 7);
+        __syncthreads();
+        item = __builtin_amdgcn_readfirstlane(claimed);
+        if (item < 0) return;
+    }
+    int ri = 0;  // the item's range (wave-uniform; range 0 unless MULTI)
     if (MULTI)
-        while (ri + 1 < a.n_ranges && (int)blockIdx.x >= a.rng_end[ri]) ++ri;
+        while (ri + 1 < a.n_ranges && item >= a.rng_end[ri]) ++ri;
     const AttnGroup &G = a.grp[MULTI ? a.rng_group[ri] : 0];
-    if (!FIXED && a.flags[blockIdx.x] == 0) return;  // done by the fixed-reference instance
     constexpr int KB = BKV * 16;  // 16-byte chunks per K tile buffer (16 KB)
     constexpr int VB = D * 8;     // chunks per V^T tile buffer (16 KB)
     // K buffers 0, 1 then V^T buffers 0, 1.
@@ -190,12 +261,9 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     int lcount = 0;
     int pieces = 1, piece = 0, rec = 0;  // key-range pieces of the item; this one; its partial record
     {
-        int bid = blockIdx.x;
+        int bid = item;
         if (SPARSE && bid < a.pre_items) {
-            if (bid >= a.heads * a.pre_tiles) {  // idle item (whole workgroup)
-                if (FIXED && threadIdx.x == 0) a.flags[blockIdx.x] = 0;
-                return;
-            }
+            if (bid >= a.heads * a.pre_tiles) return;  // idle item
             head = bid / a.pre_tiles;
             const int64_t q0 = (int64_t)(bid - head * a.pre_tiles) * BQ;
             qbase = G.q + q0 * a.ld_q;
@@ -215,10 +283,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
                 const int local = bid - item0;
                 const int idx = (local % 8) * (span / 8) + local / 8;
                 pieces = a.rng_split[ri];
-                if (idx >= a.rng_count[ri] * pieces) {  // padding item (whole workgroup)
-                    if (FIXED && threadIdx.x == 0) a.flags[blockIdx.x] = 0;
-                    return;
-                }
+                if (idx >= a.rng_count[ri] * pieces) return;  // padding item
                 piece = idx % pieces;
                 rec = idx;
                 bid = a.rng_first[ri] + idx / pieces;
@@ -288,8 +353,10 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
         if (lane == 0) vote[wave] = ok;
         __syncthreads();
         const bool wg_ok = vote[0] && vote[1] && vote[2] && vote[3];
-        if (t == 0) a.flags[blockIdx.x] = wg_ok ? 0 : 1;
-        if (!wg_ok) return;
+        if (!wg_ok) {  // left to the online instance
+            if (t == 0) a.flags[atomicAdd(a.queue + kQueueDeferred, 1)] = item;
+            return;
+        }
     }
     // Register-class hints (empty asm, no instruction): Q and O live in AGPRs,
     // which the MFMA reads directly, leaving the VGPRs for scores and P.
@@ -793,6 +860,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     }
 }
 
+
 // Largest squared key norm per head over rows [0, rows) of k, merged into
 // kmax2[head] (non-negative FP32 bit patterns compare like unsigned integers,
 // so an integer atomic maximum merges them). Workgroup (x, y) owns the rows
@@ -1005,6 +1073,10 @@ void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_
     a.scale_log2 = scale * 1.4426950408889634f;
     a.kmax2 = reinterpret_cast<const float *>(ws + plan.kmax_off);
     a.flags = reinterpret_cast<int32_t *>(ws + plan.flags_off);
+    a.queue = reinterpret_cast<int32_t *>(ws + plan.queue_off);
+    a.n_items = sch.items;
+    const AttnDeal deal = attn_deal(sch.items);
+    a.static_tickets = deal.static_tickets;
     a.part = reinterpret_cast<float *>(ws + plan.part_off);
     a.part_records = sch.split_items * sch.pieces;
     a.n_ranges = sch.n;
@@ -1049,7 +1121,7 @@ void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_
         a.rng_split[i] = sch.split[i];
         if (sch.split[i] > 1) split_range = i;
     }
-    const dim3 grid((unsigned)sch.items);
+    const dim3 grid((unsigned)deal.grid);
     if (sch.n == 1 && split_range < 0 && sch.group[0] != 0) {  // the single-range kernel reads grp[0]
         a.grp[0] = a.grp[sch.group[0]];
         a.rng_group[0] = 0;
@@ -1214,6 +1286,7 @@ void launch_sparse_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k,
     a.scale_log2 = scale * 1.4426950408889634f;
     a.kmax2 = reinterpret_cast<const float *>(ws + plan.kmax_off);
     a.flags = reinterpret_cast<int32_t *>(ws + plan.flags_off);
+    a.queue = reinterpret_cast<int32_t *>(ws + plan.queue_off);
     for (int s = 0; s < 2; ++s) {
         const VtSeg &e = plan.seg[plan.map[0][s]];
         G.sk[s] = k + g.seg[s].begin * ld_k;
@@ -1231,8 +1304,11 @@ void launch_sparse_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k,
     a.rng_split[0] = 1;
     a.prefix_len = prefix_len;
     a.tgt_rows = T;
-    const unsigned grid = (unsigned)(a.pre_items + G.tiles_per_head * heads);
-    a.rng_end[0] = (int32_t)grid;
+    a.n_items = a.pre_items + G.tiles_per_head * heads;
+    a.rng_end[0] = a.n_items;
+    const AttnDeal deal = attn_deal(a.n_items);
+    a.static_tickets = deal.static_tickets;
+    const unsigned grid = (unsigned)deal.grid;
     attention_fwd_kernel<true, true, false><<<dim3(grid), kThreads, 0, stream>>>(a);
     attention_fwd_kernel<true, false, false><<<dim3(grid), kThreads, 0, stream>>>(a);
     launch_zero_rows(o, ld_o, (int64_t)heads * D, valid_len, L_buf, stream);

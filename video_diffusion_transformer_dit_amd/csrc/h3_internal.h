@@ -40,6 +40,8 @@ struct VtSeg {
 // range is padded to a multiple of 8 items so that it starts on XCD 0 (also
 // a single range cut into pieces).
 constexpr int kAttnSlots = 256;
+// int32 words of an attention launch's work queue (ticket counters).
+constexpr int kAttnQueueWords = 16;
 // Fixed cost of one work item (Q loads, the first tiles' latency, the
 // epilogue), in key tiles of the steady loop: about 15 us against 1.8 us per
 // tile, measured on full rounds of short items.
@@ -65,7 +67,8 @@ struct VtPlan {
     int map[H3_MAX_GROUPS][H3_MAX_SEGMENTS];  // (group, segment) -> seg index
     int64_t part_off;     // byte offset of the split items' partial results (FP32 O, then (m, l) per row)
     int64_t kmax_off;     // byte offset of the per-head key norm maxima
-    int64_t flags_off;    // byte offset of one int32 per attention workgroup
+    int64_t flags_off;    // byte offset of one int32 per attention work item (the deferred-item list)
+    int64_t queue_off;    // byte offset of the launch's kAttnQueueWords work-queue words
     size_t bytes;
 };
 // groups == NULL plans one own segment [0, dense_len).

@@ -295,6 +295,7 @@ void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads
     }
     out->flags_off = 0;
     out->part_off = 0;
+    out->queue_off = 0;
     if (out->n > 0 || staged) {
         auto align = [](size_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; };
         // Partial results of the items cut into pieces: a partial round has
@@ -313,6 +314,8 @@ void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads
         // (pieces add fewer than 512 items; every range may be padded by 7)
         out->flags_off = (int64_t)out->bytes;
         out->bytes += align((size_t)((qtiles + 1) * heads + 8 * (n_launch_groups + 1) + 512) * 4);
+        out->queue_off = (int64_t)out->bytes;
+        out->bytes += align((size_t)kAttnQueueWords * 4);
     }
 }
 
