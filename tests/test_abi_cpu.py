@@ -357,7 +357,9 @@ def test_linear_stream_k_plan_and_workspace_checks():
     """The stream-K tail of h3_linear: which shapes split their last round of
     tiles (a tail of at most 4/5 of the 256 slots whose idle share, in K
     stages, is worth at least 55 stages), the partial-sum area that needs
-    (two 256 x 256 FP32 slots per range), and the workspace checks."""
+    (two 256 x 256 FP32 slots per range), the 256 bytes of tile counters of
+    launches with 8 rounds of data-parallel tiles or more, and the workspace
+    checks."""
     MB256 = 256 * 256 * 4
     # 4,096 rows x 5,376 columns: 16 x 21 = 336 tiles, a tail of 80 tiles.
     # K 21,504 (the down projection, 336 stages): 336 x 176/256 = 231 stages
@@ -367,10 +369,18 @@ def test_linear_stream_k_plan_and_workspace_checks():
     assert h3.linear_workspace_bytes(4096, 5376, 5376, h3.H3_EPI_RESIDUAL) == 256 * 2 * MB256
     # 5,424 rows, QKV projection: 22 x 63 = 1,386 tiles, tail 106, 84 x 150/256 = 49 stages idle -> no split
     assert h3.linear_workspace_bytes(5424, 16128, 5376, h3.H3_EPI_STORE) == 0
-    # 4,096 rows, the same: 16 x 168 = 2,688 tiles, tail 128, 84 x 128/256 = 42 stages idle -> no split
-    assert h3.linear_workspace_bytes(4096, 43008, 5376, h3.H3_EPI_SWIGLU) == 0
+    # 4,096 rows, the same: 16 x 168 = 2,688 tiles, tail 128, 84 x 128/256 = 42 stages idle -> no split; but
+    # 2,688 data-parallel tiles are 8 rounds or more: 256 bytes of tile counters
+    assert h3.linear_workspace_bytes(4096, 43008, 5376, h3.H3_EPI_SWIGLU) == 256
     # a tail of more than 4/5 of the slots is not split: 58,758 rows x 5,376 = 230 x 21 = 4,830 tiles, tail 222
-    assert h3.linear_workspace_bytes(58758, 5376, 21504, h3.H3_EPI_RESIDUAL) == 0
+    # (the counters only)
+    assert h3.linear_workspace_bytes(58758, 5376, 21504, h3.H3_EPI_RESIDUAL) == 256
+    # tile counters from exactly 8 rounds of data-parallel tiles on: 2,048 rows x 65,536 = 8 x 256 tiles
+    assert h3.linear_workspace_bytes(2048, 65536, 1024, h3.H3_EPI_STORE) == 256
+    assert h3.linear_workspace_bytes(2048, 65280, 1024, h3.H3_EPI_STORE) == 0
+    # both: 4,096 x 34,048 = 16 x 133 = 2,128 tiles, K 21,504: the tail of 80 splits over 256 ranges and the
+    # other 2,048 tiles draw their last rounds; the counters follow the partial sums
+    assert h3.linear_workspace_bytes(4096, 34048, 21504, h3.H3_EPI_STORE) == 256 * 2 * MB256 + 256
     # whole rounds: 2,048 rows x 8,192 columns = 8 x 32 = 256 tiles
     assert h3.linear_workspace_bytes(2048, 8192, 21504, h3.H3_EPI_STORE) == 0
     # fewer tiles than slots: 1,000 x 2,048 = 32 tiles, K 7,552 = 118 stages: 3,776 units in 256 ranges

@@ -331,6 +331,52 @@ def test_linear_stream_k_tail(epi, M, Mv, N, K):
     assert_zero_rows(c, Mv, "c")
 
 
+@pytest.mark.parametrize("epi,Mv,N,K", [(h3.H3_EPI_STORE, 2000, 65536, 192), (h3.H3_EPI_SWIGLU, 1900, 65536, 128),
+                                        (h3.H3_EPI_STORE, 2000, 65792, 3840)])
+def test_linear_drawn_tiles(epi, Mv, N, K):
+    """Launches of 8 rounds of output tiles or more: the last tiles of each
+    XCD's range are drawn from counters in the workspace, by more workgroups
+    than tiles. A tile's result does not depend on which workgroup computes
+    it, so the output equals, bit for bit, the call without a workspace (every
+    tile taken by workgroup index), also on a second call over the first
+    call's counters; sampled rows (the last ones among them) against the
+    oracle. 2,048 tiles (8 x 256, and 8 x 256 SwiGLU tiles of 128 columns),
+    and 2,056 tiles of 60 stages whose last 8 are cut into stream-K ranges
+    while the other 2,048 draw their last rounds (against the unsplit call
+    with the FP32 summation slack)."""
+    _say(f"linear drawn tiles epi={epi} Mv={Mv} N={N} K={K}")
+    need = h3.linear_workspace_bytes(Mv, N, K, epi)
+    split = need > 256
+    assert need >= 256, "the shape must draw tiles"
+    M = Mv + 5
+    ab = I.normal_bf16("ld.a", (M, K))
+    wb = I.normal_bf16("ld.w", (N, K), 0.05)
+    bb = I.normal_bf16("ld.b", (N,), 0.5)
+    cols = N // 2 if epi == h3.H3_EPI_SWIGLU else N
+    a, w, b = dev_bf16(ab), dev_bf16(wb), dev_bf16(bb)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")  # stale contents must not matter
+    c0 = poison((M, cols))
+    h3.linear(a, w, c0, Mv, epi, bias=b)
+    outs = []
+    for _ in range(2):
+        c = poison((M, cols))
+        h3.linear(a, w, c, Mv, epi, bias=b, workspace=ws)
+        outs.append(c)
+    torch.cuda.synchronize()
+    slack = BF16_SLACK if epi == h3.H3_EPI_SWIGLU else 0.0
+    for i, c in enumerate(outs):
+        if split:
+            assert_parity(f64(c)[:Mv], f64(c0)[:Mv], f"c (call {i}) vs every tile by index", slack=slack)
+        else:
+            np.testing.assert_array_equal(bits(c), bits(c0), err_msg=f"call {i}: drawn tiles differ")
+        assert_zero_rows(c, Mv, "c")
+    np.testing.assert_array_equal(bits(outs[1]), bits(outs[0]), err_msg="second call differs")
+    rows = np.unique(np.concatenate([np.arange(0, Mv, 97), np.arange(Mv - 8, Mv)]))
+    u = O.linear(O.bf16_to_f64(ab[rows]), O.bf16_to_f64(wb), O.bf16_to_f64(bb))
+    ref = O.swiglu(u, N // 2) if epi == h3.H3_EPI_SWIGLU else u
+    assert_parity(f64(outs[0])[rows], ref, "c (sampled rows)", slack=slack)
+
+
 # ---------------------------------------------------------------------------
 # attention
 # ---------------------------------------------------------------------------

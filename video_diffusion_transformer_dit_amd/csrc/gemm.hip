@@ -60,6 +60,11 @@ struct GemmArgs {
     // 256 x 256 slots per range) for the fix-up pass.
     int32_t dp_tiles, sk_tiles, sk_groups;
     float *part;
+    // Tile dealing: on each XCD, the first static_tickets workgroups take the
+    // tile of their index; the later ones draw one from the XCD's counter in
+    // `queue` (queue == nullptr: none draw).
+    int32_t *queue;
+    int32_t static_tickets;
 };
 
 // LDS operand tile: row r holds 8 chunks of 16 B (64 k values); chunk c of
@@ -274,14 +279,57 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &p, uint4 *smem, int tm
     }
 }
 
-// Data-parallel tiles: one whole tile per workgroup, the first dp_tiles tiles
-// of the grouped order, XCD-contiguous.
+// The tile (a workgroup index of the XCD-contiguous order) a drawing
+// workgroup on XCD `xcd` takes, -1 when none is left: the XCD's own counter
+// first (ticket i is tile 8 i + xcd, after the static tickets), then, once
+// that is used up, what is left of the other XCDs' (their counters read at
+// once, then one with tiles left drawn from). Thread 0 draws; the result
+// reaches the other waves through the first word of the LDS ring, between
+// barriers.
+__device__ __forceinline__ int gemm_draw(const GemmArgs &p, int xcd, uint4 *smem) {
+    if (threadIdx.x == 0) {
+        const int n = p.dp_tiles, s0 = p.static_tickets;
+        int tile = 8 * (s0 + atomicAdd(p.queue + xcd, 1)) + xcd;
+        if (tile >= n) {
+            int c[8];
+#pragma unroll
+            for (int y = 0; y < 8; ++y)
+                c[y] = __hip_atomic_load(p.queue + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            tile = -1;
+#pragma unroll
+            for (int d = 1; d < 8; ++d) {
+                const int y = (xcd + d) & 7;
+                if (tile >= 0 || 8 * (s0 + c[y]) + y >= n) continue;
+                const int u = 8 * (s0 + atomicAdd(p.queue + y, 1)) + y;
+                if (u < n) tile = u;
+            }
+        }
+        reinterpret_cast<int *>(smem)[0] = tile;
+    }
+    __syncthreads();
+    const int tile = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int *>(smem)[0]);
+    __syncthreads();  // every wave has read it before the ring is loaded
+    return tile;
+}
+
+// Data-parallel tiles: the first dp_tiles tiles of the grouped order,
+// XCD-contiguous (workgroups are dealt round-robin over the 8 XCDs, so
+// workgroup b is the (b / 8)-th of XCD b % 8 and takes tile b). In long
+// launches the last tiles of each XCD's range are drawn instead, by more
+// workgroups than tiles: an XCD that runs ahead (XCDs differ by a few percent
+// in speed under load) then takes over the end of slower XCDs' ranges
+// instead of idling, and the surplus workgroups find nothing and leave.
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
     // LDS: the ring of five 32 KB operand tiles (160 KB).
     __shared__ uint4 smem[5 * kTileChunks];
+    int bid = blockIdx.x;
+    if ((int)(blockIdx.x >> 3) >= p.static_tickets) {
+        bid = gemm_draw(p, blockIdx.x & 7, smem);
+        if (bid < 0) return;
+    }
     int tm, tn;
-    gemm_tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, p.dp_tiles, tm, tn);
+    gemm_tile_coords(bid, p.tiles_m, p.tiles_n, p.group_m, p.dp_tiles, tm, tn);
     gemm_tile<EPI, false>(p, smem, tm, tn, 0, (int)(p.K / BK), nullptr);
 }
 
@@ -395,7 +443,15 @@ void launch_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ld
     p.sk_tiles = sk ? plan.sk_tiles : 0;
     p.sk_groups = sk ? plan.sk_groups : 0;
     p.part = static_cast<float *>(workspace);
-    const dim3 grid((unsigned)p.dp_tiles);
+    p.queue = nullptr;
+    p.static_tickets = (p.dp_tiles + 7) / 8;
+    dim3 grid((unsigned)p.dp_tiles);
+    if (workspace != nullptr && plan.deal) {
+        p.queue = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(workspace) + plan.queue_off);
+        p.static_tickets = plan.static_tickets;
+        grid = dim3((unsigned)plan.grid);
+        launch_zero_rows(reinterpret_cast<uint16_t *>(p.queue), 128, 128, 0, 1, stream);  // the 8 counters
+    }
     if (p.dp_tiles > 0) {
         switch (epilogue) {
             case H3_EPI_RESIDUAL: gemm_bf16_kernel<H3_EPI_RESIDUAL><<<grid, kThreads, 0, stream>>>(p); break;

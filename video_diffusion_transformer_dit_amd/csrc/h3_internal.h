@@ -100,17 +100,28 @@ void sparse_vt_group(int64_t valid_len, int64_t prefix_len, h3_qgroup *g);
 // kSkMinStages stages each and less than one tile (so a range touches at
 // most two tiles), whose FP32 partial sums a fix-up pass adds; the other
 // dp_tiles tiles run one per workgroup. sk_groups == 0: no tail split.
+//
+// Tile dealing: when the dp_tiles fill at least kGemmDealRounds rounds, the
+// last W = max(96, T/12) of each XCD's T tiles are drawn by workgroups from
+// a per-XCD counter (W + W/2 drawing workgroups per XCD; grid workgroups in
+// all), which lets faster XCDs take over the end of slower ones' ranges. The
+// counters sit at queue_off in the workspace (256 bytes).
 constexpr int kGemmSlots = 256;
 constexpr int kSkMinStages = 8;
 constexpr int kSkWorthStages = 55;
+constexpr int kGemmDealRounds = 8;
 struct GemmPlan {
     int32_t tiles_m, tiles_n, tiles, stages;
     int32_t dp_tiles, sk_tiles, sk_groups;
     size_t part_bytes;  // 2 slots of 256 x 256 FP32 per range
+    bool deal;          // tiles drawn from counters at the end of each XCD's range
+    int32_t static_tickets, grid;
+    size_t queue_off;
+    size_t ws_bytes;    // workspace the plan needs (partial sums, then the counters)
 };
 GemmPlan gemm_plan(int64_t M_valid, int64_t N, int64_t K, int32_t epilogue);
-// Largest part_bytes of any plan with at most M_buf rows, for these (N, K, epilogue).
-size_t gemm_part_bytes_max(int64_t M_buf, int64_t N, int64_t K, int32_t epilogue);
+// Largest ws_bytes of any plan with at most M_buf rows, for these (N, K, epilogue).
+size_t gemm_ws_bytes_max(int64_t M_buf, int64_t N, int64_t K, int32_t epilogue);
 
 // Byte offsets and row strides of the block's workspace buffers.
 struct WsLayout {

@@ -219,6 +219,24 @@ void attn_schedule(const h3_qgroup *groups, int n_groups, int64_t dense_len, int
     out->items = items;
 }
 
+// The stream-K split of the last round, if it pays.
+static void gemm_plan_tail(GemmPlan &g) {
+    const int32_t tail = g.tiles % kGemmSlots;
+    if (tail == 0 || 5 * tail > 4 * kGemmSlots) return;
+    // The split costs about as much as 55 stages of the last round (the
+    // partial sums' traffic, the fix-up pass, two more launches; measured on
+    // the block's projections at 4,096 and 5,424 rows): take it only where the
+    // idle share of the last round is worth more.
+    if ((int64_t)g.stages * (kGemmSlots - tail) < (int64_t)kSkWorthStages * kGemmSlots) return;
+    const int64_t units = (int64_t)tail * g.stages;
+    const int32_t groups = (int32_t)std::min<int64_t>(kGemmSlots, units / kSkMinStages);
+    if (groups <= tail) return;  // no range would be shorter than a tile
+    g.dp_tiles = g.tiles - tail;
+    g.sk_tiles = tail;
+    g.sk_groups = groups;
+    g.part_bytes = (size_t)groups * 2 * 256 * 256 * 4;
+}
+
 GemmPlan gemm_plan(int64_t M_valid, int64_t N, int64_t K, int32_t epilogue) {
     GemmPlan g = {};
     g.tiles_m = (int32_t)((std::max<int64_t>(M_valid, 0) + 255) / 256);
@@ -226,32 +244,25 @@ GemmPlan gemm_plan(int64_t M_valid, int64_t N, int64_t K, int32_t epilogue) {
     g.tiles = g.tiles_m * g.tiles_n;
     g.stages = (int32_t)(K / 64);
     g.dp_tiles = g.tiles;
-    const int32_t tail = g.tiles % kGemmSlots;
-    if (tail == 0 || 5 * tail > 4 * kGemmSlots) return g;
-    // The split costs about as much as 55 stages of the last round (the
-    // partial sums' traffic, the fix-up pass, two more launches; measured on
-    // the block's projections at 4,096 and 5,424 rows): take it only where the
-    // idle share of the last round is worth more.
-    if ((int64_t)g.stages * (kGemmSlots - tail) < (int64_t)kSkWorthStages * kGemmSlots) return g;
-    const int64_t units = (int64_t)tail * g.stages;
-    const int32_t groups = (int32_t)std::min<int64_t>(kGemmSlots, units / kSkMinStages);
-    if (groups <= tail) return g;  // no range would be shorter than a tile
-    g.dp_tiles = g.tiles - tail;
-    g.sk_tiles = tail;
-    g.sk_groups = groups;
-    g.part_bytes = (size_t)groups * 2 * 256 * 256 * 4;
+    gemm_plan_tail(g);
+    g.ws_bytes = g.part_bytes;
+    if (g.dp_tiles >= kGemmDealRounds * kGemmSlots) {
+        const int32_t T = g.dp_tiles / 8, W = std::max(3 * kGemmSlots / 8, T / 12);
+        g.deal = true;
+        g.static_tickets = T - W;
+        g.grid = 8 * (g.static_tickets + W + W / 2);
+        g.queue_off = (g.part_bytes + 255) / 256 * 256;
+        g.ws_bytes = g.queue_off + 256;
+    }
     return g;
 }
 
-size_t gemm_part_bytes_max(int64_t M_buf, int64_t N, int64_t K, int32_t epilogue) {
-    // part_bytes grows with the tail's units, at most kGemmSlots ranges: bound
-    // it by the plan of every tile count up to M_buf's.
+size_t gemm_ws_bytes_max(int64_t M_buf, int64_t N, int64_t K, int32_t epilogue) {
+    // The partial sums grow with the tail's units (at most kGemmSlots ranges)
+    // and need not grow with M: take the plan of every tile count up to M_buf's.
     const int64_t tm_max = (std::max<int64_t>(M_buf, 0) + 255) / 256;
     size_t best = 0;
-    for (int64_t tm = 1; tm <= tm_max; ++tm) {
-        best = std::max(best, gemm_plan(tm * 256, N, K, epilogue).part_bytes);
-        if (best >= (size_t)kGemmSlots * 2 * 256 * 256 * 4) break;
-    }
+    for (int64_t tm = 1; tm <= tm_max; ++tm) best = std::max(best, gemm_plan(tm * 256, N, K, epilogue).ws_bytes);
     return best;
 }
 
@@ -322,10 +333,10 @@ void vt_plan(const h3_qgroup *groups, int n_groups, int64_t dense_len, int heads
 // Partial-sum area for the block's four projections (run one after another).
 static size_t block_gemm_part_bytes(const h3_dims *d, int64_t L_buf) {
     const int64_t H = d->hidden, F = d->ffn;
-    return std::max({gemm_part_bytes_max(L_buf, 3 * H, H, H3_EPI_STORE),
-                     gemm_part_bytes_max(L_buf, H, H, H3_EPI_RESIDUAL),
-                     gemm_part_bytes_max(L_buf, 2 * F, H, H3_EPI_SWIGLU),
-                     gemm_part_bytes_max(L_buf, H, F, H3_EPI_RESIDUAL)});
+    return std::max({gemm_ws_bytes_max(L_buf, 3 * H, H, H3_EPI_STORE),
+                     gemm_ws_bytes_max(L_buf, H, H, H3_EPI_RESIDUAL),
+                     gemm_ws_bytes_max(L_buf, 2 * F, H, H3_EPI_SWIGLU),
+                     gemm_ws_bytes_max(L_buf, H, F, H3_EPI_RESIDUAL)});
 }
 
 bool ws_layout(const h3_dims *d, int64_t L_buf, const h3_qgroup *groups, int n_groups, WsLayout *out) {
@@ -657,7 +668,7 @@ int h3_check_swiglu_lora(const uint16_t *u, int64_t ld_u, const uint16_t *du, in
 
 size_t h3_linear_workspace_bytes(int64_t M_valid, int64_t N, int64_t K, int32_t epilogue) {
     if (M_valid < 0 || N <= 0 || K <= 0 || epilogue < H3_EPI_STORE || epilogue > H3_EPI_SWIGLU) return 0;
-    return gemm_plan(M_valid, N, K, epilogue).part_bytes;
+    return gemm_plan(M_valid, N, K, epilogue).ws_bytes;
 }
 
 int h3_check_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ldw, const uint16_t *bias,
@@ -696,7 +707,7 @@ int h3_check_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t l
         if (!same(mr, mc) && overlap(mr, mc)) return H3_ERR_ALIAS;
     }
     if (workspace != nullptr) {
-        const size_t need = gemm_plan(M_valid, N, K, epilogue).part_bytes;
+        const size_t need = gemm_plan(M_valid, N, K, epilogue).ws_bytes;
         if (ws_bytes < need) return H3_ERR_WORKSPACE;
         if ((reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0) return H3_ERR_ALIGN;
         if (need > 0) {
