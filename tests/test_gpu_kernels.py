@@ -454,6 +454,45 @@ def test_attention_fixed_and_online_workgroups_in_one_call():
     assert_zero_rows(o, V, "o")
 
 
+def test_attention_long_launch_draws_items_and_defers_online_tiles():
+    """A launch of 8 rounds of work items or more (42 heads x 49 query tiles =
+    2,058 items): each XCD's last items are drawn from counters by surplus
+    workgroups, and query tiles whose score bound rules out the fixed
+    reference (their q scaled by 8; one of them among the drawn items at the
+    end of the order) go to the online instance through the deferred-item
+    list. Sampled rows of every kind against the oracle."""
+    heads, V = 42, 12500
+    L = V + 44
+    H = heads * 128
+    _say(f"attention long launch heads={heads} V={V}")
+    q = O.bf16_to_f64(I.normal_bf16("along.q", (L, H)))
+    sharp = [(256, 512), (6144, 6400), (12288, 12500)]   # query tiles 1, 24 and the last one
+    for a, b in sharp:
+        q[a:b] *= 8.0
+    qb = I.f32_to_bf16_bits(q.astype(np.float32))
+    kb = I.normal_bf16("along.k", (L, H))
+    vb = I.normal_bf16("along.v", (L, H))
+    kf = O.bf16_to_f64(kb[:V])
+    for a, b in sharp:
+        assert _score_bound(O.bf16_to_f64(qb[a:b]), kf) > 30.0
+    for a in (0, 512, 6400, 12032):
+        assert _score_bound(O.bf16_to_f64(qb[a:a + 256]), kf) <= 30.0
+    o = poison((L, H))
+    h3.attention(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), o, V, heads)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, V, 211), np.arange(256, 512, 37), np.arange(6144, 6400, 41),
+                                     np.arange(V - 12, V)]))
+    ref = O.attention(O.bf16_to_f64(qb[rows]), O.bf16_to_f64(kb[:V]), O.bf16_to_f64(vb[:V]), heads, 128)
+    got = f64(o)[rows]
+    is_sharp = np.zeros(len(rows), bool)
+    for a, b in sharp:
+        is_sharp |= (rows >= a) & (rows < b)
+    assert is_sharp.sum() >= 10 and (~is_sharp).sum() >= 40
+    assert_parity(got[is_sharp], ref[is_sharp], "o (online tiles)")
+    assert_parity(got[~is_sharp], ref[~is_sharp], "o (fixed-reference tiles)")
+    assert_zero_rows(o, V, "o")
+
+
 def _rescale_count(q_rows, k_rows, slack=40.0):
     """Per (row, head): how often the online form must raise its softmax
     reference, restated from its rule: the reference starts at the row's
