@@ -215,10 +215,10 @@ size_t h3_block_workspace_bytes(const h3_dims *dims, int64_t L_buf,
  *   H3_WS_G   g   (cols F)
  *   H3_WS_VT  attention's V^T staging (see h3_attention_workspace_bytes);
  *             its "row stride" entry holds its size in bytes.
- *   H3_WS_GEMM the projections' stream-K partial sums (see
- *             h3_linear_workspace_bytes), the largest any of the four needs
- *             at up to L_buf rows; its "row stride" entry holds its size in
- *             bytes (0 when none would split).                           */
+ *   H3_WS_GEMM the projections' workspace (stream-K partial sums and tile
+ *             counters, see h3_linear_workspace_bytes), the largest any of
+ *             the four needs at up to L_buf rows; its "row stride" entry
+ *             holds its size in bytes (0 when none needs any).           */
 enum { H3_WS_H = 0, H3_WS_QKV = 1, H3_WS_O = 2, H3_WS_X1 = 3, H3_WS_H2 = 4, H3_WS_G = 5,
        H3_WS_VT = 6, H3_WS_GEMM = 7, H3_WS_COUNT = 8 };
 int h3_block_workspace_layout(const h3_dims *dims, int64_t L_buf,
@@ -249,7 +249,12 @@ int h3_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_t ld_
                  void *workspace, size_t ws_bytes, void *stream);
 
 /* Workspace bytes h3_attention needs: for every distinct segment (dense: the
- * valid rows), heads * 128 * round_up(len, 64) BF16 values. 0 on bad input. */
+ * valid rows) not staged by h3_kv_stage, heads * 128 * round_up(len, 64) BF16
+ * values; then the partial records of query tiles cut into key-range pieces,
+ * the per-head key norm maxima, one int32 per work item (the items left to
+ * the online-softmax form) and 256 bytes of work-queue counters, each area
+ * 256-byte aligned. The call clears or writes all of it before reading it.
+ * 0 on bad input. */
 size_t h3_attention_workspace_bytes(int64_t valid_len, int32_t heads,
                                     const h3_qgroup *groups, int32_t n_groups);
 
@@ -410,16 +415,24 @@ int h3_linear(const uint16_t *a, int64_t lda, const uint16_t *w, int64_t ldw,
               int32_t n_mod_groups, const int32_t *mod_idx,
               void *workspace, size_t ws_bytes, void *stream);
 
-/* Workspace bytes h3_linear uses to split its last, partial round of output
- * tiles (stream-K tail) for M_valid rows: 0 when no split applies. With a
- * workspace of at least this size (256-byte aligned, overlapping no operand)
- * the tiles of a last round that fills at most 4/5 of the chip's 256
- * workgroup slots, and leaves idle slot time worth at least 55 K stages of
- * 64 (K/64 x the idle share), are cut into equal ranges of K stages over all
- * slots; each
- * range leaves FP32 partial sums there and a fix-up pass adds them in K
- * order and applies the epilogue. workspace NULL: one workgroup per tile.
- * A non-NULL workspace smaller than this size is H3_ERR_WORKSPACE. */
+/* Workspace bytes h3_linear uses for M_valid rows: 0 when it needs none.
+ * With a workspace of at least this size (256-byte aligned, overlapping no
+ * operand):
+ *  - the tiles of a last, partial round that fills at most 4/5 of the chip's
+ *    256 workgroup slots, and leaves idle slot time worth at least 55 K
+ *    stages of 64 (K/64 x the idle share), are cut into equal ranges of K
+ *    stages over all slots (stream-K tail); each range leaves FP32 partial
+ *    sums there and a fix-up pass adds them in K order and applies the
+ *    epilogue;
+ *  - when the other tiles fill at least 8 rounds of the slots, the last
+ *    twelfth of each XCD's share of them (at least 96) is drawn at run time
+ *    from per-XCD counters kept in the 256 bytes after the partial sums, so
+ *    that XCDs running faster under load take over the end of slower ones'
+ *    shares. The counters are cleared inside the call.
+ * The result does not depend on the workspace beyond the FP32 summation
+ * order of split tiles. workspace NULL: one workgroup per tile, taken by
+ * workgroup index. A non-NULL workspace smaller than this size is
+ * H3_ERR_WORKSPACE. Calls that overlap in time must not share a workspace. */
 size_t h3_linear_workspace_bytes(int64_t M_valid, int64_t N, int64_t K, int32_t epilogue);
 
 /* ---------------------------------------------------------------------------
