@@ -38,12 +38,13 @@
 //    the rest. P is rounded to BF16 for the P.V MFMA. The key that sets m
 //    gets p within 2^-19 of 1, so BF16(p) = 1: with one valid key both forms
 //    return that key's value exactly.
-//  * Workgroups are dealt round-robin over the 8 XCDs, and each claims its
-//    work item from its XCD's ticket counter: an XCD walks a contiguous range
-//    of items (consecutive query tiles of one head), so the workgroups
-//    resident on it stream the same K/V through its L2. The grid holds more
-//    workgroups than items, so an XCD that runs ahead takes over what is left
-//    of the others' ranges at the end instead of idling.
+//  * Workgroups are dealt round-robin over the 8 XCDs, and work items are
+//    remapped so each XCD walks a contiguous range (consecutive query tiles
+//    of one head): the workgroups resident on an XCD stream the same K/V
+//    through its L2. In long launches the last rounds of each XCD's range are
+//    drawn from a per-XCD ticket counter by more workgroups than items, so an
+//    XCD that runs ahead takes over what is left of the others' ranges
+//    instead of idling.
 #include <algorithm>
 #include <atomic>
 #include <cstdio>
@@ -186,9 +187,10 @@ struct Cursor {
 // only. The fixed-reference instance draws its own XCD's items first (word
 // xcd counts the tickets drawn past the static ones; ticket i is item
 // 8 i + xcd), then what is left of the other XCDs' (their counters are read
-// at once, then one with items left is drawn from). The online instance walks the list of items the fixed
-// one left to it, and reads the counts before it draws, so that when nothing
-// was left (the usual case) its workgroups leave without an atomic.
+// at once, then one with items left is drawn from). The online instance
+// walks the list of items the fixed one left to it, and reads the counts
+// before it draws, so that when nothing was left (the usual case) its
+// workgroups leave without an atomic.
 template <bool FIXED>
 __device__ __forceinline__ int attn_claim(const AttnArgs &a, int xcd) {
     const int n = a.n_items, s0 = a.static_tickets;
@@ -859,7 +861,6 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
         }
     }
 }
-
 
 // Largest squared key norm per head over rows [0, rows) of k, merged into
 // kmax2[head] (non-negative FP32 bit patterns compare like unsigned integers,
