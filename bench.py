@@ -48,19 +48,20 @@ def elementwise_bytes(V: int, H: int, F: int):
     return {"modnorm": 4.0 * V * H, "qk_norm_rope": 8.0 * V * H, "modnorm2": 4.0 * V * H}
 
 
-def counter_traffic(kernel: str, source: str):
+def counter_traffic(kernel: str, sources):
     """HBM-side bytes per dispatch of `kernel` from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE summary (profiles/counters.json, already scaled by
-    the copy calibration), or None when the kernel's source has changed since
-    the counters were taken."""
+    the copy calibration), or None when any of the kernel's sources has
+    changed since the counters were taken."""
     import hashlib
     try:
         with open(os.path.join(ROOT, "profiles", "counters.json")) as f:
             c = json.load(f)
-        with open(os.path.join(ROOT, "video_diffusion_transformer_dit_amd", "csrc", source), "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()[:16]
-        if c["source_sha256_16"].get(source) != sha:
-            return None
+        for source in sources:
+            with open(os.path.join(ROOT, "video_diffusion_transformer_dit_amd", "csrc", source), "rb") as f:
+                sha = hashlib.sha256(f.read()).hexdigest()[:16]
+            if c["source_sha256_16"].get(source) != sha:
+                return None
         k = c["kernels"][kernel]
         return int(k["read_bytes"] + k["write_bytes"])
     except (OSError, KeyError, ValueError):
@@ -721,7 +722,8 @@ def main(argv=None) -> int:
         "kernels": kernels,
         "roofline": {"kernel": "attention_fwd_kernel<false, true, false> (dense, fixed softmax reference)", "bound": "mfma", "achieved": round(attn_tf, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": counter_traffic("void attention_fwd_kernel<false, true, false>", "attention.hip"),
+                     "traffic": counter_traffic("void attention_fwd_kernel<false, true, false>",
+                                                ["attention_fixed.hip", "h3_attention_kernel.h"]),
                      "traffic_unit": "bytes per launch (FETCH_SIZE x2 + WRITE_SIZE x1, copy-calibrated)",
                      "work_per_launch": "4 * 58758^2 * 5376 = 7.424e13 flop (QK^T and PV over valid rows)"},
     }

@@ -21,7 +21,12 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libh3block.so")
 
-SOURCES = ["validate.cpp", "runtime.hip", "elementwise.hip", "gemm.hip", "attention.hip", "sparse.hip", "gemm_mxfp8.hip", "mx_quant.hip", "block.hip"]
+SOURCES = ["validate.cpp", "runtime.hip", "elementwise.hip", "gemm.hip", "attention.hip", "attention_fixed.hip",
+           "sparse.hip", "gemm_mxfp8.hip", "mx_quant.hip", "block.hip"]
+# Per-source device flags. attention_fixed.hip selects the VGPR form of the
+# MFMA instructions (accumulators in VGPRs unless a register-class hint says
+# otherwise), so its score accumulators need no copy out of AGPRs.
+EXTRA = {"attention_fixed.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -35,7 +40,7 @@ def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, src + ".o")
     cmd = [HIPCC] + COMMON + ["-c", path, "-o", obj]
     if src.endswith(".hip"):
-        cmd[1:1] = DEVICE
+        cmd[1:1] = DEVICE + EXTRA.get(src, [])
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
