@@ -641,6 +641,16 @@ def main(argv=None) -> int:
     vt_ws = ws[off[h3.H3_WS_VT]:off[h3.H3_WS_VT] + lds[h3.H3_WS_VT]]
     k_ms["attention"] = time_calls(torch, lambda: h3.attention(
         qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:], o, V, heads, workspace=vt_ws), kit, 1)
+    # The attention kernel's own launches: the same call over K/V staged
+    # beforehand (V^T planes and key-norm maxima from h3_kv_stage), so it runs
+    # no pre-pass, only the fixed-reference launch, the online launch (every
+    # workgroup leaves at once here) and three tiny fills.
+    st_vt, st_km = h3.kv_stage(qkv[:V, H:2 * H], qkv[:V, 2 * H:], heads)
+    st_groups = [(0, V, [(qkv[:, H:2 * H], qkv[:, 2 * H:], 0, V, (st_vt, st_km))])]
+    st_ws = torch.empty(h3.attention_workspace_bytes(V, heads, st_groups), dtype=torch.uint8, device=dev)
+    k_ms["attention_kernel"] = time_calls(torch, lambda: h3.attention(
+        qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:], o, V, heads, groups=st_groups, workspace=st_ws), kit, 1)
+    del st_vt, st_km, st_ws
     k_ms["gemm_out_residual"] = time_calls(torch, lambda: h3.linear(
         o, w["w_o"], x1, V, h3.H3_EPI_RESIDUAL, resid=x, gate=mod[:, 2], ld_gate_group=6 * H, workspace=lws), kit, 1)
     k_ms["modnorm2"] = time_calls(torch, lambda: h3.fused_modulate_norm(
@@ -676,7 +686,7 @@ def main(argv=None) -> int:
     gemm_f, attn_f = block_flops(V, H, F)
     gflops = {"gemm_qkv": 2.0 * V * H * 3 * H, "gemm_out_residual": 2.0 * V * H * H,
               "gemm_up_swiglu": 2.0 * V * H * 2 * F, "gemm_down_residual": 2.0 * V * F * H, "attention": attn_f,
-              "attention_online": attn_f}
+              "attention_kernel": attn_f, "attention_online": attn_f}
     ebytes = elementwise_bytes(V, H, F)
     kernels = {}
     for k, t in k_ms.items():
@@ -691,7 +701,7 @@ def main(argv=None) -> int:
             d.update(gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4), frac_copy=round(gbs / copy_gbs, 4))
         kernels[k] = d
 
-    attn_tf = gflops["attention"] / (k_ms["attention"] * 1e-3) / 1e12
+    attn_tf = gflops["attention"] / (k_ms["attention_kernel"] * 1e-3) / 1e12
     gemm_ms = sum(k_ms[k] for k in k_ms if k.startswith("gemm"))
     total_tf = (gemm_f + attn_f) / (ms * 1e-3) / 1e12
     out = {
@@ -717,10 +727,13 @@ def main(argv=None) -> int:
                      "library_gemm": "hipBLASLt (torch.matmul) BF16 on the QKV shape, no epilogue"},
         "block_tflops": round(total_tf, 1),
         "block_frac_mfma": round(total_tf / PEAK_BF16_TFLOPS, 4),
-        "attention_tflops": round(attn_tf, 1),
+        "attention_tflops": round(gflops["attention"] / (k_ms["attention"] * 1e-3) / 1e12, 1),
         "gemm_tflops": round(gemm_f / (gemm_ms * 1e-3) / 1e12, 1),
         "kernels": kernels,
-        "roofline": {"kernel": "attention_fwd_kernel<false, true, false> (dense, fixed softmax reference)", "bound": "mfma", "achieved": round(attn_tf, 1),
+        "roofline": {"kernel": "attention_fwd_kernel<false, true, false> (dense, fixed softmax reference)",
+                     "timed_as": "kernels.attention_kernel: the attention launches over K/V staged beforehand; "
+                                 "kernels.attention is the whole call with its V^T and key-norm pre-passes",
+                     "bound": "mfma", "achieved": round(attn_tf, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": counter_traffic("void attention_fwd_kernel<false, true, false>",
                                                 ["attention_fixed.hip", "h3_attention_kernel.h"]),

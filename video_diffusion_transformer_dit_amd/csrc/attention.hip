@@ -322,7 +322,7 @@ void launch_attention(const uint16_t *q, int64_t ld_q, const uint16_t *k, int64_
         a.rng_group[0] = 0;
     }
     if (sch.n > 1 || split_range >= 0) {
-        attention_fwd_kernel<false, true, true><<<grid, kThreads, 0, stream>>>(a);
+        launch_attention_fixed_multi(grid, a, stream);
         attention_fwd_kernel<false, false, true><<<grid, kThreads, 0, stream>>>(a);
     } else if (sch.n == 1) {
         launch_attention_fixed(false, grid, a, stream);

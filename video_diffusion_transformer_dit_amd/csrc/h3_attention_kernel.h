@@ -1,8 +1,7 @@
 // The attention kernel template for gfx950 and the launch arguments its
-// host code fills in. Included by attention.hip (host code, the online-softmax
-// instances and the multi-range fixed-reference instance) and by
-// attention_fixed.hip (the single-range fixed-reference instances, dense and
-// list mode, built with MFMAs that accumulate the scores in VGPRs).
+// host code fills in. Included by attention.hip (host code and the
+// online-softmax instances) and by attention_fixed.hip (the fixed-reference
+// instances, built with MFMAs that accumulate the scores in VGPRs).
 //
 // H3_ATTN_SCORES_IN_VGPR (0 or 1, set by the including source before this
 // header) chooses the register class of the score accumulators: 1 keeps
@@ -95,9 +94,11 @@ inline AttnDeal attn_deal(int n) {
 }
 
 
-// The single-range fixed-reference instances (dense / grouped with one range,
-// and list mode), launched from attention_fixed.hip.
+// The fixed-reference instances, built in attention_fixed.hip: one range of
+// work items (dense / list mode), and several ranges (query groups, key-range
+// pieces).
 void launch_attention_fixed(bool sparse, dim3 grid, const AttnArgs &a, hipStream_t stream);
+void launch_attention_fixed_multi(dim3 grid, const AttnArgs &a, hipStream_t stream);
 
 namespace {
 
@@ -798,10 +799,13 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     //      channels in BF16 to its own 16 KB of the now idle K / V^T buffers
     //      ([64 rows][16 chunks of 8 channels], chunk c of row r at c ^
     //      (r & 15)) and stores them back row by row, 16 bytes per lane, which
-    //      shortens a short item's tail (measured -1 to -2% at 4,096 keys).
-    //      The one-range dense instance keeps direct stores: there the LDS path
-    //      moved the key loop's register allocation and cost 0.5%. ----
-    if constexpr (MULTI) {
+    //      shortens a short item's tail (measured -1 to -2% at 4,096 keys
+    //      with the scores in AGPRs). The instances with VGPR scores store
+    //      directly: there the LDS path pushed part of O into VGPRs, and the
+    //      direct form measured 1% faster on the streaming chunk's call; the
+    //      one-range dense instance also stores directly (with the scores in
+    //      AGPRs the LDS path had cost it 0.5%). ----
+    if constexpr (MULTI && !H3_ATTN_SCORES_IN_VGPR) {
         __syncthreads();  // every wave is done with the K / V^T buffers
         uint2 *lo = reinterpret_cast<uint2 *>(smem + wave * (D * 8));
 #pragma unroll
