@@ -682,6 +682,15 @@ def main(argv=None) -> int:
     hv, wq, qv = hbuf[:V], w["w_qkv"], qkv[:V]
     lib_ms = time_calls(torch, lambda: torch.matmul(hv, wq.t(), out=qv), 3, 1)
     lib_tf = 2.0 * V * H * 3 * H / (lib_ms * 1e-3) / 1e12
+    # The matrix cores' sustained BF16 rate on operands with varying bits and
+    # no memory traffic (h3_mfma_ceiling: the GEMM tile's register pattern):
+    # under load the clock is set by power, which this rate includes.
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(cus * 256, dtype=torch.float32, device=dev)
+    mf_flops = h3.mfma_ceiling(20000, sink)
+    mf_ms = time_calls(torch, lambda: h3.mfma_ceiling(20000, sink), 40, 5)
+    mf_tf = mf_flops / (mf_ms * 1e-3) / 1e12
+    del sink
 
     gemm_f, attn_f = block_flops(V, H, F)
     gflops = {"gemm_qkv": 2.0 * V * H * 3 * H, "gemm_out_residual": 2.0 * V * H * H,
@@ -693,7 +702,8 @@ def main(argv=None) -> int:
         d = {"ms": round(t, 4)}
         if k in gflops:
             tf = gflops[k] / (t * 1e-3) / 1e12
-            d.update(tflops=round(tf, 1), frac_mfma=round(tf / PEAK_BF16_TFLOPS, 4))
+            d.update(tflops=round(tf, 1), frac_mfma=round(tf / PEAK_BF16_TFLOPS, 4),
+                     frac_mfma_ceiling=round(tf / mf_tf, 4))
             if k.startswith("gemm"):
                 d.update(frac_library_gemm=round(tf / lib_tf, 4))
         if k in ebytes:
@@ -724,6 +734,11 @@ def main(argv=None) -> int:
                     "max": round(max(step_ms), 3)},
         "ceilings": {"copy_gbs": round(copy_gbs, 1), "copy_frac_hbm": round(copy_gbs / PEAK_HBM_GBS, 4),
                      "library_gemm_tflops": round(lib_tf, 1),
+                     "mfma_varying_operands_tflops": round(mf_tf, 1),
+                     "mfma_varying_operands_frac_peak": round(mf_tf / PEAK_BF16_TFLOPS, 4),
+                     "mfma_varying_operands": "h3_mfma_ceiling: v_mfma_f32_32x32x16_bf16 in the GEMM tile's register "
+                                              "pattern on BF16 operands with varying bits, no memory traffic, "
+                                              "one workgroup per CU",
                      "library_gemm": "hipBLASLt (torch.matmul) BF16 on the QKV shape, no epilogue"},
         "block_tflops": round(total_tf, 1),
         "block_frac_mfma": round(total_tf / PEAK_BF16_TFLOPS, 4),
@@ -734,6 +749,9 @@ def main(argv=None) -> int:
                      "timed_as": "kernels.attention_kernel: the attention launches over K/V staged beforehand; "
                                  "kernels.attention is the whole call with its V^T and key-norm pre-passes",
                      "bound": "mfma", "achieved": round(attn_tf, 1),
+                     "measured_ceiling": {"value": round(mf_tf, 1), "unit": "TFLOP/s",
+                                          "frac": round(attn_tf / mf_tf, 4),
+                                          "what": "ceilings.mfma_varying_operands"},
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": counter_traffic("void attention_fwd_kernel<false, true, false>",
                                                 ["attention_fixed.hip", "h3_attention_kernel.h"]),

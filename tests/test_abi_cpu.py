@@ -557,3 +557,15 @@ def test_mxfp8_validators():
     assert chk(as_=as_ + 1) == h3.H3_ERR_ALIGN
     assert chk(c=ws) == h3.H3_ERR_ALIAS
     assert chk(epi=1) == h3.H3_ERR_NULL                           # residual without resid / gate
+
+
+def test_mfma_ceiling_validator():
+    ok = C.c_double()
+    chk = h3.LIB.h3_check_mfma_ceiling
+    assert chk(1000, addr(1), 65536, C.byref(ok)) == h3.H3_OK
+    assert chk(1000, None, 65536, C.byref(ok)) == h3.H3_ERR_NULL
+    assert chk(1000, addr(1), 65536, None) == h3.H3_ERR_NULL
+    for iters in (0, -1, (1 << 20) + 1):
+        assert chk(iters, addr(1), 65536, C.byref(ok)) == h3.H3_ERR_SHAPE
+    assert chk(1000, addr(1), 255, C.byref(ok)) == h3.H3_ERR_SHAPE
+    assert chk(1000, addr(1) + 2, 65536, C.byref(ok)) == h3.H3_ERR_ALIGN

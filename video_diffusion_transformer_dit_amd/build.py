@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libh3block.so")
 
 SOURCES = ["validate.cpp", "runtime.hip", "elementwise.hip", "gemm.hip", "attention.hip", "attention_fixed.hip",
-           "sparse.hip", "gemm_mxfp8.hip", "mx_quant.hip", "block.hip"]
+           "sparse.hip", "gemm_mxfp8.hip", "mx_quant.hip", "block.hip", "ceiling.hip"]
 # Per-source device flags. attention_fixed.hip selects the VGPR form of the
 # MFMA instructions (accumulators in VGPRs unless a register-class hint says
 # otherwise), so its score accumulators need no copy out of AGPRs.

@@ -740,6 +740,13 @@ size_t h3_kv_stage_bytes(int64_t len, int32_t heads) {
     return (size_t)heads * kHeadDim * ((len + 63) / 64 * 64) * 2;
 }
 
+int h3_check_mfma_ceiling(int32_t iters, const float *sink, int64_t sink_floats, const double *flops) {
+    if (!sink || !flops) return H3_ERR_NULL;
+    if (iters < 1 || iters > (1 << 20) || sink_floats < 256) return H3_ERR_SHAPE;
+    if (reinterpret_cast<uintptr_t>(sink) & 3u) return H3_ERR_ALIGN;
+    return H3_OK;
+}
+
 int h3_check_kv_stage(const uint16_t *k, const uint16_t *v, int64_t ld, int64_t len, int32_t heads,
                       int32_t head_dim, const uint16_t *vt, const float *kmax2) {
     if (heads <= 0 || len < 0) return H3_ERR_SHAPE;

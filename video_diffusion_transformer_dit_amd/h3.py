@@ -89,6 +89,8 @@ def _load():
         "h3_kv_stage": [P, P, I64, I64, I32, I32, P, P, P],
         "h3_check_kv_stage": [P, P, I64, I64, I32, I32, P, P],
         "h3_kv_stage_bytes": [I64, I32],
+        "h3_mfma_ceiling": [I32, P, I64, C.POINTER(C.c_double), P],
+        "h3_check_mfma_ceiling": [I32, P, I64, C.POINTER(C.c_double)],
         "h3_attention_noalloc": [P, I64, P, I64, P, I64, P, I64, I64, I64, I32, I32, F32, C.POINTER(QGroup), I32,
                                  P],
         "h3_fused_modulate_norm": [P, I64, P, I64, P, P, P, I64, I32, P, P, I64, P, I64, I64, I64, I32, F32, I32, P],
@@ -178,7 +180,7 @@ EXPORTS = ["h3_block_forward", "h3_attention", "h3_fused_modulate_norm", "h3_qk_
            "h3_block_forward_mxfp8", "h3_check_block_forward_mxfp8", "h3_block_mxfp8_workspace_bytes",
            "h3_block_mxfp8_workspace_layout", "h3_stack_forward", "h3_check_stack_forward",
            "h3_attention_noalloc", "h3_linear_workspace_bytes", "h3_kv_stage", "h3_check_kv_stage",
-           "h3_kv_stage_bytes"]
+           "h3_kv_stage_bytes", "h3_mfma_ceiling", "h3_check_mfma_ceiling"]
 
 
 def status_string(s: int) -> str:
@@ -344,6 +346,15 @@ def kv_stage(k, v, heads, vt=None, kmax2=None, stream=None):
     s = LIB.h3_kv_stage(_ptr(k), _ptr(v), k.stride(0), n, heads, 128, _ptr(vt), _ptr(kmax2), _stream(stream))
     _ok(s, "h3_kv_stage")
     return vt, kmax2
+
+
+def mfma_ceiling(iters, sink, stream=None) -> float:
+    """Launch the matrix-core ceiling probe (h3_mfma_ceiling) on `sink` (FP32
+    device tensor of at least 256 floats per CU); returns the launch's flops."""
+    fl = C.c_double(0.0)
+    s = LIB.h3_mfma_ceiling(int(iters), _ptr(sink), sink.numel(), C.byref(fl), _stream(stream))
+    _ok(s, "h3_mfma_ceiling")
+    return fl.value
 
 
 def attention_noalloc(q, k, v, o, valid_len, heads, softmax_scale=0.0, groups=None, stream=None):
