@@ -38,6 +38,11 @@
 //    the rest. P is rounded to BF16 for the P.V MFMA. The key that sets m
 //    gets p within 2^-19 of 1, so BF16(p) = 1: with one valid key both forms
 //    return that key's value exactly.
+//  * The kernel template is in h3_attention_kernel.h. The fixed-reference
+//    instances are built in attention_fixed.hip with the VGPR form of the
+//    MFMA instructions, so their score accumulators are VGPRs that the
+//    softmax reads in place; the online instances, built here, keep them in
+//    AGPRs next to Q and O.
 //  * Workgroups are dealt round-robin over the 8 XCDs, and work items are
 //    remapped so each XCD walks a contiguous range (consecutive query tiles
 //    of one head): the workgroups resident on an XCD stream the same K/V
