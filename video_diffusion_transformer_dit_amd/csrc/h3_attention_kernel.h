@@ -353,7 +353,9 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) asm volatile("" : "+a"(oacc[i][j]));
-    float l_run[2] = {0.f, 0.f};
+    // Row sums of p as two running partial sums per query block (even and
+    // odd keys of each pair), added together at the end.
+    float sa[2] = {0.f, 0.f}, sb[2] = {0.f, 0.f};
 
     // ---- tile loads (direct to LDS). A K tile is 16 slabs of 4 keys x 16
     //      chunks, a V^T tile 16 slabs of 8 channels x 8 chunks; wave w loads
@@ -616,7 +618,8 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
                     const float d = fmaxf(tm[j], 0.f);
                     const float alpha = __builtin_amdgcn_exp2f(-d);
                     m_ref[j] += d;
-                    l_run[j] *= alpha;
+                    sa[j] *= alpha;
+                    sb[j] *= alpha;
 #pragma unroll
                     for (int v = 0; v < 16; ++v) sv[j][v] -= d;
 #pragma unroll
@@ -715,7 +718,6 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
         // stores pair w-1 of the new scores from sacc into sv as y = s c -
         // m_ref (pair w-1 was summed the slot before) and takes the maximum
         // of pair w-2.
-        float sa[2] = {0.f, 0.f}, sb[2] = {0.f, 0.f};
         float mx[2] = {-__builtin_huge_valf(), -__builtin_huge_valf()};
         auto copy_pair = [&](int w) {
             const int gj = w >> 3, e = w & 7;
@@ -750,7 +752,6 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            l_run[j] += sa[j] + sb[j];
             if (!fixed) tmaxr[j] = mx[j];
         }
         if (odd) vk_cur = vk_next;
@@ -777,7 +778,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
         float2 *pml = reinterpret_cast<float2 *>(a.part + (int64_t)a.part_records * BQ * D) + (int64_t)rec * BQ;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const float l_tot = pair_sum(l_run[j]);
+            const float l_tot = pair_sum(sa[j] + sb[j]);
             const int r = (int)qw + 32 * j + l32;
             if (r < rows_left) {
 #pragma unroll
@@ -810,7 +811,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
         uint2 *lo = reinterpret_cast<uint2 *>(smem + wave * (D * 8));
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const float inv = 1.0f / pair_sum(l_run[j]);
+            const float inv = 1.0f / pair_sum(sa[j] + sb[j]);
             const int row = 32 * j + l32;
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
@@ -834,7 +835,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(AttnArgs a) 
     } else {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const float l_tot = pair_sum(l_run[j]);
+            const float l_tot = pair_sum(sa[j] + sb[j]);
             const float inv = 1.0f / l_tot;
             const int64_t q = qw + 32 * j + l32;
             if (q < rows_left) {
