@@ -336,7 +336,7 @@ def block_sparse(torch, h3, dev, q, k, v, o, V, heads, dense_ms, iters, block, p
     return out
 
 
-def mxfp8_gemms(torch, h3, dev, w, bufs, mod, L, V, H, F, bf16_ms, iters, dims, block_ms):
+def mxfp8_gemms(torch, h3, dev, w, bufs, mod, L, V, H, F, bf16_ms, iters, dims, block_ms, fp8_ceiling=None):
     """The block's four projections as MXFP8 GEMMs (E4M3 with one E8M0 scale
     per 32 along K) at the benchmark's shapes, on the block's own
     activations. Weights are quantized once, outside the timing (they are
@@ -366,13 +366,15 @@ def mxfp8_gemms(torch, h3, dev, w, bufs, mod, L, V, H, F, bf16_ms, iters, dims, 
         "gemm_down_residual": (lambda: h3.linear_mxfp8(*aq["g"], *wq["w_down"], yo, V, h3.H3_EPI_RESIDUAL, resid=x1,
                                                        gate=mod[:, 5], ld_gate_group=6 * H), 2.0 * V * F * H),
     }
-    out = {"peak_fp8_tflops": PEAK_FP8_TFLOPS, "gemms": {}}
+    out = {"peak_fp8_tflops": PEAK_FP8_TFLOPS, "measured_fp8_ceiling_tflops": fp8_ceiling, "gemms": {}}
     tot_mx, tot_bf = 0.0, 0.0
     for k, (fn, fl) in calls.items():
         t = time_calls(torch, fn, iters, 1)
         tf = fl / (t * 1e-3) / 1e12
         out["gemms"][k] = {"ms": round(t, 4), "tflops": round(tf, 1), "frac_fp8_mfma": round(tf / PEAK_FP8_TFLOPS, 4),
                            "bf16_ms": round(bf16_ms[k], 4), "speedup_vs_bf16": round(bf16_ms[k] / t, 3)}
+        if fp8_ceiling:
+            out["gemms"][k]["frac_fp8_ceiling"] = round(tf / fp8_ceiling, 4)
         tot_mx += t
         tot_bf += bf16_ms[k]
     qt = {}
@@ -690,6 +692,9 @@ def main(argv=None) -> int:
     mf_flops = h3.mfma_ceiling(20000, sink)
     mf_ms = time_calls(torch, lambda: h3.mfma_ceiling(20000, sink), 40, 5)
     mf_tf = mf_flops / (mf_ms * 1e-3) / 1e12
+    mf8_flops = h3.mfma_ceiling(10000, sink, h3.H3_CEIL_FP8)
+    mf8_ms = time_calls(torch, lambda: h3.mfma_ceiling(10000, sink, h3.H3_CEIL_FP8), 40, 5)
+    mf8_tf = mf8_flops / (mf8_ms * 1e-3) / 1e12
     del sink
 
     gemm_f, attn_f = block_flops(V, H, F)
@@ -739,6 +744,8 @@ def main(argv=None) -> int:
                      "mfma_varying_operands": "h3_mfma_ceiling: v_mfma_f32_32x32x16_bf16 in the GEMM tile's register "
                                               "pattern on BF16 operands with varying bits, no memory traffic, "
                                               "one workgroup per CU",
+                     "mfma_fp8_varying_operands_tflops": round(mf8_tf, 1),
+                     "mfma_fp8_varying_operands_frac_peak": round(mf8_tf / PEAK_FP8_TFLOPS, 4),
                      "library_gemm": "hipBLASLt (torch.matmul) BF16 on the QKV shape, no epilogue"},
         "block_tflops": round(total_tf, 1),
         "block_frac_mfma": round(total_tf / PEAK_BF16_TFLOPS, 4),
@@ -771,7 +778,7 @@ def main(argv=None) -> int:
                                                              (dims, weights, x, y, mod, ms))
         progress("block-sparse attention timed")
         out["next"]["mxfp8_gemms"] = mxfp8_gemms(torch, h3, dev, w, (hbuf, o, x, x1, h2, g, y), mod, L, V, H, F,
-                                                 k_ms, kit, dims, ms)
+                                                 k_ms, kit, dims, ms, fp8_ceiling=round(mf8_tf, 1))
         progress("MXFP8 GEMMs timed")
         out["next"]["reference_kv_cache"] = reference_kv_cache(torch, h3, dev, dims, weights, mod, gen, L, V, H)
         progress("reference K/V caching timed")

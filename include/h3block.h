@@ -724,9 +724,13 @@ int h3_check_block_forward_mxfp8(const h3_dims *dims, const h3_block_weights_mxf
  * h3_mfma_ceiling - a measured ceiling for the matrix-core roofline (not a
  * step of the block; a measurement aid for the GEMM and attention kernels).
  * Runs one workgroup of 4 waves per CU, each wave issuing `iters` rounds of
- * 16 v_mfma_f32_32x32x16_bf16 in the GEMM tile's register pattern (4 A and 4
- * B operands, 16 accumulators) on BF16 operands with varying bits, with no
- * memory traffic; time it on `stream` to get the sustained BF16 MFMA rate.
+ * 16 MFMAs in the GEMM tile's register pattern (4 A and 4 B operands, 16
+ * accumulators) on operands with varying bits, with no memory traffic; time
+ * it on `stream` to get the sustained MFMA rate.
+ *   dtype        H3_CEIL_BF16: v_mfma_f32_32x32x16_bf16;
+ *                H3_CEIL_FP8: v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3
+ *                operands with unit E8M0 scales (the MXFP8 GEMM's MFMA).
+ *                Other values: H3_ERR_UNSUPPORTED.
  *   iters        1 .. 2^20 rounds per wave.
  *   sink         device FP32 buffer of sink_floats >= 256 * (CU count)
  *                floats (4-byte aligned); receives one sum per thread so the
@@ -734,8 +738,10 @@ int h3_check_block_forward_mxfp8(const h3_dims *dims, const h3_block_weights_mxf
  *   flops        host double: set to the launch's MFMA flops.
  * H3_ERR_SHAPE when sink_floats is below 256 per CU of the current device.
  * ------------------------------------------------------------------------- */
-int h3_mfma_ceiling(int32_t iters, float *sink, int64_t sink_floats, double *flops, void *stream);
-int h3_check_mfma_ceiling(int32_t iters, const float *sink, int64_t sink_floats, const double *flops);
+enum { H3_CEIL_BF16 = 0, H3_CEIL_FP8 = 1 };
+int h3_mfma_ceiling(int32_t dtype, int32_t iters, float *sink, int64_t sink_floats, double *flops, void *stream);
+int h3_check_mfma_ceiling(int32_t dtype, int32_t iters, const float *sink, int64_t sink_floats,
+                          const double *flops);
 
 /* Human-readable name of a status code (static string). */
 const char *h3_status_string(int status);

@@ -562,10 +562,13 @@ def test_mxfp8_validators():
 def test_mfma_ceiling_validator():
     ok = C.c_double()
     chk = h3.LIB.h3_check_mfma_ceiling
-    assert chk(1000, addr(1), 65536, C.byref(ok)) == h3.H3_OK
-    assert chk(1000, None, 65536, C.byref(ok)) == h3.H3_ERR_NULL
-    assert chk(1000, addr(1), 65536, None) == h3.H3_ERR_NULL
-    for iters in (0, -1, (1 << 20) + 1):
-        assert chk(iters, addr(1), 65536, C.byref(ok)) == h3.H3_ERR_SHAPE
-    assert chk(1000, addr(1), 255, C.byref(ok)) == h3.H3_ERR_SHAPE
-    assert chk(1000, addr(1) + 2, 65536, C.byref(ok)) == h3.H3_ERR_ALIGN
+    for dt in (h3.H3_CEIL_BF16, h3.H3_CEIL_FP8):
+        assert chk(dt, 1000, addr(1), 65536, C.byref(ok)) == h3.H3_OK
+        assert chk(dt, 1000, None, 65536, C.byref(ok)) == h3.H3_ERR_NULL
+        assert chk(dt, 1000, addr(1), 65536, None) == h3.H3_ERR_NULL
+        for iters in (0, -1, (1 << 20) + 1):
+            assert chk(dt, iters, addr(1), 65536, C.byref(ok)) == h3.H3_ERR_SHAPE
+        assert chk(dt, 1000, addr(1), 255, C.byref(ok)) == h3.H3_ERR_SHAPE
+        assert chk(dt, 1000, addr(1) + 2, 65536, C.byref(ok)) == h3.H3_ERR_ALIGN
+    for dt in (-1, 2):
+        assert chk(dt, 1000, addr(1), 65536, C.byref(ok)) == h3.H3_ERR_UNSUPPORTED

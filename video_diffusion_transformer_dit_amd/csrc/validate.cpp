@@ -740,7 +740,8 @@ size_t h3_kv_stage_bytes(int64_t len, int32_t heads) {
     return (size_t)heads * kHeadDim * ((len + 63) / 64 * 64) * 2;
 }
 
-int h3_check_mfma_ceiling(int32_t iters, const float *sink, int64_t sink_floats, const double *flops) {
+int h3_check_mfma_ceiling(int32_t dtype, int32_t iters, const float *sink, int64_t sink_floats, const double *flops) {
+    if (dtype != H3_CEIL_BF16 && dtype != H3_CEIL_FP8) return H3_ERR_UNSUPPORTED;
     if (!sink || !flops) return H3_ERR_NULL;
     if (iters < 1 || iters > (1 << 20) || sink_floats < 256) return H3_ERR_SHAPE;
     if (reinterpret_cast<uintptr_t>(sink) & 3u) return H3_ERR_ALIGN;

@@ -26,6 +26,7 @@ H3_MAX_SEGMENTS = 4
 H3_MAX_GROUPS = 8
 H3_SPARSE_Q_BLOCK, H3_SPARSE_K_BLOCK, H3_SPARSE_MAX_KBLOCKS = 256, 64, 4096
 H3_ATTENTION_SCRATCH_BYTES = 128 << 20
+H3_CEIL_BF16, H3_CEIL_FP8 = 0, 1
 
 
 class H3Error(RuntimeError):
@@ -89,8 +90,8 @@ def _load():
         "h3_kv_stage": [P, P, I64, I64, I32, I32, P, P, P],
         "h3_check_kv_stage": [P, P, I64, I64, I32, I32, P, P],
         "h3_kv_stage_bytes": [I64, I32],
-        "h3_mfma_ceiling": [I32, P, I64, C.POINTER(C.c_double), P],
-        "h3_check_mfma_ceiling": [I32, P, I64, C.POINTER(C.c_double)],
+        "h3_mfma_ceiling": [I32, I32, P, I64, C.POINTER(C.c_double), P],
+        "h3_check_mfma_ceiling": [I32, I32, P, I64, C.POINTER(C.c_double)],
         "h3_attention_noalloc": [P, I64, P, I64, P, I64, P, I64, I64, I64, I32, I32, F32, C.POINTER(QGroup), I32,
                                  P],
         "h3_fused_modulate_norm": [P, I64, P, I64, P, P, P, I64, I32, P, P, I64, P, I64, I64, I64, I32, F32, I32, P],
@@ -348,11 +349,12 @@ def kv_stage(k, v, heads, vt=None, kmax2=None, stream=None):
     return vt, kmax2
 
 
-def mfma_ceiling(iters, sink, stream=None) -> float:
-    """Launch the matrix-core ceiling probe (h3_mfma_ceiling) on `sink` (FP32
-    device tensor of at least 256 floats per CU); returns the launch's flops."""
+def mfma_ceiling(iters, sink, dtype=0, stream=None) -> float:
+    """Launch the matrix-core ceiling probe (h3_mfma_ceiling; dtype
+    H3_CEIL_BF16 or H3_CEIL_FP8) on `sink` (FP32 device tensor of at least
+    256 floats per CU); returns the launch's flops."""
     fl = C.c_double(0.0)
-    s = LIB.h3_mfma_ceiling(int(iters), _ptr(sink), sink.numel(), C.byref(fl), _stream(stream))
+    s = LIB.h3_mfma_ceiling(int(dtype), int(iters), _ptr(sink), sink.numel(), C.byref(fl), _stream(stream))
     _ok(s, "h3_mfma_ceiling")
     return fl.value
 
