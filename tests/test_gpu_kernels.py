@@ -294,8 +294,9 @@ def test_linear_stream_k_tail(epi, M, Mv, N, K):
     (stream-K tail): 32 tiles of 118 stages cut into 256 ranges of 14-15
     stages (ranges straddle tiles), and 264 tiles = one whole round plus a
     tail of 8 tiles of 104 stages cut into 104 ranges of 8. Against the
-    oracle, and against the unsplit call (a different FP32 summation order
-    only)."""
+    oracle, against the unsplit call (a different FP32 summation order
+    only), and against a second call on the same workspace bit for bit (the
+    fix-up adds the partial sums in K order)."""
     _say(f"linear stream-K epi={epi} M={M} Mv={Mv} N={N} K={K}")
     need = h3.linear_workspace_bytes(Mv, N, K, epi)
     assert need > 0, "the shape must take the split path"
@@ -315,9 +316,12 @@ def test_linear_stream_k_tail(epi, M, Mv, N, K):
     ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")  # stale contents must not matter
     c = poison((M, cols))
     h3.linear(a, w, c, Mv, epi, workspace=ws, **kw)
+    c2 = poison((M, cols))
+    h3.linear(a, w, c2, Mv, epi, workspace=ws, **kw)
     c0 = poison((M, cols))
     h3.linear(a, w, c0, Mv, epi, **kw)
     torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(c2), bits(c), err_msg="second split call differs")
     u = O.linear(O.bf16_to_f64(ab[:Mv]), O.bf16_to_f64(wb), O.bf16_to_f64(bb))
     if epi == h3.H3_EPI_STORE:
         ref, slack = u, 0.0
@@ -329,6 +333,55 @@ def test_linear_stream_k_tail(epi, M, Mv, N, K):
     assert_parity(f64(c)[:Mv], ref, "c (split tail)", slack=slack)
     assert_parity(f64(c)[:Mv], f64(c0)[:Mv], "c split vs unsplit", slack=slack)
     assert_zero_rows(c, Mv, "c")
+
+
+@pytest.mark.parametrize("epi,Mv,N,K,split", [(h3.H3_EPI_RESIDUAL, 4096, 5376, 21504, True),
+                                              (h3.H3_EPI_RESIDUAL, 4096, 5376, 5376, True),
+                                              (h3.H3_EPI_STORE, 5424, 16128, 5376, False),
+                                              (h3.H3_EPI_SWIGLU, 5424, 43008, 5376, False)])
+def test_linear_block_shapes_full_size(epi, Mv, N, K, split):
+    """The block's projections at full width, in the launches the block
+    makes with its workspace: at 4,096 rows the down and output projections
+    (336 tiles: one round plus a stream-K tail of 80 tiles in 256 ranges),
+    at the streaming forward's 5,424 rows the QKV projection (1,386 tiles,
+    no split) and up + SwiGLU (3,696 tiles, the last rounds drawn). Against
+    the call without a workspace over every element (bit for bit where
+    nothing is split, else the FP32 summation slack) and sampled rows, most
+    of them in the last tile rows, against the oracle."""
+    _say(f"linear full size epi={epi} Mv={Mv} N={N} K={K}")
+    need = h3.linear_workspace_bytes(Mv, N, K, epi)
+    assert (need > 256) == split
+    ab = I.normal_bf16("lf.a", (Mv, K))
+    wb = I.normal_bf16("lf.w", (N, K), 0.02)
+    bb = I.normal_bf16("lf.b", (N,), 0.5)
+    cols = N // 2 if epi == h3.H3_EPI_SWIGLU else N
+    kw = {"bias": dev_bf16(bb)}
+    if epi == h3.H3_EPI_RESIDUAL:
+        rb = I.normal_bf16("lf.r", (Mv, N))
+        mod = I.normal_f32("lf.mod", (1, 6, N), 0.5)
+        kw.update(resid=dev_bf16(rb), gate=dev_f32(mod)[:, 2], n_mod_groups=1)
+    a, w = dev_bf16(ab), dev_bf16(wb)
+    ws = torch.full((max(need, 1),), 0x7F, dtype=torch.uint8, device="cuda") if need else None
+    c = poison((Mv, cols))
+    h3.linear(a, w, c, Mv, epi, workspace=ws, **kw)
+    c0 = poison((Mv, cols))
+    h3.linear(a, w, c0, Mv, epi, **kw)
+    torch.cuda.synchronize()
+    slack = BF16_SLACK if epi == h3.H3_EPI_SWIGLU else 0.0
+    if split:
+        assert_parity(f64(c), f64(c0), "c split vs unsplit", slack=slack)
+    else:
+        np.testing.assert_array_equal(bits(c), bits(c0), err_msg="workspace call differs")
+    rows = np.unique(np.concatenate([np.arange(0, Mv, 613), np.arange(Mv - 512, Mv, 37), np.arange(Mv - 4, Mv)]))
+    u = O.linear(O.bf16_to_f64(ab[rows]), O.bf16_to_f64(wb), O.bf16_to_f64(bb))
+    if epi == h3.H3_EPI_SWIGLU:
+        ref = O.swiglu(u, N // 2)
+    elif epi == h3.H3_EPI_RESIDUAL:
+        m = O.gather_mod(mod.astype(np.float64), None, Mv)[rows]
+        ref = O.gated_residual(O.bf16_to_f64(rb[rows]), m[:, O.GATE_A], u)
+    else:
+        ref = u
+    assert_parity(f64(c)[rows], ref, "c (sampled rows)", slack=slack)
 
 
 @pytest.mark.parametrize("epi,Mv,N,K", [(h3.H3_EPI_STORE, 2000, 65536, 192), (h3.H3_EPI_SWIGLU, 1900, 65536, 128),
