@@ -403,6 +403,25 @@ def mxfp8_gemms(torch, h3, dev, w, bufs, mod, L, V, H, F, bf16_ms, iters, dims, 
     return out
 
 
+def qkv_fill_sweep(torch, h3, dev, gen, H: int) -> int:
+    """The QKV projection's time against the fill of its last round of 256
+    workgroup slots (63 tiles per 256-row tile row): rounds of 63 to 252
+    tiles alone, then whole rounds followed by a partial one."""
+    rows = [256, 512, 768, 1024, 4096, 4352, 4608, 5120, 5376, 5424]
+    Lm = max(rows)
+    h = torch.randn((Lm, H), generator=gen, device=dev).to(torch.bfloat16)
+    wq = (0.02 * torch.randn((3 * H, H), generator=gen, device=dev)).to(torch.bfloat16)
+    qkv = torch.empty((Lm, 3 * H), dtype=torch.bfloat16, device=dev)
+    out = []
+    for m in rows:
+        ms = time_calls(torch, lambda: h3.linear(h[:m], wq, qkv[:m], m), 10, 2)  # no padding rows to zero
+        tiles = (m + 255) // 256 * 63
+        out.append({"rows": m, "tiles": tiles, "rounds": round(tiles / 256, 3), "ms": round(ms, 4)})
+        progress(f"qkv fill sweep: {m} rows, {tiles} tiles, {ms:.4f} ms")
+    print(json.dumps({"qkv_fill_sweep": out}), flush=True)
+    return 0
+
+
 def progress(msg: str) -> None:
     """One line on stderr per finished section (stdout carries only the JSON)."""
     print(f"bench: {msg}", file=sys.stderr, flush=True)
@@ -586,6 +605,9 @@ def main(argv=None) -> int:
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (the known-size reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--qkv-fill-sweep", action="store_true",
+                    help="instead of the bench: time the QKV projection (K 5,376, N 16,128, no workspace) at row "
+                         "counts whose last round of 256 tiles is filled to different degrees, one JSON line")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); the library has no multi-GPU path.",
@@ -601,6 +623,8 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     gen = torch.Generator(device=dev)
     gen.manual_seed(SEED)
+    if a.qkv_fill_sweep:
+        return qkv_fill_sweep(torch, h3, dev, gen, H)
 
     def normal(shape, std=1.0, mean=0.0, dtype=torch.bfloat16):
         t = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
